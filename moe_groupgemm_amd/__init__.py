@@ -1,0 +1,225 @@
+"""Python binding of the MoE-layer megakernel library (``libmoe_mk.so``, C ABI in include/moe_mk.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.  PyTorch
+supplies device memory and streams.  The functions carry the C names; see the header for
+the meaning of each argument.  There is no fallback: if the library is missing or a call
+fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mk.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe_mk.h")
+
+MOE_MK_SCHED_STATIC = 0
+MOE_MK_SCHED_DYNAMIC = 1
+MOE_MK_OK = 0
+MOE_MK_ERR_WATCHDOG = 1
+MOE_MK_ERR_NONFINITE = 2
+MOE_MK_ERR_QUEUE = 4
+MOE_MK_ERR_UNINIT = 8
+MOE_MK_DEBUG_DROP_NOTIFY = 1
+
+_lib = None
+
+
+class MoeMkError(RuntimeError):
+    def __init__(self, what: str, code: int):
+        super().__init__(f"{what}: {moe_mk_status_str(code)} ({code})")
+        self.code = code
+
+
+class _RoutingView(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("hist", ctypes.c_void_p),
+                ("exp_indptr", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("inv", ctypes.c_void_p),
+                ("logits", ctypes.c_void_p), ("ctl", ctypes.c_void_p)]
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with moe_groupgemm_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.moe_mk_plan.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_int]
+    L.moe_mk_plan.restype = ctypes.c_int
+    L.moe_mk_plan_destroy.argtypes = [vp]
+    L.moe_mk_plan_destroy.restype = None
+    L.moe_mk_workspace_bytes.argtypes = [vp, i64]
+    L.moe_mk_workspace_bytes.restype = sz
+    L.moe_mk_workspace_init.argtypes = [vp, vp, sz, vp]
+    L.moe_mk_workspace_init.restype = ctypes.c_int
+    L.moe_mk_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz, vp]
+    L.moe_mk_forward.restype = ctypes.c_int
+    L.moe_mk_routing_view.argtypes = [vp, i64, vp, sz, ctypes.POINTER(_RoutingView)]
+    L.moe_mk_routing_view.restype = ctypes.c_int
+    L.moe_mk_workspace_error.argtypes = [vp, vp, sz, vp, ctypes.POINTER(i32)]
+    L.moe_mk_workspace_error.restype = ctypes.c_int
+    L.moe_mk_plan_info.argtypes = [vp, ctypes.c_char_p]
+    L.moe_mk_plan_info.restype = i64
+    L.moe_mk_plan_set_debug.argtypes = [vp, i64, i32]
+    L.moe_mk_plan_set_debug.restype = ctypes.c_int
+    L.moe_mk_status_str.argtypes = [ctypes.c_int]
+    L.moe_mk_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions the C header declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(moe_mk_[a-z_]+)\s*\(", text)))
+
+
+def moe_mk_status_str(code: int) -> str:
+    return lib().moe_mk_status_str(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code != MOE_MK_OK:
+        raise MoeMkError(what, code)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def moe_mk_plan(E: int, k: int, d: int, f: int, sched: int = MOE_MK_SCHED_STATIC) -> int:
+    p = ctypes.c_void_p()
+    _check(lib().moe_mk_plan(ctypes.byref(p), E, k, d, f, sched), "moe_mk_plan")
+    return p.value
+
+
+def moe_mk_plan_destroy(plan: int) -> None:
+    lib().moe_mk_plan_destroy(plan)
+
+
+def moe_mk_workspace_bytes(plan: int, B: int) -> int:
+    return int(lib().moe_mk_workspace_bytes(plan, B))
+
+
+def moe_mk_workspace_init(plan: int, ws, stream=None) -> None:
+    _check(lib().moe_mk_workspace_init(plan, _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_mk_workspace_init")
+
+
+def moe_mk_forward(plan: int, x, Wr, router_bias, W1, W3, W2, out, B: int, ws, stream=None) -> None:
+    import torch
+    bf = torch.bfloat16
+    _check(lib().moe_mk_forward(plan, _dev_ptr(x, "x", bf), _dev_ptr(Wr, "Wr", torch.float32),
+                                _dev_ptr(router_bias, "router_bias", torch.float32), _dev_ptr(W1, "W1", bf),
+                                _dev_ptr(W3, "W3", bf), _dev_ptr(W2, "W2", bf), _dev_ptr(out, "out", bf), B,
+                                _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_mk_forward")
+
+
+def moe_mk_routing_view(plan: int, B: int, ws) -> dict:
+    """Views (no copies) of the routing arrays of the last forward with batch size B."""
+    import torch
+    v = _RoutingView()
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().moe_mk_routing_view(plan, B, ws.data_ptr(), nbytes, ctypes.byref(v)), "moe_mk_routing_view")
+    E = moe_mk_plan_info(plan, "E")
+    k = moe_mk_plan_info(plan, "k")
+    raw = ws.view(torch.uint8).reshape(-1)
+    base = ws.data_ptr()
+
+    def part(ptr, n, dtype, shape):
+        off = ptr - base
+        size = n * torch.empty((), dtype=dtype).element_size()
+        return raw[off:off + size].view(dtype).reshape(shape)
+
+    return {"topk_idx": part(v.topk_idx, B * k, torch.int32, (B, k)),
+            "topk_w": part(v.topk_w, B * k, torch.float32, (B, k)),
+            "hist": part(v.hist, E, torch.int32, (E,)),
+            "exp_indptr": part(v.exp_indptr, E + 1, torch.int32, (E + 1,)),
+            "perm": part(v.perm, B * k, torch.int32, (B * k,)),
+            "inv": part(v.inv, B * k, torch.int32, (B * k,)),
+            "logits": part(v.logits, B * E, torch.float32, (B, E)),
+            "ctl": part(v.ctl, 64, torch.int32, (64,))}
+
+
+def moe_mk_workspace_error(plan: int, ws, stream=None) -> int:
+    err = ctypes.c_int32()
+    _check(lib().moe_mk_workspace_error(plan, ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream),
+                                        ctypes.byref(err)), "moe_mk_workspace_error")
+    return int(err.value)
+
+
+def moe_mk_plan_info(plan: int, key: str) -> int:
+    v = int(lib().moe_mk_plan_info(plan, key.encode()))
+    if v < 0:
+        raise KeyError(key)
+    return v
+
+
+def moe_mk_plan_set_debug(plan: int, watchdog_ticks: int = 0, flags: int = 0) -> None:
+    _check(lib().moe_mk_plan_set_debug(plan, watchdog_ticks, flags), "moe_mk_plan_set_debug")
+
+
+class MoELayer:
+    """A plan plus a workspace sized for ``max_batch`` tokens, bound to fixed weights."""
+
+    def __init__(self, E, k, d, f, Wr, W1, W3, W2, router_bias=None, sched=MOE_MK_SCHED_STATIC,
+                 max_batch: int = 1, device=None):
+        import torch
+        self.E, self.k, self.d, self.f = E, k, d, f
+        self.Wr, self.W1, self.W3, self.W2, self.bias = Wr, W1, W3, W2, router_bias
+        self.plan = moe_mk_plan(E, k, d, f, sched)
+        nbytes = moe_mk_workspace_bytes(self.plan, max(1, max_batch))
+        self.ws = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device or "cuda")
+        moe_mk_workspace_init(self.plan, self.ws)
+        self.max_batch = max_batch
+
+    def forward(self, x, out=None, stream=None):
+        import torch
+        B = x.shape[0]
+        if B > self.max_batch:
+            raise ValueError(f"batch {B} exceeds the workspace capacity {self.max_batch}")
+        if out is None:
+            out = torch.empty((B, self.d), dtype=torch.bfloat16, device=x.device)
+        moe_mk_forward(self.plan, x, self.Wr, self.bias, self.W1, self.W3, self.W2, out, B, self.ws, stream)
+        return out
+
+    __call__ = forward
+
+    def routing(self, B):
+        return moe_mk_routing_view(self.plan, B, self.ws)
+
+    def error(self, stream=None) -> int:
+        return moe_mk_workspace_error(self.plan, self.ws, stream)
+
+    def reinit(self):
+        moe_mk_workspace_init(self.plan, self.ws)
+
+    def close(self):
+        if self.plan:
+            moe_mk_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,143 @@
+// mk_common.h -- constants, workspace layout and kernel parameters shared by the host
+// library and the megakernel (both are compiled into the same shared library).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mk {
+
+constexpr int kThreads = 256;        // 4 waves of 64 lanes per persistent workgroup
+constexpr int kTileTokens = 64;      // tokens per top-k / grouping tile (one lane per token)
+constexpr int kRouteTokens = 16;     // tokens per router task (4 per wave)
+constexpr int kRouteExperts = 16;    // experts per router task
+constexpr int kCombineTokens = 16;   // tokens per combine task
+constexpr int kBM = 64;              // GroupGEMM rows per tile (one expert's rows)
+constexpr int kBN = 64;              // GroupGEMM columns per tile
+constexpr int kBK = 64;              // GroupGEMM K step staged through LDS
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 16;
+
+// Control block: int32 words at the start of the workspace.
+enum CtlWord {
+    CTL_EPOCH = 0,     // forward counter; tags queue slots and the published task total
+    CTL_EXIT = 1,      // workgroups that left the current forward
+    CTL_ERR = 2,       // sticky error bits (MOE_MK_ERR_*)
+    CTL_QHEAD = 3,     // dynamic queue: next index to claim
+    CTL_QTAIL = 4,     // dynamic queue: next slot to fill
+    CTL_EV_TOPK = 5,   // event: all top-k tiles done (one consumer: the scan task)
+    CTL_EV_SCAN = 6,   // event: scan done; rest value 1
+    CTL_EV_Y = 7,      // event: all down-projection tiles done
+    CTL_MAGIC = 8,     // set by workspace init
+    CTL_MT_TOTAL = 9,  // number of (expert, row-tile) pairs, written by the scan task
+    CTL_TOTAL64 = 12,  // int64 at words 12..13: (epoch << 32) | total task count (dynamic mode)
+    CTL_DBG = 16,      // 8 per-kind task counters (accumulate across forwards)
+    CTL_WORDS = 64
+};
+
+constexpr int32_t kMagic = 0x4d4f4531;  // "MOE1"
+
+enum TaskKind { K_ROUTE = 0, K_TOPK = 1, K_SCAN = 2, K_GROUP = 3, K_GEMM1 = 4, K_GEMM2 = 5, K_COMBINE = 6 };
+
+struct Shape {
+    int E, k, d, f;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Task counts that depend on B only.
+struct Counts {
+    int64_t T;      // top-k / grouping tiles
+    int64_t nTG;    // router token groups
+    int64_t nEB;    // router expert blocks
+    int64_t nR;     // router tasks
+    int64_t nC;     // combine tasks
+    int64_t mt_cap; // upper bound of sum_e ceil(hist[e] / kBM)
+    int64_t NB1, NB2;
+    int64_t q_cap;  // upper bound of the pushed tasks of one forward
+};
+
+inline Counts make_counts(const Shape &s, int64_t B) {
+    Counts c;
+    c.T = ceil_div(B, kTileTokens);
+    c.nTG = ceil_div(B, kRouteTokens);
+    c.nEB = ceil_div(s.E, kRouteExperts);
+    c.nR = c.nTG * c.nEB;
+    c.nC = ceil_div(B, kCombineTokens);
+    int64_t a = B * s.k;
+    c.mt_cap = a / kBM + (a < s.E ? a : s.E) + 1;
+    c.NB1 = s.f / kBN;
+    c.NB2 = s.d / kBN;
+    c.q_cap = 2 * c.T + 1 + c.mt_cap * (c.NB1 + c.NB2) + c.nC + 64;
+    return c;
+}
+
+// Byte offsets of every workspace array, for a workspace sized for B = cap tokens.
+struct Layout {
+    size_t ctl, ev_logit, ev_exp, ev_h, logits, topk_idx, topk_w, tile_hist, tile_off, hist, indptr,
+        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, xg, h, y, qslots, total;
+    int64_t cap;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline Layout make_layout(const Shape &s, int64_t cap) {
+    Counts c = make_counts(s, cap);
+    Layout L;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t r = o;
+        o = align_up(o + bytes, 256);
+        return r;
+    };
+    const int64_t A = cap * s.k;
+    L.cap = cap;
+    L.ctl = take(CTL_WORDS * 4);
+    L.ev_logit = take((size_t)c.T * 4);
+    L.ev_exp = take((size_t)s.E * 4);
+    L.ev_h = take((size_t)c.mt_cap * 4);
+    L.logits = take((size_t)cap * s.E * 4);
+    L.topk_idx = take((size_t)A * 4);
+    L.topk_w = take((size_t)A * 4);
+    L.tile_hist = take((size_t)c.T * s.E * 4);
+    L.tile_off = take((size_t)c.T * s.E * 4);
+    L.hist = take((size_t)s.E * 4);
+    L.indptr = take((size_t)(s.E + 1) * 4);
+    L.mt_base = take((size_t)(s.E + 1) * 4);
+    L.mt_expert = take((size_t)c.mt_cap * 4);
+    L.mt_row0 = take((size_t)c.mt_cap * 4);
+    L.mt_rows = take((size_t)c.mt_cap * 4);
+    L.perm = take((size_t)A * 4);
+    L.inv = take((size_t)A * 4);
+    L.xg = take((size_t)A * s.d * 2);
+    L.h = take((size_t)A * s.f * 2);
+    L.y = take((size_t)A * s.d * 4);
+    L.qslots = take((size_t)c.q_cap * 8);
+    L.total = o;
+    return L;
+}
+
+// Kernel arguments (passed by value).
+struct Params {
+    const uint16_t *x;
+    const float *Wr;
+    const float *bias;
+    const uint16_t *W1, *W3, *W2;
+    uint16_t *out;
+    int B, E, k, d, f;
+    int sched;       // 0 static, 1 dynamic
+    int debug;       // MOE_MK_DEBUG_* bits
+    int nR, nTG, nEB, T, nC, NB1, NB2;
+    int q_cap, mt_cap;
+    long long watchdog;  // real-time ticks (100 MHz)
+    int *ctl, *ev_logit, *ev_exp, *ev_h;
+    float *logits;
+    int *topk_idx;
+    float *topk_w;
+    int *tile_hist, *tile_off, *hist, *indptr, *mt_base, *mt_expert, *mt_row0, *mt_rows, *perm, *inv;
+    uint16_t *xg, *h;
+    float *y;
+    unsigned long long *qslots;
+};
+
+}  // namespace mk

@@ -1,0 +1,111 @@
+// mk_device.h -- gfx950 device primitives for the MoE megakernel: agent-scope event
+// counters, wave64 exchanges, bf16 helpers and the bf16 MFMA wrapper.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_common.h"
+
+namespace mk {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Round to nearest even (finite values; NaN keeps a NaN pattern).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------- atomics
+// Event counters live in device memory shared by all XCDs, so every access is at agent
+// scope.  A notify is an atomic decrement with release ordering; a wait polls with
+// relaxed loads and finishes with an acquire fence.
+
+__device__ __forceinline__ int ld_relaxed(const int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(int *p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release(int *p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_relaxed(int *p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_acq_rel(int *p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+__device__ __forceinline__ unsigned long long ld_relaxed64(const unsigned long long *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed64(unsigned long long *p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void set_error(int *ctl, int bits) {
+    __hip_atomic_fetch_or(ctl + CTL_ERR, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Spin (one thread) until *p == target.  Returns false when the error word is set or the
+// watchdog expires (which also sets the error word), so callers never hang.
+__device__ __forceinline__ bool spin_until(const int *p, int target, int *ctl, long long watchdog) {
+    if (ld_relaxed(p) == target) return true;
+    const unsigned long long t0 = now_ticks();
+    for (unsigned it = 1;; ++it) {
+        __builtin_amdgcn_s_sleep(1);
+        if (ld_relaxed(p) == target) return true;
+        if ((it & 31u) == 0) {
+            if (ld_relaxed(ctl + CTL_ERR) != 0) return false;
+            if ((long long)(now_ticks() - t0) > watchdog) {
+                set_error(ctl, 1 /* MOE_MK_ERR_WATCHDOG */);
+                return false;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------- wave64
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
+        unsigned olo = (unsigned)__shfl_xor((int)lo, m, 64);
+        unsigned ohi = (unsigned)__shfl_xor((int)hi, m, 64);
+        unsigned long long o = ((unsigned long long)ohi << 32) | olo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Order-preserving map of a float (with -0 folded onto +0 beforehand) to uint32.
+__device__ __forceinline__ uint32_t float_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+}  // namespace mk

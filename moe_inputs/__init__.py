@@ -158,3 +158,33 @@ def small_case(B: int, d: int, f: int, E: int, k: int, seed: int, zipf_s: float 
     bias = make_bias(cfg)
     W1, W3, W2 = all_expert_weights(cfg)
     return cfg, x, Wr, bias, W1, W3, W2
+
+
+# ----------------------------------------------------------------------------- device copies (torch)
+
+def to_torch_bf16(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def device_weights(cfg: Config, device="cuda"):
+    """Wr, bias and the expert weights of ``cfg`` as device tensors (generated expert by expert)."""
+    import torch
+    Wr = torch.from_numpy(make_wr(cfg)).to(device)
+    b = make_bias(cfg)
+    bias = None if b is None else torch.from_numpy(b).to(device)
+    W1 = torch.empty((cfg.E, cfg.d, cfg.f), dtype=torch.bfloat16, device=device)
+    W3 = torch.empty_like(W1)
+    W2 = torch.empty((cfg.E, cfg.f, cfg.d), dtype=torch.bfloat16, device=device)
+
+    def put(e, a1, a3, a2):
+        W1[e].copy_(to_torch_bf16(a1))
+        W3[e].copy_(to_torch_bf16(a3))
+        W2[e].copy_(to_torch_bf16(a2))
+
+    for_each_expert(cfg, put)
+    return Wr, bias, W1, W3, W2
+
+
+def device_x(cfg: Config, rows: int | None = None, device="cuda"):
+    return to_torch_bf16(make_x(cfg, rows)).to(device)

@@ -1,0 +1,80 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every function the header
+declares, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+import torch
+
+import moe_groupgemm_amd as mk
+
+LIB = mk.LIB_PATH
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail("libmoe_mk.so is not built (run __graft_entry__.build())")
+    return mk.lib()
+
+
+def test_header_declares_the_boundary():
+    names = mk.header_functions()
+    for n in ("moe_mk_plan", "moe_mk_forward", "moe_mk_workspace_bytes", "moe_mk_workspace_init",
+              "moe_mk_routing_view", "moe_mk_plan_destroy", "moe_mk_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_header_function(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in mk.header_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_library_is_built_for_gfx950_only(tmp_path):
+    fb = tmp_path / "fatbin.bin"
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", LIB, str(fb)], check=True)
+    out = subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--list", "--type=o", f"--input={fb}"],
+                         capture_output=True, text=True, check=True)
+    targets = [t for t in out.stdout.split() if "amdgcn" in t]
+    assert targets and all(t.endswith("gfx950") for t in targets)
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert mk.moe_mk_status_str(code)
+    assert mk.moe_mk_status_str(0) == "ok"
+
+
+def test_null_and_bad_arguments_are_rejected(L):
+    assert L.moe_mk_workspace_bytes(None, 4) == 0
+    assert L.moe_mk_forward(None, None, None, None, None, None, None, None, 4, None, 0, None) == -1
+    assert L.moe_mk_plan(None, 8, 2, 256, 512, 0) == -1
+    p = ctypes.c_void_p()
+    assert L.moe_mk_plan(ctypes.byref(p), 8, 2, 256, 512, 7) == -1           # bad schedule
+    assert L.moe_mk_plan(ctypes.byref(p), 0, 1, 256, 512, 0) == -2           # E = 0
+    assert L.moe_mk_plan(ctypes.byref(p), 300, 2, 256, 512, 0) == -2         # E > 256
+    assert L.moe_mk_plan(ctypes.byref(p), 8, 9, 256, 512, 0) == -2           # k > E
+    assert L.moe_mk_plan(ctypes.byref(p), 32, 17, 256, 512, 0) == -2         # k > 16
+    assert L.moe_mk_plan(ctypes.byref(p), 8, 2, 200, 512, 0) == -2           # d not a multiple of 128
+    assert L.moe_mk_plan(ctypes.byref(p), 8, 2, 256, 100, 0) == -2           # f not a multiple of 128
+    assert L.moe_mk_plan_info(None, b"E") == -1
+    assert L.moe_mk_plan_set_debug(None, 0, 0) == -1
+    L.moe_mk_plan_destroy(None)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_plan_without_a_gpu_fails_cleanly(L):
+    p = ctypes.c_void_p()
+    rc = L.moe_mk_plan(ctypes.byref(p), 8, 2, 256, 512, 0)
+    assert rc in (-2, -4) and not p.value
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mk, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(mk, "_lib", None)
+    with pytest.raises(RuntimeError):
+        mk.lib()
