@@ -1,0 +1,169 @@
+"""Benchmark of the MoE-layer megakernel on one MI355X.
+
+A step is one forward of the whole layer (router, top-k, histogram/scan, grouping, both
+GroupGEMMs, combine) over one batch of synthetic inputs already resident in HBM.  The
+default workload is the Mixtral-shaped decode layer (B=32, d=4096, f=14336, E=8, k=2).
+Prints one JSON line with tokens/s, the roofline of the kernel (HBM bytes or MFMA flops
+of the activated experts per launch over the measured launch time) and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_decode")
+    ap.add_argument("--batch", type=int, default=0, help="batch size (default: the configuration's first)")
+    ap.add_argument("--sched", default="static", choices=["static", "dynamic"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens of the oracle sample (default: auto)")
+    ap.add_argument("--copy-kernel", action="store_true",
+                    help="after timing, run one 1 GiB device copy (reference for the HBM byte counters)")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, B, hist, with_bias):
+    """Bytes the layer must move and GroupGEMM flops, from the actual routing."""
+    active = int((hist > 0).sum())
+    weights = 6 * cfg.d * cfg.f * active            # W1, W3, W2 bf16 of every activated expert
+    other = 4 * cfg.d * cfg.E + 4 * B * cfg.d + (4 * cfg.E if with_bias else 0)  # Wr fp32, x and out bf16
+    flops = 6 * B * cfg.k * cfg.d * cfg.f
+    return weights + other, flops, active
+
+
+def cpu_baseline(cfg, x, Wr, bias, weights, sample, min_seconds=10.0, max_reps=20):
+    """The oracle as it stands, on a bounded sample of the same workload (repeated to ~10 s)."""
+    import oracle
+
+    cores = oracle.num_threads()
+    B = x.shape[0]
+    n = min(B, sample)
+    toks = list(range(n))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        r = oracle.routing(x[:n], Wr, bias, cfg.k)
+        oracle.moe_tokens(x, toks, r["topk_idx"], r["topk_w"], weights, cfg.d, cfg.f)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
+    return {"value": reps * n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {B} tokens of the same workload (router, top-k, grouping, fp64 SwiGLU experts, "
+                      f"combine) x {reps} repetitions = {dt:.1f} s on {cores} OpenMP threads"}
+
+
+def copy_calibration(nbytes=1 << 30):
+    """One plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    return nbytes
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer runs on one "
+              f"MI355X, with no sharding across GPUs)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import moe_groupgemm_amd as mk
+    from moe_inputs import CONFIGS, all_expert_weights, make_bias, make_wr, make_x, to_torch_bf16
+
+    cfg = CONFIGS[args.config]
+    B = args.batch or cfg.B
+    sched = mk.MOE_MK_SCHED_STATIC if args.sched == "static" else mk.MOE_MK_SCHED_DYNAMIC
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    Wr, bias = make_wr(cfg), make_bias(cfg)
+    W1, W3, W2 = all_expert_weights(cfg)
+    tWr = torch.from_numpy(Wr).to(dev)
+    tb = None if bias is None else torch.from_numpy(bias).to(dev)
+    t1, t3, t2 = (to_torch_bf16(a).to(dev) for a in (W1, W3, W2))
+    x = make_x(cfg, B)
+    tx = to_torch_bf16(x).to(dev)
+    layer = mk.MoELayer(cfg.E, cfg.k, cfg.d, cfg.f, tWr, t1, t3, t2, router_bias=tb, sched=sched,
+                        max_batch=B, device=dev)
+    out = torch.empty((B, cfg.d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    print(f"# warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        layer(tx, out)
+    torch.cuda.synchronize()
+    if layer.error():
+        raise RuntimeError(f"device error word {layer.error()}")
+    hist = layer.routing(B)["hist"].cpu().numpy()
+    alg_bytes, flops, active = algorithmic(cfg, B, hist, tb is not None)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        layer(tx, out)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if layer.error():
+        raise RuntimeError(f"device error word {layer.error()}")
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_ms = float(np.mean(per_launch_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = B / (ms_per_step / 1e3)
+    gbs = alg_bytes / (kern_ms / 1e3) / 1e9
+    tflops = flops / (kern_ms / 1e3) / 1e12
+    prefill = B >= 2048
+    if prefill:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+    line = {
+        "metric": "MoE-layer tokens/s + achieved HBM TB/s (B<=64) / MFMA TFLOP/s (B>=2048) vs peak",
+        "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.note, "B": B, "d": cfg.d, "f": cfg.f, "E": cfg.E, "k": cfg.k,
+                   "sched": args.sched, "active_experts": active},
+        "roofline": roof,
+        "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(per_launch_ms)),
+        "hbm_tbs": gbs / 1e3, "hbm_frac": gbs / PEAK_HBM_GBS,
+        "mfma_tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "algorithmic_bytes": alg_bytes, "gemm_flops": flops,
+        "grid": mk.moe_mk_plan_info(layer.plan, "grid"),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        sample = args.cpu_sample or max(1, min(B, int(2.0e10 / (6 * cfg.k * cfg.d * cfg.f))))
+        line["cpu_baseline"] = cpu_baseline(cfg, x, Wr, bias, (W1, W3, W2), sample)
+    if args.copy_kernel:
+        line["copy_kernel_bytes"] = copy_calibration()
+    layer.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

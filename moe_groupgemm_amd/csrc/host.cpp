@@ -1,6 +1,7 @@
 // host.cpp -- the C ABI of include/moe_mk.h: plans, workspace layout, argument checks and
-// the single kernel launch per forward.
+// the single kernel launch per forward.  Host code only (the device pass sees nothing).
 #include <hip/hip_runtime.h>
+#if !defined(__HIP_DEVICE_COMPILE__)
 
 #include <cstdint>
 #include <cstdlib>
@@ -189,6 +190,7 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.h = (uint16_t *)(base + L.h);
     P.y = (float *)(base + L.y);
     P.qslots = (unsigned long long *)(base + L.qslots);
+    P.trace = (long long *)(base + L.trace);
     if (hipSetDevice(plan->device) != hipSuccess) return MOE_MK_EHIP;
     if (mk_launch(P, plan->grid, (hipStream_t)stream) != hipSuccess) return MOE_MK_EHIP;
     return MOE_MK_OK;
@@ -258,3 +260,5 @@ moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks
 }
 
 }  // extern "C"
+
+#endif  // !__HIP_DEVICE_COMPILE__

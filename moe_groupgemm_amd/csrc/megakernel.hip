@@ -59,13 +59,17 @@ struct Smem {
     int epoch;
 };
 
+// The workgroup's LDS, shared by every task kind (file scope, so out-of-line task bodies
+// still address it as LDS).
+__shared__ Smem g_sm;
+
 // Phase bases of the global task index g.
 struct Bases {
     int K, S, G, M1, M2, C, total;
     bool known;  // M2/C/total are known once the scan has run
 };
 
-__device__ __forceinline__ Bases initial_bases(const Params &P) {
+__device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
     Bases b;
     b.K = P.nR;
     b.S = b.K + P.T;
@@ -76,7 +80,7 @@ __device__ __forceinline__ Bases initial_bases(const Params &P) {
     return b;
 }
 
-__device__ __forceinline__ void complete_bases(const Params &P, Bases &b, int mt_total) {
+__device__ __forceinline__ void complete_bases(const MK_C Params &P, Bases &b, int mt_total) {
     b.M2 = b.M1 + mt_total * P.NB1;
     b.C = b.M2 + mt_total * P.NB2;
     b.total = b.C + P.nC;
@@ -85,53 +89,59 @@ __device__ __forceinline__ void complete_bases(const Params &P, Bases &b, int mt
 
 // ------------------------------------------------------------------------------ event helpers (workgroup level)
 
-// Thread 0 waits for *ctr == 0; everyone then acquires.  Returns false on error/watchdog.
-__device__ bool wg_wait_zero(const Params &P, Smem &sm, const int *ctr) {
+// Thread 0 waits for *ctr == 0 and acquires (the acquire also invalidates this CU's
+// vector L1, which every wave of the group reads through); the barrier then releases the
+// group.  Returns false on error/watchdog.
+__device__ __forceinline__ bool wg_wait_zero(const MK_C Params &P, const MK_G int *ctr) {
     if (threadIdx.x == 0) {
-        bool ok = spin_until(ctr, 0, P.ctl, P.watchdog);
+        const bool ok = spin_until(ctr, 0, P.ctl, P.watchdog);
         fence_acquire();
-        sm.bcast[0] = ok ? 1 : 0;
+        g_sm.bcast[0] = ok ? 1 : 0;
     }
     __syncthreads();
-    const bool ok = sm.bcast[0] != 0;
-    fence_acquire();
+    const bool ok = g_sm.bcast[0] != 0;
     __syncthreads();
     return ok;
 }
 
-// Make every thread's global writes visible at agent scope, then synchronise the group.
-__device__ __forceinline__ void wg_release() {
-    fence_release();
+// Every wave waits for its own global stores to complete, then the group synchronises;
+// after this, one agent-scope release by a single thread publishes all of them.
+__device__ __forceinline__ void wg_stores_done() {
+    wave_drain_vm();
     __syncthreads();
 }
 
-// Push the contiguous task range [g0, g0 + cnt) onto the dynamic queue (all threads call).
-__device__ void wg_push_range(const Params &P, Smem &sm, int g0, int cnt) {
+// Push the contiguous task range [g0, g0 + cnt) onto the dynamic queue (all threads call,
+// after wg_stores_done() or another point where the data the tasks read is complete).
+__device__ __forceinline__ void wg_push_range(const MK_C Params &P, int g0, int cnt) {
     if (cnt <= 0) return;
-    if (threadIdx.x == 0) sm.bcast[1] = add_relaxed(P.ctl + CTL_QTAIL, cnt);
+    if (threadIdx.x == 0) {
+        fence_release();
+        g_sm.bcast[1] = add_relaxed(P.ctl + CTL_QTAIL, cnt);
+    }
     __syncthreads();
-    const int s0 = sm.bcast[1];
+    const int s0 = g_sm.bcast[1];
     __syncthreads();
     if (s0 + cnt > P.q_cap) {
         if (threadIdx.x == 0) set_error(P.ctl, 4 /* MOE_MK_ERR_QUEUE */);
         return;
     }
-    fence_release();
-    const unsigned long long tag = (unsigned long long)(uint32_t)sm.epoch << 32;
+    const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
     for (int i = threadIdx.x; i < cnt; i += kThreads)
         st_relaxed64(P.qslots + s0 + i, tag | (uint32_t)(g0 + i));
 }
 
-// Notify one counter from thread 0 after a group release; returns (broadcast) whether
-// this notification fired the event.  delta is added (negative = decrement).
-__device__ bool wg_notify(const Params &P, Smem &sm, int *ctr, int delta) {
-    wg_release();
+// Notify one counter: the group's stores complete, thread 0 adds delta (negative =
+// decrement) with acquire-release ordering.  Returns (to every thread) whether this
+// notification brought the counter to zero, i.e. fired the event.
+__device__ __forceinline__ bool wg_notify(const MK_C Params &P, MK_G int *ctr, int delta) {
+    wg_stores_done();
     if (threadIdx.x == 0) {
         const int old = add_acq_rel(ctr, delta);
-        sm.bcast[2] = (old + delta == 0) ? 1 : 0;
+        g_sm.bcast[2] = (old + delta == 0) ? 1 : 0;
     }
     __syncthreads();
-    const bool fired = sm.bcast[2] != 0;
+    const bool fired = g_sm.bcast[2] != 0;
     __syncthreads();
     return fired;
 }
@@ -157,7 +167,7 @@ __device__ __forceinline__ void reduce_scatter(float (&v)[64], int lane) {
     }
 }
 
-__device__ void task_route(const Params &P, int tg, int eb) {
+__device__ __attribute__((noinline)) void task_route(const MK_C Params &P, int tg, int eb) {
     const int lane = lane_id(), w = wave_id();
     const int b0 = tg * kRouteTokens + w * 4;
     const int e0 = eb * kRouteExperts;
@@ -168,7 +178,7 @@ __device__ void task_route(const Params &P, int tg, int eb) {
         for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
 
     bool tv[4];
-    const uint16_t *xp[4];
+    const MK_G uint16_t *xp[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         tv[t] = (b0 + t) < P.B;
@@ -178,9 +188,10 @@ __device__ void task_route(const Params &P, int tg, int eb) {
     bool ev[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) ev[q] = (e0 + 4 * q) < P.E;
-    const float *wp = P.Wr + (size_t)lane * P.E + e0;
+    const MK_G float *wp = P.Wr + (size_t)lane * P.E + e0;
     const size_t wstep = (size_t)64 * P.E;
     const int nst = P.d / 64;
+#pragma unroll 4
     for (int s = 0; s < nst; ++s) {
         float xv[4];
 #pragma unroll
@@ -190,7 +201,7 @@ __device__ void task_route(const Params &P, int tg, int eb) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (ev[q]) v = *(const f32x4 *)(wp + 4 * q);
+                if (ev[q]) v = *(const MK_G f32x4 *)(wp + 4 * q);
                 wr[4 * q + 0] = v[0];
                 wr[4 * q + 1] = v[1];
                 wr[4 * q + 2] = v[2];
@@ -226,15 +237,15 @@ __device__ void task_route(const Params &P, int tg, int eb) {
 // For each token: the k largest logits (ties to the lower expert index; -0 equals +0),
 // then softmax over them in fp32.  Keys are (order-preserving logit bits, ~expert) so a
 // wave-wide max picks the largest logit and, among equals, the smallest expert.
-__device__ void task_topk(const Params &P, int t, Smem &sm) {
-    int *sh = sm.u.t.hist;
+__device__ __attribute__((noinline)) void task_topk(const MK_C Params &P, int t) {
+    int *sh = g_sm.u.t.hist;
     for (int i = threadIdx.x; i < P.E; i += kThreads) sh[i] = 0;
     __syncthreads();
     const int lane = lane_id(), w = wave_id();
     for (int q = w; q < kTileTokens; q += 4) {
         const int b = t * kTileTokens + q;
         if (b >= P.B) break;
-        const float *lg = P.logits + (size_t)b * P.E;
+        const MK_G float *lg = P.logits + (size_t)b * P.E;
         unsigned long long key[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -296,7 +307,7 @@ __device__ void task_topk(const Params &P, int t, Smem &sm) {
 }
 
 // ------------------------------------------------------------------------------ SCAN
-__device__ int block_excl_scan(int v, int *part, int *total) {
+__device__ __forceinline__ int block_excl_scan(int v, int *part, int *total) {
     const int lane = lane_id(), w = wave_id();
     int x = v;
 #pragma unroll
@@ -322,7 +333,7 @@ __device__ int block_excl_scan(int v, int *part, int *total) {
 // ev_exp[e] with hist[e], ev_h[mt] with the gate/up tiles of each row tile, and ev_y with
 // the number of down-projection tiles ("Core method": the prefix sum decides how many
 // GroupGEMM tiles each expert triggers).  Returns the number of row tiles.
-__device__ int task_scan(const Params &P, Smem &sm) {
+__device__ __attribute__((noinline)) int task_scan(const MK_C Params &P) {
     const int e = threadIdx.x;
     const int E = P.E;
     int h = 0;
@@ -330,8 +341,8 @@ __device__ int task_scan(const Params &P, Smem &sm) {
         for (int t = 0; t < P.T; ++t) h += P.tile_hist[(size_t)t * E + e];
     const int mt = (h + kBM - 1) / kBM;
     int total_h, total_mt;
-    const int off = block_excl_scan(h, sm.u.s.part, &total_h);
-    const int mbase = block_excl_scan(mt, sm.u.s.part, &total_mt);
+    const int off = block_excl_scan(h, g_sm.u.s.part, &total_h);
+    const int mbase = block_excl_scan(mt, g_sm.u.s.part, &total_mt);
     if (e < E) {
         P.hist[e] = h;
         P.indptr[e] = off;
@@ -364,8 +375,8 @@ __device__ int task_scan(const Params &P, Smem &sm) {
 // is the number of earlier tokens of the tile routed to e (a token uses an expert at most
 // once), read off a 64-bit token mask per expert.  Row p = tile_off[t,e] + rank;
 // perm[p] = b*k+i, inv[b*k+i] = p, and the token's row of x is copied to xg[p].
-__device__ void task_group(const Params &P, int t, Smem &sm) {
-    GroupSmem &g = sm.u.gr;
+__device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t) {
+    GroupSmem &g = g_sm.u.gr;
     const int E = P.E, k = P.k;
     for (int i = threadIdx.x; i < E; i += kThreads) g.mask[i] = 0ull;
     __syncthreads();
@@ -392,8 +403,8 @@ __device__ void task_group(const Params &P, int t, Smem &sm) {
     for (int idx = threadIdx.x; idx < total; idx += kThreads) {
         const int q = idx / cpr, c = idx - q * cpr;
         const int tok = t * kTileTokens + q / k;
-        const u32x4 v = *((const u32x4 *)(P.x + (size_t)tok * P.d) + c);
-        *((u32x4 *)(P.xg + (size_t)g.rowmap[q] * P.d) + c) = v;
+        const u32x4 v = *((const MK_G u32x4 *)(P.x + (size_t)tok * P.d) + c);
+        *((MK_G u32x4 *)(P.xg + (size_t)g.rowmap[q] * P.d) + c) = v;
     }
 }
 
@@ -417,9 +428,9 @@ struct GemmRegs {
 };
 
 struct GemmArgs {
-    const uint16_t *A;
+    const MK_G uint16_t *A;
     int lda, nrows;
-    const uint16_t *B0, *B1;
+    const MK_G uint16_t *B0, *B1;
     int ldb, K;
 };
 
@@ -431,17 +442,17 @@ __device__ __forceinline__ void gemm_load(GemmRegs<DUAL> &R, const GemmArgs &g, 
     for (int hh = 0; hh < 2; ++hh) {
         const int r = ar + 32 * hh;
         u32x4 z = {0u, 0u, 0u, 0u};
-        if (r < g.nrows) z = *(const u32x4 *)(g.A + (size_t)r * g.lda + k0 + ac * 8);
+        if (r < g.nrows) z = *(const MK_G u32x4 *)(g.A + (size_t)r * g.lda + k0 + ac * 8);
         R.a[hh] = z;
     }
     const int kp = tid >> 3, c = tid & 7;
-    const uint16_t *p0 = g.B0 + (size_t)(k0 + 2 * kp) * g.ldb + c * 8;
-    R.b0[0] = *(const u32x4 *)p0;
-    R.b0[1] = *(const u32x4 *)(p0 + g.ldb);
+    const MK_G uint16_t *p0 = g.B0 + (size_t)(k0 + 2 * kp) * g.ldb + c * 8;
+    R.b0[0] = *(const MK_G u32x4 *)p0;
+    R.b0[1] = *(const MK_G u32x4 *)(p0 + g.ldb);
     if constexpr (DUAL) {
-        const uint16_t *p1 = g.B1 + (size_t)(k0 + 2 * kp) * g.ldb + c * 8;
-        R.b1[0] = *(const u32x4 *)p1;
-        R.b1[1] = *(const u32x4 *)(p1 + g.ldb);
+        const MK_G uint16_t *p1 = g.B1 + (size_t)(k0 + 2 * kp) * g.ldb + c * 8;
+        R.b1[0] = *(const MK_G u32x4 *)p1;
+        R.b1[1] = *(const MK_G u32x4 *)(p1 + g.ldb);
     }
 }
 
@@ -495,8 +506,10 @@ __device__ __forceinline__ void gemm_compute(const uint16_t *sA, const uint16_t 
     }
 }
 
-template <bool DUAL>
-__device__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], f32x4 (&acc1)[4], GemmSmem &s) {
+// PF register stages are in flight while LDS buffer (s & 1) holds stage s; stage s sits
+// in register set s % PF until it is written to LDS one step before its use.
+template <bool DUAL, int PF>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], f32x4 (&acc1)[4], GemmSmem &s) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
         acc0[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -504,36 +517,34 @@ __device__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], f32x4 (&acc1)[4]
     }
     const int nrb = (ga.nrows + 15) / 16;
     const int nk = ga.K / kBK;
-    GemmRegs<DUAL> R0, R1;
-    gemm_load<DUAL>(R0, ga, 0);
-    if (nk > 1) gemm_load<DUAL>(R1, ga, kBK);
-    gemm_store_lds<DUAL>(R0, s.A[0], s.B0[0], s.B1[0]);
-    if (nk > 2) gemm_load<DUAL>(R0, ga, 2 * kBK);
+    GemmRegs<DUAL> R[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (p < nk) gemm_load<DUAL>(R[p], ga, p * kBK);
+    gemm_store_lds<DUAL>(R[0], s.A[0], s.B0[0], s.B1[0]);
+    if (PF < nk) gemm_load<DUAL>(R[0], ga, PF * kBK);
     __syncthreads();
-    // Invariant at step kk: LDS buffer kk&1 holds stage kk; the register set for stage
-    // kk+1 is R1 when kk is even and R0 when kk is odd.
-    for (int kk = 0; kk < nk; kk += 2) {
-        {
-            gemm_compute<DUAL>(s.A[0], s.B0[0], s.B1[0], nrb, acc0, acc1);
-            if (kk + 1 < nk) {
-                gemm_store_lds<DUAL>(R1, s.A[1], s.B0[1], s.B1[1]);
-                if (kk + 3 < nk) gemm_load<DUAL>(R1, ga, (kk + 3) * kBK);
+    for (int kk = 0; kk < nk; kk += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int st = kk + u;
+            if (st < nk) {
+                const int buf = st & 1;
+                gemm_compute<DUAL>(s.A[buf], s.B0[buf], s.B1[buf], nrb, acc0, acc1);
+                if (st + 1 < nk) {
+                    gemm_store_lds<DUAL>(R[(u + 1) % PF], s.A[buf ^ 1], s.B0[buf ^ 1], s.B1[buf ^ 1]);
+                    if (st + 1 + PF < nk) gemm_load<DUAL>(R[(u + 1) % PF], ga, (st + 1 + PF) * kBK);
+                }
+                __syncthreads();
             }
-            __syncthreads();
-        }
-        if (kk + 1 < nk) {
-            gemm_compute<DUAL>(s.A[1], s.B0[1], s.B1[1], nrb, acc0, acc1);
-            if (kk + 2 < nk) {
-                gemm_store_lds<DUAL>(R0, s.A[0], s.B0[0], s.B1[0]);
-                if (kk + 4 < nk) gemm_load<DUAL>(R0, ga, (kk + 4) * kBK);
-            }
-            __syncthreads();
         }
     }
 }
 
+constexpr int kPF = 4;  // register prefetch depth of the GroupGEMM tiles
+
 // GEMM1 tile: h[rows, n0:n0+64] = bf16( silu(xg W1[e]) * (xg W3[e]) ) for one row tile.
-__device__ void task_gemm1(const Params &P, Smem &sm, int e, int row0, int nrows, int n) {
+__device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
     GemmArgs ga;
     ga.A = P.xg + (size_t)row0 * P.d;
     ga.lda = P.d;
@@ -543,7 +554,7 @@ __device__ void task_gemm1(const Params &P, Smem &sm, int e, int row0, int nrows
     ga.ldb = P.f;
     ga.K = P.d;
     f32x4 acc0[4], acc1[4];
-    gemm_tile<true>(ga, acc0, acc1, sm.u.g);
+    gemm_tile<true, kPF>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
     const int col = n * kBN + 16 * w + j;
@@ -562,7 +573,7 @@ __device__ void task_gemm1(const Params &P, Smem &sm, int e, int row0, int nrows
 }
 
 // GEMM2 tile: y[rows, n0:n0+64] = h[rows, :] W2[e][:, n0:n0+64] in fp32.
-__device__ void task_gemm2(const Params &P, Smem &sm, int e, int row0, int nrows, int n) {
+__device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n) {
     GemmArgs ga;
     ga.A = P.h + (size_t)row0 * P.f;
     ga.lda = P.f;
@@ -572,7 +583,7 @@ __device__ void task_gemm2(const Params &P, Smem &sm, int e, int row0, int nrows
     ga.ldb = P.d;
     ga.K = P.f;
     f32x4 acc0[4], acc1[4];
-    gemm_tile<false>(ga, acc0, acc1, sm.u.g);
+    gemm_tile<false, kPF>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
     const int col = n * kBN + 16 * w + j;
@@ -588,7 +599,7 @@ __device__ void task_gemm2(const Params &P, Smem &sm, int e, int row0, int nrows
 
 // ------------------------------------------------------------------------------ COMBINE
 // out[b, :] = bf16( sum_{i<k} w[b,i] * y[inv[b*k+i], :] ), slot order, fp32.
-__device__ void task_combine(const Params &P, int c) {
+__device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int c) {
     const int b_lo = c * kCombineTokens;
     const int b_hi = min(P.B, b_lo + kCombineTokens);
     const int nq = P.d / 4;
@@ -598,13 +609,13 @@ __device__ void task_combine(const Params &P, int c) {
             for (int i = 0; i < P.k; ++i) {
                 const int p = P.inv[(size_t)b * P.k + i];
                 const float wgt = P.topk_w[(size_t)b * P.k + i];
-                const f32x4 yv = *(const f32x4 *)(P.y + (size_t)p * P.d + 4 * q);
+                const f32x4 yv = *(const MK_G f32x4 *)(P.y + (size_t)p * P.d + 4 * q);
 #pragma unroll
                 for (int z = 0; z < 4; ++z) acc[z] = fmaf(wgt, yv[z], acc[z]);
             }
             const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
             const uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-            uint32_t *o = (uint32_t *)(P.out + (size_t)b * P.d + 4 * q);
+            MK_G uint32_t *o = (MK_G uint32_t *)(P.out + (size_t)b * P.d + 4 * q);
             o[0] = lo;
             o[1] = hi;
         }
@@ -612,18 +623,31 @@ __device__ void task_combine(const Params &P, int c) {
 }
 
 // ------------------------------------------------------------------------------ task dispatch
-__device__ __forceinline__ int route_tasks_of_tile(const Params &P, int t) {
+__device__ __forceinline__ int route_tasks_of_tile(const MK_C Params &P, int t) {
     const int g0 = t * (kTileTokens / kRouteTokens);
     const int g1 = min(g0 + kTileTokens / kRouteTokens, P.nTG);
     return (g1 - g0) * P.nEB;
 }
 
-__device__ __forceinline__ void count_task(const Params &P, int kind) {
+__device__ __forceinline__ void count_task(const MK_C Params &P, int kind) {
     if (threadIdx.x == 0) add_relaxed(P.ctl + CTL_DBG + kind, 1);
 }
 
-// Runs task g.  Returns false when the forward must be abandoned (error / watchdog).
-__device__ bool run_task(const Params &P, Smem &sm, int g, Bases &bs) {
+// Debug trace (MOE_MK_DEBUG_TRACE): per task {g | kind << 32 | workgroup << 40, obtained,
+// dependencies satisfied, finished} in real-time ticks.
+__device__ __forceinline__ void trace_task(const MK_C Params &P, int g, int kind, unsigned long long t0,
+                                           unsigned long long t1) {
+    if ((P.debug & 2) && threadIdx.x == 0) {
+        MK_G long long *e = P.trace + (size_t)g * 4;
+        e[0] = (long long)g | ((long long)kind << 32) | ((long long)blockIdx.x << 40);
+        e[1] = (long long)t0;
+        e[2] = (long long)t1;
+        e[3] = (long long)now_ticks();
+    }
+}
+
+// Runs task g (obtained at time t0).  Returns false when the forward must be abandoned.
+__device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs, unsigned long long t0) {
     const bool dyn = P.sched != 0;
     if (g < bs.K) {  // ---------------------------------------------------------- ROUTE
         const int tg = g / P.nEB, eb = g - tg * P.nEB;
@@ -632,47 +656,53 @@ __device__ bool run_task(const Params &P, Smem &sm, int g, Bases &bs) {
         const int t = tg / (kTileTokens / kRouteTokens);
         int delta = -1;
         if (dyn && (tg % (kTileTokens / kRouteTokens)) == 0 && eb == 0) delta += route_tasks_of_tile(P, t);
-        if (wg_notify(P, sm, P.ev_logit + t, delta) && dyn) wg_push_range(P, sm, bs.K + t, 1);
+        if (wg_notify(P, P.ev_logit + t, delta) && dyn) wg_push_range(P, bs.K + t, 1);
+        trace_task(P, g, K_ROUTE, t0, t0);
         return true;
     }
     if (g < bs.S) {  // ---------------------------------------------------------- TOPK
         const int t = g - bs.K;
         if (!dyn) {
             if (threadIdx.x == 0) add_relaxed(P.ev_logit + t, route_tasks_of_tile(P, t));  // arm
-            if (!wg_wait_zero(P, sm, P.ev_logit + t)) return false;
+            if (!wg_wait_zero(P, P.ev_logit + t)) return false;
         }
-        task_topk(P, t, sm);
+        const unsigned long long t1 = now_ticks();
+        task_topk(P, t);
         count_task(P, K_TOPK);
         int delta = -1;
         if (dyn && t == 0) delta += P.T;
-        if (wg_notify(P, sm, P.ctl + CTL_EV_TOPK, delta) && dyn) wg_push_range(P, sm, bs.S, 1);
+        if (wg_notify(P, P.ctl + CTL_EV_TOPK, delta) && dyn) wg_push_range(P, bs.S, 1);
+        trace_task(P, g, K_TOPK, t0, t1);
         return true;
     }
     if (g == bs.S) {  // --------------------------------------------------------- SCAN
         if (!dyn) {
             if (threadIdx.x == 0) add_relaxed(P.ctl + CTL_EV_TOPK, P.T);  // arm
-            if (!wg_wait_zero(P, sm, P.ctl + CTL_EV_TOPK)) return false;
+            if (!wg_wait_zero(P, P.ctl + CTL_EV_TOPK)) return false;
         }
-        const int mt_total = task_scan(P, sm);
+        const unsigned long long t1 = now_ticks();
+        const int mt_total = task_scan(P);
         count_task(P, K_SCAN);
         complete_bases(P, bs, mt_total);
-        wg_notify(P, sm, P.ctl + CTL_EV_SCAN, -1);
+        wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
         if (dyn) {
-            wg_push_range(P, sm, bs.G, P.T);
+            wg_push_range(P, bs.G, P.T);
             if (threadIdx.x == 0)
-                st_relaxed64((unsigned long long *)(P.ctl + CTL_TOTAL64),
-                             ((unsigned long long)(uint32_t)sm.epoch << 32) | (uint32_t)bs.total);
+                st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64),
+                             ((unsigned long long)(uint32_t)g_sm.epoch << 32) | (uint32_t)bs.total);
         }
+        trace_task(P, g, K_SCAN, t0, t1);
         return true;
     }
     if (g < bs.M1) {  // --------------------------------------------------------- GROUP
         const int t = g - bs.G;
-        if (!dyn && !wg_wait_zero(P, sm, P.ctl + CTL_EV_SCAN)) return false;
-        task_group(P, t, sm);
+        if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) return false;
+        const unsigned long long t1 = now_ticks();
+        task_group(P, t);
         count_task(P, K_GROUP);
-        GroupSmem &gr = sm.u.gr;
+        GroupSmem &gr = g_sm.u.gr;
         if (threadIdx.x == 0) gr.nfired = 0;
-        wg_release();
+        wg_stores_done();
         int skip = -1;
         if ((P.debug & 1) && t == 0) {  // debug: drop the notification of the tile's first expert
             for (int e = 0; e < P.E; ++e)
@@ -694,9 +724,10 @@ __device__ bool run_task(const Params &P, Smem &sm, int g, Bases &bs) {
             for (int i = 0; i < nf; ++i) {
                 const int e = gr.fired[i];
                 const int m0 = P.mt_base[e], m1 = P.mt_base[e + 1];
-                wg_push_range(P, sm, bs.M1 + m0 * P.NB1, (m1 - m0) * P.NB1);
+                wg_push_range(P, bs.M1 + m0 * P.NB1, (m1 - m0) * P.NB1);
             }
         }
+        trace_task(P, g, K_GROUP, t0, t1);
         return true;
     }
     if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
@@ -704,33 +735,39 @@ __device__ bool run_task(const Params &P, Smem &sm, int g, Bases &bs) {
         const int i = g - bs.M1;
         const int mt = i / P.NB1, n = i - mt * P.NB1;
         const int e = P.mt_expert[mt];
-        if (!dyn && !wg_wait_zero(P, sm, P.ev_exp + e)) return false;
-        task_gemm1(P, sm, e, P.mt_row0[mt], P.mt_rows[mt], n);
+        if (!dyn && !wg_wait_zero(P, P.ev_exp + e)) return false;
+        const unsigned long long t1 = now_ticks();
+        task_gemm1(P, e, P.mt_row0[mt], P.mt_rows[mt], n);
         count_task(P, K_GEMM1);
-        if (wg_notify(P, sm, P.ev_h + mt, -1) && dyn) wg_push_range(P, sm, bs.M2 + mt * P.NB2, P.NB2);
+        if (wg_notify(P, P.ev_h + mt, -1) && dyn) wg_push_range(P, bs.M2 + mt * P.NB2, P.NB2);
+        trace_task(P, g, K_GEMM1, t0, t1);
         return true;
     }
     if (g < bs.C) {  // ---------------------------------------------------------- GEMM2
         const int i = g - bs.M2;
         const int mt = i / P.NB2, n = i - mt * P.NB2;
-        if (!dyn && !wg_wait_zero(P, sm, P.ev_h + mt)) return false;
-        task_gemm2(P, sm, P.mt_expert[mt], P.mt_row0[mt], P.mt_rows[mt], n);
+        if (!dyn && !wg_wait_zero(P, P.ev_h + mt)) return false;
+        const unsigned long long t1 = now_ticks();
+        task_gemm2(P, P.mt_expert[mt], P.mt_row0[mt], P.mt_rows[mt], n);
         count_task(P, K_GEMM2);
-        if (wg_notify(P, sm, P.ctl + CTL_EV_Y, -1) && dyn) wg_push_range(P, sm, bs.C, P.nC);
+        if (wg_notify(P, P.ctl + CTL_EV_Y, -1) && dyn) wg_push_range(P, bs.C, P.nC);
+        trace_task(P, g, K_GEMM2, t0, t1);
         return true;
     }
     {  // ------------------------------------------------------------------------ COMBINE
         const int c = g - bs.C;
-        if (!dyn && !wg_wait_zero(P, sm, P.ctl + CTL_EV_Y)) return false;
+        if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_Y)) return false;
+        const unsigned long long t1 = now_ticks();
         task_combine(P, c);
         count_task(P, K_COMBINE);
         __syncthreads();
+        trace_task(P, g, K_COMBINE, t0, t1);
         return true;
     }
 }
 
 // Dynamic queue pop.  Returns a task index, -1 when the forward is complete, -2 on error.
-__device__ int wg_pop(const Params &P, Smem &sm) {
+__device__ __forceinline__ int wg_pop(const MK_C Params &P) {
     if (threadIdx.x == 0) {
         int g = -1;
         const int claim = add_relaxed(P.ctl + CTL_QHEAD, 1);
@@ -738,7 +775,7 @@ __device__ int wg_pop(const Params &P, Smem &sm) {
             g = claim;
         } else {
             const int slot = claim - P.nR;
-            const uint32_t ep = (uint32_t)sm.epoch;
+            const uint32_t ep = (uint32_t)g_sm.epoch;
             const unsigned long long t0 = now_ticks();
             for (unsigned it = 0;; ++it) {
                 if (slot < P.q_cap) {
@@ -748,7 +785,7 @@ __device__ int wg_pop(const Params &P, Smem &sm) {
                         break;
                     }
                 }
-                const unsigned long long tot = ld_relaxed64((const unsigned long long *)(P.ctl + CTL_TOTAL64));
+                const unsigned long long tot = ld_relaxed64((const MK_G unsigned long long *)(P.ctl + CTL_TOTAL64));
                 if ((uint32_t)(tot >> 32) == ep && claim >= (int)(uint32_t)tot) {
                     g = -1;
                     break;
@@ -768,23 +805,25 @@ __device__ int wg_pop(const Params &P, Smem &sm) {
             }
             fence_acquire();
         }
-        sm.bcast[3] = g;
+        g_sm.bcast[3] = g;
     }
     __syncthreads();
-    const int g = sm.bcast[3];
-    fence_acquire();
+    const int g = g_sm.bcast[3];
     __syncthreads();
     return g;
 }
 
-__global__ void __launch_bounds__(kThreads) moe_megakernel(Params P) {
-    __shared__ Smem sm;
+__global__ void __launch_bounds__(kThreads, 2) moe_megakernel(Params Parg) {
+    // Parg is the first kernel argument, at offset 0 of the kernel-argument segment: read it
+    // there in place rather than from a private copy.
+    (void)Parg;
+    const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
     if (threadIdx.x == 0) {
-        sm.epoch = ld_relaxed(P.ctl + CTL_EPOCH);
-        sm.bcast[0] = ld_relaxed(P.ctl + CTL_MAGIC) == kMagic;
+        g_sm.epoch = ld_relaxed(P.ctl + CTL_EPOCH);
+        g_sm.bcast[0] = ld_relaxed(P.ctl + CTL_MAGIC) == kMagic;
     }
     __syncthreads();
-    if (!sm.bcast[0]) {  // workspace never prepared: record it and touch nothing else
+    if (!g_sm.bcast[0]) {  // workspace never prepared: record it and touch nothing else
         if (threadIdx.x == 0) set_error(P.ctl, 8 /* MOE_MK_ERR_UNINIT */);
         return;
     }
@@ -792,17 +831,18 @@ __global__ void __launch_bounds__(kThreads) moe_megakernel(Params P) {
     if (P.sched == 0) {
         for (int g = blockIdx.x;; g += gridDim.x) {
             if (g >= bs.M1 && !bs.known) {
-                if (!wg_wait_zero(P, sm, P.ctl + CTL_EV_SCAN)) break;
+                if (!wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) break;
                 complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
             }
             if (bs.known && g >= bs.total) break;
-            if (!run_task(P, sm, g, bs)) break;
+            if (!run_task(P, g, bs, now_ticks())) break;
         }
     } else {
         for (;;) {
-            const int g = wg_pop(P, sm);
+            const unsigned long long t0 = now_ticks();
+            const int g = wg_pop(P);
             if (g < 0) break;
-            if (!run_task(P, sm, g, bs)) break;
+            if (!run_task(P, g, bs, t0)) break;
         }
     }
     // Leave: the last workgroup out puts the control block back to its rest state.
@@ -817,17 +857,20 @@ __global__ void __launch_bounds__(kThreads) moe_megakernel(Params P) {
                 st_relaxed(P.ctl + CTL_EV_SCAN, 1);
             }
             st_relaxed(P.ctl + CTL_EXIT, 0);
-            st_release(P.ctl + CTL_EPOCH, sm.epoch + 1);
+            st_release(P.ctl + CTL_EPOCH, g_sm.epoch + 1);
         }
     }
 }
 
 // Workspace preparation: zero everything, then set the rest values.
-__global__ void moe_ws_init(uint32_t *ws, size_t words) {
+// (Kernel signatures use plain pointers: the host pass must mangle them identically.)
+__global__ void moe_ws_init(uint32_t *ws_generic, size_t words) {
+    MK_G uint32_t *ws = (MK_G uint32_t *)ws_generic;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride) ws[i] = 0u;
 }
-__global__ void moe_ws_init_ctl(int *ctl) {
+__global__ void moe_ws_init_ctl(int *ctl_generic) {
+    MK_G int *ctl = (MK_G int *)ctl_generic;
     if (threadIdx.x == 0) {
         ctl[CTL_EPOCH] = 1;
         ctl[CTL_EV_SCAN] = 1;

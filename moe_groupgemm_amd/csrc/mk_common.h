@@ -5,6 +5,17 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Global (device) memory pointers: in device code they carry address space 1 so every
+// access compiles to global_* instructions (flat accesses would also count against the
+// LDS wait counter and stall the software pipeline).  Host code sees plain pointers.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define MK_G __attribute__((address_space(1)))
+#define MK_C __attribute__((address_space(4)))  // constant (kernel-argument) memory
+#else
+#define MK_G
+#define MK_C
+#endif
+
 namespace mk {
 
 constexpr int kThreads = 256;        // 4 waves of 64 lanes per persistent workgroup
@@ -75,7 +86,7 @@ inline Counts make_counts(const Shape &s, int64_t B) {
 // Byte offsets of every workspace array, for a workspace sized for B = cap tokens.
 struct Layout {
     size_t ctl, ev_logit, ev_exp, ev_h, logits, topk_idx, topk_w, tile_hist, tile_off, hist, indptr,
-        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, xg, h, y, qslots, total;
+        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, xg, h, y, qslots, trace, total;
     int64_t cap;
 };
 
@@ -113,31 +124,33 @@ inline Layout make_layout(const Shape &s, int64_t cap) {
     L.h = take((size_t)A * s.f * 2);
     L.y = take((size_t)A * s.d * 4);
     L.qslots = take((size_t)c.q_cap * 8);
+    L.trace = take((size_t)(c.q_cap + c.nR) * 4 * 8);
     L.total = o;
     return L;
 }
 
 // Kernel arguments (passed by value).
 struct Params {
-    const uint16_t *x;
-    const float *Wr;
-    const float *bias;
-    const uint16_t *W1, *W3, *W2;
-    uint16_t *out;
+    const MK_G uint16_t *x;
+    const MK_G float *Wr;
+    const MK_G float *bias;
+    const MK_G uint16_t *W1, *W3, *W2;
+    MK_G uint16_t *out;
     int B, E, k, d, f;
     int sched;       // 0 static, 1 dynamic
     int debug;       // MOE_MK_DEBUG_* bits
     int nR, nTG, nEB, T, nC, NB1, NB2;
     int q_cap, mt_cap;
     long long watchdog;  // real-time ticks (100 MHz)
-    int *ctl, *ev_logit, *ev_exp, *ev_h;
-    float *logits;
-    int *topk_idx;
-    float *topk_w;
-    int *tile_hist, *tile_off, *hist, *indptr, *mt_base, *mt_expert, *mt_row0, *mt_rows, *perm, *inv;
-    uint16_t *xg, *h;
-    float *y;
-    unsigned long long *qslots;
+    MK_G int *ctl, *ev_logit, *ev_exp, *ev_h;
+    MK_G float *logits;
+    MK_G int *topk_idx;
+    MK_G float *topk_w;
+    MK_G int *tile_hist, *tile_off, *hist, *indptr, *mt_base, *mt_expert, *mt_row0, *mt_rows, *perm, *inv;
+    MK_G uint16_t *xg, *h;
+    MK_G float *y;
+    MK_G unsigned long long *qslots;
+    MK_G long long *trace;  // 4 int64 per task when tracing is on
 };
 
 }  // namespace mk

@@ -29,35 +29,38 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 
 // ---------------------------------------------------------------------------- atomics
 // Event counters live in device memory shared by all XCDs, so every access is at agent
-// scope.  A notify is an atomic decrement with release ordering; a wait polls with
-// relaxed loads and finishes with an acquire fence.
+// scope.  A notify is an atomic add with release ordering (a decrement); a wait polls
+// with relaxed loads and finishes with an acquire fence.
 
-__device__ __forceinline__ int ld_relaxed(const int *p) {
+__device__ __forceinline__ int ld_relaxed(const MK_G int *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_relaxed(int *p, int v) {
+__device__ __forceinline__ void st_relaxed(MK_G int *p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_release(int *p, int v) {
+__device__ __forceinline__ void st_release(MK_G int *p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int add_relaxed(int *p, int v) {
+__device__ __forceinline__ int add_relaxed(MK_G int *p, int v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int add_acq_rel(int *p, int v) {
+__device__ __forceinline__ int add_acq_rel(MK_G int *p, int v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 __device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
-__device__ __forceinline__ unsigned long long ld_relaxed64(const unsigned long long *p) {
+// Wait until this wave's outstanding global stores (and loads) have completed.
+__device__ __forceinline__ void wave_drain_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); /* vmcnt(0) */ }
+
+__device__ __forceinline__ unsigned long long ld_relaxed64(const MK_G unsigned long long *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_relaxed64(unsigned long long *p, unsigned long long v) {
+__device__ __forceinline__ void st_relaxed64(MK_G unsigned long long *p, unsigned long long v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void set_error(int *ctl, int bits) {
+__device__ __forceinline__ void set_error(MK_G int *ctl, int bits) {
     __hip_atomic_fetch_or(ctl + CTL_ERR, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -65,7 +68,7 @@ __device__ __forceinline__ unsigned long long now_ticks() { return __builtin_amd
 
 // Spin (one thread) until *p == target.  Returns false when the error word is set or the
 // watchdog expires (which also sets the error word), so callers never hang.
-__device__ __forceinline__ bool spin_until(const int *p, int target, int *ctl, long long watchdog) {
+__device__ __forceinline__ bool spin_until(const MK_G int *p, int target, MK_G int *ctl, long long watchdog) {
     if (ld_relaxed(p) == target) return true;
     const unsigned long long t0 = now_ticks();
     for (unsigned it = 1;; ++it) {

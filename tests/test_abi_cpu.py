@@ -78,3 +78,27 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mk, "_lib", None)
     with pytest.raises(RuntimeError):
         mk.lib()
+
+
+def test_every_kernel_launched_by_the_host_exists_in_the_device_code(tmp_path):
+    # A kernel whose host-side and device-side signatures mangle differently would be
+    # launched under a name the code object does not contain.
+    fb, co = tmp_path / "fatbin.bin", tmp_path / "dev.co"
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", LIB, str(fb)], check=True)
+    subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--unbundle", "--type=o", f"--input={fb}",
+                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"], check=True)
+    syms = subprocess.run(["/opt/rocm/llvm/bin/llvm-readelf", "--syms", str(co)], capture_output=True, text=True,
+                          check=True).stdout
+    device = {line.split()[-1] for line in syms.splitlines() if " FUNC " in line}
+    host = subprocess.run(["nm", LIB], capture_output=True, text=True, check=True).stdout
+    stubs = [line.split()[-1] for line in host.splitlines() if "__device_stub__" in line]
+    assert stubs
+    for stub in stubs:
+        # _ZN2mk<len>__device_stub__<name>... -> _ZN2mk<len'><name>...
+        import re
+        m = re.match(r"(_ZN\d+\w+?)(\d+)__device_stub__(\w+)", stub)
+        assert m, stub
+        prefix, n, rest = m.group(1), int(m.group(2)), m.group(3)
+        name_len = n - len("__device_stub__")
+        kernel = f"{prefix}{name_len}{rest}"
+        assert kernel in device, f"{kernel} (host stub {stub}) missing from the device code object"
