@@ -30,6 +30,8 @@ def parse():
     ap.add_argument("--sched", default="static", choices=["static", "dynamic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens of the oracle sample (default: auto)")
+    ap.add_argument("--trace", action="store_true", help="after timing, run one traced forward and print "
+                    "per-task-kind timings to stderr")
     ap.add_argument("--copy-kernel", action="store_true",
                     help="after timing, run one 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -75,6 +77,45 @@ def copy_calibration(nbytes=1 << 30):
     b.copy_(a)
     torch.cuda.synchronize()
     return nbytes
+
+
+def trace_report(layer, x, out, B):
+    """One forward with per-task timestamps; per-kind summary on stderr (microseconds)."""
+    import numpy as np
+    import torch
+
+    import moe_groupgemm_amd as mk
+
+    mk.moe_mk_plan_set_debug(layer.plan, 0, mk.MOE_MK_DEBUG_TRACE)
+    layer(x, out)
+    torch.cuda.synchronize()
+    mk.moe_mk_plan_set_debug(layer.plan, 0, 0)
+    ctl = layer.routing(B)["ctl"].cpu().numpy()
+    tr = mk.moe_mk_trace_view(layer.plan, B, layer.ws).cpu().numpy()
+    E, k, d, f = layer.E, layer.k, layer.d, layer.f
+    tpw = 1 if B <= 512 else 4
+    nR = -(-B // (4 * tpw)) * -(-E // 16)
+    T = -(-B // 64)
+    mt = int(ctl[9])
+    total = nR + 2 * T + 1 + mt * (f // 64 + d // 64) + -(-B // 4)
+    tr = tr[:total]
+    kind = (tr[:, 0] >> 32) & 0xFF
+    wg = tr[:, 0] >> 40
+    t0 = tr[:, 1].min()
+    us = lambda v: (v - 0) / 100.0  # 100 MHz ticks -> microseconds
+    print(f"# trace: {total} tasks, {len(set(wg.tolist()))} workgroups, span {us(tr[:, 3].max() - t0):.1f} us",
+          file=sys.stderr)
+    for kd, name in enumerate(mk.TASK_KINDS):
+        m = kind == kd
+        if not m.any():
+            continue
+        wait = tr[m, 2] - tr[m, 1]
+        run = tr[m, 3] - tr[m, 2]
+        print(f"#  {name:8s} n={int(m.sum()):6d} first start {us(tr[m, 1].min() - t0):8.1f} "
+              f"ready {us(tr[m, 2].min() - t0):8.1f} last end {us(tr[m, 3].max() - t0):8.1f} | "
+              f"wait mean {us(wait.mean()):7.2f} max {us(wait.max()):7.2f} | run mean {us(run.mean()):7.2f} "
+              f"max {us(run.max()):7.2f}", file=sys.stderr)
+    del np
 
 
 def main():
@@ -155,6 +196,8 @@ def main():
         "grid": mk.moe_mk_plan_info(layer.plan, "grid"),
         "cpu_baseline": None,
     }
+    if args.trace:
+        trace_report(layer, tx, out, B)
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         sample = args.cpu_sample or max(1, min(B, int(2.0e10 / (6 * cfg.k * cfg.d * cfg.f))))

@@ -146,7 +146,7 @@ moe_mk_status_t moe_mk_workspace_error(moe_mk_plan_t plan, const void *ws, size_
                                        int32_t *err /* host */);
 
 /* Plan facts (host).  Keys: "E" "k" "d" "f" "sched" "grid" "cus" "wg_per_cu" "BM" "BN1" "BN2" "BK"
- * "route_tokens" "route_experts" "threads".  Returns -1 for an unknown key or invalid plan. */
+ * "route_experts" "threads".  Returns -1 for an unknown key or invalid plan. */
 int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
 
 /*
@@ -157,7 +157,20 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
  * watchdog and record MOE_MK_ERR_WATCHDOG instead of hanging.
  */
 #define MOE_MK_DEBUG_DROP_NOTIFY 1
+#define MOE_MK_DEBUG_TRACE 2  /* record per-task timestamps, see moe_mk_trace_view */
 moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks, int32_t flags);
+
+/*
+ * Debug view of the task trace of the last forward run with MOE_MK_DEBUG_TRACE: *trace
+ * (host) receives a device pointer to *n (host) records of four int64 each:
+ *   [0] task index g | kind << 32 | workgroup << 40   (kind: 0 router, 1 top-k, 2 scan,
+ *       3 grouping, 4 gate/up GEMM, 5 down GEMM, 6 combine)
+ *   [1] time the workgroup obtained the task, [2] time its dependencies were satisfied,
+ *   [3] time it finished; GPU real-time clock ticks (100 MHz).
+ * Records of tasks that did not run in that forward are stale.  Errors: EINVAL, EWORKSPACE.
+ */
+moe_mk_status_t moe_mk_trace_view(moe_mk_plan_t plan, int64_t B, const void *ws, size_t ws_bytes,
+                                  const int64_t **trace /* host */, int64_t *n /* host */);
 
 /* Short static description of a status code. */
 const char *moe_mk_status_str(moe_mk_status_t s);

@@ -23,6 +23,8 @@ MOE_MK_ERR_NONFINITE = 2
 MOE_MK_ERR_QUEUE = 4
 MOE_MK_ERR_UNINIT = 8
 MOE_MK_DEBUG_DROP_NOTIFY = 1
+MOE_MK_DEBUG_TRACE = 2
+TASK_KINDS = ("route", "topk", "scan", "group", "gemm1", "gemm2", "combine")
 
 _lib = None
 
@@ -67,6 +69,8 @@ def lib():
     L.moe_mk_plan_info.restype = i64
     L.moe_mk_plan_set_debug.argtypes = [vp, i64, i32]
     L.moe_mk_plan_set_debug.restype = ctypes.c_int
+    L.moe_mk_trace_view.argtypes = [vp, i64, vp, sz, ctypes.POINTER(vp), ctypes.POINTER(i64)]
+    L.moe_mk_trace_view.restype = ctypes.c_int
     L.moe_mk_status_str.argtypes = [ctypes.c_int]
     L.moe_mk_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -158,6 +162,17 @@ def moe_mk_routing_view(plan: int, B: int, ws) -> dict:
             "inv": part(v.inv, B * k, torch.int32, (B * k,)),
             "logits": part(v.logits, B * E, torch.float32, (B, E)),
             "ctl": part(v.ctl, 64, torch.int32, (64,))}
+
+
+def moe_mk_trace_view(plan: int, B: int, ws):
+    """Device view (int64 [n, 4]) of the task trace of the last traced forward."""
+    import torch
+    ptr, n = ctypes.c_void_p(), ctypes.c_int64()
+    _check(lib().moe_mk_trace_view(plan, B, ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(ptr),
+                                   ctypes.byref(n)), "moe_mk_trace_view")
+    off = ptr.value - ws.data_ptr()
+    raw = ws.view(torch.uint8).reshape(-1)
+    return raw[off:off + n.value * 32].view(torch.int64).reshape(n.value, 4)
 
 
 def moe_mk_workspace_error(plan: int, ws, stream=None) -> int:

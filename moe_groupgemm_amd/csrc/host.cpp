@@ -161,6 +161,7 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.debug = plan->debug;
     P.nR = (int)c.nR;
     P.nTG = (int)c.nTG;
+    P.tpw = (int)c.tpw;
     P.nEB = (int)c.nEB;
     P.T = (int)c.T;
     P.nC = (int)c.nC;
@@ -186,7 +187,6 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.mt_rows = (int *)(base + L.mt_rows);
     P.perm = (int *)(base + L.perm);
     P.inv = (int *)(base + L.inv);
-    P.xg = (uint16_t *)(base + L.xg);
     P.h = (uint16_t *)(base + L.h);
     P.y = (float *)(base + L.y);
     P.qslots = (unsigned long long *)(base + L.qslots);
@@ -211,6 +211,18 @@ moe_mk_status_t moe_mk_routing_view(moe_mk_plan_t plan, int64_t B, const void *w
     view->inv = (const int32_t *)(base + L.inv);
     view->logits = (const float *)(base + L.logits);
     view->ctl = (const int32_t *)(base + L.ctl);
+    return MOE_MK_OK;
+}
+
+moe_mk_status_t moe_mk_trace_view(moe_mk_plan_t plan, int64_t B, const void *ws, size_t ws_bytes,
+                                  const int64_t **trace, int64_t *n) {
+    if (!plan_ok(plan) || !ws || !trace || !n || B < 1) return MOE_MK_EINVAL;
+    const int64_t cap = capacity(plan, ws_bytes);
+    if (cap < B) return MOE_MK_EWORKSPACE;
+    const mk::Layout L = mk::make_layout(plan->s, cap);
+    const mk::Counts c = mk::make_counts(plan->s, cap);
+    *trace = (const int64_t *)((const char *)ws + L.trace);
+    *n = c.q_cap + c.nR_max;
     return MOE_MK_OK;
 }
 
@@ -244,7 +256,6 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key) {
              {"BN1", mk::kBN},
              {"BN2", mk::kBN},
              {"BK", mk::kBK},
-             {"route_tokens", mk::kRouteTokens},
              {"route_experts", mk::kRouteExperts},
              {"threads", mk::kThreads}};
     for (auto &e : t)

@@ -31,12 +31,14 @@
 namespace mk {
 
 // ------------------------------------------------------------------------------ LDS
+constexpr int kStagesLds = 3;
 struct GemmSmem {
-    uint16_t A[2][kBM * kBK];
-    uint16_t B0[2][kBN * kBK];
-    uint16_t B1[2][kBN * kBK];
+    uint16_t A[kStagesLds][kBM * kBK];
+    uint16_t B0[kStagesLds][kBK * kBN];
+    uint16_t B1[kStagesLds][kBK * kBN];
 };
 struct TopkSmem {
+    float lg[kTileTokens * kMaxE];  // a tile's logits, then the candidate lists
     int hist[kMaxE];
 };
 struct ScanSmem {
@@ -44,9 +46,12 @@ struct ScanSmem {
 };
 struct GroupSmem {
     unsigned long long mask[kMaxE];
-    int rowmap[kTileTokens * kMaxK];
     int fired[kMaxE];
     int nfired;
+};
+struct CombineSmem {
+    int row[kCombineTokens * kMaxK];
+    float w[kCombineTokens * kMaxK];
 };
 struct Smem {
     union {
@@ -54,6 +59,7 @@ struct Smem {
         TopkSmem t;
         ScanSmem s;
         GroupSmem gr;
+        CombineSmem c;
     } u;
     int bcast[4];
     int epoch;
@@ -152,158 +158,217 @@ __device__ __forceinline__ bool wg_notify(const MK_C Params &P, MK_G int *ctr, i
 // combined by a butterfly that pairs lanes l and l^32, then l^16, ... (the halves fold),
 // which every lane evaluates in the same association; the bias is added last.
 
-template <int N>
-__device__ __forceinline__ void reduce_scatter(float (&v)[64], int lane) {
-    if constexpr (N >= 2) {
-        constexpr int H = N / 2;
-        const bool up = (lane & H) != 0;
+// Sum each of NV per-lane values over the 64 lanes, leaving value v (v = 0..NV-1) in the
+// lanes whose bits 5, 4, ... (most significant first) spell v.  Level by level, lane l
+// adds the partial sum of lane l ^ M (M = 32, 16, ..., 1); the values a lane stops
+// carrying are sent to its partner instead of both lanes adding everything.  Every
+// value is therefore the sum of the 64 chains in the association of the halves fold.
+template <int NV, int M>
+__device__ __forceinline__ void reduce_scatter(float *v, int lane) {
+    if constexpr (M >= 1) {
+        if constexpr (NV >= 2) {
+            constexpr int H = NV / 2;
+            const bool up = (lane & M) != 0;
 #pragma unroll
-        for (int i = 0; i < H; ++i) {
-            const float send = up ? v[i] : v[i + H];
-            const float keep = up ? v[i + H] : v[i];
-            v[i] = keep + shfl_xor_f(send, H);
+            for (int i = 0; i < H; ++i) {
+                const float send = up ? v[i] : v[i + H];
+                const float keep = up ? v[i + H] : v[i];
+                v[i] = keep + shfl_xor_f(send, M);
+            }
+            reduce_scatter<H, M / 2>(v, lane);
+        } else {
+            v[0] = v[0] + shfl_xor_f(v[0], M);
+            reduce_scatter<1, M / 2>(v, lane);
         }
-        reduce_scatter<H>(v, lane);
     }
 }
 
-__device__ __attribute__((noinline)) void task_route(const MK_C Params &P, int tg, int eb) {
-    const int lane = lane_id(), w = wave_id();
-    const int b0 = tg * kRouteTokens + w * 4;
-    const int e0 = eb * kRouteExperts;
-    float acc[4][16];
+// One wave: TPW tokens from b0, 16 experts from e0.  Lane l owns the chains j = l, l+64,
+// ...; the loads of the next PF steps are in flight while a step is accumulated.  Tokens
+// or experts past the end load clamped (valid) addresses; their sums are never written.
+template <int TPW>
+__device__ __attribute__((noinline)) void route_wave(const MK_C Params &P, int b0, int e0) {
+    constexpr int PF = TPW == 1 ? 6 : 3;
+    constexpr int NV = TPW * 16;
+    const int lane = lane_id();
+    float acc[NV];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
+    const MK_G uint16_t *xp[TPW];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
-
-    bool tv[4];
-    const MK_G uint16_t *xp[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        tv[t] = (b0 + t) < P.B;
-        xp[t] = P.x + (size_t)(tv[t] ? b0 + t : 0) * P.d + lane;
-    }
-    const bool vec = (P.E & 3) == 0;
-    bool ev[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ev[q] = (e0 + 4 * q) < P.E;
-    const MK_G float *wp = P.Wr + (size_t)lane * P.E + e0;
-    const size_t wstep = (size_t)64 * P.E;
+    for (int t = 0; t < TPW; ++t) xp[t] = P.x + (size_t)min(b0 + t, P.B - 1) * P.d + lane;
     const int nst = P.d / 64;
-#pragma unroll 4
-    for (int s = 0; s < nst; ++s) {
-        float xv[4];
+    if ((P.E & 3) == 0) {
+        int cq[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) xv[t] = tv[t] ? bf16_to_f32(xp[t][(size_t)s * 64]) : 0.0f;
-        float wr[16];
-        if (vec) {
+        for (int q = 0; q < 4; ++q) cq[q] = min(e0 + 4 * q, P.E - 4);
+        const MK_G float *wp = P.Wr + (size_t)lane * P.E;
+        const size_t wstep = (size_t)64 * P.E;
+        float xr[PF][TPW];
+        f32x4 wr[PF][4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (ev[q]) v = *(const MK_G f32x4 *)(wp + 4 * q);
-                wr[4 * q + 0] = v[0];
-                wr[4 * q + 1] = v[1];
-                wr[4 * q + 2] = v[2];
-                wr[4 * q + 3] = v[3];
+        for (int p = 0; p < PF; ++p) {
+            if (p < nst) {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) xr[p][t] = bf16_to_f32(xp[t][(size_t)p * 64]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) wr[p][q] = *(const MK_G f32x4 *)(wp + (size_t)p * wstep + cq[q]);
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) wr[e] = (e0 + e) < P.E ? wp[e] : 0.0f;
         }
-        wp += wstep;
+        for (int s0 = 0; s0 < nst; s0 += PF) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+            for (int u = 0; u < PF; ++u) {
+                const int st = s0 + u;
+                if (st < nst) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[t][e] = fmaf(xv[t], wr[e], acc[t][e]);
+                    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+#pragma unroll
+                            for (int z = 0; z < 4; ++z)
+                                acc[t * 16 + 4 * q + z] = fmaf(xr[u][t], wr[u][q][z], acc[t * 16 + 4 * q + z]);
+                    const int nx = st + PF;
+                    if (nx < nst) {
+#pragma unroll
+                        for (int t = 0; t < TPW; ++t) xr[u][t] = bf16_to_f32(xp[t][(size_t)nx * 64]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) wr[u][q] = *(const MK_G f32x4 *)(wp + (size_t)nx * wstep + cq[q]);
+                    }
+                }
+            }
+        }
+    } else {  // E not a multiple of 4: plain scalar loads, same summation order
+        for (int st = 0; st < nst; ++st) {
+            const int j = st * 64 + lane;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const float xv = bf16_to_f32(xp[t][(size_t)st * 64]);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float wv = P.Wr[(size_t)j * P.E + min(e0 + e, P.E - 1)];
+                    acc[t * 16 + e] = fmaf(xv, wv, acc[t * 16 + e]);
+                }
+            }
+        }
     }
-    float v[64];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) v[t * 16 + e] = acc[t][e];
-    reduce_scatter<64>(v, lane);
-    // lane L now holds the full sum of value L = (token L/16, expert L%16)
-    const int b = b0 + (lane >> 4), e = e0 + (lane & 15);
-    if (b < P.B && e < P.E) {
-        const float bias = P.bias ? P.bias[e] : 0.0f;
-        const float lg = v[0] + bias;
-        if (!__builtin_isfinite(lg)) set_error(P.ctl, 2 /* MOE_MK_ERR_NONFINITE */);
-        P.logits[(size_t)b * P.E + e] = lg;
+    reduce_scatter<NV, 32>(acc, lane);
+    // lane L holds value L >> SH: token t = value / 16, expert e0 + value % 16
+    constexpr int SH = NV == 64 ? 0 : 2;
+    if ((lane & ((1 << SH) - 1)) == 0) {
+        const int v = lane >> SH;
+        const int b = b0 + v / 16, e = e0 + (v & 15);
+        if (b < P.B && e < P.E) {
+            const float bias = P.bias ? P.bias[e] : 0.0f;
+            const float lg = acc[0] + bias;
+            if (!__builtin_isfinite(lg)) set_error(P.ctl, 2 /* MOE_MK_ERR_NONFINITE */);
+            P.logits[(size_t)b * P.E + e] = lg;
+        }
     }
+}
+
+// Router task (tg, eb): tokens [4*tpw*tg, +4*tpw), wave w taking tpw of them, experts
+// [16*eb, +16).
+__device__ __attribute__((noinline)) void task_route(const MK_C Params &P, int tg, int eb) {
+    const int w = wave_id();
+    const int e0 = eb * kRouteExperts;
+    if (P.tpw == 1)
+        route_wave<1>(P, tg * 4 + w, e0);
+    else
+        route_wave<4>(P, tg * 16 + w * 4, e0);
 }
 
 // ------------------------------------------------------------------------------ TOPK
 // For each token: the k largest logits (ties to the lower expert index; -0 equals +0),
-// then softmax over them in fp32.  Keys are (order-preserving logit bits, ~expert) so a
-// wave-wide max picks the largest logit and, among equals, the smallest expert.
-__device__ __attribute__((noinline)) void task_topk(const MK_C Params &P, int t) {
-    int *sh = g_sm.u.t.hist;
-    for (int i = threadIdx.x; i < P.E; i += kThreads) sh[i] = 0;
-    __syncthreads();
+// then softmax over them in fp32.  Keys are (order-preserving logit bits, ~expert) so the
+// larger key is the larger logit and, among equal logits, the smaller expert.  The tile's
+// logits are staged in LDS; wave w keeps, for every token (one per lane), a sorted list
+// of the best keys among its quarter of the experts; wave 0 then merges the four lists.
+
+template <int KB>
+__device__ __forceinline__ void key_insert(unsigned long long (&keys)[KB], unsigned long long v) {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+        const unsigned long long hi = keys[i] > v ? keys[i] : v;
+        v = keys[i] > v ? v : keys[i];
+        keys[i] = hi;
+    }
+}
+
+template <int KB>
+__device__ __attribute__((noinline)) void topk_tile(const MK_C Params &P, int t) {
+    TopkSmem &ts = g_sm.u.t;
     const int lane = lane_id(), w = wave_id();
-    for (int q = w; q < kTileTokens; q += 4) {
-        const int b = t * kTileTokens + q;
-        if (b >= P.B) break;
-        const MK_G float *lg = P.logits + (size_t)b * P.E;
-        unsigned long long key[4];
+    const int E = P.E, k = P.k;
+    const int ntok = min(kTileTokens, P.B - t * kTileTokens);
+    // stage the tile's logits
+    const MK_G float *src = P.logits + (size_t)t * kTileTokens * E;
+    const int n4 = ntok * E / 4;  // E*ntok is a multiple of 4 when E is; otherwise copy scalars
+    if ((E & 3) == 0) {
+        for (int i = threadIdx.x; i < n4; i += kThreads) *(f32x4 *)(ts.lg + 4 * i) = *(const MK_G f32x4 *)(src + 4 * i);
+    } else {
+        for (int i = threadIdx.x; i < ntok * E; i += kThreads) ts.lg[i] = src[i];
+    }
+    for (int i = threadIdx.x; i < E; i += kThreads) ts.hist[i] = 0;
+    __syncthreads();
+    // local lists over experts [e_lo, e_hi)
+    const int per = (E + 3) / 4;
+    const int e_lo = min(E, w * per), e_hi = min(E, e_lo + per);
+    unsigned long long keys[KB];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int e = lane + 64 * c;
-            key[c] = 0ull;
-            if (e < P.E) {
-                const float l = lg[e] + 0.0f;  // folds -0 onto +0
-                key[c] = ((unsigned long long)float_key(l) << 32) | (0xffffffffu - (uint32_t)e);
-            }
+    for (int i = 0; i < KB; ++i) keys[i] = 0ull;
+    if (lane < ntok) {
+        for (int e = e_lo; e < e_hi; ++e) {
+            const float l = ts.lg[lane * E + e] + 0.0f;  // folds -0 onto +0
+            key_insert<KB>(keys, ((unsigned long long)float_key(l) << 32) | (0xffffffffu - (uint32_t)e));
         }
-        int sel_e[kMaxK];
-        float sel_l[kMaxK];
+    }
+    __syncthreads();  // logits no longer needed: the area now holds the candidate lists
+    unsigned long long *cand = (unsigned long long *)ts.lg;  // [3 waves][64 tokens][KB]
+    if (w > 0) {
 #pragma unroll
-        for (int s = 0; s < kMaxK; ++s) {
-            sel_e[s] = 0;
-            sel_l[s] = 0.0f;
-            if (s < P.k) {
-                unsigned long long best = key[0];
+        for (int i = 0; i < KB; ++i) cand[((w - 1) * kTileTokens + lane) * KB + i] = keys[i];
+    }
+    __syncthreads();
+    if (w == 0 && lane < ntok) {
+        for (int ww = 0; ww < 3; ++ww)
 #pragma unroll
-                for (int c = 1; c < 4; ++c) best = key[c] > best ? key[c] : best;
-                best = wave_max_u64(best);
-                const int eb = (int)(0xffffffffu - (uint32_t)best);
-                if ((eb & 63) == lane) {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        if ((eb >> 6) == c) key[c] = 0ull;
-                }
-                sel_e[s] = eb;
-                sel_l[s] = key_float((uint32_t)(best >> 32));
-            }
-        }
-        const float m = sel_l[0];
-        float ex[kMaxK];
+            for (int i = 0; i < KB; ++i)
+                if (i < k) key_insert<KB>(keys, cand[(ww * kTileTokens + lane) * KB + i]);
+        const int b = t * kTileTokens + lane;
+        const float m = key_float((uint32_t)(keys[0] >> 32));
+        float ex[KB];
         float sum = 0.0f;
 #pragma unroll
-        for (int s = 0; s < kMaxK; ++s) {
-            ex[s] = 0.0f;
-            if (s < P.k) {
-                ex[s] = expf(sel_l[s] - m);
-                sum += ex[s];
+        for (int i = 0; i < KB; ++i) {
+            ex[i] = 0.0f;
+            if (i < k) {
+                ex[i] = expf(key_float((uint32_t)(keys[i] >> 32)) - m);
+                sum += ex[i];
             }
         }
-        int my_e = 0;
-        float my_x = 0.0f;
 #pragma unroll
-        for (int s = 0; s < kMaxK; ++s)
-            if (s == lane) {
-                my_e = sel_e[s];
-                my_x = ex[s];
+        for (int i = 0; i < KB; ++i) {
+            if (i < k) {
+                const int e = (int)(0xffffffffu - (uint32_t)keys[i]);
+                P.topk_idx[(size_t)b * k + i] = e;
+                P.topk_w[(size_t)b * k + i] = ex[i] / sum;
+                atomicAdd(&ts.hist[e], 1);
             }
-        if (lane < P.k) {
-            P.topk_idx[(size_t)b * P.k + lane] = my_e;
-            P.topk_w[(size_t)b * P.k + lane] = my_x / sum;
-            atomicAdd(&sh[my_e], 1);
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < P.E; i += kThreads) P.tile_hist[(size_t)t * P.E + i] = sh[i];
+    for (int i = threadIdx.x; i < E; i += kThreads) P.tile_hist[(size_t)t * E + i] = ts.hist[i];
+}
+
+__device__ __attribute__((noinline)) void task_topk(const MK_C Params &P, int t) {
+    if (P.k <= 2)
+        topk_tile<2>(P, t);
+    else if (P.k <= 4)
+        topk_tile<4>(P, t);
+    else if (P.k <= 8)
+        topk_tile<8>(P, t);
+    else
+        topk_tile<16>(P, t);
 }
 
 // ------------------------------------------------------------------------------ SCAN
@@ -371,10 +436,11 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P) {
 }
 
 // ------------------------------------------------------------------------------ GROUP
-// Stable grouping of one 64-token tile: rank of (b, i) among the tile's rows of expert e
-// is the number of earlier tokens of the tile routed to e (a token uses an expert at most
-// once), read off a 64-bit token mask per expert.  Row p = tile_off[t,e] + rank;
-// perm[p] = b*k+i, inv[b*k+i] = p, and the token's row of x is copied to xg[p].
+// Stable grouping of one 64-token tile: the rank of (b, i) among the tile's rows of expert
+// e is the number of earlier tokens of the tile routed to e (a token uses an expert at
+// most once), read off a 64-bit token mask per expert.  Row p = tile_off[t,e] + rank;
+// perm[p] = b*k+i and inv[b*k+i] = p.  The rows themselves are not copied: the gate/up
+// GroupGEMM reads each grouped row of x through perm.
 __device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t) {
     GroupSmem &g = g_sm.u.gr;
     const int E = P.E, k = P.k;
@@ -394,122 +460,157 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t
             const int p = P.tile_off[(size_t)t * E + e] + rank;
             P.perm[p] = a;
             P.inv[a] = p;
-            g.rowmap[lane * k + i] = p;
         }
-    }
-    __syncthreads();
-    const int cpr = P.d / 8;  // 16-byte chunks per row
-    const int total = ntok * k * cpr;
-    for (int idx = threadIdx.x; idx < total; idx += kThreads) {
-        const int q = idx / cpr, c = idx - q * cpr;
-        const int tok = t * kTileTokens + q / k;
-        const u32x4 v = *((const MK_G u32x4 *)(P.x + (size_t)tok * P.d) + c);
-        *((MK_G u32x4 *)(P.xg + (size_t)g.rowmap[q] * P.d) + c) = v;
     }
 }
 
 // ------------------------------------------------------------------------------ GroupGEMM tiles
 // C[rows, 64 cols] = A[rows, K] * B[K, 64 cols] on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation.  A is K-contiguous (grouped token rows); B is a weight slice with N
-// contiguous ([K][ldb] row-major).  Tiles of kBK = 64 along K are staged through LDS in
-// two buffers while the next two stages are in flight in registers.  In LDS both tiles
-// are stored K-contiguous per row (A: per token row, B: per output column; B is
-// transposed in registers while being written), in 16-byte chunks XOR-swizzled by row
-// so fragment reads and transposing writes are free of bank conflicts.  Wave w owns
-// output columns [16w, 16w+16); 16-row blocks beyond the tile's rows are skipped.
+// contiguous ([K][ldb] row-major), exactly as stored.  Tiles of kBK = 64 along K go
+// straight from global memory into a ring of kStages LDS buffers (global_load_lds, no
+// staging registers), kStages - 1 of them in flight while one is consumed.
+//   A tile in LDS: [row][k], 128-byte rows; 16-byte chunk c of row r sits at c ^ swa(r).
+//     MFMA A fragment (lane i of group g: 8 consecutive k of row i) = one ds_read_b128.
+//   B tile in LDS: [k][n], 128-byte rows as in memory; chunk c of row k sits at c ^ swb(k).
+//     MFMA B fragment (8 consecutive k of column j) = two ds_read_b64_tr_b16: within each
+//     16-lane group, lane l addresses row (k0 + l/4), columns (n0 + 4*(l%4) .. +3) and
+//     receives the 4 rows' values of column n0 + l.
+// The swizzles make both fragment reads conflict-free.  Wave w owns output columns
+// [16w, 16w+16); 16-row blocks beyond the tile's rows are skipped, and rows of a partial
+// block past the tile's rows are never loaded (their outputs are discarded).
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define MK_L __attribute__((address_space(3)))
 
-template <bool DUAL>
-struct GemmRegs {
-    u32x4 a[2];
-    u32x4 b0[2];
-    u32x4 b1[DUAL ? 2 : 1];
-};
+__device__ __forceinline__ int swa(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swb(int k) { return (((k >> 1) ^ (k >> 3)) & 3) << 1; }
 
 struct GemmArgs {
-    const MK_G uint16_t *A;
-    int lda, nrows;
+    const MK_G uint16_t *arow[2];  // this lane's A rows (one per 1 KB block it loads)
+    int nrows;
     const MK_G uint16_t *B0, *B1;
     int ldb, K;
 };
 
-template <bool DUAL>
-__device__ __forceinline__ void gemm_load(GemmRegs<DUAL> &R, const GemmArgs &g, int k0) {
-    const int tid = threadIdx.x;
-    const int ar = tid >> 3, ac = tid & 7;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int r = ar + 32 * hh;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (r < g.nrows) z = *(const MK_G u32x4 *)(g.A + (size_t)r * g.lda + k0 + ac * 8);
-        R.a[hh] = z;
-    }
-    const int kp = tid >> 3, c = tid & 7;
-    const MK_G uint16_t *p0 = g.B0 + (size_t)(k0 + 2 * kp) * g.ldb + c * 8;
-    R.b0[0] = *(const MK_G u32x4 *)p0;
-    R.b0[1] = *(const MK_G u32x4 *)(p0 + g.ldb);
-    if constexpr (DUAL) {
-        const MK_G uint16_t *p1 = g.B1 + (size_t)(k0 + 2 * kp) * g.ldb + c * 8;
-        R.b1[0] = *(const MK_G u32x4 *)p1;
-        R.b1[1] = *(const MK_G u32x4 *)(p1 + g.ldb);
-    }
+__device__ __forceinline__ void lds_dma16(const MK_G void *src, MK_L void *dst_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, dst_wave_base, 16, 0, 0);
 }
 
-__device__ __forceinline__ void store_b_transposed(const u32x4 &r0, const u32x4 &r1, uint16_t *sB) {
-    const int tid = threadIdx.x;
-    const int kp = tid >> 3, c = tid & 7;
-    const int kc = kp >> 2, kw = (kp & 3) * 2;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const uint32_t lo = r0[q >> 1], hi = r1[q >> 1];
-        const uint32_t v = (q & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        const int n = 8 * c + q;
-        *(uint32_t *)(sB + n * kBK + ((kc ^ swz(n)) * 8) + kw) = v;
-    }
-}
-
+// Issue the loads of one K stage (each wave moves two 1 KB blocks of every tile).
 template <bool DUAL>
-__device__ __forceinline__ void gemm_store_lds(const GemmRegs<DUAL> &R, uint16_t *sA, uint16_t *sB0, uint16_t *sB1) {
-    const int tid = threadIdx.x;
-    const int ar = tid >> 3, ac = tid & 7;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int r = ar + 32 * hh;
-        *(u32x4 *)(sA + r * kBK + ((ac ^ swz(r)) * 8)) = R.a[hh];
-    }
-    store_b_transposed(R.b0[0], R.b0[1], sB0);
-    if constexpr (DUAL) store_b_transposed(R.b1[0], R.b1[1], sB1);
-}
-
-template <bool DUAL>
-__device__ __forceinline__ void gemm_compute(const uint16_t *sA, const uint16_t *sB0, const uint16_t *sB1, int nrb,
-                                             f32x4 (&acc0)[4], f32x4 (&acc1)[4]) {
+__device__ __forceinline__ void stage_load(const GemmArgs &g, int k0, uint16_t *sA, uint16_t *sB0, uint16_t *sB1) {
     const int lane = lane_id(), w = wave_id();
-    const int g = lane >> 4, j = lane & 15;
-    const int n = 16 * w + j;
+    const int r8 = lane >> 3, pc = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int blk = 2 * w + i;  // 1 KB block = 8 rows of 128 bytes
+        const int row = 8 * blk + r8;
+        lds_dma16(g.arow[i] + k0 + 8 * (pc ^ swa(row)), (MK_L void *)(sA + blk * 512));
+        const int kr = 8 * blk + r8;
+        const int lc = pc ^ swb(kr);
+        lds_dma16(g.B0 + (size_t)(k0 + kr) * g.ldb + 8 * lc, (MK_L void *)(sB0 + blk * 512));
+        if constexpr (DUAL) lds_dma16(g.B1 + (size_t)(k0 + kr) * g.ldb + 8 * lc, (MK_L void *)(sB1 + blk * 512));
+    }
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t *p) {
+    return (uint32_t)(uintptr_t)(const MK_L uint16_t *)p;
+}
+
+// LDS byte address of this lane's half of a B fragment (rows kbase + l/4, or + 4 for the
+// second half; columns ncol0 + 4*(l%4)).
+__device__ __forceinline__ uint32_t b_frag_addr(const uint16_t *sB, int kbase, int ncol0) {
+    const int l = lane_id() & 15;
+    const int k = kbase + (l >> 2);
+    const int col = ncol0 + 4 * (l & 3);
+    return lds_addr(sB + k * kBN + ((((col >> 3) ^ swb(k)) << 3) | (col & 7)));
+}
+
+__device__ __forceinline__ u32x4 join(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
+
+// One K step of 32: the fragment reads are issued together in one asm block that also
+// waits for them (the compiler cannot tell these reads from the DMA writes into other
+// ring buffers, and would otherwise wait for every load in flight), then the MFMAs run.
+template <bool DUAL>
+__device__ __forceinline__ void stage_compute(const uint16_t *sA, const uint16_t *sB0, const uint16_t *sB1, int nrb,
+                                              f32x4 (&acc0)[4], f32x4 (&acc1)[4]) {
+    const int lane = lane_id(), w = wave_id();
+    const int g = lane >> 4, i = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
-        const int ch = ks * 4 + g;
-        const u32x4 b0 = *(const u32x4 *)(sB0 + n * kBK + ((ch ^ swz(n)) * 8));
-        u32x4 b1 = b0;
-        if constexpr (DUAL) b1 = *(const u32x4 *)(sB1 + n * kBK + ((ch ^ swz(n)) * 8));
+        const int kb = 32 * ks + 8 * g;  // this lane group's 8 k values: kb .. kb+7
+        uint32_t aa[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            const int r = 16 * rb + i;
+            aa[rb] = lds_addr(sA + r * kBK + (((kb >> 3) ^ swa(r)) << 3));
+        }
+        const uint32_t b0l = b_frag_addr(sB0, kb, 16 * w), b0h = b_frag_addr(sB0, kb + 4, 16 * w);
+        u32x2 x0l, x0h, x1l, x1h;
+        u32x4 a0, a1, a2, a3;
+        if constexpr (DUAL) {
+            const uint32_t b1l = b_frag_addr(sB1, kb, 16 * w), b1h = b_frag_addr(sB1, kb + 4, 16 * w);
+            asm volatile(
+                "ds_read_b64_tr_b16 %0, %8\n\t"
+                "ds_read_b64_tr_b16 %1, %9\n\t"
+                "ds_read_b64_tr_b16 %2, %10\n\t"
+                "ds_read_b64_tr_b16 %3, %11\n\t"
+                "ds_read_b128 %4, %12\n\t"
+                "ds_read_b128 %5, %13\n\t"
+                "ds_read_b128 %6, %14\n\t"
+                "ds_read_b128 %7, %15\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(x0l), "=&v"(x0h), "=&v"(x1l), "=&v"(x1h), "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+                : "v"(b0l), "v"(b0h), "v"(b1l), "v"(b1h), "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
+        } else {
+            asm volatile(
+                "ds_read_b64_tr_b16 %0, %6\n\t"
+                "ds_read_b64_tr_b16 %1, %7\n\t"
+                "ds_read_b128 %2, %8\n\t"
+                "ds_read_b128 %3, %9\n\t"
+                "ds_read_b128 %4, %10\n\t"
+                "ds_read_b128 %5, %11\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(x0l), "=&v"(x0h), "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+                : "v"(b0l), "v"(b0h), "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
+            x1l = x0l;
+            x1h = x0h;
+        }
+        const u32x4 b0 = join(x0l, x0h), b1 = join(x1l, x1h);
+        const u32x4 av[4] = {a0, a1, a2, a3};
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
             if (rb < nrb) {
-                const int r = 16 * rb + j;
-                const u32x4 a = *(const u32x4 *)(sA + r * kBK + ((ch ^ swz(r)) * 8));
-                acc0[rb] = mfma_bf16_16x16x32(a, b0, acc0[rb]);
-                if constexpr (DUAL) acc1[rb] = mfma_bf16_16x16x32(a, b1, acc1[rb]);
+                acc0[rb] = mfma_bf16_16x16x32(av[rb], b0, acc0[rb]);
+                if constexpr (DUAL) acc1[rb] = mfma_bf16_16x16x32(av[rb], b1, acc1[rb]);
             }
         }
     }
 }
 
-// PF register stages are in flight while LDS buffer (s & 1) holds stage s; stage s sits
-// in register set s % PF until it is written to LDS one step before its use.
-template <bool DUAL, int PF>
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+// Workgroup barrier without the memory-model fences of __syncthreads (which would wait
+// for every LDS-DMA load in flight); the empty asm statements keep the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+constexpr int kStages = kStagesLds;  // LDS ring depth of the GroupGEMM tiles
+
+template <bool DUAL>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], f32x4 (&acc1)[4], GemmSmem &s) {
+    constexpr int kLoadsPerStage = DUAL ? 6 : 4;  // global_load_lds instructions per wave per stage
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
         acc0[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -517,44 +618,52 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], 
     }
     const int nrb = (ga.nrows + 15) / 16;
     const int nk = ga.K / kBK;
-    GemmRegs<DUAL> R[PF];
+    // prologue: stages 0 .. kStages-2 in flight (empty stages keep the wait counts uniform)
 #pragma unroll
-    for (int p = 0; p < PF; ++p)
-        if (p < nk) gemm_load<DUAL>(R[p], ga, p * kBK);
-    gemm_store_lds<DUAL>(R[0], s.A[0], s.B0[0], s.B1[0]);
-    if (PF < nk) gemm_load<DUAL>(R[0], ga, PF * kBK);
-    __syncthreads();
-    for (int kk = 0; kk < nk; kk += PF) {
-#pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            const int st = kk + u;
-            if (st < nk) {
-                const int buf = st & 1;
-                gemm_compute<DUAL>(s.A[buf], s.B0[buf], s.B1[buf], nrb, acc0, acc1);
-                if (st + 1 < nk) {
-                    gemm_store_lds<DUAL>(R[(u + 1) % PF], s.A[buf ^ 1], s.B0[buf ^ 1], s.B1[buf ^ 1]);
-                    if (st + 1 + PF < nk) gemm_load<DUAL>(R[(u + 1) % PF], ga, (st + 1 + PF) * kBK);
-                }
-                __syncthreads();
-            }
+    for (int p = 0; p < kStages - 1; ++p)
+        if (p < nk) stage_load<DUAL>(ga, p * kBK, s.A[p], s.B0[p], s.B1[p]);
+    for (int st = 0; st < nk; ++st) {
+        // stage st has landed once at most (kStages - 2) newer stages are outstanding
+        if (st + kStages - 2 < nk)
+            wait_vm<(kStages - 2) * kLoadsPerStage>();
+        else
+            wait_vm<0>();
+        bare_barrier();  // every wave's part of stage st is in LDS; buffer (st-1) is free
+        const int nxt = st + kStages - 1;
+        if (nxt < nk) {
+            const int b = nxt % kStages;
+            stage_load<DUAL>(ga, nxt * kBK, s.A[b], s.B0[b], s.B1[b]);
         }
+        const int b = st % kStages;
+        stage_compute<DUAL>(s.A[b], s.B0[b], s.B1[b], nrb, acc0, acc1);
     }
+    wait_vm<0>();
+    __syncthreads();  // the LDS ring may be reused by the next task
 }
 
-constexpr int kPF = 4;  // register prefetch depth of the GroupGEMM tiles
+// Row r of this lane's A blocks: 8 * (2w + i) + lane / 8.  Rows past the tile's end
+// re-read its last row (every wave must issue the same number of loads per stage for the
+// vmcnt-based waits); their outputs are discarded.
+__device__ __forceinline__ int a_row(int i, int nrows) {
+    return min(8 * (2 * wave_id() + i) + (lane_id() >> 3), nrows - 1);
+}
 
-// GEMM1 tile: h[rows, n0:n0+64] = bf16( silu(xg W1[e]) * (xg W3[e]) ) for one row tile.
+// GEMM1 tile: h[rows, n0:n0+64] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
+// where row p of the tile is token perm[p] / k of x.
 __device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
     GemmArgs ga;
-    ga.A = P.xg + (size_t)row0 * P.d;
-    ga.lda = P.d;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tok = P.perm[row0 + a_row(i, nrows)] / P.k;
+        ga.arow[i] = P.x + (size_t)tok * P.d;
+    }
     ga.nrows = nrows;
     ga.B0 = P.W1 + (size_t)e * P.d * P.f + (size_t)n * kBN;
     ga.B1 = P.W3 + (size_t)e * P.d * P.f + (size_t)n * kBN;
     ga.ldb = P.f;
     ga.K = P.d;
     f32x4 acc0[4], acc1[4];
-    gemm_tile<true, kPF>(ga, acc0, acc1, g_sm.u.g);
+    gemm_tile<true>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
     const int col = n * kBN + 16 * w + j;
@@ -575,15 +684,15 @@ __device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &P, int e
 // GEMM2 tile: y[rows, n0:n0+64] = h[rows, :] W2[e][:, n0:n0+64] in fp32.
 __device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n) {
     GemmArgs ga;
-    ga.A = P.h + (size_t)row0 * P.f;
-    ga.lda = P.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ga.arow[i] = P.h + (size_t)(row0 + a_row(i, nrows)) * P.f;
     ga.nrows = nrows;
     ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)n * kBN;
     ga.B1 = ga.B0;
     ga.ldb = P.d;
     ga.K = P.f;
     f32x4 acc0[4], acc1[4];
-    gemm_tile<false, kPF>(ga, acc0, acc1, g_sm.u.g);
+    gemm_tile<false>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
     const int col = n * kBN + 16 * w + j;
@@ -598,34 +707,44 @@ __device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &P, int e
 }
 
 // ------------------------------------------------------------------------------ COMBINE
-// out[b, :] = bf16( sum_{i<k} w[b,i] * y[inv[b*k+i], :] ), slot order, fp32.
+// out[b, :] = bf16( sum_{i<k} w[b,i] * y[inv[b*k+i], :] ), slot order, fp32, for
+// kCombineTokens tokens; (token, 4-column group) items are spread over the workgroup.
 __device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int c) {
+    CombineSmem &cs = g_sm.u.c;
     const int b_lo = c * kCombineTokens;
-    const int b_hi = min(P.B, b_lo + kCombineTokens);
-    const int nq = P.d / 4;
-    for (int b = b_lo; b < b_hi; ++b) {
-        for (int q = threadIdx.x; q < nq; q += kThreads) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int i = 0; i < P.k; ++i) {
-                const int p = P.inv[(size_t)b * P.k + i];
-                const float wgt = P.topk_w[(size_t)b * P.k + i];
-                const f32x4 yv = *(const MK_G f32x4 *)(P.y + (size_t)p * P.d + 4 * q);
-#pragma unroll
-                for (int z = 0; z < 4; ++z) acc[z] = fmaf(wgt, yv[z], acc[z]);
-            }
-            const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-            MK_G uint32_t *o = (MK_G uint32_t *)(P.out + (size_t)b * P.d + 4 * q);
-            o[0] = lo;
-            o[1] = hi;
-        }
+    const int nb = min(kCombineTokens, P.B - b_lo);
+    const int k = P.k;
+    for (int i = threadIdx.x; i < nb * k; i += kThreads) {
+        cs.row[i] = P.inv[(size_t)b_lo * k + i];
+        cs.w[i] = P.topk_w[(size_t)b_lo * k + i];
     }
+    __syncthreads();
+    const int nq = P.d / 4;
+    const int items = nb * nq;
+#pragma unroll 4
+    for (int it = threadIdx.x; it < items; it += kThreads) {
+        const int bb = it / nq, q = it - bb * nq;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < k; ++i) {
+            const f32x4 yv = *(const MK_G f32x4 *)(P.y + (size_t)cs.row[bb * k + i] * P.d + 4 * q);
+            const float wgt = cs.w[bb * k + i];
+#pragma unroll
+            for (int z = 0; z < 4; ++z) acc[z] = fmaf(wgt, yv[z], acc[z]);
+        }
+        const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+        *(MK_G u32x2 *)(P.out + (size_t)(b_lo + bb) * P.d + 4 * q) = u32x2{lo, hi};
+    }
+    __syncthreads();
 }
 
 // ------------------------------------------------------------------------------ task dispatch
+// Router token groups of one 64-token tile (a group is 4 * tpw tokens).
+__device__ __forceinline__ int route_groups_per_tile(const MK_C Params &P) { return kTileTokens / (4 * P.tpw); }
+
 __device__ __forceinline__ int route_tasks_of_tile(const MK_C Params &P, int t) {
-    const int g0 = t * (kTileTokens / kRouteTokens);
-    const int g1 = min(g0 + kTileTokens / kRouteTokens, P.nTG);
+    const int g0 = t * route_groups_per_tile(P);
+    const int g1 = min(g0 + route_groups_per_tile(P), P.nTG);
     return (g1 - g0) * P.nEB;
 }
 
@@ -653,9 +772,9 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         const int tg = g / P.nEB, eb = g - tg * P.nEB;
         task_route(P, tg, eb);
         count_task(P, K_ROUTE);
-        const int t = tg / (kTileTokens / kRouteTokens);
+        const int t = tg / route_groups_per_tile(P);
         int delta = -1;
-        if (dyn && (tg % (kTileTokens / kRouteTokens)) == 0 && eb == 0) delta += route_tasks_of_tile(P, t);
+        if (dyn && (tg % route_groups_per_tile(P)) == 0 && eb == 0) delta += route_tasks_of_tile(P, t);
         if (wg_notify(P, P.ev_logit + t, delta) && dyn) wg_push_range(P, bs.K + t, 1);
         trace_task(P, g, K_ROUTE, t0, t0);
         return true;

@@ -20,9 +20,8 @@ namespace mk {
 
 constexpr int kThreads = 256;        // 4 waves of 64 lanes per persistent workgroup
 constexpr int kTileTokens = 64;      // tokens per top-k / grouping tile (one lane per token)
-constexpr int kRouteTokens = 16;     // tokens per router task (4 per wave)
 constexpr int kRouteExperts = 16;    // experts per router task
-constexpr int kCombineTokens = 16;   // tokens per combine task
+constexpr int kCombineTokens = 4;    // tokens per combine task
 constexpr int kBM = 64;              // GroupGEMM rows per tile (one expert's rows)
 constexpr int kBN = 64;              // GroupGEMM columns per tile
 constexpr int kBK = 64;              // GroupGEMM K step staged through LDS
@@ -56,9 +55,14 @@ struct Shape {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Router tokens per wave: one at small batches (more, shorter tasks), four at large ones
+// (each expert-weight row loaded serves four tokens).  A router task covers 4 waves.
+inline int route_tpw(int64_t B) { return B <= 512 ? 1 : 4; }
+
 // Task counts that depend on B only.
 struct Counts {
     int64_t T;      // top-k / grouping tiles
+    int64_t tpw;    // router tokens per wave
     int64_t nTG;    // router token groups
     int64_t nEB;    // router expert blocks
     int64_t nR;     // router tasks
@@ -66,12 +70,14 @@ struct Counts {
     int64_t mt_cap; // upper bound of sum_e ceil(hist[e] / kBM)
     int64_t NB1, NB2;
     int64_t q_cap;  // upper bound of the pushed tasks of one forward
+    int64_t nR_max; // upper bound of the router tasks of any batch up to B
 };
 
 inline Counts make_counts(const Shape &s, int64_t B) {
     Counts c;
     c.T = ceil_div(B, kTileTokens);
-    c.nTG = ceil_div(B, kRouteTokens);
+    c.tpw = route_tpw(B);
+    c.nTG = ceil_div(B, 4 * c.tpw);
     c.nEB = ceil_div(s.E, kRouteExperts);
     c.nR = c.nTG * c.nEB;
     c.nC = ceil_div(B, kCombineTokens);
@@ -80,13 +86,14 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     c.NB1 = s.f / kBN;
     c.NB2 = s.d / kBN;
     c.q_cap = 2 * c.T + 1 + c.mt_cap * (c.NB1 + c.NB2) + c.nC + 64;
+    c.nR_max = ceil_div(B, 4) * c.nEB;
     return c;
 }
 
 // Byte offsets of every workspace array, for a workspace sized for B = cap tokens.
 struct Layout {
     size_t ctl, ev_logit, ev_exp, ev_h, logits, topk_idx, topk_w, tile_hist, tile_off, hist, indptr,
-        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, xg, h, y, qslots, trace, total;
+        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, h, y, qslots, trace, total;
     int64_t cap;
 };
 
@@ -120,11 +127,10 @@ inline Layout make_layout(const Shape &s, int64_t cap) {
     L.mt_rows = take((size_t)c.mt_cap * 4);
     L.perm = take((size_t)A * 4);
     L.inv = take((size_t)A * 4);
-    L.xg = take((size_t)A * s.d * 2);
     L.h = take((size_t)A * s.f * 2);
     L.y = take((size_t)A * s.d * 4);
     L.qslots = take((size_t)c.q_cap * 8);
-    L.trace = take((size_t)(c.q_cap + c.nR) * 4 * 8);
+    L.trace = take((size_t)(c.q_cap + c.nR_max) * 4 * 8);
     L.total = o;
     return L;
 }
@@ -139,7 +145,7 @@ struct Params {
     int B, E, k, d, f;
     int sched;       // 0 static, 1 dynamic
     int debug;       // MOE_MK_DEBUG_* bits
-    int nR, nTG, nEB, T, nC, NB1, NB2;
+    int nR, nTG, nEB, T, nC, NB1, NB2, tpw;
     int q_cap, mt_cap;
     long long watchdog;  // real-time ticks (100 MHz)
     MK_G int *ctl, *ev_logit, *ev_exp, *ev_h;
@@ -147,7 +153,7 @@ struct Params {
     MK_G int *topk_idx;
     MK_G float *topk_w;
     MK_G int *tile_hist, *tile_off, *hist, *indptr, *mt_base, *mt_expert, *mt_row0, *mt_rows, *perm, *inv;
-    MK_G uint16_t *xg, *h;
+    MK_G uint16_t *h;
     MK_G float *y;
     MK_G unsigned long long *qslots;
     MK_G long long *trace;  // 4 int64 per task when tracing is on

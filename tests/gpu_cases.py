@@ -53,5 +53,6 @@ def ctl_words(layer, B):
 
 def expected_task_counts(hist, B, E, d, f):
     mt = int(sum((int(h) + 63) // 64 for h in hist))
-    return {"route": -(-B // 16) * -(-E // 16), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
-            "gemm1": mt * (f // 64), "gemm2": mt * (d // 64), "combine": -(-B // 16)}
+    tpw = 1 if B <= 512 else 4  # router tokens per wave; a router task has 4 waves
+    return {"route": -(-B // (4 * tpw)) * -(-E // 16), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
+            "gemm1": mt * (f // 64), "gemm2": mt * (d // 64), "combine": -(-B // 4)}
