@@ -97,12 +97,15 @@ def trace_report(layer, x, out, B):
     nR = -(-B // (4 * tpw)) * -(-E // 16)
     T = -(-B // 64)
     mt = int(ctl[9])
-    total = nR + 2 * T + 1 + mt * (f // 64 + d // 64) + -(-B // 4)
+    a = B * k
+    S = 4 if (a <= 1024 and f >= 8192 and (f // 64) % 4 == 0) else \
+        2 if (a <= 1024 and f >= 4096 and (f // 64) % 2 == 0) else 1
+    total = nR + 2 * T + 1 + mt * (f // 64 + S * (d // 64)) + -(-B // 4)
     tr = tr[:total]
     kind = (tr[:, 0] >> 32) & 0xFF
     wg = tr[:, 0] >> 40
     t0 = tr[:, 1].min()
-    us = lambda v: (v - 0) / 100.0  # 100 MHz ticks -> microseconds
+    us = lambda v: v / 100.0  # 100 MHz ticks -> microseconds
     print(f"# trace: {total} tasks, {len(set(wg.tolist()))} workgroups, span {us(tr[:, 3].max() - t0):.1f} us",
           file=sys.stderr)
     for kd, name in enumerate(mk.TASK_KINDS):
@@ -110,11 +113,22 @@ def trace_report(layer, x, out, B):
         if not m.any():
             continue
         wait = tr[m, 2] - tr[m, 1]
-        run = tr[m, 3] - tr[m, 2]
-        print(f"#  {name:8s} n={int(m.sum()):6d} first start {us(tr[m, 1].min() - t0):8.1f} "
-              f"ready {us(tr[m, 2].min() - t0):8.1f} last end {us(tr[m, 3].max() - t0):8.1f} | "
-              f"wait mean {us(wait.mean()):7.2f} max {us(wait.max()):7.2f} | run mean {us(run.mean()):7.2f} "
-              f"max {us(run.max()):7.2f}", file=sys.stderr)
+        body = tr[m, 4] - tr[m, 2]
+        tail = tr[m, 3] - tr[m, 4]
+        print(f"#  {name:8s} n={int(m.sum()):6d} start {us(tr[m, 1].min() - t0):7.1f} ready {us(tr[m, 2].min() - t0):7.1f} "
+              f"end {us(tr[m, 3].max() - t0):7.1f} | wait {us(wait.mean()):6.2f} (max {us(wait.max()):6.1f}) | "
+              f"body {us(body.mean()):7.2f} (max {us(body.max()):6.1f}) | notify {us(tail.mean()):5.2f}",
+              file=sys.stderr)
+    # time between a workgroup finishing one task and obtaining the next (queue / loop overhead)
+    gaps = []
+    for w in set(wg.tolist()):
+        r = tr[wg == w]
+        r = r[np.argsort(r[:, 1])]
+        if len(r) > 1:
+            gaps.append(r[1:, 1] - r[:-1, 3])
+    if gaps:
+        gaps = np.concatenate(gaps)
+        print(f"#  between tasks: mean {us(gaps.mean()):.2f} us, max {us(gaps.max()):.1f} us", file=sys.stderr)
     del np
 
 

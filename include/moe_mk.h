@@ -162,11 +162,12 @@ moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks
 
 /*
  * Debug view of the task trace of the last forward run with MOE_MK_DEBUG_TRACE: *trace
- * (host) receives a device pointer to *n (host) records of four int64 each:
+ * (host) receives a device pointer to *n (host) records of eight int64 each:
  *   [0] task index g | kind << 32 | workgroup << 40   (kind: 0 router, 1 top-k, 2 scan,
  *       3 grouping, 4 gate/up GEMM, 5 down GEMM, 6 combine)
  *   [1] time the workgroup obtained the task, [2] time its dependencies were satisfied,
- *   [3] time it finished; GPU real-time clock ticks (100 MHz).
+ *   [3] time it finished, [4] time its compute ended (before its notifications);
+ *   [5..7] unused.  GPU real-time clock ticks (100 MHz).
  * Records of tasks that did not run in that forward are stale.  Errors: EINVAL, EWORKSPACE.
  */
 moe_mk_status_t moe_mk_trace_view(moe_mk_plan_t plan, int64_t B, const void *ws, size_t ws_bytes,

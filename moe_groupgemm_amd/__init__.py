@@ -165,14 +165,14 @@ def moe_mk_routing_view(plan: int, B: int, ws) -> dict:
 
 
 def moe_mk_trace_view(plan: int, B: int, ws):
-    """Device view (int64 [n, 4]) of the task trace of the last traced forward."""
+    """Device view (int64 [n, 8]) of the task trace of the last traced forward."""
     import torch
     ptr, n = ctypes.c_void_p(), ctypes.c_int64()
     _check(lib().moe_mk_trace_view(plan, B, ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(ptr),
                                    ctypes.byref(n)), "moe_mk_trace_view")
     off = ptr.value - ws.data_ptr()
     raw = ws.view(torch.uint8).reshape(-1)
-    return raw[off:off + n.value * 32].view(torch.int64).reshape(n.value, 4)
+    return raw[off:off + n.value * 64].view(torch.int64).reshape(n.value, 8)
 
 
 def moe_mk_workspace_error(plan: int, ws, stream=None) -> int:

@@ -167,6 +167,7 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.nC = (int)c.nC;
     P.NB1 = (int)c.NB1;
     P.NB2 = (int)c.NB2;
+    P.S = (int)c.S;
     P.q_cap = (int)cc.q_cap;
     P.mt_cap = (int)cc.mt_cap;
     P.watchdog = plan->watchdog;
@@ -190,6 +191,7 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.h = (uint16_t *)(base + L.h);
     P.y = (float *)(base + L.y);
     P.qslots = (unsigned long long *)(base + L.qslots);
+    P.red_ctr = (int *)(base + L.red_ctr);
     P.trace = (long long *)(base + L.trace);
     if (hipSetDevice(plan->device) != hipSuccess) return MOE_MK_EHIP;
     if (mk_launch(P, plan->grid, (hipStream_t)stream) != hipSuccess) return MOE_MK_EHIP;

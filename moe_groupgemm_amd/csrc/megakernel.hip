@@ -20,22 +20,22 @@
 //   TOPK(t)       top-k + softmax + tile histogram, 64 tokens    -> ev_topk
 //   SCAN          hist, exp_indptr, per-tile offsets, row tiles; arms ev_exp/ev_h/ev_y -> ev_scan
 //   GROUP(t)      stable ranks, perm/inv, gather of token rows    -> ev_exp[e] -= rows of e
-//   GEMM1(mt,n)   gate/up GroupGEMM tile + SwiGLU -> h            -> ev_h[mt]
-//   GEMM2(mt,n)   down GroupGEMM tile -> y                        -> ev_y
+//   GEMM1(mt,n)   gate/up GroupGEMM tile + SwiGLU -> h            -> ev_h[mt,s] (s: n's f range)
+//   GEMM2(mt,s,n) down GroupGEMM tile over f range s -> y[s]      -> ev_y
 //   COMBINE(c)    out[b] = sum_i w[b,i] y[inv[b,i]] for 16 tokens
 #include <hip/hip_runtime.h>
 
 #include "mk_common.h"
 #include "mk_device.h"
 
+#define MK_L __attribute__((address_space(3)))  // LDS pointers
+
 namespace mk {
 
 // ------------------------------------------------------------------------------ LDS
-constexpr int kStagesLds = 3;
+constexpr int kRingBytes = 72 * 1024;  // LDS ring of the GroupGEMM tiles
 struct GemmSmem {
-    uint16_t A[kStagesLds][kBM * kBK];
-    uint16_t B0[kStagesLds][kBK * kBN];
-    uint16_t B1[kStagesLds][kBK * kBN];
+    uint16_t ring[kRingBytes / 2];
 };
 struct TopkSmem {
     float lg[kTileTokens * kMaxE];  // a tile's logits, then the candidate lists
@@ -88,7 +88,7 @@ __device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
 
 __device__ __forceinline__ void complete_bases(const MK_C Params &P, Bases &b, int mt_total) {
     b.M2 = b.M1 + mt_total * P.NB1;
-    b.C = b.M2 + mt_total * P.NB2;
+    b.C = b.M2 + mt_total * P.S * P.NB2;
     b.total = b.C + P.nC;
     b.known = true;
 }
@@ -110,21 +110,18 @@ __device__ __forceinline__ bool wg_wait_zero(const MK_C Params &P, const MK_G in
     return ok;
 }
 
-// Every wave waits for its own global stores to complete, then the group synchronises;
-// after this, one agent-scope release by a single thread publishes all of them.
+// Every wave waits for its own (agent-scope) stores to complete, then the group
+// synchronises: after this, all of them are visible to every XCD.
 __device__ __forceinline__ void wg_stores_done() {
     wave_drain_vm();
     __syncthreads();
 }
 
-// Push the contiguous task range [g0, g0 + cnt) onto the dynamic queue (all threads call,
-// after wg_stores_done() or another point where the data the tasks read is complete).
+// Push the contiguous task range [g0, g0 + cnt) onto the dynamic queue (all threads call;
+// the data the pushed tasks read was published before the event that fired them).
 __device__ __forceinline__ void wg_push_range(const MK_C Params &P, int g0, int cnt) {
     if (cnt <= 0) return;
-    if (threadIdx.x == 0) {
-        fence_release();
-        g_sm.bcast[1] = add_relaxed(P.ctl + CTL_QTAIL, cnt);
-    }
+    if (threadIdx.x == 0) g_sm.bcast[1] = add_relaxed(P.ctl + CTL_QTAIL, cnt);
     __syncthreads();
     const int s0 = g_sm.bcast[1];
     __syncthreads();
@@ -137,13 +134,13 @@ __device__ __forceinline__ void wg_push_range(const MK_C Params &P, int g0, int 
         st_relaxed64(P.qslots + s0 + i, tag | (uint32_t)(g0 + i));
 }
 
-// Notify one counter: the group's stores complete, thread 0 adds delta (negative =
-// decrement) with acquire-release ordering.  Returns (to every thread) whether this
-// notification brought the counter to zero, i.e. fired the event.
+// Notify one counter: the group's published stores complete, then thread 0 adds delta
+// (negative = decrement).  Returns (to every thread) whether this notification brought
+// the counter to zero, i.e. fired the event.
 __device__ __forceinline__ bool wg_notify(const MK_C Params &P, MK_G int *ctr, int delta) {
     wg_stores_done();
     if (threadIdx.x == 0) {
-        const int old = add_acq_rel(ctr, delta);
+        const int old = add_relaxed(ctr, delta);
         g_sm.bcast[2] = (old + delta == 0) ? 1 : 0;
     }
     __syncthreads();
@@ -188,7 +185,7 @@ __device__ __forceinline__ void reduce_scatter(float *v, int lane) {
 // or experts past the end load clamped (valid) addresses; their sums are never written.
 template <int TPW>
 __device__ __attribute__((noinline)) void route_wave(const MK_C Params &P, int b0, int e0) {
-    constexpr int PF = TPW == 1 ? 6 : 3;
+    constexpr int PF = TPW == 1 ? 8 : 4;
     constexpr int NV = TPW * 16;
     const int lane = lane_id();
     float acc[NV];
@@ -204,37 +201,43 @@ __device__ __attribute__((noinline)) void route_wave(const MK_C Params &P, int b
         for (int q = 0; q < 4; ++q) cq[q] = min(e0 + 4 * q, P.E - 4);
         const MK_G float *wp = P.Wr + (size_t)lane * P.E;
         const size_t wstep = (size_t)64 * P.E;
-        float xr[PF][TPW];
+        uint16_t xr[PF][TPW];  // raw bits: converted when used, not when the load is issued
         f32x4 wr[PF][4];
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
-            if (p < nst) {
+            const int ps = min(p, nst - 1);
 #pragma unroll
-                for (int t = 0; t < TPW; ++t) xr[p][t] = bf16_to_f32(xp[t][(size_t)p * 64]);
+            for (int t = 0; t < TPW; ++t) xr[p][t] = xp[t][(size_t)ps * 64];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) wr[p][q] = *(const MK_G f32x4 *)(wp + (size_t)p * wstep + cq[q]);
-            }
+            for (int q = 0; q < 4; ++q) wr[p][q] = *(const MK_G f32x4 *)(wp + (size_t)ps * wstep + cq[q]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // Steady state without branches (a join inside the loop would make the compiler
+        // wait for every load in flight): prefetch addresses are clamped to the last step,
+        // and steps past the end are masked by x = 0, which leaves every chain bitwise
+        // unchanged (0 * w is a signed zero, and a chain that starts at +0 is never -0).
         for (int s0 = 0; s0 < nst; s0 += PF) {
 #pragma unroll
             for (int u = 0; u < PF; ++u) {
                 const int st = s0 + u;
-                if (st < nst) {
+                const bool live = st < nst;
 #pragma unroll
-                    for (int t = 0; t < TPW; ++t)
+                for (int t = 0; t < TPW; ++t) {
+                    const float xm = live ? bf16_to_f32(xr[u][t]) : 0.0f;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
+                    for (int q = 0; q < 4; ++q)
 #pragma unroll
-                            for (int z = 0; z < 4; ++z)
-                                acc[t * 16 + 4 * q + z] = fmaf(xr[u][t], wr[u][q][z], acc[t * 16 + 4 * q + z]);
-                    const int nx = st + PF;
-                    if (nx < nst) {
-#pragma unroll
-                        for (int t = 0; t < TPW; ++t) xr[u][t] = bf16_to_f32(xp[t][(size_t)nx * 64]);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) wr[u][q] = *(const MK_G f32x4 *)(wp + (size_t)nx * wstep + cq[q]);
-                    }
+                        for (int z = 0; z < 4; ++z)
+                            acc[t * 16 + 4 * q + z] = fmaf(xm, wr[u][q][z], acc[t * 16 + 4 * q + z]);
                 }
+                const int nx = min(st + PF, nst - 1);
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) xr[u][t] = xp[t][(size_t)nx * 64];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) wr[u][q] = *(const MK_G f32x4 *)(wp + (size_t)nx * wstep + cq[q]);
+                // keep the refill here: the scheduler would otherwise sink each load down to
+                // its use PF steps later, serialising the chain on memory latency
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     } else {  // E not a multiple of 4: plain scalar loads, same summation order
@@ -261,7 +264,7 @@ __device__ __attribute__((noinline)) void route_wave(const MK_C Params &P, int b
             const float bias = P.bias ? P.bias[e] : 0.0f;
             const float lg = acc[0] + bias;
             if (!__builtin_isfinite(lg)) set_error(P.ctl, 2 /* MOE_MK_ERR_NONFINITE */);
-            P.logits[(size_t)b * P.E + e] = lg;
+            pub(P.logits + (size_t)b * P.E + e, lg);
         }
     }
 }
@@ -300,11 +303,15 @@ __device__ __attribute__((noinline)) void topk_tile(const MK_C Params &P, int t)
     const int lane = lane_id(), w = wave_id();
     const int E = P.E, k = P.k;
     const int ntok = min(kTileTokens, P.B - t * kTileTokens);
-    // stage the tile's logits
+    // stage the tile's logits: 1 KB blocks straight into LDS, all in flight at once (the
+    // tail of the last block may read past the tile, still inside the workspace)
     const MK_G float *src = P.logits + (size_t)t * kTileTokens * E;
-    const int n4 = ntok * E / 4;  // E*ntok is a multiple of 4 when E is; otherwise copy scalars
     if ((E & 3) == 0) {
-        for (int i = threadIdx.x; i < n4; i += kThreads) *(f32x4 *)(ts.lg + 4 * i) = *(const MK_G f32x4 *)(src + 4 * i);
+        const int nblk = (ntok * E * 4 + 1023) / 1024;
+        for (int bk = wave_id(); bk < nblk; bk += 4)
+            __builtin_amdgcn_global_load_lds((const MK_G void *)(src + bk * 256 + lane_id() * 4),
+                                             (MK_L void *)(ts.lg + bk * 256), 16, 0, 0);
+        wave_drain_vm();
     } else {
         for (int i = threadIdx.x; i < ntok * E; i += kThreads) ts.lg[i] = src[i];
     }
@@ -350,14 +357,14 @@ __device__ __attribute__((noinline)) void topk_tile(const MK_C Params &P, int t)
         for (int i = 0; i < KB; ++i) {
             if (i < k) {
                 const int e = (int)(0xffffffffu - (uint32_t)keys[i]);
-                P.topk_idx[(size_t)b * k + i] = e;
-                P.topk_w[(size_t)b * k + i] = ex[i] / sum;
+                pub(P.topk_idx + (size_t)b * k + i, e);
+                pub(P.topk_w + (size_t)b * k + i, ex[i] / sum);
                 atomicAdd(&ts.hist[e], 1);
             }
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < E; i += kThreads) P.tile_hist[(size_t)t * E + i] = ts.hist[i];
+    for (int i = threadIdx.x; i < E; i += kThreads) pub(P.tile_hist + (size_t)t * E + i, ts.hist[i]);
 }
 
 __device__ __attribute__((noinline)) void task_topk(const MK_C Params &P, int t) {
@@ -395,7 +402,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int *part, int *total) {
 
 // hist[e] = sum_t tile_hist[t,e]; exp_indptr = exclusive prefix sum; tile_off[t,e] =
 // exp_indptr[e] + rows of e in tiles before t; row tiles of kBM rows per expert; arms
-// ev_exp[e] with hist[e], ev_h[mt] with the gate/up tiles of each row tile, and ev_y with
+// ev_exp[e] with hist[e], ev_h[mt,s] with the gate/up tiles of each (row tile, f range), and ev_y with
 // the number of down-projection tiles ("Core method": the prefix sum decides how many
 // GroupGEMM tiles each expert triggers).  Returns the number of row tiles.
 __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P) {
@@ -409,28 +416,28 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P) {
     const int off = block_excl_scan(h, g_sm.u.s.part, &total_h);
     const int mbase = block_excl_scan(mt, g_sm.u.s.part, &total_mt);
     if (e < E) {
-        P.hist[e] = h;
-        P.indptr[e] = off;
-        P.mt_base[e] = mbase;
+        pub(P.hist + e, h);
+        pub(P.indptr + e, off);
+        pub(P.mt_base + e, mbase);
         int run = off;
         for (int t = 0; t < P.T; ++t) {
-            P.tile_off[(size_t)t * E + e] = run;
+            pub(P.tile_off + (size_t)t * E + e, run);
             run += P.tile_hist[(size_t)t * E + e];
         }
         for (int m = 0; m < mt; ++m) {
             const int i = mbase + m;
-            P.mt_expert[i] = e;
-            P.mt_row0[i] = off + m * kBM;
-            P.mt_rows[i] = min(kBM, h - m * kBM);
-            add_relaxed(P.ev_h + i, P.NB1);
+            pub(P.mt_expert + i, e);
+            pub(P.mt_row0 + i, off + m * kBM);
+            pub(P.mt_rows + i, min(kBM, h - m * kBM));
+            for (int sp = 0; sp < P.S; ++sp) add_relaxed(P.ev_h + i * P.S + sp, P.NB1 / P.S);
         }
         if (h) add_relaxed(P.ev_exp + e, h);
     }
     if (e == 0) {
-        P.indptr[E] = total_h;
-        P.mt_base[E] = total_mt;
+        pub(P.indptr + E, total_h);
+        pub(P.mt_base + E, total_mt);
         st_relaxed(P.ctl + CTL_MT_TOTAL, total_mt);
-        add_relaxed(P.ctl + CTL_EV_Y, total_mt * P.NB2);
+        add_relaxed(P.ctl + CTL_EV_Y, total_mt * P.S * P.NB2);
     }
     return total_mt;
 }
@@ -458,8 +465,8 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t
             const int e = P.topk_idx[a];
             const int rank = __popcll(g.mask[e] & ((1ull << lane) - 1ull));
             const int p = P.tile_off[(size_t)t * E + e] + rank;
-            P.perm[p] = a;
-            P.inv[a] = p;
+            pub(P.perm + p, a);
+            pub(P.inv + a, p);
         }
     }
 }
@@ -468,8 +475,8 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t
 // C[rows, 64 cols] = A[rows, K] * B[K, 64 cols] on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation.  A is K-contiguous (grouped token rows); B is a weight slice with N
 // contiguous ([K][ldb] row-major), exactly as stored.  Tiles of kBK = 64 along K go
-// straight from global memory into a ring of kStages LDS buffers (global_load_lds, no
-// staging registers), kStages - 1 of them in flight while one is consumed.
+// straight from global memory into a ring of LDS stages (global_load_lds, no staging
+// registers), all but one of them in flight while one is consumed.
 //   A tile in LDS: [row][k], 128-byte rows; 16-byte chunk c of row r sits at c ^ swa(r).
 //     MFMA A fragment (lane i of group g: 8 consecutive k of row i) = one ds_read_b128.
 //   B tile in LDS: [k][n], 128-byte rows as in memory; chunk c of row k sits at c ^ swb(k).
@@ -481,10 +488,25 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t
 // block past the tile's rows are never loaded (their outputs are discarded).
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-#define MK_L __attribute__((address_space(3)))
 
 __device__ __forceinline__ int swa(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swb(int k) { return (((k >> 1) ^ (k >> 3)) & 3) << 1; }
+
+// Tile variants: DUAL (gate and up weights share the A tile) and AR, the A rows staged
+// (16 when the tile has at most 16 rows, as at decode batch sizes, else 64).  The ring of
+// stages fills the same 72 KB of LDS either way, so smaller A tiles buy deeper rings:
+// more weight bytes in flight per workgroup.
+template <bool DUAL, int AR>
+struct GemmCfg {
+    static constexpr int A_ELEMS = AR * kBK;
+    static constexpr int B_ELEMS = kBK * kBN;
+    static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS * (DUAL ? 2 : 1);
+    static constexpr int NS = (kRingBytes / 2) / STAGE_ELEMS < 8 ? (kRingBytes / 2) / STAGE_ELEMS : 8;
+    static constexpr int A_LOADS = AR == 64 ? 2 : 1;             // per wave per stage
+    static constexpr int LOADS = A_LOADS + 2 * (DUAL ? 2 : 1);   // global_load_lds per wave per stage
+    static_assert(NS >= 3, "ring too shallow");
+    static_assert((NS - 2) * LOADS < 64, "vmcnt range");
+};
 
 struct GemmArgs {
     const MK_G uint16_t *arow[2];  // this lane's A rows (one per 1 KB block it loads)
@@ -497,16 +519,30 @@ __device__ __forceinline__ void lds_dma16(const MK_G void *src, MK_L void *dst_w
     __builtin_amdgcn_global_load_lds(src, dst_wave_base, 16, 0, 0);
 }
 
-// Issue the loads of one K stage (each wave moves two 1 KB blocks of every tile).
-template <bool DUAL>
-__device__ __forceinline__ void stage_load(const GemmArgs &g, int k0, uint16_t *sA, uint16_t *sB0, uint16_t *sB1) {
+// A row loaded by this lane into 1 KB block i of the A tile (8 rows of 128 bytes each).
+template <int AR>
+__device__ __forceinline__ int a_block(int i) {
+    return AR == 64 ? 2 * wave_id() + i : (wave_id() & 1);
+}
+
+// Issue the loads of one K stage.  A: AR/8 blocks of 1 KB (with 16 rows, waves 2 and 3
+// repeat the loads of waves 0 and 1, writing identical bytes); B: each wave moves two
+// 1 KB blocks (8 k-rows of 128 bytes) of every weight tile.
+template <bool DUAL, int AR>
+__device__ __forceinline__ void stage_load(const GemmArgs &g, int k0, uint16_t *stage) {
+    using C = GemmCfg<DUAL, AR>;
+    uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
     const int lane = lane_id(), w = wave_id();
     const int r8 = lane >> 3, pc = lane & 7;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int blk = 2 * w + i;  // 1 KB block = 8 rows of 128 bytes
+    for (int i = 0; i < C::A_LOADS; ++i) {
+        const int blk = a_block<AR>(i);
         const int row = 8 * blk + r8;
         lds_dma16(g.arow[i] + k0 + 8 * (pc ^ swa(row)), (MK_L void *)(sA + blk * 512));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int blk = 2 * w + i;
         const int kr = 8 * blk + r8;
         const int lc = pc ^ swb(kr);
         lds_dma16(g.B0 + (size_t)(k0 + kr) * g.ldb + 8 * lc, (MK_L void *)(sB0 + blk * 512));
@@ -520,8 +556,8 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t *p) {
     return (uint32_t)(uintptr_t)(const MK_L uint16_t *)p;
 }
 
-// LDS byte address of this lane's half of a B fragment (rows kbase + l/4, or + 4 for the
-// second half; columns ncol0 + 4*(l%4)).
+// LDS byte address of this lane's half of a B fragment (rows kbase + l/4, columns
+// ncol0 + 4*(l%4)).
 __device__ __forceinline__ uint32_t b_frag_addr(const uint16_t *sB, int kbase, int ncol0) {
     const int l = lane_id() & 15;
     const int k = kbase + (l >> 2);
@@ -531,61 +567,75 @@ __device__ __forceinline__ uint32_t b_frag_addr(const uint16_t *sB, int kbase, i
 
 __device__ __forceinline__ u32x4 join(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
 
-// One K step of 32: the fragment reads are issued together in one asm block that also
-// waits for them (the compiler cannot tell these reads from the DMA writes into other
-// ring buffers, and would otherwise wait for every load in flight), then the MFMAs run.
-template <bool DUAL>
-__device__ __forceinline__ void stage_compute(const uint16_t *sA, const uint16_t *sB0, const uint16_t *sB1, int nrb,
-                                              f32x4 (&acc0)[4], f32x4 (&acc1)[4]) {
+// Fragment reads of one K step of 32 (B halves: b[0..1] for W1 / W2, b[2..3] for W3;
+// A: one fragment per 16-row block).  They are issued together in one asm block that
+// also waits for them: the compiler cannot tell these reads from the DMA writes into
+// other ring buffers and would otherwise wait for every load in flight.
+template <bool DUAL, int AR>
+__device__ __forceinline__ void frag_reads(const uint32_t (&ba)[4], const uint32_t (&aa)[4], u32x2 (&b)[4],
+                                           u32x4 (&a)[4]) {
+    if constexpr (DUAL && AR == 64) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
+            "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
+            "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+            : "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]), "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
+    } else if constexpr (DUAL) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %5\n\tds_read_b64_tr_b16 %1, %6\n\t"
+            "ds_read_b64_tr_b16 %2, %7\n\tds_read_b64_tr_b16 %3, %8\n\t"
+            "ds_read_b128 %4, %9\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(a[0])
+            : "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]), "v"(aa[0]));
+    } else if constexpr (AR == 64) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %6\n\tds_read_b64_tr_b16 %1, %7\n\t"
+            "ds_read_b128 %2, %8\n\tds_read_b128 %3, %9\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(b[0]), "=&v"(b[1]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+            : "v"(ba[0]), "v"(ba[1]), "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
+    } else {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %3\n\tds_read_b64_tr_b16 %1, %4\n\t"
+            "ds_read_b128 %2, %5\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(b[0]), "=&v"(b[1]), "=&v"(a[0])
+            : "v"(ba[0]), "v"(ba[1]), "v"(aa[0]));
+    }
+}
+
+template <bool DUAL, int AR>
+__device__ __forceinline__ void stage_compute(const uint16_t *stage, int nrb, f32x4 (&acc0)[4], f32x4 (&acc1)[4]) {
+    using C = GemmCfg<DUAL, AR>;
+    const uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
         const int kb = 32 * ks + 8 * g;  // this lane group's 8 k values: kb .. kb+7
-        uint32_t aa[4];
+        uint32_t aa[4], ba[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
             const int r = 16 * rb + i;
-            aa[rb] = lds_addr(sA + r * kBK + (((kb >> 3) ^ swa(r)) << 3));
+            aa[rb] = lds_addr(sA + (r % AR) * kBK + (((kb >> 3) ^ swa(r % AR)) << 3));
         }
-        const uint32_t b0l = b_frag_addr(sB0, kb, 16 * w), b0h = b_frag_addr(sB0, kb + 4, 16 * w);
-        u32x2 x0l, x0h, x1l, x1h;
-        u32x4 a0, a1, a2, a3;
-        if constexpr (DUAL) {
-            const uint32_t b1l = b_frag_addr(sB1, kb, 16 * w), b1h = b_frag_addr(sB1, kb + 4, 16 * w);
-            asm volatile(
-                "ds_read_b64_tr_b16 %0, %8\n\t"
-                "ds_read_b64_tr_b16 %1, %9\n\t"
-                "ds_read_b64_tr_b16 %2, %10\n\t"
-                "ds_read_b64_tr_b16 %3, %11\n\t"
-                "ds_read_b128 %4, %12\n\t"
-                "ds_read_b128 %5, %13\n\t"
-                "ds_read_b128 %6, %14\n\t"
-                "ds_read_b128 %7, %15\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(x0l), "=&v"(x0h), "=&v"(x1l), "=&v"(x1h), "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
-                : "v"(b0l), "v"(b0h), "v"(b1l), "v"(b1h), "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
-        } else {
-            asm volatile(
-                "ds_read_b64_tr_b16 %0, %6\n\t"
-                "ds_read_b64_tr_b16 %1, %7\n\t"
-                "ds_read_b128 %2, %8\n\t"
-                "ds_read_b128 %3, %9\n\t"
-                "ds_read_b128 %4, %10\n\t"
-                "ds_read_b128 %5, %11\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(x0l), "=&v"(x0h), "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
-                : "v"(b0l), "v"(b0h), "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
-            x1l = x0l;
-            x1h = x0h;
-        }
-        const u32x4 b0 = join(x0l, x0h), b1 = join(x1l, x1h);
-        const u32x4 av[4] = {a0, a1, a2, a3};
+        ba[0] = b_frag_addr(sB0, kb, 16 * w);
+        ba[1] = b_frag_addr(sB0, kb + 4, 16 * w);
+        ba[2] = DUAL ? b_frag_addr(sB1, kb, 16 * w) : 0u;
+        ba[3] = DUAL ? b_frag_addr(sB1, kb + 4, 16 * w) : 0u;
+        u32x2 b[4];
+        u32x4 a[4];
+        frag_reads<DUAL, AR>(ba, aa, b, a);
+        const u32x4 b0 = join(b[0], b[1]);
+        const u32x4 b1 = DUAL ? join(b[2], b[3]) : b0;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < AR / 16; ++rb) {
             if (rb < nrb) {
-                acc0[rb] = mfma_bf16_16x16x32(av[rb], b0, acc0[rb]);
-                if constexpr (DUAL) acc1[rb] = mfma_bf16_16x16x32(av[rb], b1, acc1[rb]);
+                acc0[rb] = mfma_bf16_16x16x32(a[rb], b0, acc0[rb]);
+                if constexpr (DUAL) acc1[rb] = mfma_bf16_16x16x32(a[rb], b1, acc1[rb]);
             }
         }
     }
@@ -606,11 +656,10 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-constexpr int kStages = kStagesLds;  // LDS ring depth of the GroupGEMM tiles
-
-template <bool DUAL>
+template <bool DUAL, int AR>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], f32x4 (&acc1)[4], GemmSmem &s) {
-    constexpr int kLoadsPerStage = DUAL ? 6 : 4;  // global_load_lds instructions per wave per stage
+    using C = GemmCfg<DUAL, AR>;
+    constexpr int NS = C::NS;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
         acc0[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -618,43 +667,43 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], 
     }
     const int nrb = (ga.nrows + 15) / 16;
     const int nk = ga.K / kBK;
-    // prologue: stages 0 .. kStages-2 in flight (empty stages keep the wait counts uniform)
 #pragma unroll
-    for (int p = 0; p < kStages - 1; ++p)
-        if (p < nk) stage_load<DUAL>(ga, p * kBK, s.A[p], s.B0[p], s.B1[p]);
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < nk) stage_load<DUAL, AR>(ga, p * kBK, s.ring + p * C::STAGE_ELEMS);
+    int slot = 0;  // ring slot of stage st
     for (int st = 0; st < nk; ++st) {
-        // stage st has landed once at most (kStages - 2) newer stages are outstanding
-        if (st + kStages - 2 < nk)
-            wait_vm<(kStages - 2) * kLoadsPerStage>();
+        // stage st has landed once at most NS - 2 newer stages are outstanding
+        if (st + NS - 2 < nk)
+            wait_vm<(NS - 2) * C::LOADS>();
         else
             wait_vm<0>();
-        bare_barrier();  // every wave's part of stage st is in LDS; buffer (st-1) is free
-        const int nxt = st + kStages - 1;
+        bare_barrier();  // every wave's part of stage st is in LDS; the slot of st-1 is free
+        const int nxt = st + NS - 1;
         if (nxt < nk) {
-            const int b = nxt % kStages;
-            stage_load<DUAL>(ga, nxt * kBK, s.A[b], s.B0[b], s.B1[b]);
+            const int ns = slot == 0 ? NS - 1 : slot - 1;  // (st - 1) mod NS
+            stage_load<DUAL, AR>(ga, nxt * kBK, s.ring + ns * C::STAGE_ELEMS);
         }
-        const int b = st % kStages;
-        stage_compute<DUAL>(s.A[b], s.B0[b], s.B1[b], nrb, acc0, acc1);
+        stage_compute<DUAL, AR>(s.ring + slot * C::STAGE_ELEMS, nrb, acc0, acc1);
+        slot = slot == NS - 1 ? 0 : slot + 1;
     }
     wait_vm<0>();
-    __syncthreads();  // the LDS ring may be reused by the next task
+    __syncthreads();  // the ring may be reused by the next task
 }
 
-// Row r of this lane's A blocks: 8 * (2w + i) + lane / 8.  Rows past the tile's end
-// re-read its last row (every wave must issue the same number of loads per stage for the
-// vmcnt-based waits); their outputs are discarded.
+// Row of 1 KB A block i loaded by this lane (8 rows of 128 bytes per block).  Rows past
+// the tile's end re-read its last row (every wave must issue the same number of loads
+// per stage for the vmcnt-based waits); their outputs are discarded.
+template <int AR>
 __device__ __forceinline__ int a_row(int i, int nrows) {
-    return min(8 * (2 * wave_id() + i) + (lane_id() >> 3), nrows - 1);
+    return min(8 * a_block<AR>(i) + (lane_id() >> 3), nrows - 1);
 }
 
-// GEMM1 tile: h[rows, n0:n0+64] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
-// where row p of the tile is token perm[p] / k of x.
-__device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
+template <int AR>
+__device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0, int nrows, int n) {
     GemmArgs ga;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int tok = P.perm[row0 + a_row(i, nrows)] / P.k;
+        const int tok = P.perm[row0 + a_row<AR>(i, nrows)] / P.k;
         ga.arow[i] = P.x + (size_t)tok * P.d;
     }
     ga.nrows = nrows;
@@ -663,47 +712,106 @@ __device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &P, int e
     ga.ldb = P.f;
     ga.K = P.d;
     f32x4 acc0[4], acc1[4];
-    gemm_tile<true>(ga, acc0, acc1, g_sm.u.g);
+    gemm_tile<true, AR>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
     const int col = n * kBN + 16 * w + j;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < AR / 16; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * rb + 4 * g + r;
+            const float gv = acc0[rb][r], uv = acc1[rb][r];
+            const uint32_t hv = f32_to_bf16(gv / (1.0f + __expf(-gv)) * uv);
+            // columns col and col+1 sit in lanes j and j+1: even lanes store both
+            const uint32_t nb = (uint32_t)__shfl_xor((int)hv, 1, 64);
+            if (row < nrows && (j & 1) == 0)
+                pub((MK_G uint32_t *)(P.h + (size_t)(row0 + row) * P.f + col), hv | (nb << 16));
+        }
+    }
+}
+
+// Down-projection tile over f range sp.  With S > 1 splits, every split stores its partial
+// result in y[sp]; the split that finishes a tile last (a per-tile counter) adds the S
+// partials in split order and writes the sum to y[0], so the result does not depend on
+// which split finished last.  With S = 1 the tile writes y[0] directly.
+template <int AR>
+__device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0, int nrows, int n, int sp,
+                                           int mt) {
+    const int kl = P.f / P.S;  // reduction range of this split: [sp*kl, (sp+1)*kl)
+    GemmArgs ga;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ga.arow[i] = P.h + (size_t)(row0 + a_row<AR>(i, nrows)) * P.f + (size_t)sp * kl;
+    ga.nrows = nrows;
+    ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)sp * kl * P.d + (size_t)n * kBN;
+    ga.B1 = ga.B0;
+    ga.ldb = P.d;
+    ga.K = kl;
+    f32x4 acc0[4], acc1[4];
+    gemm_tile<false, AR>(ga, acc0, acc1, g_sm.u.g);
+    const int lane = lane_id(), w = wave_id();
+    const int g = lane >> 4, j = lane & 15;
+    const int col = n * kBN + 16 * w + j;
+    const size_t split_stride = (size_t)P.B * P.k * P.d;  // floats between partial buffers
+    MK_G float *ys = P.y + (size_t)sp * split_stride;
+#pragma unroll
+    for (int rb = 0; rb < AR / 16; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * rb + 4 * g + r;
+            if (row < nrows) pub(ys + (size_t)(row0 + row) * P.d + col, acc0[rb][r]);
+        }
+    }
+    if (P.S == 1) return;
+    // count finished splits of this tile; the last one reduces
+    wg_stores_done();
+    if (threadIdx.x == 0) {
+        MK_G int *ctr = P.red_ctr + (size_t)mt * P.NB2 + n;
+        const int old = add_relaxed(ctr, 1);
+        const bool last = old == P.S - 1;
+        if (last) st_relaxed(ctr, 0);  // rest state for the next forward
+        g_sm.bcast[2] = last ? 1 : 0;
+    }
+    __syncthreads();
+    const bool last = g_sm.bcast[2] != 0;
+    __syncthreads();
+    if (!last) return;
+    fence_acquire();
+#pragma unroll
+    for (int rb = 0; rb < AR / 16; ++rb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rb + 4 * g + r;
             if (row < nrows) {
-                const float gv = acc0[rb][r], uv = acc1[rb][r];
-                const float hv = gv / (1.0f + __expf(-gv)) * uv;
-                P.h[(size_t)(row0 + row) * P.f + col] = f32_to_bf16(hv);
+                const size_t o = (size_t)(row0 + row) * P.d + col;
+                float sum = 0.0f;
+                for (int q = 0; q < P.S; ++q) {
+                    const float v = q == sp ? acc0[rb][r] : P.y[(size_t)q * split_stride + o];
+                    sum = q == 0 ? v : sum + v;
+                }
+                pub(P.y + o, sum);
             }
         }
     }
 }
 
-// GEMM2 tile: y[rows, n0:n0+64] = h[rows, :] W2[e][:, n0:n0+64] in fp32.
-__device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n) {
-    GemmArgs ga;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) ga.arow[i] = P.h + (size_t)(row0 + a_row(i, nrows)) * P.f;
-    ga.nrows = nrows;
-    ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)n * kBN;
-    ga.B1 = ga.B0;
-    ga.ldb = P.d;
-    ga.K = P.f;
-    f32x4 acc0[4], acc1[4];
-    gemm_tile<false>(ga, acc0, acc1, g_sm.u.g);
-    const int lane = lane_id(), w = wave_id();
-    const int g = lane >> 4, j = lane & 15;
-    const int col = n * kBN + 16 * w + j;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * rb + 4 * g + r;
-            if (row < nrows) P.y[(size_t)(row0 + row) * P.d + col] = acc0[rb][r];
-        }
-    }
+// GEMM1 tile: h[rows, n0:n0+64] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
+// where row p of the tile is token perm[p] / k of x.  The tile variant is chosen from the
+// tile's actual row count.
+__device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
+    if (nrows <= 16)
+        gemm1_tile<16>(P, e, row0, nrows, n);
+    else
+        gemm1_tile<64>(P, e, row0, nrows, n);
+}
+
+// GEMM2 tile: y[sp][rows, n0:n0+64] = h[rows, f range sp] W2[e][f range sp, n0:n0+64], fp32.
+__device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n,
+                                                     int sp, int mt) {
+    if (nrows <= 16)
+        gemm2_tile<16>(P, e, row0, nrows, n, sp, mt);
+    else
+        gemm2_tile<64>(P, e, row0, nrows, n, sp, mt);
 }
 
 // ------------------------------------------------------------------------------ COMBINE
@@ -721,15 +829,22 @@ __device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int
     __syncthreads();
     const int nq = P.d / 4;
     const int items = nb * nq;
-#pragma unroll 4
     for (int it = threadIdx.x; it < items; it += kThreads) {
         const int bb = it / nq, q = it - bb * nq;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < k; ++i) {
-            const f32x4 yv = *(const MK_G f32x4 *)(P.y + (size_t)cs.row[bb * k + i] * P.d + 4 * q);
-            const float wgt = cs.w[bb * k + i];
+        // all k rows of this item in flight before any is used
+        f32x4 yv[kMaxK];
 #pragma unroll
-            for (int z = 0; z < 4; ++z) acc[z] = fmaf(wgt, yv[z], acc[z]);
+        for (int i = 0; i < kMaxK; ++i)
+            if (i < k) yv[i] = *(const MK_G f32x4 *)(P.y + (size_t)cs.row[bb * k + i] * P.d + 4 * q);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kMaxK; ++i) {
+            if (i < k) {
+                const float wgt = cs.w[bb * k + i];
+#pragma unroll
+                for (int z = 0; z < 4; ++z) acc[z] = fmaf(wgt, yv[i][z], acc[z]);
+            }
         }
         const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
         const uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
@@ -753,15 +868,16 @@ __device__ __forceinline__ void count_task(const MK_C Params &P, int kind) {
 }
 
 // Debug trace (MOE_MK_DEBUG_TRACE): per task {g | kind << 32 | workgroup << 40, obtained,
-// dependencies satisfied, finished} in real-time ticks.
+// dependencies satisfied, finished, compute ended} in real-time ticks.
 __device__ __forceinline__ void trace_task(const MK_C Params &P, int g, int kind, unsigned long long t0,
-                                           unsigned long long t1) {
+                                           unsigned long long t1, unsigned long long t2) {
     if ((P.debug & 2) && threadIdx.x == 0) {
-        MK_G long long *e = P.trace + (size_t)g * 4;
+        MK_G long long *e = P.trace + (size_t)g * 8;
         e[0] = (long long)g | ((long long)kind << 32) | ((long long)blockIdx.x << 40);
         e[1] = (long long)t0;
         e[2] = (long long)t1;
         e[3] = (long long)now_ticks();
+        e[4] = (long long)t2;
     }
 }
 
@@ -771,12 +887,13 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
     if (g < bs.K) {  // ---------------------------------------------------------- ROUTE
         const int tg = g / P.nEB, eb = g - tg * P.nEB;
         task_route(P, tg, eb);
+        const unsigned long long t2 = now_ticks();
         count_task(P, K_ROUTE);
         const int t = tg / route_groups_per_tile(P);
         int delta = -1;
         if (dyn && (tg % route_groups_per_tile(P)) == 0 && eb == 0) delta += route_tasks_of_tile(P, t);
         if (wg_notify(P, P.ev_logit + t, delta) && dyn) wg_push_range(P, bs.K + t, 1);
-        trace_task(P, g, K_ROUTE, t0, t0);
+        trace_task(P, g, K_ROUTE, t0, t0, t2);
         return true;
     }
     if (g < bs.S) {  // ---------------------------------------------------------- TOPK
@@ -787,11 +904,12 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         }
         const unsigned long long t1 = now_ticks();
         task_topk(P, t);
+        const unsigned long long t2 = now_ticks();
         count_task(P, K_TOPK);
         int delta = -1;
         if (dyn && t == 0) delta += P.T;
         if (wg_notify(P, P.ctl + CTL_EV_TOPK, delta) && dyn) wg_push_range(P, bs.S, 1);
-        trace_task(P, g, K_TOPK, t0, t1);
+        trace_task(P, g, K_TOPK, t0, t1, t2);
         return true;
     }
     if (g == bs.S) {  // --------------------------------------------------------- SCAN
@@ -801,6 +919,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         }
         const unsigned long long t1 = now_ticks();
         const int mt_total = task_scan(P);
+        const unsigned long long t2 = now_ticks();
         count_task(P, K_SCAN);
         complete_bases(P, bs, mt_total);
         wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
@@ -810,7 +929,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
                 st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64),
                              ((unsigned long long)(uint32_t)g_sm.epoch << 32) | (uint32_t)bs.total);
         }
-        trace_task(P, g, K_SCAN, t0, t1);
+        trace_task(P, g, K_SCAN, t0, t1, t2);
         return true;
     }
     if (g < bs.M1) {  // --------------------------------------------------------- GROUP
@@ -818,6 +937,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) return false;
         const unsigned long long t1 = now_ticks();
         task_group(P, t);
+        const unsigned long long t2 = now_ticks();
         count_task(P, K_GROUP);
         GroupSmem &gr = g_sm.u.gr;
         if (threadIdx.x == 0) gr.nfired = 0;
@@ -833,7 +953,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         for (int e = threadIdx.x; e < P.E; e += kThreads) {
             const int cnt = __popcll(gr.mask[e]);
             if (cnt && e != skip) {
-                const int old = add_acq_rel(P.ev_exp + e, -cnt);
+                const int old = add_relaxed(P.ev_exp + e, -cnt);
                 if (dyn && old == cnt) gr.fired[atomicAdd(&gr.nfired, 1)] = e;
             }
         }
@@ -846,7 +966,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
                 wg_push_range(P, bs.M1 + m0 * P.NB1, (m1 - m0) * P.NB1);
             }
         }
-        trace_task(P, g, K_GROUP, t0, t1);
+        trace_task(P, g, K_GROUP, t0, t1, t2);
         return true;
     }
     if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
@@ -857,20 +977,24 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         if (!dyn && !wg_wait_zero(P, P.ev_exp + e)) return false;
         const unsigned long long t1 = now_ticks();
         task_gemm1(P, e, P.mt_row0[mt], P.mt_rows[mt], n);
+        const unsigned long long t2 = now_ticks();
         count_task(P, K_GEMM1);
-        if (wg_notify(P, P.ev_h + mt, -1) && dyn) wg_push_range(P, bs.M2 + mt * P.NB2, P.NB2);
-        trace_task(P, g, K_GEMM1, t0, t1);
+        const int q = mt * P.S + n / (P.NB1 / P.S);  // (row tile, f range) this tile feeds
+        if (wg_notify(P, P.ev_h + q, -1) && dyn) wg_push_range(P, bs.M2 + q * P.NB2, P.NB2);
+        trace_task(P, g, K_GEMM1, t0, t1, t2);
         return true;
     }
     if (g < bs.C) {  // ---------------------------------------------------------- GEMM2
         const int i = g - bs.M2;
-        const int mt = i / P.NB2, n = i - mt * P.NB2;
-        if (!dyn && !wg_wait_zero(P, P.ev_h + mt)) return false;
+        const int q = i / P.NB2, n = i - q * P.NB2;  // q = mt * S + split
+        const int mt = q / P.S, sp = q - mt * P.S;
+        if (!dyn && !wg_wait_zero(P, P.ev_h + q)) return false;
         const unsigned long long t1 = now_ticks();
-        task_gemm2(P, P.mt_expert[mt], P.mt_row0[mt], P.mt_rows[mt], n);
+        task_gemm2(P, P.mt_expert[mt], P.mt_row0[mt], P.mt_rows[mt], n, sp, mt);
+        const unsigned long long t2 = now_ticks();
         count_task(P, K_GEMM2);
         if (wg_notify(P, P.ctl + CTL_EV_Y, -1) && dyn) wg_push_range(P, bs.C, P.nC);
-        trace_task(P, g, K_GEMM2, t0, t1);
+        trace_task(P, g, K_GEMM2, t0, t1, t2);
         return true;
     }
     {  // ------------------------------------------------------------------------ COMBINE
@@ -878,9 +1002,10 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_Y)) return false;
         const unsigned long long t1 = now_ticks();
         task_combine(P, c);
+        const unsigned long long t2 = now_ticks();
         count_task(P, K_COMBINE);
         __syncthreads();
-        trace_task(P, g, K_COMBINE, t0, t1);
+        trace_task(P, g, K_COMBINE, t0, t1, t2);
         return true;
     }
 }
@@ -920,7 +1045,10 @@ __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
                         break;
                     }
                 }
-                __builtin_amdgcn_s_sleep(1);
+                if (it < 64)
+                    __builtin_amdgcn_s_sleep(1);
+                else
+                    __builtin_amdgcn_s_sleep(8);
             }
             fence_acquire();
         }
@@ -966,9 +1094,9 @@ __global__ void __launch_bounds__(kThreads, 2) moe_megakernel(Params Parg) {
     }
     // Leave: the last workgroup out puts the control block back to its rest state.
     __syncthreads();
+    wave_drain_vm();
     if (threadIdx.x == 0) {
-        fence_release();
-        const int old = add_acq_rel(P.ctl + CTL_EXIT, 1);
+        const int old = add_relaxed(P.ctl + CTL_EXIT, 1);
         if (old == (int)gridDim.x - 1) {
             if (ld_relaxed(P.ctl + CTL_ERR) == 0) {
                 st_relaxed(P.ctl + CTL_QHEAD, 0);
@@ -976,7 +1104,7 @@ __global__ void __launch_bounds__(kThreads, 2) moe_megakernel(Params Parg) {
                 st_relaxed(P.ctl + CTL_EV_SCAN, 1);
             }
             st_relaxed(P.ctl + CTL_EXIT, 0);
-            st_release(P.ctl + CTL_EPOCH, g_sm.epoch + 1);
+            st_relaxed(P.ctl + CTL_EPOCH, g_sm.epoch + 1);
         }
     }
 }

@@ -59,6 +59,19 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // (each expert-weight row loaded serves four tokens).  A router task covers 4 waves.
 inline int route_tpw(int64_t B) { return B <= 512 ? 1 : 4; }
 
+// K splits S of the down projection: at small batches with a long f, each down-projection
+// tile covers f/S of the reduction (partial results summed in a fixed order by the
+// combine), so tiles are smaller and each split can start as soon as the gate/up tiles of
+// its f range are done.  S > 1 only when B*k <= 1024 (bounds the partial buffers).
+inline int down_splits(const Shape &s, int64_t B) {
+    const int64_t a = B * s.k;
+    const int64_t nb1 = s.f / kBN;
+    if (a <= 1024 && s.f >= 8192 && nb1 % 4 == 0) return 4;
+    if (a <= 1024 && s.f >= 4096 && nb1 % 2 == 0) return 2;
+    return 1;
+}
+constexpr int kMaxSplits = 4;
+
 // Task counts that depend on B only.
 struct Counts {
     int64_t T;      // top-k / grouping tiles
@@ -69,6 +82,7 @@ struct Counts {
     int64_t nC;     // combine tasks
     int64_t mt_cap; // upper bound of sum_e ceil(hist[e] / kBM)
     int64_t NB1, NB2;
+    int64_t S;      // down-projection K splits
     int64_t q_cap;  // upper bound of the pushed tasks of one forward
     int64_t nR_max; // upper bound of the router tasks of any batch up to B
 };
@@ -85,7 +99,8 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     c.mt_cap = a / kBM + (a < s.E ? a : s.E) + 1;
     c.NB1 = s.f / kBN;
     c.NB2 = s.d / kBN;
-    c.q_cap = 2 * c.T + 1 + c.mt_cap * (c.NB1 + c.NB2) + c.nC + 64;
+    c.S = down_splits(s, B);
+    c.q_cap = 2 * c.T + 1 + c.mt_cap * (c.NB1 + kMaxSplits * c.NB2) + c.nC + 64;
     c.nR_max = ceil_div(B, 4) * c.nEB;
     return c;
 }
@@ -93,7 +108,7 @@ inline Counts make_counts(const Shape &s, int64_t B) {
 // Byte offsets of every workspace array, for a workspace sized for B = cap tokens.
 struct Layout {
     size_t ctl, ev_logit, ev_exp, ev_h, logits, topk_idx, topk_w, tile_hist, tile_off, hist, indptr,
-        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, h, y, qslots, trace, total;
+        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, h, y, red_ctr, qslots, trace, total;
     int64_t cap;
 };
 
@@ -113,7 +128,7 @@ inline Layout make_layout(const Shape &s, int64_t cap) {
     L.ctl = take(CTL_WORDS * 4);
     L.ev_logit = take((size_t)c.T * 4);
     L.ev_exp = take((size_t)s.E * 4);
-    L.ev_h = take((size_t)c.mt_cap * 4);
+    L.ev_h = take((size_t)c.mt_cap * kMaxSplits * 4);
     L.logits = take((size_t)cap * s.E * 4);
     L.topk_idx = take((size_t)A * 4);
     L.topk_w = take((size_t)A * 4);
@@ -128,9 +143,12 @@ inline Layout make_layout(const Shape &s, int64_t cap) {
     L.perm = take((size_t)A * 4);
     L.inv = take((size_t)A * 4);
     L.h = take((size_t)A * s.f * 2);
-    L.y = take((size_t)A * s.d * 4);
+    // y holds S partial results of B*k rows each; S > 1 only when B*k <= 1024
+    const int64_t y_rows = A > kMaxSplits * (A < 1024 ? A : 1024) ? A : kMaxSplits * (A < 1024 ? A : 1024);
+    L.y = take((size_t)y_rows * s.d * 4);
+    L.red_ctr = take((size_t)c.mt_cap * c.NB2 * 4);
     L.qslots = take((size_t)c.q_cap * 8);
-    L.trace = take((size_t)(c.q_cap + c.nR_max) * 4 * 8);
+    L.trace = take((size_t)(c.q_cap + c.nR_max) * 8 * 8);
     L.total = o;
     return L;
 }
@@ -145,7 +163,7 @@ struct Params {
     int B, E, k, d, f;
     int sched;       // 0 static, 1 dynamic
     int debug;       // MOE_MK_DEBUG_* bits
-    int nR, nTG, nEB, T, nC, NB1, NB2, tpw;
+    int nR, nTG, nEB, T, nC, NB1, NB2, tpw, S;
     int q_cap, mt_cap;
     long long watchdog;  // real-time ticks (100 MHz)
     MK_G int *ctl, *ev_logit, *ev_exp, *ev_h;
@@ -156,7 +174,8 @@ struct Params {
     MK_G uint16_t *h;
     MK_G float *y;
     MK_G unsigned long long *qslots;
-    MK_G long long *trace;  // 4 int64 per task when tracing is on
+    MK_G int *red_ctr;      // per down-projection tile: splits finished (rest 0)
+    MK_G long long *trace;  // 8 int64 per task when tracing is on
 };
 
 }  // namespace mk

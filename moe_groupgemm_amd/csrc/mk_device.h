@@ -28,9 +28,16 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------------------- atomics
-// Event counters live in device memory shared by all XCDs, so every access is at agent
-// scope.  A notify is an atomic add with release ordering (a decrement); a wait polls
-// with relaxed loads and finishes with an acquire fence.
+// Event counters and every value one task publishes to another live in device memory
+// shared by the 8 XCDs, whose L2 caches are not coherent with each other.  Published
+// values are therefore written with agent-scope stores (coherent across XCDs: the
+// same instruction the compiler uses for a relaxed agent-scope atomic store), so a
+// notification needs no L2 write-back: each wave waits for its stores to complete
+// (vmcnt 0), the workgroup synchronises, then one thread updates the counter.  A wait
+// polls the counter with agent-scope loads and ends with an agent-scope acquire fence,
+// which invalidates the CU's L1 and the XCD's non-coherent L2 lines.  (An agent-scope
+// release fence would write back the whole L2 on every notification; measured on
+// MI355X it costs several microseconds per task, the acquire a fraction of one.)
 
 __device__ __forceinline__ int ld_relaxed(const MK_G int *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -38,20 +45,22 @@ __device__ __forceinline__ int ld_relaxed(const MK_G int *p) {
 __device__ __forceinline__ void st_relaxed(MK_G int *p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_release(MK_G int *p, int v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ int add_relaxed(MK_G int *p, int v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int add_acq_rel(MK_G int *p, int v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 __device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
-// Wait until this wave's outstanding global stores (and loads) have completed.
+// Wait until this wave's outstanding vector memory operations (stores included) completed.
 __device__ __forceinline__ void wave_drain_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); /* vmcnt(0) */ }
+
+// Publishing stores (agent scope).
+__device__ __forceinline__ void pub(MK_G int *p, int v) { st_relaxed(p, v); }
+__device__ __forceinline__ void pub(MK_G float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void pub(MK_G uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ unsigned long long ld_relaxed64(const MK_G unsigned long long *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -72,7 +81,12 @@ __device__ __forceinline__ bool spin_until(const MK_G int *p, int target, MK_G i
     if (ld_relaxed(p) == target) return true;
     const unsigned long long t0 = now_ticks();
     for (unsigned it = 1;; ++it) {
-        __builtin_amdgcn_s_sleep(1);
+        // back off after a while: hundreds of idle workgroups polling one counter would
+        // otherwise crowd the memory channel it lives on
+        if (it < 64)
+            __builtin_amdgcn_s_sleep(1);
+        else
+            __builtin_amdgcn_s_sleep(8);
         if (ld_relaxed(p) == target) return true;
         if ((it & 31u) == 0) {
             if (ld_relaxed(ctl + CTL_ERR) != 0) return false;

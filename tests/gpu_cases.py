@@ -51,8 +51,19 @@ def ctl_words(layer, B):
     return layer.routing(B)["ctl"].cpu().numpy()
 
 
-def expected_task_counts(hist, B, E, d, f):
+def down_splits(B, k, f):
+    """K splits of the down projection the library uses at this batch size."""
+    a, nb1 = B * k, f // 64
+    if a <= 1024 and f >= 8192 and nb1 % 4 == 0:
+        return 4
+    if a <= 1024 and f >= 4096 and nb1 % 2 == 0:
+        return 2
+    return 1
+
+
+def expected_task_counts(hist, B, E, d, f, k):
     mt = int(sum((int(h) + 63) // 64 for h in hist))
     tpw = 1 if B <= 512 else 4  # router tokens per wave; a router task has 4 waves
+    S = down_splits(B, k, f)
     return {"route": -(-B // (4 * tpw)) * -(-E // 16), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
-            "gemm1": mt * (f // 64), "gemm2": mt * (d // 64), "combine": -(-B // 4)}
+            "gemm1": mt * (f // 64), "gemm2": mt * S * (d // 64), "combine": -(-B // 4)}

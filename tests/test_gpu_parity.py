@@ -13,7 +13,7 @@ import torch
 
 import moe_groupgemm_amd as mk
 import oracle
-from gpu_cases import (check_out, check_routing, ctl_words, dev_inputs, expected_task_counts, log,
+from gpu_cases import (check_out, check_routing, ctl_words, dev_inputs, down_splits, expected_task_counts, log,
                        routing_numpy)
 from moe_inputs import (CONFIGS, Config, bf16_bits_to_f32, device_weights, device_x, expert_weights, make_bias,
                         make_wr, make_x, small_case, to_torch_bf16)
@@ -107,6 +107,27 @@ def test_zipf_bias_small():
         full_check(x, Wr, bias, W1, W3, W2, 4, sched, f"zipf small {SNAME[sched]}")
 
 
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+@pytest.mark.parametrize("f,S", [(4096, 2), (8192, 4)])
+def test_down_projection_k_splits(f, S, sched):
+    # small batches with a long f split the down projection's reduction into S ranges
+    B, d, E, k = 21, 128, 4, 2
+    assert down_splits(B, k, f) == S
+    log(f"down-projection splits S={S} f={f} sched={SNAME[sched]}")
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=900 + S)
+    full_check(x, Wr, bias, W1, W3, W2, k, sched, f"S={S}")
+
+
+def test_down_projection_splits_static_dynamic_identical():
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(13, 128, 8192, 4, 2, seed=901)
+    outs = []
+    for sched in SCHEDS:
+        layer, out, got = run_small(x, Wr, bias, W1, W3, W2, 2, sched)
+        outs.append(out)
+        layer.close()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
 def test_zero_batch_enqueues_nothing():
     cfg, x, Wr, bias, W1, W3, W2 = small_case(4, 128, 128, 4, 2, seed=3)
     tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
@@ -146,7 +167,7 @@ def test_rest_state_and_task_counts(sched):
     assert c[1] == 0 and c[3] == 0 and c[4] == 0     # exit counter and queue at rest
     assert c[5] == 0 and c[6] == 1 and c[7] == 0     # events at rest (scan event re-armed)
     hist = routing_numpy(layer, B)["hist"]
-    exp = expected_task_counts(hist, B, E, d, f)
+    exp = expected_task_counts(hist, B, E, d, f, 2)
     delta = c[16:23] - before[16:23]
     names = ["route", "topk", "scan", "group", "gemm1", "gemm2", "combine"]
     for i, n in enumerate(names):
