@@ -96,11 +96,11 @@ def trace_report(layer, x, out, B):
     tpw = 1 if B <= 512 else 4
     nR = -(-B // (4 * tpw)) * -(-E // 16)
     T = -(-B // 64)
-    mt = int(ctl[9])
+    mt = int(ctl[mk.CTL["mt_total"]])
     a = B * k
     S = 4 if (a <= 1024 and f >= 8192 and (f // 64) % 4 == 0) else \
         2 if (a <= 1024 and f >= 4096 and (f // 64) % 2 == 0) else 1
-    total = nR + 2 * T + 1 + mt * (f // 64 + S * (d // 64)) + -(-B // 4)
+    total = nR + 2 * T + 1 + mt * (f // 64 + S * (d // 64)) + -(-B // 4) * -(-d // 1024)
     tr = tr[:total]
     kind = (tr[:, 0] >> 32) & 0xFF
     wg = tr[:, 0] >> 40

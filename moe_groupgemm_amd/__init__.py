@@ -25,6 +25,10 @@ MOE_MK_ERR_UNINIT = 8
 MOE_MK_DEBUG_DROP_NOTIFY = 1
 MOE_MK_DEBUG_TRACE = 2
 TASK_KINDS = ("route", "topk", "scan", "group", "gemm1", "gemm2", "combine")
+# control block words (see moe_mk_routing_view)
+CTL_WORDS = 256
+CTL = {"epoch": 0, "exit": 1, "err": 2, "ev_topk": 5, "ev_scan": 6, "magic": 8, "mt_total": 9,
+       "qhead": 32, "qtail": 64, "hhead": 96, "htail": 128, "ev_y": 160, "dbg": 192}
 
 _lib = None
 
@@ -161,7 +165,7 @@ def moe_mk_routing_view(plan: int, B: int, ws) -> dict:
             "perm": part(v.perm, B * k, torch.int32, (B * k,)),
             "inv": part(v.inv, B * k, torch.int32, (B * k,)),
             "logits": part(v.logits, B * E, torch.float32, (B, E)),
-            "ctl": part(v.ctl, 64, torch.int32, (64,))}
+            "ctl": part(v.ctl, CTL_WORDS, torch.int32, (CTL_WORDS,))}
 
 
 def moe_mk_trace_view(plan: int, B: int, ws):

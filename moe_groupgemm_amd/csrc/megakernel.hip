@@ -69,10 +69,18 @@ struct Smem {
 // still address it as LDS).
 __shared__ Smem g_sm;
 
-// Phase bases of the global task index g.
+// Layout of the global task index g (the static schedule walks it in order; dynamic
+// pushes use the same indices):
+//   [ROUTE][TOPK][SCAN][GROUP] then the GroupGEMM tiles by f range s (S ranges):
+//   [G1(0)] [G1(1)] [G2(0)] [G1(2)] [G2(1)] ... [G1(S-1)] [G2(S-2)] [G2(S-1)] [COMBINE]
+// where G1(s) holds the gate/up tiles whose columns fall in f range s (for every row
+// tile, Q = NB1/S per row tile) and G2(s) the down-projection tiles reducing over f range
+// s (NB2 per row tile).  Each G2 block comes one G1 block after the G1 block it consumes,
+// so the two GEMMs overlap instead of running as two phases.
 struct Bases {
-    int K, S, G, M1, M2, C, total;
-    bool known;  // M2/C/total are known once the scan has run
+    int K, S, G, M1, C, total;
+    int q1, q2;  // tasks per G1(s) block and per G2(s) block
+    bool known;  // M1-relative layout known once the scan has run
 };
 
 __device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
@@ -81,16 +89,54 @@ __device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
     b.S = b.K + P.T;
     b.G = b.S + 1;
     b.M1 = b.G + P.T;
-    b.M2 = b.C = b.total = 0x7fffffff;
+    b.C = b.total = 0x7fffffff;
+    b.q1 = b.q2 = 0;
     b.known = false;
     return b;
 }
 
 __device__ __forceinline__ void complete_bases(const MK_C Params &P, Bases &b, int mt_total) {
-    b.M2 = b.M1 + mt_total * P.NB1;
-    b.C = b.M2 + mt_total * P.S * P.NB2;
+    b.q1 = mt_total * (P.NB1 / P.S);
+    b.q2 = mt_total * P.NB2;
+    b.C = b.M1 + P.S * (b.q1 + b.q2);
     b.total = b.C + P.nC;
     b.known = true;
+}
+
+__device__ __forceinline__ int base_g1(const Bases &b, int s) {
+    return s == 0 ? b.M1 : b.M1 + b.q1 + (s - 1) * (b.q1 + b.q2);
+}
+__device__ __forceinline__ int base_g2(const Bases &b, int s, int S) {
+    return s < S - 1 ? base_g1(b, s + 1) + b.q1 : b.M1 + S * b.q1 + (S - 1) * b.q2;
+}
+
+// Decode a GroupGEMM task index: returns 1 for gate/up, 2 for down; sets the f range s and
+// the index j inside its block.
+__device__ __forceinline__ int decode_gemm(const Bases &b, int S, int g, int &s, int &j) {
+    int o = g - b.M1;
+    if (o < b.q1) {
+        s = 0;
+        j = o;
+        return 1;
+    }
+    o -= b.q1;
+    for (int r = 1; r < S; ++r) {
+        if (o < b.q1) {
+            s = r;
+            j = o;
+            return 1;
+        }
+        o -= b.q1;
+        if (o < b.q2) {
+            s = r - 1;
+            j = o;
+            return 2;
+        }
+        o -= b.q2;
+    }
+    s = S - 1;
+    j = o;
+    return 2;
 }
 
 // ------------------------------------------------------------------------------ event helpers (workgroup level)
@@ -130,8 +176,7 @@ __device__ __forceinline__ void wg_push_range(const MK_C Params &P, int g0, int 
         return;
     }
     const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
-    for (int i = threadIdx.x; i < cnt; i += kThreads)
-        st_relaxed64(P.qslots + s0 + i, tag | (uint32_t)(g0 + i));
+    for (int i = threadIdx.x; i < cnt; i += kThreads) st_relaxed64(P.qslots + s0 + i, tag | (uint32_t)(g0 + i));
 }
 
 // Notify one counter: the group's published stores complete, then thread 0 adds delta
@@ -816,10 +861,12 @@ __device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &P, int e
 
 // ------------------------------------------------------------------------------ COMBINE
 // out[b, :] = bf16( sum_{i<k} w[b,i] * y[inv[b*k+i], :] ), slot order, fp32, for
-// kCombineTokens tokens; (token, 4-column group) items are spread over the workgroup.
+// a combine task: kCombineTokens tokens x kCombineCols columns (4 columns per thread).
 __device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int c) {
     CombineSmem &cs = g_sm.u.c;
-    const int b_lo = c * kCombineTokens;
+    const int nchunks = (P.d + kCombineCols - 1) / kCombineCols;
+    const int grp = c / nchunks, chunk = c - grp * nchunks;
+    const int b_lo = grp * kCombineTokens;
     const int nb = min(kCombineTokens, P.B - b_lo);
     const int k = P.k;
     for (int i = threadIdx.x; i < nb * k; i += kThreads) {
@@ -827,28 +874,28 @@ __device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int
         cs.w[i] = P.topk_w[(size_t)b_lo * k + i];
     }
     __syncthreads();
-    const int nq = P.d / 4;
-    const int items = nb * nq;
-    for (int it = threadIdx.x; it < items; it += kThreads) {
-        const int bb = it / nq, q = it - bb * nq;
-        // all k rows of this item in flight before any is used
-        f32x4 yv[kMaxK];
+    const int q = (chunk * kCombineCols) / 4 + threadIdx.x;  // this thread's 4-column group
+    if (4 * q < P.d) {
+        for (int bb = 0; bb < nb; ++bb) {
+            // all k rows of this token in flight before any is used
+            f32x4 yv[kMaxK];
 #pragma unroll
-        for (int i = 0; i < kMaxK; ++i)
-            if (i < k) yv[i] = *(const MK_G f32x4 *)(P.y + (size_t)cs.row[bb * k + i] * P.d + 4 * q);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < kMaxK; ++i)
+                if (i < k) yv[i] = *(const MK_G f32x4 *)(P.y + (size_t)cs.row[bb * k + i] * P.d + 4 * q);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < kMaxK; ++i) {
-            if (i < k) {
-                const float wgt = cs.w[bb * k + i];
+            for (int i = 0; i < kMaxK; ++i) {
+                if (i < k) {
+                    const float wgt = cs.w[bb * k + i];
 #pragma unroll
-                for (int z = 0; z < 4; ++z) acc[z] = fmaf(wgt, yv[i][z], acc[z]);
+                    for (int z = 0; z < 4; ++z) acc[z] = fmaf(wgt, yv[i][z], acc[z]);
+                }
             }
+            const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+            *(MK_G u32x2 *)(P.out + (size_t)(b_lo + bb) * P.d + 4 * q) = u32x2{lo, hi};
         }
-        const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-        *(MK_G u32x2 *)(P.out + (size_t)(b_lo + bb) * P.d + 4 * q) = u32x2{lo, hi};
     }
     __syncthreads();
 }
@@ -925,9 +972,10 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
         if (dyn) {
             wg_push_range(P, bs.G, P.T);
-            if (threadIdx.x == 0)
-                st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64),
-                             ((unsigned long long)(uint32_t)g_sm.epoch << 32) | (uint32_t)bs.total);
+            if (threadIdx.x == 0) {  // every task of this forward now has a ticket number
+                const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
+                st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64), tag | (uint32_t)bs.total);
+            }
         }
         trace_task(P, g, K_SCAN, t0, t1, t2);
         return true;
@@ -959,36 +1007,57 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         }
         __syncthreads();
         if (dyn) {
+            // push the gate/up tiles of every expert this tile completed; task ranges are
+            // ordered by expert, so fired experts whose ranges abut go out as one range
             const int nf = gr.nfired;
-            for (int i = 0; i < nf; ++i) {
-                const int e = gr.fired[i];
-                const int m0 = P.mt_base[e], m1 = P.mt_base[e + 1];
-                wg_push_range(P, bs.M1 + m0 * P.NB1, (m1 - m0) * P.NB1);
+            if (threadIdx.x == 0) {  // sort the (few) fired experts
+                for (int i = 1; i < nf; ++i) {
+                    const int v = gr.fired[i];
+                    int j = i - 1;
+                    while (j >= 0 && gr.fired[j] > v) {
+                        gr.fired[j + 1] = gr.fired[j];
+                        --j;
+                    }
+                    gr.fired[j + 1] = v;
+                }
+            }
+            __syncthreads();
+            if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));  // block bases for the pushes
+            int i = 0;
+            while (i < nf) {
+                int j = i;
+                while (j + 1 < nf && P.mt_base[gr.fired[j] + 1] == P.mt_base[gr.fired[j + 1]]) ++j;
+                const int m0 = P.mt_base[gr.fired[i]], m1 = P.mt_base[gr.fired[j] + 1];
+                const int Q = P.NB1 / P.S;
+                for (int sp = 0; sp < P.S; ++sp) wg_push_range(P, base_g1(bs, sp) + m0 * Q, (m1 - m0) * Q);
+                i = j + 1;
             }
         }
         trace_task(P, g, K_GROUP, t0, t1, t2);
         return true;
     }
     if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
-    if (g < bs.M2) {  // --------------------------------------------------------- GEMM1
-        const int i = g - bs.M1;
-        const int mt = i / P.NB1, n = i - mt * P.NB1;
-        const int e = P.mt_expert[mt];
-        if (!dyn && !wg_wait_zero(P, P.ev_exp + e)) return false;
-        const unsigned long long t1 = now_ticks();
-        task_gemm1(P, e, P.mt_row0[mt], P.mt_rows[mt], n);
-        const unsigned long long t2 = now_ticks();
-        count_task(P, K_GEMM1);
-        const int q = mt * P.S + n / (P.NB1 / P.S);  // (row tile, f range) this tile feeds
-        if (wg_notify(P, P.ev_h + q, -1) && dyn) wg_push_range(P, bs.M2 + q * P.NB2, P.NB2);
-        trace_task(P, g, K_GEMM1, t0, t1, t2);
-        return true;
-    }
-    if (g < bs.C) {  // ---------------------------------------------------------- GEMM2
-        const int i = g - bs.M2;
-        const int q = i / P.NB2, n = i - q * P.NB2;  // q = mt * S + split
-        const int mt = q / P.S, sp = q - mt * P.S;
-        if (!dyn && !wg_wait_zero(P, P.ev_h + q)) return false;
+    if (g < bs.C) {
+        int sp, j;
+        const int kind = decode_gemm(bs, P.S, g, sp, j);
+        const int Q = P.NB1 / P.S;
+        if (kind == 1) {  // ---------------------------------------------------- GEMM1
+            const int mt = j / Q, n = sp * Q + (j - (j / Q) * Q);
+            const int e = P.mt_expert[mt];
+            if (!dyn && !wg_wait_zero(P, P.ev_exp + e)) return false;
+            const unsigned long long t1 = now_ticks();
+            task_gemm1(P, e, P.mt_row0[mt], P.mt_rows[mt], n);
+            const unsigned long long t2 = now_ticks();
+            count_task(P, K_GEMM1);
+            // f range sp of this row tile complete: its down-projection tiles are ready
+            if (wg_notify(P, P.ev_h + mt * P.S + sp, -1) && dyn)
+                wg_push_range(P, base_g2(bs, sp, P.S) + mt * P.NB2, P.NB2);
+            trace_task(P, g, K_GEMM1, t0, t1, t2);
+            return true;
+        }
+        // --------------------------------------------------------------------- GEMM2
+        const int mt = j / P.NB2, n = j - mt * P.NB2;
+        if (!dyn && !wg_wait_zero(P, P.ev_h + mt * P.S + sp)) return false;
         const unsigned long long t1 = now_ticks();
         task_gemm2(P, P.mt_expert[mt], P.mt_row0[mt], P.mt_rows[mt], n, sp, mt);
         const unsigned long long t2 = now_ticks();
@@ -1010,27 +1079,33 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
     }
 }
 
-// Dynamic queue pop.  Returns a task index, -1 when the forward is complete, -2 on error.
+// Dynamic pop.  A workgroup takes the next ticket with one atomic add; tickets below nR are
+// the router tasks (never pushed), ticket nR + i is queue slot i.  The holder of a ticket
+// whose slot is not yet filled waits on that slot alone, so idle workgroups poll distinct
+// words instead of contending for one.  Every pushed task is ready, so a filled slot runs
+// at once.  Returns a task index, -1 when the ticket lies beyond the forward's task count,
+// -2 on error.
 __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
     if (threadIdx.x == 0) {
-        int g = -1;
-        const int claim = add_relaxed(P.ctl + CTL_QHEAD, 1);
-        if (claim < P.nR) {
-            g = claim;
+        int g;
+        const uint32_t ep = (uint32_t)g_sm.epoch;
+        const int t = add_relaxed(P.ctl + CTL_QHEAD, 1);
+        if (t < P.nR) {
+            g = t;
         } else {
-            const int slot = claim - P.nR;
-            const uint32_t ep = (uint32_t)g_sm.epoch;
+            const int i = t - P.nR;
             const unsigned long long t0 = now_ticks();
             for (unsigned it = 0;; ++it) {
-                if (slot < P.q_cap) {
-                    const unsigned long long v = ld_relaxed64(P.qslots + slot);
+                if (i < P.q_cap) {
+                    const unsigned long long v = ld_relaxed64(P.qslots + i);
                     if ((uint32_t)(v >> 32) == ep) {
                         g = (int)(uint32_t)v;
                         break;
                     }
                 }
-                const unsigned long long tot = ld_relaxed64((const MK_G unsigned long long *)(P.ctl + CTL_TOTAL64));
-                if ((uint32_t)(tot >> 32) == ep && claim >= (int)(uint32_t)tot) {
+                const unsigned long long tot =
+                    ld_relaxed64((const MK_G unsigned long long *)(P.ctl + CTL_TOTAL64));
+                if ((uint32_t)(tot >> 32) == ep && t >= (int)(uint32_t)tot) {
                     g = -1;
                     break;
                 }
@@ -1048,10 +1123,10 @@ __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
                 if (it < 64)
                     __builtin_amdgcn_s_sleep(1);
                 else
-                    __builtin_amdgcn_s_sleep(8);
+                    __builtin_amdgcn_s_sleep(4);
             }
-            fence_acquire();
         }
+        fence_acquire();
         g_sm.bcast[3] = g;
     }
     __syncthreads();

@@ -22,27 +22,29 @@ constexpr int kThreads = 256;        // 4 waves of 64 lanes per persistent workg
 constexpr int kTileTokens = 64;      // tokens per top-k / grouping tile (one lane per token)
 constexpr int kRouteExperts = 16;    // experts per router task
 constexpr int kCombineTokens = 4;    // tokens per combine task
+constexpr int kCombineCols = 1024;   // model columns per combine task (4 per thread)
 constexpr int kBM = 64;              // GroupGEMM rows per tile (one expert's rows)
 constexpr int kBN = 64;              // GroupGEMM columns per tile
 constexpr int kBK = 64;              // GroupGEMM K step staged through LDS
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 16;
 
-// Control block: int32 words at the start of the workspace.
+// Control block: int32 words at the start of the workspace.  Words that many workgroups
+// update or poll at once sit on cache lines of their own (32 words = 128 bytes apart).
 enum CtlWord {
-    CTL_EPOCH = 0,     // forward counter; tags queue slots and the published task total
-    CTL_EXIT = 1,      // workgroups that left the current forward
-    CTL_ERR = 2,       // sticky error bits (MOE_MK_ERR_*)
-    CTL_QHEAD = 3,     // dynamic queue: next index to claim
-    CTL_QTAIL = 4,     // dynamic queue: next slot to fill
-    CTL_EV_TOPK = 5,   // event: all top-k tiles done (one consumer: the scan task)
-    CTL_EV_SCAN = 6,   // event: scan done; rest value 1
-    CTL_EV_Y = 7,      // event: all down-projection tiles done
-    CTL_MAGIC = 8,     // set by workspace init
-    CTL_MT_TOTAL = 9,  // number of (expert, row-tile) pairs, written by the scan task
-    CTL_TOTAL64 = 12,  // int64 at words 12..13: (epoch << 32) | total task count (dynamic mode)
-    CTL_DBG = 16,      // 8 per-kind task counters (accumulate across forwards)
-    CTL_WORDS = 64
+    CTL_EPOCH = 0,      // forward counter; tags queue slots and the published task totals
+    CTL_EXIT = 1,       // workgroups that left the current forward
+    CTL_ERR = 2,        // sticky error bits (MOE_MK_ERR_*)
+    CTL_EV_TOPK = 5,    // event: all top-k tiles done (one consumer: the scan task)
+    CTL_EV_SCAN = 6,    // event: scan done; rest value 1
+    CTL_MAGIC = 8,      // set by workspace init
+    CTL_MT_TOTAL = 9,   // number of (expert, row-tile) pairs, written by the scan task
+    CTL_TOTAL64 = 12,   // int64 at words 12..13: (epoch << 32) | task count (dynamic mode)
+    CTL_QHEAD = 32,     // dynamic queue: next ticket
+    CTL_QTAIL = 64,     // dynamic queue: slots reserved by pushers
+    CTL_EV_Y = 160,     // event: all down-projection tiles done
+    CTL_DBG = 192,      // 8 per-kind task counters (accumulate across forwards)
+    CTL_WORDS = 256
 };
 
 constexpr int32_t kMagic = 0x4d4f4531;  // "MOE1"
@@ -83,7 +85,7 @@ struct Counts {
     int64_t mt_cap; // upper bound of sum_e ceil(hist[e] / kBM)
     int64_t NB1, NB2;
     int64_t S;      // down-projection K splits
-    int64_t q_cap;  // upper bound of the pushed tasks of one forward
+    int64_t q_cap;  // upper bound of the tasks pushed to the dynamic queue in one forward
     int64_t nR_max; // upper bound of the router tasks of any batch up to B
 };
 
@@ -94,13 +96,13 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     c.nTG = ceil_div(B, 4 * c.tpw);
     c.nEB = ceil_div(s.E, kRouteExperts);
     c.nR = c.nTG * c.nEB;
-    c.nC = ceil_div(B, kCombineTokens);
+    c.nC = ceil_div(B, kCombineTokens) * ceil_div(s.d, kCombineCols);
     int64_t a = B * s.k;
     c.mt_cap = a / kBM + (a < s.E ? a : s.E) + 1;
     c.NB1 = s.f / kBN;
     c.NB2 = s.d / kBN;
     c.S = down_splits(s, B);
-    c.q_cap = 2 * c.T + 1 + c.mt_cap * (c.NB1 + kMaxSplits * c.NB2) + c.nC + 64;
+    c.q_cap = 2 * c.T + 1 + c.mt_cap * c.NB1 + c.mt_cap * kMaxSplits * c.NB2 + c.nC + 64;
     c.nR_max = ceil_div(B, 4) * c.nEB;
     return c;
 }

@@ -66,4 +66,4 @@ def expected_task_counts(hist, B, E, d, f, k):
     tpw = 1 if B <= 512 else 4  # router tokens per wave; a router task has 4 waves
     S = down_splits(B, k, f)
     return {"route": -(-B // (4 * tpw)) * -(-E // 16), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
-            "gemm1": mt * (f // 64), "gemm2": mt * S * (d // 64), "combine": -(-B // 4)}
+            "gemm1": mt * (f // 64), "gemm2": mt * S * (d // 64), "combine": -(-B // 4) * -(-d // 1024)}

@@ -163,12 +163,14 @@ def test_rest_state_and_task_counts(sched):
     torch.cuda.synchronize()
     assert layer.error() == 0
     c = ctl_words(layer, B)
-    assert c[0] == before[0] + 3                      # epoch advanced once per forward
-    assert c[1] == 0 and c[3] == 0 and c[4] == 0     # exit counter and queue at rest
-    assert c[5] == 0 and c[6] == 1 and c[7] == 0     # events at rest (scan event re-armed)
+    C = mk.CTL
+    assert c[C["epoch"]] == before[C["epoch"]] + 3    # epoch advanced once per forward
+    assert c[C["exit"]] == 0                           # exit counter at rest
+    assert c[C["qhead"]] == c[C["qtail"]] == c[C["hhead"]] == c[C["htail"]] == 0  # queues at rest
+    assert c[C["ev_topk"]] == 0 and c[C["ev_scan"]] == 1 and c[C["ev_y"]] == 0  # events at rest
     hist = routing_numpy(layer, B)["hist"]
     exp = expected_task_counts(hist, B, E, d, f, 2)
-    delta = c[16:23] - before[16:23]
+    delta = c[C["dbg"]:C["dbg"] + 7] - before[C["dbg"]:C["dbg"] + 7]
     names = ["route", "topk", "scan", "group", "gemm1", "gemm2", "combine"]
     for i, n in enumerate(names):
         assert delta[i] == 3 * exp[n], (n, delta[i], exp[n])
