@@ -27,7 +27,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_decode")
     ap.add_argument("--batch", type=int, default=0, help="batch size (default: the configuration's first)")
-    ap.add_argument("--sched", default="static", choices=["static", "dynamic"])
+    ap.add_argument("--sched", default="dynamic", choices=["static", "dynamic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens of the oracle sample (default: auto)")
     ap.add_argument("--trace", action="store_true", help="after timing, run one traced forward and print "
@@ -65,6 +65,32 @@ def cpu_baseline(cfg, x, Wr, bias, weights, sample, min_seconds=10.0, max_reps=2
     return {"value": reps * n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {B} tokens of the same workload (router, top-k, grouping, fp64 SwiGLU experts, "
                       f"combine) x {reps} repetitions = {dt:.1f} s on {cores} OpenMP threads"}
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("megakernel.hip", "mk_common.h", "mk_device.h"):
+        with open(os.path.join(ROOT, "moe_groupgemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(cfg_name, B, sched):
+    """HBM bytes per launch from the committed rocprofv3 byte-counter summary of this workload,
+    or None when there is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"megakernel_{cfg_name}_B{B}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ": " in ln and not ln.startswith(" "):
+                key, val = ln.split(": ", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash() or kv.get("sched") != sched:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
 
 
 def copy_calibration(nbytes=1 << 30):
@@ -194,7 +220,7 @@ def main():
                 "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None}
     else:
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+                "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic(cfg.name, B, args.sched)}
     line = {
         "metric": "MoE-layer tokens/s + achieved HBM TB/s (B<=64) / MFMA TFLOP/s (B>=2048) vs peak",
         "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -1103,11 +1103,13 @@ __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
                         break;
                     }
                 }
-                const unsigned long long tot =
-                    ld_relaxed64((const MK_G unsigned long long *)(P.ctl + CTL_TOTAL64));
-                if ((uint32_t)(tot >> 32) == ep && t >= (int)(uint32_t)tot) {
-                    g = -1;
-                    break;
+                if ((it & 7u) == 7u) {  // the task count is one word every waiter reads: look rarely
+                    const unsigned long long tot =
+                        ld_relaxed64((const MK_G unsigned long long *)(P.ctl + CTL_TOTAL64));
+                    if ((uint32_t)(tot >> 32) == ep && t >= (int)(uint32_t)tot) {
+                        g = -1;
+                        break;
+                    }
                 }
                 if ((it & 31u) == 31u) {
                     if (ld_relaxed(P.ctl + CTL_ERR) != 0) {
