@@ -124,15 +124,22 @@ def trace_report(layer, x, out, B):
     T = -(-B // 64)
     mt = int(ctl[mk.CTL["mt_total"]])
     a = B * k
-    S = 4 if (a <= 1024 and f >= 8192 and (f // 64) % 4 == 0) else \
-        2 if (a <= 1024 and f >= 4096 and (f // 64) % 2 == 0) else 1
-    total = nR + 2 * T + 1 + mt * (f // 64 + S * (d // 64)) + -(-B // 4) * -(-d // 1024)
+    if a >= 128 * E:  # wide tiles: 128 rows; 64 gate/up columns, 128 down-projection columns
+        S, nb1, nb2 = 1, f // mk.moe_mk_plan_info(layer.plan, "wide_BN1"), d // 128
+    else:
+        S = 4 if (a <= 1024 and f >= 8192 and (f // 64) % 4 == 0) else \
+            2 if (a <= 1024 and f >= 4096 and (f // 64) % 2 == 0) else 1
+        nb1, nb2 = f // 64, d // 64
+    # GroupGEMM blocks are padded to multiples of 8 task positions (empty tasks leave no record)
+    r8 = lambda v: (v + 7) // 8 * 8
+    total = r8(nR + 2 * T + 1) + S * (r8(mt * nb1 // S) + r8(mt * nb2)) + -(-B // 4) * -(-d // 1024)
     tr = tr[:total]
+    tr = tr[tr[:, 1] != 0]
     kind = (tr[:, 0] >> 32) & 0xFF
     wg = tr[:, 0] >> 40
     t0 = tr[:, 1].min()
     us = lambda v: v / 100.0  # 100 MHz ticks -> microseconds
-    print(f"# trace: {total} tasks, {len(set(wg.tolist()))} workgroups, span {us(tr[:, 3].max() - t0):.1f} us",
+    print(f"# trace: {len(tr)} tasks, {len(set(wg.tolist()))} workgroups, span {us(tr[:, 3].max() - t0):.1f} us",
           file=sys.stderr)
     for kd, name in enumerate(mk.TASK_KINDS):
         m = kind == kd
@@ -145,6 +152,9 @@ def trace_report(layer, x, out, B):
               f"end {us(tr[m, 3].max() - t0):7.1f} | wait {us(wait.mean()):6.2f} (max {us(wait.max()):6.1f}) | "
               f"body {us(body.mean()):7.2f} (max {us(body.max()):6.1f}) | notify {us(tail.mean()):5.2f}",
               file=sys.stderr)
+    xcc = tr[:, 5]
+    print(f"#  XCD of a task equals its workgroup index mod 8 for {100.0 * np.mean(xcc == wg % 8):.1f}% of tasks",
+          file=sys.stderr)
     # time between a workgroup finishing one task and obtaining the next (queue / loop overhead)
     gaps = []
     for w in set(wg.tolist()):

@@ -148,7 +148,11 @@ moe_mk_status_t moe_mk_workspace_error(moe_mk_plan_t plan, const void *ws, size_
                                        int32_t *err /* host */);
 
 /* Plan facts (host).  Keys: "E" "k" "d" "f" "sched" "grid" "cus" "wg_per_cu" "BM" "BN1" "BN2" "BK"
- * "route_experts" "threads".  Returns -1 for an unknown key or invalid plan. */
+ * "wide_BM" "wide_BN1" "wide_BN2" "wide_BK" "wide_min_rows" "route_experts" "threads".
+ * GroupGEMM tiles are BM x BN1 (gate/up) and BM x BN2 (down) with K steps of BK, except in
+ * forwards where B*k >= wide_min_rows*E (an expert averages that many rows): there tiles
+ * have wide_BM rows, wide_BN1 gate/up columns, wide_BN2 down columns and K steps of wide_BK.  Returns -1 for an
+ * unknown key or invalid plan. */
 int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
 
 /*
@@ -168,8 +172,9 @@ moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks
  *   [0] task index g | kind << 32 | workgroup << 40   (kind: 0 router, 1 top-k, 2 scan,
  *       3 grouping, 4 gate/up GEMM, 5 down GEMM, 6 combine)
  *   [1] time the workgroup obtained the task, [2] time its dependencies were satisfied,
- *   [3] time it finished, [4] time its compute ended (before its notifications);
- *   [5..7] unused.  GPU real-time clock ticks (100 MHz).
+ *   [3] time it finished, [4] time its compute ended (before its notifications),
+ *   all in GPU real-time clock ticks (100 MHz); [5] the XCD (accelerator die, 0..7) that
+ *   ran it; [6..7] unused.
  * Records of tasks that did not run in that forward are stale.  Errors: EINVAL, EWORKSPACE.
  */
 moe_mk_status_t moe_mk_trace_view(moe_mk_plan_t plan, int64_t B, const void *ws, size_t ws_bytes,

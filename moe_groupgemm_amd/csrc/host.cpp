@@ -165,9 +165,11 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.nEB = (int)c.nEB;
     P.T = (int)c.T;
     P.nC = (int)c.nC;
-    P.NB1 = (int)c.NB1;
-    P.NB2 = (int)c.NB2;
-    P.S = (int)c.S;
+    const mk::Tiles tl = mk::tile_config(s, B);
+    P.NB1 = tl.NB1;
+    P.NB2 = tl.NB2;
+    P.S = tl.S;
+    P.BM = tl.BM;
     P.q_cap = (int)cc.q_cap;
     P.mt_cap = (int)cc.mt_cap;
     P.watchdog = plan->watchdog;
@@ -258,6 +260,11 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key) {
              {"BN1", mk::kBN},
              {"BN2", mk::kBN},
              {"BK", mk::kBK},
+             {"wide_BM", mk::kWideBM},
+             {"wide_BN1", mk::kWideBN1},
+             {"wide_BN2", mk::kWideBN},
+             {"wide_BK", mk::kWideBK},
+             {"wide_min_rows", mk::kWideBM},
              {"route_experts", mk::kRouteExperts},
              {"threads", mk::kThreads}};
     for (auto &e : t)

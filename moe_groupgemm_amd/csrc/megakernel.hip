@@ -41,8 +41,10 @@ struct TopkSmem {
     float lg[kTileTokens * kMaxE];  // a tile's logits, then the candidate lists
     int hist[kMaxE];
 };
+constexpr int kScanStage = 16384;  // ints of tile_hist staged per round
 struct ScanSmem {
     int part[8];
+    int tiles[kScanStage];
 };
 struct GroupSmem {
     unsigned long long mask[kMaxE];
@@ -77,11 +79,22 @@ __shared__ Smem g_sm;
 // tile, Q = NB1/S per row tile) and G2(s) the down-projection tiles reducing over f range
 // s (NB2 per row tile).  Each G2 block comes one G1 block after the G1 block it consumes,
 // so the two GEMMs overlap instead of running as two phases.
+//
+// GroupGEMM blocks start at multiples of 8 and are padded to multiples of 8 (padding
+// positions are empty tasks).  Workgroups are dealt to the 8 XCDs round-robin, so in the
+// static schedule position p of a block runs on XCD p % 8.  Static mode therefore maps
+// position p to the linear tile q = (p % 8) * (size / 8) + p / 8: each XCD works through
+// one contiguous eighth of the tiles (row tile major), and the tiles sharing a row tile's
+// activations or an expert's weight columns run together on the same L2.  Dynamic mode
+// uses q = p (its pushes follow the linear order).
 struct Bases {
-    int K, S, G, M1, C, total;
-    int q1, q2;  // tasks per G1(s) block and per G2(s) block
-    bool known;  // M1-relative layout known once the scan has run
+    int K, S, G, M1, M1p, C, total;
+    int q1, q2;    // tiles per G1(s) block and per G2(s) block
+    int q1p, q2p;  // the same rounded up to multiples of 8 (block sizes)
+    bool known;    // GroupGEMM layout known once the scan has run
 };
+
+__device__ __forceinline__ int round8(int v) { return (v + 7) & ~7; }
 
 __device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
     Bases b;
@@ -89,8 +102,9 @@ __device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
     b.S = b.K + P.T;
     b.G = b.S + 1;
     b.M1 = b.G + P.T;
+    b.M1p = round8(b.M1);
     b.C = b.total = 0x7fffffff;
-    b.q1 = b.q2 = 0;
+    b.q1 = b.q2 = b.q1p = b.q2p = 0;
     b.known = false;
     return b;
 }
@@ -98,45 +112,52 @@ __device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
 __device__ __forceinline__ void complete_bases(const MK_C Params &P, Bases &b, int mt_total) {
     b.q1 = mt_total * (P.NB1 / P.S);
     b.q2 = mt_total * P.NB2;
-    b.C = b.M1 + P.S * (b.q1 + b.q2);
+    b.q1p = round8(b.q1);
+    b.q2p = round8(b.q2);
+    b.C = b.M1p + P.S * (b.q1p + b.q2p);
     b.total = b.C + P.nC;
     b.known = true;
 }
 
 __device__ __forceinline__ int base_g1(const Bases &b, int s) {
-    return s == 0 ? b.M1 : b.M1 + b.q1 + (s - 1) * (b.q1 + b.q2);
+    return s == 0 ? b.M1p : b.M1p + b.q1p + (s - 1) * (b.q1p + b.q2p);
 }
 __device__ __forceinline__ int base_g2(const Bases &b, int s, int S) {
-    return s < S - 1 ? base_g1(b, s + 1) + b.q1 : b.M1 + S * b.q1 + (S - 1) * b.q2;
+    return s < S - 1 ? base_g1(b, s + 1) + b.q1p : b.M1p + S * b.q1p + (S - 1) * b.q2p;
 }
 
-// Decode a GroupGEMM task index: returns 1 for gate/up, 2 for down; sets the f range s and
-// the index j inside its block.
-__device__ __forceinline__ int decode_gemm(const Bases &b, int S, int g, int &s, int &j) {
-    int o = g - b.M1;
-    if (o < b.q1) {
+// Decode a GroupGEMM task index: returns 1 for gate/up, 2 for down, 0 for a padding
+// position; sets the f range s and the linear tile j inside its block.
+__device__ __forceinline__ int decode_gemm(const Bases &b, int S, bool xcd_map, int g, int &s, int &j) {
+    int o = g - b.M1p, kind = 0, cnt = 0, size = 0;
+    if (o < b.q1p) {
         s = 0;
-        j = o;
-        return 1;
-    }
-    o -= b.q1;
-    for (int r = 1; r < S; ++r) {
-        if (o < b.q1) {
-            s = r;
-            j = o;
-            return 1;
+        kind = 1;
+    } else {
+        o -= b.q1p;
+        for (int r = 1; r < S && kind == 0; ++r) {
+            if (o < b.q1p) {
+                s = r;
+                kind = 1;
+            } else {
+                o -= b.q1p;
+                if (o < b.q2p) {
+                    s = r - 1;
+                    kind = 2;
+                } else {
+                    o -= b.q2p;
+                }
+            }
         }
-        o -= b.q1;
-        if (o < b.q2) {
-            s = r - 1;
-            j = o;
-            return 2;
+        if (kind == 0) {
+            s = S - 1;
+            kind = 2;
         }
-        o -= b.q2;
     }
-    s = S - 1;
-    j = o;
-    return 2;
+    cnt = kind == 1 ? b.q1 : b.q2;
+    size = kind == 1 ? b.q1p : b.q2p;
+    j = xcd_map ? (o & 7) * (size >> 3) + (o >> 3) : o;
+    return j < cnt ? kind : 0;
 }
 
 // ------------------------------------------------------------------------------ event helpers (workgroup level)
@@ -452,11 +473,19 @@ __device__ __forceinline__ int block_excl_scan(int v, int *part, int *total) {
 // GroupGEMM tiles each expert triggers).  Returns the number of row tiles.
 __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P) {
     const int e = threadIdx.x;
-    const int E = P.E;
+    const int E = P.E, BM = P.BM;
+    int *tb = g_sm.u.s.tiles;
+    const int rows = kScanStage / E;  // tile_hist rows staged per round (coalesced loads)
     int h = 0;
-    if (e < E)
-        for (int t = 0; t < P.T; ++t) h += P.tile_hist[(size_t)t * E + e];
-    const int mt = (h + kBM - 1) / kBM;
+    for (int t0 = 0; t0 < P.T; t0 += rows) {
+        const int nr = min(rows, P.T - t0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < nr * E; i += kThreads) tb[i] = P.tile_hist[(size_t)t0 * E + i];
+        __syncthreads();
+        if (e < E)
+            for (int t = 0; t < nr; ++t) h += tb[t * E + e];
+    }
+    const int mt = (h + BM - 1) / BM;
     int total_h, total_mt;
     const int off = block_excl_scan(h, g_sm.u.s.part, &total_h);
     const int mbase = block_excl_scan(mt, g_sm.u.s.part, &total_mt);
@@ -464,16 +493,11 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P) {
         pub(P.hist + e, h);
         pub(P.indptr + e, off);
         pub(P.mt_base + e, mbase);
-        int run = off;
-        for (int t = 0; t < P.T; ++t) {
-            pub(P.tile_off + (size_t)t * E + e, run);
-            run += P.tile_hist[(size_t)t * E + e];
-        }
         for (int m = 0; m < mt; ++m) {
             const int i = mbase + m;
             pub(P.mt_expert + i, e);
-            pub(P.mt_row0 + i, off + m * kBM);
-            pub(P.mt_rows + i, min(kBM, h - m * kBM));
+            pub(P.mt_row0 + i, off + m * BM);
+            pub(P.mt_rows + i, min(BM, h - m * BM));
             for (int sp = 0; sp < P.S; ++sp) add_relaxed(P.ev_h + i * P.S + sp, P.NB1 / P.S);
         }
         if (h) add_relaxed(P.ev_exp + e, h);
@@ -483,6 +507,25 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P) {
         pub(P.mt_base + E, total_mt);
         st_relaxed(P.ctl + CTL_MT_TOTAL, total_mt);
         add_relaxed(P.ctl + CTL_EV_Y, total_mt * P.S * P.NB2);
+    }
+    // per-tile row offsets: exp_indptr[e] + rows of e in earlier tiles
+    int run = off;
+    for (int t0 = 0; t0 < P.T; t0 += rows) {
+        const int nr = min(rows, P.T - t0);
+        if (t0 > 0) {  // the first round's rows are still staged unless T needed several
+            __syncthreads();
+            for (int i = threadIdx.x; i < nr * E; i += kThreads) tb[i] = P.tile_hist[(size_t)t0 * E + i];
+            __syncthreads();
+        } else if (P.T > rows) {
+            __syncthreads();
+            for (int i = threadIdx.x; i < nr * E; i += kThreads) tb[i] = P.tile_hist[i];
+            __syncthreads();
+        }
+        if (e < E)
+            for (int t = 0; t < nr; ++t) {
+                pub(P.tile_off + (size_t)(t0 + t) * E + e, run);
+                run += tb[t * E + e];
+            }
     }
     return total_mt;
 }
@@ -710,8 +753,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], 
         acc0[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc1[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int nrb = (ga.nrows + 15) / 16;
-    const int nk = ga.K / kBK;
+    const int nrb = uni((ga.nrows + 15) / 16);
+    const int nk = uni(ga.K / kBK);
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
         if (p < nk) stage_load<DUAL, AR>(ga, p * kBK, s.ring + p * C::STAGE_ELEMS);
@@ -767,7 +810,7 @@ __device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rb + 4 * g + r;
             const float gv = acc0[rb][r], uv = acc1[rb][r];
-            const uint32_t hv = f32_to_bf16(gv / (1.0f + __expf(-gv)) * uv);
+            const uint32_t hv = f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
             // columns col and col+1 sit in lanes j and j+1: even lanes store both
             const uint32_t nb = (uint32_t)__shfl_xor((int)hv, 1, 64);
             if (row < nrows && (j & 1) == 0)
@@ -840,11 +883,344 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
     }
 }
 
+// ------------------------------------------------------------------------------ wide tiles
+// At large batches (an expert averages 128 rows or more) a tile has 128 rows, K steps are
+// 32 deep, and the four waves split the tile 2 x 2: wave w owns rows 64*(w/2) .. +64 and
+// the (w%2)-th half of the columns.  Gate/up tiles are 64 columns of each weight (wave:
+// 64 x 32 of each); down-projection tiles are 128 columns (wave: 64 x 64).  Either way a
+// wave holds 64 accumulator registers, reads 4 A and 8 B fragment halves per K step in one
+// LDS batch, and issues 16 MFMAs on them.
+//   A tile in LDS: [row][k], 64-byte rows; 16-byte chunk c of row r sits at c ^ wswa(r),
+//     so the 16 rows one A fragment read touches fall on 16 distinct 16-byte bank groups.
+//   B tile in LDS: [k][n], rows as in memory (128 bytes: chunk c at c ^ swb(k); 256 bytes:
+//     chunk c at c ^ wswb(k)), so the rows one ds_read_b64_tr_b16 touches spread over
+//     distinct bank groups.
+constexpr int kWBK = kWideBK;
+__device__ __forceinline__ int wswa(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int wswb(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
+
+template <bool DUAL, int BN>
+struct WideCfg {
+    static constexpr int CB = BN / 32;                // 16-column blocks per wave
+    static constexpr int NACC = 4 * CB;               // accumulators per weight
+    static constexpr int A_ELEMS = kWideBM * kWBK;
+    static constexpr int B_ELEMS = kWBK * BN;
+    static constexpr int B_BLOCKS = B_ELEMS / 512;    // 1 KB blocks per weight and stage
+    static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS * (DUAL ? 2 : 1);
+    static constexpr int NS = (kRingBytes / 2) / STAGE_ELEMS;
+    static constexpr int LOADS = 2 + (B_BLOCKS / 4) * (DUAL ? 2 : 1);  // global_load_lds per wave per stage
+    static_assert(NS >= 3, "ring too shallow");
+    static_assert(CB == 2 || CB == 4, "column blocks per wave");
+};
+
+template <int BN>
+__device__ __forceinline__ int wide_swb(int k) {
+    return BN == 64 ? swb(k) : wswb(k);
+}
+
+// Operands of a wide tile: wave-uniform bases plus 32-bit per-lane element offsets that
+// stay fixed over the K loop (each K stage only moves the uniform bases), so the loads
+// take the scalar-base addressing form and keep few registers live.
+struct WideArgs {
+    const MK_G uint16_t *A;   // activation base (x or h)
+    uint32_t a_off[2];        // this lane's row start + 16-byte chunk, per A block it loads
+    const MK_G uint16_t *B0, *B1;  // weight tile bases (k 0, column n0)
+    uint32_t b_off[2];        // this lane's k-row * ldb + 16-byte chunk, per B block it loads
+    int ldb, K, nrows;
+};
+
+// Issue the loads of one K stage.  A: eight 1 KB blocks of 16 rows x 64 bytes, two per
+// wave (lane -> row 16*blk + lane/4, position lane%4).  B: 1 KB blocks of 1024/(2*BN)
+// k-rows of 2*BN bytes (lane -> k-row lane/(BN/8), position lane%(BN/8)).
+template <bool DUAL, int BN>
+__device__ __forceinline__ void wstage_load(const WideArgs &g, int k0, uint16_t *stage) {
+    using C = WideCfg<DUAL, BN>;
+    uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
+    const int w = wave_id();
+    const MK_G uint16_t *ab = g.A + k0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16(ab + g.a_off[i], (MK_L void *)(sA + (2 * w + i) * 512));
+    const size_t kk = (size_t)k0 * g.ldb;
+    const MK_G uint16_t *b0 = g.B0 + kk, *b1 = g.B1 + kk;
+#pragma unroll
+    for (int i = 0; i < C::B_BLOCKS / 4; ++i) {
+        const int blk = (C::B_BLOCKS / 4) * w + i;
+        lds_dma16(b0 + g.b_off[i], (MK_L void *)(sB0 + blk * 512));
+        if constexpr (DUAL) lds_dma16(b1 + g.b_off[i], (MK_L void *)(sB1 + blk * 512));
+    }
+}
+
+// Per-lane offsets of a wide tile's loads; arow(i) gives the element offset of the start
+// of the A row this lane loads for A block i.
+template <bool DUAL, int BN, typename RowOf>
+__device__ __forceinline__ void wide_offsets(WideArgs &g, RowOf arow) {
+    using C = WideCfg<DUAL, BN>;
+    const int lane = lane_id(), w = wave_id();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 16 * (2 * w + i) + (lane >> 2);
+        g.a_off[i] = arow(i) + 8u * (uint32_t)((lane & 3) ^ wswa(row));
+    }
+    constexpr int CPR = BN / 8;    // 16-byte chunks per k-row
+    constexpr int RPB = 64 / CPR;  // k-rows per 1 KB block
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int blk = (C::B_BLOCKS / 4) * w + (i < C::B_BLOCKS / 4 ? i : 0);
+        const int kr = RPB * blk + lane / CPR;
+        g.b_off[i] = (uint32_t)kr * (uint32_t)g.ldb + 8u * (uint32_t)((lane % CPR) ^ wide_swb<BN>(kr));
+    }
+}
+
+// LDS byte address of this lane's half of a B fragment (rows kbase + l/4, columns
+// ncol0 + 4*(l%4)) in a B tile of BN columns.
+template <int BN>
+__device__ __forceinline__ uint32_t wb_frag_addr(const uint16_t *sB, int kbase, int ncol0) {
+    const int l = lane_id() & 15;
+    const int k = kbase + (l >> 2);
+    const int col = ncol0 + 4 * (l & 3);
+    return lds_addr(sB + k * BN + ((((col >> 3) ^ wide_swb<BN>(k)) << 3) | (col & 7)));
+}
+
+// Four A fragments and eight B fragment halves in one asm block that also waits for them
+// (see frag_reads).
+__device__ __forceinline__ void wide_reads(const uint32_t (&ba)[8], const uint32_t (&aa)[4], u32x2 (&b)[8],
+                                           u32x4 (&a)[4]) {
+    asm volatile(
+        "ds_read_b128 %8, %20\n\tds_read_b128 %9, %21\n\tds_read_b128 %10, %22\n\tds_read_b128 %11, %23\n\t"
+        "ds_read_b64_tr_b16 %0, %12\n\tds_read_b64_tr_b16 %1, %13\n\t"
+        "ds_read_b64_tr_b16 %2, %14\n\tds_read_b64_tr_b16 %3, %15\n\t"
+        "ds_read_b64_tr_b16 %4, %16\n\tds_read_b64_tr_b16 %5, %17\n\t"
+        "ds_read_b64_tr_b16 %6, %18\n\tds_read_b64_tr_b16 %7, %19\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7]),
+          "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]), "v"(ba[4]), "v"(ba[5]), "v"(ba[6]), "v"(ba[7]),
+          "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
+}
+
+__device__ __forceinline__ void wide_reads_b(const uint32_t (&ba)[8], u32x2 (&b)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7])
+        : "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]), "v"(ba[4]), "v"(ba[5]), "v"(ba[6]), "v"(ba[7]));
+}
+
+// One K step of 32 for this wave's block; NRB = 16-row blocks of the wave that hold rows
+// (a compile-time count, so the loop body has no branches around its MFMAs).
+// B fragment halves are read in batches of eight (one batch per weight when a wave covers
+// 64 columns of it, one for both weights when it covers 32).
+template <bool DUAL, int BN, int NRB>
+__device__ __forceinline__ void wstage_compute(const uint16_t *stage, f32x4 (&acc0)[WideCfg<DUAL, BN>::NACC],
+                                               f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC]) {
+    using C = WideCfg<DUAL, BN>;
+    constexpr int CB = C::CB;
+    const uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
+    const int lane = lane_id(), w = wave_id();
+    const int g = lane >> 4, i = lane & 15;
+    const int r0 = 64 * (w >> 1), c0 = (BN / 2) * (w & 1);
+    const int kb = 8 * g;
+    uint32_t aa[4], ba[8];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int r = r0 + 16 * rb + i;
+        aa[rb] = lds_addr(sA + r * kWBK + ((g ^ wswa(r)) << 3));
+    }
+    u32x2 b[8];
+    u32x4 a[4];
+    if constexpr (CB == 2) {
+#pragma unroll
+        for (int q = 0; q < (DUAL ? 2 : 1); ++q)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const uint16_t *sB = q ? sB1 : sB0;
+                ba[2 * (q * CB + cb)] = wb_frag_addr<BN>(sB, kb, c0 + 16 * cb);
+                ba[2 * (q * CB + cb) + 1] = wb_frag_addr<BN>(sB, kb + 4, c0 + 16 * cb);
+            }
+        wide_reads(ba, aa, b, a);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            if (rb < NRB)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    acc0[CB * rb + cb] =
+                        mfma_bf16_16x16x32(a[rb], join(b[2 * cb], b[2 * cb + 1]), acc0[CB * rb + cb]);
+                    if constexpr (DUAL)
+                        acc1[CB * rb + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * (CB + cb)], b[2 * (CB + cb) + 1]),
+                                                                acc1[CB * rb + cb]);
+                }
+    } else {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            ba[2 * cb] = wb_frag_addr<BN>(sB0, kb, c0 + 16 * cb);
+            ba[2 * cb + 1] = wb_frag_addr<BN>(sB0, kb + 4, c0 + 16 * cb);
+        }
+        wide_reads(ba, aa, b, a);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            if (rb < NRB)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    acc0[4 * rb + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * cb], b[2 * cb + 1]), acc0[4 * rb + cb]);
+        if constexpr (DUAL) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                ba[2 * cb] = wb_frag_addr<BN>(sB1, kb, c0 + 16 * cb);
+                ba[2 * cb + 1] = wb_frag_addr<BN>(sB1, kb + 4, c0 + 16 * cb);
+            }
+            wide_reads_b(ba, b);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                if (rb < NRB)
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb)
+                        acc1[4 * rb + cb] =
+                            mfma_bf16_16x16x32(a[rb], join(b[2 * cb], b[2 * cb + 1]), acc1[4 * rb + cb]);
+        }
+    }
+}
+
+template <bool DUAL, int BN, int NRB>
+__device__ __forceinline__ void wide_loop(const WideArgs &ga, int nk, f32x4 (&acc0)[WideCfg<DUAL, BN>::NACC],
+                                          f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC], GemmSmem &s) {
+    using C = WideCfg<DUAL, BN>;
+    constexpr int NS = C::NS;
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < nk) wstage_load<DUAL, BN>(ga, p * kWBK, s.ring + p * C::STAGE_ELEMS);
+    int slot = 0;
+    for (int st = 0; st < nk; ++st) {
+        if (st + NS - 2 < nk)
+            wait_vm<(NS - 2) * C::LOADS>();
+        else
+            wait_vm<0>();
+        bare_barrier();
+        const int nxt = st + NS - 1;
+        if (nxt < nk) {
+            const int ns = slot == 0 ? NS - 1 : slot - 1;
+            wstage_load<DUAL, BN>(ga, nxt * kWBK, s.ring + ns * C::STAGE_ELEMS);
+        }
+        if constexpr (NRB > 0) wstage_compute<DUAL, BN, NRB>(s.ring + slot * C::STAGE_ELEMS, acc0, acc1);
+        slot = slot == NS - 1 ? 0 : slot + 1;
+    }
+    wait_vm<0>();
+    __syncthreads();
+}
+
+// The K loop of a wide tile.  Each wave runs the loop variant for the number of its
+// 16-row blocks that hold rows (waves of one tile may differ; every variant issues the
+// same loads and barriers).
+template <bool DUAL, int BN>
+__device__ __forceinline__ void wide_tile(const WideArgs &ga, f32x4 (&acc0)[WideCfg<DUAL, BN>::NACC],
+                                          f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC], GemmSmem &s) {
+    using C = WideCfg<DUAL, BN>;
+#pragma unroll
+    for (int q = 0; q < C::NACC; ++q) {
+        acc0[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int wrows = min(max(uni(ga.nrows) - 64 * (wave_id() >> 1), 0), 64);
+    const int nrb = uni((wrows + 15) / 16);
+    const int nk = uni(ga.K / kWBK);
+    switch (nrb) {
+        case 4: wide_loop<DUAL, BN, 4>(ga, nk, acc0, acc1, s); break;
+        case 3: wide_loop<DUAL, BN, 3>(ga, nk, acc0, acc1, s); break;
+        case 2: wide_loop<DUAL, BN, 2>(ga, nk, acc0, acc1, s); break;
+        case 1: wide_loop<DUAL, BN, 1>(ga, nk, acc0, acc1, s); break;
+        default: wide_loop<DUAL, BN, 0>(ga, nk, acc0, acc1, s); break;
+    }
+}
+
+// Row of A block i (16 rows) loaded by this lane in a wide tile, clamped to the tile's rows.
+__device__ __forceinline__ int wa_row(int i, int nrows) {
+    return min(16 * (2 * wave_id() + i) + (lane_id() >> 2), nrows - 1);
+}
+
+// Wide gate/up tile: 128 rows x kWideBN1 columns of h.
+__device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
+    e = uni(e);
+    row0 = uni(row0);
+    nrows = uni(nrows);
+    n = uni(n);
+    constexpr int BN = kWideBN1;
+    using C = WideCfg<true, BN>;
+    WideArgs ga;
+    ga.A = P.x;
+    ga.nrows = nrows;
+    ga.B0 = P.W1 + (size_t)e * P.d * P.f + (size_t)n * BN;
+    ga.B1 = P.W3 + (size_t)e * P.d * P.f + (size_t)n * BN;
+    ga.ldb = P.f;
+    ga.K = P.d;
+    wide_offsets<true, BN>(ga, [&](int i) {
+        return (uint32_t)(P.perm[row0 + wa_row(i, nrows)] / P.k) * (uint32_t)P.d;
+    });
+    f32x4 acc0[C::NACC], acc1[C::NACC];
+    wide_tile<true, BN>(ga, acc0, acc1, g_sm.u.g);
+    const int lane = lane_id(), w = wave_id();
+    const int g = lane >> 4, j = lane & 15;
+    const int r0 = 64 * (w >> 1), c0 = n * BN + (BN / 2) * (w & 1);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = r0 + 16 * rb + 4 * g + r;
+                const int col = c0 + 16 * cb + j;
+                const float gv = acc0[C::CB * rb + cb][r], uv = acc1[C::CB * rb + cb][r];
+                const uint32_t hv = f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
+                const uint32_t nb = (uint32_t)__shfl_xor((int)hv, 1, 64);
+                if (row < nrows && (j & 1) == 0)
+                    pub((MK_G uint32_t *)(P.h + (size_t)(row0 + row) * P.f + col), hv | (nb << 16));
+            }
+}
+
+// Wide down-projection tile: 128 rows x 128 columns of y.
+__device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n) {
+    e = uni(e);
+    row0 = uni(row0);
+    nrows = uni(nrows);
+    n = uni(n);
+    constexpr int BN = kWideBN;
+    using C = WideCfg<false, BN>;
+    WideArgs ga;
+    ga.A = P.h + (size_t)row0 * P.f;
+    ga.nrows = nrows;
+    ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)n * BN;
+    ga.B1 = ga.B0;
+    ga.ldb = P.d;
+    ga.K = P.f;
+    wide_offsets<false, BN>(ga, [&](int i) { return (uint32_t)wa_row(i, nrows) * (uint32_t)P.f; });
+    f32x4 acc0[C::NACC], acc1[C::NACC];
+    wide_tile<false, BN>(ga, acc0, acc1, g_sm.u.g);
+    const int lane = lane_id(), w = wave_id();
+    const int g = lane >> 4, j = lane & 15;
+    const int r0 = 64 * (w >> 1), c0 = n * BN + (BN / 2) * (w & 1);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = r0 + 16 * rb + 4 * g + r;
+                if (row < nrows) pub(P.y + (size_t)(row0 + row) * P.d + c0 + 16 * cb + j, acc0[C::CB * rb + cb][r]);
+            }
+}
+
 // GEMM1 tile: h[rows, n0:n0+64] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
 // where row p of the tile is token perm[p] / k of x.  The tile variant is chosen from the
 // tile's actual row count.
 __device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
-    if (nrows <= 16)
+    e = uni(e);
+    row0 = uni(row0);
+    nrows = uni(nrows);
+    n = uni(n);
+    if (P.BM == kWideBM)
+        wide_gemm1(P, e, row0, nrows, n);
+    else if (nrows <= 16)
         gemm1_tile<16>(P, e, row0, nrows, n);
     else
         gemm1_tile<64>(P, e, row0, nrows, n);
@@ -853,7 +1229,15 @@ __device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &P, int e
 // GEMM2 tile: y[sp][rows, n0:n0+64] = h[rows, f range sp] W2[e][f range sp, n0:n0+64], fp32.
 __device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n,
                                                      int sp, int mt) {
-    if (nrows <= 16)
+    e = uni(e);
+    row0 = uni(row0);
+    nrows = uni(nrows);
+    n = uni(n);
+    sp = uni(sp);
+    mt = uni(mt);
+    if (P.BM == kWideBM)
+        wide_gemm2(P, e, row0, nrows, n);
+    else if (nrows <= 16)
         gemm2_tile<16>(P, e, row0, nrows, n, sp, mt);
     else
         gemm2_tile<64>(P, e, row0, nrows, n, sp, mt);
@@ -925,6 +1309,9 @@ __device__ __forceinline__ void trace_task(const MK_C Params &P, int g, int kind
         e[2] = (long long)t1;
         e[3] = (long long)now_ticks();
         e[4] = (long long)t2;
+        uint32_t xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+        e[5] = (long long)xcc;  // the XCD that ran the task
     }
 }
 
@@ -973,15 +1360,18 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         if (dyn) {
             wg_push_range(P, bs.G, P.T);
             if (threadIdx.x == 0) {  // every task of this forward now has a ticket number
+                // (padding positions of the static layout are never pushed)
+                const int real = bs.M1 + P.S * (bs.q1 + bs.q2) + P.nC;
                 const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
-                st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64), tag | (uint32_t)bs.total);
+                st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64), tag | (uint32_t)real);
             }
         }
         trace_task(P, g, K_SCAN, t0, t1, t2);
         return true;
     }
-    if (g < bs.M1) {  // --------------------------------------------------------- GROUP
+    if (g < bs.M1p) {  // -------------------------------------------------------- GROUP
         const int t = g - bs.G;
+        if (t >= P.T) return true;  // padding before the GroupGEMM blocks
         if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) return false;
         const unsigned long long t1 = now_ticks();
         task_group(P, t);
@@ -1039,7 +1429,8 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
     if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
     if (g < bs.C) {
         int sp, j;
-        const int kind = decode_gemm(bs, P.S, g, sp, j);
+        const int kind = decode_gemm(bs, P.S, !dyn && P.BM == kWideBM, g, sp, j);
+        if (kind == 0) return true;  // padding position
         const int Q = P.NB1 / P.S;
         if (kind == 1) {  // ---------------------------------------------------- GEMM1
             const int mt = j / Q, n = sp * Q + (j - (j / Q) * Q);

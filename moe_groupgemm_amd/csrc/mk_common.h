@@ -74,6 +74,31 @@ inline int down_splits(const Shape &s, int64_t B) {
 }
 constexpr int kMaxSplits = 4;
 
+// GroupGEMM tiles of one forward.  Narrow: kBM x kBN tiles (decode and mid-size batches).
+// Wide: when an expert averages at least kWideBM rows, tiles of kWideBM rows, kBN columns
+// of each gate/up weight and kWideBN columns of the down projection, so that each staged
+// weight byte serves twice the rows.  Workspace sizes are bounded with the narrow counts,
+// which are never smaller.
+constexpr int kWideBM = 128;
+constexpr int kWideBN = 128;
+constexpr int kWideBK = 32;
+#ifndef MK_WIDE_BN1
+#define MK_WIDE_BN1 128
+#endif
+constexpr int kWideBN1 = MK_WIDE_BN1;  // gate/up columns of each weight per wide tile (64 or 128)
+struct Tiles {
+    int BM, NB1, NB2, S;
+};
+inline Tiles tile_config(const Shape &s, int64_t B) {
+    Tiles t;
+    const bool wide = B * s.k >= (int64_t)kWideBM * s.E;
+    t.BM = wide ? kWideBM : kBM;
+    t.NB1 = s.f / (wide ? kWideBN1 : kBN);
+    t.NB2 = s.d / (wide ? kWideBN : kBN);
+    t.S = wide ? 1 : down_splits(s, B);
+    return t;
+}
+
 // Task counts that depend on B only.
 struct Counts {
     int64_t T;      // top-k / grouping tiles
@@ -102,7 +127,7 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     c.NB1 = s.f / kBN;
     c.NB2 = s.d / kBN;
     c.S = down_splits(s, B);
-    c.q_cap = 2 * c.T + 1 + c.mt_cap * c.NB1 + c.mt_cap * kMaxSplits * c.NB2 + c.nC + 64;
+    c.q_cap = 2 * c.T + 1 + c.mt_cap * c.NB1 + c.mt_cap * kMaxSplits * c.NB2 + c.nC + 128;  // + block padding
     c.nR_max = ceil_div(B, 4) * c.nEB;
     return c;
 }
@@ -166,6 +191,7 @@ struct Params {
     int sched;       // 0 static, 1 dynamic
     int debug;       // MOE_MK_DEBUG_* bits
     int nR, nTG, nEB, T, nC, NB1, NB2, tpw, S;
+    int BM;          // GroupGEMM tile rows (kBM or kWideBM); columns are f / NB1 = d / NB2
     int q_cap, mt_cap;
     long long watchdog;  // real-time ticks (100 MHz)
     MK_G int *ctl, *ev_logit, *ev_exp, *ev_h;

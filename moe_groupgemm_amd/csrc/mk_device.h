@@ -100,7 +100,12 @@ __device__ __forceinline__ bool spin_until(const MK_G int *p, int target, MK_G i
 
 // ---------------------------------------------------------------------------- wave64
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
-__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+// A value every lane of the wave holds alike, made visibly wave-uniform for the compiler
+// (arguments of out-of-line functions arrive in vector registers; branching on them
+// would otherwise be compiled as divergent, with accumulators copied at every join).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// wave index within the workgroup, as a wave-uniform (scalar) value
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 

@@ -52,7 +52,7 @@ def ctl_words(layer, B):
 
 
 def down_splits(B, k, f):
-    """K splits of the down projection the library uses at this batch size."""
+    """K splits of the down projection the library uses at this batch size (narrow tiles)."""
     a, nb1 = B * k, f // 64
     if a <= 1024 and f >= 8192 and nb1 % 4 == 0:
         return 4
@@ -61,9 +61,17 @@ def down_splits(B, k, f):
     return 1
 
 
-def expected_task_counts(hist, B, E, d, f, k):
-    mt = int(sum((int(h) + 63) // 64 for h in hist))
+def tile_config(B, k, E, d, f, wide_bn1=128):
+    """(rows per tile, gate/up tiles per row tile, down tiles per row tile and split, splits):
+    wide 128-row tiles once an expert averages 128 rows, else 64-row tiles."""
+    if B * k >= 128 * E:
+        return 128, f // wide_bn1, d // 128, 1
+    return 64, f // 64, d // 64, down_splits(B, k, f)
+
+
+def expected_task_counts(hist, B, E, d, f, k, wide_bn1=128):
+    BM, NB1, NB2, S = tile_config(B, k, E, d, f, wide_bn1)
+    mt = int(sum((int(h) + BM - 1) // BM for h in hist))
     tpw = 1 if B <= 512 else 4  # router tokens per wave; a router task has 4 waves
-    S = down_splits(B, k, f)
     return {"route": -(-B // (4 * tpw)) * -(-E // 16), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
-            "gemm1": mt * (f // 64), "gemm2": mt * S * (d // 64), "combine": -(-B // 4) * -(-d // 1024)}
+            "gemm1": mt * NB1, "gemm2": mt * S * NB2, "combine": -(-B // 4) * -(-d // 1024)}

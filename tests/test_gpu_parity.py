@@ -14,7 +14,7 @@ import torch
 import moe_groupgemm_amd as mk
 import oracle
 from gpu_cases import (check_out, check_routing, ctl_words, dev_inputs, down_splits, expected_task_counts, log,
-                       routing_numpy)
+                       routing_numpy, tile_config)
 from moe_inputs import (CONFIGS, Config, bf16_bits_to_f32, device_weights, device_x, expert_weights, make_bias,
                         make_wr, make_x, small_case, to_torch_bf16)
 
@@ -118,6 +118,36 @@ def test_down_projection_k_splits(f, S, sched):
     full_check(x, Wr, bias, W1, W3, W2, k, sched, f"S={S}")
 
 
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+@pytest.mark.parametrize("B,d,f,E,k", [(300, 256, 384, 4, 2), (517, 128, 256, 16, 4), (129, 384, 128, 1, 1)])
+def test_wide_tiles(B, d, f, E, k, sched):
+    # an expert averages >= 128 rows: 128-row tiles, ragged last tiles (some with rows for
+    # one of the two row halves only), several K steps of 32
+    assert tile_config(B, k, E, d, f)[0] == 128
+    log(f"wide tiles B={B} d={d} f={f} E={E} k={k} sched={SNAME[sched]}")
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=1300 + B)
+    full_check(x, Wr, bias, W1, W3, W2, k, sched, f"wide B={B}")
+
+
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+def test_wide_tiles_constant_input(sched):
+    # every token identical: k experts take all 260 rows each (tiles of 128, 128 and 4 rows)
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(260, 128, 256, 4, 2, seed=61)
+    x[:] = x[0]
+    assert tile_config(260, 2, 4, 128, 256)[0] == 128
+    full_check(x, Wr, bias, W1, W3, W2, 2, sched, "wide constant input")
+
+
+def test_wide_tiles_static_dynamic_identical():
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(300, 256, 384, 4, 2, seed=1600)
+    outs = []
+    for sched in SCHEDS:
+        layer, out, got = run_small(x, Wr, bias, W1, W3, W2, 2, sched)
+        outs.append(out)
+        layer.close()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
 def test_down_projection_splits_static_dynamic_identical():
     cfg, x, Wr, bias, W1, W3, W2 = small_case(13, 128, 8192, 4, 2, seed=901)
     outs = []
@@ -152,9 +182,10 @@ def test_static_and_dynamic_are_bitwise_identical():
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
-def test_rest_state_and_task_counts(sched):
-    cfg, x, Wr, bias, W1, W3, W2 = small_case(90, 256, 384, 8, 2, seed=12)
-    B, d, f, E = 90, 256, 384, 8
+@pytest.mark.parametrize("B,E", [(90, 8), (300, 4)], ids=["narrow", "wide"])
+def test_rest_state_and_task_counts(B, E, sched):
+    d, f = 256, 384
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, 2, seed=12)
     tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
     layer = mk.MoELayer(E, 2, d, f, tWr, t1, t3, t2, sched=sched, max_batch=B)
     before = ctl_words(layer, B).copy()
@@ -166,10 +197,10 @@ def test_rest_state_and_task_counts(sched):
     C = mk.CTL
     assert c[C["epoch"]] == before[C["epoch"]] + 3    # epoch advanced once per forward
     assert c[C["exit"]] == 0                           # exit counter at rest
-    assert c[C["qhead"]] == c[C["qtail"]] == c[C["hhead"]] == c[C["htail"]] == 0  # queues at rest
+    assert c[C["qhead"]] == c[C["qtail"]] == 0        # queue at rest
     assert c[C["ev_topk"]] == 0 and c[C["ev_scan"]] == 1 and c[C["ev_y"]] == 0  # events at rest
     hist = routing_numpy(layer, B)["hist"]
-    exp = expected_task_counts(hist, B, E, d, f, 2)
+    exp = expected_task_counts(hist, B, E, d, f, 2, mk.moe_mk_plan_info(layer.plan, "wide_BN1"))
     delta = c[C["dbg"]:C["dbg"] + 7] - before[C["dbg"]:C["dbg"] + 7]
     names = ["route", "topk", "scan", "group", "gemm1", "gemm2", "combine"]
     for i, n in enumerate(names):
