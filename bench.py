@@ -124,8 +124,10 @@ def trace_report(layer, x, out, B):
     T = -(-B // 64)
     mt = int(ctl[mk.CTL["mt_total"]])
     a = B * k
-    if a >= 128 * E:  # wide tiles: 128 rows; 64 gate/up columns, 128 down-projection columns
-        S, nb1, nb2 = 1, f // mk.moe_mk_plan_info(layer.plan, "wide_BN1"), d // 128
+    bn1w = mk.moe_mk_plan_info(layer.plan, "wide_BN1")
+    bn2w = mk.moe_mk_plan_info(layer.plan, "wide_BN2")
+    if a >= 128 * E and d % bn2w == 0 and f % bn1w == 0:  # wide tiles (128 rows)
+        S, nb1, nb2 = 1, f // bn1w, d // bn2w
     else:
         S = 4 if (a <= 1024 and f >= 8192 and (f // 64) % 4 == 0) else \
             2 if (a <= 1024 and f >= 4096 and (f // 64) % 2 == 0) else 1

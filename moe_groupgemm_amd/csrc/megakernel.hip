@@ -886,14 +886,15 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
 // ------------------------------------------------------------------------------ wide tiles
 // At large batches (an expert averages 128 rows or more) a tile has 128 rows, K steps are
 // 32 deep, and the four waves split the tile 2 x 2: wave w owns rows 64*(w/2) .. +64 and
-// the (w%2)-th half of the columns.  Gate/up tiles are 64 columns of each weight (wave:
-// 64 x 32 of each); down-projection tiles are 128 columns (wave: 64 x 64).  Either way a
-// wave holds 64 accumulator registers, reads 4 A and 8 B fragment halves per K step in one
-// LDS batch, and issues 16 MFMAs on them.
+// the (w%2)-th half of the columns.  Gate/up tiles are kWideBN1 columns of each weight and
+// down-projection tiles kWideBN columns (with 128 and 256: a wave holds 64 x 64 of gate
+// and of up, or 64 x 128 of the down projection, 128 accumulator registers either way).
+// Per K step a wave reads its 4 A fragments and its B fragments in LDS batches of eight
+// halves and issues 32 MFMAs.
 //   A tile in LDS: [row][k], 64-byte rows; 16-byte chunk c of row r sits at c ^ wswa(r),
 //     so the 16 rows one A fragment read touches fall on 16 distinct 16-byte bank groups.
-//   B tile in LDS: [k][n], rows as in memory (128 bytes: chunk c at c ^ swb(k); 256 bytes:
-//     chunk c at c ^ wswb(k)), so the rows one ds_read_b64_tr_b16 touches spread over
+//   B tile in LDS: [k][n], rows as in memory (128 bytes: chunk c at c ^ swb(k); 256 or 512
+//     bytes: chunk c at c ^ wswb(k)), so the rows one ds_read_b64_tr_b16 touches spread over
 //     distinct bank groups.
 constexpr int kWBK = kWideBK;
 __device__ __forceinline__ int wswa(int r) { return (r >> 2) & 3; }
@@ -910,12 +911,12 @@ struct WideCfg {
     static constexpr int NS = (kRingBytes / 2) / STAGE_ELEMS;
     static constexpr int LOADS = 2 + (B_BLOCKS / 4) * (DUAL ? 2 : 1);  // global_load_lds per wave per stage
     static_assert(NS >= 3, "ring too shallow");
-    static_assert(CB == 2 || CB == 4, "column blocks per wave");
+    static_assert(CB * (DUAL ? 2 : 1) == 4 || CB * (DUAL ? 2 : 1) == 8, "B fragments in batches of four blocks");
 };
 
 template <int BN>
 __device__ __forceinline__ int wide_swb(int k) {
-    return BN == 64 ? swb(k) : wswb(k);
+    return BN == 64 ? swb(k) : wswb(k);  // 256- and 512-byte rows: bank pattern repeats every 256 bytes
 }
 
 // Operands of a wide tile: wave-uniform bases plus 32-bit per-lane element offsets that
@@ -925,7 +926,7 @@ struct WideArgs {
     const MK_G uint16_t *A;   // activation base (x or h)
     uint32_t a_off[2];        // this lane's row start + 16-byte chunk, per A block it loads
     const MK_G uint16_t *B0, *B1;  // weight tile bases (k 0, column n0)
-    uint32_t b_off[2];        // this lane's k-row * ldb + 16-byte chunk, per B block it loads
+    uint32_t b_off[4];        // this lane's k-row * ldb + 16-byte chunk, per B block it loads
     int ldb, K, nrows;
 };
 
@@ -964,8 +965,8 @@ __device__ __forceinline__ void wide_offsets(WideArgs &g, RowOf arow) {
     constexpr int CPR = BN / 8;    // 16-byte chunks per k-row
     constexpr int RPB = 64 / CPR;  // k-rows per 1 KB block
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int blk = (C::B_BLOCKS / 4) * w + (i < C::B_BLOCKS / 4 ? i : 0);
+    for (int i = 0; i < C::B_BLOCKS / 4; ++i) {
+        const int blk = (C::B_BLOCKS / 4) * w + i;
         const int kr = RPB * blk + lane / CPR;
         g.b_off[i] = (uint32_t)kr * (uint32_t)g.ldb + 8u * (uint32_t)((lane % CPR) ^ wide_swb<BN>(kr));
     }
@@ -1018,6 +1019,7 @@ __device__ __forceinline__ void wstage_compute(const uint16_t *stage, f32x4 (&ac
                                                f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC]) {
     using C = WideCfg<DUAL, BN>;
     constexpr int CB = C::CB;
+    constexpr int U = CB * (DUAL ? 2 : 1);  // 16-column B blocks of the wave (both weights)
     const uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, i = lane & 15;
@@ -1031,55 +1033,29 @@ __device__ __forceinline__ void wstage_compute(const uint16_t *stage, f32x4 (&ac
     }
     u32x2 b[8];
     u32x4 a[4];
-    if constexpr (CB == 2) {
 #pragma unroll
-        for (int q = 0; q < (DUAL ? 2 : 1); ++q)
+    for (int bt = 0; bt < U / 4; ++bt) {
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const uint16_t *sB = q ? sB1 : sB0;
-                ba[2 * (q * CB + cb)] = wb_frag_addr<BN>(sB, kb, c0 + 16 * cb);
-                ba[2 * (q * CB + cb) + 1] = wb_frag_addr<BN>(sB, kb + 4, c0 + 16 * cb);
-            }
-        wide_reads(ba, aa, b, a);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            if (rb < NRB)
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    acc0[CB * rb + cb] =
-                        mfma_bf16_16x16x32(a[rb], join(b[2 * cb], b[2 * cb + 1]), acc0[CB * rb + cb]);
-                    if constexpr (DUAL)
-                        acc1[CB * rb + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * (CB + cb)], b[2 * (CB + cb) + 1]),
-                                                                acc1[CB * rb + cb]);
-                }
-    } else {
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            ba[2 * cb] = wb_frag_addr<BN>(sB0, kb, c0 + 16 * cb);
-            ba[2 * cb + 1] = wb_frag_addr<BN>(sB0, kb + 4, c0 + 16 * cb);
+        for (int jj = 0; jj < 4; ++jj) {
+            const int u = 4 * bt + jj, q = u / CB, cb = u % CB;
+            const uint16_t *sB = q ? sB1 : sB0;
+            ba[2 * jj] = wb_frag_addr<BN>(sB, kb, c0 + 16 * cb);
+            ba[2 * jj + 1] = wb_frag_addr<BN>(sB, kb + 4, c0 + 16 * cb);
         }
-        wide_reads(ba, aa, b, a);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            if (rb < NRB)
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
-                    acc0[4 * rb + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * cb], b[2 * cb + 1]), acc0[4 * rb + cb]);
-        if constexpr (DUAL) {
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                ba[2 * cb] = wb_frag_addr<BN>(sB1, kb, c0 + 16 * cb);
-                ba[2 * cb + 1] = wb_frag_addr<BN>(sB1, kb + 4, c0 + 16 * cb);
-            }
+        if (bt == 0)
+            wide_reads(ba, aa, b, a);
+        else
             wide_reads_b(ba, b);
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-                if (rb < NRB)
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-                    for (int cb = 0; cb < 4; ++cb)
-                        acc1[4 * rb + cb] =
-                            mfma_bf16_16x16x32(a[rb], join(b[2 * cb], b[2 * cb + 1]), acc1[4 * rb + cb]);
-        }
+            for (int jj = 0; jj < 4; ++jj) {
+                const int u = 4 * bt + jj, q = u / CB, cb = u % CB;
+                if (q == 0)
+                    acc0[CB * rb + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * jj], b[2 * jj + 1]), acc0[CB * rb + cb]);
+                else
+                    acc1[CB * rb + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * jj], b[2 * jj + 1]), acc1[CB * rb + cb]);
+            }
     }
 }
 
@@ -1178,7 +1154,7 @@ __device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &P, int e
             }
 }
 
-// Wide down-projection tile: 128 rows x 128 columns of y.
+// Wide down-projection tile: 128 rows x kWideBN columns of y.
 __device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n) {
     e = uni(e);
     row0 = uni(row0);

@@ -80,7 +80,7 @@ constexpr int kMaxSplits = 4;
 // weight byte serves twice the rows.  Workspace sizes are bounded with the narrow counts,
 // which are never smaller.
 constexpr int kWideBM = 128;
-constexpr int kWideBN = 128;
+constexpr int kWideBN = 256;   // down-projection columns per wide tile
 constexpr int kWideBK = 32;
 #ifndef MK_WIDE_BN1
 #define MK_WIDE_BN1 128
@@ -91,7 +91,7 @@ struct Tiles {
 };
 inline Tiles tile_config(const Shape &s, int64_t B) {
     Tiles t;
-    const bool wide = B * s.k >= (int64_t)kWideBM * s.E;
+    const bool wide = B * s.k >= (int64_t)kWideBM * s.E && s.d % kWideBN == 0 && s.f % kWideBN1 == 0;
     t.BM = wide ? kWideBM : kBM;
     t.NB1 = s.f / (wide ? kWideBN1 : kBN);
     t.NB2 = s.d / (wide ? kWideBN : kBN);

@@ -63,9 +63,9 @@ def down_splits(B, k, f):
 
 def tile_config(B, k, E, d, f, wide_bn1=128):
     """(rows per tile, gate/up tiles per row tile, down tiles per row tile and split, splits):
-    wide 128-row tiles once an expert averages 128 rows, else 64-row tiles."""
-    if B * k >= 128 * E:
-        return 128, f // wide_bn1, d // 128, 1
+    wide 128-row tiles once an expert averages 128 rows (d a multiple of 256), else 64-row tiles."""
+    if B * k >= 128 * E and d % 256 == 0 and f % wide_bn1 == 0:
+        return 128, f // wide_bn1, d // 256, 1
     return 64, f // 64, d // 64, down_splits(B, k, f)
 
 

@@ -119,7 +119,7 @@ def test_down_projection_k_splits(f, S, sched):
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
-@pytest.mark.parametrize("B,d,f,E,k", [(300, 256, 384, 4, 2), (517, 128, 256, 16, 4), (129, 384, 128, 1, 1)])
+@pytest.mark.parametrize("B,d,f,E,k", [(300, 256, 384, 4, 2), (517, 256, 256, 16, 4), (129, 512, 128, 1, 1)])
 def test_wide_tiles(B, d, f, E, k, sched):
     # an expert averages >= 128 rows: 128-row tiles, ragged last tiles (some with rows for
     # one of the two row halves only), several K steps of 32
@@ -132,9 +132,9 @@ def test_wide_tiles(B, d, f, E, k, sched):
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
 def test_wide_tiles_constant_input(sched):
     # every token identical: k experts take all 260 rows each (tiles of 128, 128 and 4 rows)
-    cfg, x, Wr, bias, W1, W3, W2 = small_case(260, 128, 256, 4, 2, seed=61)
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(260, 256, 256, 4, 2, seed=61)
     x[:] = x[0]
-    assert tile_config(260, 2, 4, 128, 256)[0] == 128
+    assert tile_config(260, 2, 4, 256, 256)[0] == 128
     full_check(x, Wr, bias, W1, W3, W2, 2, sched, "wide constant input")
 
 
