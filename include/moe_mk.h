@@ -116,7 +116,7 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
  *   perm      int32 [B*k]    perm[p] = b*k + i: the assignment held by grouped row p
  *   inv       int32 [B*k]    inverse of perm
  *   logits    fp32  [B, E]   router logits
- *   ctl       int32 [256]    control block (ctl[2] is the error word, see below; ctl[9] the
+ *   ctl       int32 [512]    control block (ctl[2] is the error word, see below; ctl[9] the
  *                            number of (expert, row tile) pairs; ctl[192..198] per-kind task
  *                            counters accumulated over forwards)
  * Errors: EINVAL, EWORKSPACE.

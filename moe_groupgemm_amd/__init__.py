@@ -26,9 +26,9 @@ MOE_MK_DEBUG_DROP_NOTIFY = 1
 MOE_MK_DEBUG_TRACE = 2
 TASK_KINDS = ("route", "topk", "scan", "group", "gemm1", "gemm2", "combine")
 # control block words (see moe_mk_routing_view)
-CTL_WORDS = 256
+CTL_WORDS = 512
 CTL = {"epoch": 0, "exit": 1, "err": 2, "ev_topk": 5, "ev_scan": 6, "magic": 8, "mt_total": 9,
-       "qhead": 32, "qtail": 64, "ev_y": 160, "dbg": 192}
+       "qhead": 32, "qtail": 64, "ev_y": 160, "dbg": 192, "xq": 256}
 
 _lib = None
 

@@ -191,7 +191,8 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.perm = (int *)(base + L.perm);
     P.inv = (int *)(base + L.inv);
     P.h = (uint16_t *)(base + L.h);
-    P.y = (float *)(base + L.y);
+    P.y = (uint16_t *)(base + L.y);
+    P.yp = (float *)(base + L.yp);
     P.qslots = (unsigned long long *)(base + L.qslots);
     P.red_ctr = (int *)(base + L.red_ctr);
     P.trace = (long long *)(base + L.trace);

@@ -215,6 +215,42 @@ __device__ __forceinline__ bool wg_notify(const MK_C Params &P, MK_G int *ctr, i
     return fired;
 }
 
+// ------------------------------------------------------------------------------ LDS DMA helpers
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes land at
+// dst_wave_base + 16 L.
+__device__ __forceinline__ void lds_dma16(const MK_G void *src, MK_L void *dst_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, dst_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t *p) {
+    return (uint32_t)(uintptr_t)(const MK_L uint16_t *)p;
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+// Workgroup barrier without the memory-model fences of __syncthreads (which would wait
+// for every LDS-DMA load in flight); the empty asm statements keep the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Round v to bf16 and store it at row[col], two adjacent columns per 4-byte store: the
+// value of column col+1 sits in the next lane, and the even lane stores both.  Every lane
+// of the wave must call (the pair is exchanged across lanes); ok masks the store.
+__device__ __forceinline__ void store_bf16_pair(MK_G uint16_t *row, int col, float v, bool ok) {
+    const uint32_t hv = f32_to_bf16(v);
+    const uint32_t nb = (uint32_t)__shfl_xor((int)hv, 1, 64);
+    if (ok && (col & 1) == 0) pub((MK_G uint32_t *)(row + col), hv | (nb << 16));
+}
+
 // ------------------------------------------------------------------------------ ROUTE
 // logit[b,e] = sum_j x[b,j] Wr[j,e] (+ bias[e]) in the fixed fp32 order: lane l of the
 // wave accumulates j = l, l+64, ... with fma (one chain per lane), then the 64 chains are
@@ -246,80 +282,12 @@ __device__ __forceinline__ void reduce_scatter(float *v, int lane) {
     }
 }
 
-// One wave: TPW tokens from b0, 16 experts from e0.  Lane l owns the chains j = l, l+64,
-// ...; the loads of the next PF steps are in flight while a step is accumulated.  Tokens
-// or experts past the end load clamped (valid) addresses; their sums are never written.
+// Sums of one wave (lane l holds chain l of every (token, expert) pair it owns) reduced
+// over the lanes in the halves-fold order and written as logits (bias added last).
 template <int TPW>
-__device__ __attribute__((noinline)) void route_wave(const MK_C Params &P, int b0, int e0) {
-    constexpr int PF = TPW == 1 ? 8 : 4;
+__device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[TPW * 16], int b0, int e0) {
     constexpr int NV = TPW * 16;
     const int lane = lane_id();
-    float acc[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-    const MK_G uint16_t *xp[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) xp[t] = P.x + (size_t)min(b0 + t, P.B - 1) * P.d + lane;
-    const int nst = P.d / 64;
-    if ((P.E & 3) == 0) {
-        int cq[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cq[q] = min(e0 + 4 * q, P.E - 4);
-        const MK_G float *wp = P.Wr + (size_t)lane * P.E;
-        const size_t wstep = (size_t)64 * P.E;
-        uint16_t xr[PF][TPW];  // raw bits: converted when used, not when the load is issued
-        f32x4 wr[PF][4];
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int ps = min(p, nst - 1);
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) xr[p][t] = xp[t][(size_t)ps * 64];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) wr[p][q] = *(const MK_G f32x4 *)(wp + (size_t)ps * wstep + cq[q]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // Steady state without branches (a join inside the loop would make the compiler
-        // wait for every load in flight): prefetch addresses are clamped to the last step,
-        // and steps past the end are masked by x = 0, which leaves every chain bitwise
-        // unchanged (0 * w is a signed zero, and a chain that starts at +0 is never -0).
-        for (int s0 = 0; s0 < nst; s0 += PF) {
-#pragma unroll
-            for (int u = 0; u < PF; ++u) {
-                const int st = s0 + u;
-                const bool live = st < nst;
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) {
-                    const float xm = live ? bf16_to_f32(xr[u][t]) : 0.0f;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-#pragma unroll
-                        for (int z = 0; z < 4; ++z)
-                            acc[t * 16 + 4 * q + z] = fmaf(xm, wr[u][q][z], acc[t * 16 + 4 * q + z]);
-                }
-                const int nx = min(st + PF, nst - 1);
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) xr[u][t] = xp[t][(size_t)nx * 64];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) wr[u][q] = *(const MK_G f32x4 *)(wp + (size_t)nx * wstep + cq[q]);
-                // keep the refill here: the scheduler would otherwise sink each load down to
-                // its use PF steps later, serialising the chain on memory latency
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    } else {  // E not a multiple of 4: plain scalar loads, same summation order
-        for (int st = 0; st < nst; ++st) {
-            const int j = st * 64 + lane;
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const float xv = bf16_to_f32(xp[t][(size_t)st * 64]);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float wv = P.Wr[(size_t)j * P.E + min(e0 + e, P.E - 1)];
-                    acc[t * 16 + e] = fmaf(xv, wv, acc[t * 16 + e]);
-                }
-            }
-        }
-    }
     reduce_scatter<NV, 32>(acc, lane);
     // lane L holds value L >> SH: token t = value / 16, expert e0 + value % 16
     constexpr int SH = NV == 64 ? 0 : 2;
@@ -335,15 +303,155 @@ __device__ __attribute__((noinline)) void route_wave(const MK_C Params &P, int b
     }
 }
 
+// Router tile through LDS (E a multiple of 4).  The workgroup's 4*TPW tokens (wave w owns
+// TPW of them) and 16 experts share every staged slice: per 64 values of j, the 64 x 16
+// block of Wr (4 KB, each wave moving 16 of its rows) and the tokens' 64 x values (each
+// wave moving its own), in a ring of kRouteStages stages filled by global_load_lds.  Lane l
+// accumulates chain l (j = l, l+64, ... in order) of every (token, expert) pair of its wave.
+//   Wr stage in LDS: [64 rows][4 chunks of 4 experts]; chunk c of row r at c ^ rswz(r), so
+//     the 16 rows a quarter-wave reads fall on distinct 16-byte bank groups.
+//   x stage: per wave, NX blocks of 256 bytes, each two token rows of 64 bf16.
+// Tokens past B and experts past E load clamped (valid) addresses; their sums are never
+// written.
+constexpr int kRouteStages = 12;
+__device__ __forceinline__ int rswz(int r) { return (r >> 2) & 3; }
+
+template <int TPW>
+struct RouteCfg {
+    static constexpr int NX = TPW == 1 ? 1 : TPW / 2;  // 256-byte x loads per wave and stage
+    static constexpr int WR_BYTES = 64 * 16 * 4;
+    static constexpr int STAGE_BYTES = WR_BYTES + 4 * NX * 256;
+    static constexpr int LOADS = 1 + NX;
+    static_assert(kRouteStages * STAGE_BYTES <= kRingBytes, "router ring");
+    static_assert((kRouteStages - 2) * LOADS < 64, "vmcnt range");
+};
+
+template <int TPW>
+__device__ __forceinline__ void route_reads(uint32_t wa, const uint32_t (&xa)[TPW], f32x4 (&wv)[4],
+                                            uint32_t (&xr)[TPW]) {
+    const uint32_t w1 = wa ^ 16u, w2 = wa ^ 32u, w3 = wa ^ 48u;
+    if constexpr (TPW == 1) {
+        asm volatile(
+            "ds_read_b128 %0, %5\n\tds_read_b128 %1, %6\n\tds_read_b128 %2, %7\n\tds_read_b128 %3, %8\n\t"
+            "ds_read_u16 %4, %9\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(wv[0]), "=&v"(wv[1]), "=&v"(wv[2]), "=&v"(wv[3]), "=&v"(xr[0])
+            : "v"(wa), "v"(w1), "v"(w2), "v"(w3), "v"(xa[0]));
+    } else {
+        static_assert(TPW == 4, "router tokens per wave");
+        asm volatile(
+            "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+            "ds_read_u16 %4, %12\n\tds_read_u16 %5, %13\n\tds_read_u16 %6, %14\n\tds_read_u16 %7, %15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(wv[0]), "=&v"(wv[1]), "=&v"(wv[2]), "=&v"(wv[3]), "=&v"(xr[0]), "=&v"(xr[1]), "=&v"(xr[2]),
+              "=&v"(xr[3])
+            : "v"(wa), "v"(w1), "v"(w2), "v"(w3), "v"(xa[0]), "v"(xa[1]), "v"(xa[2]), "v"(xa[3]));
+    }
+}
+
+template <int TPW>
+__device__ __attribute__((noinline)) void route_tile(const MK_C Params &P, int b0, int e0) {
+    using C = RouteCfg<TPW>;
+    constexpr int NS = kRouteStages;
+    b0 = uni(b0);
+    e0 = uni(e0);
+    uint8_t *ring = (uint8_t *)g_sm.u.g.ring;
+    const int lane = lane_id(), w = wave_id();
+    const int nst = uni(P.d / 64);
+    const int E = P.E;
+    // this lane's DMA sources: Wr row 16w + lane/4 (chunk position lane%4) and, per x
+    // block i, token slot 2i + lane/32 of the wave at j pair 2*(lane%32)
+    const int wrow = 16 * w + (lane >> 2);
+    const int wcol = min(e0 + 4 * ((lane & 3) ^ rswz(wrow)), E - 4);
+    const MK_G float *wsrc = P.Wr + (size_t)wrow * E + wcol;
+    const MK_G uint16_t *xsrc[C::NX];
+#pragma unroll
+    for (int i = 0; i < C::NX; ++i) {
+        const int slot = min(2 * i + (lane >> 5), TPW - 1);
+        const int tok = min(b0 + w * TPW + slot, P.B - 1);
+        xsrc[i] = P.x + (size_t)tok * P.d + 2 * (lane & 31);
+    }
+    const size_t wstep = (size_t)64 * E;
+    auto load = [&](int st, int s) {
+        uint8_t *sp = ring + s * C::STAGE_BYTES;
+        lds_dma16(wsrc + (size_t)st * wstep, (MK_L void *)(sp + w * 1024));
+#pragma unroll
+        for (int i = 0; i < C::NX; ++i)
+            __builtin_amdgcn_global_load_lds(xsrc[i] + (size_t)st * 64,
+                                             (MK_L void *)(sp + C::WR_BYTES + (w * C::NX + i) * 256), 4, 0, 0);
+    };
+    // this lane's LDS reads: Wr row lane (chunk q at position q ^ rswz(lane)) and x[t][lane]
+    const uint32_t wa0 = (uint32_t)(lane * 64 + 16 * rswz(lane));
+    uint32_t xa0[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) xa0[t] = (uint32_t)(C::WR_BYTES + (w * C::NX + t / 2) * 256 + (t & 1) * 128 + 2 * lane);
+    float acc[TPW * 16];
+#pragma unroll
+    for (int i = 0; i < TPW * 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < nst) load(p, p);
+    const uint32_t rbase = lds_addr((const uint16_t *)ring);
+    int slot = 0;
+    for (int st = 0; st < nst; ++st) {
+        if (st + NS - 2 < nst)
+            wait_vm<(NS - 2) * C::LOADS>();
+        else
+            wait_vm<0>();
+        bare_barrier();
+        const int nxt = st + NS - 1;
+        if (nxt < nst) load(nxt, slot == 0 ? NS - 1 : slot - 1);
+        const uint32_t sb = rbase + (uint32_t)(slot * C::STAGE_BYTES);
+        uint32_t xa[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) xa[t] = sb + xa0[t];
+        f32x4 wv[4];
+        uint32_t xr[TPW];
+        route_reads<TPW>(sb + wa0, xa, wv, xr);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const float xf = __uint_as_float(xr[t] << 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int z = 0; z < 4; ++z) acc[t * 16 + 4 * q + z] = fmaf(xf, wv[q][z], acc[t * 16 + 4 * q + z]);
+        }
+        slot = slot == NS - 1 ? 0 : slot + 1;
+    }
+    wait_vm<0>();
+    __syncthreads();  // the ring may be reused by the next task
+    route_write<TPW>(P, acc, b0 + w * TPW, e0);
+}
+
+// Router wave for E not a multiple of 4: plain scalar loads, same summation order.
+__device__ __attribute__((noinline)) void route_wave_scalar(const MK_C Params &P, int b0, int e0) {
+    const int lane = lane_id();
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    const MK_G uint16_t *xp = P.x + (size_t)min(b0, P.B - 1) * P.d + lane;
+    const int nst = P.d / 64;
+    for (int st = 0; st < nst; ++st) {
+        const int j = st * 64 + lane;
+        const float xv = bf16_to_f32(xp[(size_t)st * 64]);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float wv = P.Wr[(size_t)j * P.E + min(e0 + e, P.E - 1)];
+            acc[e] = fmaf(xv, wv, acc[e]);
+        }
+    }
+    route_write<1>(P, acc, b0, e0);
+}
+
 // Router task (tg, eb): tokens [4*tpw*tg, +4*tpw), wave w taking tpw of them, experts
 // [16*eb, +16).
 __device__ __attribute__((noinline)) void task_route(const MK_C Params &P, int tg, int eb) {
-    const int w = wave_id();
     const int e0 = eb * kRouteExperts;
-    if (P.tpw == 1)
-        route_wave<1>(P, tg * 4 + w, e0);
+    if ((P.E & 3) != 0)
+        route_wave_scalar(P, tg * 4 + wave_id(), e0);
+    else if (P.tpw == 1)
+        route_tile<1>(P, tg * 4, e0);
     else
-        route_wave<4>(P, tg * 16 + w * 4, e0);
+        route_tile<4>(P, tg * 16, e0);
 }
 
 // ------------------------------------------------------------------------------ TOPK
@@ -603,9 +711,6 @@ struct GemmArgs {
     int ldb, K;
 };
 
-__device__ __forceinline__ void lds_dma16(const MK_G void *src, MK_L void *dst_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, dst_wave_base, 16, 0, 0);
-}
 
 // A row loaded by this lane into 1 KB block i of the A tile (8 rows of 128 bytes each).
 template <int AR>
@@ -640,9 +745,6 @@ __device__ __forceinline__ void stage_load(const GemmArgs &g, int k0, uint16_t *
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t *p) {
-    return (uint32_t)(uintptr_t)(const MK_L uint16_t *)p;
-}
 
 // LDS byte address of this lane's half of a B fragment (rows kbase + l/4, columns
 // ncol0 + 4*(l%4)).
@@ -729,20 +831,7 @@ __device__ __forceinline__ void stage_compute(const uint16_t *stage, int nrb, f3
     }
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
 
-// Workgroup barrier without the memory-model fences of __syncthreads (which would wait
-// for every LDS-DMA load in flight); the empty asm statements keep the compiler from
-// moving memory operations across it.
-__device__ __forceinline__ void bare_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 template <bool DUAL, int AR>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], f32x4 (&acc1)[4], GemmSmem &s) {
@@ -819,10 +908,10 @@ __device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0
     }
 }
 
-// Down-projection tile over f range sp.  With S > 1 splits, every split stores its partial
-// result in y[sp]; the split that finishes a tile last (a per-tile counter) adds the S
-// partials in split order and writes the sum to y[0], so the result does not depend on
-// which split finished last.  With S = 1 the tile writes y[0] directly.
+// Down-projection tile over f range sp.  With S = 1 the tile writes y (bf16) directly.
+// With S > 1 splits, every split stores its fp32 partial in yp[sp]; the split that
+// finishes a tile last (a per-tile counter) adds the S partials in split order and writes
+// the rounded sum to y, so the result does not depend on which split finished last.
 template <int AR>
 __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0, int nrows, int n, int sp,
                                            int mt) {
@@ -840,8 +929,18 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
     const int col = n * kBN + 16 * w + j;
+    if (P.S == 1) {
+#pragma unroll
+        for (int rb = 0; rb < AR / 16; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rb + 4 * g + r;
+                store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, col, acc0[rb][r], row < nrows);
+            }
+        return;
+    }
     const size_t split_stride = (size_t)P.B * P.k * P.d;  // floats between partial buffers
-    MK_G float *ys = P.y + (size_t)sp * split_stride;
+    MK_G float *ys = P.yp + (size_t)sp * split_stride;
 #pragma unroll
     for (int rb = 0; rb < AR / 16; ++rb) {
 #pragma unroll
@@ -850,7 +949,6 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
             if (row < nrows) pub(ys + (size_t)(row0 + row) * P.d + col, acc0[rb][r]);
         }
     }
-    if (P.S == 1) return;
     // count finished splits of this tile; the last one reduces
     wg_stores_done();
     if (threadIdx.x == 0) {
@@ -870,15 +968,13 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rb + 4 * g + r;
-            if (row < nrows) {
-                const size_t o = (size_t)(row0 + row) * P.d + col;
-                float sum = 0.0f;
-                for (int q = 0; q < P.S; ++q) {
-                    const float v = q == sp ? acc0[rb][r] : P.y[(size_t)q * split_stride + o];
-                    sum = q == 0 ? v : sum + v;
-                }
-                pub(P.y + o, sum);
+            const size_t o = (size_t)(row0 + min(row, nrows - 1)) * P.d + col;
+            float sum = 0.0f;
+            for (int q = 0; q < P.S; ++q) {
+                const float v = q == sp ? acc0[rb][r] : P.yp[(size_t)q * split_stride + o];
+                sum = q == 0 ? v : sum + v;
             }
+            store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, col, sum, row < nrows);
         }
     }
 }
@@ -1182,7 +1278,7 @@ __device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &P, int e
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = r0 + 16 * rb + 4 * g + r;
-                if (row < nrows) pub(P.y + (size_t)(row0 + row) * P.d + c0 + 16 * cb + j, acc0[C::CB * rb + cb][r]);
+                store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, c0 + 16 * cb + j, acc0[C::CB * rb + cb][r], row < nrows);
             }
 }
 
@@ -1238,18 +1334,22 @@ __device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int
     if (4 * q < P.d) {
         for (int bb = 0; bb < nb; ++bb) {
             // all k rows of this token in flight before any is used
-            f32x4 yv[kMaxK];
+            u32x2 yv[kMaxK];
 #pragma unroll
             for (int i = 0; i < kMaxK; ++i)
-                if (i < k) yv[i] = *(const MK_G f32x4 *)(P.y + (size_t)cs.row[bb * k + i] * P.d + 4 * q);
+                if (i < k) yv[i] = *(const MK_G u32x2 *)(P.y + (size_t)cs.row[bb * k + i] * P.d + 4 * q);
             __builtin_amdgcn_sched_barrier(0);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < kMaxK; ++i) {
                 if (i < k) {
                     const float wgt = cs.w[bb * k + i];
-#pragma unroll
-                    for (int z = 0; z < 4; ++z) acc[z] = fmaf(wgt, yv[i][z], acc[z]);
+                    const float y0 = __uint_as_float(yv[i][0] << 16), y1 = __uint_as_float(yv[i][0] & 0xffff0000u);
+                    const float y2 = __uint_as_float(yv[i][1] << 16), y3 = __uint_as_float(yv[i][1] & 0xffff0000u);
+                    acc[0] = fmaf(wgt, y0, acc[0]);
+                    acc[1] = fmaf(wgt, y1, acc[1]);
+                    acc[2] = fmaf(wgt, y2, acc[2]);
+                    acc[3] = fmaf(wgt, y3, acc[3]);
                 }
             }
             const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
@@ -1520,13 +1620,24 @@ __global__ void __launch_bounds__(kThreads, 2) moe_megakernel(Params Parg) {
     }
     Bases bs = initial_bases(P);
     if (P.sched == 0) {
-        for (int g = blockIdx.x;; g += gridDim.x) {
-            if (g >= bs.M1 && !bs.known) {
-                if (!wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) break;
-                complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
+        // Routing tasks: workgroup w runs g = w, w + G, ... below the GroupGEMM blocks.
+        bool ok = true;
+        for (int g = blockIdx.x; g < bs.M1p && ok; g += gridDim.x) ok = run_task(P, g, bs, now_ticks());
+        // GroupGEMM and combine tasks: position p belongs to XCD p % 8 (blocks start at
+        // multiples of 8); the workgroups of an XCD (w % 8 == x, as the hardware deals
+        // them) take that XCD's positions in increasing order from its claim counter, so
+        // tiles adjacent in the list start together and share their operands in L2.
+        if (ok && wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) {
+            complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
+            const int x = blockIdx.x & 7;
+            for (;;) {
+                if (threadIdx.x == 0) g_sm.bcast[3] = add_relaxed(P.ctl + CTL_XQ + 32 * x, 1);
+                __syncthreads();
+                const int g = bs.M1p + 8 * g_sm.bcast[3] + x;
+                __syncthreads();
+                if (g >= bs.total) break;
+                if (!run_task(P, g, bs, now_ticks())) break;
             }
-            if (bs.known && g >= bs.total) break;
-            if (!run_task(P, g, bs, now_ticks())) break;
         }
     } else {
         for (;;) {
@@ -1546,6 +1657,7 @@ __global__ void __launch_bounds__(kThreads, 2) moe_megakernel(Params Parg) {
                 st_relaxed(P.ctl + CTL_QHEAD, 0);
                 st_relaxed(P.ctl + CTL_QTAIL, 0);
                 st_relaxed(P.ctl + CTL_EV_SCAN, 1);
+                for (int x = 0; x < 8; ++x) st_relaxed(P.ctl + CTL_XQ + 32 * x, 0);
             }
             st_relaxed(P.ctl + CTL_EXIT, 0);
             st_relaxed(P.ctl + CTL_EPOCH, g_sm.epoch + 1);

@@ -44,7 +44,8 @@ enum CtlWord {
     CTL_QTAIL = 64,     // dynamic queue: slots reserved by pushers
     CTL_EV_Y = 160,     // event: all down-projection tiles done
     CTL_DBG = 192,      // 8 per-kind task counters (accumulate across forwards)
-    CTL_WORDS = 256
+    CTL_XQ = 256,       // static schedule: claim counter of XCD x's GroupGEMM list at 256 + 32x
+    CTL_WORDS = 512
 };
 
 constexpr int32_t kMagic = 0x4d4f4531;  // "MOE1"
@@ -135,7 +136,7 @@ inline Counts make_counts(const Shape &s, int64_t B) {
 // Byte offsets of every workspace array, for a workspace sized for B = cap tokens.
 struct Layout {
     size_t ctl, ev_logit, ev_exp, ev_h, logits, topk_idx, topk_w, tile_hist, tile_off, hist, indptr,
-        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, h, y, red_ctr, qslots, trace, total;
+        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, h, y, yp, red_ctr, qslots, trace, total;
     int64_t cap;
 };
 
@@ -170,9 +171,9 @@ inline Layout make_layout(const Shape &s, int64_t cap) {
     L.perm = take((size_t)A * 4);
     L.inv = take((size_t)A * 4);
     L.h = take((size_t)A * s.f * 2);
-    // y holds S partial results of B*k rows each; S > 1 only when B*k <= 1024
-    const int64_t y_rows = A > kMaxSplits * (A < 1024 ? A : 1024) ? A : kMaxSplits * (A < 1024 ? A : 1024);
-    L.y = take((size_t)y_rows * s.d * 4);
+    L.y = take((size_t)A * s.d * 2);
+    // yp holds S fp32 partial results of B*k rows each; S > 1 only when B*k <= 1024
+    L.yp = take((size_t)kMaxSplits * (A < 1024 ? A : 1024) * s.d * 4);
     L.red_ctr = take((size_t)c.mt_cap * c.NB2 * 4);
     L.qslots = take((size_t)c.q_cap * 8);
     L.trace = take((size_t)(c.q_cap + c.nR_max) * 8 * 8);
@@ -200,7 +201,8 @@ struct Params {
     MK_G float *topk_w;
     MK_G int *tile_hist, *tile_off, *hist, *indptr, *mt_base, *mt_expert, *mt_row0, *mt_rows, *perm, *inv;
     MK_G uint16_t *h;
-    MK_G float *y;
+    MK_G uint16_t *y;   // down-projection output, bf16 [B*k, d] in grouped row order
+    MK_G float *yp;     // fp32 partials of the split down projection
     MK_G unsigned long long *qslots;
     MK_G int *red_ctr;      // per down-projection tile: splits finished (rest 0)
     MK_G long long *trace;  // 8 int64 per task when tracing is on
