@@ -457,18 +457,32 @@ __device__ __attribute__((noinline)) void task_route(const MK_C Params &P, int t
 // ------------------------------------------------------------------------------ TOPK
 // For each token: the k largest logits (ties to the lower expert index; -0 equals +0),
 // then softmax over them in fp32.  Keys are (order-preserving logit bits, ~expert) so the
-// larger key is the larger logit and, among equal logits, the smaller expert.  The tile's
-// logits are staged in LDS; wave w keeps, for every token (one per lane), a sorted list
-// of the best keys among its quarter of the experts; wave 0 then merges the four lists.
+// larger key is the larger logit and, among equal logits, the smaller expert; keys are
+// unique, so the selected set and its order do not depend on the order of insertion.
+// The tile's logits are staged in LDS.  Four lanes share a token (16 tokens per wave):
+// lane quarter q keeps a sorted list of the best keys among experts [q*per, (q+1)*per),
+// visited from a per-token starting offset so the lanes of a wave read distinct LDS
+// banks; two butterfly rounds over lane pairs (xor 1, then xor 2) merge the four lists.
 
 template <int KB>
 __device__ __forceinline__ void key_insert(unsigned long long (&keys)[KB], unsigned long long v) {
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-        const unsigned long long hi = keys[i] > v ? keys[i] : v;
-        v = keys[i] > v ? v : keys[i];
+        const bool c = keys[i] > v;
+        const unsigned long long hi = c ? keys[i] : v;
+        v = c ? v : keys[i];
         keys[i] = hi;
     }
+}
+
+// Exchange with lane ^ 1 or lane ^ 2 inside each group of four lanes (DPP quad permutes,
+// no LDS round trip).
+template <int M>
+__device__ __forceinline__ unsigned long long quad_xor_u64(unsigned long long v) {
+    constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] or [2,3,0,1]
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, ctrl, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, false);
+    return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
 template <int KB>
@@ -491,39 +505,57 @@ __device__ __attribute__((noinline)) void topk_tile(const MK_C Params &P, int t)
     }
     for (int i = threadIdx.x; i < E; i += kThreads) ts.hist[i] = 0;
     __syncthreads();
-    // local lists over experts [e_lo, e_hi)
+    const int tok = 16 * w + (lane >> 2), q = lane & 3;
     const int per = (E + 3) / 4;
-    const int e_lo = min(E, w * per), e_hi = min(E, e_lo + per);
+    const int e_lo = q * per, n_e = max(0, min(per, E - e_lo));
+    const int s0 = tok % per;
     unsigned long long keys[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) keys[i] = 0ull;
-    if (lane < ntok) {
-        for (int e = e_lo; e < e_hi; ++e) {
-            const float l = ts.lg[lane * E + e] + 0.0f;  // folds -0 onto +0
-            key_insert<KB>(keys, ((unsigned long long)float_key(l) << 32) | (0xffffffffu - (uint32_t)e));
+    const float *row = ts.lg + tok * E + e_lo;
+    // eight logits read ahead of their insertions; visits past the quarter read a valid
+    // address and insert nothing (key 0 ranks below every real key)
+    for (int i0 = 0; i0 < per; i0 += 8) {
+        float lv[8];
+        int ev[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            int idx = i0 + u + s0;
+            idx -= idx >= per ? per : 0;
+            idx -= idx >= per ? per : 0;
+            ev[u] = i0 + u < per && idx < n_e ? idx : -1;
+            lv[u] = row[ev[u] >= 0 ? idx : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float l = lv[u] + 0.0f;  // folds -0 onto +0
+            const unsigned long long key =
+                ((unsigned long long)float_key(l) << 32) | (0xffffffffu - (uint32_t)(e_lo + ev[u]));
+            key_insert<KB>(keys, ev[u] >= 0 ? key : 0ull);
         }
     }
-    __syncthreads();  // logits no longer needed: the area now holds the candidate lists
-    unsigned long long *cand = (unsigned long long *)ts.lg;  // [3 waves][64 tokens][KB]
-    if (w > 0) {
+    // merge with lane ^ 1, then lane ^ 2 (every lane takes part in the exchanges)
+    {
+        unsigned long long other[KB];
 #pragma unroll
-        for (int i = 0; i < KB; ++i) cand[((w - 1) * kTileTokens + lane) * KB + i] = keys[i];
+        for (int i = 0; i < KB; ++i) other[i] = quad_xor_u64<1>(keys[i]);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) key_insert<KB>(keys, other[i]);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) other[i] = quad_xor_u64<2>(keys[i]);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) key_insert<KB>(keys, other[i]);
     }
-    __syncthreads();
-    if (w == 0 && lane < ntok) {
-        for (int ww = 0; ww < 3; ++ww)
-#pragma unroll
-            for (int i = 0; i < KB; ++i)
-                if (i < k) key_insert<KB>(keys, cand[(ww * kTileTokens + lane) * KB + i]);
-        const int b = t * kTileTokens + lane;
-        const float m = key_float((uint32_t)(keys[0] >> 32));
+    if (q == 0 && tok < ntok) {
+        const int b = t * kTileTokens + tok;
+        const float mx = key_float((uint32_t)(keys[0] >> 32));
         float ex[KB];
         float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < KB; ++i) {
             ex[i] = 0.0f;
             if (i < k) {
-                ex[i] = expf(key_float((uint32_t)(keys[i] >> 32)) - m);
+                ex[i] = expf(key_float((uint32_t)(keys[i] >> 32)) - mx);
                 sum += ex[i];
             }
         }
@@ -546,6 +578,8 @@ __device__ __attribute__((noinline)) void task_topk(const MK_C Params &P, int t)
         topk_tile<2>(P, t);
     else if (P.k <= 4)
         topk_tile<4>(P, t);
+    else if (P.k <= 6)
+        topk_tile<6>(P, t);
     else if (P.k <= 8)
         topk_tile<8>(P, t);
     else
@@ -1318,7 +1352,8 @@ __device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &P, int e
 // ------------------------------------------------------------------------------ COMBINE
 // out[b, :] = bf16( sum_{i<k} w[b,i] * y[inv[b*k+i], :] ), slot order, fp32, for
 // a combine task: kCombineTokens tokens x kCombineCols columns (4 columns per thread).
-__device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int c) {
+template <int KB>
+__device__ __forceinline__ void combine_tile(const MK_C Params &P, int c) {
     CombineSmem &cs = g_sm.u.c;
     const int nchunks = (P.d + kCombineCols - 1) / kCombineCols;
     const int grp = c / nchunks, chunk = c - grp * nchunks;
@@ -1332,24 +1367,27 @@ __device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int
     __syncthreads();
     const int q = (chunk * kCombineCols) / 4 + threadIdx.x;  // this thread's 4-column group
     if (4 * q < P.d) {
-        for (int bb = 0; bb < nb; ++bb) {
-            // all k rows of this token in flight before any is used
-            u32x2 yv[kMaxK];
+        // the rows of every token of the task in flight before any is used
+        u32x2 yv[kCombineTokens][KB];
 #pragma unroll
-            for (int i = 0; i < kMaxK; ++i)
-                if (i < k) yv[i] = *(const MK_G u32x2 *)(P.y + (size_t)cs.row[bb * k + i] * P.d + 4 * q);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int bb = 0; bb < kCombineTokens; ++bb)
+#pragma unroll
+            for (int i = 0; i < KB; ++i)
+                if (bb < nb && i < k) yv[bb][i] = *(const MK_G u32x2 *)(P.y + (size_t)cs.row[bb * k + i] * P.d + 4 * q);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int bb = 0; bb < kCombineTokens; ++bb) {
+            if (bb >= nb) break;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < kMaxK; ++i) {
+            for (int i = 0; i < KB; ++i) {
                 if (i < k) {
                     const float wgt = cs.w[bb * k + i];
-                    const float y0 = __uint_as_float(yv[i][0] << 16), y1 = __uint_as_float(yv[i][0] & 0xffff0000u);
-                    const float y2 = __uint_as_float(yv[i][1] << 16), y3 = __uint_as_float(yv[i][1] & 0xffff0000u);
-                    acc[0] = fmaf(wgt, y0, acc[0]);
-                    acc[1] = fmaf(wgt, y1, acc[1]);
-                    acc[2] = fmaf(wgt, y2, acc[2]);
-                    acc[3] = fmaf(wgt, y3, acc[3]);
+                    const u32x2 v = yv[bb][i];
+                    acc[0] = fmaf(wgt, __uint_as_float(v[0] << 16), acc[0]);
+                    acc[1] = fmaf(wgt, __uint_as_float(v[0] & 0xffff0000u), acc[1]);
+                    acc[2] = fmaf(wgt, __uint_as_float(v[1] << 16), acc[2]);
+                    acc[3] = fmaf(wgt, __uint_as_float(v[1] & 0xffff0000u), acc[3]);
                 }
             }
             const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
@@ -1358,6 +1396,17 @@ __device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int
         }
     }
     __syncthreads();
+}
+
+__device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int c) {
+    if (P.k <= 2)
+        combine_tile<2>(P, c);
+    else if (P.k <= 4)
+        combine_tile<4>(P, c);
+    else if (P.k <= 8)
+        combine_tile<8>(P, c);
+    else
+        combine_tile<16>(P, c);
 }
 
 // ------------------------------------------------------------------------------ task dispatch
@@ -1620,14 +1669,28 @@ __global__ void __launch_bounds__(kThreads, 2) moe_megakernel(Params Parg) {
     }
     Bases bs = initial_bases(P);
     if (P.sched == 0) {
-        // Routing tasks: workgroup w runs g = w, w + G, ... below the GroupGEMM blocks.
+        // Workgroup w runs g = w, w + G, ... (all tasks with narrow tiles; with wide tiles
+        // only the routing tasks below the GroupGEMM blocks).
+        const bool xcd_claims = P.BM == kWideBM;
         bool ok = true;
-        for (int g = blockIdx.x; g < bs.M1p && ok; g += gridDim.x) ok = run_task(P, g, bs, now_ticks());
-        // GroupGEMM and combine tasks: position p belongs to XCD p % 8 (blocks start at
-        // multiples of 8); the workgroups of an XCD (w % 8 == x, as the hardware deals
-        // them) take that XCD's positions in increasing order from its claim counter, so
-        // tiles adjacent in the list start together and share their operands in L2.
-        if (ok && wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) {
+        for (int g = blockIdx.x; ok; g += gridDim.x) {
+            if (xcd_claims && g >= bs.M1p) break;
+            if (g >= bs.M1 && !bs.known) {
+                if (!wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) {
+                    ok = false;
+                    break;
+                }
+                complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
+            }
+            if (bs.known && g >= bs.total) break;
+            ok = run_task(P, g, bs, now_ticks());
+        }
+        // Wide tiles: GroupGEMM and combine positions are claimed per XCD.  Position p
+        // belongs to XCD p % 8 (blocks start at multiples of 8); the workgroups of an XCD
+        // (w % 8 == x, as the hardware deals them) take that XCD's positions in increasing
+        // order from its claim counter, so tiles adjacent in the list start together and
+        // share their operands in L2.
+        if (xcd_claims && ok && wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) {
             complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
             const int x = blockIdx.x & 7;
             for (;;) {
