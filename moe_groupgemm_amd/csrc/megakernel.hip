@@ -4,10 +4,11 @@
 // MLSys 2026, section "Core method"): the layer is a graph of tasks whose dependencies
 // are event counters in device memory.  notify = atomic decrement; wait = spin until the
 // counter is zero.  Two schedulers run the same graph:
-//   static  -- workgroup w runs the tasks whose global index g satisfies g = w (mod G), in
-//              increasing g, spin-waiting on events (phases are numbered in topological
-//              order, so the smallest unfinished task can always run: no deadlock with a
-//              co-resident grid);
+//   static  -- the routing tasks go to workgroups round-robin (workgroup w runs g = w,
+//              w + G, ...); the GroupGEMM and combine tasks are partitioned over the 8 XCDs
+//              and each XCD's workgroups take its list in order; tasks spin-wait on their
+//              events (every list is in topological order, so the smallest unfinished task
+//              can always run: no deadlock with a co-resident grid);
 //   dynamic -- the router tasks are implicitly queued; every other task is pushed onto a
 //              shared queue by the task whose notification brings its event to zero
 //              ("data-dependent task triggering"), and idle workgroups pop from it.
@@ -181,6 +182,13 @@ __device__ __forceinline__ bool wg_wait_zero(const MK_C Params &P, const MK_G in
 // synchronises: after this, all of them are visible to every XCD.
 __device__ __forceinline__ void wg_stores_done() {
     wave_drain_vm();
+    __syncthreads();
+}
+
+// Make data other workgroups (or this one) published visible to this workgroup's loads:
+// thread 0 acquires at agent scope (invalidating the CU's vector L1), then the group syncs.
+__device__ __forceinline__ void wg_acquire() {
+    if (threadIdx.x == 0) fence_acquire();
     __syncthreads();
 }
 
@@ -1440,6 +1448,60 @@ __device__ __forceinline__ void trace_task(const MK_C Params &P, int g, int kind
     }
 }
 
+// Grouping of routing tile t and its notifications: perm/inv for the tile's assignments,
+// then each expert's event is decremented by the tile's rows of that expert; in dynamic
+// mode the gate/up tiles of every expert this brought to zero are pushed.
+__device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs, int t, bool dyn) {
+    task_group(P, t);
+    count_task(P, K_GROUP);
+    GroupSmem &gr = g_sm.u.gr;
+    if (threadIdx.x == 0) gr.nfired = 0;
+    wg_stores_done();
+    int skip = -1;
+    if ((P.debug & 1) && t == 0) {  // debug: drop the notification of the tile's first expert
+        for (int e = 0; e < P.E; ++e)
+            if (gr.mask[e]) {
+                skip = e;
+                break;
+            }
+    }
+    for (int e = threadIdx.x; e < P.E; e += kThreads) {
+        const int cnt = __popcll(gr.mask[e]);
+        if (cnt && e != skip) {
+            const int old = add_relaxed(P.ev_exp + e, -cnt);
+            if (dyn && old == cnt) gr.fired[atomicAdd(&gr.nfired, 1)] = e;
+        }
+    }
+    __syncthreads();
+    if (dyn) {
+        // push the gate/up tiles of every expert this tile completed; task ranges are
+        // ordered by expert, so fired experts whose ranges abut go out as one range
+        const int nf = gr.nfired;
+        if (threadIdx.x == 0) {  // sort the (few) fired experts
+            for (int i = 1; i < nf; ++i) {
+                const int v = gr.fired[i];
+                int j = i - 1;
+                while (j >= 0 && gr.fired[j] > v) {
+                    gr.fired[j + 1] = gr.fired[j];
+                    --j;
+                }
+                gr.fired[j + 1] = v;
+            }
+        }
+        __syncthreads();
+        if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));  // block bases for the pushes
+        int i = 0;
+        while (i < nf) {
+            int j = i;
+            while (j + 1 < nf && P.mt_base[gr.fired[j] + 1] == P.mt_base[gr.fired[j + 1]]) ++j;
+            const int m0 = P.mt_base[gr.fired[i]], m1 = P.mt_base[gr.fired[j] + 1];
+            const int Q = P.NB1 / P.S;
+            for (int sp = 0; sp < P.S; ++sp) wg_push_range(P, base_g1(bs, sp) + m0 * Q, (m1 - m0) * Q);
+            i = j + 1;
+        }
+    }
+}
+
 // Runs task g (obtained at time t0).  Returns false when the forward must be abandoned.
 __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs, unsigned long long t0) {
     const bool dyn = P.sched != 0;
@@ -1465,6 +1527,27 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         task_topk(P, t);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_TOPK);
+        if (P.T == 1) {
+            // The only routing tile: its histogram is the whole histogram, so the scan and
+            // the grouping run here, without the two joins between separate tasks.  Each
+            // step reads back what the previous one published from this workgroup.
+            wg_stores_done();
+            wg_acquire();
+            const int mt_total = task_scan(P);
+            count_task(P, K_SCAN);
+            complete_bases(P, bs, mt_total);
+            wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
+            wg_acquire();
+            if (dyn && threadIdx.x == 0) {
+                // tickets: routers, this task, and the GroupGEMM and combine tasks
+                const int real = bs.K + 1 + P.S * (bs.q1 + bs.q2) + P.nC;
+                const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
+                st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64), tag | (uint32_t)real);
+            }
+            group_and_notify(P, bs, 0, dyn);
+            trace_task(P, g, K_TOPK, t0, t1, t2);
+            return true;
+        }
         int delta = -1;
         if (dyn && t == 0) delta += P.T;
         if (wg_notify(P, P.ctl + CTL_EV_TOPK, delta) && dyn) wg_push_range(P, bs.S, 1);
@@ -1472,6 +1555,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         return true;
     }
     if (g == bs.S) {  // --------------------------------------------------------- SCAN
+        if (P.T == 1) return true;  // a single routing tile is scanned by its top-k task
         if (!dyn) {
             if (threadIdx.x == 0) add_relaxed(P.ctl + CTL_EV_TOPK, P.T);  // arm
             if (!wg_wait_zero(P, P.ctl + CTL_EV_TOPK)) return false;
@@ -1497,58 +1581,11 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
     if (g < bs.M1p) {  // -------------------------------------------------------- GROUP
         const int t = g - bs.G;
         if (t >= P.T) return true;  // padding before the GroupGEMM blocks
+        if (P.T == 1) return true;  // a single routing tile is grouped by its top-k task
         if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) return false;
         const unsigned long long t1 = now_ticks();
-        task_group(P, t);
-        const unsigned long long t2 = now_ticks();
-        count_task(P, K_GROUP);
-        GroupSmem &gr = g_sm.u.gr;
-        if (threadIdx.x == 0) gr.nfired = 0;
-        wg_stores_done();
-        int skip = -1;
-        if ((P.debug & 1) && t == 0) {  // debug: drop the notification of the tile's first expert
-            for (int e = 0; e < P.E; ++e)
-                if (gr.mask[e]) {
-                    skip = e;
-                    break;
-                }
-        }
-        for (int e = threadIdx.x; e < P.E; e += kThreads) {
-            const int cnt = __popcll(gr.mask[e]);
-            if (cnt && e != skip) {
-                const int old = add_relaxed(P.ev_exp + e, -cnt);
-                if (dyn && old == cnt) gr.fired[atomicAdd(&gr.nfired, 1)] = e;
-            }
-        }
-        __syncthreads();
-        if (dyn) {
-            // push the gate/up tiles of every expert this tile completed; task ranges are
-            // ordered by expert, so fired experts whose ranges abut go out as one range
-            const int nf = gr.nfired;
-            if (threadIdx.x == 0) {  // sort the (few) fired experts
-                for (int i = 1; i < nf; ++i) {
-                    const int v = gr.fired[i];
-                    int j = i - 1;
-                    while (j >= 0 && gr.fired[j] > v) {
-                        gr.fired[j + 1] = gr.fired[j];
-                        --j;
-                    }
-                    gr.fired[j + 1] = v;
-                }
-            }
-            __syncthreads();
-            if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));  // block bases for the pushes
-            int i = 0;
-            while (i < nf) {
-                int j = i;
-                while (j + 1 < nf && P.mt_base[gr.fired[j] + 1] == P.mt_base[gr.fired[j + 1]]) ++j;
-                const int m0 = P.mt_base[gr.fired[i]], m1 = P.mt_base[gr.fired[j] + 1];
-                const int Q = P.NB1 / P.S;
-                for (int sp = 0; sp < P.S; ++sp) wg_push_range(P, base_g1(bs, sp) + m0 * Q, (m1 - m0) * Q);
-                i = j + 1;
-            }
-        }
-        trace_task(P, g, K_GROUP, t0, t1, t2);
+        group_and_notify(P, bs, t, dyn);
+        trace_task(P, g, K_GROUP, t0, t1, now_ticks());
         return true;
     }
     if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
@@ -1669,28 +1706,16 @@ __global__ void __launch_bounds__(kThreads, 2) moe_megakernel(Params Parg) {
     }
     Bases bs = initial_bases(P);
     if (P.sched == 0) {
-        // Workgroup w runs g = w, w + G, ... (all tasks with narrow tiles; with wide tiles
-        // only the routing tasks below the GroupGEMM blocks).
-        const bool xcd_claims = P.BM == kWideBM;
+        // Routing tasks: workgroup w runs g = w, w + G, ... below the GroupGEMM blocks.
         bool ok = true;
-        for (int g = blockIdx.x; ok; g += gridDim.x) {
-            if (xcd_claims && g >= bs.M1p) break;
-            if (g >= bs.M1 && !bs.known) {
-                if (!wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) {
-                    ok = false;
-                    break;
-                }
-                complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
-            }
-            if (bs.known && g >= bs.total) break;
-            ok = run_task(P, g, bs, now_ticks());
-        }
-        // Wide tiles: GroupGEMM and combine positions are claimed per XCD.  Position p
-        // belongs to XCD p % 8 (blocks start at multiples of 8); the workgroups of an XCD
-        // (w % 8 == x, as the hardware deals them) take that XCD's positions in increasing
-        // order from its claim counter, so tiles adjacent in the list start together and
-        // share their operands in L2.
-        if (xcd_claims && ok && wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) {
+        for (int g = blockIdx.x; ok && g < bs.M1p; g += gridDim.x) ok = run_task(P, g, bs, now_ticks());
+        // GroupGEMM and combine positions are claimed per XCD.  Position p belongs to XCD
+        // p % 8 (the blocks start at multiples of 8); the workgroups of an XCD (w % 8 == x,
+        // as the hardware deals them) take that XCD's positions in increasing order from its
+        // claim counter, so tiles adjacent in the list start together and share operands in
+        // L2.  Each XCD's list is in topological order, so the smallest unfinished task of
+        // the forward always has its inputs done or in progress.
+        if (ok && wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) {
             complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
             const int x = blockIdx.x & 7;
             for (;;) {

@@ -182,7 +182,7 @@ def test_static_and_dynamic_are_bitwise_identical():
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
-@pytest.mark.parametrize("B,E", [(90, 8), (300, 4)], ids=["narrow", "wide"])
+@pytest.mark.parametrize("B,E", [(40, 8), (90, 8), (300, 4)], ids=["one_tile", "narrow", "wide"])
 def test_rest_state_and_task_counts(B, E, sched):
     d, f = 256, 384
     cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, 2, seed=12)
