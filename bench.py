@@ -119,22 +119,21 @@ def trace_report(layer, x, out, B):
     ctl = layer.routing(B)["ctl"].cpu().numpy()
     tr = mk.moe_mk_trace_view(layer.plan, B, layer.ws).cpu().numpy()
     E, k, d, f = layer.E, layer.k, layer.d, layer.f
+    info = lambda key: mk.moe_mk_plan_info(layer.plan, key)
+    waves = info("threads") // 64
     tpw = 1 if B <= 512 else 4
-    nR = -(-B // (4 * tpw)) * -(-E // 16)
+    nR = -(-B // (waves * tpw)) * -(-E // 16)
     T = -(-B // 64)
     mt = int(ctl[mk.CTL["mt_total"]])
     a = B * k
-    bn1w = mk.moe_mk_plan_info(layer.plan, "wide_BN1")
-    bn2w = mk.moe_mk_plan_info(layer.plan, "wide_BN2")
-    if a >= 128 * E and d % bn2w == 0 and f % bn1w == 0:  # wide tiles (128 rows)
-        S, nb1, nb2 = 1, f // bn1w, d // bn2w
+    if a >= info("wide_min_rows") * E and d % info("wide_BN2") == 0 and f % info("wide_BN1") == 0:
+        S, nb1, nb2 = 1, f // info("wide_BN1"), d // info("wide_BN2")
     else:
-        S = 4 if (a <= 1024 and f >= 8192 and (f // 64) % 4 == 0) else \
-            2 if (a <= 1024 and f >= 4096 and (f // 64) % 2 == 0) else 1
-        nb1, nb2 = f // 64, d // 64
+        nb1, nb2 = f // info("BN1"), d // info("BN2")
+        S = 4 if (a <= 1024 and f >= 8192 and nb1 % 4 == 0) else 2 if (a <= 1024 and f >= 4096 and nb1 % 2 == 0) else 1
     # GroupGEMM blocks are padded to multiples of 8 task positions (empty tasks leave no record)
     r8 = lambda v: (v + 7) // 8 * 8
-    total = r8(nR + 2 * T + 1) + S * (r8(mt * nb1 // S) + r8(mt * nb2)) + -(-B // 4) * -(-d // 1024)
+    total = r8(nR + 2 * T + 1) + S * (r8(mt * nb1 // S) + r8(mt * nb2)) + -(-B // 4) * -(-d // (4 * info("threads")))
     tr = tr[:total]
     tr = tr[tr[:, 1] != 0]
     kind = (tr[:, 0] >> 32) & 0xFF

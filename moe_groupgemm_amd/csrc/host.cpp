@@ -265,7 +265,7 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key) {
              {"wide_BN1", mk::kWideBN1},
              {"wide_BN2", mk::kWideBN},
              {"wide_BK", mk::kWideBK},
-             {"wide_min_rows", mk::kWideBM},
+             {"wide_min_rows", mk::kWideMinRows},
              {"route_experts", mk::kRouteExperts},
              {"threads", mk::kThreads}};
     for (auto &e : t)

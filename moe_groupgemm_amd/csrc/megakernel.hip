@@ -34,7 +34,7 @@
 namespace mk {
 
 // ------------------------------------------------------------------------------ LDS
-constexpr int kRingBytes = 72 * 1024;  // LDS ring of the GroupGEMM tiles
+constexpr int kRingBytes = 144 * 1024;  // LDS ring of the GroupGEMM and router tiles
 struct GemmSmem {
     uint16_t ring[kRingBytes / 2];
 };
@@ -311,27 +311,28 @@ __device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[T
     }
 }
 
-// Router tile through LDS (E a multiple of 4).  The workgroup's 4*TPW tokens (wave w owns
-// TPW of them) and 16 experts share every staged slice: per 64 values of j, the 64 x 16
-// block of Wr (4 KB, each wave moving 16 of its rows) and the tokens' 64 x values (each
-// wave moving its own), in a ring of kRouteStages stages filled by global_load_lds.  Lane l
-// accumulates chain l (j = l, l+64, ... in order) of every (token, expert) pair of its wave.
-//   Wr stage in LDS: [64 rows][4 chunks of 4 experts]; chunk c of row r at c ^ rswz(r), so
-//     the 16 rows a quarter-wave reads fall on distinct 16-byte bank groups.
-//   x stage: per wave, NX blocks of 256 bytes, each two token rows of 64 bf16.
+// Router tile through LDS (E a multiple of 4).  The workgroup's kWaves*TPW tokens (wave w
+// owns TPW of them) and 16 experts share every staged slice: per 128 values of j, the
+// 128 x 16 block of Wr (8 KB, each wave moving 16 of its rows) and the tokens' 128 x
+// values (each wave moving its own), in a ring of kRouteStages stages filled by
+// global_load_lds.  Lane l accumulates chain l (j = l, l+64, ... in order) of every
+// (token, expert) pair of its wave; a stage holds two consecutive steps of every chain.
+//   Wr stage in LDS: [128 rows][4 chunks of 4 experts]; chunk c of row r at c ^ rswz(r),
+//     so the 16 rows a quarter-wave reads fall on distinct 16-byte bank groups.
+//   x stage: per wave, TPW blocks of 256 bytes, each one token's 128 bf16 values.
 // Tokens past B and experts past E load clamped (valid) addresses; their sums are never
 // written.
-constexpr int kRouteStages = 12;
+constexpr int kRouteStages = 8;
 __device__ __forceinline__ int rswz(int r) { return (r >> 2) & 3; }
 
 template <int TPW>
 struct RouteCfg {
-    static constexpr int NX = TPW == 1 ? 1 : TPW / 2;  // 256-byte x loads per wave and stage
-    static constexpr int WR_BYTES = 64 * 16 * 4;
-    static constexpr int STAGE_BYTES = WR_BYTES + 4 * NX * 256;
-    static constexpr int LOADS = 1 + NX;
+    static constexpr int WR_BYTES = 128 * 16 * 4;
+    static constexpr int STAGE_BYTES = WR_BYTES + kWaves * TPW * 256;
+    static constexpr int LOADS = 1 + TPW;
     static_assert(kRouteStages * STAGE_BYTES <= kRingBytes, "router ring");
     static_assert((kRouteStages - 2) * LOADS < 64, "vmcnt range");
+    static_assert(WR_BYTES == kWaves * 1024, "one Wr block per wave");
 };
 
 template <int TPW>
@@ -364,34 +365,28 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &P, int b
     e0 = uni(e0);
     uint8_t *ring = (uint8_t *)g_sm.u.g.ring;
     const int lane = lane_id(), w = wave_id();
-    const int nst = uni(P.d / 64);
+    const int nst = uni(P.d / 128);
     const int E = P.E;
-    // this lane's DMA sources: Wr row 16w + lane/4 (chunk position lane%4) and, per x
-    // block i, token slot 2i + lane/32 of the wave at j pair 2*(lane%32)
+    // this lane's DMA sources: Wr row 16w + lane/4 (chunk position lane%4) and, per token
+    // t of the wave, the j pair 2*lane .. 2*lane+1 of the stage's 128 values
     const int wrow = 16 * w + (lane >> 2);
     const int wcol = min(e0 + 4 * ((lane & 3) ^ rswz(wrow)), E - 4);
     const MK_G float *wsrc = P.Wr + (size_t)wrow * E + wcol;
-    const MK_G uint16_t *xsrc[C::NX];
+    const MK_G uint16_t *xsrc[TPW];
 #pragma unroll
-    for (int i = 0; i < C::NX; ++i) {
-        const int slot = min(2 * i + (lane >> 5), TPW - 1);
-        const int tok = min(b0 + w * TPW + slot, P.B - 1);
-        xsrc[i] = P.x + (size_t)tok * P.d + 2 * (lane & 31);
+    for (int t = 0; t < TPW; ++t) {
+        const int tok = min(b0 + w * TPW + t, P.B - 1);
+        xsrc[t] = P.x + (size_t)tok * P.d + 2 * lane;
     }
-    const size_t wstep = (size_t)64 * E;
+    const size_t wstep = (size_t)128 * E;
     auto load = [&](int st, int s) {
         uint8_t *sp = ring + s * C::STAGE_BYTES;
         lds_dma16(wsrc + (size_t)st * wstep, (MK_L void *)(sp + w * 1024));
 #pragma unroll
-        for (int i = 0; i < C::NX; ++i)
-            __builtin_amdgcn_global_load_lds(xsrc[i] + (size_t)st * 64,
-                                             (MK_L void *)(sp + C::WR_BYTES + (w * C::NX + i) * 256), 4, 0, 0);
+        for (int t = 0; t < TPW; ++t)
+            __builtin_amdgcn_global_load_lds(xsrc[t] + (size_t)st * 128,
+                                             (MK_L void *)(sp + C::WR_BYTES + (w * TPW + t) * 256), 4, 0, 0);
     };
-    // this lane's LDS reads: Wr row lane (chunk q at position q ^ rswz(lane)) and x[t][lane]
-    const uint32_t wa0 = (uint32_t)(lane * 64 + 16 * rswz(lane));
-    uint32_t xa0[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) xa0[t] = (uint32_t)(C::WR_BYTES + (w * C::NX + t / 2) * 256 + (t & 1) * 128 + 2 * lane);
     float acc[TPW * 16];
 #pragma unroll
     for (int i = 0; i < TPW * 16; ++i) acc[i] = 0.0f;
@@ -409,19 +404,24 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &P, int b
         const int nxt = st + NS - 1;
         if (nxt < nst) load(nxt, slot == 0 ? NS - 1 : slot - 1);
         const uint32_t sb = rbase + (uint32_t)(slot * C::STAGE_BYTES);
-        uint32_t xa[TPW];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) xa[t] = sb + xa0[t];
-        f32x4 wv[4];
-        uint32_t xr[TPW];
-        route_reads<TPW>(sb + wa0, xa, wv, xr);
+        for (int sub = 0; sub < 2; ++sub) {
+            const int row = 64 * sub + lane;  // j = 128*st + row: chain `lane`, step 2*st + sub
+            uint32_t xa[TPW];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const float xf = __uint_as_float(xr[t] << 16);
+            for (int t = 0; t < TPW; ++t) xa[t] = sb + (uint32_t)(C::WR_BYTES + (w * TPW + t) * 256 + 2 * row);
+            f32x4 wv[4];
+            uint32_t xr[TPW];
+            route_reads<TPW>(sb + (uint32_t)(row * 64 + 16 * rswz(row)), xa, wv, xr);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int t = 0; t < TPW; ++t) {
+                const float xf = __uint_as_float(xr[t] << 16);
 #pragma unroll
-                for (int z = 0; z < 4; ++z) acc[t * 16 + 4 * q + z] = fmaf(xf, wv[q][z], acc[t * 16 + 4 * q + z]);
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int z = 0; z < 4; ++z)
+                        acc[t * 16 + 4 * q + z] = fmaf(xf, wv[q][z], acc[t * 16 + 4 * q + z]);
+            }
         }
         slot = slot == NS - 1 ? 0 : slot + 1;
     }
@@ -450,16 +450,16 @@ __device__ __attribute__((noinline)) void route_wave_scalar(const MK_C Params &P
     route_write<1>(P, acc, b0, e0);
 }
 
-// Router task (tg, eb): tokens [4*tpw*tg, +4*tpw), wave w taking tpw of them, experts
-// [16*eb, +16).
+// Router task (tg, eb): tokens [kWaves*tpw*tg, +kWaves*tpw), wave w taking tpw of them,
+// experts [16*eb, +16).
 __device__ __attribute__((noinline)) void task_route(const MK_C Params &P, int tg, int eb) {
     const int e0 = eb * kRouteExperts;
     if ((P.E & 3) != 0)
-        route_wave_scalar(P, tg * 4 + wave_id(), e0);
+        route_wave_scalar(P, tg * kWaves + wave_id(), e0);
     else if (P.tpw == 1)
-        route_tile<1>(P, tg * 4, e0);
+        route_tile<1>(P, tg * kWaves, e0);
     else
-        route_tile<4>(P, tg * 16, e0);
+        route_tile<4>(P, tg * kWaves * 4, e0);
 }
 
 // ------------------------------------------------------------------------------ TOPK
@@ -467,10 +467,10 @@ __device__ __attribute__((noinline)) void task_route(const MK_C Params &P, int t
 // then softmax over them in fp32.  Keys are (order-preserving logit bits, ~expert) so the
 // larger key is the larger logit and, among equal logits, the smaller expert; keys are
 // unique, so the selected set and its order do not depend on the order of insertion.
-// The tile's logits are staged in LDS.  Four lanes share a token (16 tokens per wave):
-// lane quarter q keeps a sorted list of the best keys among experts [q*per, (q+1)*per),
+// The tile's logits are staged in LDS.  Eight lanes share a token (8 tokens per wave):
+// lane part q keeps a sorted list of the best keys among experts [q*per, (q+1)*per),
 // visited from a per-token starting offset so the lanes of a wave read distinct LDS
-// banks; two butterfly rounds over lane pairs (xor 1, then xor 2) merge the four lists.
+// banks; three butterfly rounds over lane pairs (xor 1, 2, then 4) merge the eight lists.
 
 template <int KB>
 __device__ __forceinline__ void key_insert(unsigned long long (&keys)[KB], unsigned long long v) {
@@ -483,13 +483,19 @@ __device__ __forceinline__ void key_insert(unsigned long long (&keys)[KB], unsig
     }
 }
 
-// Exchange with lane ^ 1 or lane ^ 2 inside each group of four lanes (DPP quad permutes,
-// no LDS round trip).
+// Exchange with lane ^ M: M = 1, 2 by DPP quad permutes, M = 4 by a swizzle in bit mode
+// (and-mask 31, xor-mask 4); neither makes an LDS memory round trip.
 template <int M>
-__device__ __forceinline__ unsigned long long quad_xor_u64(unsigned long long v) {
-    constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] or [2,3,0,1]
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, ctrl, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, false);
+__device__ __forceinline__ unsigned long long lane_xor_u64(unsigned long long v) {
+    int lo, hi;
+    if constexpr (M == 4) {
+        lo = __builtin_amdgcn_ds_swizzle((int)(uint32_t)v, 0x101F);
+        hi = __builtin_amdgcn_ds_swizzle((int)(uint32_t)(v >> 32), 0x101F);
+    } else {
+        constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] or [2,3,0,1]
+        lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, ctrl, 0xF, 0xF, false);
+        hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, false);
+    }
     return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
@@ -513,8 +519,8 @@ __device__ __attribute__((noinline)) void topk_tile(const MK_C Params &P, int t)
     }
     for (int i = threadIdx.x; i < E; i += kThreads) ts.hist[i] = 0;
     __syncthreads();
-    const int tok = 16 * w + (lane >> 2), q = lane & 3;
-    const int per = (E + 3) / 4;
+    const int tok = 8 * w + (lane >> 3), q = lane & 7;
+    const int per = (E + 7) / 8;
     const int e_lo = q * per, n_e = max(0, min(per, E - e_lo));
     const int s0 = tok % per;
     unsigned long long keys[KB];
@@ -542,15 +548,19 @@ __device__ __attribute__((noinline)) void topk_tile(const MK_C Params &P, int t)
             key_insert<KB>(keys, ev[u] >= 0 ? key : 0ull);
         }
     }
-    // merge with lane ^ 1, then lane ^ 2 (every lane takes part in the exchanges)
+    // merge with lane ^ 1, lane ^ 2, then lane ^ 4 (every lane takes part in the exchanges)
     {
         unsigned long long other[KB];
 #pragma unroll
-        for (int i = 0; i < KB; ++i) other[i] = quad_xor_u64<1>(keys[i]);
+        for (int i = 0; i < KB; ++i) other[i] = lane_xor_u64<1>(keys[i]);
 #pragma unroll
         for (int i = 0; i < KB; ++i) key_insert<KB>(keys, other[i]);
 #pragma unroll
-        for (int i = 0; i < KB; ++i) other[i] = quad_xor_u64<2>(keys[i]);
+        for (int i = 0; i < KB; ++i) other[i] = lane_xor_u64<2>(keys[i]);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) key_insert<KB>(keys, other[i]);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) other[i] = lane_xor_u64<4>(keys[i]);
 #pragma unroll
         for (int i = 0; i < KB; ++i) key_insert<KB>(keys, other[i]);
     }
@@ -694,10 +704,10 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t
     const int lane = lane_id(), w = wave_id();
     const int ntok = min(kTileTokens, P.B - t * kTileTokens);
     const int b = t * kTileTokens + lane;
-    for (int i = w; i < k; i += 4)
+    for (int i = w; i < k; i += kWaves)
         if (lane < ntok) atomicOr(&g.mask[P.topk_idx[(size_t)b * k + i]], 1ull << lane);
     __syncthreads();
-    for (int i = w; i < k; i += 4) {
+    for (int i = w; i < k; i += kWaves) {
         if (lane < ntok) {
             const int a = b * k + i;
             const int e = P.topk_idx[a];
@@ -710,14 +720,14 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t
 }
 
 // ------------------------------------------------------------------------------ GroupGEMM tiles
-// C[rows, 64 cols] = A[rows, K] * B[K, 64 cols] on v_mfma_f32_16x16x32_bf16 with fp32
+// C[rows, kBN cols] = A[rows, K] * B[K, kBN cols] on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation.  A is K-contiguous (grouped token rows); B is a weight slice with N
 // contiguous ([K][ldb] row-major), exactly as stored.  Tiles of kBK = 64 along K go
 // straight from global memory into a ring of LDS stages (global_load_lds, no staging
 // registers), all but one of them in flight while one is consumed.
 //   A tile in LDS: [row][k], 128-byte rows; 16-byte chunk c of row r sits at c ^ swa(r).
 //     MFMA A fragment (lane i of group g: 8 consecutive k of row i) = one ds_read_b128.
-//   B tile in LDS: [k][n], 128-byte rows as in memory; chunk c of row k sits at c ^ swb(k).
+//   B tile in LDS: [k][n], 256-byte rows as in memory; chunk c of row k sits at c ^ wswb(k).
 //     MFMA B fragment (8 consecutive k of column j) = two ds_read_b64_tr_b16: within each
 //     16-lane group, lane l addresses row (k0 + l/4), columns (n0 + 4*(l%4) .. +3) and
 //     receives the 4 rows' values of column n0 + l.
@@ -728,58 +738,58 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int swa(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int swb(int k) { return (((k >> 1) ^ (k >> 3)) & 3) << 1; }
+__device__ __forceinline__ int wswb(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
 
 // Tile variants: DUAL (gate and up weights share the A tile) and AR, the A rows staged
 // (16 when the tile has at most 16 rows, as at decode batch sizes, else 64).  The ring of
-// stages fills the same 72 KB of LDS either way, so smaller A tiles buy deeper rings:
-// more weight bytes in flight per workgroup.
+// stages fills the same LDS either way, so smaller A tiles buy deeper rings: more weight
+// bytes in flight per workgroup.
 template <bool DUAL, int AR>
 struct GemmCfg {
     static constexpr int A_ELEMS = AR * kBK;
     static constexpr int B_ELEMS = kBK * kBN;
     static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS * (DUAL ? 2 : 1);
     static constexpr int NS = (kRingBytes / 2) / STAGE_ELEMS < 8 ? (kRingBytes / 2) / STAGE_ELEMS : 8;
-    static constexpr int A_LOADS = AR == 64 ? 2 : 1;             // per wave per stage
-    static constexpr int LOADS = A_LOADS + 2 * (DUAL ? 2 : 1);   // global_load_lds per wave per stage
+    static constexpr int B_BLOCKS = B_ELEMS / 512;                  // 1 KB blocks per weight and stage
+    static constexpr int LOADS = 1 + (B_BLOCKS / kWaves) * (DUAL ? 2 : 1);  // global_load_lds per wave per stage
+    static_assert(AR / 8 <= kWaves && B_BLOCKS % kWaves == 0, "one A block, whole B blocks per wave");
     static_assert(NS >= 3, "ring too shallow");
     static_assert((NS - 2) * LOADS < 64, "vmcnt range");
 };
 
 struct GemmArgs {
-    const MK_G uint16_t *arow[2];  // this lane's A rows (one per 1 KB block it loads)
+    const MK_G uint16_t *arow[1];  // this lane's A row (in the 1 KB block it loads)
     int nrows;
     const MK_G uint16_t *B0, *B1;
     int ldb, K;
 };
 
 
-// A row loaded by this lane into 1 KB block i of the A tile (8 rows of 128 bytes each).
+// The 1 KB block of the A tile (8 rows of 128 bytes) this wave loads: block w, or with
+// 16 rows block w % 2 (waves past the first two repeat their loads, writing identical
+// bytes, so every wave issues the same number of loads per stage).
 template <int AR>
-__device__ __forceinline__ int a_block(int i) {
-    return AR == 64 ? 2 * wave_id() + i : (wave_id() & 1);
+__device__ __forceinline__ int a_block() {
+    return wave_id() % (AR / 8);
 }
 
-// Issue the loads of one K stage.  A: AR/8 blocks of 1 KB (with 16 rows, waves 2 and 3
-// repeat the loads of waves 0 and 1, writing identical bytes); B: each wave moves two
-// 1 KB blocks (8 k-rows of 128 bytes) of every weight tile.
+// Issue the loads of one K stage.  A: one 1 KB block per wave; B: each wave moves
+// B_BLOCKS / kWaves 1 KB blocks (4 k-rows of 256 bytes) of every weight tile.
 template <bool DUAL, int AR>
 __device__ __forceinline__ void stage_load(const GemmArgs &g, int k0, uint16_t *stage) {
     using C = GemmCfg<DUAL, AR>;
     uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
     const int lane = lane_id(), w = wave_id();
-    const int r8 = lane >> 3, pc = lane & 7;
-#pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) {
-        const int blk = a_block<AR>(i);
-        const int row = 8 * blk + r8;
-        lds_dma16(g.arow[i] + k0 + 8 * (pc ^ swa(row)), (MK_L void *)(sA + blk * 512));
+    {
+        const int blk = a_block<AR>();
+        const int row = 8 * blk + (lane >> 3);
+        lds_dma16(g.arow[0] + k0 + 8 * ((lane & 7) ^ swa(row)), (MK_L void *)(sA + blk * 512));
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int blk = 2 * w + i;
-        const int kr = 8 * blk + r8;
-        const int lc = pc ^ swb(kr);
+    for (int i = 0; i < C::B_BLOCKS / kWaves; ++i) {
+        const int blk = (C::B_BLOCKS / kWaves) * w + i;
+        const int kr = 4 * blk + (lane >> 4);
+        const int lc = (lane & 15) ^ wswb(kr);
         lds_dma16(g.B0 + (size_t)(k0 + kr) * g.ldb + 8 * lc, (MK_L void *)(sB0 + blk * 512));
         if constexpr (DUAL) lds_dma16(g.B1 + (size_t)(k0 + kr) * g.ldb + 8 * lc, (MK_L void *)(sB1 + blk * 512));
     }
@@ -794,7 +804,7 @@ __device__ __forceinline__ uint32_t b_frag_addr(const uint16_t *sB, int kbase, i
     const int l = lane_id() & 15;
     const int k = kbase + (l >> 2);
     const int col = ncol0 + 4 * (l & 3);
-    return lds_addr(sB + k * kBN + ((((col >> 3) ^ swb(k)) << 3) | (col & 7)));
+    return lds_addr(sB + k * kBN + ((((col >> 3) ^ wswb(k)) << 3) | (col & 7)));
 }
 
 __device__ __forceinline__ u32x4 join(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
@@ -909,22 +919,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], 
     __syncthreads();  // the ring may be reused by the next task
 }
 
-// Row of 1 KB A block i loaded by this lane (8 rows of 128 bytes per block).  Rows past
-// the tile's end re-read its last row (every wave must issue the same number of loads
-// per stage for the vmcnt-based waits); their outputs are discarded.
+// Row of the A block this lane loads (8 rows of 128 bytes per block).  Rows past the
+// tile's end re-read its last row (every wave must issue the same number of loads per
+// stage for the vmcnt-based waits); their outputs are discarded.
 template <int AR>
-__device__ __forceinline__ int a_row(int i, int nrows) {
-    return min(8 * a_block<AR>(i) + (lane_id() >> 3), nrows - 1);
+__device__ __forceinline__ int a_row(int nrows) {
+    return min(8 * a_block<AR>() + (lane_id() >> 3), nrows - 1);
 }
 
 template <int AR>
 __device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0, int nrows, int n) {
     GemmArgs ga;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int tok = P.perm[row0 + a_row<AR>(i, nrows)] / P.k;
-        ga.arow[i] = P.x + (size_t)tok * P.d;
-    }
+    ga.arow[0] = P.x + (size_t)(P.perm[row0 + a_row<AR>(nrows)] / P.k) * P.d;
     ga.nrows = nrows;
     ga.B0 = P.W1 + (size_t)e * P.d * P.f + (size_t)n * kBN;
     ga.B1 = P.W3 + (size_t)e * P.d * P.f + (size_t)n * kBN;
@@ -959,8 +965,7 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
                                            int mt) {
     const int kl = P.f / P.S;  // reduction range of this split: [sp*kl, (sp+1)*kl)
     GemmArgs ga;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) ga.arow[i] = P.h + (size_t)(row0 + a_row<AR>(i, nrows)) * P.f + (size_t)sp * kl;
+    ga.arow[0] = P.h + (size_t)(row0 + a_row<AR>(nrows)) * P.f + (size_t)sp * kl;
     ga.nrows = nrows;
     ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)sp * kl * P.d + (size_t)n * kBN;
     ga.B1 = ga.B0;
@@ -1022,53 +1027,48 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
 }
 
 // ------------------------------------------------------------------------------ wide tiles
-// At large batches (an expert averages 128 rows or more) a tile has 128 rows, K steps are
-// 32 deep, and the four waves split the tile 2 x 2: wave w owns rows 64*(w/2) .. +64 and
-// the (w%2)-th half of the columns.  Gate/up tiles are kWideBN1 columns of each weight and
-// down-projection tiles kWideBN columns (with 128 and 256: a wave holds 64 x 64 of gate
-// and of up, or 64 x 128 of the down projection, 128 accumulator registers either way).
-// Per K step a wave reads its 4 A fragments and its B fragments in LDS batches of eight
-// halves and issues 32 MFMAs.
+// At large batches (an expert averages kWideMinRows rows or more) a tile has kWideBM = 256
+// rows, K steps are 32 deep, and the eight waves split the tile 2 x 4: wave w owns rows
+// 128*(w/4) .. +128 and the (w%4)-th quarter of the columns.  Gate/up tiles are kWideBN1 =
+// 128 columns of each weight (a wave: 128 x 32 of gate and of up) and down-projection tiles
+// kWideBN = 256 columns (a wave: 128 x 64); 128 accumulator registers either way.  Per K
+// step a wave reads 8 A fragments and 8 B fragment halves (two LDS batches) and issues 32
+// MFMAs; the workgroup stages 32 KB per 4.2 MFLOP.
 //   A tile in LDS: [row][k], 64-byte rows; 16-byte chunk c of row r sits at c ^ wswa(r),
 //     so the 16 rows one A fragment read touches fall on 16 distinct 16-byte bank groups.
-//   B tile in LDS: [k][n], rows as in memory (128 bytes: chunk c at c ^ swb(k); 256 or 512
-//     bytes: chunk c at c ^ wswb(k)), so the rows one ds_read_b64_tr_b16 touches spread over
-//     distinct bank groups.
+//   B tile in LDS: [k][n], 256- or 512-byte rows as in memory; chunk c of row k sits at
+//     c ^ wswb(k), so the rows one ds_read_b64_tr_b16 touches spread over distinct bank
+//     groups (the bank pattern repeats every 256 bytes).
 constexpr int kWBK = kWideBK;
 __device__ __forceinline__ int wswa(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int wswb(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
 
 template <bool DUAL, int BN>
 struct WideCfg {
-    static constexpr int CB = BN / 32;                // 16-column blocks per wave
-    static constexpr int NACC = 4 * CB;               // accumulators per weight
+    static constexpr int CB = BN / 64;                // 16-column blocks per wave and weight
+    static constexpr int NACC = 8 * CB;               // accumulators per weight (8 row blocks)
     static constexpr int A_ELEMS = kWideBM * kWBK;
     static constexpr int B_ELEMS = kWBK * BN;
     static constexpr int B_BLOCKS = B_ELEMS / 512;    // 1 KB blocks per weight and stage
     static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS * (DUAL ? 2 : 1);
     static constexpr int NS = (kRingBytes / 2) / STAGE_ELEMS;
-    static constexpr int LOADS = 2 + (B_BLOCKS / 4) * (DUAL ? 2 : 1);  // global_load_lds per wave per stage
+    static constexpr int LOADS = 2 + (B_BLOCKS / kWaves) * (DUAL ? 2 : 1);  // global_load_lds per wave per stage
     static_assert(NS >= 3, "ring too shallow");
-    static_assert(CB * (DUAL ? 2 : 1) == 4 || CB * (DUAL ? 2 : 1) == 8, "B fragments in batches of four blocks");
+    static_assert(CB * (DUAL ? 2 : 1) == 4, "one batch of eight B fragment halves per K step");
+    static_assert(A_ELEMS / 512 == 2 * kWaves && B_BLOCKS % kWaves == 0, "whole blocks per wave");
+    static_assert((NS - 2) * LOADS < 64, "vmcnt range");
 };
 
-template <int BN>
-__device__ __forceinline__ int wide_swb(int k) {
-    return BN == 64 ? swb(k) : wswb(k);  // 256- and 512-byte rows: bank pattern repeats every 256 bytes
-}
-
 // Operands of a wide tile: wave-uniform bases plus 32-bit per-lane element offsets that
-// stay fixed over the K loop (each K stage only moves the uniform bases), so the loads
-// take the scalar-base addressing form and keep few registers live.
+// stay fixed over the K loop (each K stage only moves the uniform bases).
 struct WideArgs {
     const MK_G uint16_t *A;   // activation base (x or h)
     uint32_t a_off[2];        // this lane's row start + 16-byte chunk, per A block it loads
     const MK_G uint16_t *B0, *B1;  // weight tile bases (k 0, column n0)
-    uint32_t b_off[4];        // this lane's k-row * ldb + 16-byte chunk, per B block it loads
+    uint32_t b_off[2];        // this lane's k-row * ldb + 16-byte chunk, per B block it loads
     int ldb, K, nrows;
 };
 
-// Issue the loads of one K stage.  A: eight 1 KB blocks of 16 rows x 64 bytes, two per
+// Issue the loads of one K stage.  A: sixteen 1 KB blocks of 16 rows x 64 bytes, two per
 // wave (lane -> row 16*blk + lane/4, position lane%4).  B: 1 KB blocks of 1024/(2*BN)
 // k-rows of 2*BN bytes (lane -> k-row lane/(BN/8), position lane%(BN/8)).
 template <bool DUAL, int BN>
@@ -1082,8 +1082,8 @@ __device__ __forceinline__ void wstage_load(const WideArgs &g, int k0, uint16_t 
     const size_t kk = (size_t)k0 * g.ldb;
     const MK_G uint16_t *b0 = g.B0 + kk, *b1 = g.B1 + kk;
 #pragma unroll
-    for (int i = 0; i < C::B_BLOCKS / 4; ++i) {
-        const int blk = (C::B_BLOCKS / 4) * w + i;
+    for (int i = 0; i < C::B_BLOCKS / kWaves; ++i) {
+        const int blk = (C::B_BLOCKS / kWaves) * w + i;
         lds_dma16(b0 + g.b_off[i], (MK_L void *)(sB0 + blk * 512));
         if constexpr (DUAL) lds_dma16(b1 + g.b_off[i], (MK_L void *)(sB1 + blk * 512));
     }
@@ -1103,10 +1103,10 @@ __device__ __forceinline__ void wide_offsets(WideArgs &g, RowOf arow) {
     constexpr int CPR = BN / 8;    // 16-byte chunks per k-row
     constexpr int RPB = 64 / CPR;  // k-rows per 1 KB block
 #pragma unroll
-    for (int i = 0; i < C::B_BLOCKS / 4; ++i) {
-        const int blk = (C::B_BLOCKS / 4) * w + i;
+    for (int i = 0; i < C::B_BLOCKS / kWaves; ++i) {
+        const int blk = (C::B_BLOCKS / kWaves) * w + i;
         const int kr = RPB * blk + lane / CPR;
-        g.b_off[i] = (uint32_t)kr * (uint32_t)g.ldb + 8u * (uint32_t)((lane % CPR) ^ wide_swb<BN>(kr));
+        g.b_off[i] = (uint32_t)kr * (uint32_t)g.ldb + 8u * (uint32_t)((lane % CPR) ^ wswb(kr));
     }
 }
 
@@ -1117,7 +1117,7 @@ __device__ __forceinline__ uint32_t wb_frag_addr(const uint16_t *sB, int kbase, 
     const int l = lane_id() & 15;
     const int k = kbase + (l >> 2);
     const int col = ncol0 + 4 * (l & 3);
-    return lds_addr(sB + k * BN + ((((col >> 3) ^ wide_swb<BN>(k)) << 3) | (col & 7)));
+    return lds_addr(sB + k * BN + ((((col >> 3) ^ wswb(k)) << 3) | (col & 7)));
 }
 
 // Four A fragments and eight B fragment halves in one asm block that also waits for them
@@ -1137,63 +1137,64 @@ __device__ __forceinline__ void wide_reads(const uint32_t (&ba)[8], const uint32
           "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
 }
 
-__device__ __forceinline__ void wide_reads_b(const uint32_t (&ba)[8], u32x2 (&b)[8]) {
+// Four A fragments in one asm block that also waits for them.
+__device__ __forceinline__ void wide_reads_a(const uint32_t (&aa)[4], u32x4 (&a)[4]) {
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
-        "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
-        "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\t"
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7])
-        : "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]), "v"(ba[4]), "v"(ba[5]), "v"(ba[6]), "v"(ba[7]));
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
 }
 
-// One K step of 32 for this wave's block; NRB = 16-row blocks of the wave that hold rows
-// (a compile-time count, so the loop body has no branches around its MFMAs).
-// B fragment halves are read in batches of eight (one batch per weight when a wave covers
-// 64 columns of it, one for both weights when it covers 32).
+// One K step of 32 for this wave's 128-row block; NRB = 16-row blocks of the wave that
+// hold rows, rounded up to even (a compile-time count, so the loop body has no branches
+// around its MFMAs).  U = 4 B blocks of 16 columns: CB of gate then CB of up, or CB = 4
+// of the down projection.
 template <bool DUAL, int BN, int NRB>
 __device__ __forceinline__ void wstage_compute(const uint16_t *stage, f32x4 (&acc0)[WideCfg<DUAL, BN>::NACC],
                                                f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC]) {
     using C = WideCfg<DUAL, BN>;
     constexpr int CB = C::CB;
-    constexpr int U = CB * (DUAL ? 2 : 1);  // 16-column B blocks of the wave (both weights)
     const uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, i = lane & 15;
-    const int r0 = 64 * (w >> 1), c0 = (BN / 2) * (w & 1);
+    const int r0 = 128 * (w >> 2), c0 = (BN / 4) * (w & 3);
     const int kb = 8 * g;
     uint32_t aa[4], ba[8];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-        const int r = r0 + 16 * rb + i;
-        aa[rb] = lds_addr(sA + r * kWBK + ((g ^ wswa(r)) << 3));
+    for (int jj = 0; jj < 4; ++jj) {
+        const int q = jj / CB, cb = jj % CB;
+        const uint16_t *sB = q ? sB1 : sB0;
+        ba[2 * jj] = wb_frag_addr<BN>(sB, kb, c0 + 16 * cb);
+        ba[2 * jj + 1] = wb_frag_addr<BN>(sB, kb + 4, c0 + 16 * cb);
     }
     u32x2 b[8];
     u32x4 a[4];
 #pragma unroll
-    for (int bt = 0; bt < U / 4; ++bt) {
+    for (int half = 0; half < 2; ++half) {
+        if (half * 4 >= NRB) break;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int u = 4 * bt + jj, q = u / CB, cb = u % CB;
-            const uint16_t *sB = q ? sB1 : sB0;
-            ba[2 * jj] = wb_frag_addr<BN>(sB, kb, c0 + 16 * cb);
-            ba[2 * jj + 1] = wb_frag_addr<BN>(sB, kb + 4, c0 + 16 * cb);
+        for (int rb = 0; rb < 4; ++rb) {
+            const int r = r0 + 16 * (4 * half + rb) + i;
+            aa[rb] = lds_addr(sA + r * kWBK + ((g ^ wswa(r)) << 3));
         }
-        if (bt == 0)
+        if (half == 0)
             wide_reads(ba, aa, b, a);
         else
-            wide_reads_b(ba, b);
+            wide_reads_a(aa, a);
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+        for (int rb = 0; rb < 4; ++rb) {
+            const int rr = 4 * half + rb;
+            if (rr < NRB)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int u = 4 * bt + jj, q = u / CB, cb = u % CB;
-                if (q == 0)
-                    acc0[CB * rb + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * jj], b[2 * jj + 1]), acc0[CB * rb + cb]);
-                else
-                    acc1[CB * rb + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * jj], b[2 * jj + 1]), acc1[CB * rb + cb]);
-            }
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int q = jj / CB, cb = jj % CB;
+                    if (q == 0)
+                        acc0[CB * rr + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * jj], b[2 * jj + 1]), acc0[CB * rr + cb]);
+                    else
+                        acc1[CB * rr + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * jj], b[2 * jj + 1]), acc1[CB * rr + cb]);
+                }
+        }
     }
 }
 
@@ -1236,14 +1237,14 @@ __device__ __forceinline__ void wide_tile(const WideArgs &ga, f32x4 (&acc0)[Wide
         acc0[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int wrows = min(max(uni(ga.nrows) - 64 * (wave_id() >> 1), 0), 64);
-    const int nrb = uni((wrows + 15) / 16);
+    const int wrows = min(max(uni(ga.nrows) - 128 * (wave_id() >> 2), 0), 128);
+    const int nrb2 = uni((wrows + 31) / 32);  // pairs of 16-row blocks
     const int nk = uni(ga.K / kWBK);
-    switch (nrb) {
-        case 4: wide_loop<DUAL, BN, 4>(ga, nk, acc0, acc1, s); break;
-        case 3: wide_loop<DUAL, BN, 3>(ga, nk, acc0, acc1, s); break;
-        case 2: wide_loop<DUAL, BN, 2>(ga, nk, acc0, acc1, s); break;
-        case 1: wide_loop<DUAL, BN, 1>(ga, nk, acc0, acc1, s); break;
+    switch (nrb2) {
+        case 4: wide_loop<DUAL, BN, 8>(ga, nk, acc0, acc1, s); break;
+        case 3: wide_loop<DUAL, BN, 6>(ga, nk, acc0, acc1, s); break;
+        case 2: wide_loop<DUAL, BN, 4>(ga, nk, acc0, acc1, s); break;
+        case 1: wide_loop<DUAL, BN, 2>(ga, nk, acc0, acc1, s); break;
         default: wide_loop<DUAL, BN, 0>(ga, nk, acc0, acc1, s); break;
     }
 }
@@ -1253,7 +1254,7 @@ __device__ __forceinline__ int wa_row(int i, int nrows) {
     return min(16 * (2 * wave_id() + i) + (lane_id() >> 2), nrows - 1);
 }
 
-// Wide gate/up tile: 128 rows x kWideBN1 columns of h.
+// Wide gate/up tile: kWideBM rows x kWideBN1 columns of h.
 __device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
     e = uni(e);
     row0 = uni(row0);
@@ -1275,9 +1276,9 @@ __device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &P, int e
     wide_tile<true, BN>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
-    const int r0 = 64 * (w >> 1), c0 = n * BN + (BN / 2) * (w & 1);
+    const int r0 = 128 * (w >> 2), c0 = n * BN + (BN / 4) * (w & 3);
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -1292,7 +1293,7 @@ __device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &P, int e
             }
 }
 
-// Wide down-projection tile: 128 rows x kWideBN columns of y.
+// Wide down-projection tile: kWideBM rows x kWideBN columns of y.
 __device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n) {
     e = uni(e);
     row0 = uni(row0);
@@ -1312,9 +1313,9 @@ __device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &P, int e
     wide_tile<false, BN>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
-    const int r0 = 64 * (w >> 1), c0 = n * BN + (BN / 2) * (w & 1);
+    const int r0 = 128 * (w >> 2), c0 = n * BN + (BN / 4) * (w & 3);
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -1419,7 +1420,7 @@ __device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int
 
 // ------------------------------------------------------------------------------ task dispatch
 // Router token groups of one 64-token tile (a group is 4 * tpw tokens).
-__device__ __forceinline__ int route_groups_per_tile(const MK_C Params &P) { return kTileTokens / (4 * P.tpw); }
+__device__ __forceinline__ int route_groups_per_tile(const MK_C Params &P) { return kTileTokens / (kWaves * P.tpw); }
 
 __device__ __forceinline__ int route_tasks_of_tile(const MK_C Params &P, int t) {
     const int g0 = t * route_groups_per_tile(P);
@@ -1690,7 +1691,7 @@ __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
     return g;
 }
 
-__global__ void __launch_bounds__(kThreads, 2) moe_megakernel(Params Parg) {
+__global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
     // Parg is the first kernel argument, at offset 0 of the kernel-argument segment: read it
     // there in place rather than from a private copy.
     (void)Parg;

@@ -18,14 +18,15 @@
 
 namespace mk {
 
-constexpr int kThreads = 256;        // 4 waves of 64 lanes per persistent workgroup
+constexpr int kWaves = 8;            // waves per persistent workgroup (one workgroup per CU)
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTileTokens = 64;      // tokens per top-k / grouping tile (one lane per token)
 constexpr int kRouteExperts = 16;    // experts per router task
 constexpr int kCombineTokens = 4;    // tokens per combine task
-constexpr int kCombineCols = 1024;   // model columns per combine task (4 per thread)
-constexpr int kBM = 64;              // GroupGEMM rows per tile (one expert's rows)
-constexpr int kBN = 64;              // GroupGEMM columns per tile
-constexpr int kBK = 64;              // GroupGEMM K step staged through LDS
+constexpr int kCombineCols = 4 * kThreads;  // model columns per combine task (4 per thread)
+constexpr int kBM = 64;              // GroupGEMM rows per narrow tile (one expert's rows)
+constexpr int kBN = 16 * kWaves;     // GroupGEMM columns per narrow tile (16 per wave)
+constexpr int kBK = 64;              // narrow GroupGEMM K step staged through LDS
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 16;
 
@@ -59,7 +60,7 @@ struct Shape {
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Router tokens per wave: one at small batches (more, shorter tasks), four at large ones
-// (each expert-weight row loaded serves four tokens).  A router task covers 4 waves.
+// (each expert-weight row loaded serves four tokens).  A router task covers kWaves waves.
 inline int route_tpw(int64_t B) { return B <= 512 ? 1 : 4; }
 
 // K splits S of the down projection: at small batches with a long f, each down-projection
@@ -76,23 +77,21 @@ inline int down_splits(const Shape &s, int64_t B) {
 constexpr int kMaxSplits = 4;
 
 // GroupGEMM tiles of one forward.  Narrow: kBM x kBN tiles (decode and mid-size batches).
-// Wide: when an expert averages at least kWideBM rows, tiles of kWideBM rows, kBN columns
-// of each gate/up weight and kWideBN columns of the down projection, so that each staged
-// weight byte serves twice the rows.  Workspace sizes are bounded with the narrow counts,
-// which are never smaller.
-constexpr int kWideBM = 128;
+// Wide: when an expert averages at least kWideMinRows rows, tiles of kWideBM rows,
+// kWideBN1 columns of each gate/up weight and kWideBN columns of the down projection, so
+// that each staged byte serves more multiply-adds.  Workspace sizes are bounded with the
+// narrow counts, which are never smaller.
+constexpr int kWideMinRows = 128;
+constexpr int kWideBM = 256;
 constexpr int kWideBN = 256;   // down-projection columns per wide tile
+constexpr int kWideBN1 = 128;  // gate/up columns of each weight per wide tile
 constexpr int kWideBK = 32;
-#ifndef MK_WIDE_BN1
-#define MK_WIDE_BN1 128
-#endif
-constexpr int kWideBN1 = MK_WIDE_BN1;  // gate/up columns of each weight per wide tile (64 or 128)
 struct Tiles {
     int BM, NB1, NB2, S;
 };
 inline Tiles tile_config(const Shape &s, int64_t B) {
     Tiles t;
-    const bool wide = B * s.k >= (int64_t)kWideBM * s.E && s.d % kWideBN == 0 && s.f % kWideBN1 == 0;
+    const bool wide = B * s.k >= (int64_t)kWideMinRows * s.E && s.d % kWideBN == 0 && s.f % kWideBN1 == 0;
     t.BM = wide ? kWideBM : kBM;
     t.NB1 = s.f / (wide ? kWideBN1 : kBN);
     t.NB2 = s.d / (wide ? kWideBN : kBN);
@@ -119,7 +118,7 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     Counts c;
     c.T = ceil_div(B, kTileTokens);
     c.tpw = route_tpw(B);
-    c.nTG = ceil_div(B, 4 * c.tpw);
+    c.nTG = ceil_div(B, kWaves * c.tpw);
     c.nEB = ceil_div(s.E, kRouteExperts);
     c.nR = c.nTG * c.nEB;
     c.nC = ceil_div(B, kCombineTokens) * ceil_div(s.d, kCombineCols);
@@ -129,7 +128,7 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     c.NB2 = s.d / kBN;
     c.S = down_splits(s, B);
     c.q_cap = 2 * c.T + 1 + c.mt_cap * c.NB1 + c.mt_cap * kMaxSplits * c.NB2 + c.nC + 128;  // + block padding
-    c.nR_max = ceil_div(B, 4) * c.nEB;
+    c.nR_max = ceil_div(B, kWaves) * c.nEB;
     return c;
 }
 

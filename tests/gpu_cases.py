@@ -51,9 +51,14 @@ def ctl_words(layer, B):
     return layer.routing(B)["ctl"].cpu().numpy()
 
 
+WAVES = 8           # waves per workgroup
+NARROW_BN = 128     # narrow GroupGEMM tile columns
+COMBINE_COLS = 2048
+
+
 def down_splits(B, k, f):
     """K splits of the down projection the library uses at this batch size (narrow tiles)."""
-    a, nb1 = B * k, f // 64
+    a, nb1 = B * k, f // NARROW_BN
     if a <= 1024 and f >= 8192 and nb1 % 4 == 0:
         return 4
     if a <= 1024 and f >= 4096 and nb1 % 2 == 0:
@@ -61,17 +66,18 @@ def down_splits(B, k, f):
     return 1
 
 
-def tile_config(B, k, E, d, f, wide_bn1=128):
+def tile_config(B, k, E, d, f, wide_bn1=128, wide_bn2=256, wide_bm=256):
     """(rows per tile, gate/up tiles per row tile, down tiles per row tile and split, splits):
-    wide 128-row tiles once an expert averages 128 rows (d a multiple of 256), else 64-row tiles."""
-    if B * k >= 128 * E and d % 256 == 0 and f % wide_bn1 == 0:
-        return 128, f // wide_bn1, d // 256, 1
-    return 64, f // 64, d // 64, down_splits(B, k, f)
+    wide tiles once an expert averages 128 rows (d, f multiples of the wide widths), else
+    64-row narrow tiles."""
+    if B * k >= 128 * E and d % wide_bn2 == 0 and f % wide_bn1 == 0:
+        return wide_bm, f // wide_bn1, d // wide_bn2, 1
+    return 64, f // NARROW_BN, d // NARROW_BN, down_splits(B, k, f)
 
 
-def expected_task_counts(hist, B, E, d, f, k, wide_bn1=128):
-    BM, NB1, NB2, S = tile_config(B, k, E, d, f, wide_bn1)
+def expected_task_counts(hist, B, E, d, f, k):
+    BM, NB1, NB2, S = tile_config(B, k, E, d, f)
     mt = int(sum((int(h) + BM - 1) // BM for h in hist))
-    tpw = 1 if B <= 512 else 4  # router tokens per wave; a router task has 4 waves
-    return {"route": -(-B // (4 * tpw)) * -(-E // 16), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
-            "gemm1": mt * NB1, "gemm2": mt * S * NB2, "combine": -(-B // 4) * -(-d // 1024)}
+    tpw = 1 if B <= 512 else 4  # router tokens per wave
+    return {"route": -(-B // (WAVES * tpw)) * -(-E // 16), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
+            "gemm1": mt * NB1, "gemm2": mt * S * NB2, "combine": -(-B // 4) * -(-d // COMBINE_COLS)}
