@@ -1149,10 +1149,13 @@ __device__ __forceinline__ void wide_reads_a(const uint32_t (&aa)[4], u32x4 (&a)
 // One K step of 32 for this wave's 128-row block; NRB = 16-row blocks of the wave that
 // hold rows, rounded up to even (a compile-time count, so the loop body has no branches
 // around its MFMAs).  U = 4 B blocks of 16 columns: CB of gate then CB of up, or CB = 4
-// of the down projection.
+// of the down projection.  The loads of a later stage (into a slot the barrier freed) are
+// issued between groups of MFMAs, so a load that waits for the memory pipeline to accept
+// it overlaps MFMAs already issued rather than the whole K step.
 template <bool DUAL, int BN, int NRB>
-__device__ __forceinline__ void wstage_compute(const uint16_t *stage, f32x4 (&acc0)[WideCfg<DUAL, BN>::NACC],
-                                               f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC]) {
+__device__ __forceinline__ void wstage_step(const uint16_t *stage, const WideArgs &ga, int k_next,
+                                            uint16_t *next_stage, f32x4 (&acc0)[WideCfg<DUAL, BN>::NACC],
+                                            f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC]) {
     using C = WideCfg<DUAL, BN>;
     constexpr int CB = C::CB;
     const uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
@@ -1160,6 +1163,26 @@ __device__ __forceinline__ void wstage_compute(const uint16_t *stage, f32x4 (&ac
     const int g = lane >> 4, i = lane & 15;
     const int r0 = 128 * (w >> 2), c0 = (BN / 4) * (w & 3);
     const int kb = 8 * g;
+    // the next stage's loads: A blocks, then B blocks (k_next < 0: none)
+    uint16_t *nA = next_stage, *nB0 = next_stage + C::A_ELEMS, *nB1 = nB0 + C::B_ELEMS;
+    const MK_G uint16_t *ab = ga.A + k_next;
+    const size_t kk = (size_t)k_next * ga.ldb;
+    auto load_a = [&]() {
+        if (k_next >= 0) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) lds_dma16(ab + ga.a_off[q], (MK_L void *)(nA + (2 * w + q) * 512));
+        }
+    };
+    auto load_b = [&]() {
+        if (k_next >= 0) {
+#pragma unroll
+            for (int q = 0; q < C::B_BLOCKS / kWaves; ++q) {
+                const int blk = (C::B_BLOCKS / kWaves) * w + q;
+                lds_dma16(ga.B0 + kk + ga.b_off[q], (MK_L void *)(nB0 + blk * 512));
+                if constexpr (DUAL) lds_dma16(ga.B1 + kk + ga.b_off[q], (MK_L void *)(nB1 + blk * 512));
+            }
+        }
+    };
     uint32_t aa[4], ba[8];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -1170,20 +1193,9 @@ __device__ __forceinline__ void wstage_compute(const uint16_t *stage, f32x4 (&ac
     }
     u32x2 b[8];
     u32x4 a[4];
+    auto mfma_rows = [&](int rb_lo, int rb_hi, int half) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        if (half * 4 >= NRB) break;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int r = r0 + 16 * (4 * half + rb) + i;
-            aa[rb] = lds_addr(sA + r * kWBK + ((g ^ wswa(r)) << 3));
-        }
-        if (half == 0)
-            wide_reads(ba, aa, b, a);
-        else
-            wide_reads_a(aa, a);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = rb_lo; rb < rb_hi; ++rb) {
             const int rr = 4 * half + rb;
             if (rr < NRB)
 #pragma unroll
@@ -1195,6 +1207,28 @@ __device__ __forceinline__ void wstage_compute(const uint16_t *stage, f32x4 (&ac
                         acc1[CB * rr + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * jj], b[2 * jj + 1]), acc1[CB * rr + cb]);
                 }
         }
+    };
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        if (half * 4 < NRB) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int r = r0 + 16 * (4 * half + rb) + i;
+                aa[rb] = lds_addr(sA + r * kWBK + ((g ^ wswa(r)) << 3));
+            }
+            if (half == 0)
+                wide_reads(ba, aa, b, a);
+            else
+                wide_reads_a(aa, a);
+        }
+        mfma_rows(0, 2, half);
+        __builtin_amdgcn_sched_barrier(0);
+        if (half == 0)
+            load_a();
+        else
+            load_b();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(2, 4, half);
     }
 }
 
@@ -1214,11 +1248,9 @@ __device__ __forceinline__ void wide_loop(const WideArgs &ga, int nk, f32x4 (&ac
             wait_vm<0>();
         bare_barrier();
         const int nxt = st + NS - 1;
-        if (nxt < nk) {
-            const int ns = slot == 0 ? NS - 1 : slot - 1;
-            wstage_load<DUAL, BN>(ga, nxt * kWBK, s.ring + ns * C::STAGE_ELEMS);
-        }
-        if constexpr (NRB > 0) wstage_compute<DUAL, BN, NRB>(s.ring + slot * C::STAGE_ELEMS, acc0, acc1);
+        const int ns = slot == 0 ? NS - 1 : slot - 1;  // the slot of stage st - 1, free now
+        wstage_step<DUAL, BN, NRB>(s.ring + slot * C::STAGE_ELEMS, ga, nxt < nk ? nxt * kWBK : -1,
+                                   s.ring + ns * C::STAGE_ELEMS, acc0, acc1);
         slot = slot == NS - 1 ? 0 : slot + 1;
     }
     wait_vm<0>();
