@@ -153,6 +153,14 @@ def trace_report(layer, x, out, B):
               f"end {us(tr[m, 3].max() - t0):7.1f} | wait {us(wait.mean()):6.2f} (max {us(wait.max()):6.1f}) | "
               f"body {us(body.mean()):7.2f} (max {us(body.max()):6.1f}) | notify {us(tail.mean()):5.2f}",
               file=sys.stderr)
+    fused = (kind == 1) & (tr[:, 6] != 0)
+    for r in tr[fused]:  # top-k task that also scans and groups (one routing tile)
+        print(f"#  top-k tail: scan {us(r[6] - r[4]):.2f} us, grouping and pushes {us(r[7] - r[6]):.2f}, "
+              f"notify {us(r[3] - r[7]):.2f}", file=sys.stderr)
+    first = np.array([tr[wg == w, 1].min() for w in sorted(set(wg.tolist()))]) - t0
+    print(f"#  first task of a workgroup obtained at: median {us(np.median(first)):.1f} us, "
+          f"90th percentile {us(np.percentile(first, 90)):.1f}, max {us(first.max()):.1f} "
+          f"(router tasks: {', '.join(f'{us(v - t0):.1f}' for v in sorted(tr[kind == 0, 1])[:8])})", file=sys.stderr)
     xcc = tr[:, 5]
     print(f"#  XCD of a task equals its workgroup index mod 8 for {100.0 * np.mean(xcc == wg % 8):.1f}% of tasks",
           file=sys.stderr)

@@ -174,7 +174,8 @@ moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks
  *   [1] time the workgroup obtained the task, [2] time its dependencies were satisfied,
  *   [3] time it finished, [4] time its compute ended (before its notifications),
  *   all in GPU real-time clock ticks (100 MHz); [5] the XCD (accelerator die, 0..7) that
- *   ran it; [6..7] unused.
+ *   ran it; [6], [7] ends of the scan and of the grouping when the top-k task of a
+ *   one-tile batch runs both itself (else 0).
  * Records of tasks that did not run in that forward are stale.  Errors: EINVAL, EWORKSPACE.
  */
 moe_mk_status_t moe_mk_trace_view(moe_mk_plan_t plan, int64_t B, const void *ws, size_t ws_bytes,

@@ -51,6 +51,9 @@ struct GroupSmem {
     unsigned long long mask[kMaxE];
     int fired[kMaxE];
     int nfired;
+    int fm0[kMaxE], fm1[kMaxE];           // row-tile range [mt_base[e], mt_base[e+1]) of each
+    int rg0[kMaxE * 4], rcnt[kMaxE * 4];  // task ranges to push (first task, count)
+    int nr, base, tot;
 };
 struct CombineSmem {
     int row[kCombineTokens * kMaxK];
@@ -314,7 +317,8 @@ __device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[T
 // Router tile through LDS (E a multiple of 4).  The workgroup's kWaves*TPW tokens (wave w
 // owns TPW of them) and 16 experts share every staged slice: per 128 values of j, the
 // 128 x 16 block of Wr (8 KB, each wave moving 16 of its rows) and the tokens' 128 x
-// values (each wave moving its own), in a ring of kRouteStages stages filled by
+// values (each wave moving its own), in a ring of as many stages as LDS holds (up to 16:
+// the loads are latency-bound, so the depth in flight sets the rate), filled by
 // global_load_lds.  Lane l accumulates chain l (j = l, l+64, ... in order) of every
 // (token, expert) pair of its wave; a stage holds two consecutive steps of every chain.
 //   Wr stage in LDS: [128 rows][4 chunks of 4 experts]; chunk c of row r at c ^ rswz(r),
@@ -322,7 +326,6 @@ __device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[T
 //   x stage: per wave, TPW blocks of 256 bytes, each one token's 128 bf16 values.
 // Tokens past B and experts past E load clamped (valid) addresses; their sums are never
 // written.
-constexpr int kRouteStages = 8;
 __device__ __forceinline__ int rswz(int r) { return (r >> 2) & 3; }
 
 template <int TPW>
@@ -330,8 +333,9 @@ struct RouteCfg {
     static constexpr int WR_BYTES = 128 * 16 * 4;
     static constexpr int STAGE_BYTES = WR_BYTES + kWaves * TPW * 256;
     static constexpr int LOADS = 1 + TPW;
-    static_assert(kRouteStages * STAGE_BYTES <= kRingBytes, "router ring");
-    static_assert((kRouteStages - 2) * LOADS < 64, "vmcnt range");
+    static constexpr int NS = kRingBytes / STAGE_BYTES < 16 ? kRingBytes / STAGE_BYTES : 16;
+    static_assert(NS >= 3 && NS * STAGE_BYTES <= kRingBytes, "router ring");
+    static_assert((NS - 2) * LOADS < 64, "vmcnt range");
     static_assert(WR_BYTES == kWaves * 1024, "one Wr block per wave");
 };
 
@@ -360,7 +364,7 @@ __device__ __forceinline__ void route_reads(uint32_t wa, const uint32_t (&xa)[TP
 template <int TPW>
 __device__ __attribute__((noinline)) void route_tile(const MK_C Params &P, int b0, int e0) {
     using C = RouteCfg<TPW>;
-    constexpr int NS = kRouteStages;
+    constexpr int NS = C::NS;
     b0 = uni(b0);
     e0 = uni(e0);
     uint8_t *ring = (uint8_t *)g_sm.u.g.ring;
@@ -627,11 +631,13 @@ __device__ __forceinline__ int block_excl_scan(int v, int *part, int *total) {
 }
 
 // hist[e] = sum_t tile_hist[t,e]; exp_indptr = exclusive prefix sum; tile_off[t,e] =
-// exp_indptr[e] + rows of e in tiles before t; row tiles of kBM rows per expert; arms
-// ev_exp[e] with hist[e], ev_h[mt,s] with the gate/up tiles of each (row tile, f range), and ev_y with
-// the number of down-projection tiles ("Core method": the prefix sum decides how many
-// GroupGEMM tiles each expert triggers).  Returns the number of row tiles.
-__device__ __attribute__((noinline)) int task_scan(const MK_C Params &P) {
+// exp_indptr[e] + rows of e in tiles before t; row tiles of P.BM rows per expert; arms
+// ev_h[mt,s] with the gate/up tiles of each (row tile, f range), ev_y with the number of
+// down-projection tiles and (unless the grouping runs in this same task) ev_exp[e] with
+// hist[e] ("Core method": the prefix sum decides how many GroupGEMM tiles each expert
+// triggers).  Events are at rest (zero) and nothing decrements them before the scan is
+// published, so arming is a plain store.  Returns the number of row tiles.
+__device__ __attribute__((noinline)) int task_scan(const MK_C Params &P, bool arm_experts) {
     const int e = threadIdx.x;
     const int E = P.E, BM = P.BM;
     int *tb = g_sm.u.s.tiles;
@@ -658,15 +664,15 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P) {
             pub(P.mt_expert + i, e);
             pub(P.mt_row0 + i, off + m * BM);
             pub(P.mt_rows + i, min(BM, h - m * BM));
-            for (int sp = 0; sp < P.S; ++sp) add_relaxed(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+            for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
         }
-        if (h) add_relaxed(P.ev_exp + e, h);
+        if (h && arm_experts) pub(P.ev_exp + e, h);
     }
     if (e == 0) {
         pub(P.indptr + E, total_h);
         pub(P.mt_base + E, total_mt);
         st_relaxed(P.ctl + CTL_MT_TOTAL, total_mt);
-        add_relaxed(P.ctl + CTL_EV_Y, total_mt * P.S * P.NB2);
+        pub(P.ctl + CTL_EV_Y, total_mt * P.S * P.NB2);
     }
     // per-tile row offsets: exp_indptr[e] + rows of e in earlier tiles
     int run = off;
@@ -1467,7 +1473,8 @@ __device__ __forceinline__ void count_task(const MK_C Params &P, int kind) {
 // Debug trace (MOE_MK_DEBUG_TRACE): per task {g | kind << 32 | workgroup << 40, obtained,
 // dependencies satisfied, finished, compute ended} in real-time ticks.
 __device__ __forceinline__ void trace_task(const MK_C Params &P, int g, int kind, unsigned long long t0,
-                                           unsigned long long t1, unsigned long long t2) {
+                                           unsigned long long t1, unsigned long long t2,
+                                           unsigned long long t3 = 0, unsigned long long t4 = 0) {
     if ((P.debug & 2) && threadIdx.x == 0) {
         MK_G long long *e = P.trace + (size_t)g * 8;
         e[0] = (long long)g | ((long long)kind << 32) | ((long long)blockIdx.x << 40);
@@ -1478,13 +1485,17 @@ __device__ __forceinline__ void trace_task(const MK_C Params &P, int g, int kind
         uint32_t xcc;
         asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
         e[5] = (long long)xcc;  // the XCD that ran the task
+        e[6] = (long long)t3;   // optional phase ends inside the task (0 when unused)
+        e[7] = (long long)t4;
     }
 }
 
 // Grouping of routing tile t and its notifications: perm/inv for the tile's assignments,
 // then each expert's event is decremented by the tile's rows of that expert; in dynamic
-// mode the gate/up tiles of every expert this brought to zero are pushed.
-__device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs, int t, bool dyn) {
+// mode the gate/up tiles of every expert this brought to zero are pushed, all ranges with
+// one reservation of queue slots.  With `whole` (the batch is this one tile, scanned by
+// the same task) every expert with rows is complete and no expert event is used.
+__device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs, int t, bool dyn, bool whole) {
     task_group(P, t);
     count_task(P, K_GROUP);
     GroupSmem &gr = g_sm.u.gr;
@@ -1500,37 +1511,71 @@ __device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs
     }
     for (int e = threadIdx.x; e < P.E; e += kThreads) {
         const int cnt = __popcll(gr.mask[e]);
-        if (cnt && e != skip) {
+        if (!cnt) continue;
+        bool fire = false;
+        if (whole) {
+            if (e == skip) {
+                if (!dyn) pub(P.ev_exp + e, 1);  // a wait that never ends (debug)
+            } else {
+                fire = dyn;
+            }
+        } else if (e != skip) {
             const int old = add_relaxed(P.ev_exp + e, -cnt);
-            if (dyn && old == cnt) gr.fired[atomicAdd(&gr.nfired, 1)] = e;
+            fire = dyn && old == cnt;
+        }
+        if (fire) {  // the expert's row tiles, loaded by each firing thread in parallel
+            const int i = atomicAdd(&gr.nfired, 1);
+            gr.fired[i] = e;
+            gr.fm0[i] = ld_relaxed(P.mt_base + e);
+            gr.fm1[i] = ld_relaxed(P.mt_base + e + 1);
         }
     }
     __syncthreads();
     if (dyn) {
         // push the gate/up tiles of every expert this tile completed; task ranges are
         // ordered by expert, so fired experts whose ranges abut go out as one range
-        const int nf = gr.nfired;
-        if (threadIdx.x == 0) {  // sort the (few) fired experts
-            for (int i = 1; i < nf; ++i) {
-                const int v = gr.fired[i];
+        if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));  // block bases for the pushes
+        if (threadIdx.x == 0) {
+            const int nf = gr.nfired;
+            for (int i = 1; i < nf; ++i) {  // sort the fired experts' ranges (they are disjoint)
+                const int v0 = gr.fm0[i], v1 = gr.fm1[i];
                 int j = i - 1;
-                while (j >= 0 && gr.fired[j] > v) {
-                    gr.fired[j + 1] = gr.fired[j];
+                while (j >= 0 && gr.fm0[j] > v0) {
+                    gr.fm0[j + 1] = gr.fm0[j];
+                    gr.fm1[j + 1] = gr.fm1[j];
                     --j;
                 }
-                gr.fired[j + 1] = v;
+                gr.fm0[j + 1] = v0;
+                gr.fm1[j + 1] = v1;
             }
+            const int Q = P.NB1 / P.S;
+            int nr = 0, tot = 0, i = 0;
+            while (i < nf) {
+                int j = i;
+                while (j + 1 < nf && gr.fm1[j] == gr.fm0[j + 1]) ++j;
+                const int m0 = gr.fm0[i], m1 = gr.fm1[j];
+                for (int sp = 0; sp < P.S; ++sp) {
+                    gr.rg0[nr] = base_g1(bs, sp) + m0 * Q;
+                    gr.rcnt[nr] = (m1 - m0) * Q;
+                    tot += gr.rcnt[nr++];
+                }
+                i = j + 1;
+            }
+            gr.nr = nr;
+            gr.tot = tot;
+            gr.base = tot ? add_relaxed(P.ctl + CTL_QTAIL, tot) : 0;
         }
         __syncthreads();
-        if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));  // block bases for the pushes
-        int i = 0;
-        while (i < nf) {
-            int j = i;
-            while (j + 1 < nf && P.mt_base[gr.fired[j] + 1] == P.mt_base[gr.fired[j + 1]]) ++j;
-            const int m0 = P.mt_base[gr.fired[i]], m1 = P.mt_base[gr.fired[j] + 1];
-            const int Q = P.NB1 / P.S;
-            for (int sp = 0; sp < P.S; ++sp) wg_push_range(P, base_g1(bs, sp) + m0 * Q, (m1 - m0) * Q);
-            i = j + 1;
+        if (gr.base + gr.tot > P.q_cap) {
+            if (threadIdx.x == 0) set_error(P.ctl, 4 /* MOE_MK_ERR_QUEUE */);
+        } else {
+            const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
+            int off = gr.base;
+            for (int r = 0; r < gr.nr; ++r) {
+                for (int i = threadIdx.x; i < gr.rcnt[r]; i += kThreads)
+                    st_relaxed64(P.qslots + off + i, tag | (uint32_t)(gr.rg0[r] + i));
+                off += gr.rcnt[r];
+            }
         }
     }
 }
@@ -1566,10 +1611,11 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
             // step reads back what the previous one published from this workgroup.
             wg_stores_done();
             wg_acquire();
-            const int mt_total = task_scan(P);
+            const int mt_total = task_scan(P, false);
             count_task(P, K_SCAN);
             complete_bases(P, bs, mt_total);
-            wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
+            const unsigned long long t3 = now_ticks();
+            wg_stores_done();
             wg_acquire();
             if (dyn && threadIdx.x == 0) {
                 // tickets: routers, this task, and the GroupGEMM and combine tasks
@@ -1577,8 +1623,11 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
                 const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
                 st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64), tag | (uint32_t)real);
             }
-            group_and_notify(P, bs, 0, dyn);
-            trace_task(P, g, K_TOPK, t0, t1, t2);
+            group_and_notify(P, bs, 0, dyn, true);
+            const unsigned long long t4 = now_ticks();
+            // static GroupGEMM tasks start once this is seen: the tables and perm/inv are out
+            wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
+            trace_task(P, g, K_TOPK, t0, t1, t2, t3, t4);
             return true;
         }
         int delta = -1;
@@ -1594,7 +1643,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
             if (!wg_wait_zero(P, P.ctl + CTL_EV_TOPK)) return false;
         }
         const unsigned long long t1 = now_ticks();
-        const int mt_total = task_scan(P);
+        const int mt_total = task_scan(P, true);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_SCAN);
         complete_bases(P, bs, mt_total);
@@ -1617,7 +1666,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         if (P.T == 1) return true;  // a single routing tile is grouped by its top-k task
         if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) return false;
         const unsigned long long t1 = now_ticks();
-        group_and_notify(P, bs, t, dyn);
+        group_and_notify(P, bs, t, dyn, false);
         trace_task(P, g, K_GROUP, t0, t1, now_ticks());
         return true;
     }
