@@ -49,11 +49,10 @@ struct ScanSmem {
 };
 struct GroupSmem {
     unsigned long long mask[kMaxE];
-    int fired[kMaxE];
-    int nfired;
-    int fm0[kMaxE], fm1[kMaxE];           // row-tile range [mt_base[e], mt_base[e+1]) of each
-    int rg0[kMaxE * 4], rcnt[kMaxE * 4];  // task ranges to push (first task, count)
-    int nr, base, tot;
+    int toff[kMaxE];  // the tile's row offsets tile_off[t, e]
+    int poff[kMaxE], pm0[kMaxE], pnm[kMaxE];  // per expert: queue offset, first row tile, row tiles
+    int part[kWaves];
+    int base;
 };
 struct CombineSmem {
     int row[kCombineTokens * kMaxK];
@@ -332,7 +331,7 @@ template <int TPW>
 struct RouteCfg {
     static constexpr int WR_BYTES = 128 * 16 * 4;
     static constexpr int STAGE_BYTES = WR_BYTES + kWaves * TPW * 256;
-    static constexpr int LOADS = 1 + TPW;
+    static constexpr int LOADS = 2;  // one Wr block and one x block per wave
     static constexpr int NS = kRingBytes / STAGE_BYTES < 16 ? kRingBytes / STAGE_BYTES : 16;
     static_assert(NS >= 3 && NS * STAGE_BYTES <= kRingBytes, "router ring");
     static_assert((NS - 2) * LOADS < 64, "vmcnt range");
@@ -376,20 +375,20 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &P, int b
     const int wrow = 16 * w + (lane >> 2);
     const int wcol = min(e0 + 4 * ((lane & 3) ^ rswz(wrow)), E - 4);
     const MK_G float *wsrc = P.Wr + (size_t)wrow * E + wcol;
-    const MK_G uint16_t *xsrc[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int tok = min(b0 + w * TPW + t, P.B - 1);
-        xsrc[t] = P.x + (size_t)tok * P.d + 2 * lane;
-    }
+    // x: with one token per wave each lane moves a j pair (4 bytes); with four, lane L
+    // moves values 8*(L%16) .. +7 of token L/16 (16 bytes), so the block is one load
+    const MK_G uint16_t *xsrc =
+        TPW == 1 ? P.x + (size_t)min(b0 + w, P.B - 1) * P.d + 2 * lane
+                 : P.x + (size_t)min(b0 + w * TPW + (lane >> 4), P.B - 1) * P.d + 8 * (lane & 15);
     const size_t wstep = (size_t)128 * E;
     auto load = [&](int st, int s) {
         uint8_t *sp = ring + s * C::STAGE_BYTES;
         lds_dma16(wsrc + (size_t)st * wstep, (MK_L void *)(sp + w * 1024));
-#pragma unroll
-        for (int t = 0; t < TPW; ++t)
-            __builtin_amdgcn_global_load_lds(xsrc[t] + (size_t)st * 128,
-                                             (MK_L void *)(sp + C::WR_BYTES + (w * TPW + t) * 256), 4, 0, 0);
+        MK_L void *xd = (MK_L void *)(sp + C::WR_BYTES + w * TPW * 256);
+        if constexpr (TPW == 1)
+            __builtin_amdgcn_global_load_lds(xsrc + (size_t)st * 128, xd, 4, 0, 0);
+        else
+            lds_dma16(xsrc + (size_t)st * 128, xd);
     };
     float acc[TPW * 16];
 #pragma unroll
@@ -458,9 +457,10 @@ __device__ __attribute__((noinline)) void route_wave_scalar(const MK_C Params &P
 // experts [16*eb, +16).
 __device__ __attribute__((noinline)) void task_route(const MK_C Params &P, int tg, int eb) {
     const int e0 = eb * kRouteExperts;
-    if ((P.E & 3) != 0)
-        route_wave_scalar(P, tg * kWaves + wave_id(), e0);
-    else if (P.tpw == 1)
+    if ((P.E & 3) != 0) {
+        const int tpw = uni(P.tpw);
+        for (int t = 0; t < tpw; ++t) route_wave_scalar(P, (tg * kWaves + wave_id()) * tpw + t, e0);
+    } else if (P.tpw == 1)
         route_tile<1>(P, tg * kWaves, e0);
     else
         route_tile<4>(P, tg * kWaves * 4, e0);
@@ -514,7 +514,7 @@ __device__ __attribute__((noinline)) void topk_tile(const MK_C Params &P, int t)
     const MK_G float *src = P.logits + (size_t)t * kTileTokens * E;
     if ((E & 3) == 0) {
         const int nblk = (ntok * E * 4 + 1023) / 1024;
-        for (int bk = wave_id(); bk < nblk; bk += 4)
+        for (int bk = wave_id(); bk < nblk; bk += kWaves)
             __builtin_amdgcn_global_load_lds((const MK_G void *)(src + bk * 256 + lane_id() * 4),
                                              (MK_L void *)(ts.lg + bk * 256), 16, 0, 0);
         wave_drain_vm();
@@ -642,12 +642,25 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P, bool ar
     const int E = P.E, BM = P.BM;
     int *tb = g_sm.u.s.tiles;
     const int rows = kScanStage / E;  // tile_hist rows staged per round (coalesced loads)
+    // stage rows [t0, t0 + nr) of tile_hist, eight loads of each thread in flight at once
+    auto stage = [&](int t0, int nr) {
+        const MK_G int *src = P.tile_hist + (size_t)t0 * E;
+        const int n = nr * E;
+        __syncthreads();
+        for (int i0 = threadIdx.x; i0 < n; i0 += 8 * kThreads) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = i0 + u * kThreads < n ? src[i0 + u * kThreads] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u * kThreads < n) tb[i0 + u * kThreads] = v[u];
+        }
+        __syncthreads();
+    };
     int h = 0;
     for (int t0 = 0; t0 < P.T; t0 += rows) {
         const int nr = min(rows, P.T - t0);
-        __syncthreads();
-        for (int i = threadIdx.x; i < nr * E; i += kThreads) tb[i] = P.tile_hist[(size_t)t0 * E + i];
-        __syncthreads();
+        stage(t0, nr);
         if (e < E)
             for (int t = 0; t < nr; ++t) h += tb[t * E + e];
     }
@@ -678,15 +691,7 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P, bool ar
     int run = off;
     for (int t0 = 0; t0 < P.T; t0 += rows) {
         const int nr = min(rows, P.T - t0);
-        if (t0 > 0) {  // the first round's rows are still staged unless T needed several
-            __syncthreads();
-            for (int i = threadIdx.x; i < nr * E; i += kThreads) tb[i] = P.tile_hist[(size_t)t0 * E + i];
-            __syncthreads();
-        } else if (P.T > rows) {
-            __syncthreads();
-            for (int i = threadIdx.x; i < nr * E; i += kThreads) tb[i] = P.tile_hist[i];
-            __syncthreads();
-        }
+        if (t0 > 0 || P.T > rows) stage(t0, nr);  // the first round's rows are still staged unless T needed several
         if (e < E)
             for (int t = 0; t < nr; ++t) {
                 pub(P.tile_off + (size_t)(t0 + t) * E + e, run);
@@ -705,20 +710,33 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P, bool ar
 __device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t) {
     GroupSmem &g = g_sm.u.gr;
     const int E = P.E, k = P.k;
-    for (int i = threadIdx.x; i < E; i += kThreads) g.mask[i] = 0ull;
-    __syncthreads();
     const int lane = lane_id(), w = wave_id();
     const int ntok = min(kTileTokens, P.B - t * kTileTokens);
     const int b = t * kTileTokens + lane;
-    for (int i = w; i < k; i += kWaves)
-        if (lane < ntok) atomicOr(&g.mask[P.topk_idx[(size_t)b * k + i]], 1ull << lane);
+    // every load of the task at once: the lane's assignments (slots w and w + kWaves;
+    // k <= 2 * kWaves) and the tile's row offsets
+    static_assert(kMaxK <= 2 * kWaves, "two slots per lane");
+    int ev[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int i = w + j * kWaves;
+        ev[j] = i < k && lane < ntok ? P.topk_idx[(size_t)b * k + i] : -1;
+    }
+    for (int i = threadIdx.x; i < E; i += kThreads) {
+        g.toff[i] = P.tile_off[(size_t)t * E + i];
+        g.mask[i] = 0ull;
+    }
     __syncthreads();
-    for (int i = w; i < k; i += kWaves) {
-        if (lane < ntok) {
-            const int a = b * k + i;
-            const int e = P.topk_idx[a];
-            const int rank = __popcll(g.mask[e] & ((1ull << lane) - 1ull));
-            const int p = P.tile_off[(size_t)t * E + e] + rank;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        if (ev[j] >= 0) atomicOr(&g.mask[ev[j]], 1ull << lane);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (ev[j] >= 0) {
+            const int a = b * k + w + j * kWaves;
+            const int rank = __popcll(g.mask[ev[j]] & ((1ull << lane) - 1ull));
+            const int p = g.toff[ev[j]] + rank;
             pub(P.perm + p, a);
             pub(P.inv + a, p);
         }
@@ -1038,29 +1056,36 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
 // 128*(w/4) .. +128 and the (w%4)-th quarter of the columns.  Gate/up tiles are kWideBN1 =
 // 128 columns of each weight (a wave: 128 x 32 of gate and of up) and down-projection tiles
 // kWideBN = 256 columns (a wave: 128 x 64); 128 accumulator registers either way.  Per K
-// step a wave reads 8 A fragments and 8 B fragment halves (two LDS batches) and issues 32
-// MFMAs; the workgroup stages 32 KB per 4.2 MFLOP.
+// step a wave reads 8 A fragments and 8 B fragment halves and issues 32 MFMAs in two groups
+// of 16 (rows 0-63, rows 64-127 of its block); the workgroup stages 32 KB per 4.2 MFLOP.
 //   A tile in LDS: [row][k], 64-byte rows; 16-byte chunk c of row r sits at c ^ wswa(r),
 //     so the 16 rows one A fragment read touches fall on 16 distinct 16-byte bank groups.
 //   B tile in LDS: [k][n], 256- or 512-byte rows as in memory; chunk c of row k sits at
 //     c ^ wswb(k), so the rows one ds_read_b64_tr_b16 touches spread over distinct bank
 //     groups (the bank pattern repeats every 256 bytes).
+// The fragments are register-pipelined: a group's MFMAs run while the fragments of the
+// next group (or of the next stage) are read, so a wave never waits on LDS before its MFMAs.
 constexpr int kWBK = kWideBK;
+constexpr int kWR = kWideBM / 2;  // rows per wave row
+constexpr int kWRB = kWR / 16;    // 16-row blocks per wave row (two groups of four)
 __device__ __forceinline__ int wswa(int r) { return (r >> 2) & 3; }
 
 template <bool DUAL, int BN>
 struct WideCfg {
     static constexpr int CB = BN / 64;                // 16-column blocks per wave and weight
-    static constexpr int NACC = 8 * CB;               // accumulators per weight (8 row blocks)
+    static constexpr int NACC = kWRB * CB;            // accumulators per weight
     static constexpr int A_ELEMS = kWideBM * kWBK;
     static constexpr int B_ELEMS = kWBK * BN;
     static constexpr int B_BLOCKS = B_ELEMS / 512;    // 1 KB blocks per weight and stage
     static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS * (DUAL ? 2 : 1);
+    static constexpr int STAGE_BYTES = 2 * STAGE_ELEMS;
     static constexpr int NS = (kRingBytes / 2) / STAGE_ELEMS;
-    static constexpr int LOADS = 2 + (B_BLOCKS / kWaves) * (DUAL ? 2 : 1);  // global_load_lds per wave per stage
-    static_assert(NS >= 3, "ring too shallow");
-    static_assert(CB * (DUAL ? 2 : 1) == 4, "one batch of eight B fragment halves per K step");
-    static_assert(A_ELEMS / 512 == 2 * kWaves && B_BLOCKS % kWaves == 0, "whole blocks per wave");
+    static constexpr int A_LOADS = 2;                 // global_load_lds per wave and stage: A, then B
+    static constexpr int LOADS = A_LOADS + (B_BLOCKS / kWaves) * (DUAL ? 2 : 1);
+    static_assert(NS >= 4, "ring too shallow");
+    static_assert(kWRB == 8, "two groups of four row blocks per wave");
+    static_assert(CB * (DUAL ? 2 : 1) == 4, "eight B fragment halves per K step");
+    static_assert(A_ELEMS / 512 == A_LOADS * kWaves && B_BLOCKS % kWaves == 0, "whole blocks per wave");
     static_assert((NS - 2) * LOADS < 64, "vmcnt range");
 };
 
@@ -1074,24 +1099,27 @@ struct WideArgs {
     int ldb, K, nrows;
 };
 
-// Issue the loads of one K stage.  A: sixteen 1 KB blocks of 16 rows x 64 bytes, two per
-// wave (lane -> row 16*blk + lane/4, position lane%4).  B: 1 KB blocks of 1024/(2*BN)
-// k-rows of 2*BN bytes (lane -> k-row lane/(BN/8), position lane%(BN/8)).
-template <bool DUAL, int BN>
+// Issue all four loads of one K stage (PART 0) or only load PART (1 .. 4: the two A blocks
+// of the wave, then its two B blocks).  A: sixteen 1 KB blocks of 16 rows x 64 bytes, two
+// per wave (lane -> row 16*blk + lane/4, position lane%4).  B: 1 KB blocks of 1024/(2*BN)
+// k-rows of 2*BN bytes (lane -> k-row lane/(BN/8), position lane%(BN/8)); a wave moves one
+// block of each weight (gate/up) or two blocks of the down projection.
+template <bool DUAL, int BN, int PART>
 __device__ __forceinline__ void wstage_load(const WideArgs &g, int k0, uint16_t *stage) {
     using C = WideCfg<DUAL, BN>;
+    static_assert(C::LOADS == 4 && C::B_BLOCKS / kWaves == (DUAL ? 1 : 2), "four loads per wave and stage");
     uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
     const int w = wave_id();
     const MK_G uint16_t *ab = g.A + k0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma16(ab + g.a_off[i], (MK_L void *)(sA + (2 * w + i) * 512));
     const size_t kk = (size_t)k0 * g.ldb;
-    const MK_G uint16_t *b0 = g.B0 + kk, *b1 = g.B1 + kk;
-#pragma unroll
-    for (int i = 0; i < C::B_BLOCKS / kWaves; ++i) {
-        const int blk = (C::B_BLOCKS / kWaves) * w + i;
-        lds_dma16(b0 + g.b_off[i], (MK_L void *)(sB0 + blk * 512));
-        if constexpr (DUAL) lds_dma16(b1 + g.b_off[i], (MK_L void *)(sB1 + blk * 512));
+    if constexpr (PART == 0 || PART == 1) lds_dma16(ab + g.a_off[0], (MK_L void *)(sA + (2 * w) * 512));
+    if constexpr (PART == 0 || PART == 2) lds_dma16(ab + g.a_off[1], (MK_L void *)(sA + (2 * w + 1) * 512));
+    if constexpr (DUAL) {
+        if constexpr (PART == 0 || PART == 3) lds_dma16(g.B0 + kk + g.b_off[0], (MK_L void *)(sB0 + w * 512));
+        if constexpr (PART == 0 || PART == 4) lds_dma16(g.B1 + kk + g.b_off[0], (MK_L void *)(sB1 + w * 512));
+    } else {
+        if constexpr (PART == 0 || PART == 3) lds_dma16(g.B0 + kk + g.b_off[0], (MK_L void *)(sB0 + (2 * w) * 512));
+        if constexpr (PART == 0 || PART == 4) lds_dma16(g.B0 + kk + g.b_off[1], (MK_L void *)(sB0 + (2 * w + 1) * 512));
     }
 }
 
@@ -1102,7 +1130,7 @@ __device__ __forceinline__ void wide_offsets(WideArgs &g, RowOf arow) {
     using C = WideCfg<DUAL, BN>;
     const int lane = lane_id(), w = wave_id();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < C::A_LOADS; ++i) {
         const int row = 16 * (2 * w + i) + (lane >> 2);
         g.a_off[i] = arow(i) + 8u * (uint32_t)((lane & 3) ^ wswa(row));
     }
@@ -1116,149 +1144,209 @@ __device__ __forceinline__ void wide_offsets(WideArgs &g, RowOf arow) {
     }
 }
 
-// LDS byte address of this lane's half of a B fragment (rows kbase + l/4, columns
-// ncol0 + 4*(l%4)) in a B tile of BN columns.
-template <int BN>
-__device__ __forceinline__ uint32_t wb_frag_addr(const uint16_t *sB, int kbase, int ncol0) {
-    const int l = lane_id() & 15;
-    const int k = kbase + (l >> 2);
-    const int col = ncol0 + 4 * (l & 3);
-    return lds_addr(sB + k * BN + ((((col >> 3) ^ wswb(k)) << 3) | (col & 7)));
-}
+// Byte offsets (within a stage) of this lane's fragment reads: `a` for the wave's first A
+// fragment (row block rb adds 1024 * rb: rows 16 apart keep the lane's swizzle), b[cb] for
+// the B fragment half of column block cb of the wave's quarter (rows kb + l/4, columns
+// 16*cb + 4*(l%4)) in the first weight.  The other halves are fixed distances away: rows
+// kb + 4 + l/4 (same swizzle) at +8*BN bytes, the up weight at +2*B_ELEMS bytes.
+template <bool DUAL, int BN>
+struct WideFragOff {
+    static constexpr int CB = WideCfg<DUAL, BN>::CB;
+    uint32_t a, b[CB];
+    __device__ __forceinline__ WideFragOff() {
+        using C = WideCfg<DUAL, BN>;
+        const int lane = lane_id(), w = wave_id();
+        const int g = lane >> 4, l = lane & 15;
+        const int r = kWR * (w >> 2) + l;
+        a = 2u * (uint32_t)(r * kWBK + ((g ^ wswa(r)) << 3));
+        const int c0 = (BN / 4) * (w & 3);
+        const int k = 8 * g + (l >> 2);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int col = c0 + 16 * cb + 4 * (l & 3);
+            b[cb] = 2u * (uint32_t)(C::A_ELEMS + k * BN + ((((col >> 3) ^ wswb(k)) << 3) | (col & 7)));
+        }
+    }
+};
 
-// Four A fragments and eight B fragment halves in one asm block that also waits for them
-// (see frag_reads).
-__device__ __forceinline__ void wide_reads(const uint32_t (&ba)[8], const uint32_t (&aa)[4], u32x2 (&b)[8],
-                                           u32x4 (&a)[4]) {
+// Fragment reads that do not wait: the wait is wfrag_wait, which names the same registers
+// as inputs and outputs, so no use of them can be placed before it.  OFF: byte offset of
+// the first of four A fragments (row blocks 16 rows = 1024 bytes apart).
+template <int OFF>
+__device__ __forceinline__ void wfrag_read_a(uint32_t addr, u32x4 (&a)[4]) {
     asm volatile(
-        "ds_read_b128 %8, %20\n\tds_read_b128 %9, %21\n\tds_read_b128 %10, %22\n\tds_read_b128 %11, %23\n\t"
-        "ds_read_b64_tr_b16 %0, %12\n\tds_read_b64_tr_b16 %1, %13\n\t"
-        "ds_read_b64_tr_b16 %2, %14\n\tds_read_b64_tr_b16 %3, %15\n\t"
-        "ds_read_b64_tr_b16 %4, %16\n\tds_read_b64_tr_b16 %5, %17\n\t"
-        "ds_read_b64_tr_b16 %6, %18\n\tds_read_b64_tr_b16 %7, %19\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7]),
-          "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-        : "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]), "v"(ba[4]), "v"(ba[5]), "v"(ba[6]), "v"(ba[7]),
-          "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
-}
-
-// Four A fragments in one asm block that also waits for them.
-__device__ __forceinline__ void wide_reads_a(const uint32_t (&aa)[4], u32x4 (&a)[4]) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
+        "ds_read_b128 %0, %4 offset:%5\n\tds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\tds_read_b128 %3, %4 offset:%8"
         : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-        : "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
+        : "v"(addr), "i"(OFF), "i"(OFF + 1024), "i"(OFF + 2048), "i"(OFF + 3072));
+}
+// The eight B fragment halves of a stage at byte address `stage`: b[2*jj + h] for block
+// jj (CB blocks of gate then CB of up, or four of the down projection) and row half h.
+// The reads wait for themselves in the same asm block (the halves are joined into MFMA
+// operands, which must not be assembled before the data is there), and that wait also
+// covers the A fragments a0 read earlier without one.
+template <bool DUAL, int BN>
+__device__ __forceinline__ void wfrag_read_b_wait(uint32_t stage, const WideFragOff<DUAL, BN> &fo, u32x2 (&b)[8],
+                                                  u32x4 (&a0)[4]) {
+    constexpr int HO = 8 * BN;                                 // rows kb + 4 + l/4
+    constexpr int QO = 2 * WideCfg<DUAL, BN>::B_ELEMS;          // the up weight
+    if constexpr (DUAL) {
+        static_assert(WideFragOff<DUAL, BN>::CB == 2, "two blocks per weight");
+        const uint32_t v0 = stage + fo.b[0], v1 = stage + fo.b[1];
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %12\n\tds_read_b64_tr_b16 %1, %12 offset:%14\n\t"
+            "ds_read_b64_tr_b16 %2, %13\n\tds_read_b64_tr_b16 %3, %13 offset:%14\n\t"
+            "ds_read_b64_tr_b16 %4, %12 offset:%15\n\tds_read_b64_tr_b16 %5, %12 offset:%16\n\t"
+            "ds_read_b64_tr_b16 %6, %13 offset:%15\n\tds_read_b64_tr_b16 %7, %13 offset:%16\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7]),
+              "+v"(a0[0]), "+v"(a0[1]), "+v"(a0[2]), "+v"(a0[3])
+            : "v"(v0), "v"(v1), "i"(HO), "i"(QO), "i"(QO + HO));
+    } else {
+        static_assert(WideFragOff<DUAL, BN>::CB == 4, "four blocks");
+        const uint32_t v0 = stage + fo.b[0], v1 = stage + fo.b[1], v2 = stage + fo.b[2], v3 = stage + fo.b[3];
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %12\n\tds_read_b64_tr_b16 %1, %12 offset:%16\n\t"
+            "ds_read_b64_tr_b16 %2, %13\n\tds_read_b64_tr_b16 %3, %13 offset:%16\n\t"
+            "ds_read_b64_tr_b16 %4, %14\n\tds_read_b64_tr_b16 %5, %14 offset:%16\n\t"
+            "ds_read_b64_tr_b16 %6, %15\n\tds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7]),
+              "+v"(a0[0]), "+v"(a0[1]), "+v"(a0[2]), "+v"(a0[3])
+            : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "i"(HO));
+    }
+}
+__device__ __forceinline__ void wfrag_wait(u32x4 (&a)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
 }
 
-// One K step of 32 for this wave's 128-row block; NRB = 16-row blocks of the wave that
-// hold rows, rounded up to even (a compile-time count, so the loop body has no branches
-// around its MFMAs).  U = 4 B blocks of 16 columns: CB of gate then CB of up, or CB = 4
-// of the down projection.  The loads of a later stage (into a slot the barrier freed) are
-// issued between groups of MFMAs, so a load that waits for the memory pipeline to accept
-// it overlaps MFMAs already issued rather than the whole K step.
-template <bool DUAL, int BN, int NRB>
-__device__ __forceinline__ void wstage_step(const uint16_t *stage, const WideArgs &ga, int k_next,
-                                            uint16_t *next_stage, f32x4 (&acc0)[WideCfg<DUAL, BN>::NACC],
-                                            f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC]) {
+// The 16 MFMAs of row blocks [4*G + lo, 4*G + hi) (those below NRB) with fragments a, b.
+template <bool DUAL, int BN, int NRB, int G>
+__device__ __forceinline__ void wide_mfma(int lo, int hi, const u32x4 (&a)[4], const u32x2 (&b)[8],
+                                          f32x4 (&acc0)[WideCfg<DUAL, BN>::NACC],
+                                          f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC]) {
+    constexpr int CB = WideCfg<DUAL, BN>::CB;
+#pragma unroll
+    for (int rb = lo; rb < hi; ++rb) {
+        const int rr = 4 * G + rb;
+        if (rr < NRB)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int q = jj / CB, cb = jj % CB;
+                const u32x4 bf = join(b[2 * jj], b[2 * jj + 1]);
+                if (q == 0)
+                    acc0[CB * rr + cb] = mfma_bf16_16x16x32(a[rb], bf, acc0[CB * rr + cb]);
+                else
+                    acc1[CB * rr + cb] = mfma_bf16_16x16x32(a[rb], bf, acc1[CB * rr + cb]);
+            }
+    }
+}
+
+// One K stage st (in ring slot st % NS), entered with its group-0 A fragments (a0) and its
+// B fragments (b) in registers:
+//   read group 1's A fragments; group-0 MFMAs with two loads of stage st+NS-1 (into the
+//   slot of stage st-1, which every wave finished reading before the last barrier); wait
+//   for group 1's fragments; this wave's loads of stage st+1 complete, then the barrier
+//   (every wave's loads of stage st+1 have landed and every wave is done with slot st);
+//   read stage st+1's group-0 A fragments into a0 (their MFMAs are issued); group-1 MFMAs
+//   with the other two loads; read stage st+1's B fragments into b once those MFMAs are
+//   issued, and wait for all of them.
+// A wave that issues a load can stall until the memory pipeline takes it, and issues no
+// MFMA meanwhile.  So the two waves that share a SIMD (w and w + 4: LATE is w >= 4) place
+// their loads at opposite points: one after each run of 8 MFMAs, the other before it, and
+// one wave's stall overlaps the other's MFMAs.
+// NRB = 16-row blocks of the wave that hold rows, rounded up to even (a compile-time count,
+// so no branches surround the MFMAs); every variant issues the same loads and barriers.
+template <bool DUAL, int BN, int NRB, bool LATE>
+__device__ __forceinline__ void wide_stage(int st, int nk, const WideArgs &ga, const WideFragOff<DUAL, BN> &fo,
+                                           uint32_t ring, uint16_t *ring_p, u32x4 (&a0)[4], u32x2 (&b)[8],
+                                           u32x4 (&a1)[4],
+                                           f32x4 (&acc0)[WideCfg<DUAL, BN>::NACC],
+                                           f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC]) {
     using C = WideCfg<DUAL, BN>;
-    constexpr int CB = C::CB;
-    const uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
-    const int lane = lane_id(), w = wave_id();
-    const int g = lane >> 4, i = lane & 15;
-    const int r0 = 128 * (w >> 2), c0 = (BN / 4) * (w & 3);
-    const int kb = 8 * g;
-    // the next stage's loads: A blocks, then B blocks (k_next < 0: none)
-    uint16_t *nA = next_stage, *nB0 = next_stage + C::A_ELEMS, *nB1 = nB0 + C::B_ELEMS;
-    const MK_G uint16_t *ab = ga.A + k_next;
-    const size_t kk = (size_t)k_next * ga.ldb;
-    auto load_a = [&]() {
-        if (k_next >= 0) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) lds_dma16(ab + ga.a_off[q], (MK_L void *)(nA + (2 * w + q) * 512));
-        }
-    };
-    auto load_b = [&]() {
-        if (k_next >= 0) {
-#pragma unroll
-            for (int q = 0; q < C::B_BLOCKS / kWaves; ++q) {
-                const int blk = (C::B_BLOCKS / kWaves) * w + q;
-                lds_dma16(ga.B0 + kk + ga.b_off[q], (MK_L void *)(nB0 + blk * 512));
-                if constexpr (DUAL) lds_dma16(ga.B1 + kk + ga.b_off[q], (MK_L void *)(nB1 + blk * 512));
-            }
-        }
-    };
-    uint32_t aa[4], ba[8];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const int q = jj / CB, cb = jj % CB;
-        const uint16_t *sB = q ? sB1 : sB0;
-        ba[2 * jj] = wb_frag_addr<BN>(sB, kb, c0 + 16 * cb);
-        ba[2 * jj + 1] = wb_frag_addr<BN>(sB, kb + 4, c0 + 16 * cb);
-    }
-    u32x2 b[8];
-    u32x4 a[4];
-    auto mfma_rows = [&](int rb_lo, int rb_hi, int half) {
-#pragma unroll
-        for (int rb = rb_lo; rb < rb_hi; ++rb) {
-            const int rr = 4 * half + rb;
-            if (rr < NRB)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int q = jj / CB, cb = jj % CB;
-                    if (q == 0)
-                        acc0[CB * rr + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * jj], b[2 * jj + 1]), acc0[CB * rr + cb]);
-                    else
-                        acc1[CB * rr + cb] = mfma_bf16_16x16x32(a[rb], join(b[2 * jj], b[2 * jj + 1]), acc1[CB * rr + cb]);
-                }
-        }
-    };
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        if (half * 4 < NRB) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int r = r0 + 16 * (4 * half + rb) + i;
-                aa[rb] = lds_addr(sA + r * kWBK + ((g ^ wswa(r)) << 3));
-            }
-            if (half == 0)
-                wide_reads(ba, aa, b, a);
-            else
-                wide_reads_a(aa, a);
-        }
-        mfma_rows(0, 2, half);
+    constexpr int NS = C::NS;
+    const uint32_t sb = ring + (uint32_t)((st % NS) * C::STAGE_BYTES);
+    const int ld = st + NS - 1;  // the stage whose loads this one issues
+    uint16_t *ld_p = ring_p + ((st + NS - 1) % NS) * C::STAGE_ELEMS;
+    const bool lds = ld < nk;
+    if constexpr (NRB > 4) wfrag_read_a<4096>(sb + fo.a, a1);
+    if constexpr (LATE) {
+        if (lds) wstage_load<DUAL, BN, 1>(ga, ld * kWBK, ld_p);
         __builtin_amdgcn_sched_barrier(0);
-        if (half == 0)
-            load_a();
+    }
+    wide_mfma<DUAL, BN, NRB, 0>(0, 2, a0, b, acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (lds) {
+        if constexpr (LATE)
+            wstage_load<DUAL, BN, 2>(ga, ld * kWBK, ld_p);
         else
-            load_b();
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_rows(2, 4, half);
+            wstage_load<DUAL, BN, 1>(ga, ld * kWBK, ld_p);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    wide_mfma<DUAL, BN, NRB, 0>(2, 4, a0, b, acc0, acc1);
+    if constexpr (!LATE) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (lds) wstage_load<DUAL, BN, 2>(ga, ld * kWBK, ld_p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NRB > 4) wfrag_wait(a1);
+    const bool more = st + 1 < nk;
+    if (more) {
+        if (lds)
+            wait_vm<(NS - 3) * C::LOADS + 2>();  // after stage st+1: stages st+2 .. st+NS-2, two of st+NS-1
+        else
+            wait_vm<0>();
+        bare_barrier();
+        if constexpr (NRB > 0) wfrag_read_a<0>(ring + (uint32_t)(((st + 1) % NS) * C::STAGE_BYTES) + fo.a, a0);
+    }
+    if constexpr (LATE) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (lds) wstage_load<DUAL, BN, 3>(ga, ld * kWBK, ld_p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wide_mfma<DUAL, BN, NRB, 1>(0, 2, a1, b, acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (lds) {
+        if constexpr (LATE)
+            wstage_load<DUAL, BN, 4>(ga, ld * kWBK, ld_p);
+        else
+            wstage_load<DUAL, BN, 3>(ga, ld * kWBK, ld_p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wide_mfma<DUAL, BN, NRB, 1>(2, 4, a1, b, acc0, acc1);
+    if constexpr (!LATE) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (lds) wstage_load<DUAL, BN, 4>(ga, ld * kWBK, ld_p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NRB > 0)
+        if (more) wfrag_read_b_wait<DUAL, BN>(ring + (uint32_t)(((st + 1) % NS) * C::STAGE_BYTES), fo, b, a0);
 }
 
-template <bool DUAL, int BN, int NRB>
+template <bool DUAL, int BN, int NRB, bool LATE>
 __device__ __forceinline__ void wide_loop(const WideArgs &ga, int nk, f32x4 (&acc0)[WideCfg<DUAL, BN>::NACC],
                                           f32x4 (&acc1)[WideCfg<DUAL, BN>::NACC], GemmSmem &s) {
     using C = WideCfg<DUAL, BN>;
     constexpr int NS = C::NS;
+    const WideFragOff<DUAL, BN> fo;
+    const uint32_t ring = lds_addr(s.ring);
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
-        if (p < nk) wstage_load<DUAL, BN>(ga, p * kWBK, s.ring + p * C::STAGE_ELEMS);
-    int slot = 0;
-    for (int st = 0; st < nk; ++st) {
-        if (st + NS - 2 < nk)
-            wait_vm<(NS - 2) * C::LOADS>();
-        else
-            wait_vm<0>();
-        bare_barrier();
-        const int nxt = st + NS - 1;
-        const int ns = slot == 0 ? NS - 1 : slot - 1;  // the slot of stage st - 1, free now
-        wstage_step<DUAL, BN, NRB>(s.ring + slot * C::STAGE_ELEMS, ga, nxt < nk ? nxt * kWBK : -1,
-                                   s.ring + ns * C::STAGE_ELEMS, acc0, acc1);
-        slot = slot == NS - 1 ? 0 : slot + 1;
+        if (p < nk) wstage_load<DUAL, BN, 0>(ga, p * kWBK, s.ring + p * C::STAGE_ELEMS);
+    // stage 0 complete (this wave's loads, then everyone's), then its fragments
+    if (nk >= NS - 1)
+        wait_vm<(NS - 2) * C::LOADS>();
+    else
+        wait_vm<0>();
+    bare_barrier();
+    u32x4 a0[4], a1[4];
+    u32x2 b[8];
+    if constexpr (NRB > 0) {
+        wfrag_read_a<0>(ring + fo.a, a0);
+        wfrag_read_b_wait<DUAL, BN>(ring, fo, b, a0);
     }
+    for (int st = 0; st < nk; ++st)
+        wide_stage<DUAL, BN, NRB, LATE>(st, nk, ga, fo, ring, s.ring, a0, b, a1, acc0, acc1);
     wait_vm<0>();
     __syncthreads();
 }
@@ -1275,15 +1363,24 @@ __device__ __forceinline__ void wide_tile(const WideArgs &ga, f32x4 (&acc0)[Wide
         acc0[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int wrows = min(max(uni(ga.nrows) - 128 * (wave_id() >> 2), 0), 128);
+    const int wrows = min(max(uni(ga.nrows) - kWR * (wave_id() >> 2), 0), kWR);
     const int nrb2 = uni((wrows + 31) / 32);  // pairs of 16-row blocks
     const int nk = uni(ga.K / kWBK);
-    switch (nrb2) {
-        case 4: wide_loop<DUAL, BN, 8>(ga, nk, acc0, acc1, s); break;
-        case 3: wide_loop<DUAL, BN, 6>(ga, nk, acc0, acc1, s); break;
-        case 2: wide_loop<DUAL, BN, 4>(ga, nk, acc0, acc1, s); break;
-        case 1: wide_loop<DUAL, BN, 2>(ga, nk, acc0, acc1, s); break;
-        default: wide_loop<DUAL, BN, 0>(ga, nk, acc0, acc1, s); break;
+    if (wave_id() < 4) {  // rows 0-127 of the tile
+        switch (nrb2) {
+            case 4: wide_loop<DUAL, BN, 8, false>(ga, nk, acc0, acc1, s); break;
+            case 3: wide_loop<DUAL, BN, 6, false>(ga, nk, acc0, acc1, s); break;
+            case 2: wide_loop<DUAL, BN, 4, false>(ga, nk, acc0, acc1, s); break;
+            default: wide_loop<DUAL, BN, 2, false>(ga, nk, acc0, acc1, s); break;  // a tile has a row
+        }
+    } else {
+        switch (nrb2) {
+            case 4: wide_loop<DUAL, BN, 8, true>(ga, nk, acc0, acc1, s); break;
+            case 3: wide_loop<DUAL, BN, 6, true>(ga, nk, acc0, acc1, s); break;
+            case 2: wide_loop<DUAL, BN, 4, true>(ga, nk, acc0, acc1, s); break;
+            case 1: wide_loop<DUAL, BN, 2, true>(ga, nk, acc0, acc1, s); break;
+            default: wide_loop<DUAL, BN, 0, true>(ga, nk, acc0, acc1, s); break;
+        }
     }
 }
 
@@ -1314,9 +1411,9 @@ __device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &P, int e
     wide_tile<true, BN>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
-    const int r0 = 128 * (w >> 2), c0 = n * BN + (BN / 4) * (w & 3);
+    const int r0 = kWR * (w >> 2), c0 = n * BN + (BN / 4) * (w & 3);
 #pragma unroll
-    for (int rb = 0; rb < 8; ++rb)
+    for (int rb = 0; rb < kWRB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -1351,9 +1448,9 @@ __device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &P, int e
     wide_tile<false, BN>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
-    const int r0 = 128 * (w >> 2), c0 = n * BN + (BN / 4) * (w & 3);
+    const int r0 = kWR * (w >> 2), c0 = n * BN + (BN / 4) * (w & 3);
 #pragma unroll
-    for (int rb = 0; rb < 8; ++rb)
+    for (int rb = 0; rb < kWRB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -1492,14 +1589,15 @@ __device__ __forceinline__ void trace_task(const MK_C Params &P, int g, int kind
 
 // Grouping of routing tile t and its notifications: perm/inv for the tile's assignments,
 // then each expert's event is decremented by the tile's rows of that expert; in dynamic
-// mode the gate/up tiles of every expert this brought to zero are pushed, all ranges with
-// one reservation of queue slots.  With `whole` (the batch is this one tile, scanned by
+// mode the gate/up tiles of every expert this brought to zero are pushed, with one
+// reservation of queue slots for all of them (a prefix sum over the experts places each
+// expert's tasks, in expert order).  With `whole` (the batch is this one tile, scanned by
 // the same task) every expert with rows is complete and no expert event is used.
 __device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs, int t, bool dyn, bool whole) {
+    static_assert(kMaxE <= kThreads, "one thread per expert");
     task_group(P, t);
     count_task(P, K_GROUP);
     GroupSmem &gr = g_sm.u.gr;
-    if (threadIdx.x == 0) gr.nfired = 0;
     wg_stores_done();
     int skip = -1;
     if ((P.debug & 1) && t == 0) {  // debug: drop the notification of the tile's first expert
@@ -1509,10 +1607,10 @@ __device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs
                 break;
             }
     }
-    for (int e = threadIdx.x; e < P.E; e += kThreads) {
-        const int cnt = __popcll(gr.mask[e]);
-        if (!cnt) continue;
-        bool fire = false;
+    const int e = threadIdx.x;
+    const int cnt = e < P.E ? __popcll(gr.mask[e]) : 0;
+    bool fire = false;
+    if (cnt) {
         if (whole) {
             if (e == skip) {
                 if (!dyn) pub(P.ev_exp + e, 1);  // a wait that never ends (debug)
@@ -1523,59 +1621,43 @@ __device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs
             const int old = add_relaxed(P.ev_exp + e, -cnt);
             fire = dyn && old == cnt;
         }
-        if (fire) {  // the expert's row tiles, loaded by each firing thread in parallel
-            const int i = atomicAdd(&gr.nfired, 1);
-            gr.fired[i] = e;
-            gr.fm0[i] = ld_relaxed(P.mt_base + e);
-            gr.fm1[i] = ld_relaxed(P.mt_base + e + 1);
-        }
+    }
+    if (!dyn) return;
+    // push the gate/up tiles of every expert this tile completed
+    if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));  // block bases for the pushes
+    int m0 = 0, nm = 0;
+    if (fire) {
+        m0 = ld_relaxed(P.mt_base + e);
+        nm = ld_relaxed(P.mt_base + e + 1) - m0;
+    }
+    const int Q = P.NB1 / P.S;  // gate/up tasks per row tile and split
+    int tot;
+    const int off = block_excl_scan(nm * Q * P.S, gr.part, &tot);
+    if (!tot) return;
+    if (threadIdx.x == 0) gr.base = add_relaxed(P.ctl + CTL_QTAIL, tot);
+    __syncthreads();
+    const int base = gr.base;
+    if (base + tot > P.q_cap) {
+        if (threadIdx.x == 0) set_error(P.ctl, 4 /* MOE_MK_ERR_QUEUE */);
+        return;
+    }
+    if (e < P.E) {
+        gr.poff[e] = base + off;
+        gr.pm0[e] = m0;
+        gr.pnm[e] = nm;
     }
     __syncthreads();
-    if (dyn) {
-        // push the gate/up tiles of every expert this tile completed; task ranges are
-        // ordered by expert, so fired experts whose ranges abut go out as one range
-        if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));  // block bases for the pushes
-        if (threadIdx.x == 0) {
-            const int nf = gr.nfired;
-            for (int i = 1; i < nf; ++i) {  // sort the fired experts' ranges (they are disjoint)
-                const int v0 = gr.fm0[i], v1 = gr.fm1[i];
-                int j = i - 1;
-                while (j >= 0 && gr.fm0[j] > v0) {
-                    gr.fm0[j + 1] = gr.fm0[j];
-                    gr.fm1[j + 1] = gr.fm1[j];
-                    --j;
-                }
-                gr.fm0[j + 1] = v0;
-                gr.fm1[j + 1] = v1;
-            }
-            const int Q = P.NB1 / P.S;
-            int nr = 0, tot = 0, i = 0;
-            while (i < nf) {
-                int j = i;
-                while (j + 1 < nf && gr.fm1[j] == gr.fm0[j + 1]) ++j;
-                const int m0 = gr.fm0[i], m1 = gr.fm1[j];
-                for (int sp = 0; sp < P.S; ++sp) {
-                    gr.rg0[nr] = base_g1(bs, sp) + m0 * Q;
-                    gr.rcnt[nr] = (m1 - m0) * Q;
-                    tot += gr.rcnt[nr++];
-                }
-                i = j + 1;
-            }
-            gr.nr = nr;
-            gr.tot = tot;
-            gr.base = tot ? add_relaxed(P.ctl + CTL_QTAIL, tot) : 0;
-        }
-        __syncthreads();
-        if (gr.base + gr.tot > P.q_cap) {
-            if (threadIdx.x == 0) set_error(P.ctl, 4 /* MOE_MK_ERR_QUEUE */);
-        } else {
-            const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
-            int off = gr.base;
-            for (int r = 0; r < gr.nr; ++r) {
-                for (int i = threadIdx.x; i < gr.rcnt[r]; i += kThreads)
-                    st_relaxed64(P.qslots + off + i, tag | (uint32_t)(gr.rg0[r] + i));
-                off += gr.rcnt[r];
-            }
+    // wave w writes the slots of experts w, w + kWaves, ..., 64 slots per store
+    const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
+    const int lane = lane_id();
+    for (int x = wave_id(); x < P.E; x += kWaves) {
+        const int n = gr.pnm[x] * Q;
+        if (!n) continue;
+        int slot = gr.poff[x];
+        for (int sp = 0; sp < P.S; ++sp) {
+            const int g0 = base_g1(bs, sp) + gr.pm0[x] * Q;
+            for (int i = lane; i < n; i += 64) st_relaxed64(P.qslots + slot + i, tag | (uint32_t)(g0 + i));
+            slot += n;
         }
     }
 }

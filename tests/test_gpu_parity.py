@@ -119,10 +119,12 @@ def test_down_projection_k_splits(f, S, sched):
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
-@pytest.mark.parametrize("B,d,f,E,k", [(300, 256, 384, 4, 2), (517, 256, 256, 16, 4), (129, 512, 128, 1, 1)])
+@pytest.mark.parametrize("B,d,f,E,k", [(300, 256, 384, 4, 2), (517, 256, 256, 16, 4), (129, 512, 128, 1, 1),
+                                       (700, 256, 256, 2, 1)])
 def test_wide_tiles(B, d, f, E, k, sched):
-    # an expert averages >= 128 rows: 128-row tiles, ragged last tiles (some with rows for
-    # one of the two row halves only), several K steps of 32
+    # an expert averages >= 128 rows: 256-row tiles, ragged last tiles (some with rows for
+    # one of the two 128-row halves only; experts of more than 256 rows with a second
+    # tile), several K steps of 32
     assert tile_config(B, k, E, d, f)[0] == 256
     log(f"wide tiles B={B} d={d} f={f} E={E} k={k} sched={SNAME[sched]}")
     cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=1300 + B)
@@ -131,10 +133,10 @@ def test_wide_tiles(B, d, f, E, k, sched):
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
 def test_wide_tiles_constant_input(sched):
-    # every token identical: k experts take all 260 rows each (tiles of 256 and 4 rows)
-    cfg, x, Wr, bias, W1, W3, W2 = small_case(260, 256, 256, 4, 2, seed=61)
+    # every token identical: k experts take all 324 rows each (tiles of 256 and 68 rows)
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(324, 256, 256, 4, 2, seed=61)
     x[:] = x[0]
-    assert tile_config(260, 2, 4, 256, 256)[0] == 256
+    assert tile_config(324, 2, 4, 256, 256)[0] == 256
     full_check(x, Wr, bias, W1, W3, W2, 2, sched, "wide constant input")
 
 
