@@ -261,6 +261,17 @@ __device__ __forceinline__ void store_bf16_pair(MK_G uint16_t *row, int col, flo
     if (ok && (col & 1) == 0) pub((MK_G uint32_t *)(row + col), hv | (nb << 16));
 }
 
+// The kernel parameters through a wave-uniform reference.  A callee receives its reference
+// in vector registers, so field reads through it would be vector loads from the kernel-
+// argument segment, each followed by a wait for all of the wave's loads; through a uniform
+// address they are scalar loads that the scalar cache keeps.
+__device__ __forceinline__ const MK_C Params &uni_params(const MK_C Params &P) {
+    const uint64_t a = (uint64_t)(uintptr_t)&P;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return *(const MK_C Params *)(uintptr_t)(lo | (hi << 32));
+}
+
 // ------------------------------------------------------------------------------ ROUTE
 // logit[b,e] = sum_j x[b,j] Wr[j,e] (+ bias[e]) in the fixed fp32 order: lane l of the
 // wave accumulates j = l, l+64, ... with fma (one chain per lane), then the 64 chains are
@@ -314,28 +325,33 @@ __device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[T
 }
 
 // Router tile through LDS (E a multiple of 4).  The workgroup's kWaves*TPW tokens (wave w
-// owns TPW of them) and 16 experts share every staged slice: per 128 values of j, the
-// 128 x 16 block of Wr (8 KB, each wave moving 16 of its rows) and the tokens' 128 x
-// values (each wave moving its own), in a ring of as many stages as LDS holds (up to 16:
-// the loads are latency-bound, so the depth in flight sets the rate), filled by
-// global_load_lds.  Lane l accumulates chain l (j = l, l+64, ... in order) of every
-// (token, expert) pair of its wave; a stage holds two consecutive steps of every chain.
-//   Wr stage in LDS: [128 rows][4 chunks of 4 experts]; chunk c of row r at c ^ rswz(r),
+// owns TPW of them) and 16 experts share every staged slice: per RPS values of j, the
+// RPS x 16 block of Wr (each wave moving RPS/8 of its rows, 1 KB per load) and the tokens'
+// RPS x values (each wave moving its own), in a ring of as many stages as LDS holds (up to
+// 16), filled by global_load_lds.  Deeper stages (RPS = 512 with one token per wave) move
+// more bytes per ring iteration, which sets a workgroup's streaming rate.  Lane l
+// accumulates chain l (j = l, l+64, ... in order) of every (token, expert) pair of its
+// wave; a stage holds RPS/64 consecutive steps of every chain.
+//   Wr stage in LDS: [RPS rows][4 chunks of 4 experts]; chunk c of row r at c ^ rswz(r),
 //     so the 16 rows a quarter-wave reads fall on distinct 16-byte bank groups.
-//   x stage: per wave, TPW blocks of 256 bytes, each one token's 128 bf16 values.
+//   x stage: per wave, TPW blocks of 2*RPS bytes, each one token's RPS bf16 values.
 // Tokens past B and experts past E load clamped (valid) addresses; their sums are never
 // written.
 __device__ __forceinline__ int rswz(int r) { return (r >> 2) & 3; }
 
-template <int TPW>
+template <int TPW, int RPS>
 struct RouteCfg {
-    static constexpr int WR_BYTES = 128 * 16 * 4;
-    static constexpr int STAGE_BYTES = WR_BYTES + kWaves * TPW * 256;
-    static constexpr int LOADS = 2;  // one Wr block and one x block per wave
+    static constexpr int WR_BYTES = RPS * 16 * 4;
+    static constexpr int WR_LOADS = WR_BYTES / 1024 / kWaves;  // 1 KB Wr loads per wave and stage
+    static constexpr int XB = 2 * RPS * TPW;                   // x bytes per wave and stage
+    static constexpr int X_LOADS = XB >= 1024 ? XB / 1024 : XB / 256;  // 16-byte lanes, else 4-byte lanes
+    static constexpr int STAGE_BYTES = WR_BYTES + kWaves * XB;
+    static constexpr int LOADS = WR_LOADS + X_LOADS;
     static constexpr int NS = kRingBytes / STAGE_BYTES < 16 ? kRingBytes / STAGE_BYTES : 16;
+    static_assert(WR_LOADS >= 1 && WR_LOADS * 1024 * kWaves == WR_BYTES, "whole Wr loads per wave");
+    static_assert(XB % 1024 == 0 || (XB < 1024 && XB % 256 == 0), "whole x loads per wave");
     static_assert(NS >= 3 && NS * STAGE_BYTES <= kRingBytes, "router ring");
     static_assert((NS - 2) * LOADS < 64, "vmcnt range");
-    static_assert(WR_BYTES == kWaves * 1024, "one Wr block per wave");
 };
 
 template <int TPW>
@@ -360,35 +376,46 @@ __device__ __forceinline__ void route_reads(uint32_t wa, const uint32_t (&xa)[TP
     }
 }
 
-template <int TPW>
-__device__ __attribute__((noinline)) void route_tile(const MK_C Params &P, int b0, int e0) {
-    using C = RouteCfg<TPW>;
+template <int TPW, int RPS>
+__device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int b0, int e0) {
+    const MK_C Params &P = uni_params(Pa);
+    using C = RouteCfg<TPW, RPS>;
     constexpr int NS = C::NS;
     b0 = uni(b0);
     e0 = uni(e0);
     uint8_t *ring = (uint8_t *)g_sm.u.g.ring;
     const int lane = lane_id(), w = wave_id();
-    const int nst = uni(P.d / 128);
+    const int nst = uni(P.d / RPS);
     const int E = P.E;
-    // this lane's DMA sources: Wr row 16w + lane/4 (chunk position lane%4) and, per token
-    // t of the wave, the j pair 2*lane .. 2*lane+1 of the stage's 128 values
-    const int wrow = 16 * w + (lane >> 2);
+    // this lane's Wr DMA source: load i of wave w covers rows RPS/8*w + 16*i + lane/4 (chunk
+    // position lane%4; the swizzle of those rows does not depend on i)
+    const int wrow = (RPS / kWaves) * w + (lane >> 2);
     const int wcol = min(e0 + 4 * ((lane & 3) ^ rswz(wrow)), E - 4);
     const MK_G float *wsrc = P.Wr + (size_t)wrow * E + wcol;
-    // x: with one token per wave each lane moves a j pair (4 bytes); with four, lane L
-    // moves values 8*(L%16) .. +7 of token L/16 (16 bytes), so the block is one load
-    const MK_G uint16_t *xsrc =
-        TPW == 1 ? P.x + (size_t)min(b0 + w, P.B - 1) * P.d + 2 * lane
-                 : P.x + (size_t)min(b0 + w * TPW + (lane >> 4), P.B - 1) * P.d + 8 * (lane & 15);
-    const size_t wstep = (size_t)128 * E;
+    // x DMA sources: byte q of the wave's x block (q = 1024*i + 16*lane, or 256*i + 4*lane)
+    // is value (q % (2*RPS))/2 of the wave's token q / (2*RPS)
+    const MK_G uint16_t *xsrc[C::X_LOADS];
+#pragma unroll
+    for (int i = 0; i < C::X_LOADS; ++i) {
+        const int q = C::XB >= 1024 ? 1024 * i + 16 * lane : 256 * i + 4 * lane;
+        const int tok = min(b0 + w * TPW + q / (2 * RPS), P.B - 1);
+        xsrc[i] = P.x + (size_t)tok * P.d + (q % (2 * RPS)) / 2;
+    }
+    const size_t wstep = (size_t)RPS * E;
     auto load = [&](int st, int s) {
         uint8_t *sp = ring + s * C::STAGE_BYTES;
-        lds_dma16(wsrc + (size_t)st * wstep, (MK_L void *)(sp + w * 1024));
-        MK_L void *xd = (MK_L void *)(sp + C::WR_BYTES + w * TPW * 256);
-        if constexpr (TPW == 1)
-            __builtin_amdgcn_global_load_lds(xsrc + (size_t)st * 128, xd, 4, 0, 0);
-        else
-            lds_dma16(xsrc + (size_t)st * 128, xd);
+#pragma unroll
+        for (int i = 0; i < C::WR_LOADS; ++i)
+            lds_dma16(wsrc + (size_t)st * wstep + (size_t)16 * i * E,
+                      (MK_L void *)(sp + ((RPS / kWaves) * w + 16 * i) * 64));
+        uint8_t *xd = sp + C::WR_BYTES + w * C::XB;
+#pragma unroll
+        for (int i = 0; i < C::X_LOADS; ++i) {
+            if constexpr (C::XB >= 1024)
+                lds_dma16(xsrc[i] + (size_t)st * RPS, (MK_L void *)(xd + 1024 * i));
+            else
+                __builtin_amdgcn_global_load_lds(xsrc[i] + (size_t)st * RPS, (MK_L void *)(xd + 256 * i), 4, 0, 0);
+        }
     };
     float acc[TPW * 16];
 #pragma unroll
@@ -408,11 +435,12 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &P, int b
         if (nxt < nst) load(nxt, slot == 0 ? NS - 1 : slot - 1);
         const uint32_t sb = rbase + (uint32_t)(slot * C::STAGE_BYTES);
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int row = 64 * sub + lane;  // j = 128*st + row: chain `lane`, step 2*st + sub
+        for (int sub = 0; sub < RPS / 64; ++sub) {
+            const int row = 64 * sub + lane;  // j = RPS*st + row: chain `lane`, step (RPS/64)*st + sub
             uint32_t xa[TPW];
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) xa[t] = sb + (uint32_t)(C::WR_BYTES + (w * TPW + t) * 256 + 2 * row);
+            for (int t = 0; t < TPW; ++t)
+                xa[t] = sb + (uint32_t)(C::WR_BYTES + w * C::XB + t * 2 * RPS + 2 * row);
             f32x4 wv[4];
             uint32_t xr[TPW];
             route_reads<TPW>(sb + (uint32_t)(row * 64 + 16 * rswz(row)), xa, wv, xr);
@@ -434,7 +462,8 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &P, int b
 }
 
 // Router wave for E not a multiple of 4: plain scalar loads, same summation order.
-__device__ __attribute__((noinline)) void route_wave_scalar(const MK_C Params &P, int b0, int e0) {
+__device__ __attribute__((noinline)) void route_wave_scalar(const MK_C Params &Pa, int b0, int e0) {
+    const MK_C Params &P = uni_params(Pa);
     const int lane = lane_id();
     float acc[16];
 #pragma unroll
@@ -455,15 +484,20 @@ __device__ __attribute__((noinline)) void route_wave_scalar(const MK_C Params &P
 
 // Router task (tg, eb): tokens [kWaves*tpw*tg, +kWaves*tpw), wave w taking tpw of them,
 // experts [16*eb, +16).
-__device__ __attribute__((noinline)) void task_route(const MK_C Params &P, int tg, int eb) {
+__device__ __attribute__((noinline)) void task_route(const MK_C Params &Pa, int tg, int eb) {
+    const MK_C Params &P = uni_params(Pa);
     const int e0 = eb * kRouteExperts;
     if ((P.E & 3) != 0) {
         const int tpw = uni(P.tpw);
         for (int t = 0; t < tpw; ++t) route_wave_scalar(P, (tg * kWaves + wave_id()) * tpw + t, e0);
-    } else if (P.tpw == 1)
-        route_tile<1>(P, tg * kWaves, e0);
-    else
-        route_tile<4>(P, tg * kWaves * 4, e0);
+    } else if (P.tpw == 1) {
+        if (P.d % 512 == 0)
+            route_tile<1, 512>(P, tg * kWaves, e0);
+        else
+            route_tile<1, 128>(P, tg * kWaves, e0);
+    } else {
+        route_tile<4, 128>(P, tg * kWaves * 4, e0);
+    }
 }
 
 // ------------------------------------------------------------------------------ TOPK
@@ -504,7 +538,8 @@ __device__ __forceinline__ unsigned long long lane_xor_u64(unsigned long long v)
 }
 
 template <int KB>
-__device__ __attribute__((noinline)) void topk_tile(const MK_C Params &P, int t) {
+__device__ __attribute__((noinline)) void topk_tile(const MK_C Params &Pa, int t) {
+    const MK_C Params &P = uni_params(Pa);
     TopkSmem &ts = g_sm.u.t;
     const int lane = lane_id(), w = wave_id();
     const int E = P.E, k = P.k;
@@ -595,7 +630,8 @@ __device__ __attribute__((noinline)) void topk_tile(const MK_C Params &P, int t)
     for (int i = threadIdx.x; i < E; i += kThreads) pub(P.tile_hist + (size_t)t * E + i, ts.hist[i]);
 }
 
-__device__ __attribute__((noinline)) void task_topk(const MK_C Params &P, int t) {
+__device__ __attribute__((noinline)) void task_topk(const MK_C Params &Pa, int t) {
+    const MK_C Params &P = uni_params(Pa);
     if (P.k <= 2)
         topk_tile<2>(P, t);
     else if (P.k <= 4)
@@ -637,7 +673,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int *part, int *total) {
 // hist[e] ("Core method": the prefix sum decides how many GroupGEMM tiles each expert
 // triggers).  Events are at rest (zero) and nothing decrements them before the scan is
 // published, so arming is a plain store.  Returns the number of row tiles.
-__device__ __attribute__((noinline)) int task_scan(const MK_C Params &P, bool arm_experts) {
+__device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, bool arm_experts) {
+    const MK_C Params &P = uni_params(Pa);
     const int e = threadIdx.x;
     const int E = P.E, BM = P.BM;
     int *tb = g_sm.u.s.tiles;
@@ -707,7 +744,8 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &P, bool ar
 // most once), read off a 64-bit token mask per expert.  Row p = tile_off[t,e] + rank;
 // perm[p] = b*k+i and inv[b*k+i] = p.  The rows themselves are not copied: the gate/up
 // GroupGEMM reads each grouped row of x through perm.
-__device__ __attribute__((noinline)) void task_group(const MK_C Params &P, int t) {
+__device__ __attribute__((noinline)) void task_group(const MK_C Params &Pa, int t) {
+    const MK_C Params &P = uni_params(Pa);
     GroupSmem &g = g_sm.u.gr;
     const int E = P.E, k = P.k;
     const int lane = lane_id(), w = wave_id();
@@ -1390,7 +1428,8 @@ __device__ __forceinline__ int wa_row(int i, int nrows) {
 }
 
 // Wide gate/up tile: kWideBM rows x kWideBN1 columns of h.
-__device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
+__device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
+    const MK_C Params &P = uni_params(Pa);
     e = uni(e);
     row0 = uni(row0);
     nrows = uni(nrows);
@@ -1429,7 +1468,8 @@ __device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &P, int e
 }
 
 // Wide down-projection tile: kWideBM rows x kWideBN columns of y.
-__device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n) {
+__device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
+    const MK_C Params &P = uni_params(Pa);
     e = uni(e);
     row0 = uni(row0);
     nrows = uni(nrows);
@@ -1463,7 +1503,8 @@ __device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &P, int e
 // GEMM1 tile: h[rows, n0:n0+64] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
 // where row p of the tile is token perm[p] / k of x.  The tile variant is chosen from the
 // tile's actual row count.
-__device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
+__device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
+    const MK_C Params &P = uni_params(Pa);
     e = uni(e);
     row0 = uni(row0);
     nrows = uni(nrows);
@@ -1477,8 +1518,9 @@ __device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &P, int e
 }
 
 // GEMM2 tile: y[sp][rows, n0:n0+64] = h[rows, f range sp] W2[e][f range sp, n0:n0+64], fp32.
-__device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n,
+__device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n,
                                                      int sp, int mt) {
+    const MK_C Params &P = uni_params(Pa);
     e = uni(e);
     row0 = uni(row0);
     nrows = uni(nrows);
@@ -1542,7 +1584,8 @@ __device__ __forceinline__ void combine_tile(const MK_C Params &P, int c) {
     __syncthreads();
 }
 
-__device__ __attribute__((noinline)) void task_combine(const MK_C Params &P, int c) {
+__device__ __attribute__((noinline)) void task_combine(const MK_C Params &Pa, int c) {
+    const MK_C Params &P = uni_params(Pa);
     if (P.k <= 2)
         combine_tile<2>(P, c);
     else if (P.k <= 4)

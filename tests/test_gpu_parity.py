@@ -101,6 +101,16 @@ def test_k_and_e_edges(k, E):
     full_check(x, Wr, bias, W1, W3, W2, k, mk.MOE_MK_SCHED_STATIC, f"k={k} E={E}")
 
 
+@pytest.mark.parametrize("B,d,E", [(13, 512, 20), (70, 1024, 8), (600, 512, 12)],
+                         ids=["deep_stages", "deep_stages_two_tiles", "four_tokens_per_wave"])
+def test_router_stage_depths(B, d, E):
+    # d a multiple of 512 with at most 512 tokens: router stages of 512 values; more than
+    # 512 tokens: four tokens per wave; E not a multiple of 16 leaves a ragged expert block
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, 128, E, 2, seed=900 + B)
+    for sched in SCHEDS:
+        full_check(x, Wr, bias, W1, W3, W2, 2, sched, f"router B={B} d={d} E={E} {SNAME[sched]}")
+
+
 def test_zipf_bias_small():
     cfg, x, Wr, bias, W1, W3, W2 = small_case(100, 256, 128, 32, 4, seed=404, zipf_s=1.2)
     for sched in SCHEDS:
