@@ -38,9 +38,25 @@ constexpr int kRingBytes = 144 * 1024;  // LDS ring of the GroupGEMM and router 
 struct GemmSmem {
     uint16_t ring[kRingBytes / 2];
 };
+// Scratch of the single-tile routing tail, over the top-k staging area once top-k is done.
+struct FusedWork {
+    unsigned long long mask[kMaxE];  // tokens of the tile per expert
+    int off[kMaxE];                  // exp_indptr[e]
+    int mtb[kMaxE + 1];              // first row tile of each expert
+    int poff[kMaxE], pnm[kMaxE];     // queue offset and row tiles of each fired expert
+    int perm[kTileTokens * kMaxK];   // the batch's perm and inv, written out contiguously
+    int inv[kTileTokens * kMaxK];
+    int part[kWaves];
+    int base;
+};
 struct TopkSmem {
-    float lg[kTileTokens * kMaxE];  // a tile's logits, then the candidate lists
+    union {
+        float lg[kTileTokens * kMaxE];  // a tile's logits, then the candidate lists
+        FusedWork fw;
+    };
     int hist[kMaxE];
+    int tk[kTileTokens * kMaxK];        // the tile's selected experts, [token][slot]
+    float tw[kTileTokens * kMaxK];      // and their weights
 };
 constexpr int kScanStage = 16384;  // ints of tile_hist staged per round
 struct ScanSmem {
@@ -604,7 +620,6 @@ __device__ __attribute__((noinline)) void topk_tile(const MK_C Params &Pa, int t
         for (int i = 0; i < KB; ++i) key_insert<KB>(keys, other[i]);
     }
     if (q == 0 && tok < ntok) {
-        const int b = t * kTileTokens + tok;
         const float mx = key_float((uint32_t)(keys[0] >> 32));
         float ex[KB];
         float sum = 0.0f;
@@ -620,13 +635,20 @@ __device__ __attribute__((noinline)) void topk_tile(const MK_C Params &Pa, int t
         for (int i = 0; i < KB; ++i) {
             if (i < k) {
                 const int e = (int)(0xffffffffu - (uint32_t)keys[i]);
-                pub(P.topk_idx + (size_t)b * k + i, e);
-                pub(P.topk_w + (size_t)b * k + i, ex[i] / sum);
                 atomicAdd(&ts.hist[e], 1);
+                ts.tk[tok * k + i] = e;
+                ts.tw[tok * k + i] = ex[i] / sum;
             }
         }
     }
     __syncthreads();
+    // the tile's selections and weights leave as contiguous rows (whole lines, not 4-byte
+    // pieces 4k bytes apart), then its histogram
+    const size_t a0 = (size_t)t * kTileTokens * k;
+    for (int i = threadIdx.x; i < ntok * k; i += kThreads) {
+        pub(P.topk_idx + a0 + i, ts.tk[i]);
+        pub(P.topk_w + a0 + i, ts.tw[i]);
+    }
     for (int i = threadIdx.x; i < E; i += kThreads) pub(P.tile_hist + (size_t)t * E + i, ts.hist[i]);
 }
 
@@ -669,11 +691,11 @@ __device__ __forceinline__ int block_excl_scan(int v, int *part, int *total) {
 // hist[e] = sum_t tile_hist[t,e]; exp_indptr = exclusive prefix sum; tile_off[t,e] =
 // exp_indptr[e] + rows of e in tiles before t; row tiles of P.BM rows per expert; arms
 // ev_h[mt,s] with the gate/up tiles of each (row tile, f range), ev_y with the number of
-// down-projection tiles and (unless the grouping runs in this same task) ev_exp[e] with
-// hist[e] ("Core method": the prefix sum decides how many GroupGEMM tiles each expert
-// triggers).  Events are at rest (zero) and nothing decrements them before the scan is
-// published, so arming is a plain store.  Returns the number of row tiles.
-__device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, bool arm_experts) {
+// down-projection tiles and ev_exp[e] with hist[e] ("Core method": the prefix sum decides
+// how many GroupGEMM tiles each expert triggers).  Events are at rest (zero) and nothing
+// decrements them before the scan is published, so arming is a plain store.  Returns the
+// number of row tiles.
+__device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa) {
     const MK_C Params &P = uni_params(Pa);
     const int e = threadIdx.x;
     const int E = P.E, BM = P.BM;
@@ -716,7 +738,7 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, bool a
             pub(P.mt_rows + i, min(BM, h - m * BM));
             for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
         }
-        if (h && arm_experts) pub(P.ev_exp + e, h);
+        if (h) pub(P.ev_exp + e, h);
     }
     if (e == 0) {
         pub(P.indptr + E, total_h);
@@ -1634,9 +1656,8 @@ __device__ __forceinline__ void trace_task(const MK_C Params &P, int g, int kind
 // then each expert's event is decremented by the tile's rows of that expert; in dynamic
 // mode the gate/up tiles of every expert this brought to zero are pushed, with one
 // reservation of queue slots for all of them (a prefix sum over the experts places each
-// expert's tasks, in expert order).  With `whole` (the batch is this one tile, scanned by
-// the same task) every expert with rows is complete and no expert event is used.
-__device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs, int t, bool dyn, bool whole) {
+// expert's tasks, in expert order).
+__device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs, int t, bool dyn) {
     static_assert(kMaxE <= kThreads, "one thread per expert");
     task_group(P, t);
     count_task(P, K_GROUP);
@@ -1653,17 +1674,9 @@ __device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs
     const int e = threadIdx.x;
     const int cnt = e < P.E ? __popcll(gr.mask[e]) : 0;
     bool fire = false;
-    if (cnt) {
-        if (whole) {
-            if (e == skip) {
-                if (!dyn) pub(P.ev_exp + e, 1);  // a wait that never ends (debug)
-            } else {
-                fire = dyn;
-            }
-        } else if (e != skip) {
-            const int old = add_relaxed(P.ev_exp + e, -cnt);
-            fire = dyn && old == cnt;
-        }
+    if (cnt && e != skip) {
+        const int old = add_relaxed(P.ev_exp + e, -cnt);
+        fire = dyn && old == cnt;
     }
     if (!dyn) return;
     // push the gate/up tiles of every expert this tile completed
@@ -1705,6 +1718,132 @@ __device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs
     }
 }
 
+// The scan and the grouping of a batch that is one routing tile, run by its top-k task
+// right after top-k, from what top-k left in LDS (the tile histogram is the histogram, the
+// tile's row offsets are exp_indptr): everything is published and nothing is read back.
+// In dynamic mode the task count is published and the gate/up tiles of every expert with
+// rows are pushed with one reservation of queue slots, made right after the scan so that
+// the atomic's round trip overlaps the grouping.  t3 receives the end time of the scan.
+__device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs, bool dyn, unsigned long long &t3) {
+    static_assert(kMaxE <= kThreads, "one thread per expert");
+    TopkSmem &ts = g_sm.u.t;
+    FusedWork &W = ts.fw;
+    const int e = threadIdx.x;
+    const int E = P.E, k = P.k, BM = P.BM;
+    int skip = -1;
+    if (P.debug & 1) {  // debug: drop the notification of the first expert with rows
+        for (int x = 0; x < E; ++x)
+            if (ts.hist[x]) {
+                skip = x;
+                break;
+            }
+    }
+    // scan ("Core method": the prefix sum decides how many GroupGEMM tiles each expert triggers)
+    const int h = e < E ? ts.hist[e] : 0;
+    const int mt = (h + BM - 1) / BM;
+    int total_h, total_mt;
+    const int off = block_excl_scan(h, W.part, &total_h);
+    const int mbase = block_excl_scan(mt, W.part, &total_mt);
+    if (e < E) {
+        W.off[e] = off;
+        W.mtb[e] = mbase;
+        W.mask[e] = 0ull;
+        pub(P.hist + e, h);
+        pub(P.indptr + e, off);
+        pub(P.tile_off + e, off);
+        pub(P.mt_base + e, mbase);
+        for (int m = 0; m < mt; ++m) {
+            const int i = mbase + m;
+            pub(P.mt_expert + i, e);
+            pub(P.mt_row0 + i, off + m * BM);
+            pub(P.mt_rows + i, min(BM, h - m * BM));
+            for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+        }
+    }
+    if (e == 0) {
+        W.mtb[E] = total_mt;
+        pub(P.indptr + E, total_h);
+        pub(P.mt_base + E, total_mt);
+        st_relaxed(P.ctl + CTL_MT_TOTAL, total_mt);
+        pub(P.ctl + CTL_EV_Y, total_mt * P.S * P.NB2);
+    }
+    count_task(P, K_SCAN);
+    complete_bases(P, bs, total_mt);
+    if (dyn && threadIdx.x == 0) {
+        // tickets: routers, this task, and the GroupGEMM and combine tasks
+        const int real = bs.K + 1 + P.S * (bs.q1 + bs.q2) + P.nC;
+        const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
+        st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64), tag | (uint32_t)real);
+    }
+    // reserve the queue slots of the pushes (the reply is first needed after the grouping)
+    const int Q = P.NB1 / P.S;  // gate/up tasks per row tile and split
+    int tot = 0, qbase = 0;
+    if (dyn) {
+        const int nm = e < E && h > 0 && e != skip ? mt : 0;
+        const int poff = block_excl_scan(nm * Q * P.S, W.part, &tot);
+        if (e < E) {
+            W.poff[e] = poff;
+            W.pnm[e] = nm;
+        }
+        if (threadIdx.x == 0 && tot) qbase = add_relaxed(P.ctl + CTL_QTAIL, tot);
+    }
+    t3 = now_ticks();
+    __syncthreads();
+    // grouping: rank of each (token, slot) among the expert's rows, tokens in order
+    const int lane = lane_id(), w = wave_id();
+    const int ntok = P.B;
+    static_assert(kMaxK <= 2 * kWaves, "two slots per lane");
+    int ev[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int i = w + j * kWaves;
+        ev[j] = i < k && lane < ntok ? ts.tk[lane * k + i] : -1;
+        if (ev[j] >= 0) atomicOr(&W.mask[ev[j]], 1ull << lane);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (ev[j] >= 0) {
+            const int a = lane * k + w + j * kWaves;
+            const int p = W.off[ev[j]] + __popcll(W.mask[ev[j]] & ((1ull << lane) - 1ull));
+            W.perm[p] = a;
+            W.inv[a] = p;
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < ntok * k; i += kThreads) {
+        pub(P.perm + i, W.perm[i]);
+        pub(P.inv + i, W.inv[i]);
+    }
+    count_task(P, K_GROUP);
+    if (!dyn) {
+        if (skip >= 0 && threadIdx.x == 0) pub(P.ev_exp + skip, 1);  // a wait that never ends (debug)
+        return;  // the caller's notification publishes everything
+    }
+    wg_stores_done();  // every table and perm/inv is out before any GroupGEMM task can start
+    if (!tot) return;
+    // push the gate/up tiles of every expert with rows (all but a debug-skipped one)
+    if (threadIdx.x == 0) W.base = qbase;
+    __syncthreads();
+    const int base = W.base;
+    if (base + tot > P.q_cap) {
+        if (threadIdx.x == 0) set_error(P.ctl, 4 /* MOE_MK_ERR_QUEUE */);
+        return;
+    }
+    // wave w writes the slots of experts w, w + kWaves, ..., 64 slots per store
+    const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
+    for (int x = w; x < E; x += kWaves) {
+        const int n = W.pnm[x] * Q;
+        if (!n) continue;
+        int slot = base + W.poff[x];
+        for (int sp = 0; sp < P.S; ++sp) {
+            const int g0 = base_g1(bs, sp) + W.mtb[x] * Q;
+            for (int i = lane; i < n; i += 64) st_relaxed64(P.qslots + slot + i, tag | (uint32_t)(g0 + i));
+            slot += n;
+        }
+    }
+}
+
 // Runs task g (obtained at time t0).  Returns false when the forward must be abandoned.
 __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs, unsigned long long t0) {
     const bool dyn = P.sched != 0;
@@ -1732,26 +1871,13 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         count_task(P, K_TOPK);
         if (P.T == 1) {
             // The only routing tile: its histogram is the whole histogram, so the scan and
-            // the grouping run here, without the two joins between separate tasks.  Each
-            // step reads back what the previous one published from this workgroup.
-            wg_stores_done();
-            wg_acquire();
-            const int mt_total = task_scan(P, false);
-            count_task(P, K_SCAN);
-            complete_bases(P, bs, mt_total);
-            const unsigned long long t3 = now_ticks();
-            wg_stores_done();
-            wg_acquire();
-            if (dyn && threadIdx.x == 0) {
-                // tickets: routers, this task, and the GroupGEMM and combine tasks
-                const int real = bs.K + 1 + P.S * (bs.q1 + bs.q2) + P.nC;
-                const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
-                st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64), tag | (uint32_t)real);
-            }
-            group_and_notify(P, bs, 0, dyn, true);
+            // the grouping run here, without the two joins between separate tasks.
+            unsigned long long t3;
+            fused_scan_group(P, bs, dyn, t3);
             const unsigned long long t4 = now_ticks();
             // static GroupGEMM tasks start once this is seen: the tables and perm/inv are out
-            wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
+            // (dynamic ones are pushed, and no task waits on the event)
+            if (!dyn) wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
             trace_task(P, g, K_TOPK, t0, t1, t2, t3, t4);
             return true;
         }
@@ -1768,7 +1894,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
             if (!wg_wait_zero(P, P.ctl + CTL_EV_TOPK)) return false;
         }
         const unsigned long long t1 = now_ticks();
-        const int mt_total = task_scan(P, true);
+        const int mt_total = task_scan(P);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_SCAN);
         complete_bases(P, bs, mt_total);
@@ -1791,7 +1917,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         if (P.T == 1) return true;  // a single routing tile is grouped by its top-k task
         if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) return false;
         const unsigned long long t1 = now_ticks();
-        group_and_notify(P, bs, t, dyn, false);
+        group_and_notify(P, bs, t, dyn);
         trace_task(P, g, K_GROUP, t0, t1, now_ticks());
         return true;
     }
@@ -1902,6 +2028,18 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
     // there in place rather than from a private copy.
     (void)Parg;
     const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
+    {
+        // Touch every 64-byte line of the parameter block once, all at the start: the first
+        // read of a line from a compute unit misses the scalar cache and waits on the
+        // kernel-argument memory, which would otherwise happen inside the first task of each
+        // kind that reads a new field.
+        static_assert(sizeof(Params) % 4 == 0, "whole words");
+        const MK_C uint32_t *pw = (const MK_C uint32_t *)&P;
+        uint32_t acc = 0;
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(Params) / 4); i += 16) acc ^= pw[i];
+        asm volatile("" ::"s"(acc));
+    }
     if (threadIdx.x == 0) {
         g_sm.epoch = ld_relaxed(P.ctl + CTL_EPOCH);
         g_sm.bcast[0] = ld_relaxed(P.ctl + CTL_MAGIC) == kMagic;
