@@ -61,6 +61,8 @@ struct TopkSmem {
 constexpr int kScanStage = 16384;  // ints of tile_hist staged per round
 struct ScanSmem {
     int part[8];
+    int ps[kThreads];      // partial sums, [thread group r][expert]
+    int carry[kMaxE];      // rows of each expert in the tiles of earlier rounds (row offsets)
     int tiles[kScanStage];
 };
 struct GroupSmem {
@@ -345,7 +347,8 @@ __device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[T
 // RPS x 16 block of Wr (each wave moving RPS/8 of its rows, 1 KB per load) and the tokens'
 // RPS x values (each wave moving its own), in a ring of as many stages as LDS holds (up to
 // 16), filled by global_load_lds.  Deeper stages (RPS = 512 with one token per wave) move
-// more bytes per ring iteration, which sets a workgroup's streaming rate.  Lane l
+// more bytes per ring iteration, which sets a workgroup's streaming rate; with four tokens
+// per wave the stages hold 256 values when d allows.  Lane l
 // accumulates chain l (j = l, l+64, ... in order) of every (token, expert) pair of its
 // wave; a stage holds RPS/64 consecutive steps of every chain.
 //   Wr stage in LDS: [RPS rows][4 chunks of 4 experts]; chunk c of row r at c ^ rswz(r),
@@ -512,7 +515,10 @@ __device__ __attribute__((noinline)) void task_route(const MK_C Params &Pa, int 
         else
             route_tile<1, 128>(P, tg * kWaves, e0);
     } else {
-        route_tile<4, 128>(P, tg * kWaves * 4, e0);
+        if (P.d % 256 == 0)
+            route_tile<4, 256>(P, tg * kWaves * 4, e0);
+        else
+            route_tile<4, 128>(P, tg * kWaves * 4, e0);
     }
 }
 
@@ -524,18 +530,58 @@ __device__ __attribute__((noinline)) void task_route(const MK_C Params &Pa, int 
 // The tile's logits are staged in LDS.  Eight lanes share a token (8 tokens per wave):
 // lane part q keeps a sorted list of the best keys among experts [q*per, (q+1)*per),
 // visited from a per-token starting offset so the lanes of a wave read distinct LDS
-// banks; three butterfly rounds over lane pairs (xor 1, 2, then 4) merge the eight lists.
+// banks, eight at a time (sorted, then merged into the list); three butterfly rounds over
+// lane pairs (xor 1, 2, then 4) merge the eight lists.
 
-template <int KB>
-__device__ __forceinline__ void key_insert(unsigned long long (&keys)[KB], unsigned long long v) {
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-        const bool c = keys[i] > v;
-        const unsigned long long hi = c ? keys[i] : v;
-        v = c ? v : keys[i];
-        keys[i] = hi;
-    }
+// Sorted lists are combined with bitonic networks (compare-exchanges of one level are
+// independent, so a lane's work is a few short dependency chains rather than one long one).
+// A list of KB keys is held in P = max(8, next power of two >= KB) slots, padded with key 0.
+__device__ __forceinline__ void key_cx(unsigned long long &a, unsigned long long &b) {  // a = max, b = min
+    const bool c = a < b;
+    const unsigned long long hi = c ? b : a;
+    b = c ? a : b;
+    a = hi;
 }
+// Sort N keys into descending order.
+template <int N>
+__device__ __forceinline__ void keys_sort(unsigned long long (&v)[N]) {
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    if ((i & k) == 0)
+                        key_cx(v[i], v[l]);
+                    else
+                        key_cx(v[l], v[i]);
+                }
+            }
+}
+// keys (KB, descending) := the KB largest of keys and other (P slots, descending): the
+// elementwise max of one list and the other reversed is bitonic and holds the P largest;
+// a bitonic merge sorts it.
+template <int KB, int P>
+__device__ __forceinline__ void keys_merge(unsigned long long (&keys)[KB], const unsigned long long (&other)[P]) {
+    static_assert(P >= KB && (P & (P - 1)) == 0, "power-of-two slots");
+    unsigned long long c[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const unsigned long long a = i < KB ? keys[i] : 0ull, b = other[P - 1 - i];
+        c[i] = a > b ? a : b;
+    }
+#pragma unroll
+    for (int j = P >> 1; j > 0; j >>= 1)
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+            if ((i ^ j) > i) key_cx(c[i], c[i ^ j]);
+#pragma unroll
+    for (int i = 0; i < KB; ++i) keys[i] = c[i];
+}
+template <int KB>
+constexpr int key_slots() { return KB <= 8 ? 8 : 16; }
 
 // Exchange with lane ^ M: M = 1, 2 by DPP quad permutes, M = 4 by a swizzle in bit mode
 // (and-mask 31, xor-mask 4); neither makes an LDS memory round trip.
@@ -595,29 +641,36 @@ __device__ __attribute__((noinline)) void topk_tile(const MK_C Params &Pa, int t
             ev[u] = i0 + u < per && idx < n_e ? idx : -1;
             lv[u] = row[ev[u] >= 0 ? idx : 0];
         }
+        constexpr int PS = key_slots<KB>();
+        unsigned long long nk[PS];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float l = lv[u] + 0.0f;  // folds -0 onto +0
-            const unsigned long long key =
-                ((unsigned long long)float_key(l) << 32) | (0xffffffffu - (uint32_t)(e_lo + ev[u]));
-            key_insert<KB>(keys, ev[u] >= 0 ? key : 0ull);
+        for (int u = 0; u < PS; ++u) {
+            nk[u] = 0ull;
+            if (u < 8) {
+                const float l = lv[u] + 0.0f;  // folds -0 onto +0
+                const unsigned long long key =
+                    ((unsigned long long)float_key(l) << 32) | (0xffffffffu - (uint32_t)(e_lo + ev[u]));
+                nk[u] = ev[u] >= 0 ? key : 0ull;
+            }
         }
+        keys_sort<PS>(nk);
+        keys_merge<KB, PS>(keys, nk);
     }
     // merge with lane ^ 1, lane ^ 2, then lane ^ 4 (every lane takes part in the exchanges)
     {
-        unsigned long long other[KB];
+        constexpr int PS = key_slots<KB>();
+        unsigned long long other[PS];
+#pragma unroll
+        for (int i = 0; i < PS; ++i) other[i] = 0ull;
 #pragma unroll
         for (int i = 0; i < KB; ++i) other[i] = lane_xor_u64<1>(keys[i]);
-#pragma unroll
-        for (int i = 0; i < KB; ++i) key_insert<KB>(keys, other[i]);
+        keys_merge<KB, PS>(keys, other);
 #pragma unroll
         for (int i = 0; i < KB; ++i) other[i] = lane_xor_u64<2>(keys[i]);
-#pragma unroll
-        for (int i = 0; i < KB; ++i) key_insert<KB>(keys, other[i]);
+        keys_merge<KB, PS>(keys, other);
 #pragma unroll
         for (int i = 0; i < KB; ++i) other[i] = lane_xor_u64<4>(keys[i]);
-#pragma unroll
-        for (int i = 0; i < KB; ++i) key_insert<KB>(keys, other[i]);
+        keys_merge<KB, PS>(keys, other);
     }
     if (q == 0 && tok < ntok) {
         const float mx = key_float((uint32_t)(keys[0] >> 32));
@@ -697,10 +750,23 @@ __device__ __forceinline__ int block_excl_scan(int v, int *part, int *total) {
 // number of row tiles.
 __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa) {
     const MK_C Params &P = uni_params(Pa);
+    ScanSmem &ss = g_sm.u.s;
     const int e = threadIdx.x;
     const int E = P.E, BM = P.BM;
-    int *tb = g_sm.u.s.tiles;
+    int *tb = ss.tiles;
     const int rows = kScanStage / E;  // tile_hist rows staged per round (coalesced loads)
+    // R threads per expert: thread (ex, r) = (tid % E, tid / E) takes the r-th contiguous
+    // chunk of each round's tiles, so the per-expert sums and the row offsets run R-wide
+    const int R = kThreads / E;
+    const int ex = threadIdx.x % E, r = threadIdx.x / E;
+    const bool act = r < R;
+    auto chunk_sum = [&](int nr) {
+        const int c = (nr + R - 1) / R;
+        int v = 0;
+        if (act)
+            for (int t = r * c; t < min(nr, (r + 1) * c); ++t) v += tb[t * E + ex];
+        return v;
+    };
     // stage rows [t0, t0 + nr) of tile_hist, eight loads of each thread in flight at once
     auto stage = [&](int t0, int nr) {
         const MK_G int *src = P.tile_hist + (size_t)t0 * E;
@@ -716,18 +782,23 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa) {
         }
         __syncthreads();
     };
-    int h = 0;
+    int hp = 0;
     for (int t0 = 0; t0 < P.T; t0 += rows) {
         const int nr = min(rows, P.T - t0);
         stage(t0, nr);
-        if (e < E)
-            for (int t = 0; t < nr; ++t) h += tb[t * E + e];
+        hp += chunk_sum(nr);
     }
+    ss.ps[threadIdx.x] = hp;
+    __syncthreads();
+    int h = 0;
+    if (e < E)
+        for (int q = 0; q < R; ++q) h += ss.ps[q * E + e];
     const int mt = (h + BM - 1) / BM;
     int total_h, total_mt;
-    const int off = block_excl_scan(h, g_sm.u.s.part, &total_h);
-    const int mbase = block_excl_scan(mt, g_sm.u.s.part, &total_mt);
+    const int off = block_excl_scan(h, ss.part, &total_h);
+    const int mbase = block_excl_scan(mt, ss.part, &total_mt);
     if (e < E) {
+        ss.carry[e] = off;
         pub(P.hist + e, h);
         pub(P.indptr + e, off);
         pub(P.mt_base + e, mbase);
@@ -746,16 +817,27 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa) {
         st_relaxed(P.ctl + CTL_MT_TOTAL, total_mt);
         pub(P.ctl + CTL_EV_Y, total_mt * P.S * P.NB2);
     }
-    // per-tile row offsets: exp_indptr[e] + rows of e in earlier tiles
-    int run = off;
+    // per-tile row offsets: exp_indptr[e] + rows of e in earlier tiles; a thread's chunk
+    // starts after the chunks of lower r and the tiles of earlier rounds
     for (int t0 = 0; t0 < P.T; t0 += rows) {
         const int nr = min(rows, P.T - t0);
         if (t0 > 0 || P.T > rows) stage(t0, nr);  // the first round's rows are still staged unless T needed several
-        if (e < E)
-            for (int t = 0; t < nr; ++t) {
-                pub(P.tile_off + (size_t)(t0 + t) * E + e, run);
-                run += tb[t * E + e];
+        else __syncthreads();                      // ps and carry written above
+        const int cs = chunk_sum(nr);
+        ss.ps[threadIdx.x] = cs;
+        __syncthreads();
+        if (act) {
+            int run = ss.carry[ex];
+            for (int q = 0; q < r; ++q) run += ss.ps[q * E + ex];
+            const int c = (nr + R - 1) / R;
+            for (int t = r * c; t < min(nr, (r + 1) * c); ++t) {
+                pub(P.tile_off + (size_t)(t0 + t) * E + ex, run);
+                run += tb[t * E + ex];
             }
+        }
+        __syncthreads();
+        if (e < E)
+            for (int q = 0; q < R; ++q) ss.carry[e] += ss.ps[q * E + e];
     }
     return total_mt;
 }
