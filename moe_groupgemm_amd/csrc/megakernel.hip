@@ -86,6 +86,7 @@ struct Smem {
     } u;
     int bcast[4];
     int epoch;
+    int total;  // the forward's task count once read (dynamic mode), else -1
 };
 
 // The workgroup's LDS, shared by every task kind (file scope, so out-of-line task bodies
@@ -1182,11 +1183,14 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rb + 4 * g + r;
             const size_t o = (size_t)(row0 + min(row, nrows - 1)) * P.d + col;
-            float sum = 0.0f;
-            for (int q = 0; q < P.S; ++q) {
-                const float v = q == sp ? acc0[rb][r] : P.yp[(size_t)q * split_stride + o];
-                sum = q == 0 ? v : sum + v;
-            }
+            float v[kMaxSplits];  // every partial loaded at once, then added in split order
+#pragma unroll
+            for (int q = 0; q < kMaxSplits; ++q)
+                v[q] = q < P.S && q != sp ? P.yp[(size_t)q * split_stride + o] : acc0[rb][r];
+            float sum = v[0];
+#pragma unroll
+            for (int q = 1; q < kMaxSplits; ++q)
+                if (q < P.S) sum += v[q];
             store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, col, sum, row < nrows);
         }
     }
@@ -2060,6 +2064,8 @@ __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
         const int t = add_relaxed(P.ctl + CTL_QHEAD, 1);
         if (t < P.nR) {
             g = t;
+        } else if (g_sm.total >= 0 && t >= g_sm.total) {
+            g = -1;  // beyond the forward's tasks: nothing will fill this slot
         } else {
             const int i = t - P.nR;
             const unsigned long long t0 = now_ticks();
@@ -2071,12 +2077,15 @@ __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
                         break;
                     }
                 }
-                if ((it & 7u) == 7u) {  // the task count is one word every waiter reads: look rarely
+                if (g_sm.total < 0 && (it & 3u) == 0u) {  // the task count, until it is known
                     const unsigned long long tot =
                         ld_relaxed64((const MK_G unsigned long long *)(P.ctl + CTL_TOTAL64));
-                    if ((uint32_t)(tot >> 32) == ep && t >= (int)(uint32_t)tot) {
-                        g = -1;
-                        break;
+                    if ((uint32_t)(tot >> 32) == ep) {
+                        g_sm.total = (int)(uint32_t)tot;
+                        if (t >= g_sm.total) {
+                            g = -1;
+                            break;
+                        }
                     }
                 }
                 if ((it & 31u) == 31u) {
@@ -2124,6 +2133,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
     }
     if (threadIdx.x == 0) {
         g_sm.epoch = ld_relaxed(P.ctl + CTL_EPOCH);
+        g_sm.total = -1;
         g_sm.bcast[0] = ld_relaxed(P.ctl + CTL_MAGIC) == kMagic;
     }
     __syncthreads();

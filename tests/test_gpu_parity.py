@@ -118,7 +118,7 @@ def test_zipf_bias_small():
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
-@pytest.mark.parametrize("f,S", [(4096, 2), (8192, 4)])
+@pytest.mark.parametrize("f,S", [(4096, 2), (8192, 4), (12288, 4)])
 def test_down_projection_k_splits(f, S, sched):
     # small batches with a long f split the down projection's reduction into S ranges
     B, d, E, k = 21, 128, 4, 2
@@ -161,7 +161,7 @@ def test_wide_tiles_static_dynamic_identical():
 
 
 def test_down_projection_splits_static_dynamic_identical():
-    cfg, x, Wr, bias, W1, W3, W2 = small_case(13, 128, 8192, 4, 2, seed=901)
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(13, 128, 12288, 4, 2, seed=901)
     outs = []
     for sched in SCHEDS:
         layer, out, got = run_small(x, Wr, bias, W1, W3, W2, 2, sched)
