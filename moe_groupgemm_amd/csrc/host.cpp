@@ -165,6 +165,7 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.nEB = (int)c.nEB;
     P.T = (int)c.T;
     P.nC = (int)c.nC;
+    P.CT = mk::combine_tokens(B, s.k);
     const mk::Tiles tl = mk::tile_config(s, B);
     P.NB1 = tl.NB1;
     P.NB2 = tl.NB2;

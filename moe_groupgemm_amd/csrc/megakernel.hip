@@ -1645,14 +1645,14 @@ __device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &Pa, int 
 
 // ------------------------------------------------------------------------------ COMBINE
 // out[b, :] = bf16( sum_{i<k} w[b,i] * y[inv[b*k+i], :] ), slot order, fp32, for
-// a combine task: kCombineTokens tokens x kCombineCols columns (4 columns per thread).
-template <int KB>
+// a combine task: CT tokens x kCombineCols columns (4 columns per thread).
+template <int KB, int CT>
 __device__ __forceinline__ void combine_tile(const MK_C Params &P, int c) {
     CombineSmem &cs = g_sm.u.c;
     const int nchunks = (P.d + kCombineCols - 1) / kCombineCols;
     const int grp = c / nchunks, chunk = c - grp * nchunks;
-    const int b_lo = grp * kCombineTokens;
-    const int nb = min(kCombineTokens, P.B - b_lo);
+    const int b_lo = grp * CT;
+    const int nb = min(CT, P.B - b_lo);
     const int k = P.k;
     for (int i = threadIdx.x; i < nb * k; i += kThreads) {
         cs.row[i] = P.inv[(size_t)b_lo * k + i];
@@ -1662,15 +1662,15 @@ __device__ __forceinline__ void combine_tile(const MK_C Params &P, int c) {
     const int q = (chunk * kCombineCols) / 4 + threadIdx.x;  // this thread's 4-column group
     if (4 * q < P.d) {
         // the rows of every token of the task in flight before any is used
-        u32x2 yv[kCombineTokens][KB];
+        u32x2 yv[CT][KB];
 #pragma unroll
-        for (int bb = 0; bb < kCombineTokens; ++bb)
+        for (int bb = 0; bb < CT; ++bb)
 #pragma unroll
             for (int i = 0; i < KB; ++i)
                 if (bb < nb && i < k) yv[bb][i] = *(const MK_G u32x2 *)(P.y + (size_t)cs.row[bb * k + i] * P.d + 4 * q);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int bb = 0; bb < kCombineTokens; ++bb) {
+        for (int bb = 0; bb < CT; ++bb) {
             if (bb >= nb) break;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1694,14 +1694,22 @@ __device__ __forceinline__ void combine_tile(const MK_C Params &P, int c) {
 
 __device__ __attribute__((noinline)) void task_combine(const MK_C Params &Pa, int c) {
     const MK_C Params &P = uni_params(Pa);
-    if (P.k <= 2)
-        combine_tile<2>(P, c);
-    else if (P.k <= 4)
-        combine_tile<4>(P, c);
-    else if (P.k <= 8)
-        combine_tile<8>(P, c);
-    else
-        combine_tile<16>(P, c);
+    if (P.CT == 8) {  // k <= 8
+        if (P.k <= 2)
+            combine_tile<2, 8>(P, c);
+        else if (P.k <= 4)
+            combine_tile<4, 8>(P, c);
+        else
+            combine_tile<8, 8>(P, c);
+    } else if (P.k <= 2) {
+        combine_tile<2, 4>(P, c);
+    } else if (P.k <= 4) {
+        combine_tile<4, 4>(P, c);
+    } else if (P.k <= 8) {
+        combine_tile<8, 4>(P, c);
+    } else {
+        combine_tile<16, 4>(P, c);
+    }
 }
 
 // ------------------------------------------------------------------------------ task dispatch

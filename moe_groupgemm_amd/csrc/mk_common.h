@@ -22,7 +22,7 @@ constexpr int kWaves = 8;            // waves per persistent workgroup (one work
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileTokens = 64;      // tokens per top-k / grouping tile (one lane per token)
 constexpr int kRouteExperts = 16;    // experts per router task
-constexpr int kCombineTokens = 4;    // tokens per combine task
+constexpr int kCombineTokens = 8;    // most tokens per combine task (see combine_tokens)
 constexpr int kCombineCols = 4 * kThreads;  // model columns per combine task (4 per thread)
 constexpr int kBM = 64;              // GroupGEMM rows per narrow tile (one expert's rows)
 constexpr int kBN = 16 * kWaves;     // GroupGEMM columns per narrow tile (16 per wave)
@@ -58,6 +58,10 @@ struct Shape {
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tokens per combine task: eight at large batches with k <= 8 (twice the rows in flight per
+// task, and half the tasks each paying a round trip for its indices), else four.
+inline int combine_tokens(int64_t B, int k) { return B >= 1024 && k <= 8 ? 8 : 4; }
 
 // Router tokens per wave: one at small batches (more, shorter tasks), four at large ones
 // (each expert-weight row loaded serves four tokens).  A router task covers kWaves waves.
@@ -123,7 +127,7 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     c.nTG = ceil_div(B, kWaves * c.tpw);
     c.nEB = ceil_div(s.E, kRouteExperts);
     c.nR = c.nTG * c.nEB;
-    c.nC = ceil_div(B, kCombineTokens) * ceil_div(s.d, kCombineCols);
+    c.nC = ceil_div(B, combine_tokens(B, s.k)) * ceil_div(s.d, kCombineCols);
     int64_t a = B * s.k;
     c.mt_cap = a / kBM + (a < s.E ? a : s.E) + 1;
     c.NB1 = s.f / kBN;
@@ -193,6 +197,7 @@ struct Params {
     int sched;       // 0 static, 1 dynamic
     int debug;       // MOE_MK_DEBUG_* bits
     int nR, nTG, nEB, T, nC, NB1, NB2, tpw, S;
+    int CT;          // tokens per combine task
     int BM;          // GroupGEMM tile rows (kBM or kWideBM); columns are f / NB1 = d / NB2
     int q_cap, mt_cap;
     long long watchdog;  // real-time ticks (100 MHz)
