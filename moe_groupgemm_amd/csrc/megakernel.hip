@@ -1535,6 +1535,35 @@ __device__ __forceinline__ int wa_row(int i, int nrows) {
     return min(16 * (2 * wave_id() + i) + (lane_id() >> 2), nrows - 1);
 }
 
+// Output of a wide tile through LDS.  The MFMA layout gives a lane one column of four rows,
+// so stored directly every store instruction writes 32-byte pieces of lines, and with the
+// write-through stores that publish results across XCDs those partial lines dominated a
+// tile's time.  Instead every wave puts its bf16 results into a [kWideBM][BN] tile in the
+// (then idle) LDS ring, 16-byte chunks of a row XOR-swizzled by row % 8 so that the 16 rows
+// one write instruction touches spread over the banks, and the workgroup then stores
+// whole rows, 8 bytes per lane.
+template <int BN>
+__device__ __forceinline__ uint32_t wout_off(int row, int byte) {  // byte offset in the LDS tile
+    return (uint32_t)(row * (2 * BN) + ((((byte >> 4) ^ (row & 7)) << 4) | (byte & 15)));
+}
+template <int BN>
+__device__ __forceinline__ void wout_put(uint8_t *tile, int row, int col, uint32_t bf) {
+    *(uint16_t *)(tile + wout_off<BN>(row, 2 * col)) = (uint16_t)bf;
+}
+// Rows [0, nrows) of the LDS tile to dst (row r at dst + r * ld elements); all threads
+// call it after the tile is complete, and the ring is free again when it returns.
+template <int BN>
+__device__ __forceinline__ void wout_store(const uint8_t *tile, MK_G uint16_t *dst, size_t ld, int nrows) {
+    constexpr int LPR = BN / 4;          // lanes per row, 8 bytes each
+    constexpr int RPI = kThreads / LPR;  // rows per pass of the workgroup
+    const int q = threadIdx.x % LPR, r = threadIdx.x / LPR;
+    for (int row = r; row < nrows; row += RPI) {
+        const unsigned long long v = *(const unsigned long long *)(tile + wout_off<BN>(row, 8 * q));
+        st_relaxed64((MK_G unsigned long long *)(dst + (size_t)row * ld + 4 * q), v);
+    }
+    __syncthreads();
+}
+
 // Wide gate/up tile: kWideBM rows x kWideBN1 columns of h.
 __device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
     const MK_C Params &P = uni_params(Pa);
@@ -1558,21 +1587,20 @@ __device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &Pa, int 
     wide_tile<true, BN>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
-    const int r0 = kWR * (w >> 2), c0 = n * BN + (BN / 4) * (w & 3);
+    const int r0 = kWR * (w >> 2), c0 = (BN / 4) * (w & 3);  // tile-relative
+    uint8_t *tile = (uint8_t *)g_sm.u.g.ring;
 #pragma unroll
     for (int rb = 0; rb < kWRB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = r0 + 16 * rb + 4 * g + r;
-                const int col = c0 + 16 * cb + j;
                 const float gv = acc0[C::CB * rb + cb][r], uv = acc1[C::CB * rb + cb][r];
                 const uint32_t hv = f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
-                const uint32_t nb = (uint32_t)__shfl_xor((int)hv, 1, 64);
-                if (row < nrows && (j & 1) == 0)
-                    pub((MK_G uint32_t *)(P.h + (size_t)(row0 + row) * P.f + col), hv | (nb << 16));
+                wout_put<BN>(tile, r0 + 16 * rb + 4 * g + r, c0 + 16 * cb + j, hv);
             }
+    __syncthreads();
+    wout_store<BN>(tile, P.h + (size_t)row0 * P.f + (size_t)n * BN, (size_t)P.f, nrows);
 }
 
 // Wide down-projection tile: kWideBM rows x kWideBN columns of y.
@@ -1596,16 +1624,17 @@ __device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &Pa, int 
     wide_tile<false, BN>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
-    const int r0 = kWR * (w >> 2), c0 = n * BN + (BN / 4) * (w & 3);
+    const int r0 = kWR * (w >> 2), c0 = (BN / 4) * (w & 3);  // tile-relative
+    uint8_t *tile = (uint8_t *)g_sm.u.g.ring;
 #pragma unroll
     for (int rb = 0; rb < kWRB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = r0 + 16 * rb + 4 * g + r;
-                store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, c0 + 16 * cb + j, acc0[C::CB * rb + cb][r], row < nrows);
-            }
+            for (int r = 0; r < 4; ++r)
+                wout_put<BN>(tile, r0 + 16 * rb + 4 * g + r, c0 + 16 * cb + j, f32_to_bf16(acc0[C::CB * rb + cb][r]));
+    __syncthreads();
+    wout_store<BN>(tile, P.y + (size_t)row0 * P.d + (size_t)n * BN, (size_t)P.d, nrows);
 }
 
 // GEMM1 tile: h[rows, n0:n0+64] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
@@ -2133,6 +2162,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
         // kernel-argument memory, which would otherwise happen inside the first task of each
         // kind that reads a new field.
         static_assert(sizeof(Params) % 4 == 0, "whole words");
+        static_assert(kWideBM * 2 * kWideBN <= kRingBytes && kWideBM * 2 * kWideBN1 <= kRingBytes, "wide output tiles fit the ring");
         const MK_C uint32_t *pw = (const MK_C uint32_t *)&P;
         uint32_t acc = 0;
 #pragma unroll
