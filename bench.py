@@ -29,6 +29,7 @@ def parse():
     ap.add_argument("--batch", type=int, default=0, help="batch size (default: the configuration's first)")
     ap.add_argument("--sched", default="dynamic", choices=["static", "dynamic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefetch", action="store_true", help="turn off the weight prefetch during routing")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens of the oracle sample (default: auto)")
     ap.add_argument("--trace", action="store_true", help="after timing, run one traced forward and print "
                     "per-task-kind timings to stderr")
@@ -112,10 +113,11 @@ def trace_report(layer, x, out, B):
 
     import moe_groupgemm_amd as mk
 
-    mk.moe_mk_plan_set_debug(layer.plan, 0, mk.MOE_MK_DEBUG_TRACE)
+    flags0 = layer.debug_flags if hasattr(layer, "debug_flags") else 0
+    mk.moe_mk_plan_set_debug(layer.plan, 0, flags0 | mk.MOE_MK_DEBUG_TRACE)
     layer(x, out)
     torch.cuda.synchronize()
-    mk.moe_mk_plan_set_debug(layer.plan, 0, 0)
+    mk.moe_mk_plan_set_debug(layer.plan, 0, flags0)
     ctl = layer.routing(B)["ctl"].cpu().numpy()
     tr = mk.moe_mk_trace_view(layer.plan, B, layer.ws).cpu().numpy()
     E, k, d, f = layer.E, layer.k, layer.d, layer.f
@@ -205,6 +207,9 @@ def main():
     layer = mk.MoELayer(cfg.E, cfg.k, cfg.d, cfg.f, tWr, t1, t3, t2, router_bias=tb, sched=sched,
                         max_batch=B, device=dev)
     out = torch.empty((B, cfg.d), dtype=torch.bfloat16, device=dev)
+    base_flags = mk.MOE_MK_DEBUG_NO_PREFETCH if args.no_prefetch else 0
+    mk.moe_mk_plan_set_debug(layer.plan, 0, base_flags)
+    layer.debug_flags = base_flags
     stream = torch.cuda.current_stream(dev)
     print(f"# warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -164,6 +164,7 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
  */
 #define MOE_MK_DEBUG_DROP_NOTIFY 1
 #define MOE_MK_DEBUG_TRACE 2  /* record per-task timestamps, see moe_mk_trace_view */
+#define MOE_MK_DEBUG_NO_PREFETCH 4  /* static schedule: no weight prefetch while a small batch is routed (A/B timing) */
 moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks, int32_t flags);
 
 /*

@@ -24,11 +24,12 @@ MOE_MK_ERR_QUEUE = 4
 MOE_MK_ERR_UNINIT = 8
 MOE_MK_DEBUG_DROP_NOTIFY = 1
 MOE_MK_DEBUG_TRACE = 2
+MOE_MK_DEBUG_NO_PREFETCH = 4
 TASK_KINDS = ("route", "topk", "scan", "group", "gemm1", "gemm2", "combine")
 # control block words (see moe_mk_routing_view)
 CTL_WORDS = 512
 CTL = {"epoch": 0, "exit": 1, "err": 2, "ev_topk": 5, "ev_scan": 6, "magic": 8, "mt_total": 9,
-       "qhead": 32, "qtail": 64, "ev_y": 160, "dbg": 192, "xq": 256}
+       "qhead": 32, "qtail": 64, "pf": 96, "ev_y": 160, "dbg": 192, "xq": 256}
 
 _lib = None
 

@@ -171,6 +171,12 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.NB2 = tl.NB2;
     P.S = tl.S;
     P.BM = tl.BM;
+    {  // after the tile configuration: the prefetch follows the gate/up tiles
+        const mk::Prefetch pf = (plan->debug & MOE_MK_DEBUG_NO_PREFETCH) ? mk::Prefetch{0, 0}
+                                                                           : mk::prefetch_plan(s, B, P.NB1, P.BM == mk::kWideBM);
+        P.pf_nt = pf.nt;
+        P.pf_lines = pf.lines;
+    }
     P.q_cap = (int)cc.q_cap;
     P.mt_cap = (int)cc.mt_cap;
     P.watchdog = plan->watchdog;

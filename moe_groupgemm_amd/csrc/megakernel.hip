@@ -2088,6 +2088,43 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
     }
 }
 
+// One chunk of the weight prefetch (512 lines, one per thread; see prefetch_plan): line L
+// is line L % 4 (W1 or W3, first or second 128 bytes) of row L / (4 pf_nt) of gate/up tile
+// (L / 4) % pf_nt in task order.  Returns false when no line is left.
+__device__ __forceinline__ bool prefetch_chunk(const MK_C Params &P) {
+    if (P.pf_lines <= 0) return false;
+    if (threadIdx.x == 0) g_sm.bcast[1] = add_relaxed(P.ctl + CTL_PF, kThreads);
+    __syncthreads();
+    const int l0 = g_sm.bcast[1];
+    __syncthreads();
+    if (l0 >= P.pf_lines) return false;
+    const int L = l0 + (int)threadIdx.x;
+    if (L < P.pf_lines) {
+        const int per_row = 4 * P.pf_nt;
+        const int r = L / per_row, rem = L - r * per_row;
+        const int i = rem >> 2, c = rem & 3;
+        const int Q = P.NB1 / P.S;
+        const int sp = i / (P.E * Q), e = (i / Q) % P.E, n = i % Q;
+        const int col = sp * (P.f / P.S) + n * kBN + (c & 1) * 64;
+        const MK_G uint16_t *W = (c >> 1) ? P.W3 : P.W1;
+        const uint32_t v = *(const MK_G uint32_t *)(W + (size_t)e * P.d * P.f + (size_t)r * P.f + col);
+        asm volatile("" ::"v"(v));  // the value is not needed, only the line's trip through the caches
+    }
+    return true;
+}
+
+// Wait for a counter to reach zero (as wg_wait_zero), prefetching weight lines meanwhile.
+__device__ __forceinline__ bool wg_wait_zero_prefetching(const MK_C Params &P, const MK_G int *ctr) {
+    for (;;) {
+        if (threadIdx.x == 0) g_sm.bcast[0] = ld_relaxed(ctr) == 0 ? 1 : 0;
+        __syncthreads();
+        const bool zero = g_sm.bcast[0] != 0;
+        __syncthreads();
+        if (zero || !prefetch_chunk(P)) break;
+    }
+    return wg_wait_zero(P, ctr);
+}
+
 // Dynamic pop.  A workgroup takes the next ticket with one atomic add; tickets below nR are
 // the router tasks (never pushed), ticket nR + i is queue slot i.  The holder of a ticket
 // whose slot is not yet filled waits on that slot alone, so idle workgroups poll distinct
@@ -2190,7 +2227,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
         // claim counter, so tiles adjacent in the list start together and share operands in
         // L2.  Each XCD's list is in topological order, so the smallest unfinished task of
         // the forward always has its inputs done or in progress.
-        if (ok && wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) {
+        if (ok && wg_wait_zero_prefetching(P, P.ctl + CTL_EV_SCAN)) {
             complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
             const int x = blockIdx.x & 7;
             for (;;) {
@@ -2219,6 +2256,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
             if (ld_relaxed(P.ctl + CTL_ERR) == 0) {
                 st_relaxed(P.ctl + CTL_QHEAD, 0);
                 st_relaxed(P.ctl + CTL_QTAIL, 0);
+                st_relaxed(P.ctl + CTL_PF, 0);
                 st_relaxed(P.ctl + CTL_EV_SCAN, 1);
                 for (int x = 0; x < 8; ++x) st_relaxed(P.ctl + CTL_XQ + 32 * x, 0);
             }

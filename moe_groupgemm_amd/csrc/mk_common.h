@@ -43,6 +43,7 @@ enum CtlWord {
     CTL_TOTAL64 = 12,   // int64 at words 12..13: (epoch << 32) | task count (dynamic mode)
     CTL_QHEAD = 32,     // dynamic queue: next ticket
     CTL_QTAIL = 64,     // dynamic queue: slots reserved by pushers
+    CTL_PF = 96,        // weight prefetch: lines claimed (rest 0)
     CTL_EV_Y = 160,     // event: all down-projection tiles done
     CTL_DBG = 192,      // 8 per-kind task counters (accumulate across forwards)
     CTL_XQ = 256,       // static schedule: claim counter of XCD x's GroupGEMM list at 256 + 32x
@@ -103,6 +104,32 @@ inline Tiles tile_config(const Shape &s, int64_t B) {
     t.NB2 = s.d / (wide ? kWideBN : kBN);
     t.S = wide ? 1 : down_splits(s, B);
     return t;
+}
+
+// Weight prefetch while a small batch is routed (static schedule).  Until the scan event
+// fires (the whole routing phase), a workgroup with nothing to do reads the leading rows of
+// the gate/up weight tiles that the first round of tasks will stream, so that those rows
+// come from the Infinity Cache (256 MB) rather than HBM once the tiles run.  (The dynamic
+// schedule does not prefetch: a workgroup waiting on its queue slot between prefetch chunks
+// started its task later, which cost more than the prefetch saved.)  Only for a batch
+// of one routing tile with narrow tiles, where each expert has at most one row tile and
+// the first round of tasks is known from the shapes (the gate/up tiles in task order, if
+// every expert has rows), and only when B*k >= E, so that most experts do.
+constexpr int64_t kPrefetchBytes = 96ll << 20;
+struct Prefetch {
+    int nt, lines;
+};
+inline Prefetch prefetch_plan(const Shape &s, int64_t B, int nb1, bool wide) {
+    Prefetch p{0, 0};
+    if (B < 1 || B > kTileTokens || wide || nb1 < 1 || B * s.k < s.E) return p;
+    const int64_t nt = (int64_t)s.E * nb1 < 256 ? (int64_t)s.E * nb1 : 256;
+    int64_t depth = kPrefetchBytes / (nt * 4 * 128);  // rows of K: 4 lines per tile row (two of each weight)
+    depth = depth < s.d ? depth : s.d;
+    depth -= depth % 64;
+    if (depth <= 0) return p;
+    p.nt = (int)nt;
+    p.lines = (int)(depth * nt * 4);
+    return p;
 }
 
 // Task counts that depend on B only.
@@ -198,6 +225,7 @@ struct Params {
     int debug;       // MOE_MK_DEBUG_* bits
     int nR, nTG, nEB, T, nC, NB1, NB2, tpw, S;
     int CT;          // tokens per combine task
+    int pf_nt, pf_lines;  // weight prefetch during routing: first gate/up tiles covered, 128-byte lines
     int BM;          // GroupGEMM tile rows (kBM or kWideBM); columns are f / NB1 = d / NB2
     int q_cap, mt_cap;
     long long watchdog;  // real-time ticks (100 MHz)

@@ -210,6 +210,7 @@ def test_rest_state_and_task_counts(B, E, sched):
     assert c[C["epoch"]] == before[C["epoch"]] + 3    # epoch advanced once per forward
     assert c[C["exit"]] == 0                           # exit counter at rest
     assert c[C["qhead"]] == c[C["qtail"]] == 0        # queue at rest
+    assert c[C["pf"]] == 0                             # weight-prefetch claims at rest
     assert all(c[C["xq"] + 32 * x] == 0 for x in range(8))  # static per-XCD claim counters at rest
     assert c[C["ev_topk"]] == 0 and c[C["ev_scan"]] == 1 and c[C["ev_y"]] == 0  # events at rest
     hist = routing_numpy(layer, B)["hist"]
