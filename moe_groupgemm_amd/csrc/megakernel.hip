@@ -1637,39 +1637,41 @@ __device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &Pa, int 
     wout_store<BN>(tile, P.y + (size_t)row0 * P.d + (size_t)n * BN, (size_t)P.d, nrows);
 }
 
-// GEMM1 tile: h[rows, n0:n0+64] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
-// where row p of the tile is token perm[p] / k of x.  The tile variant is chosen from the
-// tile's actual row count.
-__device__ __attribute__((noinline)) void task_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
+// Narrow GEMM tiles as functions of their own, each called straight from the task loop: a
+// called function saves the callee-saved registers it uses (about 60 here) to scratch and
+// restores them on return, so one call level per tile rather than a dispatcher around the
+// tile function halves that traffic.
+// GEMM1 tile: h[rows, n0:n0+128] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
+// where row p of the tile is token perm[p] / k of x; AR = staged A rows (16 or 64).
+template <int AR>
+__device__ __attribute__((noinline)) void narrow_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
     const MK_C Params &P = uni_params(Pa);
-    e = uni(e);
-    row0 = uni(row0);
-    nrows = uni(nrows);
-    n = uni(n);
+    gemm1_tile<AR>(P, uni(e), uni(row0), uni(nrows), uni(n));
+}
+// GEMM2 tile: y[rows, n0:n0+128] (or its split-sp partial) = h[rows, f range sp] W2[e][f range sp, n0:n0+128].
+template <int AR>
+__device__ __attribute__((noinline)) void narrow_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n,
+                                                       int sp, int mt) {
+    const MK_C Params &P = uni_params(Pa);
+    gemm2_tile<AR>(P, uni(e), uni(row0), uni(nrows), uni(n), uni(sp), uni(mt));
+}
+
+// The tile variant is chosen from the forward's tile shape and the tile's actual rows.
+__device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
     if (P.BM == kWideBM)
         wide_gemm1(P, e, row0, nrows, n);
     else if (nrows <= 16)
-        gemm1_tile<16>(P, e, row0, nrows, n);
+        narrow_gemm1<16>(P, e, row0, nrows, n);
     else
-        gemm1_tile<64>(P, e, row0, nrows, n);
+        narrow_gemm1<64>(P, e, row0, nrows, n);
 }
-
-// GEMM2 tile: y[sp][rows, n0:n0+64] = h[rows, f range sp] W2[e][f range sp, n0:n0+64], fp32.
-__device__ __attribute__((noinline)) void task_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n,
-                                                     int sp, int mt) {
-    const MK_C Params &P = uni_params(Pa);
-    e = uni(e);
-    row0 = uni(row0);
-    nrows = uni(nrows);
-    n = uni(n);
-    sp = uni(sp);
-    mt = uni(mt);
+__device__ __forceinline__ void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n, int sp, int mt) {
     if (P.BM == kWideBM)
         wide_gemm2(P, e, row0, nrows, n);
     else if (nrows <= 16)
-        gemm2_tile<16>(P, e, row0, nrows, n, sp, mt);
+        narrow_gemm2<16>(P, e, row0, nrows, n, sp, mt);
     else
-        gemm2_tile<64>(P, e, row0, nrows, n, sp, mt);
+        narrow_gemm2<64>(P, e, row0, nrows, n, sp, mt);
 }
 
 // ------------------------------------------------------------------------------ COMBINE
