@@ -135,7 +135,7 @@ def trace_report(layer, x, out, B):
         S = 4 if (a <= 1024 and f >= 8192 and nb1 % 4 == 0) else 2 if (a <= 1024 and f >= 4096 and nb1 % 2 == 0) else 1
     # GroupGEMM blocks are padded to multiples of 8 task positions (empty tasks leave no record)
     r8 = lambda v: (v + 7) // 8 * 8
-    total = r8(nR + 2 * T + 1) + S * (r8(mt * nb1 // S) + r8(mt * nb2)) + -(-B // (8 if B >= 1024 and k <= 8 else 4)) * -(-d // (4 * info("threads")))
+    total = r8(nR + 2 * T + 1) + S * (r8(mt * nb1 // S) + r8(mt * nb2)) + -(-B // (8 if B >= 1024 and k <= 8 else 1 if B <= 64 else 4)) * -(-d // (4 * info("threads")))
     tr = tr[:total]
     tr = tr[tr[:, 1] != 0]
     kind = (tr[:, 0] >> 32) & 0xFF

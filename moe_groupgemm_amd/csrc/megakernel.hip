@@ -1732,6 +1732,15 @@ __device__ __attribute__((noinline)) void task_combine(const MK_C Params &Pa, in
             combine_tile<4, 8>(P, c);
         else
             combine_tile<8, 8>(P, c);
+    } else if (P.CT == 1) {
+        if (P.k <= 2)
+            combine_tile<2, 1>(P, c);
+        else if (P.k <= 4)
+            combine_tile<4, 1>(P, c);
+        else if (P.k <= 8)
+            combine_tile<8, 1>(P, c);
+        else
+            combine_tile<16, 1>(P, c);
     } else if (P.k <= 2) {
         combine_tile<2, 4>(P, c);
     } else if (P.k <= 4) {

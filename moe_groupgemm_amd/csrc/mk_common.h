@@ -61,8 +61,10 @@ struct Shape {
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tokens per combine task: eight at large batches with k <= 8 (twice the rows in flight per
-// task, and half the tasks each paying a round trip for its indices), else four.
-inline int combine_tokens(int64_t B, int k) { return B >= 1024 && k <= 8 ? 8 : 4; }
+// task, and half the tasks each paying a round trip for its indices), one for a batch of
+// one routing tile (the combine is then two round trips of latency, run on as many
+// workgroups as there are tokens), else four.
+inline int combine_tokens(int64_t B, int k) { return B >= 1024 && k <= 8 ? 8 : B <= kTileTokens ? 1 : 4; }
 
 // Router tokens per wave: one at small batches (more, shorter tasks), four at large ones
 // (each expert-weight row loaded serves four tokens).  A router task covers kWaves waves.

@@ -80,4 +80,4 @@ def expected_task_counts(hist, B, E, d, f, k):
     mt = int(sum((int(h) + BM - 1) // BM for h in hist))
     tpw = 1 if B <= 512 else 4  # router tokens per wave
     return {"route": -(-B // (WAVES * tpw)) * -(-E // 16), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
-            "gemm1": mt * NB1, "gemm2": mt * S * NB2, "combine": -(-B // (8 if B >= 1024 and k <= 8 else 4)) * -(-d // COMBINE_COLS)}
+            "gemm1": mt * NB1, "gemm2": mt * S * NB2, "combine": -(-B // (8 if B >= 1024 and k <= 8 else 1 if B <= 64 else 4)) * -(-d // COMBINE_COLS)}
