@@ -511,8 +511,12 @@ __device__ __attribute__((noinline)) void task_route(const MK_C Params &Pa, int 
         const int tpw = uni(P.tpw);
         for (int t = 0; t < tpw; ++t) route_wave_scalar(P, (tg * kWaves + wave_id()) * tpw + t, e0);
     } else if (P.tpw == 1) {
-        if (P.d % 512 == 0)
+        // 512-value stages for long rows; at d <= 2048 stages of 256 let the whole slice be
+        // in flight at once (7 stages of the ring), which matters more than the stage size
+        if (P.d % 512 == 0 && P.d > 2048)
             route_tile<1, 512>(P, tg * kWaves, e0);
+        else if (P.d % 256 == 0)
+            route_tile<1, 256>(P, tg * kWaves, e0);
         else
             route_tile<1, 128>(P, tg * kWaves, e0);
     } else {
