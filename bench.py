@@ -123,7 +123,7 @@ def trace_report(layer, x, out, B):
     E, k, d, f = layer.E, layer.k, layer.d, layer.f
     info = lambda key: mk.moe_mk_plan_info(layer.plan, key)
     waves = info("threads") // 64
-    tpw = 1 if B <= 512 else 4
+    tpw = 1 if B <= 512 else 8 if E % 4 == 0 and d % 128 == 0 and -(-B // 64) * -(-E // 16) >= 512 else 4
     nR = -(-B // (waves * tpw)) * -(-E // 16)
     T = -(-B // 64)
     mt = int(ctl[mk.CTL["mt_total"]])

@@ -297,26 +297,69 @@ __device__ __forceinline__ const MK_C Params &uni_params(const MK_C Params &P) {
 // combined by a butterfly that pairs lanes l and l^32, then l^16, ... (the halves fold),
 // which every lane evaluates in the same association; the bias is added last.
 
+// Lane l ^ M's value (M = 1, 2, 4, 8: within rows of 16 lanes) by DPP, without LDS.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+    int x = __float_as_int(v);
+    if constexpr (M == 1) {
+        x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    } else if constexpr (M == 2) {
+        x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+    } else if constexpr (M == 4) {
+        x = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);  // row_half_mirror: j -> 7 - j
+        x = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, true);   // quad_perm [3,2,1,0]
+    } else {
+        static_assert(M == 8, "xor within a row");
+        x = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);  // row_ror:8
+    }
+    return __int_as_float(x);
+}
+
 // Sum each of NV per-lane values over the 64 lanes, leaving value v (v = 0..NV-1) in the
 // lanes whose bits 5, 4, ... (most significant first) spell v.  Level by level, lane l
 // adds the partial sum of lane l ^ M (M = 32, 16, ..., 1); the values a lane stops
 // carrying are sent to its partner instead of both lanes adding everything.  Every
 // value is therefore the sum of the 64 chains in the association of the halves fold.
+// The exchanges are cross-lane VALU operations (no LDS round trips): for M = 32 and 16,
+// v_permlane32_swap / v_permlane16_swap of the pair (v[i], v[i+H]) leave each lane its own
+// kept value and its partner's copy of it (lanes with bit M clear keep v[i], the others
+// v[i+H]), whose sum is the level's result; for M <= 8, DPP moves within rows.
 template <int NV, int M>
 __device__ __forceinline__ void reduce_scatter(float *v, int lane) {
     if constexpr (M >= 1) {
         if constexpr (NV >= 2) {
             constexpr int H = NV / 2;
-            const bool up = (lane & M) != 0;
+            if constexpr (M >= 16) {
 #pragma unroll
-            for (int i = 0; i < H; ++i) {
-                const float send = up ? v[i] : v[i + H];
-                const float keep = up ? v[i + H] : v[i];
-                v[i] = keep + shfl_xor_f(send, M);
+                for (int i = 0; i < H; ++i) {
+                    const unsigned a = __float_as_uint(v[i]), b = __float_as_uint(v[i + H]);
+                    unsigned p0, p1;
+                    if constexpr (M == 32) {
+                        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+                        p0 = r[0];
+                        p1 = r[1];
+                    } else {
+                        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+                        p0 = r[0];
+                        p1 = r[1];
+                    }
+                    v[i] = __uint_as_float(p0) + __uint_as_float(p1);
+                }
+            } else {
+                const bool up = (lane & M) != 0;
+#pragma unroll
+                for (int i = 0; i < H; ++i) {
+                    const float send = up ? v[i] : v[i + H];
+                    const float keep = up ? v[i + H] : v[i];
+                    v[i] = keep + lane_xor<M>(send);
+                }
             }
             reduce_scatter<H, M / 2>(v, lane);
         } else {
-            v[0] = v[0] + shfl_xor_f(v[0], M);
+            if constexpr (M >= 16)
+                v[0] = v[0] + shfl_xor_f(v[0], M);
+            else
+                v[0] = v[0] + lane_xor<M>(v[0]);
             reduce_scatter<1, M / 2>(v, lane);
         }
     }
@@ -329,6 +372,21 @@ __device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[T
     constexpr int NV = TPW * 16;
     const int lane = lane_id();
     reduce_scatter<NV, 32>(acc, lane);
+    if constexpr (NV == 128) {
+        // lane L holds values 2L (acc[0]) and 2L+1 (acc[1]): token L / 8, experts
+        // e0 + 2 * (L % 8) and the next
+        const int b = b0 + (lane >> 3), e = e0 + 2 * (lane & 7);
+        if (b < P.B) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                if (e + i < P.E) {
+                    const float lg = acc[i] + (P.bias ? P.bias[e + i] : 0.0f);
+                    if (!__builtin_isfinite(lg)) set_error(P.ctl, 2 /* MOE_MK_ERR_NONFINITE */);
+                    pub(P.logits + (size_t)b * P.E + e + i, lg);
+                }
+        }
+        return;
+    }
     // lane L holds value L >> SH: token t = value / 16, expert e0 + value % 16
     constexpr int SH = NV == 64 ? 0 : 2;
     if ((lane & ((1 << SH) - 1)) == 0) {
@@ -374,26 +432,69 @@ struct RouteCfg {
     static_assert((NS - 2) * LOADS < 64, "vmcnt range");
 };
 
-template <int TPW>
-__device__ __forceinline__ void route_reads(uint32_t wa, const uint32_t (&xa)[TPW], f32x4 (&wv)[4],
-                                            uint32_t (&xr)[TPW]) {
+// One step of a router stage: this lane's Wr row (16 experts, four 16-byte chunks at wa and
+// its swizzled neighbours) and its value of each of the wave's TPW tokens (token t at
+// xa + t * XS bytes).  The reads do not wait: route_wait names the same registers as inputs
+// and outputs, so no use of them can be placed before it.
+template <int TPW, int XS>
+__device__ __forceinline__ void route_reads(uint32_t wa, uint32_t xa, f32x4 (&wv)[4], uint32_t (&xr)[TPW]) {
     const uint32_t w1 = wa ^ 16u, w2 = wa ^ 32u, w3 = wa ^ 48u;
     if constexpr (TPW == 1) {
         asm volatile(
             "ds_read_b128 %0, %5\n\tds_read_b128 %1, %6\n\tds_read_b128 %2, %7\n\tds_read_b128 %3, %8\n\t"
-            "ds_read_u16 %4, %9\n\ts_waitcnt lgkmcnt(0)"
+            "ds_read_u16 %4, %9"
             : "=&v"(wv[0]), "=&v"(wv[1]), "=&v"(wv[2]), "=&v"(wv[3]), "=&v"(xr[0])
-            : "v"(wa), "v"(w1), "v"(w2), "v"(w3), "v"(xa[0]));
-    } else {
-        static_assert(TPW == 4, "router tokens per wave");
+            : "v"(wa), "v"(w1), "v"(w2), "v"(w3), "v"(xa));
+    } else if constexpr (TPW == 4) {
         asm volatile(
             "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
-            "ds_read_u16 %4, %12\n\tds_read_u16 %5, %13\n\tds_read_u16 %6, %14\n\tds_read_u16 %7, %15\n\t"
-            "s_waitcnt lgkmcnt(0)"
+            "ds_read_u16 %4, %12\n\tds_read_u16 %5, %12 offset:%13\n\t"
+            "ds_read_u16 %6, %12 offset:%14\n\tds_read_u16 %7, %12 offset:%15"
             : "=&v"(wv[0]), "=&v"(wv[1]), "=&v"(wv[2]), "=&v"(wv[3]), "=&v"(xr[0]), "=&v"(xr[1]), "=&v"(xr[2]),
               "=&v"(xr[3])
-            : "v"(wa), "v"(w1), "v"(w2), "v"(w3), "v"(xa[0]), "v"(xa[1]), "v"(xa[2]), "v"(xa[3]));
+            : "v"(wa), "v"(w1), "v"(w2), "v"(w3), "v"(xa), "i"(XS), "i"(2 * XS), "i"(3 * XS));
+    } else {
+        static_assert(TPW == 8, "router tokens per wave");
+        asm volatile(
+            "ds_read_b128 %0, %12\n\tds_read_b128 %1, %13\n\tds_read_b128 %2, %14\n\tds_read_b128 %3, %15\n\t"
+            "ds_read_u16 %4, %16\n\tds_read_u16 %5, %16 offset:%17\n\t"
+            "ds_read_u16 %6, %16 offset:%18\n\tds_read_u16 %7, %16 offset:%19\n\t"
+            "ds_read_u16 %8, %16 offset:%20\n\tds_read_u16 %9, %16 offset:%21\n\t"
+            "ds_read_u16 %10, %16 offset:%22\n\tds_read_u16 %11, %16 offset:%23"
+            : "=&v"(wv[0]), "=&v"(wv[1]), "=&v"(wv[2]), "=&v"(wv[3]), "=&v"(xr[0]), "=&v"(xr[1]), "=&v"(xr[2]),
+              "=&v"(xr[3]), "=&v"(xr[4]), "=&v"(xr[5]), "=&v"(xr[6]), "=&v"(xr[7])
+            : "v"(wa), "v"(w1), "v"(w2), "v"(w3), "v"(xa), "i"(XS), "i"(2 * XS), "i"(3 * XS), "i"(4 * XS),
+              "i"(5 * XS), "i"(6 * XS), "i"(7 * XS));
     }
+}
+
+// Holds the accumulators at this point of the program: the FMAs that produce them cannot
+// be moved past it (the compiler otherwise sinks a pipelined step's FMAs behind the next
+// steps' reads and waits).
+template <int N>
+__device__ __forceinline__ void pin_acc(float (&acc)[N]) {
+    static_assert(N % 16 == 0, "blocks of 16");
+#pragma unroll
+    for (int i = 0; i < N; i += 16)
+        asm volatile(""
+                     : "+v"(acc[i]), "+v"(acc[i + 1]), "+v"(acc[i + 2]), "+v"(acc[i + 3]), "+v"(acc[i + 4]),
+                       "+v"(acc[i + 5]), "+v"(acc[i + 6]), "+v"(acc[i + 7]), "+v"(acc[i + 8]), "+v"(acc[i + 9]),
+                       "+v"(acc[i + 10]), "+v"(acc[i + 11]), "+v"(acc[i + 12]), "+v"(acc[i + 13]), "+v"(acc[i + 14]),
+                       "+v"(acc[i + 15]));
+}
+
+template <int TPW>
+__device__ __forceinline__ void route_wait(f32x4 (&wv)[4], uint32_t (&xr)[TPW]) {
+    if constexpr (TPW == 1)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wv[0]), "+v"(wv[1]), "+v"(wv[2]), "+v"(wv[3]), "+v"(xr[0]));
+    else if constexpr (TPW == 4)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(wv[0]), "+v"(wv[1]), "+v"(wv[2]), "+v"(wv[3]), "+v"(xr[0]), "+v"(xr[1]), "+v"(xr[2]),
+                       "+v"(xr[3]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(wv[0]), "+v"(wv[1]), "+v"(wv[2]), "+v"(wv[3]), "+v"(xr[0]), "+v"(xr[1]), "+v"(xr[2]),
+                       "+v"(xr[3]), "+v"(xr[4]), "+v"(xr[5]), "+v"(xr[6]), "+v"(xr[7]));
 }
 
 template <int TPW, int RPS>
@@ -440,41 +541,75 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
     float acc[TPW * 16];
 #pragma unroll
     for (int i = 0; i < TPW * 16; ++i) acc[i] = 0.0f;
+    // Software-pipelined: the LDS reads of step sub+1 are issued before the FMAs of step
+    // sub and waited for after them, so the two waves of a SIMD (which leave every stage
+    // barrier together) do not both sit out the LDS latency.  The reads of a stage's first
+    // step are issued in the previous stage's last step, after that stage's barrier (stage
+    // st+1 has landed; every wave has read all of stage st, whose slot then takes the
+    // loads of stage st+NS).  Register sets alternate per step (RPS/64 steps per stage, an
+    // even count), and every read is issued unconditionally (past the last stage, from a
+    // slot of the ring, unused) so that no set is merged with another while in flight.
+    constexpr int NSUB = RPS / 64;
+    static_assert(NSUB % 2 == 0, "even steps per stage");
+    const uint32_t rbase = lds_addr((const uint16_t *)ring);
+    auto reads = [&](int slot, int sub, f32x4 (&wv)[4], uint32_t (&xr)[TPW]) {
+        const uint32_t sb = rbase + (uint32_t)(slot * C::STAGE_BYTES);
+        const int row = 64 * sub + lane;  // j = RPS*st + row: chain `lane`, step NSUB*st + sub
+        route_reads<TPW, 2 * RPS>(sb + (uint32_t)(row * 64 + 16 * rswz(row)),
+                                  sb + (uint32_t)(C::WR_BYTES + w * C::XB + 2 * row), wv, xr);
+    };
+    auto fmas = [&](const f32x4 (&wv)[4], const uint32_t (&xr)[TPW]) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const float xf = __uint_as_float(xr[t] << 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int z = 0; z < 4; ++z) acc[t * 16 + 4 * q + z] = fmaf(xf, wv[q][z], acc[t * 16 + 4 * q + z]);
+        }
+    };
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
         if (p < nst) load(p, p);
-    const uint32_t rbase = lds_addr((const uint16_t *)ring);
+    if (NS - 2 < nst)
+        wait_vm<(NS - 2) * C::LOADS>();
+    else
+        wait_vm<0>();
+    bare_barrier();
+    if (NS - 1 < nst) load(NS - 1, NS - 1);
+    f32x4 wv0[4], wv1[4];
+    uint32_t xr0[TPW], xr1[TPW];
+    reads(0, 0, wv0, xr0);
+    route_wait<TPW>(wv0, xr0);
     int slot = 0;
     for (int st = 0; st < nst; ++st) {
-        if (st + NS - 2 < nst)
-            wait_vm<(NS - 2) * C::LOADS>();
-        else
-            wait_vm<0>();
-        bare_barrier();
-        const int nxt = st + NS - 1;
-        if (nxt < nst) load(nxt, slot == 0 ? NS - 1 : slot - 1);
-        const uint32_t sb = rbase + (uint32_t)(slot * C::STAGE_BYTES);
+        const int nslot = slot == NS - 1 ? 0 : slot + 1;
 #pragma unroll
-        for (int sub = 0; sub < RPS / 64; ++sub) {
-            const int row = 64 * sub + lane;  // j = RPS*st + row: chain `lane`, step (RPS/64)*st + sub
-            uint32_t xa[TPW];
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-                xa[t] = sb + (uint32_t)(C::WR_BYTES + w * C::XB + t * 2 * RPS + 2 * row);
-            f32x4 wv[4];
-            uint32_t xr[TPW];
-            route_reads<TPW>(sb + (uint32_t)(row * 64 + 16 * rswz(row)), xa, wv, xr);
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const float xf = __uint_as_float(xr[t] << 16);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int z = 0; z < 4; ++z)
-                        acc[t * 16 + 4 * q + z] = fmaf(xf, wv[q][z], acc[t * 16 + 4 * q + z]);
+        for (int sub = 0; sub < NSUB; ++sub) {
+            f32x4 (&wc)[4] = (sub & 1) ? wv1 : wv0;
+            uint32_t (&xc)[TPW] = (sub & 1) ? xr1 : xr0;
+            f32x4 (&wn)[4] = (sub & 1) ? wv0 : wv1;
+            uint32_t (&xn)[TPW] = (sub & 1) ? xr0 : xr1;
+            if (sub + 1 < NSUB) {
+                reads(slot, sub + 1, wn, xn);
+            } else {
+                if (st + 1 < nst) {
+                    if (st + NS - 1 < nst)
+                        wait_vm<(NS - 2) * C::LOADS>();  // after stage st+1: stages st+2 .. st+NS-1
+                    else
+                        wait_vm<0>();
+                    bare_barrier();
+                    if (st + NS < nst) load(st + NS, slot);
+                }
+                reads(nslot, 0, wn, xn);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            fmas(wc, xc);
+            pin_acc(acc);
+            __builtin_amdgcn_sched_barrier(0);
+            route_wait<TPW>(wn, xn);
         }
-        slot = slot == NS - 1 ? 0 : slot + 1;
+        slot = nslot;
     }
     wait_vm<0>();
     __syncthreads();  // the ring may be reused by the next task
@@ -519,6 +654,8 @@ __device__ __attribute__((noinline)) void task_route(const MK_C Params &Pa, int 
             route_tile<1, 256>(P, tg * kWaves, e0);
         else
             route_tile<1, 128>(P, tg * kWaves, e0);
+    } else if (P.tpw == 8) {  // d % 128 == 0
+        route_tile<8, 128>(P, tg * kWaves * 8, e0);
     } else {
         if (P.d % 256 == 0)
             route_tile<4, 256>(P, tg * kWaves * 4, e0);
@@ -1982,11 +2119,32 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
     }
 }
 
+// Token group and expert block of router task g.  A task reads its group's activation rows
+// and its block's router-weight columns, and workgroup w (hence task position g in the
+// static schedule) runs on XCD w % 8.  Token-group major order (tg = g / nEB) gives XCD x
+// the expert blocks = x (mod 8) of every group: each XCD keeps its weight columns in L2 but
+// fetches all of x.  When x is the larger of the two (B > 2E: B*d bf16 values against E*d
+// fp32 ones), positions g = 8l + x instead take group 8*(l / nEB) + x and block l % nEB,
+// so the blocks of a group run together on one XCD and its rows are fetched into that L2
+// once; groups past the last multiple of 8 keep the plain order.
+__device__ __forceinline__ void route_task_coords(const MK_C Params &P, int g, int &tg, int &eb) {
+    const int full = P.nTG & ~7;
+    if (P.B > 2 * P.E && g < full * P.nEB) {
+        const int x = g & 7, l = g >> 3, lg = l / P.nEB;
+        tg = 8 * lg + x;
+        eb = l - lg * P.nEB;
+    } else {
+        tg = g / P.nEB;
+        eb = g - tg * P.nEB;
+    }
+}
+
 // Runs task g (obtained at time t0).  Returns false when the forward must be abandoned.
 __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs, unsigned long long t0) {
     const bool dyn = P.sched != 0;
     if (g < bs.K) {  // ---------------------------------------------------------- ROUTE
-        const int tg = g / P.nEB, eb = g - tg * P.nEB;
+        int tg, eb;
+        route_task_coords(P, g, tg, eb);
         task_route(P, tg, eb);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_ROUTE);

@@ -67,8 +67,15 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int combine_tokens(int64_t B, int k) { return B >= 1024 && k <= 8 ? 8 : B <= kTileTokens ? 1 : 4; }
 
 // Router tokens per wave: one at small batches (more, shorter tasks), four at large ones
-// (each expert-weight row loaded serves four tokens).  A router task covers kWaves waves.
-inline int route_tpw(int64_t B) { return B <= 512 ? 1 : 4; }
+// (each expert-weight row read from LDS serves four tokens), eight once that still leaves
+// two tasks per workgroup (each row read serves eight tokens: the reads, not the FMAs, had
+// set a task's pace; needs E % 4 == 0 and d % 128 == 0).  A task covers kWaves waves;
+// 512 tasks are two per workgroup on 256 CUs.
+inline int route_tpw(int64_t B, int64_t E, int64_t d) {
+    if (B <= 512) return 1;
+    if (E % 4 == 0 && d % 128 == 0 && ceil_div(B, 8 * kWaves) * ceil_div(E, kRouteExperts) >= 512) return 8;
+    return 4;
+}
 
 // K splits S of the down projection: at small batches with a long f, each down-projection
 // tile covers f/S of the reduction (partial results summed in a fixed order by the last
@@ -152,7 +159,7 @@ struct Counts {
 inline Counts make_counts(const Shape &s, int64_t B) {
     Counts c;
     c.T = ceil_div(B, kTileTokens);
-    c.tpw = route_tpw(B);
+    c.tpw = route_tpw(B, s.E, s.d);
     c.nTG = ceil_div(B, kWaves * c.tpw);
     c.nEB = ceil_div(s.E, kRouteExperts);
     c.nR = c.nTG * c.nEB;
