@@ -124,7 +124,8 @@ def trace_report(layer, x, out, B):
     info = lambda key: mk.moe_mk_plan_info(layer.plan, key)
     waves = info("threads") // 64
     tpw = 1 if B <= 512 else 8 if E % 4 == 0 and d % 128 == 0 and -(-B // 64) * -(-E // 16) >= 512 else 4
-    nR = -(-B // (waves * tpw)) * -(-E // 16)
+    reb = 4 if tpw == 1 and E % 4 == 0 and d % 512 == 0 and -(-B // waves) * -(-E // 16) < 64 else 16
+    nR = -(-B // (waves * tpw)) * -(-E // reb)
     T = -(-B // 64)
     mt = int(ctl[mk.CTL["mt_total"]])
     a = B * k

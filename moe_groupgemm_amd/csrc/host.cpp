@@ -163,6 +163,7 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.nTG = (int)c.nTG;
     P.tpw = (int)c.tpw;
     P.nEB = (int)c.nEB;
+    P.reb = (int)c.reb;
     P.T = (int)c.T;
     P.nC = (int)c.nC;
     P.CT = mk::combine_tokens(B, s.k);

@@ -367,9 +367,9 @@ __device__ __forceinline__ void reduce_scatter(float *v, int lane) {
 
 // Sums of one wave (lane l holds chain l of every (token, expert) pair it owns) reduced
 // over the lanes in the halves-fold order and written as logits (bias added last).
-template <int TPW>
-__device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[TPW * 16], int b0, int e0) {
-    constexpr int NV = TPW * 16;
+template <int TPW, int EPT = 16>
+__device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[TPW * EPT], int b0, int e0) {
+    constexpr int NV = TPW * EPT;
     const int lane = lane_id();
     reduce_scatter<NV, 32>(acc, lane);
     if constexpr (NV == 128) {
@@ -387,11 +387,12 @@ __device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[T
         }
         return;
     }
-    // lane L holds value L >> SH: token t = value / 16, expert e0 + value % 16
-    constexpr int SH = NV == 64 ? 0 : 2;
+    // lane L holds value L >> SH: token t = value / EPT, expert e0 + value % EPT
+    constexpr int SH = NV == 64 ? 0 : NV == 16 ? 2 : 4;
+    static_assert(NV == 128 || NV == 64 || NV == 16 || NV == 4, "values per lane");
     if ((lane & ((1 << SH) - 1)) == 0) {
         const int v = lane >> SH;
-        const int b = b0 + v / 16, e = e0 + (v & 15);
+        const int b = b0 + v / EPT, e = e0 + v % EPT;
         if (b < P.B && e < P.E) {
             const float bias = P.bias ? P.bias[e] : 0.0f;
             const float lg = acc[0] + bias;
@@ -417,9 +418,9 @@ __device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[T
 // written.
 __device__ __forceinline__ int rswz(int r) { return (r >> 2) & 3; }
 
-template <int TPW, int RPS>
+template <int TPW, int RPS, int EPT = 16>
 struct RouteCfg {
-    static constexpr int WR_BYTES = RPS * 16 * 4;
+    static constexpr int WR_BYTES = RPS * EPT * 4;
     static constexpr int WR_LOADS = WR_BYTES / 1024 / kWaves;  // 1 KB Wr loads per wave and stage
     static constexpr int XB = 2 * RPS * TPW;                   // x bytes per wave and stage
     static constexpr int X_LOADS = XB >= 1024 ? XB / 1024 : XB / 256;  // 16-byte lanes, else 4-byte lanes
@@ -436,10 +437,13 @@ struct RouteCfg {
 // its swizzled neighbours) and its value of each of the wave's TPW tokens (token t at
 // xa + t * XS bytes).  The reads do not wait: route_wait names the same registers as inputs
 // and outputs, so no use of them can be placed before it.
-template <int TPW, int XS>
+template <int TPW, int XS, int EPT = 16>
 __device__ __forceinline__ void route_reads(uint32_t wa, uint32_t xa, f32x4 (&wv)[4], uint32_t (&xr)[TPW]) {
     const uint32_t w1 = wa ^ 16u, w2 = wa ^ 32u, w3 = wa ^ 48u;
-    if constexpr (TPW == 1) {
+    if constexpr (EPT == 4) {
+        static_assert(TPW == 1, "four-expert blocks with one token per wave");
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_u16 %1, %3" : "=&v"(wv[0]), "=&v"(xr[0]) : "v"(wa), "v"(xa));
+    } else if constexpr (TPW == 1) {
         asm volatile(
             "ds_read_b128 %0, %5\n\tds_read_b128 %1, %6\n\tds_read_b128 %2, %7\n\tds_read_b128 %3, %8\n\t"
             "ds_read_u16 %4, %9"
@@ -473,19 +477,25 @@ __device__ __forceinline__ void route_reads(uint32_t wa, uint32_t xa, f32x4 (&wv
 // steps' reads and waits).
 template <int N>
 __device__ __forceinline__ void pin_acc(float (&acc)[N]) {
-    static_assert(N % 16 == 0, "blocks of 16");
+    if constexpr (N == 4) {
+        asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+    } else {
+        static_assert(N % 16 == 0, "blocks of 16");
 #pragma unroll
-    for (int i = 0; i < N; i += 16)
-        asm volatile(""
-                     : "+v"(acc[i]), "+v"(acc[i + 1]), "+v"(acc[i + 2]), "+v"(acc[i + 3]), "+v"(acc[i + 4]),
-                       "+v"(acc[i + 5]), "+v"(acc[i + 6]), "+v"(acc[i + 7]), "+v"(acc[i + 8]), "+v"(acc[i + 9]),
-                       "+v"(acc[i + 10]), "+v"(acc[i + 11]), "+v"(acc[i + 12]), "+v"(acc[i + 13]), "+v"(acc[i + 14]),
-                       "+v"(acc[i + 15]));
+        for (int i = 0; i < N; i += 16)
+            asm volatile(""
+                         : "+v"(acc[i]), "+v"(acc[i + 1]), "+v"(acc[i + 2]), "+v"(acc[i + 3]), "+v"(acc[i + 4]),
+                           "+v"(acc[i + 5]), "+v"(acc[i + 6]), "+v"(acc[i + 7]), "+v"(acc[i + 8]), "+v"(acc[i + 9]),
+                           "+v"(acc[i + 10]), "+v"(acc[i + 11]), "+v"(acc[i + 12]), "+v"(acc[i + 13]),
+                           "+v"(acc[i + 14]), "+v"(acc[i + 15]));
+    }
 }
 
-template <int TPW>
+template <int TPW, int EPT = 16>
 __device__ __forceinline__ void route_wait(f32x4 (&wv)[4], uint32_t (&xr)[TPW]) {
-    if constexpr (TPW == 1)
+    if constexpr (EPT == 4)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wv[0]), "+v"(xr[0]));
+    else if constexpr (TPW == 1)
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wv[0]), "+v"(wv[1]), "+v"(wv[2]), "+v"(wv[3]), "+v"(xr[0]));
     else if constexpr (TPW == 4)
         asm volatile("s_waitcnt lgkmcnt(0)"
@@ -497,10 +507,11 @@ __device__ __forceinline__ void route_wait(f32x4 (&wv)[4], uint32_t (&xr)[TPW]) 
                        "+v"(xr[3]), "+v"(xr[4]), "+v"(xr[5]), "+v"(xr[6]), "+v"(xr[7]));
 }
 
-template <int TPW, int RPS>
+template <int TPW, int RPS, int EPT = 16>
 __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int b0, int e0) {
     const MK_C Params &P = uni_params(Pa);
-    using C = RouteCfg<TPW, RPS>;
+    using C = RouteCfg<TPW, RPS, EPT>;
+    static_assert(EPT == 16 || (EPT == 4 && TPW == 1 && RPS == 512), "router block shapes");
     constexpr int NS = C::NS;
     b0 = uni(b0);
     e0 = uni(e0);
@@ -508,10 +519,13 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
     const int lane = lane_id(), w = wave_id();
     const int nst = uni(P.d / RPS);
     const int E = P.E;
-    // this lane's Wr DMA source: load i of wave w covers rows RPS/8*w + 16*i + lane/4 (chunk
-    // position lane%4; the swizzle of those rows does not depend on i)
-    const int wrow = (RPS / kWaves) * w + (lane >> 2);
-    const int wcol = min(e0 + 4 * ((lane & 3) ^ rswz(wrow)), E - 4);
+    // this lane's Wr DMA source.  16 experts (64-byte rows): load i of wave w covers rows
+    // RPS/8*w + 16*i + lane/4 (chunk position lane%4; the swizzle of those rows does not
+    // depend on i).  4 experts (16-byte rows, not swizzled): rows RPS/8*w + 64*i + lane.
+    constexpr int RB = 4 * EPT;     // bytes of one staged Wr row
+    constexpr int RPL = 1024 / RB;  // rows per 1 KB load
+    const int wrow = (RPS / kWaves) * w + (EPT == 16 ? (lane >> 2) : lane);
+    const int wcol = EPT == 16 ? min(e0 + 4 * ((lane & 3) ^ rswz(wrow)), E - 4) : e0;
     const MK_G float *wsrc = P.Wr + (size_t)wrow * E + wcol;
     // x DMA sources: byte q of the wave's x block (q = 1024*i + 16*lane, or 256*i + 4*lane)
     // is value (q % (2*RPS))/2 of the wave's token q / (2*RPS)
@@ -527,8 +541,8 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
         uint8_t *sp = ring + s * C::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::WR_LOADS; ++i)
-            lds_dma16(wsrc + (size_t)st * wstep + (size_t)16 * i * E,
-                      (MK_L void *)(sp + ((RPS / kWaves) * w + 16 * i) * 64));
+            lds_dma16(wsrc + (size_t)st * wstep + (size_t)RPL * i * E,
+                      (MK_L void *)(sp + ((RPS / kWaves) * w + RPL * i) * RB));
         uint8_t *xd = sp + C::WR_BYTES + w * C::XB;
 #pragma unroll
         for (int i = 0; i < C::X_LOADS; ++i) {
@@ -538,9 +552,9 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
                 __builtin_amdgcn_global_load_lds(xsrc[i] + (size_t)st * RPS, (MK_L void *)(xd + 256 * i), 4, 0, 0);
         }
     };
-    float acc[TPW * 16];
+    float acc[TPW * EPT];
 #pragma unroll
-    for (int i = 0; i < TPW * 16; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < TPW * EPT; ++i) acc[i] = 0.0f;
     // Software-pipelined: the LDS reads of step sub+1 are issued before the FMAs of step
     // sub and waited for after them, so the two waves of a SIMD (which leave every stage
     // barrier together) do not both sit out the LDS latency.  The reads of a stage's first
@@ -555,17 +569,17 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
     auto reads = [&](int slot, int sub, f32x4 (&wv)[4], uint32_t (&xr)[TPW]) {
         const uint32_t sb = rbase + (uint32_t)(slot * C::STAGE_BYTES);
         const int row = 64 * sub + lane;  // j = RPS*st + row: chain `lane`, step NSUB*st + sub
-        route_reads<TPW, 2 * RPS>(sb + (uint32_t)(row * 64 + 16 * rswz(row)),
-                                  sb + (uint32_t)(C::WR_BYTES + w * C::XB + 2 * row), wv, xr);
+        route_reads<TPW, 2 * RPS, EPT>(sb + (uint32_t)(EPT == 16 ? row * 64 + 16 * rswz(row) : row * RB),
+                                       sb + (uint32_t)(C::WR_BYTES + w * C::XB + 2 * row), wv, xr);
     };
     auto fmas = [&](const f32x4 (&wv)[4], const uint32_t (&xr)[TPW]) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const float xf = __uint_as_float(xr[t] << 16);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < EPT / 4; ++q)
 #pragma unroll
-                for (int z = 0; z < 4; ++z) acc[t * 16 + 4 * q + z] = fmaf(xf, wv[q][z], acc[t * 16 + 4 * q + z]);
+                for (int z = 0; z < 4; ++z) acc[t * EPT + 4 * q + z] = fmaf(xf, wv[q][z], acc[t * EPT + 4 * q + z]);
         }
     };
 #pragma unroll
@@ -580,7 +594,7 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
     f32x4 wv0[4], wv1[4];
     uint32_t xr0[TPW], xr1[TPW];
     reads(0, 0, wv0, xr0);
-    route_wait<TPW>(wv0, xr0);
+    route_wait<TPW, EPT>(wv0, xr0);
     int slot = 0;
     for (int st = 0; st < nst; ++st) {
         const int nslot = slot == NS - 1 ? 0 : slot + 1;
@@ -607,13 +621,13 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
             fmas(wc, xc);
             pin_acc(acc);
             __builtin_amdgcn_sched_barrier(0);
-            route_wait<TPW>(wn, xn);
+            route_wait<TPW, EPT>(wn, xn);
         }
         slot = nslot;
     }
     wait_vm<0>();
     __syncthreads();  // the ring may be reused by the next task
-    route_write<TPW>(P, acc, b0 + w * TPW, e0);
+    route_write<TPW, EPT>(P, acc, b0 + w * TPW, e0);
 }
 
 // Router wave for E not a multiple of 4: plain scalar loads, same summation order.
@@ -638,11 +652,13 @@ __device__ __attribute__((noinline)) void route_wave_scalar(const MK_C Params &P
 }
 
 // Router task (tg, eb): tokens [kWaves*tpw*tg, +kWaves*tpw), wave w taking tpw of them,
-// experts [16*eb, +16).
+// experts [reb*eb, +reb) (reb = 16, or 4 at small batches).
 __device__ __attribute__((noinline)) void task_route(const MK_C Params &Pa, int tg, int eb) {
     const MK_C Params &P = uni_params(Pa);
-    const int e0 = eb * kRouteExperts;
-    if ((P.E & 3) != 0) {
+    const int e0 = eb * P.reb;
+    if (P.reb == 4) {  // one token per wave, d % 512 == 0, E % 4 == 0
+        route_tile<1, 512, 4>(P, tg * kWaves, e0);
+    } else if ((P.E & 3) != 0) {
         const int tpw = uni(P.tpw);
         for (int t = 0; t < tpw; ++t) route_wave_scalar(P, (tg * kWaves + wave_id()) * tpw + t, e0);
     } else if (P.tpw == 1) {

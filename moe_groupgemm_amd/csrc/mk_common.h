@@ -21,7 +21,7 @@ namespace mk {
 constexpr int kWaves = 8;            // waves per persistent workgroup (one workgroup per CU)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileTokens = 64;      // tokens per top-k / grouping tile (one lane per token)
-constexpr int kRouteExperts = 16;    // experts per router task
+constexpr int kRouteExperts = 16;    // experts per router task (4 at small batches: route_reb)
 constexpr int kCombineTokens = 8;    // most tokens per combine task (see combine_tokens)
 constexpr int kCombineCols = 4 * kThreads;  // model columns per combine task (4 per thread)
 constexpr int kBM = 64;              // GroupGEMM rows per narrow tile (one expert's rows)
@@ -75,6 +75,15 @@ inline int route_tpw(int64_t B, int64_t E, int64_t d) {
     if (B <= 512) return 1;
     if (E % 4 == 0 && d % 128 == 0 && ceil_div(B, 8 * kWaves) * ceil_div(E, kRouteExperts) >= 512) return 8;
     return 4;
+}
+
+// Experts per router task: 16, or 4 when one token per wave and 16-expert blocks would
+// give fewer than 64 tasks.  Every task streams its block's whole Wr slice (4*d bytes per
+// expert), so at small batches a few CUs each read a large slice; blocks of 4 spread the
+// same bytes over four times the tasks (needs E % 4 == 0 and d % 512 == 0).
+inline int route_reb(int64_t B, int64_t E, int64_t d, int64_t tpw) {
+    if (tpw == 1 && E % 4 == 0 && d % 512 == 0 && ceil_div(B, kWaves) * ceil_div(E, kRouteExperts) < 64) return 4;
+    return kRouteExperts;
 }
 
 // K splits S of the down projection: at small batches with a long f, each down-projection
@@ -146,6 +155,7 @@ struct Counts {
     int64_t T;      // top-k / grouping tiles
     int64_t tpw;    // router tokens per wave
     int64_t nTG;    // router token groups
+    int64_t reb;    // experts per router task
     int64_t nEB;    // router expert blocks
     int64_t nR;     // router tasks
     int64_t nC;     // combine tasks
@@ -161,7 +171,8 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     c.T = ceil_div(B, kTileTokens);
     c.tpw = route_tpw(B, s.E, s.d);
     c.nTG = ceil_div(B, kWaves * c.tpw);
-    c.nEB = ceil_div(s.E, kRouteExperts);
+    c.reb = route_reb(B, s.E, s.d, c.tpw);
+    c.nEB = ceil_div(s.E, c.reb);
     c.nR = c.nTG * c.nEB;
     c.nC = ceil_div(B, combine_tokens(B, s.k)) * ceil_div(s.d, kCombineCols);
     int64_t a = B * s.k;
@@ -170,7 +181,7 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     c.NB2 = s.d / kBN;
     c.S = down_splits(s, B);
     c.q_cap = 2 * c.T + 1 + c.mt_cap * c.NB1 + c.mt_cap * kMaxSplits * c.NB2 + c.nC + 128;  // + block padding
-    c.nR_max = ceil_div(B, kWaves) * c.nEB;
+    c.nR_max = ceil_div(B, kWaves) * ceil_div(s.E, 4);
     return c;
 }
 
@@ -233,6 +244,7 @@ struct Params {
     int sched;       // 0 static, 1 dynamic
     int debug;       // MOE_MK_DEBUG_* bits
     int nR, nTG, nEB, T, nC, NB1, NB2, tpw, S;
+    int reb;         // experts per router task (4 or 16)
     int CT;          // tokens per combine task
     int pf_nt, pf_lines;  // weight prefetch during routing: first gate/up tiles covered, 128-byte lines
     int BM;          // GroupGEMM tile rows (kBM or kWideBM); columns are f / NB1 = d / NB2

@@ -78,7 +78,8 @@ def tile_config(B, k, E, d, f, wide_bn1=128, wide_bn2=256, wide_bm=256):
 def expected_task_counts(hist, B, E, d, f, k):
     BM, NB1, NB2, S = tile_config(B, k, E, d, f)
     mt = int(sum((int(h) + BM - 1) // BM for h in hist))
-    # router tokens per wave
+    # router tokens per wave, and experts per router task
     tpw = 1 if B <= 512 else 8 if E % 4 == 0 and d % 128 == 0 and -(-B // 64) * -(-E // 16) >= 512 else 4
-    return {"route": -(-B // (WAVES * tpw)) * -(-E // 16), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
+    reb = 4 if tpw == 1 and E % 4 == 0 and d % 512 == 0 and -(-B // WAVES) * -(-E // 16) < 64 else 16
+    return {"route": -(-B // (WAVES * tpw)) * -(-E // reb), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
             "gemm1": mt * NB1, "gemm2": mt * S * NB2, "combine": -(-B // (8 if B >= 1024 and k <= 8 else 1 if B <= 64 else 4)) * -(-d // COMBINE_COLS)}

@@ -101,14 +101,16 @@ def test_k_and_e_edges(k, E):
     full_check(x, Wr, bias, W1, W3, W2, k, mk.MOE_MK_SCHED_STATIC, f"k={k} E={E}")
 
 
-@pytest.mark.parametrize("B,d,E", [(13, 512, 20), (70, 1024, 8), (600, 512, 12), (2048, 256, 256), (2100, 384, 252)],
-                         ids=["deep_stages", "deep_stages_two_tiles", "four_tokens_per_wave", "eight_tokens_per_wave",
-                              "eight_tokens_ragged"])
+@pytest.mark.parametrize("B,d,E", [(13, 512, 20), (70, 1024, 8), (512, 4096, 16), (600, 512, 12), (2048, 256, 256),
+                                   (2100, 384, 252)],
+                         ids=["four_experts_ragged", "four_experts_two_groups", "deep_stages", "four_tokens_per_wave",
+                              "eight_tokens_per_wave", "eight_tokens_ragged"])
 def test_router_stage_depths(B, d, E):
-    # d a multiple of 512 with at most 512 tokens: router stages of 512 values; more than
-    # 512 tokens: four tokens per wave, eight once that leaves 512 router tasks (the last
-    # case also has a ragged token group and d not a multiple of 256); E not a multiple
-    # of 16 leaves a ragged expert block
+    # one token per wave: router tasks of 4 experts when 16-expert ones would be fewer than
+    # 64 (d a multiple of 512; E = 20 leaves five blocks), else 16 experts with stages of
+    # 512 values when d > 2048; more than 512 tokens: four tokens per wave, eight once that
+    # leaves 512 router tasks (the last case also has a ragged token group and d not a
+    # multiple of 256); E not a multiple of 16 leaves a ragged expert block
     cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, 128, E, 2, seed=900 + B)
     for sched in SCHEDS:
         full_check(x, Wr, bias, W1, W3, W2, 2, sched, f"router B={B} d={d} E={E} {SNAME[sched]}")
@@ -197,10 +199,10 @@ def test_static_and_dynamic_are_bitwise_identical():
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
-@pytest.mark.parametrize("B,E", [(40, 8), (90, 8), (300, 4), (2048, 256)],
-                         ids=["one_tile", "narrow", "wide", "router_eight_tokens"])
-def test_rest_state_and_task_counts(B, E, sched):
-    d, f = 256, 384
+@pytest.mark.parametrize("B,E,d", [(40, 8, 256), (90, 8, 256), (300, 4, 256), (2048, 256, 256), (40, 12, 512)],
+                         ids=["one_tile", "narrow", "wide", "router_eight_tokens", "router_four_experts"])
+def test_rest_state_and_task_counts(B, E, d, sched):
+    f = 384
     cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, 2, seed=12)
     tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
     layer = mk.MoELayer(E, 2, d, f, tWr, t1, t3, t2, sched=sched, max_batch=B)
