@@ -14,7 +14,13 @@
 //              ("data-dependent task triggering"), and idle workgroups pop from it.
 // The batch size B is a kernel argument: every count after the routing stage (histogram,
 // exp_indptr, tiles per expert) is derived on the device, so one compiled kernel serves
-// every B (section "Core method", symbolic shapes).
+// every B (section "Core method", symbolic shapes).  The kernel is compiled twice, once
+// per GroupGEMM tile shape (narrow tiles, or wide tiles when experts average 128 rows or
+// more), and the host launches the one the forward's shape needs: the wide tiles use
+// nearly every register and are inlined into their instantiation (called out of line,
+// each tile saved and restored about 60 registers per wave through memory), and the
+// narrow instantiation carries none of their code or register pressure.  Either serves
+// every B of its shape without recompiling.
 //
 // Task kinds and their events:
 //   ROUTE(tg,eb)  fp32 router logits for 16 tokens x 16 experts  -> ev_logit[tile]
@@ -1722,7 +1728,7 @@ __device__ __forceinline__ void wout_store(const uint8_t *tile, MK_G uint16_t *d
 }
 
 // Wide gate/up tile: kWideBM rows x kWideBN1 columns of h.
-__device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
+__device__ __forceinline__ void wide_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
     const MK_C Params &P = uni_params(Pa);
     e = uni(e);
     row0 = uni(row0);
@@ -1761,7 +1767,7 @@ __device__ __attribute__((noinline)) void wide_gemm1(const MK_C Params &Pa, int 
 }
 
 // Wide down-projection tile: kWideBM rows x kWideBN columns of y.
-__device__ __attribute__((noinline)) void wide_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
+__device__ __forceinline__ void wide_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
     const MK_C Params &P = uni_params(Pa);
     e = uni(e);
     row0 = uni(row0);
@@ -1814,16 +1820,18 @@ __device__ __attribute__((noinline)) void narrow_gemm2(const MK_C Params &Pa, in
 }
 
 // The tile variant is chosen from the forward's tile shape and the tile's actual rows.
+template <bool WIDE>
 __device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
-    if (P.BM == kWideBM)
+    if constexpr (WIDE)
         wide_gemm1(P, e, row0, nrows, n);
     else if (nrows <= 16)
         narrow_gemm1<16>(P, e, row0, nrows, n);
     else
         narrow_gemm1<64>(P, e, row0, nrows, n);
 }
+template <bool WIDE>
 __device__ __forceinline__ void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n, int sp, int mt) {
-    if (P.BM == kWideBM)
+    if constexpr (WIDE)
         wide_gemm2(P, e, row0, nrows, n);
     else if (nrows <= 16)
         narrow_gemm2<16>(P, e, row0, nrows, n, sp, mt);
@@ -2156,6 +2164,8 @@ __device__ __forceinline__ void route_task_coords(const MK_C Params &P, int g, i
 }
 
 // Runs task g (obtained at time t0).  Returns false when the forward must be abandoned.
+// WIDE: the forward's GroupGEMM tiles are wide (P.BM == kWideBM), else narrow.
+template <bool WIDE>
 __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs, unsigned long long t0) {
     const bool dyn = P.sched != 0;
     if (g < bs.K) {  // ---------------------------------------------------------- ROUTE
@@ -2244,7 +2254,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
             const int e = P.mt_expert[mt];
             if (!dyn && !wg_wait_zero(P, P.ev_exp + e)) return false;
             const unsigned long long t1 = now_ticks();
-            task_gemm1(P, e, P.mt_row0[mt], P.mt_rows[mt], n);
+            task_gemm1<WIDE>(P, e, P.mt_row0[mt], P.mt_rows[mt], n);
             const unsigned long long t2 = now_ticks();
             count_task(P, K_GEMM1);
             // f range sp of this row tile complete: its down-projection tiles are ready
@@ -2257,7 +2267,7 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         const int mt = j / P.NB2, n = j - mt * P.NB2;
         if (!dyn && !wg_wait_zero(P, P.ev_h + mt * P.S + sp)) return false;
         const unsigned long long t1 = now_ticks();
-        task_gemm2(P, P.mt_expert[mt], P.mt_row0[mt], P.mt_rows[mt], n, sp, mt);
+        task_gemm2<WIDE>(P, P.mt_expert[mt], P.mt_row0[mt], P.mt_rows[mt], n, sp, mt);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_GEMM2);
         if (wg_notify(P, P.ctl + CTL_EV_Y, -1) && dyn) wg_push_range(P, bs.C, P.nC);
@@ -2377,6 +2387,8 @@ __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
     return g;
 }
 
+// WIDE: the instantiation for wide GroupGEMM tiles (P.BM == kWideBM), else narrow ones.
+template <bool WIDE>
 __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
     // Parg is the first kernel argument, at offset 0 of the kernel-argument segment: read it
     // there in place rather than from a private copy.
@@ -2409,7 +2421,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
     if (P.sched == 0) {
         // Routing tasks: workgroup w runs g = w, w + G, ... below the GroupGEMM blocks.
         bool ok = true;
-        for (int g = blockIdx.x; ok && g < bs.M1p; g += gridDim.x) ok = run_task(P, g, bs, now_ticks());
+        for (int g = blockIdx.x; ok && g < bs.M1p; g += gridDim.x) ok = run_task<WIDE>(P, g, bs, now_ticks());
         // GroupGEMM and combine positions are claimed per XCD.  Position p belongs to XCD
         // p % 8 (the blocks start at multiples of 8); the workgroups of an XCD (w % 8 == x,
         // as the hardware deals them) take that XCD's positions in increasing order from its
@@ -2425,7 +2437,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
                 const int g = bs.M1p + 8 * g_sm.bcast[3] + x;
                 __syncthreads();
                 if (g >= bs.total) break;
-                if (!run_task(P, g, bs, now_ticks())) break;
+                if (!run_task<WIDE>(P, g, bs, now_ticks())) break;
             }
         }
     } else {
@@ -2433,7 +2445,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
             const unsigned long long t0 = now_ticks();
             const int g = wg_pop(P);
             if (g < 0) break;
-            if (!run_task(P, g, bs, t0)) break;
+            if (!run_task<WIDE>(P, g, bs, t0)) break;
         }
     }
     // Leave: the last workgroup out puts the control block back to its rest state.
@@ -2475,7 +2487,10 @@ __global__ void moe_ws_init_ctl(int *ctl_generic) {
 
 // ------------------------------------------------------------------------------ launch glue
 hipError_t mk_launch(const mk::Params &p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL(mk::moe_megakernel, dim3(grid), dim3(mk::kThreads), 0, stream, p);
+    if (p.BM == mk::kWideBM)
+        hipLaunchKernelGGL(mk::moe_megakernel<true>, dim3(grid), dim3(mk::kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(mk::moe_megakernel<false>, dim3(grid), dim3(mk::kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -2490,5 +2505,11 @@ hipError_t mk_ws_init(void *ws, size_t bytes, hipStream_t stream) {
 }
 
 hipError_t mk_occupancy(int *blocks_per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk::moe_megakernel, mk::kThreads, 0);
+    // both instantiations: the persistent grid must be co-resident for either
+    int narrow = 0, wide = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&narrow, mk::moe_megakernel<false>, mk::kThreads, 0);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&wide, mk::moe_megakernel<true>, mk::kThreads, 0);
+    *blocks_per_cu = narrow < wide ? narrow : wide;
+    return e;
 }
