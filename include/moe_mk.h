@@ -24,7 +24,8 @@
  *   - Functions return a moe_mk_status_t; nothing throws or aborts across the ABI.
  *     Arguments are checked before anything is enqueued.
  *   - The batch size B is symbolic: it is an argument of every forward, never of the
- *     plan, and one compiled kernel serves every B with no recompilation and no graph.
+ *     plan, and the kernel (compiled once per GroupGEMM tile shape, narrow or wide) serves
+ *     every B with no recompilation and no graph.
  */
 #ifndef MOE_MK_H
 #define MOE_MK_H
