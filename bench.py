@@ -242,7 +242,7 @@ def main():
     prefill = B >= 2048
     if prefill:
         roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None}
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(cfg.name, B, args.sched)}
     else:
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic(cfg.name, B, args.sched)}
