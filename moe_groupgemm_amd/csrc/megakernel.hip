@@ -561,8 +561,8 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
     float acc[TPW * EPT];
 #pragma unroll
     for (int i = 0; i < TPW * EPT; ++i) acc[i] = 0.0f;
-    // Software-pipelined: the LDS reads of step sub+1 are issued before the FMAs of step
-    // sub and waited for after them, so the two waves of a SIMD (which leave every stage
+    // Software-pipelined: the LDS reads of the next step (group of steps) are issued before
+    // the FMAs of the current one and waited for after them, so the two waves of a SIMD (which leave every stage
     // barrier together) do not both sit out the LDS latency.  The reads of a stage's first
     // step are issued in the previous stage's last step, after that stage's barrier (stage
     // st+1 has landed; every wave has read all of stage st, whose slot then takes the
@@ -597,21 +597,35 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
         wait_vm<0>();
     bare_barrier();
     if (NS - 1 < nst) load(NS - 1, NS - 1);
-    f32x4 wv0[4], wv1[4];
-    uint32_t xr0[TPW], xr1[TPW];
-    reads(0, 0, wv0, xr0);
-    route_wait<TPW, EPT>(wv0, xr0);
+    // With one token per wave a step has only 4 or 16 FMAs per lane, too few to cover an LDS
+    // round trip: U consecutive steps (the same chains, in ascending order) share one.
+    constexpr int UW = TPW == 1 ? (EPT == 4 ? 4 : 2) : 1;
+    constexpr int U = UW <= NSUB / 2 ? UW : NSUB / 2;
+    constexpr int NG = NSUB / U;  // read groups per stage (even: the register sets alternate)
+    static_assert(NSUB % U == 0 && NG % 2 == 0, "whole, even groups per stage");
+    f32x4 wvA[U][4], wvB[U][4];
+    uint32_t xrA[U][TPW], xrB[U][TPW];
+    auto reads_g = [&](int slot, int grp, f32x4 (&wv)[U][4], uint32_t (&xr)[U][TPW]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) reads(slot, grp * U + u, wv[u], xr[u]);
+    };
+    auto wait_g = [&](f32x4 (&wv)[U][4], uint32_t (&xr)[U][TPW]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) route_wait<TPW, EPT>(wv[u], xr[u]);
+    };
+    reads_g(0, 0, wvA, xrA);
+    wait_g(wvA, xrA);
     int slot = 0;
     for (int st = 0; st < nst; ++st) {
         const int nslot = slot == NS - 1 ? 0 : slot + 1;
 #pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) {
-            f32x4 (&wc)[4] = (sub & 1) ? wv1 : wv0;
-            uint32_t (&xc)[TPW] = (sub & 1) ? xr1 : xr0;
-            f32x4 (&wn)[4] = (sub & 1) ? wv0 : wv1;
-            uint32_t (&xn)[TPW] = (sub & 1) ? xr0 : xr1;
-            if (sub + 1 < NSUB) {
-                reads(slot, sub + 1, wn, xn);
+        for (int grp = 0; grp < NG; ++grp) {
+            f32x4 (&wc)[U][4] = (grp & 1) ? wvB : wvA;
+            uint32_t (&xc)[U][TPW] = (grp & 1) ? xrB : xrA;
+            f32x4 (&wn)[U][4] = (grp & 1) ? wvA : wvB;
+            uint32_t (&xn)[U][TPW] = (grp & 1) ? xrA : xrB;
+            if (grp + 1 < NG) {
+                reads_g(slot, grp + 1, wn, xn);
             } else {
                 if (st + 1 < nst) {
                     if (st + NS - 1 < nst)
@@ -621,13 +635,14 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
                     bare_barrier();
                     if (st + NS < nst) load(st + NS, slot);
                 }
-                reads(nslot, 0, wn, xn);
+                reads_g(nslot, 0, wn, xn);
             }
             __builtin_amdgcn_sched_barrier(0);
-            fmas(wc, xc);
+#pragma unroll
+            for (int u = 0; u < U; ++u) fmas(wc[u], xc[u]);
             pin_acc(acc);
             __builtin_amdgcn_sched_barrier(0);
-            route_wait<TPW, EPT>(wn, xn);
+            wait_g(wn, xn);
         }
         slot = nslot;
     }
