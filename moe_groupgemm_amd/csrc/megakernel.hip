@@ -899,14 +899,23 @@ __device__ __attribute__((noinline)) void task_topk(const MK_C Params &Pa, int t
 }
 
 // ------------------------------------------------------------------------------ SCAN
+// Exclusive prefix sum of v over the workgroup's threads (and the total).  The wave's
+// inclusive scan is done with DPP moves, no LDS round trips: within each row of 16 lanes the
+// sums of the previous 1, 2, 4, 8 lanes (row_shr; lanes without a source add 0), then lane 15
+// of rows 0 and 2 into rows 1 and 3 (row_bcast:15) and lane 31 into rows 2 and 3
+// (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
+    return x;
+}
 __device__ __forceinline__ int block_excl_scan(int v, int *part, int *total) {
     const int lane = lane_id(), w = wave_id();
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == 63) part[w] = x;
     __syncthreads();
     int pre = 0, tot = 0;
