@@ -1824,10 +1824,10 @@ __device__ __forceinline__ void wide_gemm2(const MK_C Params &Pa, int e, int row
     wout_store<BN>(tile, P.y + (size_t)row0 * P.d + (size_t)n * BN, (size_t)P.d, nrows);
 }
 
-// Narrow GEMM tiles as functions of their own, each called straight from the task loop: a
-// called function saves the callee-saved registers it uses (about 60 here) to scratch and
-// restores them on return, so one call level per tile rather than a dispatcher around the
-// tile function halves that traffic.
+// Narrow GEMM tiles as functions of their own, each called straight from the task loop.
+// They fit in the caller-saved registers, so a call saves and restores nothing (a function
+// that uses callee-saved registers stores them to scratch memory and reloads them on every
+// call; the wide tiles, which need nearly all registers, are inlined for that reason).
 // GEMM1 tile: h[rows, n0:n0+128] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
 // where row p of the tile is token perm[p] / k of x; AR = staged A rows (16 or 64).
 template <int AR>
