@@ -35,6 +35,12 @@ def parse():
                     "per-task-kind timings to stderr")
     ap.add_argument("--copy-kernel", action="store_true",
                     help="after timing, run one 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--flush", choices=["read", "write"], default=None,
+                    help="also time launches each preceded by a 1 GiB read (or write) of a scratch buffer, "
+                    "which evicts the Infinity Cache; reported under 'cold' (a write also leaves its dirty "
+                    "lines to be written back during the next launch)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the box's achievable copy bandwidth and bf16 GEMM rate")
     return ap.parse_args()
 
 
@@ -104,6 +110,42 @@ def copy_calibration(nbytes=1 << 30):
     b.copy_(a)
     torch.cuda.synchronize()
     return nbytes
+
+
+def achievable_peaks(dev, reps=10):
+    """What this machine reaches on plain library work: a 1 GiB device-to-device copy (bytes read
+    plus written per second) and an 8192^3 bf16 matrix product (hipBLASLt through torch)."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * n * reps / (s.elapsed_time(e) / 1e3) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    y = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    z = torch.empty(m, m, dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        torch.mm(x, y, out=z)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        torch.mm(x, y, out=z)
+    e.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2.0 * m ** 3 * reps / (s.elapsed_time(e) / 1e3) / 1e12
+    del x, y, z
+    torch.cuda.empty_cache()
+    return copy_gbs, gemm_tflops
 
 
 def trace_report(layer, x, out, B):
@@ -261,6 +303,32 @@ def main():
         "grid": mk.moe_mk_plan_info(layer.plan, "grid"),
         "cpu_baseline": None,
     }
+    if args.flush:
+        # the same launches, each after a 1 GiB write that evicts the Infinity Cache, so the
+        # weights come from HBM even where the activated ones would fit in the cache
+        scratch = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+        sink = torch.empty(1, dtype=torch.float32, device=dev)
+        cold_ms = []
+        for i in range(min(args.steps, 10)):
+            if args.flush == "write":
+                scratch.fill_(float(i))
+            else:
+                torch.sum(scratch, dim=0, keepdim=True, out=sink)
+            s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            layer(tx, out)
+            e0.record(stream)
+            torch.cuda.synchronize()
+            cold_ms.append(s0.elapsed_time(e0))
+        del scratch, sink
+        cms = float(np.median(cold_ms))
+        line["cold"] = {"flush": args.flush, "kernel_ms_median": cms, "kernel_ms_min": float(np.min(cold_ms)),
+                        "hbm_frac": alg_bytes / (cms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                        "mfma_frac": flops / (cms / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
+    if not args.no_peaks:
+        copy_gbs, gemm_tflops = achievable_peaks(dev)
+        line["achievable"] = {"copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,
+                              "hbm_frac_of_copy": gbs / copy_gbs, "mfma_frac_of_gemm": tflops / gemm_tflops}
     if args.trace:
         trace_report(layer, tx, out, B)
     if not args.no_cpu_baseline:
