@@ -514,7 +514,7 @@ __device__ __forceinline__ void route_wait(f32x4 (&wv)[4], uint32_t (&xr)[TPW]) 
 }
 
 template <int TPW, int RPS, int EPT = 16>
-__device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int b0, int e0) {
+__device__ __forceinline__ void route_tile_body(const MK_C Params &Pa, int b0, int e0) {
     const MK_C Params &P = uni_params(Pa);
     using C = RouteCfg<TPW, RPS, EPT>;
     static_assert(EPT == 16 || (EPT == 4 && TPW == 1 && RPS == 512), "router block shapes");
@@ -650,6 +650,10 @@ __device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int 
     __syncthreads();  // the ring may be reused by the next task
     route_write<TPW, EPT>(P, acc, b0 + w * TPW, e0);
 }
+template <int TPW, int RPS, int EPT = 16>
+__device__ __attribute__((noinline)) void route_tile(const MK_C Params &Pa, int b0, int e0) {
+    route_tile_body<TPW, RPS, EPT>(Pa, b0, e0);
+}
 
 // Router wave for E not a multiple of 4: plain scalar loads, same summation order.
 __device__ __attribute__((noinline)) void route_wave_scalar(const MK_C Params &Pa, int b0, int e0) {
@@ -674,8 +678,11 @@ __device__ __attribute__((noinline)) void route_wave_scalar(const MK_C Params &P
 
 // Router task (tg, eb): tokens [kWaves*tpw*tg, +kWaves*tpw), wave w taking tpw of them,
 // experts [reb*eb, +reb) (reb = 16, or 4 at small batches).
-__device__ __attribute__((noinline)) void task_route(const MK_C Params &Pa, int tg, int eb) {
-    const MK_C Params &P = uni_params(Pa);
+// INL: the eight-tokens-per-wave tile (nearly every register) is inlined instead of called,
+// so it saves no registers through memory; used by the wide-tile instantiation, where large
+// batches route (the other tiles fit in the caller-saved registers and stay calls).
+template <bool INL>
+__device__ __forceinline__ void task_route_body(const MK_C Params &P, int tg, int eb) {
     const int e0 = eb * P.reb;
     if (P.reb == 4) {  // one token per wave, d % 512 == 0, E % 4 == 0
         route_tile<1, 512, 4>(P, tg * kWaves, e0);
@@ -692,13 +699,19 @@ __device__ __attribute__((noinline)) void task_route(const MK_C Params &Pa, int 
         else
             route_tile<1, 128>(P, tg * kWaves, e0);
     } else if (P.tpw == 8) {  // d % 128 == 0
-        route_tile<8, 128>(P, tg * kWaves * 8, e0);
+        if constexpr (INL)
+            route_tile_body<8, 128>(P, tg * kWaves * 8, e0);
+        else
+            route_tile<8, 128>(P, tg * kWaves * 8, e0);
     } else {
         if (P.d % 256 == 0)
             route_tile<4, 256>(P, tg * kWaves * 4, e0);
         else
             route_tile<4, 128>(P, tg * kWaves * 4, e0);
     }
+}
+__device__ __attribute__((noinline)) void task_route(const MK_C Params &Pa, int tg, int eb) {
+    task_route_body<false>(uni_params(Pa), tg, eb);
 }
 
 // ------------------------------------------------------------------------------ TOPK
@@ -2195,7 +2208,10 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
     if (g < bs.K) {  // ---------------------------------------------------------- ROUTE
         int tg, eb;
         route_task_coords(P, g, tg, eb);
-        task_route(P, tg, eb);
+        if constexpr (WIDE)
+            task_route_body<true>(P, tg, eb);
+        else
+            task_route(P, tg, eb);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_ROUTE);
         const int t = tg / route_groups_per_tile(P);
