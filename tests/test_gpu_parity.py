@@ -263,7 +263,11 @@ def test_uninitialised_workspace_is_reported():
 # ------------------------------------------------------------------------------ full-size configurations
 
 def _full_config(name, sched, sample):
-    cfg = CONFIGS[name]
+    return _full_config_of(CONFIGS[name], sched, sample)
+
+
+def _full_config_of(cfg, sched, sample):
+    name = cfg.name
     log(f"config {name} sched={SNAME[sched]}: generating inputs")
     tWr, tb, t1, t3, t2 = device_weights(cfg)
     Wr, bias = make_wr(cfg), make_bias(cfg)
@@ -322,3 +326,18 @@ def test_config_deepseek_zipf(sched):
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
 def test_config_prefill(sched):
     _full_config("prefill", sched, sample=8)
+
+
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+def test_large_batch_prefill_shape(sched):
+    # four times the prefill batch (131072 routed rows): queue capacity, the per-XCD lists,
+    # eight-token router tasks and wide tiles at a size well past the benchmark's
+    cfg = Config("prefill_x4", d=2048, f=768, E=128, k=8, batches=(16384,), seed=606)
+    _full_config_of(cfg, sched, sample=6)
+
+
+def test_max_experts_and_top_k_wide():
+    # the largest E and k the plan accepts, at a batch whose 128 rows per expert take wide tiles
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(2048, 256, 128, 256, 16, seed=707)
+    for sched in SCHEDS:
+        full_check(x, Wr, bias, W1, W3, W2, 16, sched, f"E=256 k=16 B=2048 {SNAME[sched]}")
