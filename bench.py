@@ -303,9 +303,12 @@ def main():
         "grid": mk.moe_mk_plan_info(layer.plan, "grid"),
         "cpu_baseline": None,
     }
+    if args.trace:  # first, while nothing else has run on the device since the timed launches
+        trace_report(layer, tx, out, B)
     if args.flush:
-        # the same launches, each after a 1 GiB write that evicts the Infinity Cache, so the
-        # weights come from HBM even where the activated ones would fit in the cache
+        # the same launches, each after a 1 GiB read (or write) of a scratch buffer that evicts
+        # the Infinity Cache, so the weights come from HBM even where the activated ones would
+        # fit in the cache
         scratch = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
         sink = torch.empty(1, dtype=torch.float32, device=dev)
         cold_ms = []
@@ -329,8 +332,6 @@ def main():
         copy_gbs, gemm_tflops = achievable_peaks(dev)
         line["achievable"] = {"copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,
                               "hbm_frac_of_copy": gbs / copy_gbs, "mfma_frac_of_gemm": tflops / gemm_tflops}
-    if args.trace:
-        trace_report(layer, tx, out, B)
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         sample = args.cpu_sample or max(1, min(B, int(2.0e10 / (6 * cfg.k * cfg.d * cfg.f))))
