@@ -23,13 +23,13 @@
 // every B of its shape without recompiling.
 //
 // Task kinds and their events:
-//   ROUTE(tg,eb)  fp32 router logits for 16 tokens x 16 experts  -> ev_logit[tile]
+//   ROUTE(tg,eb)  fp32 router logits, 8*tpw tokens x reb experts   -> ev_logit[tile]
 //   TOPK(t)       top-k + softmax + tile histogram, 64 tokens    -> ev_topk
 //   SCAN          hist, exp_indptr, per-tile offsets, row tiles; arms ev_exp/ev_h/ev_y -> ev_scan
-//   GROUP(t)      stable ranks, perm/inv, gather of token rows    -> ev_exp[e] -= rows of e
+//   GROUP(t)      stable ranks -> perm/inv (GEMM1 gathers the rows) -> ev_exp[e] -= rows of e
 //   GEMM1(mt,n)   gate/up GroupGEMM tile + SwiGLU -> h            -> ev_h[mt,s] (s: n's f range)
 //   GEMM2(mt,s,n) down GroupGEMM tile over f range s -> y[s]      -> ev_y
-//   COMBINE(c)    out[b] = sum_i w[b,i] y[inv[b,i]] for 16 tokens
+//   COMBINE(c)    out[b] = sum_i w[b,i] y[inv[b,i]] for 1, 4 or 8 tokens
 #include <hip/hip_runtime.h>
 
 #include "mk_common.h"
@@ -409,16 +409,18 @@ __device__ __forceinline__ void route_write(const MK_C Params &P, float (&acc)[T
 }
 
 // Router tile through LDS (E a multiple of 4).  The workgroup's kWaves*TPW tokens (wave w
-// owns TPW of them) and 16 experts share every staged slice: per RPS values of j, the
-// RPS x 16 block of Wr (each wave moving RPS/8 of its rows, 1 KB per load) and the tokens'
-// RPS x values (each wave moving its own), in a ring of as many stages as LDS holds (up to
-// 16), filled by global_load_lds.  Deeper stages (RPS = 512 with one token per wave) move
+// owns TPW of them) and EPT experts (16, or 4 when a small batch spreads its router over
+// more workgroups) share every staged slice: per RPS values of j, the RPS x EPT block of Wr
+// (each wave moving 1/8 of it, 1 KB per load) and the tokens' RPS x values (each wave
+// moving its own), in a ring of as many stages as LDS holds (up to 16), filled by
+// global_load_lds.  Deeper stages (RPS = 512 with one token per wave) move
 // more bytes per ring iteration, which sets a workgroup's streaming rate; with four tokens
 // per wave the stages hold 256 values when d allows.  Lane l
 // accumulates chain l (j = l, l+64, ... in order) of every (token, expert) pair of its
 // wave; a stage holds RPS/64 consecutive steps of every chain.
-//   Wr stage in LDS: [RPS rows][4 chunks of 4 experts]; chunk c of row r at c ^ rswz(r),
-//     so the 16 rows a quarter-wave reads fall on distinct 16-byte bank groups.
+//   Wr stage in LDS: [RPS rows][EPT/4 chunks of 4 experts]; with EPT = 16 chunk c of row r
+//     sits at c ^ rswz(r), so the 16 rows a quarter-wave reads fall on distinct 16-byte
+//     bank groups (one chunk per row needs no swizzle).
 //   x stage: per wave, TPW blocks of 2*RPS bytes, each one token's RPS bf16 values.
 // Tokens past B and experts past E load clamped (valid) addresses; their sums are never
 // written.
