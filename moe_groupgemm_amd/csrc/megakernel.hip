@@ -19,8 +19,9 @@
 // more), and the host launches the one the forward's shape needs: the wide tiles use
 // nearly every register and are inlined into their instantiation (called out of line,
 // each tile saved and restored about 60 registers per wave through memory), and the
-// narrow instantiation carries none of their code or register pressure.  Either serves
-// every B of its shape without recompiling.
+// narrow instantiation carries none of their code or register pressure (the wide one
+// calls the out-of-line narrow tiles for row tiles of a few rows).  Either serves every B
+// of its shape without recompiling.
 //
 // Task kinds and their events:
 //   ROUTE(tg,eb)  fp32 router logits, 8*tpw tokens x reb experts   -> ev_logit[tile]
@@ -1859,9 +1860,16 @@ __device__ __attribute__((noinline)) void narrow_gemm2(const MK_C Params &Pa, in
 }
 
 // The tile variant is chosen from the forward's tile shape and the tile's actual rows.
+// A wide-shape task whose row tile holds at most kBM rows (the last row tile of an expert
+// with a few rows past a multiple of kWideBM) streams its whole weight tile for those few
+// rows, so its time is set by the weight bytes it keeps in flight.  The narrow tile code
+// keeps about twice as many weight bytes in flight per stage ring, so such a task runs as
+// narrow tiles over the same columns (one for gate/up, kWideBN / kBN for the down
+// projection); the output and its events are the same.
 template <bool WIDE>
 __device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
-    if constexpr (WIDE)
+    static_assert(kWideBN1 == kBN, "a wide gate/up tile spans one narrow tile's columns");
+    if (WIDE && nrows > kBM)
         wide_gemm1(P, e, row0, nrows, n);
     else if (nrows <= 16)
         narrow_gemm1<16>(P, e, row0, nrows, n);
@@ -1870,12 +1878,23 @@ __device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0
 }
 template <bool WIDE>
 __device__ __forceinline__ void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n, int sp, int mt) {
-    if constexpr (WIDE)
-        wide_gemm2(P, e, row0, nrows, n);
-    else if (nrows <= 16)
+    if constexpr (WIDE) {
+        static_assert(kWideBN % kBN == 0, "a wide down tile spans whole narrow tiles");
+        if (nrows > kBM) {
+            wide_gemm2(P, e, row0, nrows, n);
+            return;
+        }
+        for (int q = 0; q < kWideBN / kBN; ++q) {  // S = 1 with wide tiles
+            if (nrows <= 16)
+                narrow_gemm2<16>(P, e, row0, nrows, (kWideBN / kBN) * n + q, 0, mt);
+            else
+                narrow_gemm2<64>(P, e, row0, nrows, (kWideBN / kBN) * n + q, 0, mt);
+        }
+    } else if (nrows <= 16) {
         narrow_gemm2<16>(P, e, row0, nrows, n, sp, mt);
-    else
+    } else {
         narrow_gemm2<64>(P, e, row0, nrows, n, sp, mt);
+    }
 }
 
 // ------------------------------------------------------------------------------ COMBINE

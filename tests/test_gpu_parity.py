@@ -155,6 +155,33 @@ def test_wide_tiles_constant_input(sched):
     full_check(x, Wr, bias, W1, W3, W2, 2, sched, "wide constant input")
 
 
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+def test_wide_forward_thin_row_tiles(sched):
+    # Routing set by the input: logit e of token b is x[b, e] (Wr is the identity on the
+    # first E values of j), so each expert receives an exact row count.  In this wide-tile
+    # forward the row tiles of at most 64 rows (1, 16, 17, 64 rows past 256; experts of 11
+    # and 68 rows) run as narrow tiles, the others (65 past 256, 68 alone) as wide tiles.
+    counts = [257, 272, 273, 320, 11, 68, 321]
+    E, k, d, f = len(counts), 2, 512, 256
+    slots = np.repeat(np.arange(E), counts)
+    B = len(slots) // k
+    assert tile_config(B, k, E, d, f)[0] == 256
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=1700)
+    x[:, :E] = 0
+    x[np.arange(B), slots[:B]] = 0x4040       # bf16 3.0: slot 0
+    x[np.arange(B), slots[B:]] = 0x3FC0       # bf16 1.5: slot 1 (a different expert)
+    assert np.all(slots[:B] != slots[B:])
+    Wr[:] = 0
+    Wr[np.arange(E), np.arange(E)] = 1.0
+    log(f"wide forward with thin row tiles B={B} counts={counts} sched={SNAME[sched]}")
+    ref = oracle.forward(x, Wr, bias, W1, W3, W2, k)
+    assert np.array_equal(ref["hist"], counts)
+    layer, out, got = run_small(x, Wr, bias, W1, W3, W2, k, sched)
+    check_routing(got, ref, B, E)
+    check_out(out, ref["out"], "wide forward, thin row tiles")
+    layer.close()
+
+
 def test_wide_tiles_static_dynamic_identical():
     cfg, x, Wr, bias, W1, W3, W2 = small_case(300, 256, 384, 4, 2, seed=1600)
     outs = []
