@@ -41,7 +41,8 @@ typedef struct moe_mk_plan_s *moe_mk_plan_t;  /* opaque, host-side, immutable af
 
 /* Task scheduling ("Event Tensor", Core method, static and dynamic scheduling). */
 typedef enum {
-    MOE_MK_SCHED_STATIC = 0,  /* every persistent workgroup walks a fixed share of the task list and spin-waits on events */
+    MOE_MK_SCHED_STATIC = 0,  /* persistent workgroups take tasks from fixed per-XCD lists (then, with narrow tiles, what
+                                 the other XCDs' lists have left) and spin-wait on events */
     MOE_MK_SCHED_DYNAMIC = 1  /* the task that fires an event pushes its consumers onto a shared queue; idle workgroups pop */
 } moe_mk_sched_t;
 

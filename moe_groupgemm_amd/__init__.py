@@ -29,7 +29,7 @@ TASK_KINDS = ("route", "topk", "scan", "group", "gemm1", "gemm2", "combine")
 # control block words (see moe_mk_routing_view)
 CTL_WORDS = 512
 CTL = {"epoch": 0, "exit": 1, "err": 2, "ev_topk": 5, "ev_scan": 6, "magic": 8, "mt_total": 9,
-       "qhead": 32, "qtail": 64, "pf": 96, "ev_y": 160, "dbg": 192, "xq": 256}
+       "qhead": 32, "qtail": 64, "pf": 96, "cq": 128, "ev_y": 160, "dbg": 192, "xq": 256}
 
 _lib = None
 

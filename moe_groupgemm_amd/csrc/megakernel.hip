@@ -5,8 +5,9 @@
 // are event counters in device memory.  notify = atomic decrement; wait = spin until the
 // counter is zero.  Two schedulers run the same graph:
 //   static  -- the routing tasks go to workgroups round-robin (workgroup w runs g = w,
-//              w + G, ...); the GroupGEMM and combine tasks are partitioned over the 8 XCDs
-//              and each XCD's workgroups take its list in order; tasks spin-wait on their
+//              w + G, ...); the GroupGEMM tasks are partitioned over the 8 XCDs and each
+//              XCD's workgroups take its list in order, then what the other XCDs have left;
+//              the combine tasks come last from one shared counter; tasks spin-wait on their
 //              events (every list is in topological order, so the smallest unfinished task
 //              can always run: no deadlock with a co-resident grid);
 //   dynamic -- the router tasks are implicitly queued; every other task is pushed onto a
@@ -111,7 +112,8 @@ __shared__ Smem g_sm;
 //
 // GroupGEMM blocks start at multiples of 8 and are padded to multiples of 8 (padding
 // positions are empty tasks).  Workgroups are dealt to the 8 XCDs round-robin, so in the
-// static schedule position p of a block runs on XCD p % 8.  Static mode therefore maps
+// static schedule position p of a block runs on XCD p % 8 (unless another XCD takes it once
+// its own positions are done).  Static mode therefore maps
 // position p to the linear tile q = (p % 8) * (size / 8) + p / 8: each XCD works through
 // one contiguous eighth of the tiles (row tile major), and the tiles sharing a row tile's
 // activations or an expert's weight columns run together on the same L2.  Dynamic mode
@@ -2483,21 +2485,56 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
         // Routing tasks: workgroup w runs g = w, w + G, ... below the GroupGEMM blocks.
         bool ok = true;
         for (int g = blockIdx.x; ok && g < bs.M1p; g += gridDim.x) ok = run_task<WIDE>(P, g, bs, now_ticks());
-        // GroupGEMM and combine positions are claimed per XCD.  Position p belongs to XCD
-        // p % 8 (the blocks start at multiples of 8); the workgroups of an XCD (w % 8 == x,
-        // as the hardware deals them) take that XCD's positions in increasing order from its
-        // claim counter, so tiles adjacent in the list start together and share operands in
-        // L2.  Each XCD's list is in topological order, so the smallest unfinished task of
-        // the forward always has its inputs done or in progress.
+        // GroupGEMM positions are claimed per XCD.  Position p belongs to XCD p % 8 (the
+        // blocks start at multiples of 8); the workgroups of an XCD (w % 8 == x, as the
+        // hardware deals them) take that XCD's positions in increasing order from its claim
+        // counter, so tiles adjacent in the list start together and share operands in L2.
+        // Each XCD's list is in topological order, so the smallest unfinished task of the
+        // forward always has its inputs done or in progress.
+        // Narrow tiles: once its XCD's list has no GroupGEMM position left, a workgroup
+        // takes unclaimed GroupGEMM positions of the other XCDs from their counters (thread
+        // 0 looks at a counter first and claims only while it shows a GroupGEMM position),
+        // so that the XCDs finish the GroupGEMM phase together even when skewed routing
+        // gives them unequal work.  Combine tasks, which wait for every down-projection tile
+        // and read rows written on every XCD, are then claimed from one counter shared by
+        // all workgroups; a workgroup reaches them only when no GroupGEMM position is left
+        // unclaimed.  A claim is exclusive whoever makes it and a claimed position is always
+        // run, so every task runs exactly once.  (One call site runs the tasks: the task code
+        // is large, and a second inlined copy slowed every tile.)  Wide tiles, and forwards
+        // of fewer than two GroupGEMM positions per workgroup, keep every position, combine
+        // included, on its own XCD: there taking other XCDs' tiles made the forward slower.
         if (ok && wg_wait_zero_prefetching(P, P.ctl + CTL_EV_SCAN)) {
             complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
             const int x = blockIdx.x & 7;
+            // (a forward of a few tiles per workgroup gains nothing, and its idle workgroups
+            // would only load the counters that the busy ones claim from)
+            const bool steal = !WIDE && bs.C - bs.M1p >= 2 * (int)gridDim.x;
+            int y = 0;  // list of XCD x + y: 0 its own, 1..7 the others, 8: combine tasks
             for (;;) {
-                if (threadIdx.x == 0) g_sm.bcast[3] = add_relaxed(P.ctl + CTL_XQ + 32 * x, 1);
-                __syncthreads();
-                const int g = bs.M1p + 8 * g_sm.bcast[3] + x;
-                __syncthreads();
-                if (g >= bs.total) break;
+                int g;
+                if (!steal || y < 8) {
+                    const int xs = (x + y) & 7;
+                    if (threadIdx.x == 0) {
+                        MK_G int *ctr = P.ctl + CTL_XQ + 32 * xs;
+                        g_sm.bcast[3] = y == 0 || bs.M1p + 8 * ld_relaxed(ctr) + xs < bs.C ? add_relaxed(ctr, 1) : -1;
+                    }
+                    __syncthreads();
+                    const int c = g_sm.bcast[3];
+                    __syncthreads();
+                    g = bs.M1p + 8 * c + xs;
+                    if (!steal) {
+                        if (g >= bs.total) break;
+                    } else if (c < 0 || g >= bs.C) {  // no GroupGEMM position left in this list
+                        ++y;
+                        continue;
+                    }
+                } else {
+                    if (threadIdx.x == 0) g_sm.bcast[3] = add_relaxed(P.ctl + CTL_CQ, 1);
+                    __syncthreads();
+                    g = bs.C + g_sm.bcast[3];
+                    __syncthreads();
+                    if (g >= bs.total) break;
+                }
                 if (!run_task<WIDE>(P, g, bs, now_ticks())) break;
             }
         }
@@ -2520,6 +2557,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
                 st_relaxed(P.ctl + CTL_QTAIL, 0);
                 st_relaxed(P.ctl + CTL_PF, 0);
                 st_relaxed(P.ctl + CTL_EV_SCAN, 1);
+                st_relaxed(P.ctl + CTL_CQ, 0);
                 for (int x = 0; x < 8; ++x) st_relaxed(P.ctl + CTL_XQ + 32 * x, 0);
             }
             st_relaxed(P.ctl + CTL_EXIT, 0);

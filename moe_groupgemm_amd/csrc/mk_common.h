@@ -44,6 +44,7 @@ enum CtlWord {
     CTL_QHEAD = 32,     // dynamic queue: next ticket
     CTL_QTAIL = 64,     // dynamic queue: slots reserved by pushers
     CTL_PF = 96,        // weight prefetch: lines claimed (rest 0)
+    CTL_CQ = 128,       // static schedule: combine tasks claimed (rest 0)
     CTL_EV_Y = 160,     // event: all down-projection tiles done
     CTL_DBG = 192,      // 8 per-kind task counters (accumulate across forwards)
     CTL_XQ = 256,       // static schedule: claim counter of XCD x's GroupGEMM list at 256 + 32x

@@ -245,6 +245,7 @@ def test_rest_state_and_task_counts(B, E, d, sched):
     assert c[C["qhead"]] == c[C["qtail"]] == 0        # queue at rest
     assert c[C["pf"]] == 0                             # weight-prefetch claims at rest
     assert all(c[C["xq"] + 32 * x] == 0 for x in range(8))  # static per-XCD claim counters at rest
+    assert c[C["cq"]] == 0                             # static combine claim counter at rest
     assert c[C["ev_topk"]] == 0 and c[C["ev_scan"]] == 1 and c[C["ev_y"]] == 0  # events at rest
     hist = routing_numpy(layer, B)["hist"]
     exp = expected_task_counts(hist, B, E, d, f, 2)
