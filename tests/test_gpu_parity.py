@@ -226,10 +226,13 @@ def test_static_and_dynamic_are_bitwise_identical():
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
-@pytest.mark.parametrize("B,E,d", [(40, 8, 256), (90, 8, 256), (300, 4, 256), (2048, 256, 256), (40, 12, 512)],
-                         ids=["one_tile", "narrow", "wide", "router_eight_tokens", "router_four_experts"])
-def test_rest_state_and_task_counts(B, E, d, sched):
-    f = 384
+@pytest.mark.parametrize("B,E,d,f", [(40, 8, 256, 384), (90, 8, 256, 384), (300, 4, 256, 384), (2048, 256, 256, 384),
+                                     (40, 12, 512, 384), (256, 64, 512, 1024)],
+                         ids=["one_tile", "narrow", "wide", "router_eight_tokens", "router_four_experts",
+                              "static_takes_other_xcds"])
+def test_rest_state_and_task_counts(B, E, d, f, sched):
+    # the last case has more than two GroupGEMM positions per workgroup (static: workgroups
+    # take other XCDs' positions, combine tasks from one counter); every task runs once
     cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, 2, seed=12)
     tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
     layer = mk.MoELayer(E, 2, d, f, tWr, t1, t3, t2, sched=sched, max_batch=B)
