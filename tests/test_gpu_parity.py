@@ -326,6 +326,29 @@ def _full_config_of(cfg, sched, sample):
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+def test_threshold_batches_one_plan(sched):
+    # one plan and one workspace, batch sizes on both sides of every batch-size switch:
+    # one routing tile or several (64/65), tokens per router wave (512/513), narrow or wide
+    # tiles (B*k = 1022/1024 rows for 8 experts: 511/512), tokens per combine task
+    # (1023/1024), then back to the smallest; every output is compared in full
+    E, k, d, f = 8, 2, 256, 256
+    Bmax = 1025
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(Bmax, d, f, E, k, seed=1900)
+    tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
+    layer = mk.MoELayer(E, k, d, f, tWr, t1, t3, t2, router_bias=tb, sched=sched, max_batch=Bmax)
+    for B in (64, 65, 511, 512, 513, 1023, 1024, 1025, 1):
+        log(f"threshold batch B={B} tiles={'wide' if tile_config(B, k, E, d, f)[0] == 256 else 'narrow'} "
+            f"sched={SNAME[sched]}")
+        out = layer(tx[:B])
+        torch.cuda.synchronize()
+        assert layer.error() == 0
+        ref = oracle.forward(x[:B], Wr, bias, W1, W3, W2, k)
+        check_routing(routing_numpy(layer, B), ref, B, E)
+        check_out(out.float().cpu().numpy(), ref["out"], f"threshold B={B}")
+    layer.close()
+
+
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
 def test_config_mixtral_decode(sched):
     _full_config("mixtral_decode", sched, sample=8)
 
