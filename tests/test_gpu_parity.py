@@ -278,6 +278,32 @@ def test_watchdog_turns_a_lost_notify_into_an_error(sched):
     layer.close()
 
 
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+def test_nonfinite_input_is_reported(sched):
+    # a NaN and an infinity in x make router logits non-finite: the forward ends with
+    # MOE_MK_ERR_NONFINITE in the error word, and after re-initialising the workspace a
+    # clean input runs exactly as usual
+    B = 90
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, 256, 256, 8, 2, seed=23)
+    bad = x.copy()
+    bad[5, 17] = 0x7FC0   # bf16 quiet NaN
+    bad[70, 3] = 0x7F80   # bf16 +infinity
+    tx, tWr, tb, t1, t3, t2 = dev_inputs(bad, Wr, bias, W1, W3, W2)
+    layer = mk.MoELayer(8, 2, 256, 256, tWr, t1, t3, t2, sched=sched, max_batch=B)
+    layer(tx)
+    torch.cuda.synchronize()
+    assert layer.error() & mk.MOE_MK_ERR_NONFINITE
+    layer.reinit()
+    clean = to_torch_bf16(x).cuda()
+    out = layer(clean)
+    torch.cuda.synchronize()
+    assert layer.error() == 0
+    ref = oracle.forward(x, Wr, bias, W1, W3, W2, 2)
+    check_routing(routing_numpy(layer, B), ref, B, 8)
+    check_out(out.float().cpu().numpy(), ref["out"], "after a non-finite input")
+    layer.close()
+
+
 def test_uninitialised_workspace_is_reported():
     cfg, x, Wr, bias, W1, W3, W2 = small_case(8, 128, 128, 4, 2, seed=22)
     tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
