@@ -58,6 +58,8 @@ def _load():
     lib.oracle_expert_row.argtypes = [u16p, u16p, u16p, u16p, i64, i64, f64p]
     lib.oracle_moe_token.argtypes = [u16p, i64, ctypes.c_void_p, f64p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, i64, i64, f64p]
+    lib.oracle_moe_tokens.argtypes = [u16p, i64, ctypes.c_void_p, i64, i64, ctypes.c_void_p, f64p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, i64, f64p]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     del i32p
@@ -164,18 +166,20 @@ def expert_row(xrow, W1e, W3e, W2e) -> np.ndarray:
 
 
 def moe_tokens(x, tokens, idx, w, experts, d: int, f: int) -> np.ndarray:
-    """Layer output (fp64 [len(tokens), d]) for the listed tokens.
+    """Layer output (fp64 [len(tokens), d]) for the listed tokens, computed token-parallel.
 
     ``experts`` is either a tuple of full arrays (W1 [E,d,f], W3 [E,d,f], W2 [E,f,d]) or a
-    callable ``e -> (W1e, W3e, W2e)`` that returns one expert's arrays.
+    callable ``e -> (W1e, W3e, W2e)`` that returns one expert's arrays.  Each token's values
+    are the same whatever the thread count (``oracle_moe_tokens``).
     """
     lib = _load()
     x = np.ascontiguousarray(x, dtype=np.uint16)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     w = np.ascontiguousarray(w, dtype=np.float64)
     k = idx.shape[1]
-    tokens = [int(t) for t in tokens]
-    used = sorted({int(e) for t in tokens for e in idx[t]})
+    toks = np.ascontiguousarray(np.asarray([int(t) for t in tokens], dtype=np.int64))
+    assert toks.size == 0 or (toks.min() >= 0 and toks.max() < min(x.shape[0], idx.shape[0]))
+    used = sorted({int(e) for e in idx[toks].reshape(-1)}) if toks.size else []
     E = int(max(used)) + 1 if used else 1
     keep = {}
     if callable(experts):
@@ -184,23 +188,35 @@ def moe_tokens(x, tokens, idx, w, experts, d: int, f: int) -> np.ndarray:
     else:
         W1, W3, W2 = experts
         for e in used:
-            keep[e] = (W1[e], W3[e], W2[e])
+            keep[e] = tuple(np.ascontiguousarray(a, dtype=np.uint16) for a in (W1[e], W3[e], W2[e]))
     for e, (a1, a3, a2) in keep.items():
         assert a1.shape == (d, f) and a3.shape == (d, f) and a2.shape == (f, d)
-        assert a1.flags.c_contiguous and a3.flags.c_contiguous and a2.flags.c_contiguous
     P = ctypes.c_void_p * E
     t1, t3, t2 = P(), P(), P()
     for e, (a1, a3, a2) in keep.items():
         t1[e], t3[e], t2[e] = a1.ctypes.data, a3.ctypes.data, a2.ctypes.data
-    out = np.empty((len(tokens), d), dtype=np.float64)
-    for r, t in enumerate(tokens):
-        row = np.ascontiguousarray(x[t])
-        ib = np.ascontiguousarray(idx[t])
-        wb = np.ascontiguousarray(w[t])
-        o = np.empty(d, dtype=np.float64)
-        _check(lib.oracle_moe_token(_ptr(row), k, _ptr(ib), _ptr(wb), t1, t3, t2, d, f, _ptr(o)), "moe_token")
-        out[r] = o
+    out = np.empty((toks.size, d), dtype=np.float64)
+    _check(lib.oracle_moe_tokens(_ptr(x), d, _ptr(toks), toks.size, k, _ptr(idx), _ptr(w), t1, t3, t2, f,
+                                 _ptr(out)), "moe_tokens")
     return out
+
+
+def moe_token(xrow, idx_row, w_row, experts, d: int, f: int) -> np.ndarray:
+    """One token's layer output (fp64 [d]) with the expert columns shared over threads
+    (``oracle_moe_token``)."""
+    lib = _load()
+    xrow = np.ascontiguousarray(xrow, dtype=np.uint16)
+    ib = np.ascontiguousarray(idx_row, dtype=np.int32)
+    wb = np.ascontiguousarray(w_row, dtype=np.float64)
+    W1, W3, W2 = experts
+    E = W1.shape[0]
+    keep = [tuple(np.ascontiguousarray(a, dtype=np.uint16) for a in (W1[e], W3[e], W2[e])) for e in range(E)]
+    P = ctypes.c_void_p * E
+    t1, t3, t2 = P(*[a[0].ctypes.data for a in keep]), P(*[a[1].ctypes.data for a in keep]), \
+        P(*[a[2].ctypes.data for a in keep])
+    o = np.empty(d, dtype=np.float64)
+    _check(lib.oracle_moe_token(_ptr(xrow), ib.size, _ptr(ib), _ptr(wb), t1, t3, t2, d, f, _ptr(o)), "moe_token")
+    return o
 
 
 def forward(x, Wr, bias, W1, W3, W2, k):

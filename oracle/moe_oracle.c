@@ -212,51 +212,98 @@ int oracle_permutation(const int32_t *idx, const int32_t *exp_indptr, int64_t B,
  *   h[n] = g[n] / (1 + exp(-g[n])) * u[n]                           (SwiGLU, W1 = gate)
  *   y[j] = sum_n h[n] W2[n,j]                                       (W2: [f, d])
  * x is one bf16 row of length d; y has length d.
+ *
+ * The work is split into blocks of output columns.  Every column is computed by the
+ * same loop (c ascending for g and u, n ascending for y) whichever thread runs its
+ * block, so the result does not depend on how the blocks are shared out.
  */
-int oracle_expert_row(const uint16_t *xrow, const uint16_t *W1e, const uint16_t *W3e,
-                      const uint16_t *W2e, int64_t d, int64_t f, double *y)
+#define ORACLE_COL_BLOCK 256
+
+/* Gate/up columns [n0, n1): g and u (zero on entry) summed over c, then h. */
+static void expert_gateup_block(const uint16_t *xrow, const uint16_t *W1e, const uint16_t *W3e,
+                                int64_t d, int64_t f, int64_t n0, int64_t n1,
+                                double *g, double *u, double *h)
 {
-    if (d <= 0 || f <= 0) return -1;
-    if (!xrow || !W1e || !W3e || !W2e || !y) return -1;
+    for (int64_t c = 0; c < d; ++c) {
+        double xc = (double)bf16_value(xrow[c]);
+        const uint16_t *w1 = W1e + c * f;
+        const uint16_t *w3 = W3e + c * f;
+        for (int64_t n = n0; n < n1; ++n) {
+            g[n] += xc * (double)bf16_value(w1[n]);
+            u[n] += xc * (double)bf16_value(w3[n]);
+        }
+    }
+    for (int64_t n = n0; n < n1; ++n) h[n] = g[n] / (1.0 + exp(-g[n])) * u[n];
+}
+
+/* Down-projection columns [j0, j1): y[j] summed over n. */
+static void expert_down_block(const double *h, const uint16_t *W2e, int64_t d, int64_t f,
+                              int64_t j0, int64_t j1, double *y)
+{
+    for (int64_t j = j0; j < j1; ++j) y[j] = 0.0;
+    for (int64_t n = 0; n < f; ++n) {
+        const uint16_t *w2 = W2e + n * d;
+        for (int64_t j = j0; j < j1; ++j) y[j] += h[n] * (double)bf16_value(w2[j]);
+    }
+}
+
+/* parallel_blocks: share the column blocks over OpenMP threads (one row at a time), or
+ * run them in order on the calling thread (when rows are shared out instead). */
+static int expert_row_impl(const uint16_t *xrow, const uint16_t *W1e, const uint16_t *W3e,
+                           const uint16_t *W2e, int64_t d, int64_t f, double *y, int parallel_blocks)
+{
     double *g = (double *)calloc((size_t)f, sizeof(double));
     double *u = (double *)calloc((size_t)f, sizeof(double));
     double *h = (double *)malloc((size_t)f * sizeof(double));
     if (!g || !u || !h) { free(g); free(u); free(h); return -3; }
-    const int64_t NB = 256; /* column block handled by one thread */
-#pragma omp parallel for schedule(static)
-    for (int64_t n0 = 0; n0 < f; n0 += NB) {
-        int64_t n1 = n0 + NB < f ? n0 + NB : f;
-        for (int64_t c = 0; c < d; ++c) {
-            double xc = (double)bf16_value(xrow[c]);
-            const uint16_t *w1 = W1e + c * f;
-            const uint16_t *w3 = W3e + c * f;
-            for (int64_t n = n0; n < n1; ++n) {
-                g[n] += xc * (double)bf16_value(w1[n]);
-                u[n] += xc * (double)bf16_value(w3[n]);
-            }
-        }
-        for (int64_t n = n0; n < n1; ++n) h[n] = g[n] / (1.0 + exp(-g[n])) * u[n];
-    }
-#pragma omp parallel for schedule(static)
-    for (int64_t j0 = 0; j0 < d; j0 += NB) {
-        int64_t j1 = j0 + NB < d ? j0 + NB : d;
-        for (int64_t j = j0; j < j1; ++j) y[j] = 0.0;
-        for (int64_t n = 0; n < f; ++n) {
-            const uint16_t *w2 = W2e + n * d;
-            for (int64_t j = j0; j < j1; ++j) y[j] += h[n] * (double)bf16_value(w2[j]);
-        }
-    }
+    const int64_t NB = ORACLE_COL_BLOCK;
+#pragma omp parallel for schedule(static) if (parallel_blocks)
+    for (int64_t n0 = 0; n0 < f; n0 += NB)
+        expert_gateup_block(xrow, W1e, W3e, d, f, n0, n0 + NB < f ? n0 + NB : f, g, u, h);
+#pragma omp parallel for schedule(static) if (parallel_blocks)
+    for (int64_t j0 = 0; j0 < d; j0 += NB)
+        expert_down_block(h, W2e, d, f, j0, j0 + NB < d ? j0 + NB : d, y);
     free(g);
     free(u);
     free(h);
     return 0;
 }
 
+int oracle_expert_row(const uint16_t *xrow, const uint16_t *W1e, const uint16_t *W3e,
+                      const uint16_t *W2e, int64_t d, int64_t f, double *y)
+{
+    if (d <= 0 || f <= 0) return -1;
+    if (!xrow || !W1e || !W3e || !W2e || !y) return -1;
+    return expert_row_impl(xrow, W1e, W3e, W2e, d, f, y, 1);
+}
+
 /*
  * One token's layer output, fp64: out[j] = sum_{i<k} w[i] * y_i[j], slot order,
- * where y_i is expert idx[i] applied to the token's row.  Expert weights are passed
- * as per-expert pointer tables W1[e], W3[e], W2[e] (entries of experts this token does
- * not use may be NULL), so callers can hold only the experts they need.
+ * where y_i is expert idx[i] applied to the token's row.
+ */
+static int moe_token_impl(const uint16_t *xrow, int64_t k, const int32_t *idx, const double *w,
+                          const uint16_t *const *W1, const uint16_t *const *W3,
+                          const uint16_t *const *W2, int64_t d, int64_t f, double *out,
+                          int parallel_blocks)
+{
+    double *y = (double *)malloc((size_t)d * sizeof(double));
+    if (!y) return -3;
+    for (int64_t j = 0; j < d; ++j) out[j] = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        int32_t e = idx[i];
+        if (e < 0 || !W1[e] || !W3[e] || !W2[e]) { free(y); return -2; }
+        int rc = expert_row_impl(xrow, W1[e], W3[e], W2[e], d, f, y, parallel_blocks);
+        if (rc) { free(y); return rc; }
+        for (int64_t j = 0; j < d; ++j) out[j] += w[i] * y[j];
+    }
+    free(y);
+    return 0;
+}
+
+/*
+ * Expert weights are passed as per-expert pointer tables W1[e], W3[e], W2[e] (entries of
+ * experts the token does not use may be NULL), so callers can hold only the experts they
+ * need.  The column blocks of each expert row are shared over OpenMP threads.
  */
 int oracle_moe_token(const uint16_t *xrow, int64_t k, const int32_t *idx, const double *w,
                      const uint16_t *const *W1, const uint16_t *const *W3,
@@ -264,16 +311,31 @@ int oracle_moe_token(const uint16_t *xrow, int64_t k, const int32_t *idx, const 
 {
     if (k <= 0 || d <= 0 || f <= 0) return -1;
     if (!xrow || !idx || !w || !W1 || !W3 || !W2 || !out) return -1;
-    double *y = (double *)malloc((size_t)d * sizeof(double));
-    if (!y) return -3;
-    for (int64_t j = 0; j < d; ++j) out[j] = 0.0;
-    for (int64_t i = 0; i < k; ++i) {
-        int32_t e = idx[i];
-        if (!W1[e] || !W3[e] || !W2[e]) { free(y); return -2; }
-        int rc = oracle_expert_row(xrow, W1[e], W3[e], W2[e], d, f, y);
-        if (rc) { free(y); return rc; }
-        for (int64_t j = 0; j < d; ++j) out[j] += w[i] * y[j];
+    return moe_token_impl(xrow, k, idx, w, W1, W3, W2, d, f, out, 1);
+}
+
+/*
+ * The layer output of n listed tokens, fp64: out[r, :] is oracle_moe_token of token
+ * tokens[r] (row tokens[r] of x [*, d], its slots idx[tokens[r], :] and weights
+ * w[tokens[r], :], both [*, k]).  The tokens are shared over OpenMP threads, one token per
+ * thread at a time; each token's arithmetic is exactly that of oracle_moe_token.
+ */
+int oracle_moe_tokens(const uint16_t *x, int64_t d, const int64_t *tokens, int64_t n, int64_t k,
+                      const int32_t *idx, const double *w, const uint16_t *const *W1,
+                      const uint16_t *const *W3, const uint16_t *const *W2, int64_t f,
+                      double *out)
+{
+    if (n < 0 || k <= 0 || d <= 0 || f <= 0) return -1;
+    if (n == 0) return 0;
+    if (!x || !tokens || !idx || !w || !W1 || !W3 || !W2 || !out) return -1;
+    int rc_all = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : rc_all)
+    for (int64_t r = 0; r < n; ++r) {
+        const int64_t t = tokens[r];
+        int rc = t < 0 ? -1
+                       : moe_token_impl(x + t * d, k, idx + t * k, w + t * k, W1, W3, W2, d, f,
+                                        out + r * d, 0);
+        if (rc) rc_all |= 1;
     }
-    free(y);
-    return 0;
+    return rc_all ? -2 : 0;
 }
