@@ -121,6 +121,7 @@ def moe_mk_plan(E: int, k: int, d: int, f: int, sched: int = MOE_MK_SCHED_STATIC
 
 
 def moe_mk_plan_destroy(plan: int) -> None:
+    _SHAPES.pop(plan, None)
     lib().moe_mk_plan_destroy(plan)
 
 
@@ -133,9 +134,48 @@ def moe_mk_workspace_init(plan: int, ws, stream=None) -> None:
            "moe_mk_workspace_init")
 
 
+_SHAPES = {}
+
+
+def _plan_shape(plan: int):
+    """(E, k, d, f) of a plan (cached per plan handle)."""
+    sh = _SHAPES.get(plan)
+    if sh is None:
+        sh = tuple(moe_mk_plan_info(plan, key) for key in ("E", "k", "d", "f"))
+        _SHAPES[plan] = sh
+    return sh
+
+
+def _check_shape(t, name, shape):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_forward_args(plan, x, Wr, router_bias, W1, W3, W2, out, B, ws):
+    """Shapes and devices of every tensor against the plan's (E, k, d, f) and B; the C ABI
+    sees only pointers, so a mis-shaped tensor would be read or written out of bounds."""
+    E, k, d, f = _plan_shape(plan)
+    if B < 0:
+        raise ValueError(f"B must be >= 0, got {B}")
+    for t, name in ((x, "x"), (out, "out")):
+        if t.dim() != 2 or t.shape[1] != d or t.shape[0] < B:
+            raise ValueError(f"{name} must have shape (>= {B}, {d}), got {tuple(t.shape)}")
+    _check_shape(Wr, "Wr", (d, E))
+    _check_shape(router_bias, "router_bias", (E,))
+    _check_shape(W1, "W1", (E, d, f))
+    _check_shape(W3, "W3", (E, d, f))
+    _check_shape(W2, "W2", (E, f, d))
+    devs = {t.device for t in (x, Wr, router_bias, W1, W3, W2, out, ws) if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"every tensor must be on one device, got {sorted(str(v) for v in devs)}")
+
+
 def moe_mk_forward(plan: int, x, Wr, router_bias, W1, W3, W2, out, B: int, ws, stream=None) -> None:
     import torch
     bf = torch.bfloat16
+    _check_forward_args(plan, x, Wr, router_bias, W1, W3, W2, out, B, ws)
     _check(lib().moe_mk_forward(plan, _dev_ptr(x, "x", bf), _dev_ptr(Wr, "Wr", torch.float32),
                                 _dev_ptr(router_bias, "router_bias", torch.float32), _dev_ptr(W1, "W1", bf),
                                 _dev_ptr(W3, "W3", bf), _dev_ptr(W2, "W2", bf), _dev_ptr(out, "out", bf), B,
@@ -206,6 +246,9 @@ class MoELayer:
         import torch
         self.E, self.k, self.d, self.f = E, k, d, f
         self.Wr, self.W1, self.W3, self.W2, self.bias = Wr, W1, W3, W2, router_bias
+        for t, name, shape in ((Wr, "Wr", (d, E)), (router_bias, "router_bias", (E,)), (W1, "W1", (E, d, f)),
+                               (W3, "W3", (E, d, f)), (W2, "W2", (E, f, d))):
+            _check_shape(t, name, shape)
         self.plan = moe_mk_plan(E, k, d, f, sched)
         nbytes = moe_mk_workspace_bytes(self.plan, max(1, max_batch))
         self.ws = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device or "cuda")
@@ -214,6 +257,8 @@ class MoELayer:
 
     def forward(self, x, out=None, stream=None):
         import torch
+        if x.dim() != 2 or x.shape[1] != self.d:
+            raise ValueError(f"x must have shape (B, {self.d}), got {tuple(x.shape)}")
         B = x.shape[0]
         if B > self.max_batch:
             raise ValueError(f"batch {B} exceeds the workspace capacity {self.max_batch}")

@@ -3,12 +3,14 @@
 #include <hip/hip_runtime.h>
 #if !defined(__HIP_DEVICE_COMPILE__)
 
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
 #include <new>
 
 #include "../../include/moe_mk.h"
+#include "mk_capacity.h"
 #include "mk_common.h"
 
 hipError_t mk_launch(const mk::Params &p, int grid, hipStream_t stream);
@@ -24,9 +26,7 @@ struct moe_mk_plan_s {
     int grid;
     long long watchdog;
     int debug;
-    // cache of the last workspace size -> capacity lookup
-    size_t cached_bytes;
-    int64_t cached_cap;
+    uint64_t id;  // unique over the process lifetime (keys the per-thread capacity cache)
 };
 
 namespace {
@@ -37,26 +37,11 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool plan_ok(moe_mk_plan_t p) { return p != nullptr && p->s.E > 0; }
 
-size_t bytes_for(const mk::Shape &s, int64_t B) {
-    if (B < 1) B = 1;
-    return mk::make_layout(s, B).total;
-}
+size_t bytes_for(const mk::Shape &s, int64_t B) { return mk::workspace_bytes_for(s, B); }
 
-// Largest B whose requirement fits in ws_bytes (0 when even B = 1 does not fit).
-int64_t capacity(moe_mk_plan_t p, size_t ws_bytes) {
-    if (p->cached_bytes == ws_bytes) return p->cached_cap;
-    int64_t lo = 0, hi = ((int64_t)1 << 31) / p->s.k;  // B*k < 2^31
-    while (lo < hi) {
-        const int64_t mid = lo + (hi - lo + 1) / 2;
-        if (bytes_for(p->s, mid) <= ws_bytes)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    p->cached_bytes = ws_bytes;
-    p->cached_cap = lo;
-    return lo;
-}
+std::atomic<uint64_t> g_next_plan_id{1};
+
+int64_t capacity(moe_mk_plan_t p, size_t ws_bytes) { return mk::workspace_capacity(p->s, p->id, ws_bytes); }
 
 }  // namespace
 
@@ -99,13 +84,14 @@ moe_mk_status_t moe_mk_plan(moe_mk_plan_t *plan, int E, int k, int d, int f, moe
     p->grid = p->cus * occ;
     const char *env = std::getenv("MOE_MK_GRID");  // debugging aid: cap the persistent grid
     if (env) {
-        const int g = std::atoi(env);
-        if (g > 0 && g < p->grid) p->grid = g;
+        // whole groups of 8 workgroups: the static schedule gives each of the 8 XCDs its own
+        // list, taken by the workgroups w with w % 8 == x, so every list needs a workgroup
+        const int g = std::atoi(env) / 8 * 8;
+        if (g >= 8 && g < p->grid) p->grid = g;
     }
     p->watchdog = kDefaultWatchdog;
     p->debug = 0;
-    p->cached_bytes = (size_t)-1;
-    p->cached_cap = 0;
+    p->id = g_next_plan_id.fetch_add(1);
     *plan = p;
     return MOE_MK_OK;
 }

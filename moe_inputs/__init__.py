@@ -167,8 +167,13 @@ def to_torch_bf16(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
 
 
-def device_weights(cfg: Config, device="cuda"):
-    """Wr, bias and the expert weights of ``cfg`` as device tensors (generated expert by expert)."""
+def device_weights(cfg: Config, device="cuda", keep=None):
+    """Wr, bias and the expert weights of ``cfg`` as device tensors (generated expert by expert).
+
+    With ``keep`` (a set of expert indices) the host arrays of those experts are also
+    returned, as a sixth item ``{e: (W1e, W3e, W2e)}``, so the same draws can serve a
+    host-side computation without being generated twice.
+    """
     import torch
     Wr = torch.from_numpy(make_wr(cfg)).to(device)
     b = make_bias(cfg)
@@ -176,13 +181,18 @@ def device_weights(cfg: Config, device="cuda"):
     W1 = torch.empty((cfg.E, cfg.d, cfg.f), dtype=torch.bfloat16, device=device)
     W3 = torch.empty_like(W1)
     W2 = torch.empty((cfg.E, cfg.f, cfg.d), dtype=torch.bfloat16, device=device)
+    kept = {}
 
     def put(e, a1, a3, a2):
         W1[e].copy_(to_torch_bf16(a1))
         W3[e].copy_(to_torch_bf16(a3))
         W2[e].copy_(to_torch_bf16(a2))
+        if keep is not None and e in keep:
+            kept[e] = (a1, a3, a2)
 
     for_each_expert(cfg, put)
+    if keep is not None:
+        return Wr, bias, W1, W3, W2, kept
     return Wr, bias, W1, W3, W2
 
 

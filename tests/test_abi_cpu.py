@@ -102,3 +102,26 @@ def test_every_kernel_launched_by_the_host_exists_in_the_device_code(tmp_path):
         name_len = n - len("__device_stub__")
         kernel = f"{prefix}{name_len}{rest}"
         assert kernel in device, f"{kernel} (host stub {stub}) missing from the device code object"
+
+
+def test_binding_rejects_mis_shaped_tensors():
+    # the C ABI sees only pointers, so the binding checks every shape against the plan's
+    # (E, k, d, f) and B before anything reaches the library (CPU tensors: the check comes
+    # before any device pointer is taken)
+    E, k, d, f, B = 4, 2, 128, 256, 5
+    fake_plan = 0x7E57
+    mk._SHAPES[fake_plan] = (E, k, d, f)
+    try:
+        t = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt)
+        good = dict(x=t(B, d), Wr=t(d, E, dt=torch.float32), router_bias=None, W1=t(E, d, f), W3=t(E, d, f),
+                    W2=t(E, f, d), out=t(B, d), B=B, ws=t(64, dt=torch.uint8))
+        mk._check_forward_args(fake_plan, **good)
+        bad = [("x", t(B, d + 128)), ("x", t(B - 1, d)), ("out", t(B - 1, d)), ("out", t(B, d, 1)),
+               ("Wr", t(E, d, dt=torch.float32)), ("router_bias", t(E + 1, dt=torch.float32)),
+               ("W1", t(E, f, d)), ("W3", t(E - 1, d, f)), ("W2", t(E, d, f)), ("B", -1)]
+        for name, val in bad:
+            args = dict(good, **{name: val})
+            with pytest.raises(ValueError):
+                mk.moe_mk_forward(fake_plan, **args)
+    finally:
+        mk._SHAPES.pop(fake_plan, None)

@@ -2,8 +2,9 @@
 
 Routing (logits, top-k indices, histogram, exp_indptr, perm, inv) must match bit for bit;
 topk_w within 1e-6; the layer output within 2e-2 * max|ref| (bf16 operands, fp32
-accumulation).  Small cases compare every token; the full-size configurations compare
-routing for every token and the output on sampled tokens the oracle computes one by one.
+accumulation).  Every case compares routing and output on every token, except the
+four-times-prefill batch, whose output is compared on a token of every row tile of every
+expert.
 """
 import gc
 
@@ -15,8 +16,7 @@ import moe_groupgemm_amd as mk
 import oracle
 from gpu_cases import (check_out, check_routing, ctl_words, dev_inputs, down_splits, expected_task_counts, log,
                        routing_numpy, tile_config)
-from moe_inputs import (CONFIGS, Config, bf16_bits_to_f32, device_weights, device_x, expert_weights, make_bias,
-                        make_wr, make_x, small_case, to_torch_bf16)
+from moe_inputs import CONFIGS, Config, device_weights, make_bias, make_wr, make_x, small_case, to_torch_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -237,10 +237,14 @@ def test_rest_state_and_task_counts(B, E, d, f, sched):
     tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
     layer = mk.MoELayer(E, 2, d, f, tWr, t1, t3, t2, sched=sched, max_batch=B)
     before = ctl_words(layer, B).copy()
-    for _ in range(3):
-        layer(tx)
+    outs = [layer(tx) for _ in range(3)]
     torch.cuda.synchronize()
     assert layer.error() == 0
+    ref = oracle.forward(x, Wr, bias, W1, W3, W2, 2)
+    check_routing(routing_numpy(layer, B), ref, B, E)
+    check_out(outs[0].float().cpu().numpy(), ref["out"], f"rest state B={B} E={E}")
+    for o in outs[1:]:  # every forward from the rest state gives the same bits
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     c = ctl_words(layer, B)
     C = mk.CTL
     assert c[C["epoch"]] == before[C["epoch"]] + 3    # epoch advanced once per forward
@@ -345,37 +349,92 @@ def test_uninitialised_workspace_is_reported():
 
 
 # ------------------------------------------------------------------------------ full-size configurations
+# Each full configuration runs at its real size and is compared with the oracle on EVERY
+# token (the oracle's token-parallel call), except the four-times-prefill batch, which is
+# compared on a few hundred tokens chosen so that every row tile of every expert holds at
+# least one of them.  Inputs and oracle results are computed once per configuration and
+# shared by both schedules.
 
-def _full_config(name, sched, sample):
-    return _full_config_of(CONFIGS[name], sched, sample)
+_FULL = {"key": None, "val": None}
 
 
-def _full_config_of(cfg, sched, sample):
-    name = cfg.name
-    log(f"config {name} sched={SNAME[sched]}: generating inputs")
-    tWr, tb, t1, t3, t2 = device_weights(cfg)
-    Wr, bias = make_wr(cfg), make_bias(cfg)
-    results = []
+class _FullCase:
+    """Host inputs, device weights and (lazily) oracle results of one configuration."""
+
+    def __init__(self, cfg):
+        log(f"config {cfg.name}: generating inputs, routing on the oracle")
+        self.cfg = cfg
+        self.x_all = make_x(cfg)
+        self.Wr, self.bias = make_wr(cfg), make_bias(cfg)
+        self.routing = {B: oracle.routing(self.x_all[:B], self.Wr, self.bias, cfg.k) for B in cfg.batches}
+        used = set()
+        for r in self.routing.values():
+            used |= {int(e) for e in np.unique(r["topk_idx"])}
+        tWr, tb, t1, t3, t2, self.host = device_weights(cfg, keep=used)
+        self.dev = (tWr, tb, t1, t3, t2)
+        self.tx_all = to_torch_bf16(self.x_all).cuda()
+        self.outs = {}
+
+    def ref_out(self, B, toks):
+        key = (B, tuple(toks))
+        if key not in self.outs:
+            r = self.routing[B]
+            log(f"  oracle: {len(toks)} tokens of B={B}")
+            self.outs[key] = oracle.moe_tokens(self.x_all[:B], toks, r["topk_idx"], r["topk_w"],
+                                               lambda e: self.host[e], self.cfg.d, self.cfg.f)
+        return self.outs[key]
+
+
+def _case(cfg):
+    if _FULL["key"] != cfg:
+        _FULL["key"], _FULL["val"] = None, None
+        gc.collect()
+        torch.cuda.empty_cache()
+        _FULL["val"] = _FullCase(cfg)
+        _FULL["key"] = cfg
+    return _FULL["val"]
+
+
+def _tokens_of_every_row_tile(r, k, BM):
+    """One token from the first row, every BM-th row and the last row of each expert's segment."""
+    toks = set()
+    ip = r["exp_indptr"]
+    for e in range(len(ip) - 1):
+        lo, hi = int(ip[e]), int(ip[e + 1])
+        for p in list(range(lo, hi, BM)) + ([hi - 1] if hi > lo else []):
+            toks.add(int(r["perm"][p]) // k)
+    return sorted(toks)
+
+
+def _full_config_of(cfg, sched, tokens="all"):
+    c = _case(cfg)
+    tWr, tb, t1, t3, t2 = c.dev
+    log(f"config {cfg.name} sched={SNAME[sched]}")
     layer = mk.MoELayer(cfg.E, cfg.k, cfg.d, cfg.f, tWr, t1, t3, t2, router_bias=tb, sched=sched,
                         max_batch=max(cfg.batches))
-    x_all = make_x(cfg)
-    tx_all = to_torch_bf16(x_all).cuda()
+    results = []
     for B in cfg.batches:
-        x = x_all[:B]
-        out = layer(tx_all[:B])
+        out = layer(c.tx_all[:B])
         torch.cuda.synchronize()
         assert layer.error() == 0
-        got = routing_numpy(layer, B)
-        ref = oracle.routing(x, Wr, bias, cfg.k)
-        check_routing(got, ref, B, cfg.E)
-        toks = sorted(set(np.linspace(0, B - 1, min(B, sample)).astype(int).tolist()))
-        ref_out = oracle.moe_tokens(x, toks, ref["topk_idx"], ref["topk_w"], lambda e: expert_weights(cfg, e),
-                                    cfg.d, cfg.f)
-        check_out(out.float().cpu().numpy()[toks], ref_out, f"{name} B={B} ({len(toks)} tokens)")
+        ref = c.routing[B]
+        check_routing(routing_numpy(layer, B), ref, B, cfg.E)
+        if tokens == "all":
+            toks = list(range(B))
+        else:
+            toks = _tokens_of_every_row_tile(ref, cfg.k, tile_config(B, cfg.k, cfg.E, cfg.d, cfg.f)[0])
+            assert len(toks) >= tokens, len(toks)
+        ref_out = c.ref_out(B, toks)
+        got = out.float().cpu().numpy()
+        check_out(got[toks], ref_out, f"{cfg.name} B={B} ({len(toks)} of {B} tokens)")
         results.append((B, out.clone()))
-        log(f"  B={B}: routing exact, output within tolerance")
+        log(f"  B={B}: routing exact, output within tolerance on {len(toks)} tokens")
     layer.close()
-    return results, (tWr, tb, t1, t3, t2, tx_all)
+    return results, c
+
+
+def _full_config(name, sched):
+    return _full_config_of(CONFIGS[name], sched)
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
@@ -403,18 +462,19 @@ def test_threshold_batches_one_plan(sched):
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
 def test_config_mixtral_decode(sched):
-    _full_config("mixtral_decode", sched, sample=8)
+    _full_config("mixtral_decode", sched)
 
 
 def test_config_sweep_one_plan_no_recompile():
     cfg = CONFIGS["sweep"]
-    results, (tWr, tb, t1, t3, t2, tx_all) = _full_config("sweep", mk.MOE_MK_SCHED_STATIC, sample=12)
+    results, c = _full_config("sweep", mk.MOE_MK_SCHED_STATIC)
+    tWr, tb, t1, t3, t2 = c.dev
     # the same batches run on fresh workspaces in isolation give bitwise the same output,
     # and the leading tokens of a larger batch equal a smaller batch (batch-prefix invariance)
     full = dict(results)
     for B in (3, 57):
         layer = mk.MoELayer(cfg.E, cfg.k, cfg.d, cfg.f, tWr, t1, t3, t2, max_batch=B)
-        out = layer(tx_all[:B])
+        out = layer(c.tx_all[:B])
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), full[B].view(torch.int16))
         assert torch.equal(full[512][:B].view(torch.int16), out.view(torch.int16))
@@ -422,25 +482,36 @@ def test_config_sweep_one_plan_no_recompile():
 
 
 def test_config_sweep_dynamic():
-    _full_config("sweep", mk.MOE_MK_SCHED_DYNAMIC, sample=6)
+    _full_config("sweep", mk.MOE_MK_SCHED_DYNAMIC)
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
 def test_config_deepseek_zipf(sched):
-    _full_config("deepseek_zipf", sched, sample=4)
+    _full_config("deepseek_zipf", sched)
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
 def test_config_prefill(sched):
-    _full_config("prefill", sched, sample=8)
+    _full_config("prefill", sched)
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
 def test_large_batch_prefill_shape(sched):
     # four times the prefill batch (131072 routed rows): queue capacity, the per-XCD lists,
-    # eight-token router tasks and wide tiles at a size well past the benchmark's
+    # eight-token router tasks and wide tiles at a size well past the benchmark's; the output
+    # is compared on a token of every row tile of every expert (first rows and last rows)
     cfg = Config("prefill_x4", d=2048, f=768, E=128, k=8, batches=(16384,), seed=606)
-    _full_config_of(cfg, sched, sample=6)
+    _full_config_of(cfg, sched, tokens=256)
+
+
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+def test_wide_long_k_every_token(sched):
+    # wide tiles with the prefill's long reduction (d = 2048: 64 stages of the gate/up ring,
+    # f = 768 for the down projection), about 256 rows per expert so experts take one full
+    # tile and some a second, thin one; every token compared
+    cfg = Config("wide_long_k", d=2048, f=768, E=8, k=2, batches=(1024,), seed=808)
+    assert tile_config(1024, 2, 8, 2048, 768)[0] == 256
+    _full_config_of(cfg, sched)
 
 
 def test_max_experts_and_top_k_wide():

@@ -20,3 +20,14 @@ def test_workspace_layout_holds_every_batch(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout[-4000:]
     assert " 0 failures" in r.stdout
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_capacity_lookups_from_two_threads_on_one_plan(tmp_path):
+    exe = str(tmp_path / "host_capacity_check")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-pthread", "-I", CSRC,
+                    os.path.join(HERE, "host_capacity_check.cpp"), "-o", exe], check=True, capture_output=True,
+                   text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout[-4000:]
+    assert " 0 failures" in r.stdout
