@@ -101,6 +101,13 @@ inline int down_splits(const Shape &s, int64_t B) {
     return 1;
 }
 constexpr int kMaxSplits = 4;
+// The most splits any batch size takes for this shape (sizes the partial buffers).
+inline int max_down_splits(const Shape &s) {
+    const int64_t nb1 = s.f / kBN;
+    if (s.f >= 8192 && nb1 % 4 == 0) return 4;
+    if (s.f >= 4096 && nb1 % 2 == 0) return 2;
+    return 1;
+}
 
 // GroupGEMM tiles of one forward.  Narrow: kBM x kBN tiles (decode and mid-size batches).
 // Wide: when an expert averages at least kWideMinRows rows, tiles of kWideBM rows,
@@ -181,7 +188,10 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     c.NB1 = s.f / kBN;
     c.NB2 = s.d / kBN;
     c.S = down_splits(s, B);
-    c.q_cap = 2 * c.T + 1 + c.mt_cap * c.NB1 + c.mt_cap * kMaxSplits * c.NB2 + c.nC + 128;  // + block padding
+    // combine tasks of any batch up to B (a task has at least one token), so that the queue,
+    // and with it the workspace, grows with B
+    const int64_t nC_max = B * ceil_div(s.d, kCombineCols);
+    c.q_cap = 2 * c.T + 1 + c.mt_cap * c.NB1 + c.mt_cap * kMaxSplits * c.NB2 + nC_max + 128;  // + block padding
     c.nR_max = ceil_div(B, kWaves) * ceil_div(s.E, 4);
     return c;
 }
@@ -225,8 +235,10 @@ inline Layout make_layout(const Shape &s, int64_t cap) {
     L.inv = take((size_t)A * 4);
     L.h = take((size_t)A * s.f * 2);
     L.y = take((size_t)A * s.d * 2);
-    // yp holds S fp32 partial results of B*k rows each; S > 1 only when B*k <= 1024
-    L.yp = take((size_t)kMaxSplits * (A < 1024 ? A : 1024) * s.d * 4);
+    // yp holds S fp32 partial results of B*k rows each; S > 1 only when B*k <= 1024, and
+    // never for a shape whose f is too short to split
+    const int smax = max_down_splits(s);
+    L.yp = take(smax > 1 ? (size_t)smax * (A < 1024 ? A : 1024) * s.d * 4 : 0);
     L.red_ctr = take((size_t)c.mt_cap * c.NB2 * 4);
     L.qslots = take((size_t)c.q_cap * 8);
     L.trace = take((size_t)(c.q_cap + c.nR_max) * 8 * 8);
@@ -263,5 +275,6 @@ struct Params {
     MK_G int *red_ctr;      // per down-projection tile: splits finished (rest 0)
     MK_G long long *trace;  // 8 int64 per task when tracing is on
 };
+
 
 }  // namespace mk

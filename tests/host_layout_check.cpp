@@ -99,13 +99,24 @@ int main() {
                 // fp32 partials of a split down projection: S planes of B*k rows of d
                 if (t.S > 1) {
                     const size_t need = (size_t)t.S * A * s.d * 4;
-                    const size_t have = (size_t)kMaxSplits * std::min<int64_t>(Acap, 1024) * s.d * 4;
+                    CHECK(t.S <= max_down_splits(s), "S %d > max %d", t.S, max_down_splits(s));
+                    const size_t have = (size_t)max_down_splits(s) * std::min<int64_t>(Acap, 1024) * s.d * 4;
                     CHECK(need <= have, "E=%d B=%lld: split partials %zu > %zu", s.E, (long long)B, need, have);
                     CHECK(L.red_ctr - L.yp >= need, "yp region too small");
                 }
                 CHECK(L.h - L.inv >= (size_t)A * 4 && L.y - L.h >= (size_t)A * s.f * 2, "h region");
                 CHECK(L.yp - L.y >= (size_t)A * s.d * 2, "y region");
             }
+        }
+    }
+    // the requirement grows with the capacity at every step (the capacity lookup bisects it)
+    for (const Shape &s : shapes) {
+        size_t prev = 0;
+        for (int64_t cap = 1; cap <= 2200; ++cap) {
+            const size_t t = make_layout(s, cap).total;
+            CHECK(t >= prev, "E=%d k=%d d=%d f=%d cap=%lld: total %zu < %zu", s.E, s.k, s.d, s.f, (long long)cap,
+                  t, prev);
+            prev = t;
         }
     }
     std::printf("%d cases, %d failures\n", cases, fails);
