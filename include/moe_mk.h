@@ -109,6 +109,30 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
                                void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_mk_forward without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  It allocates nothing: no hipMalloc, no hipFree, no allocating library call.
+ * The workspace is a static scratch array of MOE_MK_SCRATCH_BYTES in the library's device
+ * code, one per GPU, held by each GPU that loads the library until the process ends.
+ *   x .. out, B, stream  as for moe_mk_forward.
+ *   err   device int32 (4-byte aligned) or NULL: receives this forward's device error bits
+ *         (MOE_MK_ERR_*, 0 when none) when the kernel ends.  After a device error the
+ *         kernel puts the scratch back to its rest state itself, so the next call runs clean.
+ * The largest B is the capacity of the scratch for this plan's shape (the B for which
+ * moe_mk_workspace_bytes(plan, B) <= MOE_MK_SCRATCH_BYTES); a larger B returns EWORKSPACE
+ * and enqueues nothing.  The first call on a device looks up the scratch's device address;
+ * the first call of a plan on a device (after another plan used it, or ever) also enqueues
+ * the scratch's preparation (two small fill kernels) on stream before the forward.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time on one GPU
+ * (other streams, other threads) race and give undefined results.
+ * Errors: EINVAL, EWORKSPACE, EUNSUPPORTED (device index >= 64), EHIP.
+ */
+#define MOE_MK_SCRATCH_BYTES ((size_t)64 << 20)
+moe_mk_status_t moe_mk_forward_noalloc(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias,
+                                       const void *W1, const void *W3, const void *W2, void *out, int64_t B,
+                                       int32_t *err, void *stream);
+
+/*
  * Device pointers into the workspace of the most recent forward with batch size B.
  * Valid until the next forward on that workspace.
  *   topk_idx  int32 [B, k]   expert of each (token, slot), slot 0 = largest logit

@@ -66,6 +66,8 @@ def lib():
     L.moe_mk_workspace_init.restype = ctypes.c_int
     L.moe_mk_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz, vp]
     L.moe_mk_forward.restype = ctypes.c_int
+    L.moe_mk_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp]
+    L.moe_mk_forward_noalloc.restype = ctypes.c_int
     L.moe_mk_routing_view.argtypes = [vp, i64, vp, sz, ctypes.POINTER(_RoutingView)]
     L.moe_mk_routing_view.restype = ctypes.c_int
     L.moe_mk_workspace_error.argtypes = [vp, vp, sz, vp, ctypes.POINTER(i32)]
@@ -181,6 +183,21 @@ def moe_mk_forward(plan: int, x, Wr, router_bias, W1, W3, W2, out, B: int, ws, s
                                 _dev_ptr(W3, "W3", bf), _dev_ptr(W2, "W2", bf), _dev_ptr(out, "out", bf), B,
                                 _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_mk_forward")
+
+
+def moe_mk_forward_noalloc(plan: int, x, Wr, router_bias, W1, W3, W2, out, B: int, err=None, stream=None) -> None:
+    """moe_mk_forward on the library's static per-GPU scratch (allocates nothing); ``err``:
+    optional int32 device tensor of one element receiving the forward's device error bits."""
+    import torch
+    bf = torch.bfloat16
+    _check_forward_args(plan, x, Wr, router_bias, W1, W3, W2, out, B, err if err is not None else x)
+    if err is not None and err.numel() < 1:
+        raise ValueError("err must hold one int32")
+    _check(lib().moe_mk_forward_noalloc(plan, _dev_ptr(x, "x", bf), _dev_ptr(Wr, "Wr", torch.float32),
+                                        _dev_ptr(router_bias, "router_bias", torch.float32), _dev_ptr(W1, "W1", bf),
+                                        _dev_ptr(W3, "W3", bf), _dev_ptr(W2, "W2", bf), _dev_ptr(out, "out", bf), B,
+                                        _dev_ptr(err, "err", torch.int32), _stream(stream)),
+           "moe_mk_forward_noalloc")
 
 
 def moe_mk_routing_view(plan: int, B: int, ws) -> dict:

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -16,6 +17,7 @@
 hipError_t mk_launch(const mk::Params &p, int grid, hipStream_t stream);
 hipError_t mk_ws_init(void *ws, size_t bytes, hipStream_t stream);
 hipError_t mk_occupancy(int *blocks_per_cu);
+hipError_t mk_scratch(void **ptr, size_t *bytes);
 
 struct moe_mk_plan_s {
     mk::Shape s;
@@ -111,25 +113,31 @@ moe_mk_status_t moe_mk_workspace_init(moe_mk_plan_t plan, void *ws, size_t ws_by
     return MOE_MK_OK;
 }
 
-moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias,
-                               const void *W1, const void *W3, const void *W2, void *out, int64_t B, void *ws,
-                               size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both forward entry points (everything but the workspace).
+moe_mk_status_t check_forward(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias,
+                              const void *W1, const void *W3, const void *W2, void *out, int64_t B) {
     if (!plan_ok(plan)) return MOE_MK_EINVAL;
-    const mk::Shape &s = plan->s;
-    if (B < 0 || B * s.k >= ((int64_t)1 << 31)) return MOE_MK_EINVAL;
+    if (B < 0 || B * plan->s.k >= ((int64_t)1 << 31)) return MOE_MK_EINVAL;
     if (B == 0) return MOE_MK_OK;
-    if (!x || !Wr || !W1 || !W3 || !W2 || !out || !ws) return MOE_MK_EINVAL;
-    if (!aligned16(x) || !aligned16(Wr) || !aligned16(W1) || !aligned16(W3) || !aligned16(W2) ||
-        !aligned16(out) || !aligned16(ws))
+    if (!x || !Wr || !W1 || !W3 || !W2 || !out) return MOE_MK_EINVAL;
+    if (!aligned16(x) || !aligned16(Wr) || !aligned16(W1) || !aligned16(W3) || !aligned16(W2) || !aligned16(out))
         return MOE_MK_EINVAL;
     if (router_bias && ((uintptr_t)router_bias & 3u)) return MOE_MK_EINVAL;
-    const int64_t cap = capacity(plan, ws_bytes);
-    if (cap < B) return MOE_MK_EWORKSPACE;
+    return MOE_MK_OK;
+}
+
+// Kernel arguments of a forward of B tokens whose workspace (a layout for cap tokens)
+// starts at base.
+mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias, const void *W1,
+                       const void *W3, const void *W2, void *out, int64_t B, char *base, int64_t cap) {
+    const mk::Shape &s = plan->s;
     const mk::Layout L = mk::make_layout(s, cap);
     const mk::Counts c = mk::make_counts(s, B);
     const mk::Counts cc = mk::make_counts(s, cap);
-    char *base = (char *)ws;
-
     mk::Params P;
     P.x = (const uint16_t *)x;
     P.Wr = Wr;
@@ -190,7 +198,62 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     P.qslots = (unsigned long long *)(base + L.qslots);
     P.red_ctr = (int *)(base + L.red_ctr);
     P.trace = (long long *)(base + L.trace);
+    P.err_out = nullptr;
+    P.heal = 0;
+    return P;
+}
+
+static_assert(MOE_MK_SCRATCH_BYTES == mk::kScratchBytes, "the header states the scratch size");
+
+// Per device: the plan whose layout the static scratch currently holds (0: none yet).
+std::mutex g_scratch_mu;
+uint64_t g_scratch_plan[64] = {};
+
+}  // namespace
+
+extern "C" {
+
+moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias,
+                               const void *W1, const void *W3, const void *W2, void *out, int64_t B, void *ws,
+                               size_t ws_bytes, void *stream) {
+    const moe_mk_status_t st = check_forward(plan, x, Wr, router_bias, W1, W3, W2, out, B);
+    if (st != MOE_MK_OK || B == 0) return st;
+    if (!ws || !aligned16(ws)) return MOE_MK_EINVAL;
+    const int64_t cap = capacity(plan, ws_bytes);
+    if (cap < B) return MOE_MK_EWORKSPACE;
+    const mk::Params P = make_params(plan, x, Wr, router_bias, W1, W3, W2, out, B, (char *)ws, cap);
     if (hipSetDevice(plan->device) != hipSuccess) return MOE_MK_EHIP;
+    if (mk_launch(P, plan->grid, (hipStream_t)stream) != hipSuccess) return MOE_MK_EHIP;
+    return MOE_MK_OK;
+}
+
+moe_mk_status_t moe_mk_forward_noalloc(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias,
+                                       const void *W1, const void *W3, const void *W2, void *out, int64_t B,
+                                       int32_t *err, void *stream) {
+    const moe_mk_status_t st = check_forward(plan, x, Wr, router_bias, W1, W3, W2, out, B);
+    if (st != MOE_MK_OK || B == 0) return st;
+    if (err && ((uintptr_t)err & 3u)) return MOE_MK_EINVAL;
+    if (hipSetDevice(plan->device) != hipSuccess) return MOE_MK_EHIP;
+    if (plan->device < 0 || plan->device >= 64) return MOE_MK_EUNSUPPORTED;
+    void *base = nullptr;
+    size_t bytes = 0;
+    if (mk_scratch(&base, &bytes) != hipSuccess) return MOE_MK_EHIP;
+    const int64_t cap = capacity(plan, bytes);
+    if (cap < B) return MOE_MK_EWORKSPACE;
+    {
+        // The scratch is shared by every plan on this device.  Its rest state is valid for
+        // one layout (one plan shape), so it is prepared again whenever another plan uses it:
+        // the zero fill and the control block's rest values, enqueued before the forward.
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (g_scratch_plan[plan->device] != plan->id) {
+            if (mk_ws_init(base, mk::make_layout(plan->s, cap).total, (hipStream_t)stream) != hipSuccess)
+                return MOE_MK_EHIP;
+            g_scratch_plan[plan->device] = plan->id;
+        }
+    }
+    mk::Params P = make_params(plan, x, Wr, router_bias, W1, W3, W2, out, B, (char *)base, cap);
+    P.err_out = err;
+    P.heal = 1;
     if (mk_launch(P, plan->grid, (hipStream_t)stream) != hipSuccess) return MOE_MK_EHIP;
     return MOE_MK_OK;
 }

@@ -34,6 +34,8 @@
 //   COMBINE(c)    out[b] = sum_i w[b,i] y[inv[b,i]] for 1, 4 or 8 tokens
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "mk_common.h"
 #include "mk_device.h"
 
@@ -2478,6 +2480,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
     __syncthreads();
     if (!g_sm.bcast[0]) {  // workspace never prepared: record it and touch nothing else
         if (threadIdx.x == 0) set_error(P.ctl, 8 /* MOE_MK_ERR_UNINIT */);
+        if (P.err_out && blockIdx.x == 0 && threadIdx.x == 0) st_relaxed(P.err_out, 8);
         return;
     }
     Bases bs = initial_bases(P);
@@ -2551,18 +2554,41 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
     wave_drain_vm();
     if (threadIdx.x == 0) {
         const int old = add_relaxed(P.ctl + CTL_EXIT, 1);
-        if (old == (int)gridDim.x - 1) {
-            if (ld_relaxed(P.ctl + CTL_ERR) == 0) {
-                st_relaxed(P.ctl + CTL_QHEAD, 0);
-                st_relaxed(P.ctl + CTL_QTAIL, 0);
-                st_relaxed(P.ctl + CTL_PF, 0);
-                st_relaxed(P.ctl + CTL_EV_SCAN, 1);
-                st_relaxed(P.ctl + CTL_CQ, 0);
-                for (int x = 0; x < 8; ++x) st_relaxed(P.ctl + CTL_XQ + 32 * x, 0);
-            }
-            st_relaxed(P.ctl + CTL_EXIT, 0);
-            st_relaxed(P.ctl + CTL_EPOCH, g_sm.epoch + 1);
+        g_sm.bcast[0] = old == (int)gridDim.x - 1;
+        g_sm.bcast[1] = g_sm.bcast[0] ? ld_relaxed(P.ctl + CTL_ERR) : 0;
+    }
+    __syncthreads();
+    if (!g_sm.bcast[0]) return;  // every other workgroup has left once this one gets here
+    const int err = g_sm.bcast[1];
+    if (err != 0 && P.heal) {
+        // After a device error the event counters hold partial counts: zero every counter
+        // this forward can have touched (the router tiles' events, the experts' events, the
+        // row tiles' gate/up events and the split-reduction counters), then the rest state
+        // below applies as after a clean forward.
+        for (int i = threadIdx.x; i < P.T; i += kThreads) st_relaxed(P.ev_logit + i, 0);
+        for (int i = threadIdx.x; i < P.E; i += kThreads) st_relaxed(P.ev_exp + i, 0);
+        for (int i = threadIdx.x; i < P.mt_cap * kMaxSplits; i += kThreads) st_relaxed(P.ev_h + i, 0);
+        for (int i = threadIdx.x; i < P.mt_cap * (P.d / kBN); i += kThreads) st_relaxed(P.red_ctr + i, 0);
+        wave_drain_vm();
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        if (err == 0 || P.heal) {
+            st_relaxed(P.ctl + CTL_QHEAD, 0);
+            st_relaxed(P.ctl + CTL_QTAIL, 0);
+            st_relaxed(P.ctl + CTL_PF, 0);
+            st_relaxed(P.ctl + CTL_EV_SCAN, 1);
+            st_relaxed(P.ctl + CTL_CQ, 0);
+            for (int x = 0; x < 8; ++x) st_relaxed(P.ctl + CTL_XQ + 32 * x, 0);
         }
+        if (err != 0 && P.heal) {
+            st_relaxed(P.ctl + CTL_EV_TOPK, 0);
+            st_relaxed(P.ctl + CTL_EV_Y, 0);
+            st_relaxed(P.ctl + CTL_ERR, 0);
+        }
+        if (P.err_out) st_relaxed(P.err_out, err);
+        st_relaxed(P.ctl + CTL_EXIT, 0);
+        st_relaxed(P.ctl + CTL_EPOCH, g_sm.epoch + 1);
     }
 }
 
@@ -2601,6 +2627,38 @@ hipError_t mk_ws_init(void *ws, size_t bytes, hipStream_t stream) {
     hipLaunchKernelGGL(mk::moe_ws_init, dim3(blocks), dim3(256), 0, stream, (uint32_t *)ws, words);
     hipLaunchKernelGGL(mk::moe_ws_init_ctl, dim3(1), dim3(64), 0, stream, (int *)ws);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------ static scratch
+// The workspace of the allocation-free entry point: a file-scope device array, of which every
+// GPU that loads this library holds its own copy (at its own address) until the process ends.
+// In host code the name `scratch` is only a stand-in for the symbol: its device address is
+// looked up once per device with hipGetSymbolAddress and kept, and only that address is ever
+// passed to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[mk::kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+
+// Device address and size of the current device's scratch (looked up on the first call for
+// each device, with that device current).
+hipError_t mk_scratch(void **ptr, size_t *bytes) {
+    static std::mutex mu;
+    static void *addr[kMaxScratchDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = mk::kScratchBytes;
+    return hipSuccess;
 }
 
 hipError_t mk_occupancy(int *blocks_per_cu) {

@@ -274,7 +274,15 @@ struct Params {
     MK_G unsigned long long *qslots;
     MK_G int *red_ctr;      // per down-projection tile: splits finished (rest 0)
     MK_G long long *trace;  // 8 int64 per task when tracing is on
+    // Used by the allocation-free entry point: the error bits of the forward are stored at
+    // *err_out (0 when none; NULL: not reported), and with heal set the last workgroup out
+    // puts the control block and the event counters back to their rest state even after a
+    // device error (clearing the error word), so the next forward starts clean.
+    MK_G int *err_out;
+    int heal;
 };
 
+// The static scratch of the allocation-free entry point (one per GPU).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
 
 }  // namespace mk
