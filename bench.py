@@ -2,10 +2,15 @@
 
 A step is one forward of the whole layer (router, top-k, histogram/scan, grouping, both
 GroupGEMMs, combine) over one batch of synthetic inputs already resident in HBM.  The
-default workload is the Mixtral-shaped decode layer (B=32, d=4096, f=14336, E=8, k=2).
-Prints one JSON line with tokens/s, the roofline of the kernel (HBM bytes or MFMA flops
-of the activated experts per launch over the measured launch time) and the CPU oracle
-timed on a bounded sample of the same workload.
+headline workload (`value`) is the Mixtral-shaped decode layer (B=32, d=4096, f=14336,
+E=8, k=2).  The same JSON line lists every other configuration under `workloads`: the
+prefill-sized layer (B=4096, MFMA roofline) and the DeepSeek-shaped skewed layer on both
+schedules, the six batches of the dynamic-shape sweep on one plan, and the tiny layer.
+Each carries the kernel time, its roofline fraction (HBM bytes of the activated experts
+per launch, or GroupGEMM flops, over the measured launch time), the HBM traffic from the
+committed rocprofv3 counter summary when it was taken on the current kernel source, and
+for B <= 64 the launch time after evicting the Infinity Cache.  The CPU oracle is timed
+on a bounded sample of the headline workload.
 """
 import argparse
 import json
@@ -41,6 +46,9 @@ def parse():
                     "lines to be written back during the next launch)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the box's achievable copy bandwidth and bf16 GEMM rate")
+    ap.add_argument("--workloads", default="all",
+                    help="configurations timed beside the headline one: 'all', 'none', or a comma list of "
+                    "config:sched (e.g. prefill:static,sweep:dynamic)")
     return ap.parse_args()
 
 
@@ -83,10 +91,14 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+def profile_path(cfg_name, B, sched, kind):
+    return os.path.join(ROOT, "profiles", f"megakernel_{cfg_name}_B{B}_{sched}_{kind}.txt")
+
+
 def measured_traffic(cfg_name, B, sched):
     """HBM bytes per launch from the committed rocprofv3 byte-counter summary of this workload,
     or None when there is none or the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"megakernel_{cfg_name}_B{B}_pmc.txt")
+    path = profile_path(cfg_name, B, sched, "pmc")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -155,32 +167,15 @@ def trace_report(layer, x, out, B):
 
     import moe_groupgemm_amd as mk
 
-    flags0 = layer.debug_flags if hasattr(layer, "debug_flags") else 0
+    flags0 = getattr(layer, "debug_flags", 0)
+    view = mk.moe_mk_trace_view(layer.plan, B, layer.ws)
+    view.zero_()  # records left from earlier traced forwards would look like tasks of this one
     mk.moe_mk_plan_set_debug(layer.plan, 0, flags0 | mk.MOE_MK_DEBUG_TRACE)
     layer(x, out)
     torch.cuda.synchronize()
     mk.moe_mk_plan_set_debug(layer.plan, 0, flags0)
-    ctl = layer.routing(B)["ctl"].cpu().numpy()
-    tr = mk.moe_mk_trace_view(layer.plan, B, layer.ws).cpu().numpy()
-    E, k, d, f = layer.E, layer.k, layer.d, layer.f
-    info = lambda key: mk.moe_mk_plan_info(layer.plan, key)
-    waves = info("threads") // 64
-    tpw = 1 if B <= 512 else 8 if E % 4 == 0 and d % 128 == 0 and -(-B // 64) * -(-E // 16) >= 512 else 4
-    reb = 4 if tpw == 1 and E % 4 == 0 and d % 512 == 0 and -(-B // waves) * -(-E // 16) < 64 else 16
-    nR = -(-B // (waves * tpw)) * -(-E // reb)
-    T = -(-B // 64)
-    mt = int(ctl[mk.CTL["mt_total"]])
-    a = B * k
-    if a >= info("wide_min_rows") * E and d % info("wide_BN2") == 0 and f % info("wide_BN1") == 0:
-        S, nb1, nb2 = 1, f // info("wide_BN1"), d // info("wide_BN2")
-    else:
-        nb1, nb2 = f // info("BN1"), d // info("BN2")
-        S = 4 if (a <= 1024 and f >= 8192 and nb1 % 4 == 0) else 2 if (a <= 1024 and f >= 4096 and nb1 % 2 == 0) else 1
-    # GroupGEMM blocks are padded to multiples of 8 task positions (empty tasks leave no record)
-    r8 = lambda v: (v + 7) // 8 * 8
-    total = r8(nR + 2 * T + 1) + S * (r8(mt * nb1 // S) + r8(mt * nb2)) + -(-B // (8 if B >= 1024 and k <= 8 else 1 if B <= 64 else 4)) * -(-d // (4 * info("threads")))
-    tr = tr[:total]
-    tr = tr[tr[:, 1] != 0]
+    tr = view.cpu().numpy()
+    tr = tr[tr[:, 1] != 0]  # tasks that ran (padding positions of the static layout leave no record)
     kind = (tr[:, 0] >> 32) & 0xFF
     wg = tr[:, 0] >> 40
     t0 = tr[:, 1].min()
@@ -204,13 +199,11 @@ def trace_report(layer, x, out, B):
               f"notify {us(r[3] - r[7]):.2f}", file=sys.stderr)
     first = np.array([tr[wg == w, 1].min() for w in sorted(set(wg.tolist()))]) - t0
     print(f"#  first task of a workgroup obtained at: median {us(np.median(first)):.1f} us, "
-          f"90th percentile {us(np.percentile(first, 90)):.1f}, max {us(first.max()):.1f} "
-          f"(router tasks: {', '.join(f'{us(v - t0):.1f}' for v in sorted(tr[kind == 0, 1])[:8])})", file=sys.stderr)
+          f"90th percentile {us(np.percentile(first, 90)):.1f}, max {us(first.max()):.1f}", file=sys.stderr)
     xcc = tr[:, 5]
     print(f"#  XCD of a task equals its workgroup index mod 8 for {100.0 * np.mean(xcc == wg % 8):.1f}% of tasks",
           file=sys.stderr)
-    # time between a workgroup finishing one task and obtaining the next (queue / loop overhead)
-    gaps = []
+    gaps = []  # time between a workgroup finishing one task and obtaining the next
     for w in set(wg.tolist()):
         r = tr[wg == w]
         r = r[np.argsort(r[:, 1])]
@@ -219,7 +212,112 @@ def trace_report(layer, x, out, B):
     if gaps:
         gaps = np.concatenate(gaps)
         print(f"#  between tasks: mean {us(gaps.mean()):.2f} us, max {us(gaps.max()):.1f} us", file=sys.stderr)
-    del np
+
+
+def time_launches(layer, tx, out, stream, steps):
+    """Per-launch kernel times (ms) from HIP events recorded on the launch stream."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        layer(tx, out)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
+
+
+def time_cold(layer, tx, out, stream, reps, flush, dev):
+    """Launch times (ms) each after evicting the Infinity Cache by a 1 GiB read (or write)."""
+    import torch
+    scratch = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(1, dtype=torch.float32, device=dev)
+    ms = []
+    for i in range(reps):
+        if flush == "write":
+            scratch.fill_(float(i))
+        else:
+            torch.sum(scratch, dim=0, keepdim=True, out=sink)
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        layer(tx, out)
+        e0.record(stream)
+        torch.cuda.synchronize()
+        ms.append(s0.elapsed_time(e0))
+    del scratch, sink
+    return ms
+
+
+def roofline(cfg_name, B, sched, alg_bytes, flops, kern_ms):
+    """Roofline of the launch: MFMA for prefill-sized batches (B >= 2048), else HBM."""
+    gbs = alg_bytes / (kern_ms / 1e3) / 1e9
+    tflops = flops / (kern_ms / 1e3) / 1e12
+    traffic = measured_traffic(cfg_name, B, sched)
+    if B >= 2048:
+        return {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic}
+    return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "traffic": traffic}
+
+
+def measure_workload(cfg_name, sched_name, steps, warmup, dev, batches=None, cold_reps=10):
+    """Time the layer of one configuration (each of its batches on one plan and workspace)."""
+    import numpy as np
+    import torch
+
+    import moe_groupgemm_amd as mk
+    from moe_inputs import CONFIGS, device_weights, make_x, to_torch_bf16
+
+    cfg = CONFIGS[cfg_name]
+    batches = batches or cfg.batches
+    sched = mk.MOE_MK_SCHED_STATIC if sched_name == "static" else mk.MOE_MK_SCHED_DYNAMIC
+    print(f"# workload {cfg_name} {sched_name} B={list(batches)}", file=sys.stderr, flush=True)
+    tWr, tb, t1, t3, t2 = device_weights(cfg, device=dev)
+    tx_all = to_torch_bf16(make_x(cfg, max(batches))).to(dev)
+    layer = mk.MoELayer(cfg.E, cfg.k, cfg.d, cfg.f, tWr, t1, t3, t2, router_bias=tb, sched=sched,
+                        max_batch=max(batches), device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = []
+    for B in batches:
+        tx = tx_all[:B]
+        out = torch.empty((B, cfg.d), dtype=torch.bfloat16, device=dev)
+        for _ in range(warmup):
+            layer(tx, out)
+        torch.cuda.synchronize()
+        if layer.error():
+            raise RuntimeError(f"device error word {layer.error()} ({cfg_name} B={B} {sched_name})")
+        hist = layer.routing(B)["hist"].cpu().numpy()
+        alg_bytes, flops, active = algorithmic(cfg, B, hist, tb is not None)
+        ms, _ = time_launches(layer, tx, out, stream, steps)
+        if layer.error():
+            raise RuntimeError(f"device error word {layer.error()} ({cfg_name} B={B} {sched_name})")
+        kern_ms = float(np.mean(ms))
+        e = {"workload": cfg.note, "config": cfg_name, "B": B, "sched": sched_name, "active_experts": active,
+             "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(ms)), "tokens_per_s": B / (kern_ms / 1e3),
+             "roofline": roofline(cfg_name, B, sched_name, alg_bytes, flops, kern_ms),
+             "hbm_frac": alg_bytes / (kern_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+             "mfma_frac": flops / (kern_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+             "algorithmic_bytes": alg_bytes, "gemm_flops": flops}
+        if B <= 64 and cold_reps:
+            cms = float(np.median(time_cold(layer, tx, out, stream, cold_reps, "read", dev)))
+            e["cold"] = {"flush": "read", "kernel_ms_median": cms,
+                         "hbm_frac": alg_bytes / (cms / 1e3) / 1e9 / PEAK_HBM_GBS}
+        res.append(e)
+        print(f"#   B={B}: {kern_ms * 1e3:.1f} us, {e['roofline']['bound']} {e['roofline']['frac']:.3f}",
+              file=sys.stderr, flush=True)
+    layer.close()
+    del layer, tWr, tb, t1, t3, t2, tx_all
+    torch.cuda.empty_cache()
+    return res
+
+
+# configurations listed beside the headline line (configuration, schedule)
+WORKLOADS = [("prefill", "static"), ("prefill", "dynamic"), ("deepseek_zipf", "static"),
+             ("deepseek_zipf", "dynamic"), ("sweep", "static"), ("sweep", "dynamic"), ("tiny", "static"),
+             ("tiny", "dynamic"), ("mixtral_decode", "static")]
 
 
 def main():
@@ -262,32 +360,14 @@ def main():
         raise RuntimeError(f"device error word {layer.error()}")
     hist = layer.routing(B)["hist"].cpu().numpy()
     alg_bytes, flops, active = algorithmic(cfg, B, hist, tb is not None)
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        layer(tx, out)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    per_launch_ms, wall = time_launches(layer, tx, out, stream, args.steps)
     if layer.error():
         raise RuntimeError(f"device error word {layer.error()}")
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     kern_ms = float(np.mean(per_launch_ms))
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = B / (ms_per_step / 1e3)
     gbs = alg_bytes / (kern_ms / 1e3) / 1e9
     tflops = flops / (kern_ms / 1e3) / 1e12
-    prefill = B >= 2048
-    if prefill:
-        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(cfg.name, B, args.sched)}
-    else:
-        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic(cfg.name, B, args.sched)}
     line = {
         "metric": "MoE-layer tokens/s + achieved HBM TB/s (B<=64) / MFMA TFLOP/s (B>=2048) vs peak",
         "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -295,7 +375,7 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.note, "B": B, "d": cfg.d, "f": cfg.f, "E": cfg.E, "k": cfg.k,
                    "sched": args.sched, "active_experts": active},
-        "roofline": roof,
+        "roofline": roofline(cfg.name, B, args.sched, alg_bytes, flops, kern_ms),
         "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(per_launch_ms)),
         "hbm_tbs": gbs / 1e3, "hbm_frac": gbs / PEAK_HBM_GBS,
         "mfma_tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
@@ -305,29 +385,22 @@ def main():
     }
     if args.trace:  # first, while nothing else has run on the device since the timed launches
         trace_report(layer, tx, out, B)
-    if args.flush:
-        # the same launches, each after a 1 GiB read (or write) of a scratch buffer that evicts
-        # the Infinity Cache, so the weights come from HBM even where the activated ones would
-        # fit in the cache
-        scratch = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
-        sink = torch.empty(1, dtype=torch.float32, device=dev)
-        cold_ms = []
-        for i in range(min(args.steps, 10)):
-            if args.flush == "write":
-                scratch.fill_(float(i))
-            else:
-                torch.sum(scratch, dim=0, keepdim=True, out=sink)
-            s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record(stream)
-            layer(tx, out)
-            e0.record(stream)
-            torch.cuda.synchronize()
-            cold_ms.append(s0.elapsed_time(e0))
-        del scratch, sink
+    if args.flush or B <= 64:
+        cold_ms = time_cold(layer, tx, out, stream, min(args.steps, 10), args.flush or "read", dev)
         cms = float(np.median(cold_ms))
-        line["cold"] = {"flush": args.flush, "kernel_ms_median": cms, "kernel_ms_min": float(np.min(cold_ms)),
+        line["cold"] = {"flush": args.flush or "read", "kernel_ms_median": cms,
+                        "kernel_ms_min": float(np.min(cold_ms)),
                         "hbm_frac": alg_bytes / (cms / 1e3) / 1e9 / PEAK_HBM_GBS,
                         "mfma_frac": flops / (cms / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
+    layer.close()
+    del layer, t1, t3, t2
+    torch.cuda.empty_cache()
+    if args.workloads != "none":
+        wanted = WORKLOADS if args.workloads == "all" else \
+            [tuple(w.split(":")) for w in args.workloads.split(",")]
+        line["workloads"] = []
+        for name, sch in wanted:
+            line["workloads"].extend(measure_workload(name, sch, args.steps, args.warmup, dev))
     if not args.no_peaks:
         copy_gbs, gemm_tflops = achievable_peaks(dev)
         line["achievable"] = {"copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,
@@ -338,7 +411,6 @@ def main():
         line["cpu_baseline"] = cpu_baseline(cfg, x, Wr, bias, (W1, W3, W2), sample)
     if args.copy_kernel:
         line["copy_kernel_bytes"] = copy_calibration()
-    layer.close()
     print(json.dumps(line), flush=True)
 
 

@@ -182,6 +182,19 @@ moe_mk_status_t moe_mk_workspace_error(moe_mk_plan_t plan, const void *ws, size_
 int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
 
 /*
+ * Per-forward facts of a batch of B tokens on this plan (host, no device access): the
+ * counts and tile shapes the library picks from B for one forward.  Keys:
+ *   "T"                       64-token routing tiles (top-k and grouping tasks)
+ *   "route_tasks"             router tasks; "route_tokens_per_wave", "route_experts_per_task"
+ *   "combine_tasks"           combine tasks; "combine_tokens" tokens per combine task
+ *   "BM" "NB1" "NB2" "S"      GroupGEMM row-tile rows, gate/up and down-projection tiles
+ *                             per row tile and f range, f ranges of the down projection
+ *   "wide"                    1 when the forward uses the wide tile shape
+ * Returns -1 for an unknown key, an invalid plan, B < 1 or B*k >= 2^31.
+ */
+int64_t moe_mk_forward_info(moe_mk_plan_t plan, int64_t B, const char *key);
+
+/*
  * Debug controls for tests (host): watchdog limit in GPU real-time ticks (100 MHz;
  * 0 restores the default of 2 s) and a flag word (MOE_MK_DEBUG_*).  They apply to later
  * forwards of this plan.  MOE_MK_DEBUG_DROP_NOTIFY makes the first grouping task skip

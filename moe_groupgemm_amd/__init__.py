@@ -74,6 +74,8 @@ def lib():
     L.moe_mk_workspace_error.restype = ctypes.c_int
     L.moe_mk_plan_info.argtypes = [vp, ctypes.c_char_p]
     L.moe_mk_plan_info.restype = i64
+    L.moe_mk_forward_info.argtypes = [vp, i64, ctypes.c_char_p]
+    L.moe_mk_forward_info.restype = i64
     L.moe_mk_plan_set_debug.argtypes = [vp, i64, i32]
     L.moe_mk_plan_set_debug.restype = ctypes.c_int
     L.moe_mk_trace_view.argtypes = [vp, i64, vp, sz, ctypes.POINTER(vp), ctypes.POINTER(i64)]
@@ -246,6 +248,13 @@ def moe_mk_workspace_error(plan: int, ws, stream=None) -> int:
 
 def moe_mk_plan_info(plan: int, key: str) -> int:
     v = int(lib().moe_mk_plan_info(plan, key.encode()))
+    if v < 0:
+        raise KeyError(key)
+    return v
+
+
+def moe_mk_forward_info(plan: int, B: int, key: str) -> int:
+    v = int(lib().moe_mk_forward_info(plan, B, key.encode()))
     if v < 0:
         raise KeyError(key)
     return v

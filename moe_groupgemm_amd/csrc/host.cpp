@@ -330,6 +330,30 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key) {
     return -1;
 }
 
+int64_t moe_mk_forward_info(moe_mk_plan_t plan, int64_t B, const char *key) {
+    if (!plan_ok(plan) || !key || B < 1 || B * plan->s.k >= ((int64_t)1 << 31)) return -1;
+    const mk::Shape &s = plan->s;
+    const mk::Counts c = mk::make_counts(s, B);
+    const mk::Tiles t = mk::tile_config(s, B);
+    struct {
+        const char *k;
+        int64_t v;
+    } tab[] = {{"T", c.T},
+               {"route_tasks", c.nR},
+               {"route_tokens_per_wave", c.tpw},
+               {"route_experts_per_task", c.reb},
+               {"combine_tasks", c.nC},
+               {"combine_tokens", mk::combine_tokens(B, s.k)},
+               {"BM", t.BM},
+               {"NB1", t.NB1},
+               {"NB2", t.NB2},
+               {"S", t.S},
+               {"wide", t.BM == mk::kWideBM ? 1 : 0}};
+    for (auto &e : tab)
+        if (std::strcmp(e.k, key) == 0) return e.v;
+    return -1;
+}
+
 moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks, int32_t flags) {
     if (!plan_ok(plan) || watchdog_ticks < 0) return MOE_MK_EINVAL;
     plan->watchdog = watchdog_ticks ? watchdog_ticks : kDefaultWatchdog;

@@ -51,35 +51,11 @@ def ctl_words(layer, B):
     return layer.routing(B)["ctl"].cpu().numpy()
 
 
-WAVES = 8           # waves per workgroup
-NARROW_BN = 128     # narrow GroupGEMM tile columns
-COMBINE_COLS = 2048
-
-
-def down_splits(B, k, f):
-    """K splits of the down projection the library uses at this batch size (narrow tiles)."""
-    a, nb1 = B * k, f // NARROW_BN
-    if a <= 1024 and f >= 8192 and nb1 % 4 == 0:
-        return 4
-    if a <= 1024 and f >= 4096 and nb1 % 2 == 0:
-        return 2
-    return 1
-
-
-def tile_config(B, k, E, d, f, wide_bn1=128, wide_bn2=256, wide_bm=256):
-    """(rows per tile, gate/up tiles per row tile, down tiles per row tile and split, splits):
-    wide tiles once an expert averages 128 rows (d, f multiples of the wide widths), else
-    64-row narrow tiles."""
-    if B * k >= 128 * E and d % wide_bn2 == 0 and f % wide_bn1 == 0:
-        return wide_bm, f // wide_bn1, d // wide_bn2, 1
-    return 64, f // NARROW_BN, d // NARROW_BN, down_splits(B, k, f)
-
-
-def expected_task_counts(hist, B, E, d, f, k):
-    BM, NB1, NB2, S = tile_config(B, k, E, d, f)
+def expected_task_counts(plan, hist, B):
+    """Tasks of each kind one forward runs, from the library's own per-batch choices
+    (moe_mk_forward_info) and the routing histogram."""
+    info = lambda key: mk.moe_mk_forward_info(plan, B, key)
+    BM, NB1, NB2, S = info("BM"), info("NB1"), info("NB2"), info("S")
     mt = int(sum((int(h) + BM - 1) // BM for h in hist))
-    # router tokens per wave, and experts per router task
-    tpw = 1 if B <= 512 else 8 if E % 4 == 0 and d % 128 == 0 and -(-B // 64) * -(-E // 16) >= 512 else 4
-    reb = 4 if tpw == 1 and E % 4 == 0 and d % 512 == 0 and -(-B // WAVES) * -(-E // 16) < 64 else 16
-    return {"route": -(-B // (WAVES * tpw)) * -(-E // reb), "topk": -(-B // 64), "scan": 1, "group": -(-B // 64),
-            "gemm1": mt * NB1, "gemm2": mt * S * NB2, "combine": -(-B // (8 if B >= 1024 and k <= 8 else 1 if B <= 64 else 4)) * -(-d // COMBINE_COLS)}
+    return {"route": info("route_tasks"), "topk": info("T"), "scan": 1, "group": info("T"),
+            "gemm1": mt * NB1, "gemm2": mt * S * NB2, "combine": info("combine_tasks")}

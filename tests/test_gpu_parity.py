@@ -14,8 +14,7 @@ import torch
 
 import moe_groupgemm_amd as mk
 import oracle
-from gpu_cases import (check_out, check_routing, ctl_words, dev_inputs, down_splits, expected_task_counts, log,
-                       routing_numpy, tile_config)
+from gpu_cases import check_out, check_routing, ctl_words, dev_inputs, expected_task_counts, log, routing_numpy
 from moe_inputs import CONFIGS, Config, device_weights, make_bias, make_wr, make_x, small_case, to_torch_bf16
 
 pytestmark = pytest.mark.gpu
@@ -29,6 +28,15 @@ def _free_memory():
     yield
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def _info(E, k, d, f, B, key):
+    """The library's per-batch choice `key` (moe_mk_forward_info) for a plan of this shape."""
+    plan = mk.moe_mk_plan(E, k, d, f, mk.MOE_MK_SCHED_STATIC)
+    try:
+        return mk.moe_mk_forward_info(plan, B, key)
+    finally:
+        mk.moe_mk_plan_destroy(plan)
 
 
 def run_small(x, Wr, bias, W1, W3, W2, k, sched, max_batch=None):
@@ -127,7 +135,7 @@ def test_zipf_bias_small():
 def test_down_projection_k_splits(f, S, sched):
     # small batches with a long f split the down projection's reduction into S ranges
     B, d, E, k = 21, 128, 4, 2
-    assert down_splits(B, k, f) == S
+    assert _info(E, k, d, f, B, "S") == S
     log(f"down-projection splits S={S} f={f} sched={SNAME[sched]}")
     cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=900 + S)
     full_check(x, Wr, bias, W1, W3, W2, k, sched, f"S={S}")
@@ -140,7 +148,7 @@ def test_wide_tiles(B, d, f, E, k, sched):
     # an expert averages >= 128 rows: 256-row tiles, ragged last tiles (some with rows for
     # one of the two 128-row halves only; experts of more than 256 rows with a second
     # tile), several K steps of 32
-    assert tile_config(B, k, E, d, f)[0] == 256
+    assert _info(E, k, d, f, B, "wide") == 1
     log(f"wide tiles B={B} d={d} f={f} E={E} k={k} sched={SNAME[sched]}")
     cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=1300 + B)
     full_check(x, Wr, bias, W1, W3, W2, k, sched, f"wide B={B}")
@@ -151,7 +159,7 @@ def test_wide_tiles_constant_input(sched):
     # every token identical: k experts take all 324 rows each (tiles of 256 and 68 rows)
     cfg, x, Wr, bias, W1, W3, W2 = small_case(324, 256, 256, 4, 2, seed=61)
     x[:] = x[0]
-    assert tile_config(324, 2, 4, 256, 256)[0] == 256
+    assert _info(4, 2, 256, 256, 324, "wide") == 1
     full_check(x, Wr, bias, W1, W3, W2, 2, sched, "wide constant input")
 
 
@@ -165,7 +173,7 @@ def test_wide_forward_thin_row_tiles(sched):
     E, k, d, f = len(counts), 2, 512, 256
     slots = np.repeat(np.arange(E), counts)
     B = len(slots) // k
-    assert tile_config(B, k, E, d, f)[0] == 256
+    assert _info(E, k, d, f, B, "wide") == 1
     cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=1700)
     x[:, :E] = 0
     x[np.arange(B), slots[:B]] = 0x4040       # bf16 3.0: slot 0
@@ -255,7 +263,7 @@ def test_rest_state_and_task_counts(B, E, d, f, sched):
     assert c[C["cq"]] == 0                             # static combine claim counter at rest
     assert c[C["ev_topk"]] == 0 and c[C["ev_scan"]] == 1 and c[C["ev_y"]] == 0  # events at rest
     hist = routing_numpy(layer, B)["hist"]
-    exp = expected_task_counts(hist, B, E, d, f, 2)
+    exp = expected_task_counts(layer.plan, hist, B)
     delta = c[C["dbg"]:C["dbg"] + 7] - before[C["dbg"]:C["dbg"] + 7]
     names = ["route", "topk", "scan", "group", "gemm1", "gemm2", "combine"]
     for i, n in enumerate(names):
@@ -422,7 +430,7 @@ def _full_config_of(cfg, sched, tokens="all"):
         if tokens == "all":
             toks = list(range(B))
         else:
-            toks = _tokens_of_every_row_tile(ref, cfg.k, tile_config(B, cfg.k, cfg.E, cfg.d, cfg.f)[0])
+            toks = _tokens_of_every_row_tile(ref, cfg.k, mk.moe_mk_forward_info(layer.plan, B, "BM"))
             assert len(toks) >= tokens, len(toks)
         ref_out = c.ref_out(B, toks)
         got = out.float().cpu().numpy()
@@ -449,7 +457,7 @@ def test_threshold_batches_one_plan(sched):
     tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
     layer = mk.MoELayer(E, k, d, f, tWr, t1, t3, t2, router_bias=tb, sched=sched, max_batch=Bmax)
     for B in (64, 65, 511, 512, 513, 1023, 1024, 1025, 1):
-        log(f"threshold batch B={B} tiles={'wide' if tile_config(B, k, E, d, f)[0] == 256 else 'narrow'} "
+        log(f"threshold batch B={B} tiles={'wide' if mk.moe_mk_forward_info(layer.plan, B, 'wide') else 'narrow'} "
             f"sched={SNAME[sched]}")
         out = layer(tx[:B])
         torch.cuda.synchronize()
@@ -510,7 +518,7 @@ def test_wide_long_k_every_token(sched):
     # f = 768 for the down projection), about 256 rows per expert so experts take one full
     # tile and some a second, thin one; every token compared
     cfg = Config("wide_long_k", d=2048, f=768, E=8, k=2, batches=(1024,), seed=808)
-    assert tile_config(1024, 2, 8, 2048, 768)[0] == 256
+    assert _info(8, 2, 2048, 768, 1024, "wide") == 1
     _full_config_of(cfg, sched)
 
 
