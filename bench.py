@@ -48,7 +48,7 @@ def parse():
                     help="skip measuring the box's achievable copy bandwidth and bf16 GEMM rate")
     ap.add_argument("--workloads", default="all",
                     help="configurations timed beside the headline one: 'all', 'none', or a comma list of "
-                    "config:sched (e.g. prefill:static,sweep:dynamic)")
+                    "config:sched[:policy] (e.g. prefill:static,sweep:dynamic,prefill:static:narrow_only)")
     return ap.parse_args()
 
 
@@ -263,8 +263,14 @@ def roofline(cfg_name, B, sched, alg_bytes, flops, kern_ms):
             "traffic": traffic}
 
 
-def measure_workload(cfg_name, sched_name, steps, warmup, dev, batches=None, cold_reps=10):
-    """Time the layer of one configuration (each of its batches on one plan and workspace)."""
+TILE_POLICIES = {"by_rows": 0, "narrow_only": 8, "batch_rule": 16}  # MOE_MK_DEBUG_* flags
+
+
+def measure_workload(cfg_name, sched_name, steps, warmup, dev, batches=None, cold_reps=10, policy="by_rows"):
+    """Time the layer of one configuration (each of its batches on one plan and workspace).
+    policy: the row-tile shape of each expert chosen from its row count ('by_rows', the
+    library's default), narrow for every expert ('narrow_only'), or chosen from the batch size alone
+    ('batch_rule': every expert wide when B*k >= 128*E) for comparison."""
     import numpy as np
     import torch
 
@@ -274,11 +280,12 @@ def measure_workload(cfg_name, sched_name, steps, warmup, dev, batches=None, col
     cfg = CONFIGS[cfg_name]
     batches = batches or cfg.batches
     sched = mk.MOE_MK_SCHED_STATIC if sched_name == "static" else mk.MOE_MK_SCHED_DYNAMIC
-    print(f"# workload {cfg_name} {sched_name} B={list(batches)}", file=sys.stderr, flush=True)
+    print(f"# workload {cfg_name} {sched_name} {policy} B={list(batches)}", file=sys.stderr, flush=True)
     tWr, tb, t1, t3, t2 = device_weights(cfg, device=dev)
     tx_all = to_torch_bf16(make_x(cfg, max(batches))).to(dev)
     layer = mk.MoELayer(cfg.E, cfg.k, cfg.d, cfg.f, tWr, t1, t3, t2, router_bias=tb, sched=sched,
                         max_batch=max(batches), device=dev)
+    mk.moe_mk_plan_set_debug(layer.plan, 0, TILE_POLICIES[policy])
     stream = torch.cuda.current_stream(dev)
     res = []
     for B in batches:
@@ -295,7 +302,10 @@ def measure_workload(cfg_name, sched_name, steps, warmup, dev, batches=None, col
         if layer.error():
             raise RuntimeError(f"device error word {layer.error()} ({cfg_name} B={B} {sched_name})")
         kern_ms = float(np.mean(ms))
-        e = {"workload": cfg.note, "config": cfg_name, "B": B, "sched": sched_name, "active_experts": active,
+        ctl = layer.routing(B)["ctl"].cpu().numpy()
+        e = {"workload": cfg.note, "config": cfg_name, "B": B, "sched": sched_name, "tile_policy": policy,
+             "row_tiles": int(ctl[mk.CTL["mt_total"]]), "wide_row_tiles": int(ctl[mk.CTL["mw"]]),
+             "active_experts": active,
              "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(ms)), "tokens_per_s": B / (kern_ms / 1e3),
              "roofline": roofline(cfg_name, B, sched_name, alg_bytes, flops, kern_ms),
              "hbm_frac": alg_bytes / (kern_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
@@ -314,10 +324,14 @@ def measure_workload(cfg_name, sched_name, steps, warmup, dev, batches=None, col
     return res
 
 
-# configurations listed beside the headline line (configuration, schedule)
-WORKLOADS = [("prefill", "static"), ("prefill", "dynamic"), ("deepseek_zipf", "static"),
-             ("deepseek_zipf", "dynamic"), ("sweep", "static"), ("sweep", "dynamic"), ("tiny", "static"),
-             ("tiny", "dynamic"), ("mixtral_decode", "static")]
+# configurations listed beside the headline line (configuration, schedule[, tile policy]);
+# the skewed and prefill-sized layers also run with each fixed row-tile shape, beside the
+# per-expert choice
+WORKLOADS = [("prefill", "static"), ("prefill", "dynamic"), ("prefill", "static", "narrow_only"),
+             ("prefill", "static", "batch_rule"), ("deepseek_zipf", "static"), ("deepseek_zipf", "dynamic"),
+             ("deepseek_zipf", "dynamic", "narrow_only"), ("deepseek_zipf", "dynamic", "batch_rule"),
+             ("sweep", "static"), ("sweep", "dynamic"), ("tiny", "static"), ("tiny", "dynamic"),
+             ("mixtral_decode", "static")]
 
 
 def main():
@@ -399,8 +413,9 @@ def main():
         wanted = WORKLOADS if args.workloads == "all" else \
             [tuple(w.split(":")) for w in args.workloads.split(",")]
         line["workloads"] = []
-        for name, sch in wanted:
-            line["workloads"].extend(measure_workload(name, sch, args.steps, args.warmup, dev))
+        for w in wanted:
+            line["workloads"].extend(measure_workload(w[0], w[1], args.steps, args.warmup, dev,
+                                                      policy=w[2] if len(w) > 2 else "by_rows"))
     if not args.no_peaks:
         copy_gbs, gemm_tflops = achievable_peaks(dev)
         line["achievable"] = {"copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,

@@ -24,8 +24,10 @@
  *   - Functions return a moe_mk_status_t; nothing throws or aborts across the ABI.
  *     Arguments are checked before anything is enqueued.
  *   - The batch size B is symbolic: it is an argument of every forward, never of the
- *     plan, and the kernel (compiled once per GroupGEMM tile shape, narrow or wide) serves
- *     every B with no recompilation and no graph.
+ *     plan, and one compiled kernel serves every B with no recompilation and no graph.
+ *     Counts that follow from B (routing tiles, router and combine task shapes, f splits of
+ *     the down projection) are kernel arguments; the GroupGEMM tile shape of each expert
+ *     (64-row or 256-row tiles) is chosen on the device from that expert's row count.
  */
 #ifndef MOE_MK_H
 #define MOE_MK_H
@@ -59,7 +61,7 @@ typedef enum {
  * Create a plan for a layer with E experts, top-k routing, model width d and expert
  * hidden width f, on the current HIP device.
  *   Supported: gfx950; d and f multiples of 128; 1 <= E <= 256; 1 <= k <= min(E, 16).
- *   The tile configuration depends on (E, k, d, f) only.
+ *   The plan fixes no batch size and no tile configuration (see moe_mk_forward_info).
  *   *plan receives a new plan (release with moe_mk_plan_destroy).
  * Errors: EINVAL (plan == NULL, bad sched), EUNSUPPORTED (shape, device), EHIP.
  */
@@ -143,8 +145,10 @@ moe_mk_status_t moe_mk_forward_noalloc(moe_mk_plan_t plan, const void *x, const 
  *   inv       int32 [B*k]    inverse of perm
  *   logits    fp32  [B, E]   router logits
  *   ctl       int32 [512]    control block (ctl[2] is the error word, see below; ctl[9] the
- *                            number of (expert, row tile) pairs; ctl[192..198] per-kind task
- *                            counters accumulated over forwards)
+ *                            number of (expert, row tile) pairs, ctl[10] how many of them are
+ *                            wide; ctl[192..198] per-kind task counters accumulated over
+ *                            forwards)
+ *   mt_*      int32 [mt_cap] the forward's row tiles (see the struct)
  * Errors: EINVAL, EWORKSPACE.
  */
 typedef struct {
@@ -156,6 +160,10 @@ typedef struct {
     const int32_t *inv;
     const float *logits;
     const int32_t *ctl;
+    const int32_t *mt_expert;  /* row tile i (i < ctl[9], in expert order): expert, first    */
+    const int32_t *mt_row0;    /* grouped row, rows; a row tile of more than BM rows is wide */
+    const int32_t *mt_rows;    /* (up to wide_BM rows), ctl[10] of them                       */
+    int64_t mt_cap;            /* length of the three row-tile arrays (host value)            */
 } moe_mk_routing_view_t;
 
 moe_mk_status_t moe_mk_routing_view(moe_mk_plan_t plan, int64_t B, const void *ws, size_t ws_bytes,
@@ -187,9 +195,13 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
  *   "T"                       64-token routing tiles (top-k and grouping tasks)
  *   "route_tasks"             router tasks; "route_tokens_per_wave", "route_experts_per_task"
  *   "combine_tasks"           combine tasks; "combine_tokens" tokens per combine task
- *   "BM" "NB1" "NB2" "S"      GroupGEMM row-tile rows, gate/up and down-projection tiles
- *                             per row tile and f range, f ranges of the down projection
- *   "wide"                    1 when the forward uses the wide tile shape
+ *   "NB1"                     gate/up tiles per row tile (either shape)
+ *   "NB2" "NB2_wide"          down-projection tiles per narrow row tile and f range, and
+ *                             per wide row tile
+ *   "S"                       f ranges of the down projection (1: not split)
+ *   "wide_ok"                 1 when experts may take wide row tiles in this forward (the
+ *                             kernel then gives them to experts with at least
+ *                             plan_info("wide_min_rows") rows; see moe_mk_routing_view)
  * Returns -1 for an unknown key, an invalid plan, B < 1 or B*k >= 2^31.
  */
 int64_t moe_mk_forward_info(moe_mk_plan_t plan, int64_t B, const char *key);
@@ -204,6 +216,9 @@ int64_t moe_mk_forward_info(moe_mk_plan_t plan, int64_t B, const char *key);
 #define MOE_MK_DEBUG_DROP_NOTIFY 1
 #define MOE_MK_DEBUG_TRACE 2  /* record per-task timestamps, see moe_mk_trace_view */
 #define MOE_MK_DEBUG_NO_PREFETCH 4  /* static schedule: no weight prefetch while a small batch is routed (A/B timing) */
+#define MOE_MK_DEBUG_NARROW_ONLY 8  /* every expert takes narrow row tiles (A/B timing of the tile choice) */
+#define MOE_MK_DEBUG_BATCH_RULE 16  /* tile shape from the batch size alone: every expert with more than BM
+                                       rows wide when B*k >= 128*E, else all narrow (A/B timing) */
 moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks, int32_t flags);
 
 /*

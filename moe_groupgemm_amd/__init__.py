@@ -25,10 +25,12 @@ MOE_MK_ERR_UNINIT = 8
 MOE_MK_DEBUG_DROP_NOTIFY = 1
 MOE_MK_DEBUG_TRACE = 2
 MOE_MK_DEBUG_NO_PREFETCH = 4
+MOE_MK_DEBUG_NARROW_ONLY = 8
+MOE_MK_DEBUG_BATCH_RULE = 16
 TASK_KINDS = ("route", "topk", "scan", "group", "gemm1", "gemm2", "combine")
 # control block words (see moe_mk_routing_view)
 CTL_WORDS = 512
-CTL = {"epoch": 0, "exit": 1, "err": 2, "ev_topk": 5, "ev_scan": 6, "magic": 8, "mt_total": 9,
+CTL = {"epoch": 0, "exit": 1, "err": 2, "ev_topk": 5, "ev_scan": 6, "magic": 8, "mt_total": 9, "mw": 10,
        "qhead": 32, "qtail": 64, "pf": 96, "cq": 128, "ev_y": 160, "dbg": 192, "xq": 256}
 
 _lib = None
@@ -43,7 +45,8 @@ class MoeMkError(RuntimeError):
 class _RoutingView(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("hist", ctypes.c_void_p),
                 ("exp_indptr", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("inv", ctypes.c_void_p),
-                ("logits", ctypes.c_void_p), ("ctl", ctypes.c_void_p)]
+                ("logits", ctypes.c_void_p), ("ctl", ctypes.c_void_p), ("mt_expert", ctypes.c_void_p),
+                ("mt_row0", ctypes.c_void_p), ("mt_rows", ctypes.c_void_p), ("mt_cap", ctypes.c_int64)]
 
 
 def lib():
@@ -225,7 +228,10 @@ def moe_mk_routing_view(plan: int, B: int, ws) -> dict:
             "perm": part(v.perm, B * k, torch.int32, (B * k,)),
             "inv": part(v.inv, B * k, torch.int32, (B * k,)),
             "logits": part(v.logits, B * E, torch.float32, (B, E)),
-            "ctl": part(v.ctl, CTL_WORDS, torch.int32, (CTL_WORDS,))}
+            "ctl": part(v.ctl, CTL_WORDS, torch.int32, (CTL_WORDS,)),
+            "mt_expert": part(v.mt_expert, v.mt_cap, torch.int32, (v.mt_cap,)),
+            "mt_row0": part(v.mt_row0, v.mt_cap, torch.int32, (v.mt_cap,)),
+            "mt_rows": part(v.mt_rows, v.mt_cap, torch.int32, (v.mt_cap,))}
 
 
 def moe_mk_trace_view(plan: int, B: int, ws):

@@ -164,11 +164,20 @@ mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const
     const mk::Tiles tl = mk::tile_config(s, B);
     P.NB1 = tl.NB1;
     P.NB2 = tl.NB2;
+    P.NB2w = tl.NB2w;
     P.S = tl.S;
-    P.BM = tl.BM;
+    P.wide_ok = tl.wide_ok;
+    // experts with at least wide_min rows take wide row tiles (always more than one routing
+    // tile's worth of rows, so a batch of one routing tile has narrow row tiles only)
+    if (plan->debug & MOE_MK_DEBUG_NARROW_ONLY)
+        P.wide_min = 1 << 30;
+    else if (plan->debug & MOE_MK_DEBUG_BATCH_RULE)
+        P.wide_min = B * s.k >= (int64_t)mk::kBatchRuleRows * s.E ? mk::kWideMinRows : 1 << 30;
+    else
+        P.wide_min = mk::kWideMinRows;
     {  // after the tile configuration: the prefetch follows the gate/up tiles
         const mk::Prefetch pf = (plan->debug & MOE_MK_DEBUG_NO_PREFETCH) ? mk::Prefetch{0, 0}
-                                                                           : mk::prefetch_plan(s, B, P.NB1, P.BM == mk::kWideBM);
+                                                                           : mk::prefetch_plan(s, B, P.NB1, false);
         P.pf_nt = pf.nt;
         P.pf_lines = pf.lines;
     }
@@ -273,6 +282,10 @@ moe_mk_status_t moe_mk_routing_view(moe_mk_plan_t plan, int64_t B, const void *w
     view->inv = (const int32_t *)(base + L.inv);
     view->logits = (const float *)(base + L.logits);
     view->ctl = (const int32_t *)(base + L.ctl);
+    view->mt_expert = (const int32_t *)(base + L.mt_expert);
+    view->mt_row0 = (const int32_t *)(base + L.mt_row0);
+    view->mt_rows = (const int32_t *)(base + L.mt_rows);
+    view->mt_cap = mk::make_counts(plan->s, cap).mt_cap;
     return MOE_MK_OK;
 }
 
@@ -344,11 +357,11 @@ int64_t moe_mk_forward_info(moe_mk_plan_t plan, int64_t B, const char *key) {
                {"route_experts_per_task", c.reb},
                {"combine_tasks", c.nC},
                {"combine_tokens", mk::combine_tokens(B, s.k)},
-               {"BM", t.BM},
                {"NB1", t.NB1},
                {"NB2", t.NB2},
+               {"NB2_wide", t.NB2w},
                {"S", t.S},
-               {"wide", t.BM == mk::kWideBM ? 1 : 0}};
+               {"wide_ok", t.wide_ok}};
     for (auto &e : tab)
         if (std::strcmp(e.k, key) == 0) return e.v;
     return -1;

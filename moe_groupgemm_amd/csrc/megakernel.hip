@@ -109,8 +109,12 @@ __shared__ Smem g_sm;
 //   [G1(0)] [G1(1)] [G2(0)] [G1(2)] [G2(1)] ... [G1(S-1)] [G2(S-2)] [G2(S-1)] [COMBINE]
 // where G1(s) holds the gate/up tiles whose columns fall in f range s (for every row
 // tile, Q = NB1/S per row tile) and G2(s) the down-projection tiles reducing over f range
-// s (NB2 per row tile).  Each G2 block comes one G1 block after the G1 block it consumes,
-// so the two GEMMs overlap instead of running as two phases.
+// s (N2 per row tile: NB2w tasks of kWideBN columns when the forward has a wide row tile,
+// where a narrow row tile's task runs kWideBN / kBN narrow tiles; else NB2 of kBN).  Row
+// tiles are numbered in expert order, so that an expert's tiles (a wide one and its thin
+// remainder) sit side by side in every list and share the expert's weights in L2.  Each G2
+// block comes one G1 block after the G1 block it consumes, so the two GEMMs overlap
+// instead of running as two phases.
 //
 // GroupGEMM blocks start at multiples of 8 and are padded to multiples of 8 (padding
 // positions are empty tasks).  Workgroups are dealt to the 8 XCDs round-robin, so in the
@@ -124,6 +128,8 @@ struct Bases {
     int K, S, G, M1, M1p, C, total;
     int q1, q2;    // tiles per G1(s) block and per G2(s) block
     int q1p, q2p;  // the same rounded up to multiples of 8 (block sizes)
+    int N2;        // down-projection tasks per row tile and f range
+    bool wide;     // the forward has wide row tiles
     bool known;    // GroupGEMM layout known once the scan has run
 };
 
@@ -137,14 +143,21 @@ __device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
     b.M1 = b.G + P.T;
     b.M1p = round8(b.M1);
     b.C = b.total = 0x7fffffff;
-    b.q1 = b.q2 = b.q1p = b.q2p = 0;
+    b.q1 = b.q2 = b.q1p = b.q2p = b.N2 = 0;
+    b.wide = false;
     b.known = false;
     return b;
 }
 
-__device__ __forceinline__ void complete_bases(const MK_C Params &P, Bases &b, int mt_total) {
+// mt_total row tiles, mw of them wide.  The counts are made visibly wave-uniform so that
+// the layout lives in scalar registers: held in vector registers across the task body, it
+// pushed the wide tiles' K loops into spills.
+__device__ __forceinline__ void complete_bases(const MK_C Params &P, Bases &b, int mt_total, int mw) {
+    mt_total = uni(mt_total);
+    b.wide = uni(mw) > 0;
+    b.N2 = b.wide ? P.NB2w : P.NB2;
     b.q1 = mt_total * (P.NB1 / P.S);
-    b.q2 = mt_total * P.NB2;
+    b.q2 = mt_total * b.N2;
     b.q1p = round8(b.q1);
     b.q2p = round8(b.q2);
     b.C = b.M1p + P.S * (b.q1p + b.q2p);
@@ -157,6 +170,10 @@ __device__ __forceinline__ int base_g1(const Bases &b, int s) {
 }
 __device__ __forceinline__ int base_g2(const Bases &b, int s, int S) {
     return s < S - 1 ? base_g1(b, s + 1) + b.q1p : b.M1p + S * b.q1p + (S - 1) * b.q2p;
+}
+// The layout as the scan task published it (row tiles and wide row tiles, one line).
+__device__ __forceinline__ void complete_bases_from_ctl(const MK_C Params &P, Bases &b) {
+    complete_bases(P, b, ld_relaxed(P.ctl + CTL_MT_TOTAL), ld_relaxed(P.ctl + CTL_MW));
 }
 
 // Decode a GroupGEMM task index: returns 1 for gate/up, 2 for down, 0 for a padding
@@ -684,11 +701,9 @@ __device__ __attribute__((noinline)) void route_wave_scalar(const MK_C Params &P
 }
 
 // Router task (tg, eb): tokens [kWaves*tpw*tg, +kWaves*tpw), wave w taking tpw of them,
-// experts [reb*eb, +reb) (reb = 16, or 4 at small batches).
-// INL: the eight-tokens-per-wave tile (nearly every register) is inlined instead of called,
-// so it saves no registers through memory; used by the wide-tile instantiation, where large
-// batches route (the other tiles fit in the caller-saved registers and stay calls).
-template <bool INL>
+// experts [reb*eb, +reb) (reb = 16, or 4 at small batches).  The eight-tokens-per-wave
+// tile (nearly every register) is inlined instead of called, so it saves no registers
+// through memory; the other tiles fit in the caller-saved registers and stay calls.
 __device__ __forceinline__ void task_route_body(const MK_C Params &P, int tg, int eb) {
     const int e0 = eb * P.reb;
     if (P.reb == 4) {  // one token per wave, d % 512 == 0, E % 4 == 0
@@ -706,19 +721,13 @@ __device__ __forceinline__ void task_route_body(const MK_C Params &P, int tg, in
         else
             route_tile<1, 128>(P, tg * kWaves, e0);
     } else if (P.tpw == 8) {  // d % 128 == 0
-        if constexpr (INL)
-            route_tile_body<8, 128>(P, tg * kWaves * 8, e0);
-        else
-            route_tile<8, 128>(P, tg * kWaves * 8, e0);
+        route_tile_body<8, 128>(P, tg * kWaves * 8, e0);
     } else {
         if (P.d % 256 == 0)
             route_tile<4, 256>(P, tg * kWaves * 4, e0);
         else
             route_tile<4, 128>(P, tg * kWaves * 4, e0);
     }
-}
-__device__ __attribute__((noinline)) void task_route(const MK_C Params &Pa, int tg, int eb) {
-    task_route_body<false>(uni_params(Pa), tg, eb);
 }
 
 // ------------------------------------------------------------------------------ TOPK
@@ -949,18 +958,64 @@ __device__ __forceinline__ int block_excl_scan(int v, int *part, int *total) {
     return pre + x - v;
 }
 
+// Row tiles of an expert with h rows: nw wide ones (kWideBM rows each, the last possibly
+// fewer but more than kBM) and nn narrow ones (kBM rows each, the last possibly fewer).
+// The shape is chosen per expert from its own row count ("RaMP": the best kernel
+// configuration follows the routing histogram, not the batch size): wide row tiles read
+// an expert's weight tiles once for up to kWideBM rows, narrow ones keep more weight bytes
+// in flight per workgroup and split the down projection at small batches.  A wide expert's
+// remainder of at most kBM rows goes to one narrow row tile.
+struct ExpertTiles {
+    int nw, nn, full, rem;
+};
+__device__ __forceinline__ ExpertTiles expert_tiles(const MK_C Params &P, int h) {
+    ExpertTiles t;
+    if (P.wide_ok && h >= P.wide_min) {
+        t.full = h / kWideBM;
+        t.rem = h - t.full * kWideBM;
+        t.nw = t.full + (t.rem > kBM ? 1 : 0);
+        t.nn = t.rem > 0 && t.rem <= kBM ? 1 : 0;
+    } else {
+        t.full = t.rem = t.nw = 0;
+        t.nn = (h + kBM - 1) / kBM;
+    }
+    return t;
+}
+
+// Publish expert e's row tiles (h rows from grouped row off) as row tiles mbase.. (its wide
+// ones first), each with its gate/up events armed (NB1/S tiles per f range).  A row tile's
+// shape follows from its rows: wide ones hold more than kBM rows, narrow ones at most kBM.
+__device__ __forceinline__ void publish_row_tiles(const MK_C Params &P, int e, int h, int off, const ExpertTiles &t,
+                                                  int mbase) {
+    for (int m = 0; m < t.nw; ++m) {
+        const int i = mbase + m;
+        pub(P.mt_expert + i, e);
+        pub(P.mt_row0 + i, off + m * kWideBM);
+        pub(P.mt_rows + i, min(kWideBM, h - m * kWideBM));
+        for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+    }
+    const int r0 = t.nw ? t.full * kWideBM : 0;  // a wide expert's remainder, or all rows
+    for (int m = 0; m < t.nn; ++m) {
+        const int i = mbase + t.nw + m;
+        pub(P.mt_expert + i, e);
+        pub(P.mt_row0 + i, off + r0 + m * kBM);
+        pub(P.mt_rows + i, min(kBM, h - r0 - m * kBM));
+        for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+    }
+}
+
 // hist[e] = sum_t tile_hist[t,e]; exp_indptr = exclusive prefix sum; tile_off[t,e] =
-// exp_indptr[e] + rows of e in tiles before t; row tiles of P.BM rows per expert; arms
-// ev_h[mt,s] with the gate/up tiles of each (row tile, f range), ev_y with the number of
-// down-projection tiles and ev_exp[e] with hist[e] ("Core method": the prefix sum decides
-// how many GroupGEMM tiles each expert triggers).  Events are at rest (zero) and nothing
-// decrements them before the scan is published, so arming is a plain store.  Returns the
-// number of row tiles.
-__device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa) {
+// exp_indptr[e] + rows of e in tiles before t; each expert's row tiles (expert_tiles);
+// arms ev_h[mt,s] with the gate/up tiles of each (row tile, f range), ev_y with the number
+// of down-projection tiles and ev_exp[e] with hist[e] ("Core method": the prefix sum
+// decides how many GroupGEMM tiles each expert triggers).  Events are at rest (zero) and
+// nothing decrements them before the scan is published, so arming is a plain store.
+// Returns the number of row tiles and (mw) of wide ones.
+__device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &mw_out) {
     const MK_C Params &P = uni_params(Pa);
     ScanSmem &ss = g_sm.u.s;
     const int e = threadIdx.x;
-    const int E = P.E, BM = P.BM;
+    const int E = P.E;
     int *tb = ss.tiles;
     const int rows = kScanStage / E;  // tile_hist rows staged per round (coalesced loads)
     // R threads per expert: thread (ex, r) = (tid % E, tid / E) takes the r-th contiguous
@@ -1001,30 +1056,27 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa) {
     int h = 0;
     if (e < E)
         for (int q = 0; q < R; ++q) h += ss.ps[q * E + e];
-    const int mt = (h + BM - 1) / BM;
-    int total_h, total_mt;
+    const ExpertTiles et = expert_tiles(P, e < E ? h : 0);
+    int total_h, total_mt, total_w;
     const int off = block_excl_scan(h, ss.part, &total_h);
-    const int mbase = block_excl_scan(mt, ss.part, &total_mt);
+    const int mbase = block_excl_scan(et.nw + et.nn, ss.part, &total_mt);
+    block_excl_scan(et.nw, ss.part, &total_w);
     if (e < E) {
         ss.carry[e] = off;
         pub(P.hist + e, h);
         pub(P.indptr + e, off);
         pub(P.mt_base + e, mbase);
-        for (int m = 0; m < mt; ++m) {
-            const int i = mbase + m;
-            pub(P.mt_expert + i, e);
-            pub(P.mt_row0 + i, off + m * BM);
-            pub(P.mt_rows + i, min(BM, h - m * BM));
-            for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
-        }
+        publish_row_tiles(P, e, h, off, et, mbase);
         if (h) pub(P.ev_exp + e, h);
     }
     if (e == 0) {
         pub(P.indptr + E, total_h);
         pub(P.mt_base + E, total_mt);
         st_relaxed(P.ctl + CTL_MT_TOTAL, total_mt);
-        pub(P.ctl + CTL_EV_Y, total_mt * P.S * P.NB2);
+        st_relaxed(P.ctl + CTL_MW, total_w);
+        pub(P.ctl + CTL_EV_Y, P.S * total_mt * (total_w > 0 ? P.NB2w : P.NB2));
     }
+    mw_out = total_w;
     // per-tile row offsets: exp_indptr[e] + rows of e in earlier tiles; a thread's chunk
     // starts after the chunks of lower r and the tiles of earlier rounds
     for (int t0 = 0; t0 < P.T; t0 += rows) {
@@ -1863,16 +1915,13 @@ __device__ __attribute__((noinline)) void narrow_gemm2(const MK_C Params &Pa, in
     gemm2_tile<AR>(P, uni(e), uni(row0), uni(nrows), uni(n), uni(sp), uni(mt));
 }
 
-// The tile variant is chosen from the forward's tile shape and the tile's actual rows.
-// A wide-shape task whose row tile holds at most kBM rows (the last row tile of an expert
-// with a few rows past a multiple of kWideBM) streams its whole weight tile for those few
-// rows, so its time is set by the weight bytes it keeps in flight.  The narrow tile code
-// keeps about twice as many weight bytes in flight per stage ring, so such a task runs as
-// narrow tiles over the same columns (one for gate/up, kWideBN / kBN for the down
-// projection); the output and its events are the same.
+// The tile code follows the row tile's rows: a row tile of more than kBM rows is a wide one
+// (see expert_tiles), narrow row tiles of at most 16 rows stage only 16 A rows.  In a forward
+// with wide row tiles a down-projection task spans kWideBN columns, which a narrow row tile
+// covers with kWideBN / kBN narrow tiles (no f splits then).
+// WIDE: the code may meet wide row tiles (the task loop of forwards that have them).
 template <bool WIDE>
 __device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
-    static_assert(kWideBN1 == kBN, "a wide gate/up tile spans one narrow tile's columns");
     if (WIDE && nrows > kBM)
         wide_gemm1(P, e, row0, nrows, n);
     else if (nrows <= 16)
@@ -1882,13 +1931,11 @@ __device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0
 }
 template <bool WIDE>
 __device__ __forceinline__ void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n, int sp, int mt) {
-    if constexpr (WIDE) {
-        static_assert(kWideBN % kBN == 0, "a wide down tile spans whole narrow tiles");
-        if (nrows > kBM) {
-            wide_gemm2(P, e, row0, nrows, n);
-            return;
-        }
-        for (int q = 0; q < kWideBN / kBN; ++q) {  // S = 1 with wide tiles
+    static_assert(kWideBN % kBN == 0, "a wide down tile spans whole narrow tiles");
+    if (WIDE && nrows > kBM) {
+        wide_gemm2(P, e, row0, nrows, n);
+    } else if (WIDE) {
+        for (int q = 0; q < kWideBN / kBN; ++q) {  // S = 1 with wide row tiles
             if (nrows <= 16)
                 narrow_gemm2<16>(P, e, row0, nrows, (kWideBN / kBN) * n + q, 0, mt);
             else
@@ -2041,7 +2088,7 @@ __device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs
     }
     if (!dyn) return;
     // push the gate/up tiles of every expert this tile completed
-    if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));  // block bases for the pushes
+    if (!bs.known) complete_bases_from_ctl(P, bs);  // block bases for the pushes
     int m0 = 0, nm = 0;
     if (fire) {
         m0 = ld_relaxed(P.mt_base + e);
@@ -2090,7 +2137,9 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
     TopkSmem &ts = g_sm.u.t;
     FusedWork &W = ts.fw;
     const int e = threadIdx.x;
-    const int E = P.E, k = P.k, BM = P.BM;
+    // A batch of one routing tile gives an expert at most kTileTokens rows, fewer than
+    // wide_min: every row tile is narrow (at most one per expert).
+    const int E = P.E, k = P.k, BM = kBM;
     int skip = -1;
     if (P.debug & 1) {  // debug: drop the notification of the first expert with rows
         for (int x = 0; x < E; ++x)
@@ -2126,10 +2175,11 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
         pub(P.indptr + E, total_h);
         pub(P.mt_base + E, total_mt);
         st_relaxed(P.ctl + CTL_MT_TOTAL, total_mt);
+        st_relaxed(P.ctl + CTL_MW, 0);
         pub(P.ctl + CTL_EV_Y, total_mt * P.S * P.NB2);
     }
     count_task(P, K_SCAN);
-    complete_bases(P, bs, total_mt);
+    complete_bases(P, bs, total_mt, 0);
     if (dyn && threadIdx.x == 0) {
         // tickets: routers, this task, and the GroupGEMM and combine tasks
         const int real = bs.K + 1 + P.S * (bs.q1 + bs.q2) + P.nC;
@@ -2226,17 +2276,19 @@ __device__ __forceinline__ void route_task_coords(const MK_C Params &P, int g, i
 }
 
 // Runs task g (obtained at time t0).  Returns false when the forward must be abandoned.
-// WIDE: the forward's GroupGEMM tiles are wide (P.BM == kWideBM), else narrow.
+// WIDE: the copy of the task code that can run wide row tiles.  The other copy (used until a
+// forward is known to have them, and throughout forwards that have none) leaves them out, so
+// its routing and narrow-tile paths are compiled without the wide tiles' register pressure;
+// it returns kNeedWide, without running the task, for a GroupGEMM task of a forward that
+// has wide row tiles.
+constexpr int kTaskDone = 1, kNeedWide = 2;
 template <bool WIDE>
-__device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs, unsigned long long t0) {
+__device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, unsigned long long t0) {
     const bool dyn = P.sched != 0;
     if (g < bs.K) {  // ---------------------------------------------------------- ROUTE
         int tg, eb;
         route_task_coords(P, g, tg, eb);
-        if constexpr (WIDE)
-            task_route_body<true>(P, tg, eb);
-        else
-            task_route(P, tg, eb);
+        task_route_body(P, tg, eb);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_ROUTE);
         const int t = tg / route_groups_per_tile(P);
@@ -2244,13 +2296,13 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
         if (dyn && (tg % route_groups_per_tile(P)) == 0 && eb == 0) delta += route_tasks_of_tile(P, t);
         if (wg_notify(P, P.ev_logit + t, delta) && dyn) wg_push_range(P, bs.K + t, 1);
         trace_task(P, g, K_ROUTE, t0, t0, t2);
-        return true;
+        return kTaskDone;
     }
     if (g < bs.S) {  // ---------------------------------------------------------- TOPK
         const int t = g - bs.K;
         if (!dyn) {
             if (threadIdx.x == 0) add_relaxed(P.ev_logit + t, route_tasks_of_tile(P, t));  // arm
-            if (!wg_wait_zero(P, P.ev_logit + t)) return false;
+            if (!wg_wait_zero(P, P.ev_logit + t)) return 0;
         }
         const unsigned long long t1 = now_ticks();
         task_topk(P, t);
@@ -2266,25 +2318,26 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
             // (dynamic ones are pushed, and no task waits on the event)
             if (!dyn) wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
             trace_task(P, g, K_TOPK, t0, t1, t2, t3, t4);
-            return true;
+            return kTaskDone;
         }
         int delta = -1;
         if (dyn && t == 0) delta += P.T;
         if (wg_notify(P, P.ctl + CTL_EV_TOPK, delta) && dyn) wg_push_range(P, bs.S, 1);
         trace_task(P, g, K_TOPK, t0, t1, t2);
-        return true;
+        return kTaskDone;
     }
     if (g == bs.S) {  // --------------------------------------------------------- SCAN
-        if (P.T == 1) return true;  // a single routing tile is scanned by its top-k task
+        if (P.T == 1) return kTaskDone;  // a single routing tile is scanned by its top-k task
         if (!dyn) {
             if (threadIdx.x == 0) add_relaxed(P.ctl + CTL_EV_TOPK, P.T);  // arm
-            if (!wg_wait_zero(P, P.ctl + CTL_EV_TOPK)) return false;
+            if (!wg_wait_zero(P, P.ctl + CTL_EV_TOPK)) return 0;
         }
         const unsigned long long t1 = now_ticks();
-        const int mt_total = task_scan(P);
+        int mw = 0;
+        const int mt_total = task_scan(P, mw);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_SCAN);
-        complete_bases(P, bs, mt_total);
+        complete_bases(P, bs, mt_total, mw);
         wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
         if (dyn) {
             wg_push_range(P, bs.G, P.T);
@@ -2296,59 +2349,63 @@ __device__ __forceinline__ bool run_task(const MK_C Params &P, int g, Bases &bs,
             }
         }
         trace_task(P, g, K_SCAN, t0, t1, t2);
-        return true;
+        return kTaskDone;
     }
     if (g < bs.M1p) {  // -------------------------------------------------------- GROUP
         const int t = g - bs.G;
-        if (t >= P.T) return true;  // padding before the GroupGEMM blocks
-        if (P.T == 1) return true;  // a single routing tile is grouped by its top-k task
-        if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) return false;
+        if (t >= P.T) return kTaskDone;  // padding before the GroupGEMM blocks
+        if (P.T == 1) return kTaskDone;  // a single routing tile is grouped by its top-k task
+        if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) return 0;
         const unsigned long long t1 = now_ticks();
         group_and_notify(P, bs, t, dyn);
         trace_task(P, g, K_GROUP, t0, t1, now_ticks());
-        return true;
+        return kTaskDone;
     }
-    if (!bs.known) complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
+    if (!bs.known) complete_bases_from_ctl(P, bs);
+    if constexpr (!WIDE) {
+        if (bs.wide && g < bs.C) return kNeedWide;
+    }
     if (g < bs.C) {
         int sp, j;
-        const int kind = decode_gemm(bs, P.S, !dyn && P.BM == kWideBM, g, sp, j);
-        if (kind == 0) return true;  // padding position
+        // static schedule with wide row tiles: each XCD takes a contiguous eighth of a block
+        const int kind = decode_gemm(bs, P.S, !dyn && bs.wide, g, sp, j);
+        if (kind == 0) return kTaskDone;  // padding position
         const int Q = P.NB1 / P.S;
         if (kind == 1) {  // ---------------------------------------------------- GEMM1
             const int mt = j / Q, n = sp * Q + (j - (j / Q) * Q);
-            const int e = P.mt_expert[mt];
-            if (!dyn && !wg_wait_zero(P, P.ev_exp + e)) return false;
+            const int e = uni(P.mt_expert[mt]);
+            if (!dyn && !wg_wait_zero(P, P.ev_exp + e)) return 0;
             const unsigned long long t1 = now_ticks();
-            task_gemm1<WIDE>(P, e, P.mt_row0[mt], P.mt_rows[mt], n);
+            task_gemm1<WIDE>(P, e, uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), n);
             const unsigned long long t2 = now_ticks();
             count_task(P, K_GEMM1);
             // f range sp of this row tile complete: its down-projection tiles are ready
             if (wg_notify(P, P.ev_h + mt * P.S + sp, -1) && dyn)
-                wg_push_range(P, base_g2(bs, sp, P.S) + mt * P.NB2, P.NB2);
+                wg_push_range(P, base_g2(bs, sp, P.S) + mt * bs.N2, bs.N2);
             trace_task(P, g, K_GEMM1, t0, t1, t2);
-            return true;
+            return kTaskDone;
         }
         // --------------------------------------------------------------------- GEMM2
-        const int mt = j / P.NB2, n = j - mt * P.NB2;
-        if (!dyn && !wg_wait_zero(P, P.ev_h + mt * P.S + sp)) return false;
+        const int mt = j / bs.N2, n = j - mt * bs.N2;
+        if (!dyn && !wg_wait_zero(P, P.ev_h + mt * P.S + sp)) return 0;
         const unsigned long long t1 = now_ticks();
-        task_gemm2<WIDE>(P, P.mt_expert[mt], P.mt_row0[mt], P.mt_rows[mt], n, sp, mt);
+        task_gemm2<WIDE>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), n, sp, mt);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_GEMM2);
         if (wg_notify(P, P.ctl + CTL_EV_Y, -1) && dyn) wg_push_range(P, bs.C, P.nC);
         trace_task(P, g, K_GEMM2, t0, t1, t2);
-        return true;
+        return kTaskDone;
     }
     {  // ------------------------------------------------------------------------ COMBINE
         const int c = g - bs.C;
-        if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_Y)) return false;
+        if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_Y)) return 0;
         const unsigned long long t1 = now_ticks();
         task_combine(P, c);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_COMBINE);
         __syncthreads();
         trace_task(P, g, K_COMBINE, t0, t1, t2);
-        return true;
+        return kTaskDone;
     }
 }
 
@@ -2452,8 +2509,73 @@ __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
     return g;
 }
 
-// WIDE: the instantiation for wide GroupGEMM tiles (P.BM == kWideBM), else narrow ones.
-template <bool WIDE>
+// Static schedule: the next task of this workgroup.
+//   Routing tasks (phase 0): workgroup w runs g = w, w + G, ... below the GroupGEMM blocks.
+//   GroupGEMM positions (phase 1, once the scan event fired) are claimed per XCD.  Position p
+// belongs to XCD p % 8 (the blocks start at multiples of 8); the workgroups of an XCD
+// (w % 8 == x, as the hardware deals them) take that XCD's positions in increasing order from
+// its claim counter, so tiles adjacent in the list start together and share operands in L2.
+// Each XCD's list is in topological order, so the smallest unfinished task of the forward
+// always has its inputs done or in progress.
+//   With narrow row tiles only (and at least two GroupGEMM positions per workgroup), once its
+// XCD's list has no GroupGEMM position left, a workgroup takes unclaimed GroupGEMM positions
+// of the other XCDs from their counters (thread 0 looks at a counter first and claims only
+// while it shows a GroupGEMM position), so that the XCDs finish the GroupGEMM phase together
+// even when skewed routing gives them unequal work.  Combine tasks, which wait for every
+// down-projection tile and read rows written on every XCD, are then claimed from one counter
+// shared by all workgroups; a workgroup reaches them only when no GroupGEMM position is left
+// unclaimed.  A claim is exclusive whoever makes it and a claimed position is always run, so
+// every task runs exactly once.  With wide row tiles every position, combine included, stays
+// on its own XCD: there taking other XCDs' tiles made the forward slower (the stolen tiles
+// lose their L2 neighbours).
+// Returns -1 when this workgroup has nothing left, -2 on an error.
+struct StaticCursor {
+    int g;       // next routing position (phase 0)
+    int phase;   // 0 routing, 1 GroupGEMM and combine claims
+    int y;       // list of XCD x + y being claimed from: 0 its own, 1..7 the others, 8 combine
+    bool steal;  // take other XCDs' positions once the own list is done
+};
+__device__ __forceinline__ int static_next(const MK_C Params &P, Bases &bs, StaticCursor &c) {
+    if (c.phase == 0) {
+        if (c.g < bs.M1p) {
+            const int g = c.g;
+            c.g += gridDim.x;
+            return g;
+        }
+        if (!wg_wait_zero_prefetching(P, P.ctl + CTL_EV_SCAN)) return -2;
+        complete_bases_from_ctl(P, bs);
+        // (a forward of a few tiles per workgroup gains nothing from stealing, and its idle
+        // workgroups would only load the counters that the busy ones claim from)
+        c.steal = !bs.wide && bs.C - bs.M1p >= 2 * (int)gridDim.x;
+        c.phase = 1;
+    }
+    const int x = blockIdx.x & 7;
+    for (;;) {
+        if (!c.steal || c.y < 8) {
+            const int xs = (x + c.y) & 7;
+            if (threadIdx.x == 0) {
+                MK_G int *ctr = P.ctl + CTL_XQ + 32 * xs;
+                g_sm.bcast[3] = c.y == 0 || bs.M1p + 8 * ld_relaxed(ctr) + xs < bs.C ? add_relaxed(ctr, 1) : -1;
+            }
+            __syncthreads();
+            const int cl = g_sm.bcast[3];
+            __syncthreads();
+            const int g = bs.M1p + 8 * cl + xs;
+            if (!c.steal) return g >= bs.total ? -1 : g;
+            if (cl < 0 || g >= bs.C) {  // no GroupGEMM position left in this list
+                ++c.y;
+                continue;
+            }
+            return g;
+        }
+        if (threadIdx.x == 0) g_sm.bcast[3] = add_relaxed(P.ctl + CTL_CQ, 1);
+        __syncthreads();
+        const int g = bs.C + g_sm.bcast[3];
+        __syncthreads();
+        return g >= bs.total ? -1 : g;
+    }
+}
+
 __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
     // Parg is the first kernel argument, at offset 0 of the kernel-argument segment: read it
     // there in place rather than from a private copy.
@@ -2484,70 +2606,39 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
         return;
     }
     Bases bs = initial_bases(P);
-    if (P.sched == 0) {
-        // Routing tasks: workgroup w runs g = w, w + G, ... below the GroupGEMM blocks.
-        bool ok = true;
-        for (int g = blockIdx.x; ok && g < bs.M1p; g += gridDim.x) ok = run_task<WIDE>(P, g, bs, now_ticks());
-        // GroupGEMM positions are claimed per XCD.  Position p belongs to XCD p % 8 (the
-        // blocks start at multiples of 8); the workgroups of an XCD (w % 8 == x, as the
-        // hardware deals them) take that XCD's positions in increasing order from its claim
-        // counter, so tiles adjacent in the list start together and share operands in L2.
-        // Each XCD's list is in topological order, so the smallest unfinished task of the
-        // forward always has its inputs done or in progress.
-        // Narrow tiles: once its XCD's list has no GroupGEMM position left, a workgroup
-        // takes unclaimed GroupGEMM positions of the other XCDs from their counters (thread
-        // 0 looks at a counter first and claims only while it shows a GroupGEMM position),
-        // so that the XCDs finish the GroupGEMM phase together even when skewed routing
-        // gives them unequal work.  Combine tasks, which wait for every down-projection tile
-        // and read rows written on every XCD, are then claimed from one counter shared by
-        // all workgroups; a workgroup reaches them only when no GroupGEMM position is left
-        // unclaimed.  A claim is exclusive whoever makes it and a claimed position is always
-        // run, so every task runs exactly once.  (One call site runs the tasks: the task code
-        // is large, and a second inlined copy slowed every tile.)  Wide tiles, and forwards
-        // of fewer than two GroupGEMM positions per workgroup, keep every position, combine
-        // included, on its own XCD: there taking other XCDs' tiles made the forward slower.
-        if (ok && wg_wait_zero_prefetching(P, P.ctl + CTL_EV_SCAN)) {
-            complete_bases(P, bs, ld_relaxed(P.ctl + CTL_MT_TOTAL));
-            const int x = blockIdx.x & 7;
-            // (a forward of a few tiles per workgroup gains nothing, and its idle workgroups
-            // would only load the counters that the busy ones claim from)
-            const bool steal = !WIDE && bs.C - bs.M1p >= 2 * (int)gridDim.x;
-            int y = 0;  // list of XCD x + y: 0 its own, 1..7 the others, 8: combine tasks
-            for (;;) {
-                int g;
-                if (!steal || y < 8) {
-                    const int xs = (x + y) & 7;
-                    if (threadIdx.x == 0) {
-                        MK_G int *ctr = P.ctl + CTL_XQ + 32 * xs;
-                        g_sm.bcast[3] = y == 0 || bs.M1p + 8 * ld_relaxed(ctr) + xs < bs.C ? add_relaxed(ctr, 1) : -1;
-                    }
-                    __syncthreads();
-                    const int c = g_sm.bcast[3];
-                    __syncthreads();
-                    g = bs.M1p + 8 * c + xs;
-                    if (!steal) {
-                        if (g >= bs.total) break;
-                    } else if (c < 0 || g >= bs.C) {  // no GroupGEMM position left in this list
-                        ++y;
-                        continue;
-                    }
-                } else {
-                    if (threadIdx.x == 0) g_sm.bcast[3] = add_relaxed(P.ctl + CTL_CQ, 1);
-                    __syncthreads();
-                    g = bs.C + g_sm.bcast[3];
-                    __syncthreads();
-                    if (g >= bs.total) break;
-                }
-                if (!run_task<WIDE>(P, g, bs, now_ticks())) break;
-            }
+    // Two task loops, each with one call site of its copy of the task code: the first runs
+    // forwards without wide row tiles, and every task until a forward is known to have them;
+    // the second takes over from there (with the task that found out, if any).
+    StaticCursor cur;
+    cur.g = blockIdx.x;
+    cur.phase = 0;
+    cur.y = 0;
+    cur.steal = false;
+    int g = -1;
+    unsigned long long t0 = 0;
+    bool wide_loop = false, pending = false;
+    for (;;) {
+        t0 = now_ticks();
+        g = uni(P.sched != 0 ? wg_pop(P) : static_next(P, bs, cur));
+        if (g < 0) break;
+        const int r = run_task<false>(P, g, bs, t0);
+        if (r != kTaskDone) {
+            wide_loop = pending = r == kNeedWide;
+            break;
         }
-    } else {
-        for (;;) {
-            const unsigned long long t0 = now_ticks();
-            const int g = wg_pop(P);
+        if (bs.known && bs.wide) {
+            wide_loop = true;
+            break;
+        }
+    }
+    while (wide_loop) {
+        if (!pending) {
+            t0 = now_ticks();
+            g = uni(P.sched != 0 ? wg_pop(P) : static_next(P, bs, cur));
             if (g < 0) break;
-            if (!run_task<WIDE>(P, g, bs, t0)) break;
         }
+        pending = false;
+        if (run_task<true>(P, g, bs, t0) != kTaskDone) break;
     }
     // Leave: the last workgroup out puts the control block back to its rest state.
     __syncthreads();
@@ -2612,10 +2703,7 @@ __global__ void moe_ws_init_ctl(int *ctl_generic) {
 
 // ------------------------------------------------------------------------------ launch glue
 hipError_t mk_launch(const mk::Params &p, int grid, hipStream_t stream) {
-    if (p.BM == mk::kWideBM)
-        hipLaunchKernelGGL(mk::moe_megakernel<true>, dim3(grid), dim3(mk::kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(mk::moe_megakernel<false>, dim3(grid), dim3(mk::kThreads), 0, stream, p);
+    hipLaunchKernelGGL(mk::moe_megakernel, dim3(grid), dim3(mk::kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -2662,11 +2750,5 @@ hipError_t mk_scratch(void **ptr, size_t *bytes) {
 }
 
 hipError_t mk_occupancy(int *blocks_per_cu) {
-    // both instantiations: the persistent grid must be co-resident for either
-    int narrow = 0, wide = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&narrow, mk::moe_megakernel<false>, mk::kThreads, 0);
-    if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&wide, mk::moe_megakernel<true>, mk::kThreads, 0);
-    *blocks_per_cu = narrow < wide ? narrow : wide;
-    return e;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk::moe_megakernel, mk::kThreads, 0);
 }

@@ -40,6 +40,7 @@ enum CtlWord {
     CTL_EV_SCAN = 6,    // event: scan done; rest value 1
     CTL_MAGIC = 8,      // set by workspace init
     CTL_MT_TOTAL = 9,   // number of (expert, row-tile) pairs, written by the scan task
+    CTL_MW = 10,        // how many of them are wide row tiles, written by the scan task
     CTL_TOTAL64 = 12,   // int64 at words 12..13: (epoch << 32) | task count (dynamic mode)
     CTL_QHEAD = 32,     // dynamic queue: next ticket
     CTL_QTAIL = 64,     // dynamic queue: slots reserved by pushers
@@ -109,26 +110,41 @@ inline int max_down_splits(const Shape &s) {
     return 1;
 }
 
-// GroupGEMM tiles of one forward.  Narrow: kBM x kBN tiles (decode and mid-size batches).
-// Wide: when an expert averages at least kWideMinRows rows, tiles of kWideBM rows,
-// kWideBN1 columns of each gate/up weight and kWideBN columns of the down projection, so
-// that each staged byte serves more multiply-adds.  Workspace sizes are bounded with the
-// narrow counts, which are never smaller.
-constexpr int kWideMinRows = 128;
+// GroupGEMM tiles.  Every expert's rows are cut into row tiles of one of two shapes, chosen
+// per expert on the device from its row count once the histogram is known (the scan task):
+//   narrow  kBM = 64 rows; gate/up tiles of kBN = 128 columns of each weight, down-projection
+//           tiles of kBN columns, the down projection optionally split over f (S ranges);
+//   wide    kWideBM = 256 rows; gate/up tiles of kWideBN1 = 128 columns of each weight,
+//           down-projection tiles of kWideBN = 256 columns, so that each staged byte serves
+//           more multiply-adds.  An expert with wide row tiles puts a remainder of at most
+//           kBM rows in one narrow row tile.
+// Wide row tiles need S = 1 and d, f multiples of their widths.  By default they go to every
+// expert with more than kBM rows: such an expert needs two or more narrow row tiles, each of
+// which streams all of its weight tiles again, where wide row tiles stream them once per
+// kWideBM rows (debug flags force narrow tiles, or a choice from the batch size alone).
+constexpr int kWideMinRows = kBM + 1;
+// The batch-size-only choice the debug flag reproduces: every expert wide when the batch
+// averages at least this many rows per expert.
+constexpr int kBatchRuleRows = 128;
 constexpr int kWideBM = 256;
 constexpr int kWideBN = 256;   // down-projection columns per wide tile
 constexpr int kWideBN1 = 128;  // gate/up columns of each weight per wide tile
 constexpr int kWideBK = 32;
+static_assert(kWideBN1 == kBN, "gate/up tiles of both shapes span the same columns");
 struct Tiles {
-    int BM, NB1, NB2, S;
+    int NB1;     // gate/up tiles per row tile (f / 128, both shapes)
+    int NB2;     // down-projection tiles per narrow row tile and f range (d / 128)
+    int NB2w;    // down-projection tiles per wide row tile (d / 256)
+    int S;       // f ranges of the down projection
+    int wide_ok; // wide row tiles allowed in this forward
 };
 inline Tiles tile_config(const Shape &s, int64_t B) {
     Tiles t;
-    const bool wide = B * s.k >= (int64_t)kWideMinRows * s.E && s.d % kWideBN == 0 && s.f % kWideBN1 == 0;
-    t.BM = wide ? kWideBM : kBM;
-    t.NB1 = s.f / (wide ? kWideBN1 : kBN);
-    t.NB2 = s.d / (wide ? kWideBN : kBN);
-    t.S = wide ? 1 : down_splits(s, B);
+    t.NB1 = s.f / kBN;
+    t.NB2 = s.d / kBN;
+    t.NB2w = s.d / kWideBN;
+    t.S = down_splits(s, B);
+    t.wide_ok = t.S == 1 && s.d % kWideBN == 0 && s.f % kWideBN1 == 0;
     return t;
 }
 
@@ -256,11 +272,12 @@ struct Params {
     int B, E, k, d, f;
     int sched;       // 0 static, 1 dynamic
     int debug;       // MOE_MK_DEBUG_* bits
-    int nR, nTG, nEB, T, nC, NB1, NB2, tpw, S;
+    int nR, nTG, nEB, T, nC, tpw;
+    int NB1, NB2, NB2w, S, wide_ok;  // see Tiles
+    int wide_min;    // an expert takes wide row tiles when it has at least this many rows (> kTileTokens)
     int reb;         // experts per router task (4 or 16)
     int CT;          // tokens per combine task
     int pf_nt, pf_lines;  // weight prefetch during routing: first gate/up tiles covered, 128-byte lines
-    int BM;          // GroupGEMM tile rows (kBM or kWideBM); columns are f / NB1 = d / NB2
     int q_cap, mt_cap;
     long long watchdog;  // real-time ticks (100 MHz)
     MK_G int *ctl, *ev_logit, *ev_exp, *ev_h;

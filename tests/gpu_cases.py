@@ -51,11 +51,44 @@ def ctl_words(layer, B):
     return layer.routing(B)["ctl"].cpu().numpy()
 
 
-def expected_task_counts(plan, hist, B):
-    """Tasks of each kind one forward runs, from the library's own per-batch choices
-    (moe_mk_forward_info) and the routing histogram."""
-    info = lambda key: mk.moe_mk_forward_info(plan, B, key)
-    BM, NB1, NB2, S = info("BM"), info("NB1"), info("NB2"), info("S")
-    mt = int(sum((int(h) + BM - 1) // BM for h in hist))
+def row_tiles(layer, B):
+    """The forward's row tiles as the scan task published them: (expert, row0, rows) per row
+    tile in expert order, and how many are wide (more than 64 rows)."""
+    r = layer.routing(B)
+    ctl = r["ctl"].cpu().numpy()
+    mt, mw = int(ctl[mk.CTL["mt_total"]]), int(ctl[mk.CTL["mw"]])
+    tiles = np.stack([r[key][:mt].cpu().numpy() for key in ("mt_expert", "mt_row0", "mt_rows")], axis=1)
+    return tiles, mw
+
+
+def check_row_tiles(tiles, mw, hist, indptr, wide_min, BM=64, wide_BM=256):
+    """The row tiles partition every expert's grouped rows, in expert order and in row order
+    within an expert: a wide tile holds more than BM and at most wide_BM rows and goes to an
+    expert with at least wide_min rows, a narrow one at most BM; mw counts the wide ones."""
+    assert np.all(tiles[:, 2] >= 1) and np.all(tiles[:, 2] <= wide_BM)
+    assert np.count_nonzero(tiles[:, 2] > BM) == mw
+    assert np.all(np.diff(tiles[:, 0]) >= 0) and np.all(np.diff(tiles[:, 1]) > 0)
+    for e in range(len(hist)):
+        mine = tiles[tiles[:, 0] == e]
+        assert int(mine[:, 2].sum()) == int(hist[e])
+        if len(mine):
+            starts = mine[:, 1]
+            ends = starts + mine[:, 2]
+            assert starts[0] == indptr[e] and np.all(starts[1:] == ends[:-1]) and ends[-1] == indptr[e + 1]
+        wide = np.count_nonzero(mine[:, 2] > BM)
+        if hist[e] >= wide_min:
+            assert wide == hist[e] // wide_BM + (1 if hist[e] % wide_BM > BM else 0), (e, hist[e], wide)
+        else:
+            assert wide == 0, (e, hist[e])
+
+
+def expected_task_counts(layer, B):
+    """Tasks of each kind one forward runs, from the library's per-batch choices
+    (moe_mk_forward_info) and the row tiles the scan task chose."""
+    info = lambda key: mk.moe_mk_forward_info(layer.plan, B, key)
+    tiles, mw = row_tiles(layer, B)
+    mt = len(tiles)
+    S = info("S")
     return {"route": info("route_tasks"), "topk": info("T"), "scan": 1, "group": info("T"),
-            "gemm1": mt * NB1, "gemm2": mt * S * NB2, "combine": info("combine_tasks")}
+            "gemm1": mt * info("NB1"), "gemm2": S * mt * (info("NB2_wide") if mw else info("NB2")),
+            "combine": info("combine_tasks")}

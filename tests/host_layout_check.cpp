@@ -80,9 +80,12 @@ int main() {
                 const Tiles t = tile_config(s, B);
                 const int64_t A = B * s.k;
                 CHECK(c.nR <= cc.nR_max, "nR %lld > nR_max %lld", (long long)c.nR, (long long)cc.nR_max);
-                for (const auto &h : histograms(B, s.E, s.k, t.BM)) {
+                // row tiles: an expert's wide tiling never has more tiles than its narrow
+                // one (nor more down-projection tiles: NB2w < NB2), so the narrow counts bound
+                // every mix of shapes the kernel can choose
+                for (const auto &h : histograms(B, s.E, s.k, kBM)) {
                     ++cases;
-                    const int64_t mt = row_tiles(h, t.BM);
+                    const int64_t mt = row_tiles(h, kBM);
                     CHECK(mt <= cc.mt_cap, "E=%d k=%d B=%lld cap=%lld: row tiles %lld > mt_cap %lld", s.E, s.k,
                           (long long)B, (long long)cap, (long long)mt, (long long)cc.mt_cap);
                     // task indices of the static layout: routing, padded GroupGEMM blocks, combine

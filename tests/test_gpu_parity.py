@@ -14,7 +14,8 @@ import torch
 
 import moe_groupgemm_amd as mk
 import oracle
-from gpu_cases import check_out, check_routing, ctl_words, dev_inputs, expected_task_counts, log, routing_numpy
+from gpu_cases import (check_out, check_routing, check_row_tiles, ctl_words, dev_inputs, expected_task_counts, log,
+                       routing_numpy, row_tiles)
 from moe_inputs import CONFIGS, Config, device_weights, make_bias, make_wr, make_x, small_case, to_torch_bf16
 
 pytestmark = pytest.mark.gpu
@@ -53,14 +54,28 @@ def run_small(x, Wr, bias, W1, W3, W2, k, sched, max_batch=None):
     return layer, res, got
 
 
-def full_check(x, Wr, bias, W1, W3, W2, k, sched, what):
+def full_check(x, Wr, bias, W1, W3, W2, k, sched, what, debug=0):
+    """Routing and output of one forward against the oracle, and the row tiles against the
+    histogram; returns the output and the number of wide row tiles."""
     B = x.shape[0]
+    E, d, f = W1.shape
     ref = oracle.forward(x, Wr, bias, W1, W3, W2, k)
-    layer, out, got = run_small(x, Wr, bias, W1, W3, W2, k, sched)
-    check_routing(got, ref, B, W1.shape[0])
+    tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
+    layer = mk.MoELayer(E, k, d, f, tWr, t1, t3, t2, router_bias=tb, sched=sched, max_batch=B)
+    mk.moe_mk_plan_set_debug(layer.plan, 0, debug)
+    out = layer(tx).float().cpu().numpy()
+    torch.cuda.synchronize()
+    assert layer.error() == 0
+    check_routing(routing_numpy(layer, B), ref, B, E)
     check_out(out, ref["out"], what)
+    tiles, mw = row_tiles(layer, B)
+    wide_min = mk.moe_mk_plan_info(layer.plan, "wide_min_rows")
+    if debug & mk.MOE_MK_DEBUG_NARROW_ONLY or not mk.moe_mk_forward_info(layer.plan, B, "wide_ok") or \
+            (debug & mk.MOE_MK_DEBUG_BATCH_RULE and B * k < 128 * E):
+        wide_min = 1 << 30
+    check_row_tiles(tiles, mw, ref["hist"], ref["exp_indptr"], wide_min)
     layer.close()
-    return out
+    return out, mw
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
@@ -91,7 +106,7 @@ def test_ragged_multi_tile(sched):
 def test_zero_input_all_ties(sched):
     cfg, x, Wr, bias, W1, W3, W2 = small_case(37, 128, 128, 8, 2, seed=5)
     x[:] = 0
-    out = full_check(x, Wr, bias, W1, W3, W2, 2, sched, "zero input")
+    out, _ = full_check(x, Wr, bias, W1, W3, W2, 2, sched, "zero input")
     assert np.all(out == 0)
 
 
@@ -148,10 +163,10 @@ def test_wide_tiles(B, d, f, E, k, sched):
     # an expert averages >= 128 rows: 256-row tiles, ragged last tiles (some with rows for
     # one of the two 128-row halves only; experts of more than 256 rows with a second
     # tile), several K steps of 32
-    assert _info(E, k, d, f, B, "wide") == 1
     log(f"wide tiles B={B} d={d} f={f} E={E} k={k} sched={SNAME[sched]}")
     cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=1300 + B)
-    full_check(x, Wr, bias, W1, W3, W2, k, sched, f"wide B={B}")
+    _, mw = full_check(x, Wr, bias, W1, W3, W2, k, sched, f"wide B={B}")
+    assert mw > 0
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
@@ -159,21 +174,21 @@ def test_wide_tiles_constant_input(sched):
     # every token identical: k experts take all 324 rows each (tiles of 256 and 68 rows)
     cfg, x, Wr, bias, W1, W3, W2 = small_case(324, 256, 256, 4, 2, seed=61)
     x[:] = x[0]
-    assert _info(4, 2, 256, 256, 324, "wide") == 1
-    full_check(x, Wr, bias, W1, W3, W2, 2, sched, "wide constant input")
+    _, mw = full_check(x, Wr, bias, W1, W3, W2, 2, sched, "wide constant input")
+    assert mw == 4  # two experts of 324 rows: a wide tile of 256 and one of 68 rows each
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
 def test_wide_forward_thin_row_tiles(sched):
     # Routing set by the input: logit e of token b is x[b, e] (Wr is the identity on the
-    # first E values of j), so each expert receives an exact row count.  In this wide-tile
-    # forward the row tiles of at most 64 rows (1, 16, 17, 64 rows past 256; experts of 11
-    # and 68 rows) run as narrow tiles, the others (65 past 256, 68 alone) as wide tiles.
+    # first E values of j), so each expert receives an exact row count.  Experts of more than
+    # 64 rows take wide row tiles (68 rows: one wide tile); their remainders of at most 64 rows
+    # past a multiple of 256 (1, 16, 17, 64 rows) are narrow row tiles, as is the expert of 11
+    # rows; the remainder of 65 rows is a wide row tile.
     counts = [257, 272, 273, 320, 11, 68, 321]
     E, k, d, f = len(counts), 2, 512, 256
     slots = np.repeat(np.arange(E), counts)
     B = len(slots) // k
-    assert _info(E, k, d, f, B, "wide") == 1
     cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=1700)
     x[:, :E] = 0
     x[np.arange(B), slots[:B]] = 0x4040       # bf16 3.0: slot 0
@@ -187,6 +202,9 @@ def test_wide_forward_thin_row_tiles(sched):
     layer, out, got = run_small(x, Wr, bias, W1, W3, W2, k, sched)
     check_routing(got, ref, B, E)
     check_out(out, ref["out"], "wide forward, thin row tiles")
+    tiles, mw = row_tiles(layer, B)
+    check_row_tiles(tiles, mw, ref["hist"], ref["exp_indptr"], 65)
+    assert mw == 7 and len(tiles) - mw == 5
     layer.close()
 
 
@@ -263,7 +281,7 @@ def test_rest_state_and_task_counts(B, E, d, f, sched):
     assert c[C["cq"]] == 0                             # static combine claim counter at rest
     assert c[C["ev_topk"]] == 0 and c[C["ev_scan"]] == 1 and c[C["ev_y"]] == 0  # events at rest
     hist = routing_numpy(layer, B)["hist"]
-    exp = expected_task_counts(layer.plan, hist, B)
+    exp = expected_task_counts(layer, B)
     delta = c[C["dbg"]:C["dbg"] + 7] - before[C["dbg"]:C["dbg"] + 7]
     names = ["route", "topk", "scan", "group", "gemm1", "gemm2", "combine"]
     for i, n in enumerate(names):
@@ -404,7 +422,8 @@ def _case(cfg):
 
 
 def _tokens_of_every_row_tile(r, k, BM):
-    """One token from the first row, every BM-th row and the last row of each expert's segment."""
+    """One token from the first row, every BM-th row and the last row of each expert's segment
+    (with BM = 64 this hits every row tile of either shape)."""
     toks = set()
     ip = r["exp_indptr"]
     for e in range(len(ip) - 1):
@@ -430,7 +449,7 @@ def _full_config_of(cfg, sched, tokens="all"):
         if tokens == "all":
             toks = list(range(B))
         else:
-            toks = _tokens_of_every_row_tile(ref, cfg.k, mk.moe_mk_forward_info(layer.plan, B, "BM"))
+            toks = _tokens_of_every_row_tile(ref, cfg.k, 64)
             assert len(toks) >= tokens, len(toks)
         ref_out = c.ref_out(B, toks)
         got = out.float().cpu().numpy()
@@ -457,8 +476,7 @@ def test_threshold_batches_one_plan(sched):
     tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
     layer = mk.MoELayer(E, k, d, f, tWr, t1, t3, t2, router_bias=tb, sched=sched, max_batch=Bmax)
     for B in (64, 65, 511, 512, 513, 1023, 1024, 1025, 1):
-        log(f"threshold batch B={B} tiles={'wide' if mk.moe_mk_forward_info(layer.plan, B, 'wide') else 'narrow'} "
-            f"sched={SNAME[sched]}")
+        log(f"threshold batch B={B} sched={SNAME[sched]}")
         out = layer(tx[:B])
         torch.cuda.synchronize()
         assert layer.error() == 0
@@ -518,7 +536,6 @@ def test_wide_long_k_every_token(sched):
     # f = 768 for the down projection), about 256 rows per expert so experts take one full
     # tile and some a second, thin one; every token compared
     cfg = Config("wide_long_k", d=2048, f=768, E=8, k=2, batches=(1024,), seed=808)
-    assert _info(8, 2, 2048, 768, 1024, "wide") == 1
     _full_config_of(cfg, sched)
 
 
@@ -527,3 +544,23 @@ def test_max_experts_and_top_k_wide():
     cfg, x, Wr, bias, W1, W3, W2 = small_case(2048, 256, 128, 256, 16, seed=707)
     for sched in SCHEDS:
         full_check(x, Wr, bias, W1, W3, W2, 16, sched, f"E=256 k=16 B=2048 {SNAME[sched]}")
+
+
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+@pytest.mark.parametrize("B", [600, 200], ids=["batch_600", "batch_200"])
+@pytest.mark.parametrize("policy", [0, mk.MOE_MK_DEBUG_NARROW_ONLY, mk.MOE_MK_DEBUG_BATCH_RULE],
+                         ids=["by_rows", "narrow_only", "batch_rule"])
+def test_tile_shape_per_expert(policy, sched, B):
+    # Skewed routing (Zipf bias): a few experts receive hundreds of rows, most a few dozen.
+    # The scan chooses each expert's row-tile shape from its own row count (default: wide
+    # above 64 rows), or the debug policy forces all narrow or decides from the batch size
+    # alone (B = 600 averages 150 rows per expert: wide; B = 200 averages 50: narrow); every
+    # choice gives the oracle's result.
+    d, f, E, k = 256, 256, 16, 4
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=1800, zipf_s=1.2)
+    ref = oracle.routing(x, Wr, bias, k)
+    assert ref["hist"].max() > 64 and np.count_nonzero(ref["hist"] <= 64) >= 4
+    log(f"tile shape per expert B={B} policy={policy} sched={SNAME[sched]} hist={ref['hist'].tolist()}")
+    _, mw = full_check(x, Wr, bias, W1, W3, W2, k, sched, f"per-expert tiles policy={policy}", debug=policy)
+    narrow = policy == mk.MOE_MK_DEBUG_NARROW_ONLY or (policy == mk.MOE_MK_DEBUG_BATCH_RULE and B * k < 128 * E)
+    assert (mw == 0) == narrow
