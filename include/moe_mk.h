@@ -7,13 +7,13 @@
  *   histogram and exp_indptr prefix sum -> token grouping (permutation + row gather)
  *   -> expert GroupGEMM 1 (gate/up, SwiGLU) -> expert GroupGEMM 2 (down)
  *   -> weighted combine.
- * The steps follow "Event Tensor: A Unified Abstraction for Compiling Dynamic
- * Megakernel" (MLSys 2026): section "Problem" (MoE routing, token grouping and
- * GroupGEMM depend on the runtime top-k; dynamic batch sizes must not force a
- * recompile) and section "Core method" (grouping tiles update the event of the expert
- * chosen at run time; the exp_indptr prefix sum decides how many GroupGEMM tiles each
- * expert triggers; events are integer counters where notify is an atomic decrement
- * and wait is a spin until zero; static per-CU queues or a dynamic atomic queue).
+ *
+ * Pages cited below ("Source:" on every declaration):
+ *   [ET]   "Event Tensor: A Unified Abstraction for Compiling Dynamic Megakernel (MLSys
+ *          2026)", sections Problem, Core method, Key results.
+ *   [L112] "Lecture 112: Production Megakernels for Real-World Inference", Key takeaways
+ *          and Technical details.
+ *   [RaMP] "RaMP: Runtime-Aware Megakernel Polymorphism for Mixture-of-Experts", abstract.
  *
  * Conventions for every entry point:
  *   - Device pointers point to device memory of the plan's device; host pointers are
@@ -28,6 +28,8 @@
  *     Counts that follow from B (routing tiles, router and combine task shapes, f splits of
  *     the down projection) are kernel arguments; the GroupGEMM tile shape of each expert
  *     (64-row or 256-row tiles) is chosen on the device from that expert's row count.
+ *   - Host-side calls on one plan may come from several threads at once, except
+ *     moe_mk_plan_set_debug and moe_mk_plan_destroy.
  */
 #ifndef MOE_MK_H
 #define MOE_MK_H
@@ -39,51 +41,87 @@
 extern "C" {
 #endif
 
-typedef struct moe_mk_plan_s *moe_mk_plan_t;  /* opaque, host-side, immutable after creation */
+/*
+ * Opaque host-side plan: the layer shape (E, k, d, f), the schedule and the device.  It is
+ * never written after creation.
+ * Source: [ET] Core method (shape dynamism: one runtime instantiated for the actual values
+ * of symbolic dimensions such as the batch, without recompiling).
+ */
+typedef struct moe_mk_plan_s *moe_mk_plan_t;
 
-/* Task scheduling ("Event Tensor", Core method, static and dynamic scheduling). */
+/*
+ * Task scheduling.
+ * Source: [ET] Core method (static scheduling: tasks assigned to per-SM queues ahead of
+ * time, synchronised by counter semaphores and spin-waits; dynamic scheduling: the event
+ * that fires pushes its consumer tasks onto a shared queue with an atomic, idle SMs pop).
+ */
 typedef enum {
     MOE_MK_SCHED_STATIC = 0,  /* persistent workgroups take tasks from fixed per-XCD lists (then, with narrow tiles, what
-                                 the other XCDs' lists have left) and spin-wait on events */
-    MOE_MK_SCHED_DYNAMIC = 1  /* the task that fires an event pushes its consumers onto a shared queue; idle workgroups pop */
+                                 the other XCDs' lists have left) and spin-wait on events; relies on the whole grid
+                                 (one workgroup per CU) being resident at once, as on a GPU not shared with other
+                                 kernels: a workgroup held back by another stream's kernel delays the forward until
+                                 it is scheduled, and a wait longer than the watchdog (2 s) ends the forward with
+                                 MOE_MK_ERR_WATCHDOG instead of hanging */
+    MOE_MK_SCHED_DYNAMIC = 1, /* the task that fires an event pushes its consumers onto a shared queue; idle workgroups
+                                 pop.  Every task handed out is ready, so any number of resident workgroups progresses */
+    MOE_MK_SCHED_STATIC_COOPERATIVE = 2 /* the static schedule launched as a cooperative kernel: the runtime guarantees
+                                 the grid is co-resident, or refuses the launch (MOE_MK_EHIP).  Measured on MI355X it
+                                 adds about 15-45 us per forward; for GPUs shared with other kernels */
 } moe_mk_sched_t;
 
+/*
+ * Status of every call.
+ * Source: none on the pages (this library's error reporting).
+ */
 typedef enum {
     MOE_MK_OK = 0,
     MOE_MK_EINVAL = -1,        /* bad argument: null pointer, misalignment, negative size, ... */
     MOE_MK_EUNSUPPORTED = -2,  /* shape or device outside the supported range */
     MOE_MK_EWORKSPACE = -3,    /* workspace too small, or not initialised */
-    MOE_MK_EHIP = -4,          /* a HIP runtime call failed */
+    MOE_MK_EHIP = -4,          /* a HIP runtime call failed (including a refused cooperative launch) */
     MOE_MK_EDEVICE = -5        /* the kernel reported an error in the workspace (watchdog, bad routing) */
 } moe_mk_status_t;
 
 /*
  * Create a plan for a layer with E experts, top-k routing, model width d and expert
- * hidden width f, on the current HIP device.
+ * hidden width f, on the current HIP device, with schedule sched.
  *   Supported: gfx950; d and f multiples of 128; 1 <= E <= 256; 1 <= k <= min(E, 16).
  *   The plan fixes no batch size and no tile configuration (see moe_mk_forward_info).
- *   *plan receives a new plan (release with moe_mk_plan_destroy).
- * Errors: EINVAL (plan == NULL, bad sched), EUNSUPPORTED (shape, device), EHIP.
+ *   *plan (host) receives a new plan, owned by the caller (release with
+ *   moe_mk_plan_destroy); on an error it receives NULL.
+ * Errors: EINVAL (plan == NULL, bad sched), EUNSUPPORTED (shape, device, or no cooperative
+ * launch for MOE_MK_SCHED_STATIC_COOPERATIVE), EHIP.
+ * Source: [ET] Core method (symbolic shapes: the batch is a symbolic dimension, bound at
+ * run time); [L112] Key takeaways, "Symbolic Representation of Work".
  */
 moe_mk_status_t moe_mk_plan(moe_mk_plan_t *plan, int E, int k, int d, int f, moe_mk_sched_t sched);
 
-/* Release a plan (NULL is ignored). */
+/*
+ * Release a plan (NULL is ignored).  No forward of it may be pending on the host side.
+ * Source: none on the pages (plan bookkeeping).
+ */
 void moe_mk_plan_destroy(moe_mk_plan_t plan);
 
 /*
- * Bytes of device workspace that a forward with batch size B needs (monotone in B).
+ * Bytes of device workspace that a forward with batch size B needs (grows with B).
  * Returns 0 for an invalid plan or B < 0 or B*k >= 2^31.
  * A workspace of N bytes serves every B whose requirement is <= N; its internal layout
- * depends only on N, so one workspace can serve a sequence of different batch sizes.
+ * depends only on N, so one workspace can serve a sequence of different batch sizes.  It
+ * holds the event counters (sized from the symbolic batch), the task queue and the
+ * intermediates.
+ * Source: [ET] Core method (event tensors with symbolic dimensions, lowered to plain
+ * integer tensors).
  */
 size_t moe_mk_workspace_bytes(moe_mk_plan_t plan, int64_t B);
 
 /*
  * Prepare a workspace (device pointer ws, ws_bytes bytes): clears it and sets the
- * control block to its rest state, enqueued on stream (hipStream_t, may be NULL).
- * Needed once per allocation, and again after a forward reported MOE_MK_EDEVICE.
- * Afterwards every forward leaves the control block in its rest state by itself.
+ * control block and every event counter to its rest state, enqueued on stream
+ * (hipStream_t, may be NULL) as fill kernels (no memset).  Needed once per allocation, and
+ * again after a forward reported MOE_MK_EDEVICE.  Afterwards every forward leaves the
+ * control block in its rest state by itself.
  * Errors: EINVAL, EWORKSPACE (ws_bytes smaller than the B = 1 requirement), EHIP.
+ * Source: [ET] Core method (an event is an integer counter with a wait count).
  */
 moe_mk_status_t moe_mk_workspace_init(moe_mk_plan_t plan, void *ws, size_t ws_bytes, void *stream);
 
@@ -98,13 +136,19 @@ moe_mk_status_t moe_mk_workspace_init(moe_mk_plan_t plan, void *ws, size_t ws_by
  *   W2           bf16 [E, f, d]        down projection of every expert
  *   out          bf16 [B, d]           layer output (written, never read)
  *   ws, ws_bytes device workspace prepared by moe_mk_workspace_init; it must not be used
- *                by two forwards at the same time.
+ *                by two forwards at the same time.  Every buffer stays owned by the caller.
  * Routing is exact: logits use 64 interleaved fp32 fma chains over d (chain j mod 64,
  * ascending j) folded in halves, plus the bias; top-k orders by logit, ties to the
  * lower expert index; within an expert the grouped rows keep ascending token order.
  * Errors: EINVAL (null or misaligned pointer, B < 0, B*k >= 2^31), EWORKSPACE, EHIP.
  * Faults detected on the device (a wait that exceeds the watchdog, a non-finite
  * logit) are recorded in the workspace; see moe_mk_workspace_error.
+ * Source: [ET] Problem (MoE routing, token grouping and the GroupGEMM depend on the
+ * runtime top-k; batch sizes change between calls) and Core method (data-dependent event
+ * update: a grouping tile updates the event of the expert each token chose; data-dependent
+ * task triggering: the exp_indptr prefix sum sets how many GroupGEMM tiles each expert
+ * triggers; notify is an atomic decrement, wait a spin on zero); [L112] Technical
+ * details, "Execution Model" (one persistent kernel whose cores take tasks from a queue).
  */
 moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias,
                                const void *W1, const void *W3, const void *W2, void *out, int64_t B,
@@ -128,6 +172,7 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
  * Every call on one GPU shares that GPU's scratch: calls that overlap in time on one GPU
  * (other streams, other threads) race and give undefined results.
  * Errors: EINVAL, EWORKSPACE, EUNSUPPORTED (device index >= 64), EHIP.
+ * Source: none on the pages; for callers that cannot allocate (above).
  */
 #define MOE_MK_SCRATCH_BYTES ((size_t)64 << 20)
 moe_mk_status_t moe_mk_forward_noalloc(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias,
@@ -135,8 +180,8 @@ moe_mk_status_t moe_mk_forward_noalloc(moe_mk_plan_t plan, const void *x, const 
                                        int32_t *err, void *stream);
 
 /*
- * Device pointers into the workspace of the most recent forward with batch size B.
- * Valid until the next forward on that workspace.
+ * Device pointers into the workspace of the most recent forward with batch size B (no
+ * copies; they stay owned by the workspace and are valid until its next forward).
  *   topk_idx  int32 [B, k]   expert of each (token, slot), slot 0 = largest logit
  *   topk_w    fp32  [B, k]   softmax weight of each slot
  *   hist      int32 [E]      rows routed to each expert
@@ -150,6 +195,9 @@ moe_mk_status_t moe_mk_forward_noalloc(moe_mk_plan_t plan, const void *x, const 
  *                            forwards)
  *   mt_*      int32 [mt_cap] the forward's row tiles (see the struct)
  * Errors: EINVAL, EWORKSPACE.
+ * Source: [ET] Core method (data-dependent event update by the grouping tiles; the
+ * exp_indptr prefix sum triggers each expert's GroupGEMM tiles); [RaMP] abstract (the
+ * runtime expert histogram sets each expert's tile configuration).
  */
 typedef struct {
     const int32_t *topk_idx;
@@ -166,6 +214,11 @@ typedef struct {
     int64_t mt_cap;            /* length of the three row-tile arrays (host value)            */
 } moe_mk_routing_view_t;
 
+/*
+ * Fill *view (host) with the pointers above for the last forward of B tokens on the
+ * workspace ws (ws_bytes bytes).  Errors: EINVAL, EWORKSPACE.
+ * Source: [ET] Core method (data-dependent event update and task triggering).
+ */
 moe_mk_status_t moe_mk_routing_view(moe_mk_plan_t plan, int64_t B, const void *ws, size_t ws_bytes,
                                     moe_mk_routing_view_t *view /* host */);
 
@@ -173,6 +226,8 @@ moe_mk_status_t moe_mk_routing_view(moe_mk_plan_t plan, int64_t B, const void *w
  * Read the workspace's error word (synchronises stream).  *err (host) receives 0 when no
  * device fault was recorded, otherwise a bit set of MOE_MK_ERR_*.
  * Returns OK, EINVAL or EHIP.
+ * Source: [ET] Core method (wait is a spin on zero; here every spin is bounded by a
+ * watchdog, whose expiry is recorded instead of hanging).
  */
 #define MOE_MK_ERR_WATCHDOG 1   /* a wait or queue pop exceeded the watchdog */
 #define MOE_MK_ERR_NONFINITE 2  /* a router logit was NaN or infinite */
@@ -181,12 +236,15 @@ moe_mk_status_t moe_mk_routing_view(moe_mk_plan_t plan, int64_t B, const void *w
 moe_mk_status_t moe_mk_workspace_error(moe_mk_plan_t plan, const void *ws, size_t ws_bytes, void *stream,
                                        int32_t *err /* host */);
 
-/* Plan facts (host).  Keys: "E" "k" "d" "f" "sched" "grid" "cus" "wg_per_cu" "BM" "BN1" "BN2" "BK"
- * "wide_BM" "wide_BN1" "wide_BN2" "wide_BK" "wide_min_rows" "route_experts" "threads".
- * GroupGEMM tiles are BM x BN1 (gate/up) and BM x BN2 (down) with K steps of BK, except in
- * forwards where B*k >= wide_min_rows*E (an expert averages that many rows): there tiles
- * have wide_BM rows, wide_BN1 gate/up columns, wide_BN2 down columns and K steps of wide_BK.  Returns -1 for an
- * unknown key or invalid plan. */
+/*
+ * Plan facts (host).  Keys: "E" "k" "d" "f" "sched" "grid" "cus" "wg_per_cu" "BM" "BN1"
+ * "BN2" "BK" "wide_BM" "wide_BN1" "wide_BN2" "wide_BK" "wide_min_rows" "route_experts"
+ * "threads".  Narrow GroupGEMM tiles are BM rows x BN1 gate/up (BN2 down) columns with K
+ * steps of BK; wide ones wide_BM rows x wide_BN1 gate/up (wide_BN2 down) columns with K
+ * steps of wide_BK, taken by experts with at least wide_min_rows rows.  Returns -1 for an
+ * unknown key or invalid plan.
+ * Source: none on the pages (plan bookkeeping).
+ */
 int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
 
 /*
@@ -196,22 +254,26 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
  *   "route_tasks"             router tasks; "route_tokens_per_wave", "route_experts_per_task"
  *   "combine_tasks"           combine tasks; "combine_tokens" tokens per combine task
  *   "NB1"                     gate/up tiles per row tile (either shape)
- *   "NB2" "NB2_wide"          down-projection tiles per narrow row tile and f range, and
- *                             per wide row tile
+ *   "NB2" "NB2_wide"          down-projection tiles per row tile and f range in a forward
+ *                             without wide row tiles, and per row tile in one with them
  *   "S"                       f ranges of the down projection (1: not split)
  *   "wide_ok"                 1 when experts may take wide row tiles in this forward (the
  *                             kernel then gives them to experts with at least
  *                             plan_info("wide_min_rows") rows; see moe_mk_routing_view)
  * Returns -1 for an unknown key, an invalid plan, B < 1 or B*k >= 2^31.
+ * Source: [RaMP] abstract (what follows from the batch size alone, as opposed to the
+ * routing distribution, which only the device sees).
  */
 int64_t moe_mk_forward_info(moe_mk_plan_t plan, int64_t B, const char *key);
 
 /*
  * Debug controls for tests (host): watchdog limit in GPU real-time ticks (100 MHz;
  * 0 restores the default of 2 s) and a flag word (MOE_MK_DEBUG_*).  They apply to later
- * forwards of this plan.  MOE_MK_DEBUG_DROP_NOTIFY makes the first grouping task skip
- * one of its event notifications, so the waiting GroupGEMM tasks must leave through the
- * watchdog and record MOE_MK_ERR_WATCHDOG instead of hanging.
+ * forwards of this plan; no forward may be issued on the plan from another thread meanwhile.
+ * MOE_MK_DEBUG_DROP_NOTIFY makes the first grouping task skip one of its event
+ * notifications, so the waiting GroupGEMM tasks must leave through the watchdog and record
+ * MOE_MK_ERR_WATCHDOG instead of hanging.
+ * Source: none on the pages (test and measurement controls).
  */
 #define MOE_MK_DEBUG_DROP_NOTIFY 1
 #define MOE_MK_DEBUG_TRACE 2  /* record per-task timestamps, see moe_mk_trace_view */
@@ -223,7 +285,8 @@ moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks
 
 /*
  * Debug view of the task trace of the last forward run with MOE_MK_DEBUG_TRACE: *trace
- * (host) receives a device pointer to *n (host) records of eight int64 each:
+ * (host) receives a device pointer (into the workspace) to *n (host) records of eight
+ * int64 each:
  *   [0] task index g | kind << 32 | workgroup << 40   (kind: 0 router, 1 top-k, 2 scan,
  *       3 grouping, 4 gate/up GEMM, 5 down GEMM, 6 combine)
  *   [1] time the workgroup obtained the task, [2] time its dependencies were satisfied,
@@ -232,11 +295,16 @@ moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks
  *   ran it; [6], [7] ends of the scan and of the grouping when the top-k task of a
  *   one-tile batch runs both itself (else 0).
  * Records of tasks that did not run in that forward are stale.  Errors: EINVAL, EWORKSPACE.
+ * Source: [L112] Key takeaways, "Dependency Tracking (Barriers)" (consumers start before
+ * all producers have finished: the trace shows when each task's dependencies were met).
  */
 moe_mk_status_t moe_mk_trace_view(moe_mk_plan_t plan, int64_t B, const void *ws, size_t ws_bytes,
                                   const int64_t **trace /* host */, int64_t *n /* host */);
 
-/* Short static description of a status code. */
+/*
+ * Short static description of a status code (never NULL; owned by the library).
+ * Source: none on the pages (error reporting).
+ */
 const char *moe_mk_status_str(moe_mk_status_t s);
 
 #ifdef __cplusplus

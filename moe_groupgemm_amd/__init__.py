@@ -17,6 +17,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moe_mk.h")
 
 MOE_MK_SCHED_STATIC = 0
 MOE_MK_SCHED_DYNAMIC = 1
+MOE_MK_SCHED_STATIC_COOPERATIVE = 2
 MOE_MK_OK = 0
 MOE_MK_ERR_WATCHDOG = 1
 MOE_MK_ERR_NONFINITE = 2

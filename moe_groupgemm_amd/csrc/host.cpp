@@ -14,7 +14,7 @@
 #include "mk_capacity.h"
 #include "mk_common.h"
 
-hipError_t mk_launch(const mk::Params &p, int grid, hipStream_t stream);
+hipError_t mk_launch(const mk::Params &p, int grid, hipStream_t stream, bool cooperative);
 hipError_t mk_ws_init(void *ws, size_t bytes, hipStream_t stream);
 hipError_t mk_occupancy(int *blocks_per_cu);
 hipError_t mk_scratch(void **ptr, size_t *bytes);
@@ -64,7 +64,15 @@ const char *moe_mk_status_str(moe_mk_status_t s) {
 moe_mk_status_t moe_mk_plan(moe_mk_plan_t *plan, int E, int k, int d, int f, moe_mk_sched_t sched) {
     if (!plan) return MOE_MK_EINVAL;
     *plan = nullptr;
-    if (sched != MOE_MK_SCHED_STATIC && sched != MOE_MK_SCHED_DYNAMIC) return MOE_MK_EINVAL;
+    if (sched != MOE_MK_SCHED_STATIC && sched != MOE_MK_SCHED_DYNAMIC && sched != MOE_MK_SCHED_STATIC_COOPERATIVE)
+        return MOE_MK_EINVAL;
+    if (sched == MOE_MK_SCHED_STATIC_COOPERATIVE) {
+        int coop = 0;
+        int d = 0;
+        if (hipGetDevice(&d) != hipSuccess) return MOE_MK_EHIP;
+        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, d) != hipSuccess) return MOE_MK_EHIP;
+        if (!coop) return MOE_MK_EUNSUPPORTED;
+    }
     if (E < 1 || E > mk::kMaxE || k < 1 || k > mk::kMaxK || k > E) return MOE_MK_EUNSUPPORTED;
     if (d < 128 || f < 128 || d % 128 != 0 || f % 128 != 0) return MOE_MK_EUNSUPPORTED;
     if ((int64_t)d * f * E >= ((int64_t)1 << 40)) return MOE_MK_EUNSUPPORTED;
@@ -151,7 +159,7 @@ mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const
     P.k = s.k;
     P.d = s.d;
     P.f = s.f;
-    P.sched = plan->sched;
+    P.sched = plan->sched == MOE_MK_SCHED_DYNAMIC ? 1 : 0;  // the kernel knows static (0) or dynamic (1)
     P.debug = plan->debug;
     P.nR = (int)c.nR;
     P.nTG = (int)c.nTG;
@@ -232,7 +240,8 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     if (cap < B) return MOE_MK_EWORKSPACE;
     const mk::Params P = make_params(plan, x, Wr, router_bias, W1, W3, W2, out, B, (char *)ws, cap);
     if (hipSetDevice(plan->device) != hipSuccess) return MOE_MK_EHIP;
-    if (mk_launch(P, plan->grid, (hipStream_t)stream) != hipSuccess) return MOE_MK_EHIP;
+    if (mk_launch(P, plan->grid, (hipStream_t)stream, plan->sched == MOE_MK_SCHED_STATIC_COOPERATIVE) != hipSuccess)
+        return MOE_MK_EHIP;
     return MOE_MK_OK;
 }
 
@@ -263,7 +272,8 @@ moe_mk_status_t moe_mk_forward_noalloc(moe_mk_plan_t plan, const void *x, const 
     mk::Params P = make_params(plan, x, Wr, router_bias, W1, W3, W2, out, B, (char *)base, cap);
     P.err_out = err;
     P.heal = 1;
-    if (mk_launch(P, plan->grid, (hipStream_t)stream) != hipSuccess) return MOE_MK_EHIP;
+    if (mk_launch(P, plan->grid, (hipStream_t)stream, plan->sched == MOE_MK_SCHED_STATIC_COOPERATIVE) != hipSuccess)
+        return MOE_MK_EHIP;
     return MOE_MK_OK;
 }
 

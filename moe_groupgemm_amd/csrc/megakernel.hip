@@ -2702,7 +2702,18 @@ __global__ void moe_ws_init_ctl(int *ctl_generic) {
 }  // namespace mk
 
 // ------------------------------------------------------------------------------ launch glue
-hipError_t mk_launch(const mk::Params &p, int grid, hipStream_t stream) {
+// The static schedule binds routing tasks to workgroups and has tasks spin-wait on events
+// that other workgroups' tasks notify, so it relies on its grid being resident all at once.
+// With cooperative set it is launched as a cooperative kernel, which the runtime refuses (an
+// error, not a hang) when the grid cannot be co-resident.  The dynamic schedule never waits
+// for a task bound to a workgroup (every task it hands out is ready) and is launched plainly.
+hipError_t mk_launch(const mk::Params &p, int grid, hipStream_t stream, bool cooperative) {
+    if (cooperative) {
+        mk::Params arg = p;
+        void *args[] = {&arg};
+        return hipLaunchCooperativeKernel((const void *)mk::moe_megakernel, dim3(grid), dim3(mk::kThreads), args, 0,
+                                          stream);
+    }
     hipLaunchKernelGGL(mk::moe_megakernel, dim3(grid), dim3(mk::kThreads), 0, stream, p);
     return hipGetLastError();
 }

@@ -125,3 +125,26 @@ def test_binding_rejects_mis_shaped_tensors():
                 mk.moe_mk_forward(fake_plan, **args)
     finally:
         mk._SHAPES.pop(fake_plan, None)
+
+
+def test_every_declaration_states_its_source():
+    # each function and type of the C ABI carries, in the comment block right above it, a
+    # "Source:" line citing the page and section that defines the operation (or saying that
+    # it is library bookkeeping with no counterpart on the pages)
+    import re
+    text = open(mk.HEADER).read()
+    body = text[text.index('extern "C" {'):]
+    decls = [m for m in re.finditer(r"^(?:typedef [^;{]*\{|typedef struct \w+ \*\w+;|[a-z_][\w ]*\*?\s*(moe_mk_\w+)\s*\()",
+                                     body, re.M)]
+    covered = {m.group(1) for m in decls if m.group(1)}
+    assert covered == set(mk.header_functions())  # every function declaration is checked
+    assert len(decls) - len(covered) == 4          # and the four types
+    for m in decls:
+        before = body[:m.start()]
+        block = before[before.rfind("\n/*") + 1:]  # the last comment block that starts a line
+        assert "*/" in block, m.group(0)
+        # the comment block may be followed by #define lines, but by no other declaration
+        between = block[block.index("*/") + 2:]
+        assert all(ln.startswith("#define") or ln.startswith(" ") or not ln.strip() for ln in between.splitlines()), \
+            (m.group(0), between)
+        assert "Source:" in block, f"no Source: line above {m.group(0)!r}"

@@ -564,3 +564,14 @@ def test_tile_shape_per_expert(policy, sched, B):
     _, mw = full_check(x, Wr, bias, W1, W3, W2, k, sched, f"per-expert tiles policy={policy}", debug=policy)
     narrow = policy == mk.MOE_MK_DEBUG_NARROW_ONLY or (policy == mk.MOE_MK_DEBUG_BATCH_RULE and B * k < 128 * E)
     assert (mw == 0) == narrow
+
+
+@pytest.mark.parametrize("B,d,f,E,k", [(16, 256, 512, 8, 2), (203, 256, 384, 16, 4), (300, 256, 384, 4, 2)],
+                         ids=["one_tile", "ragged_multi_tile", "wide"])
+def test_static_cooperative_launch(B, d, f, E, k):
+    # the static schedule launched as a cooperative kernel (co-residency guaranteed by the
+    # runtime) gives the plain static launch's output bit for bit
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=2100 + B)
+    out_c, _ = full_check(x, Wr, bias, W1, W3, W2, k, mk.MOE_MK_SCHED_STATIC_COOPERATIVE, f"cooperative B={B}")
+    out_s, _ = full_check(x, Wr, bias, W1, W3, W2, k, mk.MOE_MK_SCHED_STATIC, f"static B={B}")
+    assert np.array_equal(out_c.view(np.uint32), out_s.view(np.uint32))
