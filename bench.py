@@ -46,6 +46,8 @@ def parse():
                     "lines to be written back during the next launch)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the box's achievable copy bandwidth and bf16 GEMM rate")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the comparison with the same layer as one kernel per phase (plain and graph)")
     ap.add_argument("--workloads", default="all",
                     help="configurations timed beside the headline one: 'all', 'none', or a comma list of "
                     "config:sched[:policy] (e.g. prefill:static,sweep:dynamic,prefill:static:narrow_only)")
@@ -324,6 +326,83 @@ def measure_workload(cfg_name, sched_name, steps, warmup, dev, batches=None, col
     return res
 
 
+def unfused_comparison(cfg_name, steps, warmup, dev, batches=None):
+    """The megakernel (both schedules) beside the same layer as seven kernels, one per phase,
+    launched plainly and replayed from a HIP graph; and the warm-up each approach needs per
+    batch size (a graph must be captured and instantiated for every B; the megakernel needs
+    nothing).  Kernel-side times come from HIP events around each forward on its stream."""
+    import numpy as np
+    import torch
+
+    import moe_groupgemm_amd as mk
+    from moe_inputs import CONFIGS, device_weights, make_x, to_torch_bf16
+
+    cfg = CONFIGS[cfg_name]
+    batches = batches or cfg.batches
+    print(f"# unfused comparison {cfg_name} B={list(batches)}", file=sys.stderr, flush=True)
+    tWr, tb, t1, t3, t2 = device_weights(cfg, device=dev)
+    tx_all = to_torch_bf16(make_x(cfg, max(batches))).to(dev)
+    layers = {name: mk.MoELayer(cfg.E, cfg.k, cfg.d, cfg.f, tWr, t1, t3, t2, router_bias=tb, sched=sc,
+                                max_batch=max(batches), device=dev)
+              for name, sc in (("static", mk.MOE_MK_SCHED_STATIC), ("dynamic", mk.MOE_MK_SCHED_DYNAMIC))}
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+    res = []
+    for B in batches:
+        tx = tx_all[:B]
+        out = torch.empty((B, cfg.d), dtype=torch.bfloat16, device=dev)
+        lay = layers["dynamic"]
+        for _ in range(warmup):
+            layers["static"](tx, out)
+            lay(tx, out)
+            lay.forward_unfused(tx, out)
+        torch.cuda.synchronize()
+        e = {"config": cfg_name, "B": B,
+             "megakernel_static_us": timed(lambda: layers["static"](tx, out), steps),
+             "megakernel_dynamic_us": timed(lambda: lay(tx, out), steps),
+             "unfused_us": timed(lambda: lay.forward_unfused(tx, out), steps)}
+        # warm-up of the graph approach at this B: capture and instantiate, then the first replay
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            lay.forward_unfused(tx, out)
+        t1c = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        e["unfused_graph_capture_ms"] = (t1c - t0) * 1e3
+        e["unfused_graph_first_replay_ms"] = (time.perf_counter() - t1c) * 1e3
+        e["unfused_graph_us"] = timed(g.replay, steps)
+        del g
+        # the megakernel at a batch size it has not run yet needs no capture: its first call
+        # is an ordinary launch (wall time to completion, host included)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        layers["static"](tx, out)
+        torch.cuda.synchronize()
+        e["megakernel_call_ms"] = (time.perf_counter() - t0) * 1e3
+        if lay.error() or layers["static"].error():
+            raise RuntimeError(f"device error in the unfused comparison ({cfg_name} B={B})")
+        res.append(e)
+        print(f"#   B={B}: megakernel {e['megakernel_static_us']:.1f} / {e['megakernel_dynamic_us']:.1f} us, "
+              f"unfused {e['unfused_us']:.1f} us, graph {e['unfused_graph_us']:.1f} us "
+              f"(capture {e['unfused_graph_capture_ms']:.2f} ms)", file=sys.stderr, flush=True)
+    for lay in layers.values():
+        lay.close()
+    del layers, tWr, tb, t1, t3, t2, tx_all
+    torch.cuda.empty_cache()
+    return res
+
+
 # configurations listed beside the headline line (configuration, schedule[, tile policy]);
 # the skewed and prefill-sized layers also run with each fixed row-tile shape, beside the
 # per-expert choice
@@ -416,6 +495,10 @@ def main():
         for w in wanted:
             line["workloads"].extend(measure_workload(w[0], w[1], args.steps, args.warmup, dev,
                                                       policy=w[2] if len(w) > 2 else "by_rows"))
+    if not args.no_unfused:
+        line["unfused"] = []
+        for name in ("tiny", "sweep", "mixtral_decode", "prefill"):
+            line["unfused"].extend(unfused_comparison(name, args.steps, args.warmup, dev))
     if not args.no_peaks:
         copy_gbs, gemm_tflops = achievable_peaks(dev)
         line["achievable"] = {"copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,

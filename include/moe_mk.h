@@ -155,6 +155,23 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
                                void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The same layer as moe_mk_forward, run as seven kernels launched one after another on
+ * stream (router, top-k, scan, grouping, gate/up GroupGEMM, down GroupGEMM, combine), one
+ * task per workgroup, synchronised by the kernel boundaries alone: the launch-per-phase
+ * baseline the megakernel is measured against, plainly or captured in a HIP graph (the
+ * launches record no memset).  Same arguments, ownership and errors as moe_mk_forward;
+ * the output is bitwise that of moe_mk_forward (same tile code and summation order).  A
+ * graph of it holds B and the pointers: another B needs another capture.
+ * Source: [ET] Problem (launch overhead of 5-10 us per kernel and coarse synchronisation at
+ * kernel boundaries; a CUDA graph removes the launch overhead but keeps the boundaries) and
+ * Key results (warm-up without re-capture); [L112] Technical details, "Kernel Launch
+ * Overhead Mitigation".
+ */
+moe_mk_status_t moe_mk_forward_unfused(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias,
+                                       const void *W1, const void *W3, const void *W2, void *out, int64_t B,
+                                       void *ws, size_t ws_bytes, void *stream);
+
+/*
  * moe_mk_forward without a caller workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation).  It allocates nothing: no hipMalloc, no hipFree, no allocating library call.

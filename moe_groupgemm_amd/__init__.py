@@ -70,6 +70,8 @@ def lib():
     L.moe_mk_workspace_init.restype = ctypes.c_int
     L.moe_mk_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz, vp]
     L.moe_mk_forward.restype = ctypes.c_int
+    L.moe_mk_forward_unfused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz, vp]
+    L.moe_mk_forward_unfused.restype = ctypes.c_int
     L.moe_mk_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp]
     L.moe_mk_forward_noalloc.restype = ctypes.c_int
     L.moe_mk_routing_view.argtypes = [vp, i64, vp, sz, ctypes.POINTER(_RoutingView)]
@@ -191,6 +193,18 @@ def moe_mk_forward(plan: int, x, Wr, router_bias, W1, W3, W2, out, B: int, ws, s
            "moe_mk_forward")
 
 
+def moe_mk_forward_unfused(plan: int, x, Wr, router_bias, W1, W3, W2, out, B: int, ws, stream=None) -> None:
+    """The layer as seven kernels, one per phase (the launch-per-phase baseline)."""
+    import torch
+    bf = torch.bfloat16
+    _check_forward_args(plan, x, Wr, router_bias, W1, W3, W2, out, B, ws)
+    _check(lib().moe_mk_forward_unfused(plan, _dev_ptr(x, "x", bf), _dev_ptr(Wr, "Wr", torch.float32),
+                                        _dev_ptr(router_bias, "router_bias", torch.float32), _dev_ptr(W1, "W1", bf),
+                                        _dev_ptr(W3, "W3", bf), _dev_ptr(W2, "W2", bf), _dev_ptr(out, "out", bf), B,
+                                        _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_mk_forward_unfused")
+
+
 def moe_mk_forward_noalloc(plan: int, x, Wr, router_bias, W1, W3, W2, out, B: int, err=None, stream=None) -> None:
     """moe_mk_forward on the library's static per-GPU scratch (allocates nothing); ``err``:
     optional int32 device tensor of one element receiving the forward's device error bits."""
@@ -301,6 +315,19 @@ class MoELayer:
         return out
 
     __call__ = forward
+
+    def forward_unfused(self, x, out=None, stream=None):
+        """The same layer as one kernel per phase (the launch-per-phase baseline)."""
+        import torch
+        if x.dim() != 2 or x.shape[1] != self.d:
+            raise ValueError(f"x must have shape (B, {self.d}), got {tuple(x.shape)}")
+        B = x.shape[0]
+        if B > self.max_batch:
+            raise ValueError(f"batch {B} exceeds the workspace capacity {self.max_batch}")
+        if out is None:
+            out = torch.empty((B, self.d), dtype=torch.bfloat16, device=x.device)
+        moe_mk_forward_unfused(self.plan, x, self.Wr, self.bias, self.W1, self.W3, self.W2, out, B, self.ws, stream)
+        return out
 
     def routing(self, B):
         return moe_mk_routing_view(self.plan, B, self.ws)

@@ -18,6 +18,7 @@ hipError_t mk_launch(const mk::Params &p, int grid, hipStream_t stream, bool coo
 hipError_t mk_ws_init(void *ws, size_t bytes, hipStream_t stream);
 hipError_t mk_occupancy(int *blocks_per_cu);
 hipError_t mk_scratch(void **ptr, size_t *bytes);
+hipError_t mk_launch_unfused(const mk::Params &p, hipStream_t stream);
 
 struct moe_mk_plan_s {
     mk::Shape s;
@@ -217,6 +218,7 @@ mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const
     P.trace = (long long *)(base + L.trace);
     P.err_out = nullptr;
     P.heal = 0;
+    P.unfused = 0;
     return P;
 }
 
@@ -242,6 +244,21 @@ moe_mk_status_t moe_mk_forward(moe_mk_plan_t plan, const void *x, const float *W
     if (hipSetDevice(plan->device) != hipSuccess) return MOE_MK_EHIP;
     if (mk_launch(P, plan->grid, (hipStream_t)stream, plan->sched == MOE_MK_SCHED_STATIC_COOPERATIVE) != hipSuccess)
         return MOE_MK_EHIP;
+    return MOE_MK_OK;
+}
+
+moe_mk_status_t moe_mk_forward_unfused(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias,
+                                       const void *W1, const void *W3, const void *W2, void *out, int64_t B, void *ws,
+                                       size_t ws_bytes, void *stream) {
+    const moe_mk_status_t st = check_forward(plan, x, Wr, router_bias, W1, W3, W2, out, B);
+    if (st != MOE_MK_OK || B == 0) return st;
+    if (!ws || !aligned16(ws)) return MOE_MK_EINVAL;
+    const int64_t cap = capacity(plan, ws_bytes);
+    if (cap < B) return MOE_MK_EWORKSPACE;
+    mk::Params P = make_params(plan, x, Wr, router_bias, W1, W3, W2, out, B, (char *)ws, cap);
+    P.unfused = 1;
+    if (hipSetDevice(plan->device) != hipSuccess) return MOE_MK_EHIP;
+    if (mk_launch_unfused(P, (hipStream_t)stream) != hipSuccess) return MOE_MK_EHIP;
     return MOE_MK_OK;
 }
 

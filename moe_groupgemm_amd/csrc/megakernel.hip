@@ -992,7 +992,8 @@ __device__ __forceinline__ void publish_row_tiles(const MK_C Params &P, int e, i
         pub(P.mt_expert + i, e);
         pub(P.mt_row0 + i, off + m * kWideBM);
         pub(P.mt_rows + i, min(kWideBM, h - m * kWideBM));
-        for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+        if (!P.unfused)
+            for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
     }
     const int r0 = t.nw ? t.full * kWideBM : 0;  // a wide expert's remainder, or all rows
     for (int m = 0; m < t.nn; ++m) {
@@ -1000,7 +1001,8 @@ __device__ __forceinline__ void publish_row_tiles(const MK_C Params &P, int e, i
         pub(P.mt_expert + i, e);
         pub(P.mt_row0 + i, off + r0 + m * kBM);
         pub(P.mt_rows + i, min(kBM, h - r0 - m * kBM));
-        for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+        if (!P.unfused)
+            for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
     }
 }
 
@@ -1067,14 +1069,14 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &m
         pub(P.indptr + e, off);
         pub(P.mt_base + e, mbase);
         publish_row_tiles(P, e, h, off, et, mbase);
-        if (h) pub(P.ev_exp + e, h);
+        if (h && !P.unfused) pub(P.ev_exp + e, h);
     }
     if (e == 0) {
         pub(P.indptr + E, total_h);
         pub(P.mt_base + E, total_mt);
         st_relaxed(P.ctl + CTL_MT_TOTAL, total_mt);
         st_relaxed(P.ctl + CTL_MW, total_w);
-        pub(P.ctl + CTL_EV_Y, P.S * total_mt * (total_w > 0 ? P.NB2w : P.NB2));
+        if (!P.unfused) pub(P.ctl + CTL_EV_Y, P.S * total_mt * (total_w > 0 ? P.NB2w : P.NB2));
     }
     mw_out = total_w;
     // per-tile row offsets: exp_indptr[e] + rows of e in earlier tiles; a thread's chunk
@@ -2699,6 +2701,60 @@ __global__ void moe_ws_init_ctl(int *ctl_generic) {
     }
 }
 
+// ------------------------------------------------------------------------------ unfused pipeline
+// The same layer as one kernel per phase, for comparison with the megakernel: each kernel runs
+// one task per workgroup with the megakernel's task code, and the kernel boundaries are the
+// only synchronisation (what "Event Tensor", Problem, describes as the launch-per-kernel model
+// with coarse synchronisation at kernel boundaries; a HIP graph of these launches removes
+// the host launch cost but keeps the boundaries).  The GroupGEMM kernels are launched with
+// the grid of the most row tiles the workspace allows; workgroups past the row tiles the scan
+// found return at once.
+__global__ void __launch_bounds__(kThreads, 1) moe_unfused_route(Params Parg) {
+    const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
+    int tg, eb;
+    route_task_coords(P, uni((int)blockIdx.x), tg, eb);
+    task_route_body(P, tg, eb);
+}
+__global__ void __launch_bounds__(kThreads, 1) moe_unfused_topk(Params Parg) {
+    const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
+    task_topk(P, uni((int)blockIdx.x));
+}
+__global__ void __launch_bounds__(kThreads, 1) moe_unfused_scan(Params Parg) {
+    const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
+    int mw = 0;
+    task_scan(P, mw);
+}
+__global__ void __launch_bounds__(kThreads, 1) moe_unfused_group(Params Parg) {
+    const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
+    task_group(P, uni((int)blockIdx.x));
+}
+// Gate/up tile j = (row tile, column tile) of f range sp = blockIdx.y.
+__global__ void __launch_bounds__(kThreads, 1) moe_unfused_gemm1(Params Parg) {
+    const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
+    const int mt_total = uni(ld_relaxed(P.ctl + CTL_MT_TOTAL));
+    const int Q = P.NB1 / P.S, j = uni((int)blockIdx.x), sp = uni((int)blockIdx.y);
+    const int mt = j / Q;
+    if (mt >= mt_total) return;
+    task_gemm1<true>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), sp * Q + (j - mt * Q));
+}
+// Down-projection tile j of f range sp = blockIdx.y.
+__global__ void __launch_bounds__(kThreads, 1) moe_unfused_gemm2(Params Parg) {
+    const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
+    const int mt_total = uni(ld_relaxed(P.ctl + CTL_MT_TOTAL));
+    const bool wide = uni(ld_relaxed(P.ctl + CTL_MW)) > 0;
+    const int N2 = wide ? P.NB2w : P.NB2, j = uni((int)blockIdx.x), sp = uni((int)blockIdx.y);
+    const int mt = j / N2;
+    if (mt >= mt_total) return;
+    if (wide)
+        task_gemm2<true>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), j - mt * N2, sp, mt);
+    else
+        task_gemm2<false>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), j - mt * N2, sp, mt);
+}
+__global__ void __launch_bounds__(kThreads, 1) moe_unfused_combine(Params Parg) {
+    const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
+    task_combine(P, uni((int)blockIdx.x));
+}
+
 }  // namespace mk
 
 // ------------------------------------------------------------------------------ launch glue
@@ -2715,6 +2771,20 @@ hipError_t mk_launch(const mk::Params &p, int grid, hipStream_t stream, bool coo
                                           stream);
     }
     hipLaunchKernelGGL(mk::moe_megakernel, dim3(grid), dim3(mk::kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+// The unfused pipeline: seven launches on stream (grids from the host-known counts; the
+// GroupGEMM grids cover the most row tiles the workspace holds).
+hipError_t mk_launch_unfused(const mk::Params &p, hipStream_t stream) {
+    const dim3 blk(mk::kThreads);
+    hipLaunchKernelGGL(mk::moe_unfused_route, dim3(p.nR), blk, 0, stream, p);
+    hipLaunchKernelGGL(mk::moe_unfused_topk, dim3(p.T), blk, 0, stream, p);
+    hipLaunchKernelGGL(mk::moe_unfused_scan, dim3(1), blk, 0, stream, p);
+    hipLaunchKernelGGL(mk::moe_unfused_group, dim3(p.T), blk, 0, stream, p);
+    hipLaunchKernelGGL(mk::moe_unfused_gemm1, dim3(p.mt_cap * (p.NB1 / p.S), p.S), blk, 0, stream, p);
+    hipLaunchKernelGGL(mk::moe_unfused_gemm2, dim3(p.mt_cap * p.NB2, p.S), blk, 0, stream, p);
+    hipLaunchKernelGGL(mk::moe_unfused_combine, dim3(p.nC), blk, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -297,6 +297,9 @@ struct Params {
     // device error (clearing the error word), so the next forward starts clean.
     MK_G int *err_out;
     int heal;
+    // Set for the phase-per-kernel pipeline (the unfused baseline): kernel boundaries order
+    // the phases, so the scan arms no events and the workspace stays at its rest state.
+    int unfused;
 };
 
 // The static scratch of the allocation-free entry point (one per GPU).

@@ -575,3 +575,60 @@ def test_static_cooperative_launch(B, d, f, E, k):
     out_c, _ = full_check(x, Wr, bias, W1, W3, W2, k, mk.MOE_MK_SCHED_STATIC_COOPERATIVE, f"cooperative B={B}")
     out_s, _ = full_check(x, Wr, bias, W1, W3, W2, k, mk.MOE_MK_SCHED_STATIC, f"static B={B}")
     assert np.array_equal(out_c.view(np.uint32), out_s.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------ unfused pipeline
+
+@pytest.mark.parametrize("B,d,f,E,k,zipf", [(16, 256, 512, 8, 2, None), (203, 256, 384, 16, 4, None),
+                                            (300, 256, 384, 4, 2, None), (21, 128, 8192, 4, 2, None),
+                                            (600, 256, 256, 16, 4, 1.2), (1, 256, 256, 8, 2, None)],
+                         ids=["one_tile", "ragged_multi_tile", "wide", "down_splits", "zipf_mixed_tiles", "B1"])
+def test_unfused_pipeline_matches_megakernel(B, d, f, E, k, zipf):
+    # seven kernels, one per phase, with the megakernel's task code: routing exact, output
+    # within tolerance of the oracle and bitwise the megakernel's; the workspace stays at rest
+    # (a megakernel forward on it afterwards is unaffected)
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=2300 + B, zipf_s=zipf)
+    ref = oracle.forward(x, Wr, bias, W1, W3, W2, k)
+    tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
+    layer = mk.MoELayer(E, k, d, f, tWr, t1, t3, t2, router_bias=tb, sched=mk.MOE_MK_SCHED_STATIC, max_batch=B)
+    log(f"unfused pipeline B={B} d={d} f={f} E={E} k={k}")
+    out_u = layer.forward_unfused(tx)
+    torch.cuda.synchronize()
+    check_routing(routing_numpy(layer, B), ref, B, E)
+    check_out(out_u.float().cpu().numpy(), ref["out"], f"unfused B={B}")
+    out_m = layer(tx)
+    torch.cuda.synchronize()
+    assert layer.error() == 0
+    assert torch.equal(out_u.view(torch.int16), out_m.view(torch.int16))
+    layer.close()
+
+
+@pytest.mark.parametrize("path", ["unfused", "megakernel"])
+def test_graph_replays_match_eager(path):
+    # the forward captured in a HIP graph (no memset nodes: the unfused pipeline arms no
+    # events, the megakernel restores its control block itself), replayed several times with
+    # eager forwards and synchronisations in between; every replay equals the eager result
+    B, d, f, E, k = 90, 256, 384, 8, 2
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=2400)
+    tx, tWr, tb, t1, t3, t2 = dev_inputs(x, Wr, bias, W1, W3, W2)
+    layer = mk.MoELayer(E, k, d, f, tWr, t1, t3, t2, sched=mk.MOE_MK_SCHED_DYNAMIC, max_batch=B)
+    run = layer.forward_unfused if path == "unfused" else layer.forward
+    out = torch.empty((B, d), dtype=torch.bfloat16, device="cuda")
+    ref = run(tx).clone()
+    torch.cuda.synchronize()
+    run(tx, out)  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(tx, out)
+    for rep in range(4):
+        out.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        eager = layer(tx)  # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(eager.view(torch.int16), ref.view(torch.int16))
+    assert layer.error() == 0
+    del g
+    layer.close()
