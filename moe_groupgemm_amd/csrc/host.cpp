@@ -197,6 +197,8 @@ mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const
     P.ev_logit = (int *)(base + L.ev_logit);
     P.ev_exp = (int *)(base + L.ev_exp);
     P.ev_h = (int *)(base + L.ev_h);
+    P.ev_d = (int *)(base + L.ev_d);
+    P.nch = (int)mk::ceil_div(s.d, mk::kCombineCols);
     P.logits = (float *)(base + L.logits);
     P.topk_idx = (int *)(base + L.topk_idx);
     P.topk_w = (float *)(base + L.topk_w);
@@ -210,6 +212,7 @@ mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const
     P.mt_rows = (int *)(base + L.mt_rows);
     P.perm = (int *)(base + L.perm);
     P.inv = (int *)(base + L.inv);
+    P.amt = (int *)(base + L.amt);
     P.h = (uint16_t *)(base + L.h);
     P.y = (uint16_t *)(base + L.y);
     P.yp = (float *)(base + L.yp);

@@ -54,8 +54,9 @@ struct FusedWork {
     int off[kMaxE];                  // exp_indptr[e]
     int mtb[kMaxE + 1];              // first row tile of each expert
     int poff[kMaxE], pnm[kMaxE];     // queue offset and row tiles of each fired expert
-    int perm[kTileTokens * kMaxK];   // the batch's perm and inv, written out contiguously
+    int perm[kTileTokens * kMaxK];   // the batch's perm, inv and row tiles, written out contiguously
     int inv[kTileTokens * kMaxK];
+    int amt[kTileTokens * kMaxK];
     int part[kWaves];
     int base;
 };
@@ -78,6 +79,7 @@ struct ScanSmem {
 struct GroupSmem {
     unsigned long long mask[kMaxE];
     int toff[kMaxE];  // the tile's row offsets tile_off[t, e]
+    int eoff[kMaxE], emt[kMaxE], erows[kMaxE];  // per expert: exp_indptr, first row tile, rows per row tile
     int poff[kMaxE], pm0[kMaxE], pnm[kMaxE];  // per expert: queue offset, first row tile, row tiles
     int part[kWaves];
     int base;
@@ -982,18 +984,26 @@ __device__ __forceinline__ ExpertTiles expert_tiles(const MK_C Params &P, int h)
     return t;
 }
 
+// Events of row tile i: its gate/up tiles per f range (NB1/S each, ev_h) and its
+// down-projection tiles of bn2 columns per combine chunk (ev_d).
+__device__ __forceinline__ void arm_row_tile(const MK_C Params &P, int i, int bn2) {
+    if (P.unfused) return;  // kernel boundaries order the phases there
+    for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+    for (int c = 0; c < P.nch; ++c) pub(P.ev_d + i * P.nch + c, min(kCombineCols, P.d - c * kCombineCols) / bn2);
+}
+
 // Publish expert e's row tiles (h rows from grouped row off) as row tiles mbase.. (its wide
-// ones first), each with its gate/up events armed (NB1/S tiles per f range).  A row tile's
-// shape follows from its rows: wide ones hold more than kBM rows, narrow ones at most kBM.
+// ones first), each with its events armed (arm_row_tile; bn2 columns per down-projection
+// tile).  A row tile's shape follows from its rows: wide ones hold more than kBM rows, narrow
+// ones at most kBM.
 __device__ __forceinline__ void publish_row_tiles(const MK_C Params &P, int e, int h, int off, const ExpertTiles &t,
-                                                  int mbase) {
+                                                  int mbase, int bn2) {
     for (int m = 0; m < t.nw; ++m) {
         const int i = mbase + m;
         pub(P.mt_expert + i, e);
         pub(P.mt_row0 + i, off + m * kWideBM);
         pub(P.mt_rows + i, min(kWideBM, h - m * kWideBM));
-        if (!P.unfused)
-            for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+        arm_row_tile(P, i, bn2);
     }
     const int r0 = t.nw ? t.full * kWideBM : 0;  // a wide expert's remainder, or all rows
     for (int m = 0; m < t.nn; ++m) {
@@ -1001,8 +1011,7 @@ __device__ __forceinline__ void publish_row_tiles(const MK_C Params &P, int e, i
         pub(P.mt_expert + i, e);
         pub(P.mt_row0 + i, off + r0 + m * kBM);
         pub(P.mt_rows + i, min(kBM, h - r0 - m * kBM));
-        if (!P.unfused)
-            for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+        arm_row_tile(P, i, bn2);
     }
 }
 
@@ -1068,7 +1077,7 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &m
         pub(P.hist + e, h);
         pub(P.indptr + e, off);
         pub(P.mt_base + e, mbase);
-        publish_row_tiles(P, e, h, off, et, mbase);
+        publish_row_tiles(P, e, h, off, et, mbase, total_w > 0 ? kWideBN : kBN);
         if (h && !P.unfused) pub(P.ev_exp + e, h);
     }
     if (e == 0) {
@@ -1076,8 +1085,12 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &m
         pub(P.mt_base + E, total_mt);
         st_relaxed(P.ctl + CTL_MT_TOTAL, total_mt);
         st_relaxed(P.ctl + CTL_MW, total_w);
-        if (!P.unfused) pub(P.ctl + CTL_EV_Y, P.S * total_mt * (total_w > 0 ? P.NB2w : P.NB2));
+        if (!P.unfused && P.sched) pub(P.ctl + CTL_EV_G1, P.S * total_mt);
     }
+    // The routing tiles' events (at rest once their top-k ran) now count each tile's
+    // grouping task: the combine tasks of a tile's tokens read its perm/inv and row tiles.
+    if (!P.unfused)
+        for (int t = threadIdx.x; t < P.T; t += kThreads) pub(P.ev_logit + t, 1);
     mw_out = total_w;
     // per-tile row offsets: exp_indptr[e] + rows of e in earlier tiles; a thread's chunk
     // starts after the chunks of lower r and the tiles of earlier rounds
@@ -1128,6 +1141,10 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &Pa, int 
     }
     for (int i = threadIdx.x; i < E; i += kThreads) {
         g.toff[i] = P.tile_off[(size_t)t * E + i];
+        g.eoff[i] = P.indptr[i];
+        g.emt[i] = P.mt_base[i];
+        const int h = P.hist[i];
+        g.erows[i] = expert_tiles(P, h).nw ? kWideBM : kBM;
         g.mask[i] = 0ull;
     }
     __syncthreads();
@@ -1138,11 +1155,15 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &Pa, int 
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         if (ev[j] >= 0) {
+            const int e = ev[j];
             const int a = b * k + w + j * kWaves;
-            const int rank = __popcll(g.mask[ev[j]] & ((1ull << lane) - 1ull));
-            const int p = g.toff[ev[j]] + rank;
+            const int rank = __popcll(g.mask[e] & ((1ull << lane) - 1ull));
+            const int p = g.toff[e] + rank;
             pub(P.perm + p, a);
             pub(P.inv + a, p);
+            // the row tile of grouped row p: the expert's tiles hold erows rows each from its
+            // first row (a wide expert's last tile holds the remainder)
+            pub(P.amt + a, g.emt[e] + (p - g.eoff[e]) / g.erows[e]);
         }
     }
 }
@@ -1388,8 +1409,10 @@ __device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0
 // With S > 1 splits, every split stores its fp32 partial in yp[sp]; the split that
 // finishes a tile last (a per-tile counter) adds the S partials in split order and writes
 // the rounded sum to y, so the result does not depend on which split finished last.
+// Returns whether this call completed the y tile (always with S = 1; with S > 1 only for the
+// split that added the partials).
 template <int AR>
-__device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0, int nrows, int n, int sp,
+__device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0, int nrows, int n, int sp,
                                            int mt) {
     const int kl = P.f / P.S;  // reduction range of this split: [sp*kl, (sp+1)*kl)
     GemmArgs ga;
@@ -1412,7 +1435,7 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
                 const int row = 16 * rb + 4 * g + r;
                 store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, col, acc0[rb][r], row < nrows);
             }
-        return;
+        return true;
     }
     const size_t split_stride = (size_t)P.B * P.k * P.d;  // floats between partial buffers
     MK_G float *ys = P.yp + (size_t)sp * split_stride;
@@ -1436,7 +1459,7 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
     __syncthreads();
     const bool last = g_sm.bcast[2] != 0;
     __syncthreads();
-    if (!last) return;
+    if (!last) return false;
     fence_acquire();
 #pragma unroll
     for (int rb = 0; rb < AR / 16; ++rb) {
@@ -1455,6 +1478,7 @@ __device__ __forceinline__ void gemm2_tile(const MK_C Params &P, int e, int row0
             store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, col, sum, row < nrows);
         }
     }
+    return true;
 }
 
 // ------------------------------------------------------------------------------ wide tiles
@@ -1911,10 +1935,10 @@ __device__ __attribute__((noinline)) void narrow_gemm1(const MK_C Params &Pa, in
 }
 // GEMM2 tile: y[rows, n0:n0+128] (or its split-sp partial) = h[rows, f range sp] W2[e][f range sp, n0:n0+128].
 template <int AR>
-__device__ __attribute__((noinline)) void narrow_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n,
+__device__ __attribute__((noinline)) bool narrow_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n,
                                                        int sp, int mt) {
     const MK_C Params &P = uni_params(Pa);
-    gemm2_tile<AR>(P, uni(e), uni(row0), uni(nrows), uni(n), uni(sp), uni(mt));
+    return gemm2_tile<AR>(P, uni(e), uni(row0), uni(nrows), uni(n), uni(sp), uni(mt));
 }
 
 // The tile code follows the row tile's rows: a row tile of more than kBM rows is a wide one
@@ -1931,41 +1955,55 @@ __device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0
     else
         narrow_gemm1<64>(P, e, row0, nrows, n);
 }
+// Returns whether the task completed its y tile (see gemm2_tile).
 template <bool WIDE>
-__device__ __forceinline__ void task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n, int sp, int mt) {
+__device__ __forceinline__ bool task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n, int sp, int mt) {
     static_assert(kWideBN % kBN == 0, "a wide down tile spans whole narrow tiles");
     if (WIDE && nrows > kBM) {
         wide_gemm2(P, e, row0, nrows, n);
-    } else if (WIDE) {
+        return true;
+    }
+    if (WIDE) {
         for (int q = 0; q < kWideBN / kBN; ++q) {  // S = 1 with wide row tiles
             if (nrows <= 16)
                 narrow_gemm2<16>(P, e, row0, nrows, (kWideBN / kBN) * n + q, 0, mt);
             else
                 narrow_gemm2<64>(P, e, row0, nrows, (kWideBN / kBN) * n + q, 0, mt);
         }
-    } else if (nrows <= 16) {
-        narrow_gemm2<16>(P, e, row0, nrows, n, sp, mt);
-    } else {
-        narrow_gemm2<64>(P, e, row0, nrows, n, sp, mt);
+        return true;
     }
+    if (nrows <= 16) return narrow_gemm2<16>(P, e, row0, nrows, n, sp, mt);
+    return narrow_gemm2<64>(P, e, row0, nrows, n, sp, mt);
 }
 
 // ------------------------------------------------------------------------------ COMBINE
 // out[b, :] = bf16( sum_{i<k} w[b,i] * y[inv[b*k+i], :] ), slot order, fp32, for
 // a combine task: CT tokens x kCombineCols columns (4 columns per thread).
+// The task first waits for the down-projection tiles its rows need: each (token, slot) row
+// lies in one row tile, whose event for this column chunk counts its y tiles not yet written
+// (in the unfused pipeline the kernel boundary has already ordered them).  Returns false
+// when a wait ended on the watchdog or the error word; t1 receives the time the waits ended.
 template <int KB, int CT>
-__device__ __forceinline__ void combine_tile(const MK_C Params &P, int c) {
+__device__ __forceinline__ bool combine_tile(const MK_C Params &P, int c, unsigned long long &t1) {
     CombineSmem &cs = g_sm.u.c;
-    const int nchunks = (P.d + kCombineCols - 1) / kCombineCols;
+    const int nchunks = P.nch;
     const int grp = c / nchunks, chunk = c - grp * nchunks;
     const int b_lo = grp * CT;
     const int nb = min(CT, P.B - b_lo);
     const int k = P.k;
+    // the grouping of the tokens' routing tile is done (a batch of one routing tile is grouped
+    // before the scan event that every combine task comes after)
+    if (!P.unfused && P.T > 1 && !wg_wait_zero(P, P.ev_logit + b_lo / kTileTokens)) return false;
+    bool ok = true;
     for (int i = threadIdx.x; i < nb * k; i += kThreads) {
         cs.row[i] = P.inv[(size_t)b_lo * k + i];
         cs.w[i] = P.topk_w[(size_t)b_lo * k + i];
+        if (!P.unfused) ok = ok && spin_until(P.ev_d + P.amt[(size_t)b_lo * k + i] * nchunks + chunk, 0, P.ctl,
+                                             P.watchdog);
     }
-    __syncthreads();
+    if (__syncthreads_or(!ok)) return false;
+    if (!P.unfused) wg_acquire();  // the rows written on other CUs, visible to this CU's loads
+    t1 = now_ticks();
     const int q = (chunk * kCombineCols) / 4 + threadIdx.x;  // this thread's 4-column group
     if (4 * q < P.d) {
         // the rows of every token of the task in flight before any is used
@@ -1997,34 +2035,35 @@ __device__ __forceinline__ void combine_tile(const MK_C Params &P, int c) {
         }
     }
     __syncthreads();
+    return true;
 }
 
-__device__ __attribute__((noinline)) void task_combine(const MK_C Params &Pa, int c) {
+__device__ __attribute__((noinline)) bool task_combine(const MK_C Params &Pa, int c, unsigned long long &t1) {
     const MK_C Params &P = uni_params(Pa);
     if (P.CT == 8) {  // k <= 8
         if (P.k <= 2)
-            combine_tile<2, 8>(P, c);
+            return combine_tile<2, 8>(P, c, t1);
         else if (P.k <= 4)
-            combine_tile<4, 8>(P, c);
+            return combine_tile<4, 8>(P, c, t1);
         else
-            combine_tile<8, 8>(P, c);
+            return combine_tile<8, 8>(P, c, t1);
     } else if (P.CT == 1) {
         if (P.k <= 2)
-            combine_tile<2, 1>(P, c);
+            return combine_tile<2, 1>(P, c, t1);
         else if (P.k <= 4)
-            combine_tile<4, 1>(P, c);
+            return combine_tile<4, 1>(P, c, t1);
         else if (P.k <= 8)
-            combine_tile<8, 1>(P, c);
+            return combine_tile<8, 1>(P, c, t1);
         else
-            combine_tile<16, 1>(P, c);
+            return combine_tile<16, 1>(P, c, t1);
     } else if (P.k <= 2) {
-        combine_tile<2, 4>(P, c);
+        return combine_tile<2, 4>(P, c, t1);
     } else if (P.k <= 4) {
-        combine_tile<4, 4>(P, c);
+        return combine_tile<4, 4>(P, c, t1);
     } else if (P.k <= 8) {
-        combine_tile<8, 4>(P, c);
+        return combine_tile<8, 4>(P, c, t1);
     } else {
-        combine_tile<16, 4>(P, c);
+        return combine_tile<16, 4>(P, c, t1);
     }
 }
 
@@ -2073,6 +2112,7 @@ __device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs
     count_task(P, K_GROUP);
     GroupSmem &gr = g_sm.u.gr;
     wg_stores_done();
+    if (threadIdx.x == 0) add_relaxed(P.ev_logit + t, -1);  // the tile is grouped (see task_scan)
     int skip = -1;
     if ((P.debug & 1) && t == 0) {  // debug: drop the notification of the tile's first expert
         for (int e = 0; e < P.E; ++e)
@@ -2169,7 +2209,7 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
             pub(P.mt_expert + i, e);
             pub(P.mt_row0 + i, off + m * BM);
             pub(P.mt_rows + i, min(BM, h - m * BM));
-            for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+            arm_row_tile(P, i, kBN);
         }
     }
     if (e == 0) {
@@ -2178,7 +2218,7 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
         pub(P.mt_base + E, total_mt);
         st_relaxed(P.ctl + CTL_MT_TOTAL, total_mt);
         st_relaxed(P.ctl + CTL_MW, 0);
-        pub(P.ctl + CTL_EV_Y, total_mt * P.S * P.NB2);
+        if (P.sched) pub(P.ctl + CTL_EV_G1, P.S * total_mt);
     }
     count_task(P, K_SCAN);
     complete_bases(P, bs, total_mt, 0);
@@ -2221,12 +2261,14 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
             const int p = W.off[ev[j]] + __popcll(W.mask[ev[j]] & ((1ull << lane) - 1ull));
             W.perm[p] = a;
             W.inv[a] = p;
+            W.amt[a] = W.mtb[ev[j]];  // an expert of a one-tile batch has at most one row tile
         }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < ntok * k; i += kThreads) {
         pub(P.perm + i, W.perm[i]);
         pub(P.inv + i, W.inv[i]);
+        pub(P.amt + i, W.amt[i]);
     }
     count_task(P, K_GROUP);
     if (!dyn) {
@@ -2381,9 +2423,13 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
             task_gemm1<WIDE>(P, e, uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), n);
             const unsigned long long t2 = now_ticks();
             count_task(P, K_GEMM1);
-            // f range sp of this row tile complete: its down-projection tiles are ready
-            if (wg_notify(P, P.ev_h + mt * P.S + sp, -1) && dyn)
+            // f range sp of this row tile complete: its down-projection tiles are ready; once
+            // every row tile's have been pushed, the combine tasks follow them in the queue
+            // (each waits for the down-projection tiles of its own rows)
+            if (wg_notify(P, P.ev_h + mt * P.S + sp, -1) && dyn) {
                 wg_push_range(P, base_g2(bs, sp, P.S) + mt * bs.N2, bs.N2);
+                if (wg_notify(P, P.ctl + CTL_EV_G1, -1)) wg_push_range(P, bs.C, P.nC);
+            }
             trace_task(P, g, K_GEMM1, t0, t1, t2);
             return kTaskDone;
         }
@@ -2391,18 +2437,18 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         const int mt = j / bs.N2, n = j - mt * bs.N2;
         if (!dyn && !wg_wait_zero(P, P.ev_h + mt * P.S + sp)) return 0;
         const unsigned long long t1 = now_ticks();
-        task_gemm2<WIDE>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), n, sp, mt);
+        const bool done = task_gemm2<WIDE>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), n, sp, mt);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_GEMM2);
-        if (wg_notify(P, P.ctl + CTL_EV_Y, -1) && dyn) wg_push_range(P, bs.C, P.nC);
+        // y tile (mt, n) written: one fewer tile of its combine chunk
+        if (done) wg_notify(P, P.ev_d + mt * P.nch + n * (bs.wide ? kWideBN : kBN) / kCombineCols, -1);
         trace_task(P, g, K_GEMM2, t0, t1, t2);
         return kTaskDone;
     }
     {  // ------------------------------------------------------------------------ COMBINE
         const int c = g - bs.C;
-        if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_Y)) return 0;
-        const unsigned long long t1 = now_ticks();
-        task_combine(P, c);
+        unsigned long long t1 = 0;
+        if (!task_combine(P, c, t1)) return 0;
         const unsigned long long t2 = now_ticks();
         count_task(P, K_COMBINE);
         __syncthreads();
@@ -2662,6 +2708,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
         for (int i = threadIdx.x; i < P.E; i += kThreads) st_relaxed(P.ev_exp + i, 0);
         for (int i = threadIdx.x; i < P.mt_cap * kMaxSplits; i += kThreads) st_relaxed(P.ev_h + i, 0);
         for (int i = threadIdx.x; i < P.mt_cap * (P.d / kBN); i += kThreads) st_relaxed(P.red_ctr + i, 0);
+        for (int i = threadIdx.x; i < P.mt_cap * P.nch; i += kThreads) st_relaxed(P.ev_d + i, 0);
         wave_drain_vm();
         __syncthreads();
     }
@@ -2676,7 +2723,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
         }
         if (err != 0 && P.heal) {
             st_relaxed(P.ctl + CTL_EV_TOPK, 0);
-            st_relaxed(P.ctl + CTL_EV_Y, 0);
+            st_relaxed(P.ctl + CTL_EV_G1, 0);
             st_relaxed(P.ctl + CTL_ERR, 0);
         }
         if (P.err_out) st_relaxed(P.err_out, err);
@@ -2752,7 +2799,8 @@ __global__ void __launch_bounds__(kThreads, 1) moe_unfused_gemm2(Params Parg) {
 }
 __global__ void __launch_bounds__(kThreads, 1) moe_unfused_combine(Params Parg) {
     const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
-    task_combine(P, uni((int)blockIdx.x));
+    unsigned long long t1;
+    task_combine(P, uni((int)blockIdx.x), t1);
 }
 
 }  // namespace mk

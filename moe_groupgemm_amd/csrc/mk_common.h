@@ -46,7 +46,7 @@ enum CtlWord {
     CTL_QTAIL = 64,     // dynamic queue: slots reserved by pushers
     CTL_PF = 96,        // weight prefetch: lines claimed (rest 0)
     CTL_CQ = 128,       // static schedule: combine tasks claimed (rest 0)
-    CTL_EV_Y = 160,     // event: all down-projection tiles done
+    CTL_EV_G1 = 160,    // event: (row tile, f range) gate/up groups still open (dynamic schedule; fires the combine pushes)
     CTL_DBG = 192,      // 8 per-kind task counters (accumulate across forwards)
     CTL_XQ = 256,       // static schedule: claim counter of XCD x's GroupGEMM list at 256 + 32x
     CTL_WORDS = 512
@@ -67,6 +67,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // one routing tile (the combine is then two round trips of latency, run on as many
 // workgroups as there are tokens), else four.
 inline int combine_tokens(int64_t B, int k) { return B >= 1024 && k <= 8 ? 8 : B <= kTileTokens ? 1 : 4; }
+static_assert(kTileTokens % kCombineTokens == 0, "a combine task's tokens lie in one routing tile");
 
 // Router tokens per wave: one at small batches (more, shorter tasks), four at large ones
 // (each expert-weight row read from LDS serves four tokens), eight once that still leaves
@@ -214,8 +215,8 @@ inline Counts make_counts(const Shape &s, int64_t B) {
 
 // Byte offsets of every workspace array, for a workspace sized for B = cap tokens.
 struct Layout {
-    size_t ctl, ev_logit, ev_exp, ev_h, logits, topk_idx, topk_w, tile_hist, tile_off, hist, indptr,
-        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, h, y, yp, red_ctr, qslots, trace, total;
+    size_t ctl, ev_logit, ev_exp, ev_h, ev_d, logits, topk_idx, topk_w, tile_hist, tile_off, hist, indptr,
+        mt_base, mt_expert, mt_row0, mt_rows, perm, inv, amt, h, y, yp, red_ctr, qslots, trace, total;
     int64_t cap;
 };
 
@@ -236,6 +237,7 @@ inline Layout make_layout(const Shape &s, int64_t cap) {
     L.ev_logit = take((size_t)c.T * 4);
     L.ev_exp = take((size_t)s.E * 4);
     L.ev_h = take((size_t)c.mt_cap * kMaxSplits * 4);
+    L.ev_d = take((size_t)c.mt_cap * ceil_div(s.d, kCombineCols) * 4);
     L.logits = take((size_t)cap * s.E * 4);
     L.topk_idx = take((size_t)A * 4);
     L.topk_w = take((size_t)A * 4);
@@ -249,6 +251,7 @@ inline Layout make_layout(const Shape &s, int64_t cap) {
     L.mt_rows = take((size_t)c.mt_cap * 4);
     L.perm = take((size_t)A * 4);
     L.inv = take((size_t)A * 4);
+    L.amt = take((size_t)A * 4);
     L.h = take((size_t)A * s.f * 2);
     L.y = take((size_t)A * s.d * 2);
     // yp holds S fp32 partial results of B*k rows each; S > 1 only when B*k <= 1024, and
@@ -281,10 +284,16 @@ struct Params {
     int q_cap, mt_cap;
     long long watchdog;  // real-time ticks (100 MHz)
     MK_G int *ctl, *ev_logit, *ev_exp, *ev_h;
+    // ev_d[mt * nch + c]: down-projection tiles of row tile mt in column chunk c (kCombineCols
+    // columns, the span of one combine task) not yet written; the combine tasks wait on the
+    // events of the row tiles their tokens' rows sit in (rest 0)
+    MK_G int *ev_d;
+    int nch;
     MK_G float *logits;
     MK_G int *topk_idx;
     MK_G float *topk_w;
     MK_G int *tile_hist, *tile_off, *hist, *indptr, *mt_base, *mt_expert, *mt_row0, *mt_rows, *perm, *inv;
+    MK_G int *amt;  // row tile of each assignment b*k+i (written by the grouping)
     MK_G uint16_t *h;
     MK_G uint16_t *y;   // down-projection output, bf16 [B*k, d] in grouped row order
     MK_G float *yp;     // fp32 partials of the split down projection

@@ -279,7 +279,7 @@ def test_rest_state_and_task_counts(B, E, d, f, sched):
     assert c[C["pf"]] == 0                             # weight-prefetch claims at rest
     assert all(c[C["xq"] + 32 * x] == 0 for x in range(8))  # static per-XCD claim counters at rest
     assert c[C["cq"]] == 0                             # static combine claim counter at rest
-    assert c[C["ev_topk"]] == 0 and c[C["ev_scan"]] == 1 and c[C["ev_y"]] == 0  # events at rest
+    assert c[C["ev_topk"]] == 0 and c[C["ev_scan"]] == 1 and c[C["ev_g1"]] == 0  # events at rest
     hist = routing_numpy(layer, B)["hist"]
     exp = expected_task_counts(layer, B)
     delta = c[C["dbg"]:C["dbg"] + 7] - before[C["dbg"]:C["dbg"] + 7]
