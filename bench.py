@@ -46,6 +46,10 @@ def parse():
                     "lines to be written back during the next launch)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the box's achievable copy bandwidth and bf16 GEMM rate")
+    ap.add_argument("--summarize", choices=["stats", "pmc", "mfma"], default=None,
+                    help="write the profiles/ summary of rocprofv3 output under --prof-dir (no GPU use)")
+    ap.add_argument("--prof-dir", default=None)
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache launches of a B <= 64 workload")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip the comparison with the same layer as one kernel per phase (plain and graph)")
     ap.add_argument("--workloads", default="all",
@@ -112,6 +116,111 @@ def measured_traffic(cfg_name, B, sched):
     if kv.get("kernel_source_sha256") != kernel_source_hash() or kv.get("sched") != sched:
         return None
     return float(kv["traffic_bytes_per_launch"])
+
+
+# ------------------------------------------------------------------------------ profile summaries
+# The committed summaries under profiles/ are written from rocprofv3 CSV output by
+# `python3 bench.py --summarize stats|pmc|mfma --prof-dir DIR --config C --batch B --sched S`,
+# where DIR holds the output of the rocprofv3 commands each summary quotes (run from the
+# repository root on the GPU machine; <repo> stands for that root).
+
+def _prof_cmd(args, what):
+    run = (f"python3 <repo>/bench.py --config {args.config} --batch {args.batch} --sched {args.sched} "
+           f"--no-cpu-baseline --no-peaks --no-unfused --no-cold --workloads none")
+    d = f"<repo>/gpurun_out/prof_{args.config}_B{args.batch}_{args.sched}"
+    if what == "stats":
+        return (f"cd /tmp && export TMPDIR=/tmp && timeout -k 10 300 rocprofv3 --kernel-trace --stats -d {d}/stats "
+                f"-o p --output-format csv -- {run} --steps 20 --warmup 3")
+    if what == "mfma":
+        return (f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                f"SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE -d {d}/mfma -o p --output-format csv "
+                f"-- {run} --steps 3 --warmup 1")
+    return (f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {what} -d {d}/{what.lower()} "
+            f"-o p --output-format csv -- {run} --steps 3 --warmup 1 --copy-kernel")
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, kernel, counter, largest=False):
+    """Mean over the dispatches of `kernel` of the summed value of `counter` (or the largest
+    dispatch's value: the 1 GiB calibration copy among the smaller input uploads)."""
+    per = {}
+    for r in rows:
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        return None, 0
+    if largest:
+        return max(per.values()), 1
+    return sum(per.values()) / len(per), len(per)
+
+
+def summarize(args):
+    name = f"megakernel_{args.config}_B{args.batch}_{args.sched}"
+    lines = [f"# rocprofv3 {args.summarize}: {name}", "", "commands (from the repository root):"]
+    kern = "moe_megakernel"
+    if args.summarize == "stats":
+        lines.append("  " + _prof_cmd(args, "stats"))
+        rows = _csv_rows(os.path.join(args.prof_dir, "stats"), "kernel_stats.csv")
+        lines += ["", '"Name","Calls","AverageNs","MinNs","MaxNs"']
+        avg = None
+        for r in rows:
+            lines.append(f'"{r["Name"]}",{r["Calls"]},{float(r["AverageNs"]):.1f},{r["MinNs"]},{r["MaxNs"]}')
+            if kern in r["Name"]:
+                avg = float(r["AverageNs"]) / 1e3
+        lines += ["", f"megakernel_avg_us: {avg:.2f}"]
+    elif args.summarize == "pmc":
+        lines += ["  " + _prof_cmd(args, "FETCH_SIZE"), "  " + _prof_cmd(args, "WRITE_SIZE"),
+                  "  (--copy-kernel adds one 1 GiB device-to-device copy whose counter readings calibrate the scale)"]
+        fr = _csv_rows(os.path.join(args.prof_dir, "fetch_size"), "counter_collection.csv")
+        wr = _csv_rows(os.path.join(args.prof_dir, "write_size"), "counter_collection.csv")
+        f_kib, nf = _per_dispatch(fr, kern, "FETCH_SIZE")
+        w_kib, nw = _per_dispatch(wr, kern, "WRITE_SIZE")
+        cf, _ = _per_dispatch(fr, "copyBuffer", "FETCH_SIZE", largest=True)
+        cw, _ = _per_dispatch(wr, "copyBuffer", "WRITE_SIZE", largest=True)
+        # the 1 GiB copy reads and writes 1 GiB: the counters' KiB readings for it give the scales
+        fs, ws = (1 << 20) / cf, (1 << 20) / cw
+        traffic = (f_kib * fs + w_kib * ws) * 1024
+        lines += ["", f"megakernel FETCH_SIZE KiB per dispatch (mean of {nf}): {f_kib:.3f}",
+                  f"megakernel WRITE_SIZE KiB per dispatch (mean of {nw}): {w_kib:.3f}",
+                  f"1 GiB copy FETCH_SIZE KiB: {cf:.3f}  -> fetch scale {fs:.5f}",
+                  f"1 GiB copy WRITE_SIZE KiB: {cw:.3f}  -> write scale {ws:.5f}",
+                  f"read bytes per launch: {f_kib * fs * 1024:.0f}", f"written bytes per launch: {w_kib * ws * 1024:.0f}",
+                  f"sched: {args.sched}", f"traffic_bytes_per_launch: {traffic:.0f}",
+                  f"kernel_source_sha256: {kernel_source_hash()}"]
+    else:
+        lines.append("  " + _prof_cmd(args, "mfma"))
+        rows = _csv_rows(os.path.join(args.prof_dir, "mfma"), "counter_collection.csv")
+        vals = {c: _per_dispatch(rows, kern, c) for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                                           "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")}
+        busy, mops, gui = (vals[c][0] for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                                "GRBM_GUI_ACTIVE"))
+        lines += ["", f"per dispatch of the megakernel (mean of {vals['GRBM_GUI_ACTIVE'][1]}; summed over XCDs and SIMDs):"]
+        lines += [f"  {c:30s} {v[0]:.0f}" for c, v in vals.items()]
+        # GRBM_GUI_ACTIVE sums the 8 XCDs' busy cycles; 1024 SIMDs issue MFMAs
+        durs = {}
+        for r in rows:
+            if kern in r["Kernel_Name"]:
+                durs[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        dur = sum(durs.values()) / len(durs)
+        lines += [f"  dispatch duration under the profiler: {dur:.1f} us (mean)",
+                  f"  clock while the kernel runs: {gui / 8 / dur / 1e3:.2f} GHz (GUI-active cycles per XCD / duration)",
+                  f"  MFMA busy fraction (busy cycles / (GUI-active cycles per XCD x 1024 SIMDs)): "
+                  f"{busy / (gui / 8 * 1024):.3f}",
+                  f"  issued bf16 MFMA work: {mops * 512 / 1e9:.1f} GFLOP (MOPS x 512)",
+                  f"kernel_source_sha256: {kernel_source_hash()}"]
+    out = profile_path(args.config, args.batch, args.sched, args.summarize)
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out)
 
 
 def copy_calibration(nbytes=1 << 30):
@@ -415,6 +524,11 @@ WORKLOADS = [("prefill", "static"), ("prefill", "dynamic"), ("prefill", "static"
 
 def main():
     args = parse()
+    if args.summarize:
+        from moe_inputs import CONFIGS
+        args.batch = args.batch or CONFIGS[args.config].B
+        summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer runs on one "
               f"MI355X, with no sharding across GPUs)", file=sys.stderr)
@@ -478,7 +592,7 @@ def main():
     }
     if args.trace:  # first, while nothing else has run on the device since the timed launches
         trace_report(layer, tx, out, B)
-    if args.flush or B <= 64:
+    if args.flush or (B <= 64 and not args.no_cold):
         cold_ms = time_cold(layer, tx, out, stream, min(args.steps, 10), args.flush or "read", dev)
         cms = float(np.median(cold_ms))
         line["cold"] = {"flush": args.flush or "read", "kernel_ms_median": cms,
