@@ -2576,10 +2576,13 @@ __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
 // every task runs exactly once.  With wide row tiles every position, combine included, stays
 // on its own XCD: there taking other XCDs' tiles made the forward slower (the stolen tiles
 // lose their L2 neighbours).
+//   A forward with no more GroupGEMM and combine positions than workgroups claims nothing:
+// workgroup w runs position M1p + w (again on XCD w % 8), which spares each one a claim on a
+// counter that its XCD's other workgroups hit at the same moment.
 // Returns -1 when this workgroup has nothing left, -2 on an error.
 struct StaticCursor {
-    int g;       // next routing position (phase 0)
-    int phase;   // 0 routing, 1 GroupGEMM and combine claims
+    int g;       // next routing position (phase 0); the fixed position (phase 2)
+    int phase;   // 0 routing, 1 GroupGEMM and combine claims, 2 one fixed position
     int y;       // list of XCD x + y being claimed from: 0 its own, 1..7 the others, 8 combine
     bool steal;  // take other XCDs' positions once the own list is done
 };
@@ -2595,7 +2598,13 @@ __device__ __forceinline__ int static_next(const MK_C Params &P, Bases &bs, Stat
         // (a forward of a few tiles per workgroup gains nothing from stealing, and its idle
         // workgroups would only load the counters that the busy ones claim from)
         c.steal = !bs.wide && bs.C - bs.M1p >= 2 * (int)gridDim.x;
-        c.phase = 1;
+        c.phase = bs.total - bs.M1p <= (int)gridDim.x ? 2 : 1;
+        c.g = bs.M1p + (int)blockIdx.x;
+    }
+    if (c.phase == 2) {
+        const int g = c.g;
+        c.g = 0x7fffffff;
+        return g >= bs.total ? -1 : g;
     }
     const int x = blockIdx.x & 7;
     for (;;) {
