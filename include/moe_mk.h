@@ -256,7 +256,8 @@ moe_mk_status_t moe_mk_workspace_error(moe_mk_plan_t plan, const void *ws, size_
 /*
  * Plan facts (host).  Keys: "E" "k" "d" "f" "sched" "grid" "cus" "wg_per_cu" "BM" "BN1"
  * "BN2" "BK" "wide_BM" "wide_BN1" "wide_BN2" "wide_BK" "wide_min_rows" "route_experts"
- * "threads".  Narrow GroupGEMM tiles are BM rows x BN1 gate/up (BN2 down) columns with K
+ * "threads".  Narrow GroupGEMM tiles are BM rows x BN1 gate/up (BN2 down) columns (half as
+ * many in the forwards forward_info("BN") names) with K
  * steps of BK; wide ones wide_BM rows x wide_BN1 gate/up (wide_BN2 down) columns with K
  * steps of wide_BK, taken by experts with at least wide_min_rows rows.  Returns -1 for an
  * unknown key or invalid plan.
@@ -270,9 +271,15 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
  *   "T"                       64-token routing tiles (top-k and grouping tasks)
  *   "route_tasks"             router tasks; "route_tokens_per_wave", "route_experts_per_task"
  *   "combine_tasks"           combine tasks; "combine_tokens" tokens per combine task
- *   "NB1"                     gate/up tiles per row tile (either shape)
+ *   "BN"                      columns of a narrow tile in this forward: plan_info("BN1"), or
+ *                             half of it for the smallest batches (every expert narrow and
+ *                             twice the gate/up tiles of all its row tiles still at most one
+ *                             per workgroup), so that more compute units stream the weights
+ *   "NB1"                     gate/up tiles per row tile (f / BN, or f / wide_BN1 = f / BN1
+ *                             for a wide row tile)
  *   "NB2" "NB2_wide"          down-projection tiles per row tile and f range in a forward
- *                             without wide row tiles, and per row tile in one with them
+ *                             without wide row tiles (d / BN), and per row tile in one with
+ *                             them
  *   "S"                       f ranges of the down projection (1: not split)
  *   "wide_ok"                 1 when experts may take wide row tiles in this forward (the
  *                             kernel then gives them to experts with at least

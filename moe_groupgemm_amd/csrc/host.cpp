@@ -171,6 +171,7 @@ mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const
     P.nC = (int)c.nC;
     P.CT = mk::combine_tokens(B, s.k);
     const mk::Tiles tl = mk::tile_config(s, B);
+    P.BN = tl.BN;
     P.NB1 = tl.NB1;
     P.NB2 = tl.NB2;
     P.NB2w = tl.NB2w;
@@ -387,6 +388,7 @@ int64_t moe_mk_forward_info(moe_mk_plan_t plan, int64_t B, const char *key) {
                {"route_experts_per_task", c.reb},
                {"combine_tasks", c.nC},
                {"combine_tokens", mk::combine_tokens(B, s.k)},
+               {"BN", t.BN},
                {"NB1", t.NB1},
                {"NB2", t.NB2},
                {"NB2_wide", t.NB2w},

@@ -1077,7 +1077,7 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &m
         pub(P.hist + e, h);
         pub(P.indptr + e, off);
         pub(P.mt_base + e, mbase);
-        publish_row_tiles(P, e, h, off, et, mbase, total_w > 0 ? kWideBN : kBN);
+        publish_row_tiles(P, e, h, off, et, mbase, total_w > 0 ? kWideBN : P.BN);
         if (h && !P.unfused) pub(P.ev_exp + e, h);
     }
     if (e == 0) {
@@ -1183,20 +1183,28 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &Pa, int 
 // The swizzles make both fragment reads conflict-free.  Wave w owns output columns
 // [16w, 16w+16); 16-row blocks beyond the tile's rows are skipped, and rows of a partial
 // block past the tile's rows are never loaded (their outputs are discarded).
+// Half-width tiles (BN = kHalfBN = 64 columns, the smallest batches): the B tile rows are 128
+// bytes, chunk c of row k at c ^ hswb(k); wave w owns columns [16 (w%4), +16) and the K step of
+// 32 in each 64-deep stage that its half (w/4) takes; waves 4-7 hand their sums to waves 0-3
+// through LDS at the end, which add them (first half + second half) and write the outputs.
+//   hswb keeps the two chunks of a fragment read adjacent and gives the four even (and the four
+//   odd) rows that one half-wave's ds_read_b64_tr_b16 touches four different chunk pairs, so
+//   each half-wave reads 256 bytes from 64 distinct banks.
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int swa(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int wswb(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
+__device__ __forceinline__ int hswb(int k) { return (((k >> 1) & 1) | (((k >> 3) & 1) << 1)) << 1; }
 
 // Tile variants: DUAL (gate and up weights share the A tile) and AR, the A rows staged
 // (16 when the tile has at most 16 rows, as at decode batch sizes, else 64).  The ring of
 // stages fills the same LDS either way, so smaller A tiles buy deeper rings: more weight
 // bytes in flight per workgroup.
-template <bool DUAL, int AR>
+template <bool DUAL, int AR, int BN = kBN>
 struct GemmCfg {
     static constexpr int A_ELEMS = AR * kBK;
-    static constexpr int B_ELEMS = kBK * kBN;
+    static constexpr int B_ELEMS = kBK * BN;
     static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS * (DUAL ? 2 : 1);
     static constexpr int NS = (kRingBytes / 2) / STAGE_ELEMS < 8 ? (kRingBytes / 2) / STAGE_ELEMS : 8;
     static constexpr int B_BLOCKS = B_ELEMS / 512;                  // 1 KB blocks per weight and stage
@@ -1223,10 +1231,11 @@ __device__ __forceinline__ int a_block() {
 }
 
 // Issue the loads of one K stage.  A: one 1 KB block per wave; B: each wave moves
-// B_BLOCKS / kWaves 1 KB blocks (4 k-rows of 256 bytes) of every weight tile.
-template <bool DUAL, int AR>
+// B_BLOCKS / kWaves 1 KB blocks (4 k-rows of 256 bytes, or 8 of 128 bytes at half width) of
+// every weight tile.
+template <bool DUAL, int AR, int BN = kBN>
 __device__ __forceinline__ void stage_load(const GemmArgs &g, int k0, uint16_t *stage) {
-    using C = GemmCfg<DUAL, AR>;
+    using C = GemmCfg<DUAL, AR, BN>;
     uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
     const int lane = lane_id(), w = wave_id();
     {
@@ -1237,8 +1246,9 @@ __device__ __forceinline__ void stage_load(const GemmArgs &g, int k0, uint16_t *
 #pragma unroll
     for (int i = 0; i < C::B_BLOCKS / kWaves; ++i) {
         const int blk = (C::B_BLOCKS / kWaves) * w + i;
-        const int kr = 4 * blk + (lane >> 4);
-        const int lc = (lane & 15) ^ wswb(kr);
+        constexpr int CPR = BN / 8;  // 16-byte chunks per k-row
+        const int kr = (64 / CPR) * blk + lane / CPR;
+        const int lc = (lane % CPR) ^ (BN == kBN ? wswb(kr) : hswb(kr));
         lds_dma16(g.B0 + (size_t)(k0 + kr) * g.ldb + 8 * lc, (MK_L void *)(sB0 + blk * 512));
         if constexpr (DUAL) lds_dma16(g.B1 + (size_t)(k0 + kr) * g.ldb + 8 * lc, (MK_L void *)(sB1 + blk * 512));
     }
@@ -1248,12 +1258,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 
 // LDS byte address of this lane's half of a B fragment (rows kbase + l/4, columns
-// ncol0 + 4*(l%4)).
+// ncol0 + 4*(l%4)) in a B tile of BN columns.
+template <int BN = kBN>
 __device__ __forceinline__ uint32_t b_frag_addr(const uint16_t *sB, int kbase, int ncol0) {
     const int l = lane_id() & 15;
     const int k = kbase + (l >> 2);
     const int col = ncol0 + 4 * (l & 3);
-    return lds_addr(sB + k * kBN + ((((col >> 3) ^ wswb(k)) << 3) | (col & 7)));
+    const int sw = BN == kBN ? wswb(k) : hswb(k);
+    return lds_addr(sB + k * BN + ((((col >> 3) ^ sw) << 3) | (col & 7)));
 }
 
 __device__ __forceinline__ u32x4 join(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
@@ -1298,14 +1310,17 @@ __device__ __forceinline__ void frag_reads(const uint32_t (&ba)[4], const uint32
     }
 }
 
-template <bool DUAL, int AR>
+template <bool DUAL, int AR, int BN = kBN>
 __device__ __forceinline__ void stage_compute(const uint16_t *stage, int nrb, f32x4 (&acc0)[4], f32x4 (&acc1)[4]) {
-    using C = GemmCfg<DUAL, AR>;
+    using C = GemmCfg<DUAL, AR, BN>;
+    constexpr bool HALF = BN == kHalfBN;
     const uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, i = lane & 15;
+    const int n0 = 16 * (HALF ? (w & 3) : w);  // this wave's 16 columns
 #pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks) {
+    for (int kq = 0; kq < (HALF ? 1 : kBK / 32); ++kq) {
+        const int ks = HALF ? (w >> 2) : kq;  // at half width each half of the waves takes one K step
         const int kb = 32 * ks + 8 * g;  // this lane group's 8 k values: kb .. kb+7
         uint32_t aa[4], ba[4];
 #pragma unroll
@@ -1313,10 +1328,10 @@ __device__ __forceinline__ void stage_compute(const uint16_t *stage, int nrb, f3
             const int r = 16 * rb + i;
             aa[rb] = lds_addr(sA + (r % AR) * kBK + (((kb >> 3) ^ swa(r % AR)) << 3));
         }
-        ba[0] = b_frag_addr(sB0, kb, 16 * w);
-        ba[1] = b_frag_addr(sB0, kb + 4, 16 * w);
-        ba[2] = DUAL ? b_frag_addr(sB1, kb, 16 * w) : 0u;
-        ba[3] = DUAL ? b_frag_addr(sB1, kb + 4, 16 * w) : 0u;
+        ba[0] = b_frag_addr<BN>(sB0, kb, n0);
+        ba[1] = b_frag_addr<BN>(sB0, kb + 4, n0);
+        ba[2] = DUAL ? b_frag_addr<BN>(sB1, kb, n0) : 0u;
+        ba[3] = DUAL ? b_frag_addr<BN>(sB1, kb + 4, n0) : 0u;
         u32x2 b[4];
         u32x4 a[4];
         frag_reads<DUAL, AR>(ba, aa, b, a);
@@ -1334,9 +1349,9 @@ __device__ __forceinline__ void stage_compute(const uint16_t *stage, int nrb, f3
 
 
 
-template <bool DUAL, int AR>
+template <bool DUAL, int AR, int BN = kBN>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], f32x4 (&acc1)[4], GemmSmem &s) {
-    using C = GemmCfg<DUAL, AR>;
+    using C = GemmCfg<DUAL, AR, BN>;
     constexpr int NS = C::NS;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -1347,7 +1362,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], 
     const int nk = uni(ga.K / kBK);
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
-        if (p < nk) stage_load<DUAL, AR>(ga, p * kBK, s.ring + p * C::STAGE_ELEMS);
+        if (p < nk) stage_load<DUAL, AR, BN>(ga, p * kBK, s.ring + p * C::STAGE_ELEMS);
     int slot = 0;  // ring slot of stage st
     for (int st = 0; st < nk; ++st) {
         // stage st has landed once at most NS - 2 newer stages are outstanding
@@ -1359,13 +1374,41 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], 
         const int nxt = st + NS - 1;
         if (nxt < nk) {
             const int ns = slot == 0 ? NS - 1 : slot - 1;  // (st - 1) mod NS
-            stage_load<DUAL, AR>(ga, nxt * kBK, s.ring + ns * C::STAGE_ELEMS);
+            stage_load<DUAL, AR, BN>(ga, nxt * kBK, s.ring + ns * C::STAGE_ELEMS);
         }
-        stage_compute<DUAL, AR>(s.ring + slot * C::STAGE_ELEMS, nrb, acc0, acc1);
+        stage_compute<DUAL, AR, BN>(s.ring + slot * C::STAGE_ELEMS, nrb, acc0, acc1);
         slot = slot == NS - 1 ? 0 : slot + 1;
     }
     wait_vm<0>();
     __syncthreads();  // the ring may be reused by the next task
+    if constexpr (BN == kHalfBN) {
+        // waves 4-7 (second K half) hand their sums to waves 0-3 (same columns), which add
+        // them after their own: [wave % 4][row block][gate, up][4 values][64 lanes] floats
+        constexpr int NRB = AR / 16;
+        float *red = (float *)s.ring;
+        const int w = wave_id(), lane = lane_id();
+        auto at = [&](int rb, int q, int r) { return (((((w & 3) * NRB + rb) * 2 + q) * 4 + r) << 6) + lane; };
+        if (w >= 4) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    red[at(rb, 0, r)] = acc0[rb][r];
+                    if constexpr (DUAL) red[at(rb, 1, r)] = acc1[rb][r];
+                }
+        }
+        __syncthreads();
+        if (w < 4) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc0[rb][r] = acc0[rb][r] + red[at(rb, 0, r)];
+                    if constexpr (DUAL) acc1[rb][r] = acc1[rb][r] + red[at(rb, 1, r)];
+                }
+        }
+        __syncthreads();  // the ring may be reused by the next task
+    }
 }
 
 // Row of the A block this lane loads (8 rows of 128 bytes per block).  Rows past the
@@ -1376,20 +1419,21 @@ __device__ __forceinline__ int a_row(int nrows) {
     return min(8 * a_block<AR>() + (lane_id() >> 3), nrows - 1);
 }
 
-template <int AR>
+template <int AR, int BN = kBN>
 __device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0, int nrows, int n) {
     GemmArgs ga;
     ga.arow[0] = P.x + (size_t)(P.perm[row0 + a_row<AR>(nrows)] / P.k) * P.d;
     ga.nrows = nrows;
-    ga.B0 = P.W1 + (size_t)e * P.d * P.f + (size_t)n * kBN;
-    ga.B1 = P.W3 + (size_t)e * P.d * P.f + (size_t)n * kBN;
+    ga.B0 = P.W1 + (size_t)e * P.d * P.f + (size_t)n * BN;
+    ga.B1 = P.W3 + (size_t)e * P.d * P.f + (size_t)n * BN;
     ga.ldb = P.f;
     ga.K = P.d;
     f32x4 acc0[4], acc1[4];
-    gemm_tile<true, AR>(ga, acc0, acc1, g_sm.u.g);
+    gemm_tile<true, AR, BN>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
-    const int col = n * kBN + 16 * w + j;
+    if (BN == kHalfBN && w >= 4) return;  // (their sums went to waves 0-3)
+    const int col = n * BN + 16 * (BN == kHalfBN ? (w & 3) : w) + j;
 #pragma unroll
     for (int rb = 0; rb < AR / 16; ++rb) {
 #pragma unroll
@@ -1411,29 +1455,31 @@ __device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0
 // the rounded sum to y, so the result does not depend on which split finished last.
 // Returns whether this call completed the y tile (always with S = 1; with S > 1 only for the
 // split that added the partials).
-template <int AR>
+template <int AR, int BN = kBN>
 __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0, int nrows, int n, int sp,
                                            int mt) {
     const int kl = P.f / P.S;  // reduction range of this split: [sp*kl, (sp+1)*kl)
     GemmArgs ga;
     ga.arow[0] = P.h + (size_t)(row0 + a_row<AR>(nrows)) * P.f + (size_t)sp * kl;
     ga.nrows = nrows;
-    ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)sp * kl * P.d + (size_t)n * kBN;
+    ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)sp * kl * P.d + (size_t)n * BN;
     ga.B1 = ga.B0;
     ga.ldb = P.d;
     ga.K = kl;
     f32x4 acc0[4], acc1[4];
-    gemm_tile<false, AR>(ga, acc0, acc1, g_sm.u.g);
+    gemm_tile<false, AR, BN>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
-    const int col = n * kBN + 16 * w + j;
+    // at half width waves 4-7 handed their sums to waves 0-3 and write nothing
+    const bool own = BN == kBN || w < 4;
+    const int col = n * BN + 16 * (BN == kHalfBN ? (w & 3) : w) + j;
     if (P.S == 1) {
 #pragma unroll
         for (int rb = 0; rb < AR / 16; ++rb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * rb + 4 * g + r;
-                store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, col, acc0[rb][r], row < nrows);
+                store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, col, acc0[rb][r], own && row < nrows);
             }
         return true;
     }
@@ -1444,7 +1490,7 @@ __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rb + 4 * g + r;
-            if (row < nrows) pub(ys + (size_t)(row0 + row) * P.d + col, acc0[rb][r]);
+            if (own && row < nrows) pub(ys + (size_t)(row0 + row) * P.d + col, acc0[rb][r]);
         }
     }
     // count finished splits of this tile; the last one reduces
@@ -1461,6 +1507,7 @@ __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0
     __syncthreads();
     if (!last) return false;
     fence_acquire();
+    if (!own) return true;
 #pragma unroll
     for (int rb = 0; rb < AR / 16; ++rb) {
 #pragma unroll
@@ -1928,17 +1975,17 @@ __device__ __forceinline__ void wide_gemm2(const MK_C Params &Pa, int e, int row
 // call; the wide tiles, which need nearly all registers, are inlined for that reason).
 // GEMM1 tile: h[rows, n0:n0+128] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
 // where row p of the tile is token perm[p] / k of x; AR = staged A rows (16 or 64).
-template <int AR>
+template <int AR, int BN = kBN>
 __device__ __attribute__((noinline)) void narrow_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
     const MK_C Params &P = uni_params(Pa);
-    gemm1_tile<AR>(P, uni(e), uni(row0), uni(nrows), uni(n));
+    gemm1_tile<AR, BN>(P, uni(e), uni(row0), uni(nrows), uni(n));
 }
 // GEMM2 tile: y[rows, n0:n0+128] (or its split-sp partial) = h[rows, f range sp] W2[e][f range sp, n0:n0+128].
-template <int AR>
+template <int AR, int BN = kBN>
 __device__ __attribute__((noinline)) bool narrow_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n,
                                                        int sp, int mt) {
     const MK_C Params &P = uni_params(Pa);
-    return gemm2_tile<AR>(P, uni(e), uni(row0), uni(nrows), uni(n), uni(sp), uni(mt));
+    return gemm2_tile<AR, BN>(P, uni(e), uni(row0), uni(nrows), uni(n), uni(sp), uni(mt));
 }
 
 // The tile code follows the row tile's rows: a row tile of more than kBM rows is a wide one
@@ -1950,6 +1997,8 @@ template <bool WIDE>
 __device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
     if (WIDE && nrows > kBM)
         wide_gemm1(P, e, row0, nrows, n);
+    else if (!WIDE && uni(P.BN) == kHalfBN)  // (never in a forward with wide row tiles)
+        nrows <= 16 ? narrow_gemm1<16, kHalfBN>(P, e, row0, nrows, n) : narrow_gemm1<64, kHalfBN>(P, e, row0, nrows, n);
     else if (nrows <= 16)
         narrow_gemm1<16>(P, e, row0, nrows, n);
     else
@@ -1972,6 +2021,9 @@ __device__ __forceinline__ bool task_gemm2(const MK_C Params &P, int e, int row0
         }
         return true;
     }
+    if (uni(P.BN) == kHalfBN)
+        return nrows <= 16 ? narrow_gemm2<16, kHalfBN>(P, e, row0, nrows, n, sp, mt)
+                           : narrow_gemm2<64, kHalfBN>(P, e, row0, nrows, n, sp, mt);
     if (nrows <= 16) return narrow_gemm2<16>(P, e, row0, nrows, n, sp, mt);
     return narrow_gemm2<64>(P, e, row0, nrows, n, sp, mt);
 }
@@ -2209,7 +2261,7 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
             pub(P.mt_expert + i, e);
             pub(P.mt_row0 + i, off + m * BM);
             pub(P.mt_rows + i, min(BM, h - m * BM));
-            arm_row_tile(P, i, kBN);
+            arm_row_tile(P, i, P.BN);
         }
     }
     if (e == 0) {
@@ -2319,6 +2371,16 @@ __device__ __forceinline__ void route_task_coords(const MK_C Params &P, int g, i
     }
 }
 
+// Static schedule: publish the scan's result word (called after the notify that drained the
+// scan's stores): the row-tile count and whether any row tile is wide, tagged with the epoch.
+__device__ __forceinline__ void publish_scan(const MK_C Params &P, int mt_total, int mw) {
+    if (threadIdx.x == 0) {
+        const unsigned long long v = ((unsigned long long)(uint32_t)g_sm.epoch << 32) | (mw > 0 ? 0x80000000ull : 0ull) |
+                                     (uint32_t)mt_total;
+        st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_SCAN64), v);
+    }
+}
+
 // Runs task g (obtained at time t0).  Returns false when the forward must be abandoned.
 // WIDE: the copy of the task code that can run wide row tiles.  The other copy (used until a
 // forward is known to have them, and throughout forwards that have none) leaves them out, so
@@ -2360,7 +2422,10 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
             const unsigned long long t4 = now_ticks();
             // static GroupGEMM tasks start once this is seen: the tables and perm/inv are out
             // (dynamic ones are pushed, and no task waits on the event)
-            if (!dyn) wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
+            if (!dyn) {
+                wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
+                publish_scan(P, bs.q1 / (P.NB1 / P.S), 0);  // (q1 = row tiles x gate/up tiles per f range)
+            }
             trace_task(P, g, K_TOPK, t0, t1, t2, t3, t4);
             return kTaskDone;
         }
@@ -2383,6 +2448,7 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         count_task(P, K_SCAN);
         complete_bases(P, bs, mt_total, mw);
         wg_notify(P, P.ctl + CTL_EV_SCAN, -1);
+        if (!dyn) publish_scan(P, mt_total, mw);
         if (dyn) {
             wg_push_range(P, bs.G, P.T);
             if (threadIdx.x == 0) {  // every task of this forward now has a ticket number
@@ -2418,7 +2484,9 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         if (kind == 1) {  // ---------------------------------------------------- GEMM1
             const int mt = j / Q, n = sp * Q + (j - (j / Q) * Q);
             const int e = uni(P.mt_expert[mt]);
-            if (!dyn && !wg_wait_zero(P, P.ev_exp + e)) return 0;
+            // (a batch of one routing tile was grouped before the layout was published, and its
+            // experts' events stay at rest, unless the debug flag holds one back)
+            if (!dyn && (P.T > 1 || (P.debug & 1)) && !wg_wait_zero(P, P.ev_exp + e)) return 0;
             const unsigned long long t1 = now_ticks();
             task_gemm1<WIDE>(P, e, uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), n);
             const unsigned long long t2 = now_ticks();
@@ -2441,7 +2509,7 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         const unsigned long long t2 = now_ticks();
         count_task(P, K_GEMM2);
         // y tile (mt, n) written: one fewer tile of its combine chunk
-        if (done) wg_notify(P, P.ev_d + mt * P.nch + n * (bs.wide ? kWideBN : kBN) / kCombineCols, -1);
+        if (done) wg_notify(P, P.ev_d + mt * P.nch + n * (bs.wide ? kWideBN : P.BN) / kCombineCols, -1);
         trace_task(P, g, K_GEMM2, t0, t1, t2);
         return kTaskDone;
     }
@@ -2492,6 +2560,56 @@ __device__ __forceinline__ bool wg_wait_zero_prefetching(const MK_C Params &P, c
         if (zero || !prefetch_chunk(P)) break;
     }
     return wg_wait_zero(P, ctr);
+}
+
+// Static schedule: wait for this forward's scan result word (prefetching weight lines
+// meanwhile), acquire, and complete the GroupGEMM layout from it.  One load gives both the
+// event and the layout, where waiting on the scan event and then reading the row-tile counts
+// took two round trips.  Returns false on error or watchdog.
+__device__ __forceinline__ bool wg_wait_scan(const MK_C Params &P, Bases &bs) {
+    const uint32_t ep = (uint32_t)g_sm.epoch;
+    const MK_G unsigned long long *word = (const MK_G unsigned long long *)(P.ctl + CTL_SCAN64);
+    if (P.pf_lines > 0) {
+        for (;;) {
+            if (threadIdx.x == 0) g_sm.bcast[0] = (uint32_t)(ld_relaxed64(word) >> 32) == ep ? 1 : 0;
+            __syncthreads();
+            const bool ready = g_sm.bcast[0] != 0;
+            __syncthreads();
+            if (ready || !prefetch_chunk(P)) break;
+        }
+    }
+    if (threadIdx.x == 0) {
+        unsigned long long v = ld_relaxed64(word);
+        bool ok = true;
+        const unsigned long long t0 = now_ticks();
+        for (unsigned it = 1; (uint32_t)(v >> 32) != ep; ++it) {
+            if (it < 64)
+                __builtin_amdgcn_s_sleep(1);
+            else
+                __builtin_amdgcn_s_sleep(8);
+            v = ld_relaxed64(word);
+            if ((it & 31u) == 0) {
+                if (ld_relaxed(P.ctl + CTL_ERR) != 0) {
+                    ok = false;
+                    break;
+                }
+                if ((long long)(now_ticks() - t0) > P.watchdog) {
+                    set_error(P.ctl, 1 /* MOE_MK_ERR_WATCHDOG */);
+                    ok = false;
+                    break;
+                }
+            }
+        }
+        fence_acquire();
+        g_sm.bcast[0] = ok ? 1 : 0;
+        g_sm.bcast[1] = (int)(uint32_t)v;
+    }
+    __syncthreads();
+    const bool ok = g_sm.bcast[0] != 0;
+    const uint32_t v = (uint32_t)g_sm.bcast[1];
+    __syncthreads();
+    if (ok) complete_bases(P, bs, (int)(v & 0x7fffffffu), (int)(v >> 31));
+    return ok;
 }
 
 // Dynamic pop.  A workgroup takes the next ticket with one atomic add; tickets below nR are
@@ -2593,8 +2711,7 @@ __device__ __forceinline__ int static_next(const MK_C Params &P, Bases &bs, Stat
             c.g += gridDim.x;
             return g;
         }
-        if (!wg_wait_zero_prefetching(P, P.ctl + CTL_EV_SCAN)) return -2;
-        complete_bases_from_ctl(P, bs);
+        if (!wg_wait_scan(P, bs)) return -2;
         // (a forward of a few tiles per workgroup gains nothing from stealing, and its idle
         // workgroups would only load the counters that the busy ones claim from)
         c.steal = !bs.wide && bs.C - bs.M1p >= 2 * (int)gridDim.x;
@@ -2716,7 +2833,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
         for (int i = threadIdx.x; i < P.T; i += kThreads) st_relaxed(P.ev_logit + i, 0);
         for (int i = threadIdx.x; i < P.E; i += kThreads) st_relaxed(P.ev_exp + i, 0);
         for (int i = threadIdx.x; i < P.mt_cap * kMaxSplits; i += kThreads) st_relaxed(P.ev_h + i, 0);
-        for (int i = threadIdx.x; i < P.mt_cap * (P.d / kBN); i += kThreads) st_relaxed(P.red_ctr + i, 0);
+        for (int i = threadIdx.x; i < P.mt_cap * (P.d / kHalfBN); i += kThreads) st_relaxed(P.red_ctr + i, 0);
         for (int i = threadIdx.x; i < P.mt_cap * P.nch; i += kThreads) st_relaxed(P.ev_d + i, 0);
         wave_drain_vm();
         __syncthreads();
@@ -2791,7 +2908,10 @@ __global__ void __launch_bounds__(kThreads, 1) moe_unfused_gemm1(Params Parg) {
     const int Q = P.NB1 / P.S, j = uni((int)blockIdx.x), sp = uni((int)blockIdx.y);
     const int mt = j / Q;
     if (mt >= mt_total) return;
-    task_gemm1<true>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), sp * Q + (j - mt * Q));
+    if (uni(ld_relaxed(P.ctl + CTL_MW)) > 0)
+        task_gemm1<true>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), sp * Q + (j - mt * Q));
+    else
+        task_gemm1<false>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), sp * Q + (j - mt * Q));
 }
 // Down-projection tile j of f range sp = blockIdx.y.
 __global__ void __launch_bounds__(kThreads, 1) moe_unfused_gemm2(Params Parg) {

@@ -26,6 +26,8 @@ constexpr int kCombineTokens = 8;    // most tokens per combine task (see combin
 constexpr int kCombineCols = 4 * kThreads;  // model columns per combine task (4 per thread)
 constexpr int kBM = 64;              // GroupGEMM rows per narrow tile (one expert's rows)
 constexpr int kBN = 16 * kWaves;     // GroupGEMM columns per narrow tile (16 per wave)
+constexpr int kHalfBN = kBN / 2;     // columns of a half-width narrow tile (smallest batches)
+constexpr int kGridDefault = 256;    // persistent workgroups per forward (one per CU)
 constexpr int kBK = 64;              // narrow GroupGEMM K step staged through LDS
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 16;
@@ -42,6 +44,9 @@ enum CtlWord {
     CTL_MT_TOTAL = 9,   // number of (expert, row-tile) pairs, written by the scan task
     CTL_MW = 10,        // how many of them are wide row tiles, written by the scan task
     CTL_TOTAL64 = 12,   // int64 at words 12..13: (epoch << 32) | task count (dynamic mode)
+    CTL_SCAN64 = 14,    // int64 at words 14..15: (epoch << 32) | (1 << 31 if any row tile is wide) | row
+                        // tiles, stored by the scan after its tables (static mode: the GroupGEMM
+                        // workgroups wait on this word, which gives the event and the layout at once)
     CTL_QHEAD = 32,     // dynamic queue: next ticket
     CTL_QTAIL = 64,     // dynamic queue: slots reserved by pushers
     CTL_PF = 96,        // weight prefetch: lines claimed (rest 0)
@@ -132,20 +137,34 @@ constexpr int kWideBN = 256;   // down-projection columns per wide tile
 constexpr int kWideBN1 = 128;  // gate/up columns of each weight per wide tile
 constexpr int kWideBK = 32;
 static_assert(kWideBN1 == kBN, "gate/up tiles of both shapes span the same columns");
+// Half-width narrow tiles.  When even half-width gate/up tiles of every row tile the batch can
+// have fit in one round of the grid, and the batch's experts all take narrow row tiles (B*k <=
+// kBM rows in all, so no expert reaches kWideMinRows), the narrow tiles span kHalfBN columns:
+// twice as many tiles, each streaming half the weight bytes, so that twice as many compute
+// units stream the few experts of a tiny batch.  Inside a half-width tile the eight waves take
+// four 16-column blocks and two halves of every K step, and add the halves through LDS.
+inline bool half_width(const Shape &s, int64_t B) {
+    const int64_t a = B * s.k, rt = a < s.E ? a : s.E;  // most row tiles such a batch can have
+    // (a half-width gate/up tile of a short reduction, under 256 KB of weights, is all fixed
+    // cost: ring fill, epilogue, notify; halving it gains nothing)
+    return a <= kBM && 2 * rt * (s.f / kBN) <= kGridDefault && (int64_t)s.d * kHalfBN * 4 >= (256 << 10);
+}
 struct Tiles {
-    int NB1;     // gate/up tiles per row tile (f / 128, both shapes)
-    int NB2;     // down-projection tiles per narrow row tile and f range (d / 128)
+    int BN;      // columns of a narrow tile: kBN, or kHalfBN (half_width)
+    int NB1;     // gate/up tiles per row tile (f / BN; f / 128 for wide row tiles)
+    int NB2;     // down-projection tiles per narrow row tile and f range (d / BN)
     int NB2w;    // down-projection tiles per wide row tile (d / 256)
     int S;       // f ranges of the down projection
     int wide_ok; // wide row tiles allowed in this forward
 };
 inline Tiles tile_config(const Shape &s, int64_t B) {
     Tiles t;
-    t.NB1 = s.f / kBN;
-    t.NB2 = s.d / kBN;
+    t.BN = half_width(s, B) ? kHalfBN : kBN;
+    t.NB1 = s.f / t.BN;
+    t.NB2 = s.d / t.BN;
     t.NB2w = s.d / kWideBN;
     t.S = down_splits(s, B);
-    t.wide_ok = t.S == 1 && s.d % kWideBN == 0 && s.f % kWideBN1 == 0;
+    t.wide_ok = t.S == 1 && t.BN == kBN && s.d % kWideBN == 0 && s.f % kWideBN1 == 0;
     return t;
 }
 
@@ -164,7 +183,7 @@ struct Prefetch {
 };
 inline Prefetch prefetch_plan(const Shape &s, int64_t B, int nb1, bool wide) {
     Prefetch p{0, 0};
-    if (B < 1 || B > kTileTokens || wide || nb1 < 1 || B * s.k < s.E) return p;
+    if (B < 1 || B > kTileTokens || wide || nb1 < 1 || B * s.k < s.E || half_width(s, B)) return p;
     const int64_t nt = (int64_t)s.E * nb1 < 256 ? (int64_t)s.E * nb1 : 256;
     int64_t depth = kPrefetchBytes / (nt * 4 * 128);  // rows of K: 4 lines per tile row (two of each weight)
     depth = depth < s.d ? depth : s.d;
@@ -202,8 +221,8 @@ inline Counts make_counts(const Shape &s, int64_t B) {
     c.nC = ceil_div(B, combine_tokens(B, s.k)) * ceil_div(s.d, kCombineCols);
     int64_t a = B * s.k;
     c.mt_cap = a / kBM + (a < s.E ? a : s.E) + 1;
-    c.NB1 = s.f / kBN;
-    c.NB2 = s.d / kBN;
+    c.NB1 = s.f / kHalfBN;  // upper bounds over both narrow tile widths (sizes the queue
+    c.NB2 = s.d / kHalfBN;  // and the split counters)
     c.S = down_splits(s, B);
     // combine tasks of any batch up to B (a task has at least one token), so that the queue,
     // and with it the workspace, grows with B
@@ -276,7 +295,7 @@ struct Params {
     int sched;       // 0 static, 1 dynamic
     int debug;       // MOE_MK_DEBUG_* bits
     int nR, nTG, nEB, T, nC, tpw;
-    int NB1, NB2, NB2w, S, wide_ok;  // see Tiles
+    int BN, NB1, NB2, NB2w, S, wide_ok;  // see Tiles
     int wide_min;    // an expert takes wide row tiles when it has at least this many rows (> kTileTokens)
     int reb;         // experts per router task (4 or 16)
     int CT;          // tokens per combine task

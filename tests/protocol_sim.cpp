@@ -138,7 +138,7 @@ struct Sim {
     struct Ctl {
         std::atomic<int> qhead{0}, qtail{0}, exit{0}, err{0}, ev_topk{0}, ev_scan{1}, ev_g1{0}, cq{0};
         std::atomic<int> xq[8];
-        std::atomic<uint64_t> total64{0};
+        std::atomic<uint64_t> total64{0}, scan64{0};
         Ctl() {
             for (auto &x : xq) x.store(0);
         }
@@ -299,6 +299,7 @@ struct Sim {
             publish_tables(true);
             for (int t = 0; t < T; ++t) ev_logit[t].store(1, std::memory_order_relaxed);  // grouped event
             notify(ctl->ev_scan, -1);
+            if (!dyn) publish_scan();
             if (dyn) {
                 push_range(G, T);
                 const int real = M1 + c.S * (q1 + q2) + nC;
@@ -328,7 +329,8 @@ struct Sim {
             if (kind == 0) return true;
             if (kind == 1) {  // GEMM1
                 const int m = j / Q, n = sp * Q + j % Q, e = r.mt_expert[m];
-                if (!dyn && !wait_zero(ev_exp[e])) return false;
+                // a one-tile batch was grouped before the layout was published: no wait
+                if (!dyn && (T > 1 || c.drop_notify) && !wait_zero(ev_exp[e])) return false;
                 for (int t = 0; t < T; ++t)
                     if (r.tcnt[t][e]) CHECK(P[t] == 1);
                 H[(size_t)m * c.NB1 + n] = 1;
@@ -378,6 +380,28 @@ struct Sim {
         OUT[cc] = 1;
         return true;
     }
+    // static: the scan's result word (epoch, row tiles, wide), stored after the scan's tables
+    void publish_scan() {
+        ctl->scan64.store((epoch << 32) | (wide ? 0x80000000ull : 0ull) | (uint32_t)mt, std::memory_order_release);
+    }
+    bool wait_scan() {
+        const auto t0 = std::chrono::steady_clock::now();
+        for (unsigned it = 0;; ++it) {
+            const uint64_t v = ctl->scan64.load(std::memory_order_acquire);
+            if ((v >> 32) == epoch) {
+                CHECK((int)(v & 0x7fffffff) == mt && ((v >> 31) & 1) == (uint64_t)wide);
+                return true;
+            }
+            if (ctl->err.load(std::memory_order_relaxed)) return false;
+            if ((it & 63u) == 0 &&
+                std::chrono::duration_cast<std::chrono::microseconds>(std::chrono::steady_clock::now() - t0).count() >
+                    watchdog_us) {
+                ctl->err.fetch_or(1);
+                return false;
+            }
+            std::this_thread::yield();
+        }
+    }
     int first_expert(int t) const {
         for (int e = 0; e < c.E; ++e)
             if (r.tcnt[t][e]) return e;
@@ -410,6 +434,7 @@ struct Sim {
         }
         if (c.drop_notify) ev_exp[first_expert(0)].store(1, std::memory_order_relaxed);  // a wait that never ends
         notify(ctl->ev_scan, -1);
+        publish_scan();
         return true;
     }
 
@@ -425,7 +450,7 @@ struct Sim {
                 cu.g += c.W;
                 return g;
             }
-            if (!wait_zero(ctl->ev_scan)) return -2;
+            if (!wait_scan()) return -2;
             cu.steal = !wide && Cb - M1p >= 2 * c.W;
             cu.phase = total - M1p <= c.W ? 2 : 1;
             cu.g = M1p + w;

@@ -546,6 +546,28 @@ def test_max_experts_and_top_k_wide():
         full_check(x, Wr, bias, W1, W3, W2, 16, sched, f"E=256 k=16 B=2048 {SNAME[sched]}")
 
 
+@pytest.mark.parametrize("shape", [
+    (1, 2048, 1408, 64, 6),   # the sweep's B = 1: six 1-row tiles, half-width gate/up and down tiles
+    (40, 1024, 256, 4, 1),    # up to 40 rows per expert: the 64-row staging of the half-width tile
+    (3, 1024, 4096, 4, 1),    # half width with the down projection split in two f ranges
+    (2, 1024, 8192, 4, 1),    # ... and in four
+], ids=["sweep_b1", "rows_40", "split_2", "split_4"])
+def test_half_width_tiles(shape):
+    # The smallest batches take narrow tiles of half the columns (forward_info "BN"), whose
+    # eight waves split each K step in two halves and add them through LDS: every token
+    # against the oracle on both schedules, and the two schedules bitwise equal.
+    B, d, f, E, k = shape
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=1900 + B)
+    outs = []
+    for sched in SCHEDS:
+        plan = mk.moe_mk_plan(E, k, d, f, sched)
+        assert mk.moe_mk_forward_info(plan, B, "BN") == mk.moe_mk_plan_info(plan, "BN1") // 2
+        mk.moe_mk_plan_destroy(plan)
+        out, _ = full_check(x, Wr, bias, W1, W3, W2, k, sched, f"half width B={B} d={d} f={f} {SNAME[sched]}")
+        outs.append(out)
+    assert np.array_equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
 @pytest.mark.parametrize("B", [600, 200], ids=["batch_600", "batch_200"])
 @pytest.mark.parametrize("policy", [0, mk.MOE_MK_DEBUG_NARROW_ONLY, mk.MOE_MK_DEBUG_BATCH_RULE],
