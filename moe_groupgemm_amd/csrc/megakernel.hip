@@ -261,9 +261,15 @@ __device__ __forceinline__ void wg_push_range(const MK_C Params &P, int g0, int 
 
 // Notify one counter: the group's published stores complete, then thread 0 adds delta
 // (negative = decrement).  Returns (to every thread) whether this notification brought
-// the counter to zero, i.e. fired the event.
+// the counter to zero, i.e. fired the event.  In the static schedule nobody acts on the
+// firing (the consumers poll), so the add goes out without waiting for its reply, and the
+// result is false.
 __device__ __forceinline__ bool wg_notify(const MK_C Params &P, MK_G int *ctr, int delta) {
     wg_stores_done();
+    if (P.sched == 0) {
+        if (threadIdx.x == 0) add_relaxed_noret(ctr, delta);
+        return false;
+    }
     if (threadIdx.x == 0) {
         const int old = add_relaxed(ctr, delta);
         g_sm.bcast[2] = (old + delta == 0) ? 1 : 0;
@@ -2177,8 +2183,10 @@ __device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs
     const int cnt = e < P.E ? __popcll(gr.mask[e]) : 0;
     bool fire = false;
     if (cnt && e != skip) {
-        const int old = add_relaxed(P.ev_exp + e, -cnt);
-        fire = dyn && old == cnt;
+        if (dyn)
+            fire = add_relaxed(P.ev_exp + e, -cnt) == cnt;
+        else
+            add_relaxed_noret(P.ev_exp + e, -cnt);
     }
     if (!dyn) return;
     // push the gate/up tiles of every expert this tile completed

@@ -48,6 +48,10 @@ __device__ __forceinline__ void st_relaxed(MK_G int *p, int v) {
 __device__ __forceinline__ int add_relaxed(MK_G int *p, int v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The same without a reply: the wave goes on without waiting for the atomic to be performed.
+__device__ __forceinline__ void add_relaxed_noret(MK_G int *p, int v) {
+    (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // Wait until this wave's outstanding vector memory operations (stores included) completed.
