@@ -1028,7 +1028,10 @@ __device__ __forceinline__ void publish_row_tiles(const MK_C Params &P, int e, i
 // decides how many GroupGEMM tiles each expert triggers).  Events are at rest (zero) and
 // nothing decrements them before the scan is published, so arming is a plain store.
 // Returns the number of row tiles and (mw) of wide ones.
-__device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &mw_out) {
+// ph (optional): receives the times the histogram scans and the row-tile publication ended
+// (trace records).
+__device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &mw_out,
+                                                   unsigned long long *ph = nullptr) {
     const MK_C Params &P = uni_params(Pa);
     ScanSmem &ss = g_sm.u.s;
     const int e = threadIdx.x;
@@ -1078,6 +1081,7 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &m
     const int off = block_excl_scan(h, ss.part, &total_h);
     const int mbase = block_excl_scan(et.nw + et.nn, ss.part, &total_mt);
     block_excl_scan(et.nw, ss.part, &total_w);
+    if (ph) ph[0] = now_ticks();
     if (e < E) {
         ss.carry[e] = off;
         pub(P.hist + e, h);
@@ -1098,6 +1102,7 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &m
     if (!P.unfused)
         for (int t = threadIdx.x; t < P.T; t += kThreads) pub(P.ev_logit + t, 1);
     mw_out = total_w;
+    if (ph) ph[1] = now_ticks();
     // per-tile row offsets: exp_indptr[e] + rows of e in earlier tiles; a thread's chunk
     // starts after the chunks of lower r and the tiles of earlier rounds
     for (int t0 = 0; t0 < P.T; t0 += rows) {
@@ -2164,12 +2169,16 @@ __device__ __forceinline__ void trace_task(const MK_C Params &P, int g, int kind
 // mode the gate/up tiles of every expert this brought to zero are pushed, with one
 // reservation of queue slots for all of them (a prefix sum over the experts places each
 // expert's tasks, in expert order).
-__device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs, int t, bool dyn) {
+// ph (optional): receives the times the grouping's stores were issued and had completed.
+__device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs, int t, bool dyn,
+                                                 unsigned long long *ph = nullptr) {
     static_assert(kMaxE <= kThreads, "one thread per expert");
     task_group(P, t);
     count_task(P, K_GROUP);
     GroupSmem &gr = g_sm.u.gr;
+    if (ph) ph[0] = now_ticks();
     wg_stores_done();
+    if (ph) ph[1] = now_ticks();
     if (threadIdx.x == 0) add_relaxed(P.ev_logit + t, -1);  // the tile is grouped (see task_scan)
     int skip = -1;
     if ((P.debug & 1) && t == 0) {  // debug: drop the notification of the tile's first expert
@@ -2451,7 +2460,8 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         }
         const unsigned long long t1 = now_ticks();
         int mw = 0;
-        const int mt_total = task_scan(P, mw);
+        unsigned long long ph[2];
+        const int mt_total = task_scan(P, mw, ph);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_SCAN);
         complete_bases(P, bs, mt_total, mw);
@@ -2466,7 +2476,7 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
                 st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64), tag | (uint32_t)real);
             }
         }
-        trace_task(P, g, K_SCAN, t0, t1, t2);
+        trace_task(P, g, K_SCAN, t0, t1, t2, ph[0], ph[1]);
         return kTaskDone;
     }
     if (g < bs.M1p) {  // -------------------------------------------------------- GROUP
@@ -2475,8 +2485,9 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         if (P.T == 1) return kTaskDone;  // a single routing tile is grouped by its top-k task
         if (!dyn && !wg_wait_zero(P, P.ctl + CTL_EV_SCAN)) return 0;
         const unsigned long long t1 = now_ticks();
-        group_and_notify(P, bs, t, dyn);
-        trace_task(P, g, K_GROUP, t0, t1, now_ticks());
+        unsigned long long ph[2];
+        group_and_notify(P, bs, t, dyn, ph);
+        trace_task(P, g, K_GROUP, t0, t1, now_ticks(), ph[0], ph[1]);
         return kTaskDone;
     }
     if (!bs.known) complete_bases_from_ctl(P, bs);
@@ -2685,23 +2696,27 @@ __device__ __forceinline__ int wg_pop(const MK_C Params &P) {
 
 // Static schedule: the next task of this workgroup.
 //   Routing tasks (phase 0): workgroup w runs g = w, w + G, ... below the GroupGEMM blocks.
-//   GroupGEMM positions (phase 1, once the scan event fired) are claimed per XCD.  Position p
+//   GroupGEMM positions (phase 1, once the scan's result word is out) are claimed per XCD.  Position p
 // belongs to XCD p % 8 (the blocks start at multiples of 8); the workgroups of an XCD
 // (w % 8 == x, as the hardware deals them) take that XCD's positions in increasing order from
 // its claim counter, so tiles adjacent in the list start together and share operands in L2.
 // Each XCD's list is in topological order, so the smallest unfinished task of the forward
 // always has its inputs done or in progress.
-//   With narrow row tiles only (and at least two GroupGEMM positions per workgroup), once its
-// XCD's list has no GroupGEMM position left, a workgroup takes unclaimed GroupGEMM positions
-// of the other XCDs from their counters (thread 0 looks at a counter first and claims only
-// while it shows a GroupGEMM position), so that the XCDs finish the GroupGEMM phase together
-// even when skewed routing gives them unequal work.  Combine tasks, which wait for every
-// down-projection tile and read rows written on every XCD, are then claimed from one counter
-// shared by all workgroups; a workgroup reaches them only when no GroupGEMM position is left
-// unclaimed.  A claim is exclusive whoever makes it and a claimed position is always run, so
-// every task runs exactly once.  With wide row tiles every position, combine included, stays
-// on its own XCD: there taking other XCDs' tiles made the forward slower (the stolen tiles
-// lose their L2 neighbours).
+//   With at least two GroupGEMM positions per workgroup, once its XCD's list has no GroupGEMM
+// position left, a workgroup takes unclaimed GroupGEMM positions of the other XCDs from their
+// counters (thread 0 looks at a counter first and claims only while it shows a position to
+// take), so that the XCDs finish the GroupGEMM phase together even when skewed routing or
+// heavy tiles give them unequal work.  In a forward with wide row tiles only down-projection
+// positions are taken that way: a gate/up tile run away from its list's XCD loses the L2
+// neighbours that share its weights and activations (taking those too made prefill slower),
+// while a down-projection tile left at the end of a list would otherwise hold the combine up.
+// Claims are monotonic, so a position seen there is at most claimed later.  Combine tasks,
+// which wait for down-projection tiles and read rows written on every XCD, are then claimed
+// from one counter shared by all workgroups; a workgroup reaches them only when no
+// GroupGEMM position is left that it may take.  A claim is exclusive whoever makes it and a
+// claimed position is always run, so every task runs exactly once.  (Other XCDs' gate/up
+// positions of a wide forward are left to their own workgroups, which take their list in
+// order and so reach them.)
 //   A forward with no more GroupGEMM and combine positions than workgroups claims nothing:
 // workgroup w runs position M1p + w (again on XCD w % 8), which spares each one a claim on a
 // counter that its XCD's other workgroups hit at the same moment.
@@ -2722,7 +2737,7 @@ __device__ __forceinline__ int static_next(const MK_C Params &P, Bases &bs, Stat
         if (!wg_wait_scan(P, bs)) return -2;
         // (a forward of a few tiles per workgroup gains nothing from stealing, and its idle
         // workgroups would only load the counters that the busy ones claim from)
-        c.steal = !bs.wide && bs.C - bs.M1p >= 2 * (int)gridDim.x;
+        c.steal = bs.C - bs.M1p >= 2 * (int)gridDim.x;
         c.phase = bs.total - bs.M1p <= (int)gridDim.x ? 2 : 1;
         c.g = bs.M1p + (int)blockIdx.x;
     }
@@ -2737,7 +2752,12 @@ __device__ __forceinline__ int static_next(const MK_C Params &P, Bases &bs, Stat
             const int xs = (x + c.y) & 7;
             if (threadIdx.x == 0) {
                 MK_G int *ctr = P.ctl + CTL_XQ + 32 * xs;
-                g_sm.bcast[3] = c.y == 0 || bs.M1p + 8 * ld_relaxed(ctr) + xs < bs.C ? add_relaxed(ctr, 1) : -1;
+                int take = 1;
+                if (c.y != 0) {  // another XCD's list: claim only while it shows a position to take
+                    const int nx = bs.M1p + 8 * ld_relaxed(ctr) + xs;
+                    take = nx < bs.C && (!bs.wide || nx >= bs.M1p + bs.q1p);
+                }
+                g_sm.bcast[3] = take ? add_relaxed(ctr, 1) : -1;
             }
             __syncthreads();
             const int cl = g_sm.bcast[3];

@@ -451,7 +451,7 @@ struct Sim {
                 return g;
             }
             if (!wait_scan()) return -2;
-            cu.steal = !wide && Cb - M1p >= 2 * c.W;
+            cu.steal = Cb - M1p >= 2 * c.W;
             cu.phase = total - M1p <= c.W ? 2 : 1;
             cu.g = M1p + w;
         }
@@ -464,7 +464,12 @@ struct Sim {
         for (;;) {
             if (!cu.steal || cu.y < 8) {
                 const int xs = (x + cu.y) & 7;
-                const int cl = cu.y == 0 || M1p + 8 * ctl->xq[xs].load() + xs < Cb ? ctl->xq[xs].fetch_add(1) : -1;
+                bool take = true;
+                if (cu.y != 0) {  // other XCDs' lists: wide forwards take down-projection positions only
+                    const int nx = M1p + 8 * ctl->xq[xs].load() + xs;
+                    take = nx < Cb && (!wide || nx >= M1p + q1p);
+                }
+                const int cl = take ? ctl->xq[xs].fetch_add(1) : -1;
                 const int g = M1p + 8 * cl + xs;
                 if (!cu.steal) return g >= total ? -1 : g;
                 if (cl < 0 || g >= Cb) {
