@@ -122,14 +122,16 @@ __shared__ Smem g_sm;
 // positions are empty tasks).  Workgroups are dealt to the 8 XCDs round-robin, so in the
 // static schedule position p of a block runs on XCD p % 8 (unless another XCD takes it once
 // its own positions are done).  Static mode therefore maps
-// position p to the linear tile q = (p % 8) * (size / 8) + p / 8: each XCD works through
-// one contiguous eighth of the tiles (row tile major), and the tiles sharing a row tile's
-// activations or an expert's weight columns run together on the same L2.  Dynamic mode
-// uses q = p (its pushes follow the linear order).
+// the positions of XCD x, in order, to the tiles of row tiles [mt x / 8, mt (x+1) / 8) (row
+// tile major; see xcd_blocks) when the forward has wide row tiles, so that the tiles sharing a
+// row tile's activations or an expert's weight columns run together on the same L2, and both
+// GEMMs of a row tile on one XCD.  Otherwise, and in dynamic mode (whose pushes follow the
+// linear order), position p is linear tile p.
 struct Bases {
     int K, S, G, M1, M1p, C, total;
+    int mt;        // row tiles
     int q1, q2;    // tiles per G1(s) block and per G2(s) block
-    int q1p, q2p;  // the same rounded up to multiples of 8 (block sizes)
+    int q1p, q2p;  // block sizes: q1, q2 rounded up to multiples of 8 (see complete_bases)
     int N2;        // down-projection tasks per row tile and f range
     bool wide;     // the forward has wide row tiles
     bool known;    // GroupGEMM layout known once the scan has run
@@ -145,7 +147,7 @@ __device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
     b.M1 = b.G + P.T;
     b.M1p = round8(b.M1);
     b.C = b.total = 0x7fffffff;
-    b.q1 = b.q2 = b.q1p = b.q2p = b.N2 = 0;
+    b.mt = b.q1 = b.q2 = b.q1p = b.q2p = b.N2 = 0;
     b.wide = false;
     b.known = false;
     return b;
@@ -154,14 +156,27 @@ __device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
 // mt_total row tiles, mw of them wide.  The counts are made visibly wave-uniform so that
 // the layout lives in scalar registers: held in vector registers across the task body, it
 // pushed the wide tiles' K loops into spills.
+// In the static schedule with wide row tiles the blocks are dealt to the XCDs by whole row
+// tiles (xcd_blocks): XCD x takes row tiles [mt x / 8, mt (x+1) / 8) in both blocks, each list
+// padded to ceil(mt / 8) row tiles' worth, so that no row tile's gate/up tiles are split
+// between two XCDs (a down-projection list that began with a row tile shared with the previous
+// XCD's list waited for that list's last gate/up tiles).
+__device__ __forceinline__ bool xcd_blocks(const MK_C Params &P, const Bases &b) { return P.sched == 0 && b.wide; }
 __device__ __forceinline__ void complete_bases(const MK_C Params &P, Bases &b, int mt_total, int mw) {
     mt_total = uni(mt_total);
+    b.mt = mt_total;
     b.wide = uni(mw) > 0;
     b.N2 = b.wide ? P.NB2w : P.NB2;
     b.q1 = mt_total * (P.NB1 / P.S);
     b.q2 = mt_total * b.N2;
-    b.q1p = round8(b.q1);
-    b.q2p = round8(b.q2);
+    if (xcd_blocks(P, b)) {
+        const int per = (mt_total + 7) >> 3;  // row tiles of the longest XCD list
+        b.q1p = 8 * per * (P.NB1 / P.S);
+        b.q2p = 8 * per * b.N2;
+    } else {
+        b.q1p = round8(b.q1);
+        b.q2p = round8(b.q2);
+    }
     b.C = b.M1p + P.S * (b.q1p + b.q2p);
     b.total = b.C + P.nC;
     b.known = true;
@@ -179,8 +194,10 @@ __device__ __forceinline__ void complete_bases_from_ctl(const MK_C Params &P, Ba
 }
 
 // Decode a GroupGEMM task index: returns 1 for gate/up, 2 for down, 0 for a padding
-// position; sets the f range s and the linear tile j inside its block.
-__device__ __forceinline__ int decode_gemm(const Bases &b, int S, bool xcd_map, int g, int &s, int &j) {
+// position; sets the f range s and the linear tile j inside its block.  xcd_map: the blocks
+// are dealt to the XCDs by whole row tiles (xcd_blocks); Q: gate/up tiles per row tile and f
+// range (a down-projection row tile has b.N2).
+__device__ __forceinline__ int decode_gemm(const Bases &b, int S, bool xcd_map, int g, int &s, int &j, int Q) {
     int o = g - b.M1p, kind = 0, cnt = 0, size = 0;
     if (o < b.q1p) {
         s = 0;
@@ -208,7 +225,15 @@ __device__ __forceinline__ int decode_gemm(const Bases &b, int S, bool xcd_map, 
     }
     cnt = kind == 1 ? b.q1 : b.q2;
     size = kind == 1 ? b.q1p : b.q2p;
-    j = xcd_map ? (o & 7) * (size >> 3) + (o >> 3) : o;
+    (void)size;
+    if (xcd_map) {  // position o runs on XCD o % 8: the (o / 8)-th tile of that XCD's row tiles
+        const int per = kind == 1 ? Q : b.N2, x = o & 7;
+        const int r0 = (b.mt * x) >> 3, r1 = (b.mt * (x + 1)) >> 3;
+        const int i = o >> 3;
+        j = r0 * per + i;
+        return i < (r1 - r0) * per ? kind : 0;
+    }
+    j = o;
     return j < cnt ? kind : 0;
 }
 
@@ -2497,7 +2522,7 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
     if (g < bs.C) {
         int sp, j;
         // static schedule with wide row tiles: each XCD takes a contiguous eighth of a block
-        const int kind = decode_gemm(bs, P.S, !dyn && bs.wide, g, sp, j);
+        const int kind = decode_gemm(bs, P.S, xcd_blocks(P, bs), g, sp, j, P.NB1 / P.S);
         if (kind == 0) return kTaskDone;  // padding position
         const int Q = P.NB1 / P.S;
         if (kind == 1) {  // ---------------------------------------------------- GEMM1

@@ -94,6 +94,14 @@ int main() {
                     const int64_t total = round8(M1) + t.S * (round8(q1) + round8(q2)) + c.nC;
                     CHECK(total <= records, "E=%d k=%d B=%lld cap=%lld: %lld tasks > %lld trace records", s.E, s.k,
                           (long long)B, (long long)cap, (long long)total, (long long)records);
+                    // static schedule with wide row tiles: XCD lists of whole row tiles, each
+                    // padded to ceil(mt / 8) row tiles (at most as many row tiles as narrow)
+                    if (t.wide_ok) {
+                        const int64_t per = (mt + 7) / 8;
+                        const int64_t tw = round8(M1) + 8 * per * (t.NB1 / t.S) + 8 * per * t.NB2w + c.nC;
+                        CHECK(tw <= records, "E=%d k=%d B=%lld cap=%lld: %lld wide-layout tasks > %lld trace records",
+                              s.E, s.k, (long long)B, (long long)cap, (long long)tw, (long long)records);
+                    }
                     // dynamic queue: every pushed task (top-k, grouping, both GEMMs, combine) has a slot
                     const int64_t pushed = 2 * c.T + 1 + t.S * (q1 + q2) + c.nC;
                     CHECK(pushed <= cc.q_cap, "E=%d k=%d B=%lld cap=%lld: %lld pushes > q_cap %lld", s.E, s.k,

@@ -167,6 +167,10 @@ struct Sim {
         bn2 = wide ? 256 : 128;
         Q = c.NB1 / c.S;
         q1 = mt * Q, q2 = mt * N2, q1p = round8(q1), q2p = round8(q2);
+        if (!c.dynamic && wide) {  // static, wide: XCD lists of whole row tiles, padded alike
+            const int per = (mt + 7) / 8;
+            q1p = 8 * per * Q, q2p = 8 * per * N2;
+        }
         Cb = M1p + c.S * (q1p + q2p);
         nch = cdiv(c.d, kChunk);
         nC = cdiv(c.B, c.CT) * nch;
@@ -208,8 +212,13 @@ struct Sim {
             }
             if (kind == 0) s = c.S - 1, kind = 2;
         }
-        const int cnt = kind == 1 ? q1 : q2, size = kind == 1 ? q1p : q2p;
-        j = xcd_map ? (o & 7) * (size >> 3) + (o >> 3) : o;
+        const int cnt = kind == 1 ? q1 : q2;
+        if (xcd_map) {  // XCD o % 8 takes row tiles [mt x / 8, mt (x+1) / 8)
+            const int per = kind == 1 ? Q : N2, x = o & 7, r0 = mt * x / 8, r1 = mt * (x + 1) / 8, i = o >> 3;
+            j = r0 * per + i;
+            return i < (r1 - r0) * per ? kind : 0;
+        }
+        j = o;
         return j < cnt ? kind : 0;
     }
     void route_coords(int g, int &tg, int &eb) const {
