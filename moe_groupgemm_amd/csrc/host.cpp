@@ -204,7 +204,6 @@ mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const
     P.topk_idx = (int *)(base + L.topk_idx);
     P.topk_w = (float *)(base + L.topk_w);
     P.tile_hist = (int *)(base + L.tile_hist);
-    P.tile_off = (int *)(base + L.tile_off);
     P.hist = (int *)(base + L.hist);
     P.indptr = (int *)(base + L.indptr);
     P.mt_base = (int *)(base + L.mt_base);

@@ -73,12 +73,12 @@ constexpr int kScanStage = 16384;  // ints of tile_hist staged per round
 struct ScanSmem {
     int part[8];
     int ps[kThreads];      // partial sums, [thread group r][expert]
-    int carry[kMaxE];      // rows of each expert in the tiles of earlier rounds (row offsets)
     int tiles[kScanStage];
 };
 struct GroupSmem {
     unsigned long long mask[kMaxE];
-    int toff[kMaxE];  // the tile's row offsets tile_off[t, e]
+    int toff[kMaxE];  // the tile's row offsets: exp_indptr[e] + rows of e in earlier tiles
+    int ps[kThreads];  // partial sums of the earlier tiles' rows, [thread group r][expert]
     int eoff[kMaxE], emt[kMaxE], erows[kMaxE];  // per expert: exp_indptr, first row tile, rows per row tile
     int poff[kMaxE], pm0[kMaxE], pnm[kMaxE];  // per expert: queue offset, first row tile, row tiles
     int part[kWaves];
@@ -1046,15 +1046,15 @@ __device__ __forceinline__ void publish_row_tiles(const MK_C Params &P, int e, i
     }
 }
 
-// hist[e] = sum_t tile_hist[t,e]; exp_indptr = exclusive prefix sum; tile_off[t,e] =
-// exp_indptr[e] + rows of e in tiles before t; each expert's row tiles (expert_tiles);
-// arms ev_h[mt,s] with the gate/up tiles of each (row tile, f range), ev_y with the number
-// of down-projection tiles and ev_exp[e] with hist[e] ("Core method": the prefix sum
-// decides how many GroupGEMM tiles each expert triggers).  Events are at rest (zero) and
-// nothing decrements them before the scan is published, so arming is a plain store.
-// Returns the number of row tiles and (mw) of wide ones.
-// ph (optional): receives the times the histogram scans and the row-tile publication ended
-// (trace records).
+// hist[e] = sum_t tile_hist[t,e]; exp_indptr = exclusive prefix sum; each expert's row tiles
+// (expert_tiles); arms ev_h[mt,s] with the gate/up tiles of each (row tile, f range), ev_d
+// with the down-projection tiles of each (row tile, column chunk) and ev_exp[e] with
+// hist[e] ("Core method": the prefix sum decides how many GroupGEMM tiles each expert
+// triggers).  Events are at rest (zero) and nothing decrements them before the scan is
+// published, so arming is a plain store.  (Each grouping task sums the earlier tiles' rows
+// of every expert itself, so no per-tile offsets are published here.)  Returns the number of
+// row tiles and (mw) of wide ones; ph (optional) receives the times the histogram scans and
+// the publication ended (trace records).
 __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &mw_out,
                                                    unsigned long long *ph = nullptr) {
     const MK_C Params &P = uni_params(Pa);
@@ -1063,38 +1063,30 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &m
     const int E = P.E;
     int *tb = ss.tiles;
     const int rows = kScanStage / E;  // tile_hist rows staged per round (coalesced loads)
-    // R threads per expert: thread (ex, r) = (tid % E, tid / E) takes the r-th contiguous
-    // chunk of each round's tiles, so the per-expert sums and the row offsets run R-wide
+    // R threads per expert: thread (ex, r) = (tid % E, tid / E) sums the r-th contiguous
+    // chunk of each round's tiles
     const int R = kThreads / E;
     const int ex = threadIdx.x % E, r = threadIdx.x / E;
     const bool act = r < R;
-    auto chunk_sum = [&](int nr) {
-        const int c = (nr + R - 1) / R;
-        int v = 0;
-        if (act)
-            for (int t = r * c; t < min(nr, (r + 1) * c); ++t) v += tb[t * E + ex];
-        return v;
-    };
-    // stage rows [t0, t0 + nr) of tile_hist, eight loads of each thread in flight at once
-    auto stage = [&](int t0, int nr) {
-        const MK_G int *src = P.tile_hist + (size_t)t0 * E;
-        const int n = nr * E;
-        __syncthreads();
-        for (int i0 = threadIdx.x; i0 < n; i0 += 8 * kThreads) {
-            int v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = i0 + u * kThreads < n ? src[i0 + u * kThreads] : 0;
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (i0 + u * kThreads < n) tb[i0 + u * kThreads] = v[u];
-        }
-        __syncthreads();
-    };
     int hp = 0;
     for (int t0 = 0; t0 < P.T; t0 += rows) {
         const int nr = min(rows, P.T - t0);
-        stage(t0, nr);
-        hp += chunk_sum(nr);
+        // stage rows [t0, t0 + nr) of tile_hist, sixteen loads of each thread in flight at once
+        const MK_G int *src = P.tile_hist + (size_t)t0 * E;
+        const int n = nr * E;
+        __syncthreads();
+        for (int i0 = threadIdx.x; i0 < n; i0 += 16 * kThreads) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = i0 + u * kThreads < n ? src[i0 + u * kThreads] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (i0 + u * kThreads < n) tb[i0 + u * kThreads] = v[u];
+        }
+        __syncthreads();
+        const int c = (nr + R - 1) / R;
+        if (act)
+            for (int t = r * c; t < min(nr, (r + 1) * c); ++t) hp += tb[t * E + ex];
     }
     ss.ps[threadIdx.x] = hp;
     __syncthreads();
@@ -1108,7 +1100,6 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &m
     block_excl_scan(et.nw, ss.part, &total_w);
     if (ph) ph[0] = now_ticks();
     if (e < E) {
-        ss.carry[e] = off;
         pub(P.hist + e, h);
         pub(P.indptr + e, off);
         pub(P.mt_base + e, mbase);
@@ -1128,35 +1119,14 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &m
         for (int t = threadIdx.x; t < P.T; t += kThreads) pub(P.ev_logit + t, 1);
     mw_out = total_w;
     if (ph) ph[1] = now_ticks();
-    // per-tile row offsets: exp_indptr[e] + rows of e in earlier tiles; a thread's chunk
-    // starts after the chunks of lower r and the tiles of earlier rounds
-    for (int t0 = 0; t0 < P.T; t0 += rows) {
-        const int nr = min(rows, P.T - t0);
-        if (t0 > 0 || P.T > rows) stage(t0, nr);  // the first round's rows are still staged unless T needed several
-        else __syncthreads();                      // ps and carry written above
-        const int cs = chunk_sum(nr);
-        ss.ps[threadIdx.x] = cs;
-        __syncthreads();
-        if (act) {
-            int run = ss.carry[ex];
-            for (int q = 0; q < r; ++q) run += ss.ps[q * E + ex];
-            const int c = (nr + R - 1) / R;
-            for (int t = r * c; t < min(nr, (r + 1) * c); ++t) {
-                pub(P.tile_off + (size_t)(t0 + t) * E + ex, run);
-                run += tb[t * E + ex];
-            }
-        }
-        __syncthreads();
-        if (e < E)
-            for (int q = 0; q < R; ++q) ss.carry[e] += ss.ps[q * E + e];
-    }
     return total_mt;
 }
 
 // ------------------------------------------------------------------------------ GROUP
 // Stable grouping of one 64-token tile: the rank of (b, i) among the tile's rows of expert
 // e is the number of earlier tokens of the tile routed to e (a token uses an expert at
-// most once), read off a 64-bit token mask per expert.  Row p = tile_off[t,e] + rank;
+// most once), read off a 64-bit token mask per expert.  Row p = toff[e] + rank, where toff[e] =
+// exp_indptr[e] + the rows of e in earlier tiles (summed here from tile_hist);
 // perm[p] = b*k+i and inv[b*k+i] = p.  The rows themselves are not copied: the gate/up
 // GroupGEMM reads each grouped row of x through perm.
 __device__ __attribute__((noinline)) void task_group(const MK_C Params &Pa, int t) {
@@ -1175,8 +1145,22 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &Pa, int 
         const int i = w + j * kWaves;
         ev[j] = i < k && lane < ntok ? P.topk_idx[(size_t)b * k + i] : -1;
     }
+    // rows of each expert in the tiles before this one: thread (ex, r) sums the r-th chunk of
+    // tiles [0, t) of tile_hist (R threads per expert), eight loads in flight at a time
+    {
+        const int R = kThreads / E, ex = threadIdx.x % E, r = threadIdx.x / E;
+        const int c = (t + R - 1) / R, ta = min(t, r * c), tz = r < R ? min(t, (r + 1) * c) : ta;
+        int sum = 0;
+        for (int t0 = ta; t0 < tz; t0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = t0 + u < tz ? P.tile_hist[(size_t)(t0 + u) * E + ex] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
+        g.ps[threadIdx.x] = sum;
+    }
     for (int i = threadIdx.x; i < E; i += kThreads) {
-        g.toff[i] = P.tile_off[(size_t)t * E + i];
         g.eoff[i] = P.indptr[i];
         g.emt[i] = P.mt_base[i];
         const int h = P.hist[i];
@@ -1184,6 +1168,11 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &Pa, int 
         g.mask[i] = 0ull;
     }
     __syncthreads();
+    for (int i = threadIdx.x; i < E; i += kThreads) {
+        int o = g.eoff[i];
+        for (int q = 0; q < kThreads / E; ++q) o += g.ps[q * E + i];
+        g.toff[i] = o;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
         if (ev[j] >= 0) atomicOr(&g.mask[ev[j]], 1ull << lane);
@@ -2296,7 +2285,6 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
         W.mask[e] = 0ull;
         pub(P.hist + e, h);
         pub(P.indptr + e, off);
-        pub(P.tile_off + e, off);
         pub(P.mt_base + e, mbase);
         for (int m = 0; m < mt; ++m) {
             const int i = mbase + m;

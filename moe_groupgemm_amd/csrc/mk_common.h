@@ -234,7 +234,7 @@ inline Counts make_counts(const Shape &s, int64_t B) {
 
 // Byte offsets of every workspace array, for a workspace sized for B = cap tokens.
 struct Layout {
-    size_t ctl, ev_logit, ev_exp, ev_h, ev_d, logits, topk_idx, topk_w, tile_hist, tile_off, hist, indptr,
+    size_t ctl, ev_logit, ev_exp, ev_h, ev_d, logits, topk_idx, topk_w, tile_hist, hist, indptr,
         mt_base, mt_expert, mt_row0, mt_rows, perm, inv, amt, h, y, yp, red_ctr, qslots, trace, total;
     int64_t cap;
 };
@@ -261,7 +261,6 @@ inline Layout make_layout(const Shape &s, int64_t cap) {
     L.topk_idx = take((size_t)A * 4);
     L.topk_w = take((size_t)A * 4);
     L.tile_hist = take((size_t)c.T * s.E * 4);
-    L.tile_off = take((size_t)c.T * s.E * 4);
     L.hist = take((size_t)s.E * 4);
     L.indptr = take((size_t)(s.E + 1) * 4);
     L.mt_base = take((size_t)(s.E + 1) * 4);
@@ -311,7 +310,7 @@ struct Params {
     MK_G float *logits;
     MK_G int *topk_idx;
     MK_G float *topk_w;
-    MK_G int *tile_hist, *tile_off, *hist, *indptr, *mt_base, *mt_expert, *mt_row0, *mt_rows, *perm, *inv;
+    MK_G int *tile_hist, *hist, *indptr, *mt_base, *mt_expert, *mt_row0, *mt_rows, *perm, *inv;
     MK_G int *amt;  // row tile of each assignment b*k+i (written by the grouping)
     MK_G uint16_t *h;
     MK_G uint16_t *y;   // down-projection output, bf16 [B*k, d] in grouped row order

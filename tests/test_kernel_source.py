@@ -16,7 +16,7 @@ SRC = os.path.join(HERE, "..", "moe_groupgemm_amd", "csrc", "megakernel.hip")
 
 # Workspace arrays read by tasks other than their writer (out is read only after the kernel
 # ends, trace only by the host, so both may be written with plain stores).
-PUBLISHED = ("h", "y", "yp", "perm", "inv", "amt", "logits", "topk_idx", "topk_w", "tile_hist", "tile_off",
+PUBLISHED = ("h", "y", "yp", "perm", "inv", "amt", "logits", "topk_idx", "topk_w", "tile_hist",
              "hist", "indptr", "mt_base", "mt_expert", "mt_row0", "mt_rows", "qslots", "ev_logit", "ev_exp",
              "ev_h", "ev_d", "red_ctr", "ctl")
 
