@@ -362,11 +362,13 @@ def time_cold(layer, tx, out, stream, reps, flush, dev):
     return ms
 
 
-def roofline(cfg_name, B, sched, alg_bytes, flops, kern_ms):
-    """Roofline of the launch: MFMA for prefill-sized batches (B >= 2048), else HBM."""
+def roofline(cfg_name, B, sched, alg_bytes, flops, kern_ms, policy="by_rows"):
+    """Roofline of the launch: MFMA for prefill-sized batches (B >= 2048), else HBM.  The
+    counter traffic comes from the profiles of the library's own tile choice ('by_rows'), so
+    it is null for the comparison policies."""
     gbs = alg_bytes / (kern_ms / 1e3) / 1e9
     tflops = flops / (kern_ms / 1e3) / 1e12
-    traffic = measured_traffic(cfg_name, B, sched)
+    traffic = measured_traffic(cfg_name, B, sched) if policy == "by_rows" else None
     if B >= 2048:
         return {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic}
@@ -418,7 +420,7 @@ def measure_workload(cfg_name, sched_name, steps, warmup, dev, batches=None, col
              "row_tiles": int(ctl[mk.CTL["mt_total"]]), "wide_row_tiles": int(ctl[mk.CTL["mw"]]),
              "active_experts": active,
              "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(ms)), "tokens_per_s": B / (kern_ms / 1e3),
-             "roofline": roofline(cfg_name, B, sched_name, alg_bytes, flops, kern_ms),
+             "roofline": roofline(cfg_name, B, sched_name, alg_bytes, flops, kern_ms, policy),
              "hbm_frac": alg_bytes / (kern_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
              "mfma_frac": flops / (kern_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
              "algorithmic_bytes": alg_bytes, "gemm_flops": flops}
