@@ -2515,12 +2515,14 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         const int Q = P.NB1 / P.S;
         if (kind == 1) {  // ---------------------------------------------------- GEMM1
             const int mt = j / Q, n = sp * Q + (j - (j / Q) * Q);
-            const int e = uni(P.mt_expert[mt]);
+            // the row tile's table entries are read together (one round trip)
+            const int e_ = P.mt_expert[mt], r0_ = P.mt_row0[mt], nr_ = P.mt_rows[mt];
+            const int e = uni(e_);
             // (a batch of one routing tile was grouped before the layout was published, and its
             // experts' events stay at rest, unless the debug flag holds one back)
             if (!dyn && (P.T > 1 || (P.debug & 1)) && !wg_wait_zero(P, P.ev_exp + e)) return 0;
             const unsigned long long t1 = now_ticks();
-            task_gemm1<WIDE>(P, e, uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), n);
+            task_gemm1<WIDE>(P, e, uni(r0_), uni(nr_), n);
             const unsigned long long t2 = now_ticks();
             count_task(P, K_GEMM1);
             // f range sp of this row tile complete: its down-projection tiles are ready; once
@@ -2535,9 +2537,12 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         }
         // --------------------------------------------------------------------- GEMM2
         const int mt = j / bs.N2, n = j - mt * bs.N2;
+        // the row tile's table entries (published with the scan result this workgroup has
+        // acquired) are read before the wait, so the two round trips overlap
+        const int e_ = P.mt_expert[mt], r0_ = P.mt_row0[mt], nr_ = P.mt_rows[mt];
         if (!dyn && !wg_wait_zero(P, P.ev_h + mt * P.S + sp)) return 0;
         const unsigned long long t1 = now_ticks();
-        const bool done = task_gemm2<WIDE>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), n, sp, mt);
+        const bool done = task_gemm2<WIDE>(P, uni(e_), uni(r0_), uni(nr_), n, sp, mt);
         const unsigned long long t2 = now_ticks();
         count_task(P, K_GEMM2);
         // y tile (mt, n) written: one fewer tile of its combine chunk
