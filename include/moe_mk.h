@@ -56,8 +56,9 @@ typedef struct moe_mk_plan_s *moe_mk_plan_t;
  * that fires pushes its consumer tasks onto a shared queue with an atomic, idle SMs pop).
  */
 typedef enum {
-    MOE_MK_SCHED_STATIC = 0,  /* persistent workgroups take tasks from fixed per-XCD lists (then, with narrow tiles, what
-                                 the other XCDs' lists have left) and spin-wait on events; relies on the whole grid
+    MOE_MK_SCHED_STATIC = 0,  /* persistent workgroups take tasks from fixed per-XCD lists (then what the other XCDs'
+                                 lists have left: any GroupGEMM position, or with wide row tiles down-projection
+                                 positions only) and spin-wait on events; relies on the whole grid
                                  (one workgroup per CU) being resident at once, as on a GPU not shared with other
                                  kernels: a workgroup held back by another stream's kernel delays the forward until
                                  it is scheduled, and a wait longer than the watchdog (2 s) ends the forward with
@@ -257,8 +258,8 @@ moe_mk_status_t moe_mk_workspace_error(moe_mk_plan_t plan, const void *ws, size_
  * Plan facts (host).  Keys: "E" "k" "d" "f" "sched" "grid" "cus" "wg_per_cu" "BM" "BN1"
  * "BN2" "BK" "wide_BM" "wide_BN1" "wide_BN2" "wide_BK" "wide_min_rows" "route_experts"
  * "threads".  Narrow GroupGEMM tiles are BM rows x BN1 gate/up (BN2 down) columns (half as
- * many in the forwards forward_info("BN") names) with K
- * steps of BK; wide ones wide_BM rows x wide_BN1 gate/up (wide_BN2 down) columns with K
+ * many in the forwards where forward_info("BN") says so) with K steps of BK; wide ones
+ * wide_BM rows x wide_BN1 gate/up (wide_BN2 down) columns with K
  * steps of wide_BK, taken by experts with at least wide_min_rows rows.  Returns -1 for an
  * unknown key or invalid plan.
  * Source: none on the pages (plan bookkeeping).

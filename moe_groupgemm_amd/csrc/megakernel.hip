@@ -15,23 +15,26 @@
 //              ("data-dependent task triggering"), and idle workgroups pop from it.
 // The batch size B is a kernel argument: every count after the routing stage (histogram,
 // exp_indptr, tiles per expert) is derived on the device, so one compiled kernel serves
-// every B (section "Core method", symbolic shapes).  The kernel is compiled twice, once
-// per GroupGEMM tile shape (narrow tiles, or wide tiles when experts average 128 rows or
-// more), and the host launches the one the forward's shape needs: the wide tiles use
-// nearly every register and are inlined into their instantiation (called out of line,
-// each tile saved and restored about 60 registers per wave through memory), and the
-// narrow instantiation carries none of their code or register pressure (the wide one
-// calls the out-of-line narrow tiles for row tiles of a few rows).  Either serves every B
-// of its shape without recompiling.
+// every B and every routing (section "Core method", symbolic shapes).  The scan chooses
+// each expert's GroupGEMM tile shape from its row count (64-row narrow tiles, or 256-row
+// wide tiles above 64 rows).  The task loop exists twice in the kernel: the wide tiles use
+// nearly every register and are inlined into the copy that runs forwards with wide row
+// tiles (called out of line, each tile saved and restored about 60 registers per wave
+// through memory), and the other copy, which runs every task until a forward is known to
+// have them, carries none of their code or register pressure (the narrow tiles are
+// out-of-line functions that both copies call).
 //
 // Task kinds and their events:
 //   ROUTE(tg,eb)  fp32 router logits, 8*tpw tokens x reb experts   -> ev_logit[tile]
 //   TOPK(t)       top-k + softmax + tile histogram, 64 tokens    -> ev_topk
-//   SCAN          hist, exp_indptr, per-tile offsets, row tiles; arms ev_exp/ev_h/ev_y -> ev_scan
-//   GROUP(t)      stable ranks -> perm/inv (GEMM1 gathers the rows) -> ev_exp[e] -= rows of e
+//   SCAN          hist, exp_indptr, row tiles and their shapes; arms ev_exp/ev_h/ev_d and
+//                 re-arms ev_logit as the tiles' grouping events -> ev_scan, scan result word
+//   GROUP(t)      stable ranks -> perm/inv/amt (GEMM1 gathers the rows) -> ev_exp[e] -= rows
+//                 of e, ev_logit[t]
 //   GEMM1(mt,n)   gate/up GroupGEMM tile + SwiGLU -> h            -> ev_h[mt,s] (s: n's f range)
-//   GEMM2(mt,s,n) down GroupGEMM tile over f range s -> y[s]      -> ev_y
-//   COMBINE(c)    out[b] = sum_i w[b,i] y[inv[b,i]] for 1, 4 or 8 tokens
+//   GEMM2(mt,s,n) down GroupGEMM tile over f range s -> y         -> ev_d[mt, column chunk]
+//   COMBINE(c)    out[b] = sum_i w[b,i] y[inv[b,i]] for 1, 4 or 8 tokens and 2048 columns,
+//                 after its tokens' grouping and the row tiles its rows use
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -2069,7 +2072,7 @@ __device__ __forceinline__ bool combine_tile(const MK_C Params &P, int c, unsign
     const int nb = min(CT, P.B - b_lo);
     const int k = P.k;
     // the grouping of the tokens' routing tile is done (a batch of one routing tile is grouped
-    // before the scan event that every combine task comes after)
+    // before the scan result that every combine task comes after)
     if (!P.unfused && P.T > 1 && !wg_wait_zero(P, P.ev_logit + b_lo / kTileTokens)) return false;
     bool ok = true;
     for (int i = threadIdx.x; i < nb * k; i += kThreads) {
