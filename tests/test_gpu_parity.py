@@ -655,3 +655,33 @@ def test_graph_replays_match_eager(path):
     assert layer.error() == 0
     del g
     layer.close()
+
+
+def _random_shapes(n, seed):
+    """Seeded layer shapes within what the plan accepts, sized so that the oracle finishes
+    each in about a second (B*k*d*f below 2e9): every tile shape and both task loops are met
+    (one and several routing tiles, half-width, narrow and wide row tiles, splits)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = int(rng.choice([4, 8, 12, 16, 32, 64]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        d = int(rng.choice([256, 512, 1024, 2048]))
+        f = int(rng.choice([128, 256, 384, 512, 768, 1024, 4096]))
+        B = int(rng.choice([1, 2, 5, 17, 64, 65, 130, 257, 700, 1500, 3000]))
+        zipf = float(rng.choice([0.0, 1.2]))
+        if B * k * d * f > 2e9:
+            continue
+        out.append((B, d, f, E, k, zipf))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(10, 2024), ids=lambda s: "B%d_d%d_f%d_E%d_k%d_z%g" % s)
+def test_random_shapes(shape):
+    # Every token against the oracle on both schedules, the two bitwise equal, and the row
+    # tiles against the histogram.
+    B, d, f, E, k, zipf = shape
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=3000 + B + E, zipf_s=zipf or None)
+    outs = [full_check(x, Wr, bias, W1, W3, W2, k, sched, f"random B={B} d={d} f={f} E={E} k={k} {SNAME[sched]}")[0]
+            for sched in SCHEDS]
+    assert np.array_equal(outs[0], outs[1])
