@@ -1564,8 +1564,11 @@ __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0
 // kWideBN = 256 columns (a wave: 128 x 64); 128 accumulator registers either way.  Per K
 // step a wave reads 8 A fragments and 8 B fragment halves and issues 32 MFMAs in two groups
 // of 16 (rows 0-63, rows 64-127 of its block); the workgroup stages 32 KB per 4.2 MFLOP.
-//   A tile in LDS: [row][k], 64-byte rows; 16-byte chunk c of row r sits at c ^ wswa(r),
-//     so the 16 rows one A fragment read touches fall on 16 distinct 16-byte bank groups.
+//   A tile in LDS: [row][k], 64-byte rows; 16-byte chunk c of row r sits at c ^ wswa(r).
+//     Measured with the LDS bank-conflict counter on MI355X: rows r and r+4 of a fragment
+//     read have to differ in the 32-byte half of their chunk; a swizzle of bits 2 and 3 of
+//     the row that flips both chunk bits between them reads conflict-free, where XORing
+//     (r >> 2) & 3 alone spent half the read cycles in conflicts.
 //   B tile in LDS: [k][n], 256- or 512-byte rows as in memory; chunk c of row k sits at
 //     c ^ wswb(k), so the rows one ds_read_b64_tr_b16 touches spread over distinct bank
 //     groups (the bank pattern repeats every 256 bytes).
@@ -1574,7 +1577,7 @@ __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0
 constexpr int kWBK = kWideBK;
 constexpr int kWR = kWideBM / 2;  // rows per wave row
 constexpr int kWRB = kWR / 16;    // 16-row blocks per wave row (two groups of four)
-__device__ __forceinline__ int wswa(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int wswa(int r) { return ((r >> 2) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 1); }
 
 template <bool DUAL, int BN>
 struct WideCfg {
