@@ -1208,7 +1208,8 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &Pa, int 
 //     MFMA B fragment (8 consecutive k of column j) = two ds_read_b64_tr_b16: within each
 //     16-lane group, lane l addresses row (k0 + l/4), columns (n0 + 4*(l%4) .. +3) and
 //     receives the 4 rows' values of column n0 + l.
-// The swizzles make both fragment reads conflict-free.  Wave w owns output columns
+// The swizzles make both fragment reads conflict-free (checked with the LDS bank-conflict
+// counter on probes of these address patterns).  Wave w owns output columns
 // [16w, 16w+16); 16-row blocks beyond the tile's rows are skipped, and rows of a partial
 // block past the tile's rows are never loaded (their outputs are discarded).
 // Half-width tiles (BN = kHalfBN = 64 columns, the smallest batches): the B tile rows are 128
@@ -1221,7 +1222,12 @@ __device__ __attribute__((noinline)) void task_group(const MK_C Params &Pa, int 
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int swa(int r) { return (r ^ (r >> 3)) & 7; }
+// Chosen by timing every chunk swizzle that is a linear (XOR) function of row bits 0..4 and
+// checking the winner with the LDS bank-conflict counter: zero conflict cycles, where
+// (r ^ (r >> 3)) & 7 spent half the read cycles in conflicts on MI355X.
+__device__ __forceinline__ int swa(int r) {
+    return ((r >> 1) & 1) | ((((r >> 1) ^ (r >> 2) ^ (r >> 4)) & 1) << 1) | (((r >> 2) & 1) << 2);
+}
 __device__ __forceinline__ int wswb(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
 __device__ __forceinline__ int hswb(int k) { return (((k >> 1) & 1) | (((k >> 3) & 1) << 1)) << 1; }
 
