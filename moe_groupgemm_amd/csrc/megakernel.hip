@@ -1772,7 +1772,9 @@ __device__ __forceinline__ void wide_mfma(int lo, int hi, const u32x4 (&a)[4], c
 // one wave's stall overlaps the other's MFMAs.
 // NRB = 16-row blocks of the wave that hold rows, rounded up to even (a compile-time count,
 // so no branches surround the MFMAs); every variant issues the same loads and barriers.
-template <bool DUAL, int BN, int NRB, bool LATE>
+// TAIL: 0 for the stages that issue loads (st + NS - 1 < nk), 1 for the later ones but the
+// last, 2 for the last; the three variants are separate loops, so no stage branches on them.
+template <bool DUAL, int BN, int NRB, bool LATE, int TAIL>
 __device__ __forceinline__ void wide_stage(int st, int nk, const WideArgs &ga, const WideFragOff<DUAL, BN> &fo,
                                            uint32_t ring, uint16_t *ring_p, u32x4 (&a0)[4], u32x2 (&b)[8],
                                            u32x4 (&a1)[4],
@@ -1783,7 +1785,7 @@ __device__ __forceinline__ void wide_stage(int st, int nk, const WideArgs &ga, c
     const uint32_t sb = ring + (uint32_t)((st % NS) * C::STAGE_BYTES);
     const int ld = st + NS - 1;  // the stage whose loads this one issues
     uint16_t *ld_p = ring_p + ((st + NS - 1) % NS) * C::STAGE_ELEMS;
-    const bool lds = ld < nk;
+    constexpr bool lds = TAIL == 0;
     if constexpr (NRB > 4) wfrag_read_a<4096>(sb + fo.a, a1);
     if constexpr (LATE) {
         if (lds) wstage_load<DUAL, BN, 1>(ga, ld * kWBK, ld_p);
@@ -1805,9 +1807,9 @@ __device__ __forceinline__ void wide_stage(int st, int nk, const WideArgs &ga, c
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NRB > 4) wfrag_wait(a1);
-    const bool more = st + 1 < nk;
+    constexpr bool more = TAIL < 2;
     if (more) {
-        if (lds)
+        if constexpr (lds)
             wait_vm<(NS - 3) * C::LOADS + 2>();  // after stage st+1: stages st+2 .. st+NS-2, two of st+NS-1
         else
             wait_vm<0>();
@@ -1860,8 +1862,12 @@ __device__ __forceinline__ void wide_loop(const WideArgs &ga, int nk, f32x4 (&ac
         wfrag_read_a<0>(ring + fo.a, a0);
         wfrag_read_b_wait<DUAL, BN>(ring, fo, b, a0);
     }
-    for (int st = 0; st < nk; ++st)
-        wide_stage<DUAL, BN, NRB, LATE>(st, nk, ga, fo, ring, s.ring, a0, b, a1, acc0, acc1);
+    int st = 0;
+    for (; st < nk - (NS - 1); ++st)
+        wide_stage<DUAL, BN, NRB, LATE, 0>(st, nk, ga, fo, ring, s.ring, a0, b, a1, acc0, acc1);
+    for (; st < nk - 1; ++st)
+        wide_stage<DUAL, BN, NRB, LATE, 1>(st, nk, ga, fo, ring, s.ring, a0, b, a1, acc0, acc1);
+    if (st < nk) wide_stage<DUAL, BN, NRB, LATE, 2>(st, nk, ga, fo, ring, s.ring, a0, b, a1, acc0, acc1);
     wait_vm<0>();
     __syncthreads();
 }
