@@ -326,6 +326,21 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
+// Wait until at most n stages of L loads each are outstanding (n clamped to 0 .. MAXN; the
+// count of s_waitcnt is an immediate, so this picks one of MAXN + 1 waits).
+template <int L, int MAXN>
+__device__ __forceinline__ void wait_vm_stages(int n) {
+    if constexpr (MAXN > 0) {
+        if (n >= MAXN) {
+            wait_vm<MAXN * L>();
+            return;
+        }
+        wait_vm_stages<L, MAXN - 1>(n);
+    } else {
+        wait_vm<0>();
+    }
+}
+
 // Workgroup barrier without the memory-model fences of __syncthreads (which would wait
 // for every LDS-DMA load in flight); the empty asm statements keep the compiler from
 // moving memory operations across it.
@@ -1398,20 +1413,42 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], 
     for (int p = 0; p < NS - 1; ++p)
         if (p < nk) stage_load<DUAL, AR, BN>(ga, p * kBK, s.ring + p * C::STAGE_ELEMS);
     int slot = 0;  // ring slot of stage st
-    for (int st = 0; st < nk; ++st) {
-        // stage st has landed once at most NS - 2 newer stages are outstanding
-        if (st + NS - 2 < nk)
-            wait_vm<(NS - 2) * C::LOADS>();
-        else
-            wait_vm<0>();
-        bare_barrier();  // every wave's part of stage st is in LDS; the slot of st-1 is free
-        const int nxt = st + NS - 1;
-        if (nxt < nk) {
+    if constexpr (AR == 16) {
+        // Small tiles (decode batch sizes): the stages that issue the loads of stage st + NS - 1,
+        // then the last NS - 1 stages, which issue none, as two loops, so no stage branches on
+        // whether it loads.  (For 64-row tiles the two copies of the stage body cost more
+        // registers than the called function keeps free, so they keep one loop.)
+        int st = 0;
+        for (; st < nk - (NS - 1); ++st) {
+            wait_vm<(NS - 2) * C::LOADS>();  // stage st has landed: at most NS - 2 newer stages outstanding
+            bare_barrier();  // every wave's part of stage st is in LDS; the slot of st-1 is free
             const int ns = slot == 0 ? NS - 1 : slot - 1;  // (st - 1) mod NS
-            stage_load<DUAL, AR, BN>(ga, nxt * kBK, s.ring + ns * C::STAGE_ELEMS);
+            stage_load<DUAL, AR, BN>(ga, (st + NS - 1) * kBK, s.ring + ns * C::STAGE_ELEMS);
+            stage_compute<DUAL, AR, BN>(s.ring + slot * C::STAGE_ELEMS, nrb, acc0, acc1);
+            slot = slot == NS - 1 ? 0 : slot + 1;
         }
-        stage_compute<DUAL, AR, BN>(s.ring + slot * C::STAGE_ELEMS, nrb, acc0, acc1);
-        slot = slot == NS - 1 ? 0 : slot + 1;
+        for (; st < nk; ++st) {
+            wait_vm_stages<C::LOADS, NS - 2>(nk - 1 - st);  // stage st has landed (nk-1-st newer ones may not have)
+            bare_barrier();
+            stage_compute<DUAL, AR, BN>(s.ring + slot * C::STAGE_ELEMS, nrb, acc0, acc1);
+            slot = slot == NS - 1 ? 0 : slot + 1;
+        }
+    } else {
+        for (int st = 0; st < nk; ++st) {
+            // stage st has landed once at most NS - 2 newer stages are outstanding
+            if (st + NS - 2 < nk)
+                wait_vm<(NS - 2) * C::LOADS>();
+            else
+                wait_vm<0>();
+            bare_barrier();  // every wave's part of stage st is in LDS; the slot of st-1 is free
+            const int nxt = st + NS - 1;
+            if (nxt < nk) {
+                const int ns = slot == 0 ? NS - 1 : slot - 1;  // (st - 1) mod NS
+                stage_load<DUAL, AR, BN>(ga, nxt * kBK, s.ring + ns * C::STAGE_ELEMS);
+            }
+            stage_compute<DUAL, AR, BN>(s.ring + slot * C::STAGE_ELEMS, nrb, acc0, acc1);
+            slot = slot == NS - 1 ? 0 : slot + 1;
+        }
     }
     wait_vm<0>();
     __syncthreads();  // the ring may be reused by the next task
