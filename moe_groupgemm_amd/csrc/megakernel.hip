@@ -1599,6 +1599,36 @@ __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0
     return true;
 }
 
+// Down-projection task of a narrow row tile in a forward with wide row tiles: y[rows, 256
+// columns from 256*n2] = h[rows, :] W2[e][:, those columns], run as one two-weight tile (the
+// column halves take the places of the gate and up weights), so the task streams 512-byte
+// W2 row segments through one K loop instead of two 128-column tiles one after the other.
+template <int AR>
+__device__ __forceinline__ void gemm2_pair_tile(const MK_C Params &P, int e, int row0, int nrows, int n2) {
+    static_assert(kWideBN == 2 * kBN, "a pair of narrow column blocks spans a wide down-projection task");
+    GemmArgs ga;
+    ga.arow[0] = P.h + (size_t)(row0 + a_row<AR>(nrows)) * P.f;
+    ga.nrows = nrows;
+    ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)n2 * kWideBN;
+    ga.B1 = ga.B0 + kBN;
+    ga.ldb = P.d;
+    ga.K = P.f;
+    f32x4 acc0[4], acc1[4];
+    gemm_tile<true, AR, kBN>(ga, acc0, acc1, g_sm.u.g);
+    const int lane = lane_id(), w = wave_id();
+    const int g = lane >> 4, j = lane & 15;
+    const int col = n2 * kWideBN + 16 * w + j;
+#pragma unroll
+    for (int rb = 0; rb < AR / 16; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * rb + 4 * g + r;
+            MK_G uint16_t *yr = P.y + (size_t)(row0 + row) * P.d;
+            store_bf16_pair(yr, col, acc0[rb][r], row < nrows);
+            store_bf16_pair(yr, col + kBN, acc1[rb][r], row < nrows);
+        }
+}
+
 // ------------------------------------------------------------------------------ wide tiles
 // At large batches (an expert averages kWideMinRows rows or more) a tile has kWideBM = 256
 // rows, K steps are 32 deep, and the eight waves split the tile 2 x 4: wave w owns rows
@@ -2068,10 +2098,17 @@ __device__ __attribute__((noinline)) bool narrow_gemm2(const MK_C Params &Pa, in
     return gemm2_tile<AR, BN>(P, uni(e), uni(row0), uni(nrows), uni(n), uni(sp), uni(mt));
 }
 
+template <int AR>
+__device__ __attribute__((noinline)) void narrow_gemm2_pair(const MK_C Params &Pa, int e, int row0, int nrows,
+                                                            int n2) {
+    const MK_C Params &P = uni_params(Pa);
+    gemm2_pair_tile<AR>(P, uni(e), uni(row0), uni(nrows), uni(n2));
+}
+
 // The tile code follows the row tile's rows: a row tile of more than kBM rows is a wide one
 // (see expert_tiles), narrow row tiles of at most 16 rows stage only 16 A rows.  In a forward
 // with wide row tiles a down-projection task spans kWideBN columns, which a narrow row tile
-// covers with kWideBN / kBN narrow tiles (no f splits then).
+// covers with one two-weight narrow tile over both column halves (no f splits then).
 // WIDE: the code may meet wide row tiles (the task loop of forwards that have them).
 template <bool WIDE>
 __device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
@@ -2092,13 +2129,11 @@ __device__ __forceinline__ bool task_gemm2(const MK_C Params &P, int e, int row0
         wide_gemm2(P, e, row0, nrows, n);
         return true;
     }
-    if (WIDE) {
-        for (int q = 0; q < kWideBN / kBN; ++q) {  // S = 1 with wide row tiles
-            if (nrows <= 16)
-                narrow_gemm2<16>(P, e, row0, nrows, (kWideBN / kBN) * n + q, 0, mt);
-            else
-                narrow_gemm2<64>(P, e, row0, nrows, (kWideBN / kBN) * n + q, 0, mt);
-        }
+    if (WIDE) {  // S = 1 with wide row tiles; both column halves in one tile
+        if (nrows <= 16)
+            narrow_gemm2_pair<16>(P, e, row0, nrows, n);
+        else
+            narrow_gemm2_pair<64>(P, e, row0, nrows, n);
         return true;
     }
     if (uni(P.BN) == kHalfBN)
