@@ -175,6 +175,7 @@ mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const
     P.NB1 = tl.NB1;
     P.NB2 = tl.NB2;
     P.NB2w = tl.NB2w;
+    P.DC = tl.DC;
     P.S = tl.S;
     P.wide_ok = tl.wide_ok;
     // experts with at least wide_min rows take wide row tiles (always more than one routing
@@ -391,6 +392,7 @@ int64_t moe_mk_forward_info(moe_mk_plan_t plan, int64_t B, const char *key) {
                {"NB1", t.NB1},
                {"NB2", t.NB2},
                {"NB2_wide", t.NB2w},
+               {"down_cols", t.DC},
                {"S", t.S},
                {"wide_ok", t.wide_ok}};
     for (auto &e : tab)

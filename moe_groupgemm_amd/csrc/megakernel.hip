@@ -1121,7 +1121,7 @@ __device__ __attribute__((noinline)) int task_scan(const MK_C Params &Pa, int &m
         pub(P.hist + e, h);
         pub(P.indptr + e, off);
         pub(P.mt_base + e, mbase);
-        publish_row_tiles(P, e, h, off, et, mbase, total_w > 0 ? kWideBN : P.BN);
+        publish_row_tiles(P, e, h, off, et, mbase, total_w > 0 ? kWideBN : P.DC);
         if (h && !P.unfused) pub(P.ev_exp + e, h);
     }
     if (e == 0) {
@@ -2129,7 +2129,7 @@ __device__ __forceinline__ bool task_gemm2(const MK_C Params &P, int e, int row0
         wide_gemm2(P, e, row0, nrows, n);
         return true;
     }
-    if (WIDE) {  // S = 1 with wide row tiles; both column halves in one tile
+    if (WIDE || uni(P.DC) == kWideBN) {  // S = 1: both column halves in one tile
         if (nrows <= 16)
             narrow_gemm2_pair<16>(P, e, row0, nrows, n);
         else
@@ -2381,7 +2381,7 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
             pub(P.mt_expert + i, e);
             pub(P.mt_row0 + i, off + m * BM);
             pub(P.mt_rows + i, min(BM, h - m * BM));
-            arm_row_tile(P, i, P.BN);
+            arm_row_tile(P, i, P.DC);
         }
     }
     if (e == 0) {
@@ -2636,7 +2636,7 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         const unsigned long long t2 = now_ticks();
         count_task(P, K_GEMM2);
         // y tile (mt, n) written: one fewer tile of its combine chunk
-        if (done) wg_notify(P, P.ev_d + mt * P.nch + n * (bs.wide ? kWideBN : P.BN) / kCombineCols, -1);
+        if (done) wg_notify(P, P.ev_d + mt * P.nch + n * (bs.wide ? kWideBN : P.DC) / kCombineCols, -1);
         trace_task(P, g, K_GEMM2, t0, t1, t2);
         return kTaskDone;
     }

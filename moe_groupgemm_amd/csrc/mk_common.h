@@ -120,6 +120,8 @@ inline int max_down_splits(const Shape &s) {
 // per expert on the device from its row count once the histogram is known (the scan task):
 //   narrow  kBM = 64 rows; gate/up tiles of kBN = 128 columns of each weight, down-projection
 //           tiles of kBN columns, the down projection optionally split over f (S ranges);
+//           when it is not split (S = 1), a down-projection tile takes two such column blocks
+//           (kWideBN columns, two weight blocks against one staged h tile);
 //   wide    kWideBM = 256 rows; gate/up tiles of kWideBN1 = 128 columns of each weight,
 //           down-projection tiles of kWideBN = 256 columns, so that each staged byte serves
 //           more multiply-adds.  An expert with wide row tiles puts a remainder of at most
@@ -152,8 +154,11 @@ inline bool half_width(const Shape &s, int64_t B) {
 struct Tiles {
     int BN;      // columns of a narrow tile: kBN, or kHalfBN (half_width)
     int NB1;     // gate/up tiles per row tile (f / BN; f / 128 for wide row tiles)
-    int NB2;     // down-projection tiles per narrow row tile and f range (d / BN)
+    int NB2;     // down-projection tiles per narrow row tile and f range (d / DC)
     int NB2w;    // down-projection tiles per wide row tile (d / 256)
+    int DC;      // columns of a down-projection task in a forward without wide row tiles: 256
+                 // (both 128-column halves in one two-weight tile) when the down projection is
+                 // not split, BN otherwise
     int S;       // f ranges of the down projection
     int wide_ok; // wide row tiles allowed in this forward
 };
@@ -161,9 +166,10 @@ inline Tiles tile_config(const Shape &s, int64_t B) {
     Tiles t;
     t.BN = half_width(s, B) ? kHalfBN : kBN;
     t.NB1 = s.f / t.BN;
-    t.NB2 = s.d / t.BN;
-    t.NB2w = s.d / kWideBN;
     t.S = down_splits(s, B);
+    t.DC = t.S == 1 && t.BN == kBN && s.d % kWideBN == 0 ? kWideBN : t.BN;
+    t.NB2 = s.d / t.DC;
+    t.NB2w = s.d / kWideBN;
     t.wide_ok = t.S == 1 && t.BN == kBN && s.d % kWideBN == 0 && s.f % kWideBN1 == 0;
     return t;
 }
@@ -294,7 +300,7 @@ struct Params {
     int sched;       // 0 static, 1 dynamic
     int debug;       // MOE_MK_DEBUG_* bits
     int nR, nTG, nEB, T, nC, tpw;
-    int BN, NB1, NB2, NB2w, S, wide_ok;  // see Tiles
+    int BN, NB1, NB2, NB2w, S, wide_ok, DC;  // see Tiles
     int wide_min;    // an expert takes wide row tiles when it has at least this many rows (> kTileTokens)
     int reb;         // experts per router task (4 or 16)
     int CT;          // tokens per combine task
