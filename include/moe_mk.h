@@ -279,8 +279,11 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
  *   "NB1"                     gate/up tiles per row tile (f / BN, or f / wide_BN1 = f / BN1
  *                             for a wide row tile)
  *   "NB2" "NB2_wide"          down-projection tiles per row tile and f range in a forward
- *                             without wide row tiles (d / BN), and per row tile in one with
- *                             them
+ *                             without wide row tiles (d / down_cols), and per row tile in one
+ *                             with them (d / wide_BN2)
+ *   "down_cols"               columns of a down-projection tile in a forward without wide row
+ *                             tiles: wide_BN2 (two narrow column blocks in one tile) when BN is
+ *                             BN1 and d a multiple of wide_BN2, else BN
  *   "S"                       f ranges of the down projection (1: not split)
  *   "wide_ok"                 1 when experts may take wide row tiles in this forward (the
  *                             kernel then gives them to experts with at least

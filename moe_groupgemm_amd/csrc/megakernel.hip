@@ -1524,33 +1524,39 @@ __device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0
 // With S > 1 splits, every split stores its fp32 partial in yp[sp]; the split that
 // finishes a tile last (a per-tile counter) adds the S partials in split order and writes
 // the rounded sum to y, so the result does not depend on which split finished last.
+// PAIR: the task spans kWideBN = 2 kBN columns from kWideBN*n, run as one two-weight tile
+// whose weight slots (those of gate and up in a gate/up tile) hold the two column halves, so
+// it streams 512-byte W2 row segments through one K loop instead of two 256-byte ones.
 // Returns whether this call completed the y tile (always with S = 1; with S > 1 only for the
-// split that added the partials).
-template <int AR, int BN = kBN>
+// split that added the partials).  SPLITS = false: code for S = 1 only.
+template <int AR, int BN = kBN, bool PAIR = false, bool SPLITS = true>
 __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0, int nrows, int n, int sp,
                                            int mt) {
+    static_assert(!PAIR || (BN == kBN && kWideBN == 2 * kBN), "a pair of narrow column blocks spans a wide task");
     const int kl = P.f / P.S;  // reduction range of this split: [sp*kl, (sp+1)*kl)
     GemmArgs ga;
     ga.arow[0] = P.h + (size_t)(row0 + a_row<AR>(nrows)) * P.f + (size_t)sp * kl;
     ga.nrows = nrows;
-    ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)sp * kl * P.d + (size_t)n * BN;
-    ga.B1 = ga.B0;
+    ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)sp * kl * P.d + (size_t)n * (PAIR ? kWideBN : BN);
+    ga.B1 = PAIR ? ga.B0 + kBN : ga.B0;
     ga.ldb = P.d;
     ga.K = kl;
     f32x4 acc0[4], acc1[4];
-    gemm_tile<false, AR, BN>(ga, acc0, acc1, g_sm.u.g);
+    gemm_tile<PAIR, AR, BN>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
     // at half width waves 4-7 handed their sums to waves 0-3 and write nothing
     const bool own = BN == kBN || w < 4;
-    const int col = n * BN + 16 * (BN == kHalfBN ? (w & 3) : w) + j;
-    if (P.S == 1) {
+    const int col = n * (PAIR ? kWideBN : BN) + 16 * (BN == kHalfBN ? (w & 3) : w) + j;
+    if (!SPLITS || P.S == 1) {
 #pragma unroll
         for (int rb = 0; rb < AR / 16; ++rb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * rb + 4 * g + r;
-                store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, col, acc0[rb][r], own && row < nrows);
+                MK_G uint16_t *yr = P.y + (size_t)(row0 + row) * P.d;
+                store_bf16_pair(yr, col, acc0[rb][r], own && row < nrows);
+                if constexpr (PAIR) store_bf16_pair(yr, col + kBN, acc1[rb][r], row < nrows);
             }
         return true;
     }
@@ -1561,7 +1567,10 @@ __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rb + 4 * g + r;
-            if (own && row < nrows) pub(ys + (size_t)(row0 + row) * P.d + col, acc0[rb][r]);
+            if (own && row < nrows) {
+                pub(ys + (size_t)(row0 + row) * P.d + col, acc0[rb][r]);
+                if constexpr (PAIR) pub(ys + (size_t)(row0 + row) * P.d + col + kBN, acc1[rb][r]);
+            }
         }
     }
     // count finished splits of this tile; the last one reduces
@@ -1580,53 +1589,28 @@ __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0
     fence_acquire();
     if (!own) return true;
 #pragma unroll
-    for (int rb = 0; rb < AR / 16; ++rb) {
+    for (int half = 0; half < (PAIR ? 2 : 1); ++half) {
+        const int c = col + half * kBN;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * rb + 4 * g + r;
-            const size_t o = (size_t)(row0 + min(row, nrows - 1)) * P.d + col;
-            float v[kMaxSplits];  // every partial loaded at once, then added in split order
+        for (int rb = 0; rb < AR / 16; ++rb) {
 #pragma unroll
-            for (int q = 0; q < kMaxSplits; ++q)
-                v[q] = q < P.S && q != sp ? P.yp[(size_t)q * split_stride + o] : acc0[rb][r];
-            float sum = v[0];
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rb + 4 * g + r;
+                const size_t o = (size_t)(row0 + min(row, nrows - 1)) * P.d + c;
+                const float mine = half ? acc1[rb][r] : acc0[rb][r];
+                float v[kMaxSplits];  // every partial loaded at once, then added in split order
 #pragma unroll
-            for (int q = 1; q < kMaxSplits; ++q)
-                if (q < P.S) sum += v[q];
-            store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, col, sum, row < nrows);
+                for (int q = 0; q < kMaxSplits; ++q)
+                    v[q] = q < P.S && q != sp ? P.yp[(size_t)q * split_stride + o] : mine;
+                float sum = v[0];
+#pragma unroll
+                for (int q = 1; q < kMaxSplits; ++q)
+                    if (q < P.S) sum += v[q];
+                store_bf16_pair(P.y + (size_t)(row0 + row) * P.d, c, sum, row < nrows);
+            }
         }
     }
     return true;
-}
-
-// Down-projection task of a narrow row tile in a forward with wide row tiles: y[rows, 256
-// columns from 256*n2] = h[rows, :] W2[e][:, those columns], run as one two-weight tile (the
-// column halves take the places of the gate and up weights), so the task streams 512-byte
-// W2 row segments through one K loop instead of two 128-column tiles one after the other.
-template <int AR>
-__device__ __forceinline__ void gemm2_pair_tile(const MK_C Params &P, int e, int row0, int nrows, int n2) {
-    static_assert(kWideBN == 2 * kBN, "a pair of narrow column blocks spans a wide down-projection task");
-    GemmArgs ga;
-    ga.arow[0] = P.h + (size_t)(row0 + a_row<AR>(nrows)) * P.f;
-    ga.nrows = nrows;
-    ga.B0 = P.W2 + (size_t)e * P.f * P.d + (size_t)n2 * kWideBN;
-    ga.B1 = ga.B0 + kBN;
-    ga.ldb = P.d;
-    ga.K = P.f;
-    f32x4 acc0[4], acc1[4];
-    gemm_tile<true, AR, kBN>(ga, acc0, acc1, g_sm.u.g);
-    const int lane = lane_id(), w = wave_id();
-    const int g = lane >> 4, j = lane & 15;
-    const int col = n2 * kWideBN + 16 * w + j;
-#pragma unroll
-    for (int rb = 0; rb < AR / 16; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * rb + 4 * g + r;
-            MK_G uint16_t *yr = P.y + (size_t)(row0 + row) * P.d;
-            store_bf16_pair(yr, col, acc0[rb][r], row < nrows);
-            store_bf16_pair(yr, col + kBN, acc1[rb][r], row < nrows);
-        }
 }
 
 // ------------------------------------------------------------------------------ wide tiles
@@ -2098,17 +2082,21 @@ __device__ __attribute__((noinline)) bool narrow_gemm2(const MK_C Params &Pa, in
     return gemm2_tile<AR, BN>(P, uni(e), uni(row0), uni(nrows), uni(n), uni(sp), uni(mt));
 }
 
-template <int AR>
-__device__ __attribute__((noinline)) void narrow_gemm2_pair(const MK_C Params &Pa, int e, int row0, int nrows,
-                                                            int n2) {
+// ... over kWideBN columns as one two-weight tile (gemm2_tile PAIR); SPLITS: S > 1 possible
+// (the split code raises a 64-row tile's registers past the caller-saved set, so S = 1 has
+// its own copy).
+template <int AR, bool SPLITS>
+__device__ __attribute__((noinline)) bool narrow_gemm2_pair(const MK_C Params &Pa, int e, int row0, int nrows,
+                                                            int n2, int sp, int mt) {
     const MK_C Params &P = uni_params(Pa);
-    gemm2_pair_tile<AR>(P, uni(e), uni(row0), uni(nrows), uni(n2));
+    return gemm2_tile<AR, kBN, true, SPLITS>(P, uni(e), uni(row0), uni(nrows), uni(n2), uni(sp), uni(mt));
 }
 
 // The tile code follows the row tile's rows: a row tile of more than kBM rows is a wide one
 // (see expert_tiles), narrow row tiles of at most 16 rows stage only 16 A rows.  In a forward
-// with wide row tiles a down-projection task spans kWideBN columns, which a narrow row tile
-// covers with one two-weight narrow tile over both column halves (no f splits then).
+// with wide row tiles, and in any forward with full-width narrow tiles and d a multiple of
+// kWideBN (Params::DC), a down-projection task spans kWideBN columns, which a narrow row tile
+// covers with one two-weight narrow tile over both column halves.
 // WIDE: the code may meet wide row tiles (the task loop of forwards that have them).
 template <bool WIDE>
 __device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
@@ -2129,12 +2117,12 @@ __device__ __forceinline__ bool task_gemm2(const MK_C Params &P, int e, int row0
         wide_gemm2(P, e, row0, nrows, n);
         return true;
     }
-    if (WIDE || uni(P.DC) == kWideBN) {  // S = 1: both column halves in one tile
-        if (nrows <= 16)
-            narrow_gemm2_pair<16>(P, e, row0, nrows, n);
-        else
-            narrow_gemm2_pair<64>(P, e, row0, nrows, n);
-        return true;
+    if (WIDE || uni(P.DC) == kWideBN) {  // both column halves in one tile
+        if (!WIDE && uni(P.S) > 1)  // (never in a forward with wide row tiles)
+            return nrows <= 16 ? narrow_gemm2_pair<16, true>(P, e, row0, nrows, n, sp, mt)
+                               : narrow_gemm2_pair<64, true>(P, e, row0, nrows, n, sp, mt);
+        return nrows <= 16 ? narrow_gemm2_pair<16, false>(P, e, row0, nrows, n, sp, mt)
+                           : narrow_gemm2_pair<64, false>(P, e, row0, nrows, n, sp, mt);
     }
     if (uni(P.BN) == kHalfBN)
         return nrows <= 16 ? narrow_gemm2<16, kHalfBN>(P, e, row0, nrows, n, sp, mt)

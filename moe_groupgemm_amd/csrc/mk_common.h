@@ -120,8 +120,8 @@ inline int max_down_splits(const Shape &s) {
 // per expert on the device from its row count once the histogram is known (the scan task):
 //   narrow  kBM = 64 rows; gate/up tiles of kBN = 128 columns of each weight, down-projection
 //           tiles of kBN columns, the down projection optionally split over f (S ranges);
-//           when it is not split (S = 1), a down-projection tile takes two such column blocks
-//           (kWideBN columns, two weight blocks against one staged h tile);
+//           when d allows, a down-projection tile takes two such column blocks (kWideBN
+//           columns, two weight blocks against one staged h tile);
 //   wide    kWideBM = 256 rows; gate/up tiles of kWideBN1 = 128 columns of each weight,
 //           down-projection tiles of kWideBN = 256 columns, so that each staged byte serves
 //           more multiply-adds.  An expert with wide row tiles puts a remainder of at most
@@ -157,8 +157,8 @@ struct Tiles {
     int NB2;     // down-projection tiles per narrow row tile and f range (d / DC)
     int NB2w;    // down-projection tiles per wide row tile (d / 256)
     int DC;      // columns of a down-projection task in a forward without wide row tiles: 256
-                 // (both 128-column halves in one two-weight tile) when the down projection is
-                 // not split, BN otherwise
+                 // (both 128-column halves in one two-weight tile) with full-width tiles and d a
+                 // multiple of 256, BN otherwise
     int S;       // f ranges of the down projection
     int wide_ok; // wide row tiles allowed in this forward
 };
@@ -167,7 +167,7 @@ inline Tiles tile_config(const Shape &s, int64_t B) {
     t.BN = half_width(s, B) ? kHalfBN : kBN;
     t.NB1 = s.f / t.BN;
     t.S = down_splits(s, B);
-    t.DC = t.S == 1 && t.BN == kBN && s.d % kWideBN == 0 ? kWideBN : t.BN;
+    t.DC = t.BN == kBN && s.d % kWideBN == 0 ? kWideBN : t.BN;
     t.NB2 = s.d / t.DC;
     t.NB2w = s.d / kWideBN;
     t.wide_ok = t.S == 1 && t.BN == kBN && s.d % kWideBN == 0 && s.f % kWideBN1 == 0;

@@ -90,10 +90,10 @@ def expected_task_counts(layer, B):
     mt = len(tiles)
     S = info("S")
     # a down-projection tile of a forward without wide row tiles spans two narrow column
-    # blocks exactly when the down projection is not split and the tiles are full width
+    # blocks exactly when the tiles are full width and d holds whole pairs of them
     dc = info("down_cols")
     assert dc * info("NB2") == layer.d, (dc, info("NB2"), layer.d)
-    assert dc == (2 * info("BN") if S == 1 and info("BN") == mk.moe_mk_plan_info(layer.plan, "BN1")
+    assert dc == (2 * info("BN") if info("BN") == mk.moe_mk_plan_info(layer.plan, "BN1")
                   and layer.d % (2 * info("BN")) == 0 else info("BN")), (dc, S, info("BN"))
     return {"route": info("route_tasks"), "topk": info("T"), "scan": 1, "group": info("T"),
             "gemm1": mt * info("NB1"), "gemm2": S * mt * (info("NB2_wide") if mw else info("NB2")),

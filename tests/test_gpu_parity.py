@@ -218,6 +218,37 @@ def test_wide_tiles_static_dynamic_identical():
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
 
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+@pytest.mark.parametrize("d,f,S,dc", [(256, 4096, 2, 256), (384, 512, 1, 128)], ids=["split_pairs", "no_split"])
+def test_exact_row_counts_narrow_forward(d, f, S, dc, sched):
+    # A narrow forward whose routing is set by the input (token b's logit e is x[b, e]), so
+    # the experts receive exactly 1, 16, 17, 40, 3, 0, 5 and 2 rows: row tiles at both sides of
+    # the 16-row tile variant.  With d = 256 the down projection is split in two f ranges and
+    # its tasks are two-weight tiles of 256 columns (forward_info "down_cols"), each split's
+    # partials added by the last one; with d = 384 it is not split and its tasks are
+    # 128-column tiles.
+    counts = [1, 16, 17, 40, 3, 0, 5, 2]
+    E, k = len(counts), 1
+    B = sum(counts)
+    assert _info(E, k, d, f, B, "S") == S and _info(E, k, d, f, B, "down_cols") == dc
+    slots = np.repeat(np.arange(E), counts)
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=1800 + d)
+    x[:, :E] = 0
+    x[np.arange(B), slots] = 0x4040  # bf16 3.0
+    Wr[:] = 0
+    Wr[np.arange(E), np.arange(E)] = 1.0
+    log(f"exact row counts d={d} f={f} counts={counts} sched={SNAME[sched]}")
+    ref = oracle.forward(x, Wr, bias, W1, W3, W2, k)
+    assert np.array_equal(ref["hist"], counts)
+    layer, out, got = run_small(x, Wr, bias, W1, W3, W2, k, sched)
+    check_routing(got, ref, B, E)
+    check_out(out, ref["out"], f"exact row counts d={d}")
+    tiles, mw = row_tiles(layer, B)
+    check_row_tiles(tiles, mw, ref["hist"], ref["exp_indptr"], 1 << 30)
+    assert mw == 0 and len(tiles) == 7
+    layer.close()
+
+
 def test_down_projection_splits_static_dynamic_identical():
     cfg, x, Wr, bias, W1, W3, W2 = small_case(13, 128, 12288, 4, 2, seed=901)
     outs = []
