@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=0, help="batch size (default: the configuration's first)")
     ap.add_argument("--sched", default="dynamic", choices=["static", "dynamic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--policy", default="by_rows", choices=["by_rows", "narrow_only", "batch_rule", "grouped_gate_up"],
+                    help="tile policy of the headline run (the library's own choice by default; the others are "
+                    "A/B comparisons)")
     ap.add_argument("--no-prefetch", action="store_true", help="turn off the weight prefetch during routing")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens of the oracle sample (default: auto)")
     ap.add_argument("--trace", action="store_true", help="after timing, run one traced forward and print "
@@ -376,7 +379,9 @@ def roofline(cfg_name, B, sched, alg_bytes, flops, kern_ms, policy="by_rows"):
             "traffic": traffic}
 
 
-TILE_POLICIES = {"by_rows": 0, "narrow_only": 8, "batch_rule": 16}  # MOE_MK_DEBUG_* flags
+# MOE_MK_DEBUG_* flags; 'grouped_gate_up' keeps the gate/up tiles on grouped rows where the library
+# would run them over all tokens from the start of the forward (forward_info "all_token_gate_up")
+TILE_POLICIES = {"by_rows": 0, "narrow_only": 8, "batch_rule": 16, "grouped_gate_up": 32}
 
 
 def measure_workload(cfg_name, sched_name, steps, warmup, dev, batches=None, cold_reps=10, policy="by_rows"):
@@ -418,6 +423,8 @@ def measure_workload(cfg_name, sched_name, steps, warmup, dev, batches=None, col
         ctl = layer.routing(B)["ctl"].cpu().numpy()
         e = {"workload": cfg.note, "config": cfg_name, "B": B, "sched": sched_name, "tile_policy": policy,
              "row_tiles": int(ctl[mk.CTL["mt_total"]]), "wide_row_tiles": int(ctl[mk.CTL["mw"]]),
+             "all_token_gate_up": bool(mk.moe_mk_forward_info(layer.plan, B, "all_token_gate_up"))
+             and not TILE_POLICIES[policy] & mk.MOE_MK_DEBUG_GROUPED_GATE_UP,
              "active_experts": active,
              "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(ms)), "tokens_per_s": B / (kern_ms / 1e3),
              "roofline": roofline(cfg_name, B, sched_name, alg_bytes, flops, kern_ms, policy),
@@ -521,7 +528,8 @@ WORKLOADS = [("prefill", "static"), ("prefill", "dynamic"), ("prefill", "static"
              ("prefill", "static", "batch_rule"), ("deepseek_zipf", "static"), ("deepseek_zipf", "dynamic"),
              ("deepseek_zipf", "dynamic", "narrow_only"), ("deepseek_zipf", "dynamic", "batch_rule"),
              ("sweep", "static"), ("sweep", "dynamic"), ("tiny", "static"), ("tiny", "dynamic"),
-             ("mixtral_decode", "static")]
+             ("tiny", "static", "grouped_gate_up"), ("mixtral_decode", "static"),
+             ("mixtral_decode", "dynamic", "grouped_gate_up")]
 
 
 def main():
@@ -557,7 +565,7 @@ def main():
     layer = mk.MoELayer(cfg.E, cfg.k, cfg.d, cfg.f, tWr, t1, t3, t2, router_bias=tb, sched=sched,
                         max_batch=B, device=dev)
     out = torch.empty((B, cfg.d), dtype=torch.bfloat16, device=dev)
-    base_flags = mk.MOE_MK_DEBUG_NO_PREFETCH if args.no_prefetch else 0
+    base_flags = (mk.MOE_MK_DEBUG_NO_PREFETCH if args.no_prefetch else 0) | TILE_POLICIES[args.policy]
     mk.moe_mk_plan_set_debug(layer.plan, 0, base_flags)
     layer.debug_flags = base_flags
     stream = torch.cuda.current_stream(dev)
@@ -583,8 +591,10 @@ def main():
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.note, "B": B, "d": cfg.d, "f": cfg.f, "E": cfg.E, "k": cfg.k,
-                   "sched": args.sched, "active_experts": active},
-        "roofline": roofline(cfg.name, B, args.sched, alg_bytes, flops, kern_ms),
+                   "sched": args.sched, "active_experts": active,
+                   "all_token_gate_up": bool(mk.moe_mk_forward_info(layer.plan, B, "all_token_gate_up"))
+                   and not base_flags & mk.MOE_MK_DEBUG_GROUPED_GATE_UP},
+        "roofline": roofline(cfg.name, B, args.sched, alg_bytes, flops, kern_ms, args.policy),
         "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(per_launch_ms)),
         "hbm_tbs": gbs / 1e3, "hbm_frac": gbs / PEAK_HBM_GBS,
         "mfma_tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,

@@ -288,6 +288,13 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
  *   "wide_ok"                 1 when experts may take wide row tiles in this forward (the
  *                             kernel then gives them to experts with at least
  *                             plan_info("wide_min_rows") rows; see moe_mk_routing_view)
+ *   "all_token_gate_up"       1 when this forward runs every expert's gate/up tiles over all
+ *                             B tokens, started before the routing is known (a batch of one
+ *                             routing tile in which under half an expert is expected to get no
+ *                             token: E (1 - k/E)^B <= 1/2, full-width tiles); the down
+ *                             projection then gathers its rows from them, and the routing view
+ *                             lists one row tile per expert (rows 0 for an expert without
+ *                             tokens).  0 with MOE_MK_DEBUG_GROUPED_GATE_UP set.
  * Returns -1 for an unknown key, an invalid plan, B < 1 or B*k >= 2^31.
  * Source: [RaMP] abstract (what follows from the batch size alone, as opposed to the
  * routing distribution, which only the device sees).
@@ -309,6 +316,8 @@ int64_t moe_mk_forward_info(moe_mk_plan_t plan, int64_t B, const char *key);
 #define MOE_MK_DEBUG_NARROW_ONLY 8  /* every expert takes narrow row tiles (A/B timing of the tile choice) */
 #define MOE_MK_DEBUG_BATCH_RULE 16  /* tile shape from the batch size alone: every expert with more than BM
                                        rows wide when B*k >= 128*E, else all narrow (A/B timing) */
+#define MOE_MK_DEBUG_GROUPED_GATE_UP 32  /* never the all-token gate/up: gate/up tiles over grouped rows only,
+                                            after the routing (A/B timing; see forward_info) */
 moe_mk_status_t moe_mk_plan_set_debug(moe_mk_plan_t plan, int64_t watchdog_ticks, int32_t flags);
 
 /*

@@ -28,6 +28,7 @@ MOE_MK_DEBUG_TRACE = 2
 MOE_MK_DEBUG_NO_PREFETCH = 4
 MOE_MK_DEBUG_NARROW_ONLY = 8
 MOE_MK_DEBUG_BATCH_RULE = 16
+MOE_MK_DEBUG_GROUPED_GATE_UP = 32
 TASK_KINDS = ("route", "topk", "scan", "group", "gemm1", "gemm2", "combine")
 # control block words (see moe_mk_routing_view)
 CTL_WORDS = 512

@@ -141,6 +141,10 @@ moe_mk_status_t check_forward(moe_mk_plan_t plan, const void *x, const float *Wr
 
 // Kernel arguments of a forward of B tokens whose workspace (a layout for cap tokens)
 // starts at base.
+bool dense_forward(moe_mk_plan_t plan, int64_t B) {
+    return !(plan->debug & MOE_MK_DEBUG_GROUPED_GATE_UP) && mk::all_token_gate_up(plan->s, B);
+}
+
 mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const float *router_bias, const void *W1,
                        const void *W3, const void *W2, void *out, int64_t B, char *base, int64_t cap) {
     const mk::Shape &s = plan->s;
@@ -186,9 +190,15 @@ mk::Params make_params(moe_mk_plan_t plan, const void *x, const float *Wr, const
         P.wide_min = B * s.k >= (int64_t)mk::kBatchRuleRows * s.E ? mk::kWideMinRows : 1 << 30;
     else
         P.wide_min = mk::kWideMinRows;
-    {  // after the tile configuration: the prefetch follows the gate/up tiles
-        const mk::Prefetch pf = (plan->debug & MOE_MK_DEBUG_NO_PREFETCH) ? mk::Prefetch{0, 0}
-                                                                           : mk::prefetch_plan(s, B, P.NB1, false);
+    P.dense = dense_forward(plan, B) ? 1 : 0;
+    // dynamic schedule: tickets without a queue slot (the routers; with the all-token gate/up also
+    // the top-k task and the gate/up tiles of every expert, in f-range order)
+    P.nImp = P.nR + (P.dense ? 1 + s.E * P.NB1 : 0);
+    {  // after the tile configuration: the prefetch follows the gate/up tiles (none is needed when
+       // they run from the start)
+        const mk::Prefetch pf = (plan->debug & MOE_MK_DEBUG_NO_PREFETCH) || P.dense
+                                    ? mk::Prefetch{0, 0}
+                                    : mk::prefetch_plan(s, B, P.NB1, false);
         P.pf_nt = pf.nt;
         P.pf_lines = pf.lines;
     }
@@ -261,6 +271,8 @@ moe_mk_status_t moe_mk_forward_unfused(moe_mk_plan_t plan, const void *x, const 
     if (cap < B) return MOE_MK_EWORKSPACE;
     mk::Params P = make_params(plan, x, Wr, router_bias, W1, W3, W2, out, B, (char *)ws, cap);
     P.unfused = 1;
+    P.dense = 0;  // one kernel per phase: the gate/up kernel runs after the grouping
+    P.nImp = P.nR;
     if (hipSetDevice(plan->device) != hipSuccess) return MOE_MK_EHIP;
     if (mk_launch_unfused(P, (hipStream_t)stream) != hipSuccess) return MOE_MK_EHIP;
     return MOE_MK_OK;
@@ -394,7 +406,8 @@ int64_t moe_mk_forward_info(moe_mk_plan_t plan, int64_t B, const char *key) {
                {"NB2_wide", t.NB2w},
                {"down_cols", t.DC},
                {"S", t.S},
-               {"wide_ok", t.wide_ok}};
+               {"wide_ok", t.wide_ok},
+               {"all_token_gate_up", dense_forward(plan, B) ? 1 : 0}};
     for (auto &e : tab)
         if (std::strcmp(e.k, key) == 0) return e.v;
     return -1;

@@ -137,7 +137,8 @@ struct Bases {
     int q1p, q2p;  // block sizes: q1, q2 rounded up to multiples of 8 (see complete_bases)
     int N2;        // down-projection tasks per row tile and f range
     bool wide;     // the forward has wide row tiles
-    bool known;    // GroupGEMM layout known once the scan has run
+    bool known;    // GroupGEMM layout known once the scan has run (all-token gate/up: from the start)
+    bool routed;   // static schedule: this workgroup has seen the scan's result word
 };
 
 __device__ __forceinline__ int round8(int v) { return (v + 7) & ~7; }
@@ -153,6 +154,7 @@ __device__ __forceinline__ Bases initial_bases(const MK_C Params &P) {
     b.mt = b.q1 = b.q2 = b.q1p = b.q2p = b.N2 = 0;
     b.wide = false;
     b.known = false;
+    b.routed = false;
     return b;
 }
 
@@ -285,6 +287,18 @@ __device__ __forceinline__ void wg_push_range(const MK_C Params &P, int g0, int 
     }
     const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
     for (int i = threadIdx.x; i < cnt; i += kThreads) st_relaxed64(P.qslots + s0 + i, tag | (uint32_t)(g0 + i));
+}
+
+// The same from one thread (the slots' data was published before the event that fired them).
+__device__ __forceinline__ void thread_push_range(const MK_C Params &P, int g0, int cnt) {
+    if (cnt <= 0) return;
+    const int s0 = add_relaxed(P.ctl + CTL_QTAIL, cnt);
+    if (s0 + cnt > P.q_cap) {
+        set_error(P.ctl, 4 /* MOE_MK_ERR_QUEUE */);
+        return;
+    }
+    const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
+    for (int i = 0; i < cnt; ++i) st_relaxed64(P.qslots + s0 + i, tag | (uint32_t)(g0 + i));
 }
 
 // Notify one counter: the group's published stores complete, then thread 0 adds delta
@@ -1035,9 +1049,12 @@ __device__ __forceinline__ ExpertTiles expert_tiles(const MK_C Params &P, int h)
 
 // Events of row tile i: its gate/up tiles per f range (NB1/S each, ev_h) and its
 // down-projection tiles of bn2 columns per combine chunk (ev_d).
-__device__ __forceinline__ void arm_row_tile(const MK_C Params &P, int i, int bn2) {
+// (gate_up = false: only ev_d; the all-token gate/up arms ev_h with atomic adds, since its
+// gate/up tiles may have counted them down before the scan)
+__device__ __forceinline__ void arm_row_tile(const MK_C Params &P, int i, int bn2, bool gate_up = true) {
     if (P.unfused) return;  // kernel boundaries order the phases there
-    for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
+    if (gate_up)
+        for (int sp = 0; sp < P.S; ++sp) pub(P.ev_h + i * P.S + sp, P.NB1 / P.S);
     for (int c = 0; c < P.nch; ++c) pub(P.ev_d + i * P.nch + c, min(kCombineCols, P.d - c * kCombineCols) / bn2);
 }
 
@@ -1334,6 +1351,14 @@ __device__ __forceinline__ void frag_reads(const uint32_t (&ba)[4], const uint32
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
             : "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]), "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]));
+    } else if constexpr (DUAL && AR == 32) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %6\n\tds_read_b64_tr_b16 %1, %7\n\t"
+            "ds_read_b64_tr_b16 %2, %8\n\tds_read_b64_tr_b16 %3, %9\n\t"
+            "ds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(a[0]), "=&v"(a[1])
+            : "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]), "v"(aa[0]), "v"(aa[1]));
     } else if constexpr (DUAL) {
         asm volatile(
             "ds_read_b64_tr_b16 %0, %5\n\tds_read_b64_tr_b16 %1, %6\n\t"
@@ -1342,6 +1367,7 @@ __device__ __forceinline__ void frag_reads(const uint32_t (&ba)[4], const uint32
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(a[0])
             : "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]), "v"(aa[0]));
+        static_assert(AR == 16, "two-weight tiles stage 16, 32 or 64 A rows");
     } else if constexpr (AR == 64) {
         asm volatile(
             "ds_read_b64_tr_b16 %0, %6\n\tds_read_b64_tr_b16 %1, %7\n\t"
@@ -1356,6 +1382,7 @@ __device__ __forceinline__ void frag_reads(const uint32_t (&ba)[4], const uint32
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(b[0]), "=&v"(b[1]), "=&v"(a[0])
             : "v"(ba[0]), "v"(ba[1]), "v"(aa[0]));
+        static_assert(AR == 16, "one-weight tiles stage 16 or 64 A rows");
     }
 }
 
@@ -1490,10 +1517,51 @@ __device__ __forceinline__ int a_row(int nrows) {
     return min(8 * a_block<AR>() + (lane_id() >> 3), nrows - 1);
 }
 
-template <int AR, int BN = kBN>
-__device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0, int nrows, int n) {
+// All-token gate/up: wait until this forward's routing tables are out (the scan's result word
+// carries the forward's epoch), then acquire.  Returns false on an error or the watchdog.
+__device__ __forceinline__ bool wg_wait_routed(const MK_C Params &P) {
+    if (threadIdx.x == 0) {
+        const uint32_t ep = (uint32_t)g_sm.epoch;
+        const MK_G unsigned long long *word = (const MK_G unsigned long long *)(P.ctl + CTL_SCAN64);
+        bool ok = true;
+        const unsigned long long t0 = now_ticks();
+        for (unsigned it = 1; (uint32_t)(ld_relaxed64(word) >> 32) != ep; ++it) {
+            if (it < 64)
+                __builtin_amdgcn_s_sleep(1);
+            else
+                __builtin_amdgcn_s_sleep(8);
+            if ((it & 31u) == 0) {
+                if (ld_relaxed(P.ctl + CTL_ERR) != 0) {
+                    ok = false;
+                    break;
+                }
+                if ((long long)(now_ticks() - t0) > P.watchdog) {
+                    set_error(P.ctl, 1 /* MOE_MK_ERR_WATCHDOG */);
+                    ok = false;
+                    break;
+                }
+            }
+        }
+        fence_acquire();
+        g_sm.bcast[0] = ok ? 1 : 0;
+    }
+    __syncthreads();
+    const bool ok = g_sm.bcast[0] != 0;
+    __syncthreads();
+    return ok;
+}
+
+// Gate/up tile of row tile (e, row0, nrows), columns n*BN.. of f, written to h rows row0...
+// DENSE (all-token gate/up, a tile that started before the routing was known): the A rows are
+// x rows 0..nrows-1, every token of the batch, in order; once the K loop is done the tile waits
+// for the routing and writes the row of each token that chose expert e to that token's grouped
+// h row (inv), dropping the others.  Otherwise the A rows are grouped rows, gathered from x
+// through perm.  Returns false when the wait for the routing failed.
+template <int AR, int BN = kBN, bool DENSE = false>
+__device__ __forceinline__ bool gemm1_tile(const MK_C Params &P, int e, int row0, int nrows, int n) {
     GemmArgs ga;
-    ga.arow[0] = P.x + (size_t)(P.perm[row0 + a_row<AR>(nrows)] / P.k) * P.d;
+    const int ar = a_row<AR>(nrows);
+    ga.arow[0] = P.x + (size_t)(DENSE ? ar : P.perm[row0 + ar] / P.k) * P.d;
     ga.nrows = nrows;
     ga.B0 = P.W1 + (size_t)e * P.d * P.f + (size_t)n * BN;
     ga.B1 = P.W3 + (size_t)e * P.d * P.f + (size_t)n * BN;
@@ -1501,9 +1569,21 @@ __device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0
     ga.K = P.d;
     f32x4 acc0[4], acc1[4];
     gemm_tile<true, AR, BN>(ga, acc0, acc1, g_sm.u.g);
+    int *dmap = (int *)g_sm.u.g.ring;  // DENSE: grouped h row of each token, or -1 (the ring is free now)
+    if constexpr (DENSE) {
+        static_assert(BN == kBN, "all-token tiles are full width");
+        if (!wg_wait_routed(P)) return false;
+        for (int t = threadIdx.x; t < nrows; t += kThreads) {
+            int dst = -1;
+            for (int i = 0; i < P.k; ++i)
+                if (P.topk_idx[(size_t)t * P.k + i] == e) dst = P.inv[(size_t)t * P.k + i];
+            dmap[t] = dst;
+        }
+        __syncthreads();  // (the notify that follows the tile syncs again before the ring is reused)
+    }
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
-    if (BN == kHalfBN && w >= 4) return;  // (their sums went to waves 0-3)
+    if (BN == kHalfBN && w >= 4) return true;  // (their sums went to waves 0-3)
     const int col = n * BN + 16 * (BN == kHalfBN ? (w & 3) : w) + j;
 #pragma unroll
     for (int rb = 0; rb < AR / 16; ++rb) {
@@ -1514,10 +1594,13 @@ __device__ __forceinline__ void gemm1_tile(const MK_C Params &P, int e, int row0
             const uint32_t hv = f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
             // columns col and col+1 sit in lanes j and j+1: even lanes store both
             const uint32_t nb = (uint32_t)__shfl_xor((int)hv, 1, 64);
-            if (row < nrows && (j & 1) == 0)
-                pub((MK_G uint32_t *)(P.h + (size_t)(row0 + row) * P.f + col), hv | (nb << 16));
+            if (row < nrows && (j & 1) == 0) {
+                const int dr = DENSE ? dmap[row] : row0 + row;
+                if (dr >= 0) pub((MK_G uint32_t *)(P.h + (size_t)dr * P.f + col), hv | (nb << 16));
+            }
         }
     }
+    return true;
 }
 
 // Down-projection tile over f range sp.  With S = 1 the tile writes y (bf16) directly.
@@ -2069,10 +2152,17 @@ __device__ __forceinline__ void wide_gemm2(const MK_C Params &Pa, int e, int row
 // call; the wide tiles, which need nearly all registers, are inlined for that reason).
 // GEMM1 tile: h[rows, n0:n0+128] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
 // where row p of the tile is token perm[p] / k of x; AR = staged A rows (16 or 64).
-template <int AR, int BN = kBN>
-__device__ __attribute__((noinline)) void narrow_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
+template <int AR, int BN = kBN, bool DENSE = false>
+__device__ __attribute__((noinline)) bool narrow_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
     const MK_C Params &P = uni_params(Pa);
-    gemm1_tile<AR, BN>(P, uni(e), uni(row0), uni(nrows), uni(n));
+    return gemm1_tile<AR, BN, DENSE>(P, uni(e), uni(row0), uni(nrows), uni(n));
+}
+// All-token gate/up tile of expert e over every token of the batch (see gemm1_tile).
+__device__ __forceinline__ bool dense_gemm1(const MK_C Params &P, int e, int n) {
+    const int B = uni(P.B);
+    if (B <= 16) return narrow_gemm1<16, kBN, true>(P, e, 0, B, n);
+    if (B <= 32) return narrow_gemm1<32, kBN, true>(P, e, 0, B, n);
+    return narrow_gemm1<64, kBN, true>(P, e, 0, B, n);
 }
 // GEMM2 tile: y[rows, n0:n0+128] (or its split-sp partial) = h[rows, f range sp] W2[e][f range sp, n0:n0+128].
 template <int AR, int BN = kBN>
@@ -2329,6 +2419,16 @@ __device__ __forceinline__ void group_and_notify(const MK_C Params &P, Bases &bs
     }
 }
 
+// Publish the scan's result word (static schedule, and dynamic all-token gate/up forwards; called
+// after the scan's stores were drained): the row-tile count and whether any row tile is wide, tagged with the epoch.
+__device__ __forceinline__ void publish_scan(const MK_C Params &P, int mt_total, int mw) {
+    if (threadIdx.x == 0) {
+        const unsigned long long v = ((unsigned long long)(uint32_t)g_sm.epoch << 32) | (mw > 0 ? 0x80000000ull : 0ull) |
+                                     (uint32_t)mt_total;
+        st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_SCAN64), v);
+    }
+}
+
 // The scan and the grouping of a batch that is one routing tile, run by its top-k task
 // right after top-k, from what top-k left in LDS (the tile histogram is the histogram, the
 // tile's row offsets are exp_indptr): everything is published and nothing is read back.
@@ -2353,7 +2453,8 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
     }
     // scan ("Core method": the prefix sum decides how many GroupGEMM tiles each expert triggers)
     const int h = e < E ? ts.hist[e] : 0;
-    const int mt = (h + BM - 1) / BM;
+    // (all-token gate/up: row tile e is expert e's rows, none for an expert without tokens)
+    const int mt = P.dense ? (e < E ? 1 : 0) : (h + BM - 1) / BM;
     int total_h, total_mt;
     const int off = block_excl_scan(h, W.part, &total_h);
     const int mbase = block_excl_scan(mt, W.part, &total_mt);
@@ -2369,7 +2470,7 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
             pub(P.mt_expert + i, e);
             pub(P.mt_row0 + i, off + m * BM);
             pub(P.mt_rows + i, min(BM, h - m * BM));
-            arm_row_tile(P, i, P.DC);
+            if (!P.dense || h > 0) arm_row_tile(P, i, P.DC, !P.dense);
         }
     }
     if (e == 0) {
@@ -2382,16 +2483,20 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
     }
     count_task(P, K_SCAN);
     complete_bases(P, bs, total_mt, 0);
+    // all-token gate/up: the down-projection tasks of the experts with tokens are the only
+    // GroupGEMM tasks pushed
+    int active = 0;
+    if (dyn && P.dense) (void)block_excl_scan(h > 0 ? 1 : 0, W.part, &active);
     if (dyn && threadIdx.x == 0) {
         // tickets: routers, this task, and the GroupGEMM and combine tasks
-        const int real = bs.K + 1 + P.S * (bs.q1 + bs.q2) + P.nC;
+        const int real = bs.K + 1 + P.S * (P.dense ? bs.q1 + active * bs.N2 : bs.q1 + bs.q2) + P.nC;
         const unsigned long long tag = (unsigned long long)(uint32_t)g_sm.epoch << 32;
         st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_TOTAL64), tag | (uint32_t)real);
     }
     // reserve the queue slots of the pushes (the reply is first needed after the grouping)
     const int Q = P.NB1 / P.S;  // gate/up tasks per row tile and split
     int tot = 0, qbase = 0;
-    if (dyn) {
+    if (dyn && !P.dense) {
         const int nm = e < E && h > 0 && e != skip ? mt : 0;
         const int poff = block_excl_scan(nm * Q * P.S, W.part, &tot);
         if (e < E) {
@@ -2431,6 +2536,33 @@ __device__ __forceinline__ void fused_scan_group(const MK_C Params &P, Bases &bs
         pub(P.amt + i, W.amt[i]);
     }
     count_task(P, K_GROUP);
+    if (P.dense) {
+        // Arm each (expert, f range) gate/up event with its tile count.  Its gate/up tiles have
+        // been counting it down since the forward began, so the add that brings it to zero (this
+        // one, or a tile's later) fires it; whoever fires it pushes the expert's down-projection
+        // tasks of that f range (dynamic schedule; static ones wait for the scan's result word
+        // and then for zero).  Everything the down projection reads goes out first.
+        wg_stores_done();
+        const int Q1 = P.NB1 / P.S;
+        if (e < E) {
+            // (debug: a skipped expert's events are armed with one count too many, so they never fire)
+            const int arm = e == skip ? Q1 + 1 : Q1;
+            for (int sp = 0; sp < P.S; ++sp) {
+                MK_G int *ctr = P.ev_h + e * P.S + sp;
+                if (!dyn) {
+                    add_relaxed_noret(ctr, arm);  // (drained by the caller's notification)
+                    continue;
+                }
+                if (add_relaxed(ctr, arm) + arm != 0) continue;  // a gate/up tile will fire it
+                if (h > 0) thread_push_range(P, base_g2(bs, sp, P.S) + e * bs.N2, bs.N2);
+                if (add_relaxed(P.ctl + CTL_EV_G1, -1) == 1) thread_push_range(P, bs.C, P.nC);
+            }
+        }
+        // dynamic: the result word tells the gate/up tiles that the routing is known (the tables
+        // went out above); static: the caller's notification drains the arming and publishes it
+        if (dyn) publish_scan(P, E, 0);
+        return;
+    }
     if (!dyn) {
         if (skip >= 0 && threadIdx.x == 0) pub(P.ev_exp + skip, 1);  // a wait that never ends (debug)
         return;  // the caller's notification publishes everything
@@ -2479,16 +2611,6 @@ __device__ __forceinline__ void route_task_coords(const MK_C Params &P, int g, i
     }
 }
 
-// Static schedule: publish the scan's result word (called after the notify that drained the
-// scan's stores): the row-tile count and whether any row tile is wide, tagged with the epoch.
-__device__ __forceinline__ void publish_scan(const MK_C Params &P, int mt_total, int mw) {
-    if (threadIdx.x == 0) {
-        const unsigned long long v = ((unsigned long long)(uint32_t)g_sm.epoch << 32) | (mw > 0 ? 0x80000000ull : 0ull) |
-                                     (uint32_t)mt_total;
-        st_relaxed64((MK_G unsigned long long *)(P.ctl + CTL_SCAN64), v);
-    }
-}
-
 // Runs task g (obtained at time t0).  Returns false when the forward must be abandoned.
 // WIDE: the copy of the task code that can run wide row tiles.  The other copy (used until a
 // forward is known to have them, and throughout forwards that have none) leaves them out, so
@@ -2496,6 +2618,25 @@ __device__ __forceinline__ void publish_scan(const MK_C Params &P, int mt_total,
 // it returns kNeedWide, without running the task, for a GroupGEMM task of a forward that
 // has wide row tiles.
 constexpr int kTaskDone = 1, kNeedWide = 2;
+__device__ __forceinline__ bool wg_wait_scan(const MK_C Params &P, Bases &bs);
+
+// All-token gate/up forwards: whether this forward's routing tables are out (the scan's result
+// word carries the forward's epoch), with an acquire when they are.  One load, until this
+// workgroup has once seen them.
+__device__ __forceinline__ bool routing_seen(const MK_C Params &P, Bases &bs) {
+    if (bs.routed) return true;
+    if (threadIdx.x == 0) {
+        const unsigned long long v = ld_relaxed64((const MK_G unsigned long long *)(P.ctl + CTL_SCAN64));
+        const bool r = (uint32_t)(v >> 32) == (uint32_t)g_sm.epoch;
+        if (r) fence_acquire();
+        g_sm.bcast[0] = r ? 1 : 0;
+    }
+    __syncthreads();
+    const bool r = g_sm.bcast[0] != 0;
+    __syncthreads();
+    bs.routed = r;
+    return r;
+}
 template <bool WIDE>
 __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, unsigned long long t0) {
     const bool dyn = P.sched != 0;
@@ -2506,15 +2647,19 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         const unsigned long long t2 = now_ticks();
         count_task(P, K_ROUTE);
         const int t = tg / route_groups_per_tile(P);
+        // (dynamic: the first task of the tile arms its event and the one that fires it pushes the
+        // top-k task, except with the all-token gate/up, whose top-k task arms and waits as in
+        // the static schedule)
+        const bool push = dyn && !P.dense;
         int delta = -1;
-        if (dyn && (tg % route_groups_per_tile(P)) == 0 && eb == 0) delta += route_tasks_of_tile(P, t);
-        if (wg_notify(P, P.ev_logit + t, delta) && dyn) wg_push_range(P, bs.K + t, 1);
+        if (push && (tg % route_groups_per_tile(P)) == 0 && eb == 0) delta += route_tasks_of_tile(P, t);
+        if (wg_notify(P, P.ev_logit + t, delta) && push) wg_push_range(P, bs.K + t, 1);
         trace_task(P, g, K_ROUTE, t0, t0, t2);
         return kTaskDone;
     }
     if (g < bs.S) {  // ---------------------------------------------------------- TOPK
         const int t = g - bs.K;
-        if (!dyn) {
+        if (!dyn || P.dense) {
             if (threadIdx.x == 0) add_relaxed(P.ev_logit + t, route_tasks_of_tile(P, t));  // arm
             if (!wg_wait_zero(P, P.ev_logit + t)) return 0;
         }
@@ -2593,6 +2738,38 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         const int Q = P.NB1 / P.S;
         if (kind == 1) {  // ---------------------------------------------------- GEMM1
             const int mt = j / Q, n = sp * Q + (j - (j / Q) * Q);
+            if constexpr (!WIDE) {  // (an all-token forward has no wide row tiles)
+            if (P.dense) {
+                // All-token gate/up forward: row tile mt is expert mt's rows.  A tile that starts
+                // before the routing is known runs over every token and keeps the expert's rows
+                // at its end; one that starts later runs over the expert's grouped rows, if any.
+                const unsigned long long t1 = now_ticks();
+                if (routing_seen(P, bs)) {
+                    const int r0_ = P.mt_row0[mt], nr_ = P.mt_rows[mt];
+                    if (uni(nr_) > 0) task_gemm1<false>(P, mt, uni(r0_), uni(nr_), n);
+                } else {
+                    if (!dense_gemm1(P, mt, n)) return 0;
+                    bs.routed = true;  // (it waited for the scan's result word)
+                }
+                const unsigned long long t2 = now_ticks();
+                count_task(P, K_GEMM1);
+                // Firing the event means the scan has armed it, so the routing tables are out:
+                // push the expert's down-projection tiles of this f range if it has rows.
+                if (wg_notify(P, P.ev_h + mt * P.S + sp, -1) && dyn) {
+                    if (threadIdx.x == 0) {
+                        fence_acquire();
+                        g_sm.bcast[0] = ld_relaxed(P.mt_rows + mt);
+                    }
+                    __syncthreads();
+                    const int rows = g_sm.bcast[0];
+                    __syncthreads();
+                    if (rows > 0) wg_push_range(P, base_g2(bs, sp, P.S) + mt * bs.N2, bs.N2);
+                    if (wg_notify(P, P.ctl + CTL_EV_G1, -1)) wg_push_range(P, bs.C, P.nC);
+                }
+                trace_task(P, g, K_GEMM1, t0, t1, t2);
+                return kTaskDone;
+            }
+            }
             // the row tile's table entries are read together (one round trip)
             const int e_ = P.mt_expert[mt], r0_ = P.mt_row0[mt], nr_ = P.mt_rows[mt];
             const int e = uni(e_);
@@ -2615,9 +2792,16 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         }
         // --------------------------------------------------------------------- GEMM2
         const int mt = j / bs.N2, n = j - mt * bs.N2;
+        // (all-token gate/up, static: the layout was known from the start, the routing tables
+        // are out once the scan's result word is)
+        if (P.dense && !dyn && !bs.routed) {
+            if (!wg_wait_scan(P, bs)) return 0;
+            bs.routed = true;
+        }
         // the row tile's table entries (published with the scan result this workgroup has
         // acquired) are read before the wait, so the two round trips overlap
         const int e_ = P.mt_expert[mt], r0_ = P.mt_row0[mt], nr_ = P.mt_rows[mt];
+        if (P.dense && uni(nr_) == 0) return kTaskDone;  // an expert without tokens (static positions)
         if (!dyn && !wg_wait_zero(P, P.ev_h + mt * P.S + sp)) return 0;
         const unsigned long long t1 = now_ticks();
         const bool done = task_gemm2<WIDE>(P, uni(e_), uni(r0_), uni(nr_), n, sp, mt);
@@ -2631,6 +2815,10 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
     {  // ------------------------------------------------------------------------ COMBINE
         const int c = g - bs.C;
         unsigned long long t1 = 0;
+        if (P.dense && !dyn && !bs.routed) {  // (see GEMM2)
+            if (!wg_wait_scan(P, bs)) return 0;
+            bs.routed = true;
+        }
         if (!task_combine(P, c, t1)) return 0;
         const unsigned long long t2 = now_ticks();
         count_task(P, K_COMBINE);
@@ -2727,23 +2915,30 @@ __device__ __forceinline__ bool wg_wait_scan(const MK_C Params &P, Bases &bs) {
     return ok;
 }
 
-// Dynamic pop.  A workgroup takes the next ticket with one atomic add; tickets below nR are
-// the router tasks (never pushed), ticket nR + i is queue slot i.  The holder of a ticket
+// Dynamic pop.  A workgroup takes the next ticket with one atomic add; tickets below nImp are
+// handed out without a queue slot (the router tasks, and with the all-token gate/up the top-k
+// task and every gate/up tile), ticket nImp + i is queue slot i.  The holder of a ticket
 // whose slot is not yet filled waits on that slot alone, so idle workgroups poll distinct
 // words instead of contending for one.  Every pushed task is ready, so a filled slot runs
 // at once.  Returns a task index, -1 when the ticket lies beyond the forward's task count,
 // -2 on error.
-__device__ __forceinline__ int wg_pop(const MK_C Params &P) {
+__device__ __forceinline__ int wg_pop(const MK_C Params &P, const Bases &bs) {
     if (threadIdx.x == 0) {
         int g;
         const uint32_t ep = (uint32_t)g_sm.epoch;
         const int t = add_relaxed(P.ctl + CTL_QHEAD, 1);
         if (t < P.nR) {
             g = t;
+        } else if (t < P.nImp) {
+            // all-token gate/up: ticket nR is the top-k task (index nR), then come the gate/up
+            // tiles of every expert, f range by f range
+            const int u = t - P.nR - 1;
+            const int sp = u < 0 ? 0 : u / bs.q1;
+            g = u < 0 ? t : base_g1(bs, sp) + (u - sp * bs.q1);
         } else if (g_sm.total >= 0 && t >= g_sm.total) {
             g = -1;  // beyond the forward's tasks: nothing will fill this slot
         } else {
-            const int i = t - P.nR;
+            const int i = t - P.nImp;
             const unsigned long long t0 = now_ticks();
             for (unsigned it = 0;; ++it) {
                 if (i < P.q_cap) {
@@ -2830,7 +3025,9 @@ __device__ __forceinline__ int static_next(const MK_C Params &P, Bases &bs, Stat
             c.g += gridDim.x;
             return g;
         }
-        if (!wg_wait_scan(P, bs)) return -2;
+        // (all-token gate/up: the layout is known from the start and the gate/up tiles wait for
+        // nothing; the tasks that read routing results wait for the result word themselves)
+        if (!P.dense && !wg_wait_scan(P, bs)) return -2;
         // (a forward of a few tiles per workgroup gains nothing from stealing, and its idle
         // workgroups would only load the counters that the busy ones claim from)
         c.steal = bs.C - bs.M1p >= 2 * (int)gridDim.x;
@@ -2904,6 +3101,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
         return;
     }
     Bases bs = initial_bases(P);
+    if (P.dense) complete_bases(P, bs, P.E, 0);  // one row tile per expert, known before routing
     // Two task loops, each with one call site of its copy of the task code: the first runs
     // forwards without wide row tiles, and every task until a forward is known to have them;
     // the second takes over from there (with the task that found out, if any).
@@ -2917,7 +3115,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
     bool wide_loop = false, pending = false;
     for (;;) {
         t0 = now_ticks();
-        g = uni(P.sched != 0 ? wg_pop(P) : static_next(P, bs, cur));
+        g = uni(P.sched != 0 ? wg_pop(P, bs) : static_next(P, bs, cur));
         if (g < 0) break;
         const int r = run_task<false>(P, g, bs, t0);
         if (r != kTaskDone) {
@@ -2932,7 +3130,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_megakernel(Params Parg) {
     while (wide_loop) {
         if (!pending) {
             t0 = now_ticks();
-            g = uni(P.sched != 0 ? wg_pop(P) : static_next(P, bs, cur));
+            g = uni(P.sched != 0 ? wg_pop(P, bs) : static_next(P, bs, cur));
             if (g < 0) break;
         }
         pending = false;

@@ -151,6 +151,20 @@ inline bool half_width(const Shape &s, int64_t B) {
     // cost: ring fill, epilogue, notify; halving it gains nothing)
     return a <= kBM && 2 * rt * (s.f / kBN) <= kGridDefault && (int64_t)s.d * kHalfBN * 4 >= (256 << 10);
 }
+// All-token gate/up (a batch of one routing tile in which nearly every expert has rows):
+// every expert's gate/up tiles run over all B tokens instead of its grouped rows, so they
+// depend on nothing and start with the forward, streaming the weights while the batch is
+// routed; the down projection gathers each grouped row's h from them (row e*B + token).  The
+// extra multiply-adds cost nothing at these batch sizes (the tiles are bound by their weight
+// bytes); the cost is the gate/up weights of experts that end up with no rows, so the mode is
+// taken only when under half an expert is expected to be idle under uniform routing
+// (E (1 - k/E)^B <= 1/2) and the tiles are full width.
+inline bool all_token_gate_up(const Shape &s, int64_t B) {
+    if (B < 1 || B > kTileTokens || half_width(s, B)) return false;
+    double p = 1.0;
+    for (int64_t i = 0; i < B; ++i) p *= 1.0 - (double)s.k / (double)s.E;
+    return (double)s.E * p <= 0.5;
+}
 struct Tiles {
     int BN;      // columns of a narrow tile: kBN, or kHalfBN (half_width)
     int NB1;     // gate/up tiles per row tile (f / BN; f / 128 for wide row tiles)
@@ -333,6 +347,12 @@ struct Params {
     // Set for the phase-per-kernel pipeline (the unfused baseline): kernel boundaries order
     // the phases, so the scan arms no events and the workspace stays at its rest state.
     int unfused;
+    // All-token gate/up (all_token_gate_up): row tile e is expert e's rows (possibly none),
+    // gate/up tile (e, n) computes h rows e*B .. e*B + B - 1 for every token, and in the dynamic
+    // schedule the top-k task and the gate/up tiles are handed out without a push.
+    int dense;
+    int nImp;  // dynamic schedule: tickets handed out without a queue slot (routers, and with dense the top-k
+               // task and the gate/up tiles)
 };
 
 // The static scratch of the allocation-free entry point (one per GPU).

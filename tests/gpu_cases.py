@@ -61,10 +61,19 @@ def row_tiles(layer, B):
     return tiles, mw
 
 
-def check_row_tiles(tiles, mw, hist, indptr, wide_min, BM=64, wide_BM=256):
+def check_row_tiles(tiles, mw, hist, indptr, wide_min, BM=64, wide_BM=256, all_token=False):
     """The row tiles partition every expert's grouped rows, in expert order and in row order
     within an expert: a wide tile holds more than BM and at most wide_BM rows and goes to an
-    expert with at least wide_min rows, a narrow one at most BM; mw counts the wide ones."""
+    expert with at least wide_min rows, a narrow one at most BM; mw counts the wide ones.
+    all_token (a forward with the all-token gate/up): row tile e holds exactly expert e's rows,
+    none for an expert without tokens."""
+    if all_token:
+        E = len(hist)
+        assert mw == 0 and len(tiles) == E
+        assert np.array_equal(tiles[:, 0], np.arange(E))
+        assert np.array_equal(tiles[:, 1], indptr[:E]) and np.array_equal(tiles[:, 2], hist)
+        assert np.all(hist <= BM)
+        return
     assert np.all(tiles[:, 2] >= 1) and np.all(tiles[:, 2] <= wide_BM)
     assert np.count_nonzero(tiles[:, 2] > BM) == mw
     assert np.all(np.diff(tiles[:, 0]) >= 0) and np.all(np.diff(tiles[:, 1]) > 0)
@@ -88,6 +97,12 @@ def expected_task_counts(layer, B):
     info = lambda key: mk.moe_mk_forward_info(layer.plan, B, key)
     tiles, mw = row_tiles(layer, B)
     mt = len(tiles)
+    if info("all_token_gate_up"):
+        # gate/up tiles of every expert over all tokens; down-projection tiles only for the
+        # experts that received tokens
+        gemm1, mt = mt * info("NB1"), int(np.count_nonzero(tiles[:, 2]))
+    else:
+        gemm1 = mt * info("NB1")
     S = info("S")
     # a down-projection tile of a forward without wide row tiles spans two narrow column
     # blocks exactly when the tiles are full width and d holds whole pairs of them
@@ -96,5 +111,5 @@ def expected_task_counts(layer, B):
     assert dc == (2 * info("BN") if info("BN") == mk.moe_mk_plan_info(layer.plan, "BN1")
                   and layer.d % (2 * info("BN")) == 0 else info("BN")), (dc, S, info("BN"))
     return {"route": info("route_tasks"), "topk": info("T"), "scan": 1, "group": info("T"),
-            "gemm1": mt * info("NB1"), "gemm2": S * mt * (info("NB2_wide") if mw else info("NB2")),
+            "gemm1": gemm1, "gemm2": S * mt * (info("NB2_wide") if mw else info("NB2")),
             "combine": info("combine_tasks")}

@@ -116,6 +116,20 @@ int main() {
                     CHECK(L.red_ctr - L.yp >= need, "yp region too small");
                 }
                 CHECK(L.h - L.inv >= (size_t)A * 4 && L.y - L.h >= (size_t)A * s.f * 2, "h region");
+                if (all_token_gate_up(s, B)) {
+                    // one row tile per expert, every expert's gate/up tiles in the static layout
+                    // and the trace, down-projection tasks pushed per expert
+                    ++cases;
+                    CHECK(A >= s.E && s.E <= cc.mt_cap, "E=%d B=%lld cap=%lld: all-token row tiles %d > mt_cap %lld",
+                          s.E, (long long)B, (long long)cap, s.E, (long long)cc.mt_cap);
+                    const int64_t M1 = c.nR + 2 * c.T + 1;
+                    const int64_t total = round8(M1) + t.S * (round8(s.E * (t.NB1 / t.S)) + round8(s.E * t.NB2)) + c.nC;
+                    CHECK(total <= records, "E=%d B=%lld cap=%lld: all-token tasks %lld > %lld trace records", s.E,
+                          (long long)B, (long long)cap, (long long)total, (long long)records);
+                    const int64_t pushed = t.S * s.E * t.NB2 + c.nC;
+                    CHECK(pushed <= cc.q_cap, "E=%d B=%lld cap=%lld: all-token pushes %lld > q_cap %lld", s.E,
+                          (long long)B, (long long)cap, (long long)pushed, (long long)cc.q_cap);
+                }
                 CHECK(L.yp - L.y >= (size_t)A * s.d * 2, "y region");
             }
         }

@@ -73,7 +73,9 @@ def full_check(x, Wr, bias, W1, W3, W2, k, sched, what, debug=0):
     if debug & mk.MOE_MK_DEBUG_NARROW_ONLY or not mk.moe_mk_forward_info(layer.plan, B, "wide_ok") or \
             (debug & mk.MOE_MK_DEBUG_BATCH_RULE and B * k < 128 * E):
         wide_min = 1 << 30
-    check_row_tiles(tiles, mw, ref["hist"], ref["exp_indptr"], wide_min)
+    all_token = bool(mk.moe_mk_forward_info(layer.plan, B, "all_token_gate_up")) and \
+        not debug & mk.MOE_MK_DEBUG_GROUPED_GATE_UP
+    check_row_tiles(tiles, mw, ref["hist"], ref["exp_indptr"], wide_min, all_token=all_token)
     layer.close()
     return out, mw
 
@@ -92,6 +94,31 @@ def test_tiny_config(sched):
     log(f"config tiny sched={SNAME[sched]}")
     cfg2, x, Wr, bias, W1, W3, W2 = small_case(cfg.B, cfg.d, cfg.f, cfg.E, cfg.k, seed=cfg.seed)
     full_check(x, Wr, bias, W1, W3, W2, cfg.k, sched, "tiny config")
+
+
+# Batches of one routing tile in which nearly every expert has tokens run the all-token gate/up
+# (forward_info "all_token_gate_up"): each expert's gate/up tiles take every token of the batch,
+# started before the routing, and the down projection gathers its rows from them.  Per output
+# element that is the same MFMA sequence as over the grouped rows, so the result equals the
+# grouped gate/up (MOE_MK_DEBUG_GROUPED_GATE_UP) bit for bit.  Cases: 16, 32 and 64 staged A rows,
+# a four-way split down projection, k = E, and Zipf routing that leaves experts without tokens.
+@pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
+@pytest.mark.parametrize("B,d,f,E,k,zipf", [(16, 256, 512, 8, 2, None), (24, 256, 384, 8, 2, None),
+                                           (64, 256, 256, 16, 4, None), (32, 256, 8192, 8, 2, None),
+                                           (5, 128, 256, 4, 4, None), (57, 256, 384, 64, 6, None),
+                                           (48, 256, 384, 16, 6, 2.0)],
+                         ids=["a16", "a32", "a64", "split4", "k_eq_E", "sweep_shape", "zipf_idle_experts"])
+def test_all_token_gate_up(B, d, f, E, k, zipf, sched):
+    log(f"all-token gate/up B={B} d={d} f={f} E={E} k={k} zipf={zipf} sched={SNAME[sched]}")
+    assert _info(E, k, d, f, B, "all_token_gate_up") == 1
+    cfg, x, Wr, bias, W1, W3, W2 = small_case(B, d, f, E, k, seed=4000 + B, zipf_s=zipf)
+    ref = oracle.forward(x, Wr, bias, W1, W3, W2, k)
+    if zipf:
+        assert np.count_nonzero(ref["hist"] == 0) >= 1  # experts that get no token
+    dense, _ = full_check(x, Wr, bias, W1, W3, W2, k, sched, "all-token gate/up")
+    grouped, _ = full_check(x, Wr, bias, W1, W3, W2, k, sched, "grouped gate/up",
+                            debug=mk.MOE_MK_DEBUG_GROUPED_GATE_UP)
+    assert np.array_equal(dense.view(np.uint32), grouped.view(np.uint32))
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
