@@ -288,13 +288,12 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
  *   "wide_ok"                 1 when experts may take wide row tiles in this forward (the
  *                             kernel then gives them to experts with at least
  *                             plan_info("wide_min_rows") rows; see moe_mk_routing_view)
- *   "all_token_gate_up"       1 when this forward runs every expert's gate/up tiles over all
- *                             B tokens, started before the routing is known (a batch of one
- *                             routing tile in which under half an expert is expected to get no
- *                             token: E (1 - k/E)^B <= 1/2, full-width tiles); the down
- *                             projection then gathers its rows from them, and the routing view
- *                             lists one row tile per expert (rows 0 for an expert without
- *                             tokens).  0 with MOE_MK_DEBUG_GROUPED_GATE_UP set.
+ *   "all_token_gate_up"       1 when gate/up tiles that start before the routing is known run
+ *                             over all B tokens and keep their expert's rows at the end (a
+ *                             batch of one routing tile in which an expert gets no token with
+ *                             probability (1 - k/E)^B <= 1/4, full-width tiles); the routing
+ *                             view then lists one row tile per expert (rows 0 for an expert
+ *                             without tokens).  0 with MOE_MK_DEBUG_GROUPED_GATE_UP set.
  * Returns -1 for an unknown key, an invalid plan, B < 1 or B*k >= 2^31.
  * Source: [RaMP] abstract (what follows from the batch size alone, as opposed to the
  * routing distribution, which only the device sees).

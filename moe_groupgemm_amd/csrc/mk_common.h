@@ -151,19 +151,19 @@ inline bool half_width(const Shape &s, int64_t B) {
     // cost: ring fill, epilogue, notify; halving it gains nothing)
     return a <= kBM && 2 * rt * (s.f / kBN) <= kGridDefault && (int64_t)s.d * kHalfBN * 4 >= (256 << 10);
 }
-// All-token gate/up (a batch of one routing tile in which nearly every expert has rows):
-// every expert's gate/up tiles run over all B tokens instead of its grouped rows, so they
-// depend on nothing and start with the forward, streaming the weights while the batch is
-// routed; the down projection gathers each grouped row's h from them (row e*B + token).  The
-// extra multiply-adds cost nothing at these batch sizes (the tiles are bound by their weight
-// bytes); the cost is the gate/up weights of experts that end up with no rows, so the mode is
-// taken only when under half an expert is expected to be idle under uniform routing
-// (E (1 - k/E)^B <= 1/2) and the tiles are full width.
+// All-token gate/up (a batch of one routing tile in which most experts get tokens): gate/up
+// tiles that start before the routing is known run over all B tokens instead of waiting for
+// their expert's grouped rows, and keep the rows of the tokens that chose the expert once the
+// routing is out; tiles that start later run over the grouped rows (or only notify, for an
+// expert without tokens).  The extra multiply-adds cost nothing at these batch sizes (the tiles
+// are bound by their weight bytes); the cost is the weight bytes of the early tiles whose expert
+// ends up without tokens, so the mode is taken when an expert is idle with probability at most
+// 1/4 under uniform routing ((1 - k/E)^B <= 1/4) and the tiles are full width.
 inline bool all_token_gate_up(const Shape &s, int64_t B) {
     if (B < 1 || B > kTileTokens || half_width(s, B)) return false;
     double p = 1.0;
     for (int64_t i = 0; i < B; ++i) p *= 1.0 - (double)s.k / (double)s.E;
-    return (double)s.E * p <= 0.5;
+    return p <= 0.25;
 }
 struct Tiles {
     int BN;      // columns of a narrow tile: kBN, or kHalfBN (half_width)
