@@ -13,6 +13,12 @@
 //     notification on purpose, where the watchdog must end the forward;
 //   * the control words and every counter are back at their rest values afterwards, and
 //     the next forward (next epoch) runs on the same control block.
+// Shapes marked dense run the all-token gate/up of a one-tile batch: one row tile per expert
+// (possibly empty), gate/up tiles that start before the scan's result word compute over every
+// token and then wait for it, later ones only if their expert has rows; the scan arms the
+// gate/up events with atomic adds (the tiles may have counted them down already) and whoever
+// brings one to zero fires it; in the dynamic schedule the top-k task and the gate/up tiles
+// are tickets without a queue slot.
 // Events follow the kernel: a counter rests at 0 (the scan event at 1); producers add
 // their deltas and the consumer (static) arms it with the expected count before waiting,
 // so a counter may pass through negative values; the event fires when it reaches 0.
@@ -54,6 +60,7 @@ struct Config {
     double zipf;  // 0: uniform routing
     bool dynamic;
     bool drop_notify;
+    bool dense;  // all-token gate/up (a batch of one routing tile)
 };
 
 int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -99,6 +106,10 @@ Routing make_routing(const Config &c, std::mt19937_64 &rng) {
     for (int e = 0; e < c.E; ++e) {
         r.mt_base[e] = (int)r.mt_expert.size();
         const int h = r.hist[e];
+        if (c.dense) {  // row tile e: all of expert e's rows (at most 64), possibly none
+            r.mt_expert.push_back(e), r.mt_row0.push_back(r.indptr[e]), r.mt_rows.push_back(h);
+            continue;
+        }
         int done = 0;
         if (c.wide_ok && h > kBM) {
             erows[e] = kWideBM;
@@ -130,7 +141,7 @@ Routing make_routing(const Config &c, std::mt19937_64 &rng) {
 struct Sim {
     const Config &c;
     const Routing &r;
-    int T, gpt, nTG, nEB, nR, K, Sg, G, M1, M1p, mt, q1, q2, q1p, q2p, N2, bn2, nch, Cb, nC, total, Q;
+    int T, gpt, nTG, nEB, nR, K, Sg, G, M1, M1p, mt, q1, q2, q1p, q2p, N2, bn2, nch, Cb, nC, total, Q, nImp;
     bool wide;
     uint64_t epoch;
     long long watchdog_us;
@@ -175,6 +186,7 @@ struct Sim {
         nch = cdiv(c.d, kChunk);
         nC = cdiv(c.B, c.CT) * nch;
         total = Cb + nC;
+        nImp = nR + (c.dense ? 1 + c.E * c.NB1 : 0);
         ev_logit = std::vector<std::atomic<int>>(T);
         ev_exp = std::vector<std::atomic<int>>(c.E);
         ev_h = std::vector<std::atomic<int>>((size_t)mt * c.S);
@@ -276,15 +288,16 @@ struct Sim {
             route_coords(g, tg, eb);
             L[(size_t)tg * nEB + eb] = 1;
             const int t = tg / gpt;
+            const bool push = dyn && !c.dense;  // (dense: the top-k task has a ticket and waits)
             int delta = -1;
-            if (dyn && tg % gpt == 0 && eb == 0) delta += route_tasks_of_tile(t);
-            if (notify(ev_logit[t], delta) && dyn) push_range(K + t, 1);
+            if (push && tg % gpt == 0 && eb == 0) delta += route_tasks_of_tile(t);
+            if (notify(ev_logit[t], delta) && push) push_range(K + t, 1);
             return true;
         }
         if (g < Sg) {  // TOPK
             runs[g]++;
             const int t = g - K;
-            if (!dyn) {
+            if (!dyn || c.dense) {
                 ev_logit[t].fetch_add(route_tasks_of_tile(t), std::memory_order_relaxed);  // arm
                 if (!wait_zero(ev_logit[t])) return false;
             }
@@ -336,6 +349,21 @@ struct Sim {
             const int kind = decode_gemm(!dyn && wide, g, sp, j);
             runs[g]++;
             if (kind == 0) return true;
+            if (kind == 1 && c.dense) {  // GEMM1, all-token gate/up: row tile m is expert m
+                const int m = j / Q, n = sp * Q + j % Q;
+                if (!scan_seen()) {  // before the routing: every token, then wait for it
+                    if (!wait_scan()) return false;
+                }
+                CHECK(TAB == 1 && P[0] == 1);  // the tables and perm/inv it keeps rows by
+                H[(size_t)m * c.NB1 + n] = 1;
+                if (PLANT == 2 && m == 0 && n == 0) notify(ev_h[(size_t)m * c.S + sp], -1);
+                if (notify(ev_h[(size_t)m * c.S + sp], -1) && dyn) {
+                    CHECK(TAB == 1);
+                    if (r.mt_rows[m] > 0) push_range(base_g2(sp) + m * N2, N2);
+                    if (notify(ctl->ev_g1, -1)) push_range(Cb, nC);
+                }
+                return true;
+            }
             if (kind == 1) {  // GEMM1
                 const int m = j / Q, n = sp * Q + j % Q, e = r.mt_expert[m];
                 // a one-tile batch was grouped before the layout was published: no wait
@@ -352,6 +380,8 @@ struct Sim {
             }
             // GEMM2
             const int m = j / N2, n = j % N2;
+            if (c.dense && !dyn && !wait_scan()) return false;  // the layout was known without it
+            if (c.dense && r.mt_rows[m] == 0) return true;       // an expert without tokens
             if (!dyn && PLANT != 1 && !wait_zero(ev_h[(size_t)m * c.S + sp])) return false;
             for (int nn = sp * Q; nn < (sp + 1) * Q; ++nn) CHECK(H[(size_t)m * c.NB1 + nn] == 1);
             bool done = true;
@@ -377,6 +407,7 @@ struct Sim {
         runs[g]++;
         const int cc = g - Cb, grp = cc / nch, chunk = cc % nch;
         const int b_lo = grp * c.CT, nb = std::min(c.CT, c.B - b_lo);
+        if (c.dense && !dyn && !wait_scan()) return false;
         if (T > 1 && !wait_zero(ev_logit[b_lo / kTile])) return false;
         CHECK(P[b_lo / kTile] == 1);
         for (int i = 0; i < nb * c.k; ++i)
@@ -390,6 +421,7 @@ struct Sim {
         return true;
     }
     // static: the scan's result word (epoch, row tiles, wide), stored after the scan's tables
+    bool scan_seen() const { return (ctl->scan64.load(std::memory_order_acquire) >> 32) == epoch; }
     void publish_scan() {
         ctl->scan64.store((epoch << 32) | (wide ? 0x80000000ull : 0ull) | (uint32_t)mt, std::memory_order_release);
     }
@@ -421,7 +453,9 @@ struct Sim {
         for (int e = 0; e < c.E; ++e)
             if (arm_exp && r.hist[e]) ev_exp[e].store(r.hist[e], std::memory_order_relaxed);
         for (int m = 0; m < mt; ++m) {
-            for (int s = 0; s < c.S; ++s) ev_h[(size_t)m * c.S + s].store(Q, std::memory_order_relaxed);
+            if (c.dense && r.mt_rows[m] == 0) continue;  // no down projection, no combine reads it
+            if (!c.dense)  // (dense: armed by atomic adds, see fused_scan_group)
+                for (int s = 0; s < c.S; ++s) ev_h[(size_t)m * c.S + s].store(Q, std::memory_order_relaxed);
             for (int ch = 0; ch < nch; ++ch)
                 ev_d[(size_t)m * nch + ch].store(std::min(kChunk, c.d - ch * kChunk) / bn2, std::memory_order_relaxed);
         }
@@ -434,6 +468,25 @@ struct Sim {
     bool fused_scan_group(bool dyn) {  // a batch of one routing tile: scan and grouping in top-k
         publish_tables(false);  // the experts' events stay at rest: no grouping task decrements them
         P[0] = 1;
+        if (c.dense) {
+            int active = 0;
+            for (int e = 0; e < c.E; ++e) active += r.hist[e] > 0;
+            if (dyn) {
+                const int real = K + 1 + c.S * (q1 + active * N2) + nC;
+                ctl->total64.store((epoch << 32) | (uint32_t)real, std::memory_order_release);
+            }
+            const int skip = c.drop_notify ? first_expert(0) : -1;
+            for (int e = 0; e < c.E; ++e)
+                for (int s = 0; s < c.S; ++s) {
+                    const int arm = e == skip ? Q + 1 : Q;  // (a dropped notification: never fires)
+                    if (!notify(ev_h[(size_t)e * c.S + s], arm) || !dyn) continue;
+                    if (r.mt_rows[e] > 0) push_range(base_g2(s) + e * N2, N2);
+                    if (notify(ctl->ev_g1, -1)) push_range(Cb, nC);
+                }
+            if (!dyn) notify(ctl->ev_scan, -1);
+            publish_scan();
+            return true;
+        }
         if (dyn) {
             const int real = K + 1 + c.S * (q1 + q2) + nC;
             ctl->total64.store((epoch << 32) | (uint32_t)real, std::memory_order_release);
@@ -459,7 +512,7 @@ struct Sim {
                 cu.g += c.W;
                 return g;
             }
-            if (!wait_scan()) return -2;
+            if (!c.dense && !wait_scan()) return -2;  // (dense: the layout is known from the start)
             cu.steal = Cb - M1p >= 2 * c.W;
             cu.phase = total - M1p <= c.W ? 2 : 1;
             cu.g = M1p + w;
@@ -494,8 +547,14 @@ struct Sim {
     int pop(int &known_total) {
         const int t = ctl->qhead.fetch_add(1);
         if (t < nR) return t;
+        if (t < nImp) {  // dense: the top-k task, then every gate/up tile, f range by f range
+            const int u = t - nR - 1;
+            if (u < 0) return t;
+            const int sp = u / q1;
+            return base_g1(sp) + (u - sp * q1);
+        }
         if (known_total >= 0 && t >= known_total) return -1;
-        const int i = t - nR;
+        const int i = t - nImp;
         const auto t0 = std::chrono::steady_clock::now();
         for (unsigned it = 0;; ++it) {
             if (i < (int)slots->size()) {
@@ -563,7 +622,9 @@ int forward(const Config &c, const Routing &r, Sim::Ctl &ctl, std::vector<std::a
             else if (g >= s.G && g < s.M1p) expect = s.T > 1 && g - s.G < s.T;
             else if (g >= s.M1p && g < s.Cb) {
                 int sp, j;
-                expect = s.decode_gemm(false, g, sp, j) != 0;
+                const int kind = s.decode_gemm(false, g, sp, j);
+                expect = kind != 0;
+                if (c.dense && kind == 2) expect = r.mt_rows[j / s.N2] > 0;  // pushed only with rows
             }
         }
         if (s.runs[g].load() != expect) {
@@ -602,6 +663,13 @@ int main(int argc, char **argv) {
         {1500, 16,  8, 2304,  8, 16, 3, 18, 9,  1, 8,  24, true,  0.0},
         {600,  16,  4,  256,  4, 16, 2,  2, 1,  1, 4,  16, true,  1.2},
         {130,  64,  1,  256,  4, 16, 2,  2, 1,  1, 4,  16, true,  1.2},
+        // all-token gate/up (dense): the tiny layer, the sweep at B = 57 and 16, a split down
+        // projection, and Zipf routing that leaves experts without tokens
+        {16,    8,  2,  256,  1, 4,  4,  2, 1,  1, 1,  16, false, 0.0, false, false, true},
+        {57,   64,  6, 2048,  1, 4, 11, 16, 8,  1, 1,  16, false, 0.0, false, false, true},
+        {16,   64,  6, 2048,  1, 4, 11, 16, 8,  1, 1,  24, false, 0.0, false, false, true},
+        {32,    8,  2, 4096,  1, 4, 112, 32, 16, 4, 1,  16, false, 0.0, false, false, true},
+        {48,   16,  6,  256,  1, 4,  3,  2, 1,  1, 1,  16, false, 2.0, false, false, true},
     };
     std::vector<std::atomic<uint64_t>> slots(1 << 16);
     for (auto &s : slots) s.store(0);
@@ -631,7 +699,7 @@ int main(int argc, char **argv) {
     // a dropped notification must end the forward through the watchdog, then the control
     // block is usable again
     for (int dyn = 0; dyn < 2; ++dyn)
-        for (const Config *bp : {&shapes[2], &shapes[4]}) {
+        for (const Config *bp : {&shapes[2], &shapes[4], &shapes[10]}) {
             Config c = *bp;
             c.dynamic = dyn != 0;
             c.drop_notify = true;
