@@ -328,6 +328,13 @@ __device__ __forceinline__ bool wg_notify(const MK_C Params &P, MK_G int *ctr, i
 __device__ __forceinline__ void lds_dma16(const MK_G void *src, MK_L void *dst_wave_base) {
     __builtin_amdgcn_global_load_lds(src, dst_wave_base, 16, 0, 0);
 }
+// The same with the non-temporal hint (cache policy bit nt), for the weight tiles of an expert
+// that has a single row tile: its weight bytes are read once.  On MI355X such loads measured
+// much faster (a decode forward streaming 2.8 GB of weights: 491 -> 446 us); for experts whose
+// row tiles share weight columns through L2 (and in the wide tiles) the hint measured slower.
+__device__ __forceinline__ void lds_dma16_nt(const MK_G void *src, MK_L void *dst_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, dst_wave_base, 16, 0, 2);
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t *p) {
     return (uint32_t)(uintptr_t)(const MK_L uint16_t *)p;
@@ -1299,7 +1306,7 @@ __device__ __forceinline__ int a_block() {
 // Issue the loads of one K stage.  A: one 1 KB block per wave; B: each wave moves
 // B_BLOCKS / kWaves 1 KB blocks (4 k-rows of 256 bytes, or 8 of 128 bytes at half width) of
 // every weight tile.
-template <bool DUAL, int AR, int BN = kBN>
+template <bool DUAL, int AR, int BN = kBN, bool NT = false>
 __device__ __forceinline__ void stage_load(const GemmArgs &g, int k0, uint16_t *stage) {
     using C = GemmCfg<DUAL, AR, BN>;
     uint16_t *sA = stage, *sB0 = stage + C::A_ELEMS, *sB1 = sB0 + C::B_ELEMS;
@@ -1315,8 +1322,15 @@ __device__ __forceinline__ void stage_load(const GemmArgs &g, int k0, uint16_t *
         constexpr int CPR = BN / 8;  // 16-byte chunks per k-row
         const int kr = (64 / CPR) * blk + lane / CPR;
         const int lc = (lane % CPR) ^ (BN == kBN ? wswb(kr) : hswb(kr));
-        lds_dma16(g.B0 + (size_t)(k0 + kr) * g.ldb + 8 * lc, (MK_L void *)(sB0 + blk * 512));
-        if constexpr (DUAL) lds_dma16(g.B1 + (size_t)(k0 + kr) * g.ldb + 8 * lc, (MK_L void *)(sB1 + blk * 512));
+        const MK_G uint16_t *b0 = g.B0 + (size_t)(k0 + kr) * g.ldb + 8 * lc;
+        const MK_G uint16_t *b1 = g.B1 + (size_t)(k0 + kr) * g.ldb + 8 * lc;
+        if constexpr (NT) {
+            lds_dma16_nt(b0, (MK_L void *)(sB0 + blk * 512));
+            if constexpr (DUAL) lds_dma16_nt(b1, (MK_L void *)(sB1 + blk * 512));
+        } else {
+            lds_dma16(b0, (MK_L void *)(sB0 + blk * 512));
+            if constexpr (DUAL) lds_dma16(b1, (MK_L void *)(sB1 + blk * 512));
+        }
     }
 }
 
@@ -1425,7 +1439,7 @@ __device__ __forceinline__ void stage_compute(const uint16_t *stage, int nrb, f3
 
 
 
-template <bool DUAL, int AR, int BN = kBN>
+template <bool DUAL, int AR, int BN = kBN, bool NT = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], f32x4 (&acc1)[4], GemmSmem &s) {
     using C = GemmCfg<DUAL, AR, BN>;
     constexpr int NS = C::NS;
@@ -1438,7 +1452,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], 
     const int nk = uni(ga.K / kBK);
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
-        if (p < nk) stage_load<DUAL, AR, BN>(ga, p * kBK, s.ring + p * C::STAGE_ELEMS);
+        if (p < nk) stage_load<DUAL, AR, BN, NT>(ga, p * kBK, s.ring + p * C::STAGE_ELEMS);
     int slot = 0;  // ring slot of stage st
     if constexpr (AR == 16) {
         // Small tiles (decode batch sizes): the stages that issue the loads of stage st + NS - 1,
@@ -1450,7 +1464,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], 
             wait_vm<(NS - 2) * C::LOADS>();  // stage st has landed: at most NS - 2 newer stages outstanding
             bare_barrier();  // every wave's part of stage st is in LDS; the slot of st-1 is free
             const int ns = slot == 0 ? NS - 1 : slot - 1;  // (st - 1) mod NS
-            stage_load<DUAL, AR, BN>(ga, (st + NS - 1) * kBK, s.ring + ns * C::STAGE_ELEMS);
+            stage_load<DUAL, AR, BN, NT>(ga, (st + NS - 1) * kBK, s.ring + ns * C::STAGE_ELEMS);
             stage_compute<DUAL, AR, BN>(s.ring + slot * C::STAGE_ELEMS, nrb, acc0, acc1);
             slot = slot == NS - 1 ? 0 : slot + 1;
         }
@@ -1471,7 +1485,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &ga, f32x4 (&acc0)[4], 
             const int nxt = st + NS - 1;
             if (nxt < nk) {
                 const int ns = slot == 0 ? NS - 1 : slot - 1;  // (st - 1) mod NS
-                stage_load<DUAL, AR, BN>(ga, nxt * kBK, s.ring + ns * C::STAGE_ELEMS);
+                stage_load<DUAL, AR, BN, NT>(ga, nxt * kBK, s.ring + ns * C::STAGE_ELEMS);
             }
             stage_compute<DUAL, AR, BN>(s.ring + slot * C::STAGE_ELEMS, nrb, acc0, acc1);
             slot = slot == NS - 1 ? 0 : slot + 1;
@@ -1557,7 +1571,8 @@ __device__ __forceinline__ bool wg_wait_routed(const MK_C Params &P) {
 // for the routing and writes the row of each token that chose expert e to that token's grouped
 // h row (inv), dropping the others.  Otherwise the A rows are grouped rows, gathered from x
 // through perm.  Returns false when the wait for the routing failed.
-template <int AR, int BN = kBN, bool DENSE = false>
+// NT: the weight loads carry the non-temporal hint (the expert has this row tile only).
+template <int AR, int BN = kBN, bool DENSE = false, bool NT = false>
 __device__ __forceinline__ bool gemm1_tile(const MK_C Params &P, int e, int row0, int nrows, int n) {
     GemmArgs ga;
     const int ar = a_row<AR>(nrows);
@@ -1568,7 +1583,7 @@ __device__ __forceinline__ bool gemm1_tile(const MK_C Params &P, int e, int row0
     ga.ldb = P.f;
     ga.K = P.d;
     f32x4 acc0[4], acc1[4];
-    gemm_tile<true, AR, BN>(ga, acc0, acc1, g_sm.u.g);
+    gemm_tile<true, AR, BN, NT>(ga, acc0, acc1, g_sm.u.g);
     int *dmap = (int *)g_sm.u.g.ring;  // DENSE: grouped h row of each token, or -1 (the ring is free now)
     if constexpr (DENSE) {
         static_assert(BN == kBN, "all-token tiles are full width");
@@ -1612,7 +1627,7 @@ __device__ __forceinline__ bool gemm1_tile(const MK_C Params &P, int e, int row0
 // it streams 512-byte W2 row segments through one K loop instead of two 256-byte ones.
 // Returns whether this call completed the y tile (always with S = 1; with S > 1 only for the
 // split that added the partials).  SPLITS = false: code for S = 1 only.
-template <int AR, int BN = kBN, bool PAIR = false, bool SPLITS = true>
+template <int AR, int BN = kBN, bool PAIR = false, bool SPLITS = true, bool NT = false>
 __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0, int nrows, int n, int sp,
                                            int mt) {
     static_assert(!PAIR || (BN == kBN && kWideBN == 2 * kBN), "a pair of narrow column blocks spans a wide task");
@@ -1625,7 +1640,7 @@ __device__ __forceinline__ bool gemm2_tile(const MK_C Params &P, int e, int row0
     ga.ldb = P.d;
     ga.K = kl;
     f32x4 acc0[4], acc1[4];
-    gemm_tile<PAIR, AR, BN>(ga, acc0, acc1, g_sm.u.g);
+    gemm_tile<PAIR, AR, BN, NT>(ga, acc0, acc1, g_sm.u.g);
     const int lane = lane_id(), w = wave_id();
     const int g = lane >> 4, j = lane & 15;
     // at half width waves 4-7 handed their sums to waves 0-3 and write nothing
@@ -2152,34 +2167,35 @@ __device__ __forceinline__ void wide_gemm2(const MK_C Params &Pa, int e, int row
 // call; the wide tiles, which need nearly all registers, are inlined for that reason).
 // GEMM1 tile: h[rows, n0:n0+128] = bf16( silu(x_g W1[e]) * (x_g W3[e]) ) for one row tile,
 // where row p of the tile is token perm[p] / k of x; AR = staged A rows (16 or 64).
-template <int AR, int BN = kBN, bool DENSE = false>
+template <int AR, int BN = kBN, bool DENSE = false, bool NT = false>
 __device__ __attribute__((noinline)) bool narrow_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
     const MK_C Params &P = uni_params(Pa);
-    return gemm1_tile<AR, BN, DENSE>(P, uni(e), uni(row0), uni(nrows), uni(n));
+    return gemm1_tile<AR, BN, DENSE, NT>(P, uni(e), uni(row0), uni(nrows), uni(n));
 }
 // All-token gate/up tile of expert e over every token of the batch (see gemm1_tile).
 __device__ __forceinline__ bool dense_gemm1(const MK_C Params &P, int e, int n) {
     const int B = uni(P.B);
-    if (B <= 16) return narrow_gemm1<16, kBN, true>(P, e, 0, B, n);
-    if (B <= 32) return narrow_gemm1<32, kBN, true>(P, e, 0, B, n);
-    return narrow_gemm1<64, kBN, true>(P, e, 0, B, n);
+    // (an all-token forward's expert has one row tile)
+    if (B <= 16) return narrow_gemm1<16, kBN, true, true>(P, e, 0, B, n);
+    if (B <= 32) return narrow_gemm1<32, kBN, true, true>(P, e, 0, B, n);
+    return narrow_gemm1<64, kBN, true, true>(P, e, 0, B, n);
 }
 // GEMM2 tile: y[rows, n0:n0+128] (or its split-sp partial) = h[rows, f range sp] W2[e][f range sp, n0:n0+128].
-template <int AR, int BN = kBN>
+template <int AR, int BN = kBN, bool NT = false>
 __device__ __attribute__((noinline)) bool narrow_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n,
                                                        int sp, int mt) {
     const MK_C Params &P = uni_params(Pa);
-    return gemm2_tile<AR, BN>(P, uni(e), uni(row0), uni(nrows), uni(n), uni(sp), uni(mt));
+    return gemm2_tile<AR, BN, false, true, NT>(P, uni(e), uni(row0), uni(nrows), uni(n), uni(sp), uni(mt));
 }
 
 // ... over kWideBN columns as one two-weight tile (gemm2_tile PAIR); SPLITS: S > 1 possible
 // (the split code raises a 64-row tile's registers past the caller-saved set, so S = 1 has
 // its own copy).
-template <int AR, bool SPLITS>
+template <int AR, bool SPLITS, bool NT = false>
 __device__ __attribute__((noinline)) bool narrow_gemm2_pair(const MK_C Params &Pa, int e, int row0, int nrows,
                                                             int n2, int sp, int mt) {
     const MK_C Params &P = uni_params(Pa);
-    return gemm2_tile<AR, kBN, true, SPLITS>(P, uni(e), uni(row0), uni(nrows), uni(n2), uni(sp), uni(mt));
+    return gemm2_tile<AR, kBN, true, SPLITS, NT>(P, uni(e), uni(row0), uni(nrows), uni(n2), uni(sp), uni(mt));
 }
 
 // The tile code follows the row tile's rows: a row tile of more than kBM rows is a wide one
@@ -2188,38 +2204,60 @@ __device__ __attribute__((noinline)) bool narrow_gemm2_pair(const MK_C Params &P
 // kWideBN (Params::DC), a down-projection task spans kWideBN columns, which a narrow row tile
 // covers with one two-weight narrow tile over both column halves.
 // WIDE: the code may meet wide row tiles (the task loop of forwards that have them).
+template <bool WIDE, bool NT>
+__device__ __forceinline__ void narrow_task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
+    if (!WIDE && uni(P.BN) == kHalfBN)  // (never in a forward with wide row tiles)
+        nrows <= 16 ? narrow_gemm1<16, kHalfBN, false, NT>(P, e, row0, nrows, n)
+                    : narrow_gemm1<64, kHalfBN, false, NT>(P, e, row0, nrows, n);
+    else if (nrows <= 16)
+        narrow_gemm1<16, kBN, false, NT>(P, e, row0, nrows, n);
+    else
+        narrow_gemm1<64, kBN, false, NT>(P, e, row0, nrows, n);
+}
+// single: the row tile holds all of its expert's rows (its narrow tiles' weight loads then
+// carry the non-temporal hint; see lds_dma16_nt).
 template <bool WIDE>
-__device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n) {
+__device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n, bool single) {
     if (WIDE && nrows > kBM)
         wide_gemm1(P, e, row0, nrows, n);
-    else if (!WIDE && uni(P.BN) == kHalfBN)  // (never in a forward with wide row tiles)
-        nrows <= 16 ? narrow_gemm1<16, kHalfBN>(P, e, row0, nrows, n) : narrow_gemm1<64, kHalfBN>(P, e, row0, nrows, n);
-    else if (nrows <= 16)
-        narrow_gemm1<16>(P, e, row0, nrows, n);
+    else if (single)
+        narrow_task_gemm1<WIDE, true>(P, e, row0, nrows, n);
     else
-        narrow_gemm1<64>(P, e, row0, nrows, n);
+        narrow_task_gemm1<WIDE, false>(P, e, row0, nrows, n);
+}
+template <bool WIDE, bool NT>
+__device__ __forceinline__ bool narrow_task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n, int sp,
+                                                  int mt) {
+    if (WIDE || uni(P.DC) == kWideBN) {  // both column halves in one tile
+        if (!WIDE && uni(P.S) > 1)  // (never in a forward with wide row tiles)
+            return nrows <= 16 ? narrow_gemm2_pair<16, true, NT>(P, e, row0, nrows, n, sp, mt)
+                               : narrow_gemm2_pair<64, true, NT>(P, e, row0, nrows, n, sp, mt);
+        return nrows <= 16 ? narrow_gemm2_pair<16, false, NT>(P, e, row0, nrows, n, sp, mt)
+                           : narrow_gemm2_pair<64, false, NT>(P, e, row0, nrows, n, sp, mt);
+    }
+    if (uni(P.BN) == kHalfBN)
+        return nrows <= 16 ? narrow_gemm2<16, kHalfBN, NT>(P, e, row0, nrows, n, sp, mt)
+                           : narrow_gemm2<64, kHalfBN, NT>(P, e, row0, nrows, n, sp, mt);
+    if (nrows <= 16) return narrow_gemm2<16, kBN, NT>(P, e, row0, nrows, n, sp, mt);
+    return narrow_gemm2<64, kBN, NT>(P, e, row0, nrows, n, sp, mt);
 }
 // Returns whether the task completed its y tile (see gemm2_tile).
 template <bool WIDE>
-__device__ __forceinline__ bool task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n, int sp, int mt) {
+__device__ __forceinline__ bool task_gemm2(const MK_C Params &P, int e, int row0, int nrows, int n, int sp, int mt,
+                                           bool single) {
     static_assert(kWideBN % kBN == 0, "a wide down tile spans whole narrow tiles");
     if (WIDE && nrows > kBM) {
         wide_gemm2(P, e, row0, nrows, n);
         return true;
     }
-    if (WIDE || uni(P.DC) == kWideBN) {  // both column halves in one tile
-        if (!WIDE && uni(P.S) > 1)  // (never in a forward with wide row tiles)
-            return nrows <= 16 ? narrow_gemm2_pair<16, true>(P, e, row0, nrows, n, sp, mt)
-                               : narrow_gemm2_pair<64, true>(P, e, row0, nrows, n, sp, mt);
-        return nrows <= 16 ? narrow_gemm2_pair<16, false>(P, e, row0, nrows, n, sp, mt)
-                           : narrow_gemm2_pair<64, false>(P, e, row0, nrows, n, sp, mt);
-    }
-    if (uni(P.BN) == kHalfBN)
-        return nrows <= 16 ? narrow_gemm2<16, kHalfBN>(P, e, row0, nrows, n, sp, mt)
-                           : narrow_gemm2<64, kHalfBN>(P, e, row0, nrows, n, sp, mt);
-    if (nrows <= 16) return narrow_gemm2<16>(P, e, row0, nrows, n, sp, mt);
-    return narrow_gemm2<64>(P, e, row0, nrows, n, sp, mt);
+    return single ? narrow_task_gemm2<WIDE, true>(P, e, row0, nrows, n, sp, mt)
+                  : narrow_task_gemm2<WIDE, false>(P, e, row0, nrows, n, sp, mt);
 }
+
+// Whether row tile mt (of expert e, mt_total row tiles in expert order) holds all of the
+// expert's rows: neither neighbour belongs to e.  (The neighbours' entries are loaded with the
+// tile's own, in one round trip.)
+__device__ __forceinline__ bool single_row_tile(int e, int e_prev, int e_next) { return e_prev != e && e_next != e; }
 
 // ------------------------------------------------------------------------------ COMBINE
 // out[b, :] = bf16( sum_{i<k} w[b,i] * y[inv[b*k+i], :] ), slot order, fp32, for
@@ -2746,7 +2784,7 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
                 const unsigned long long t1 = now_ticks();
                 if (routing_seen(P, bs)) {
                     const int r0_ = P.mt_row0[mt], nr_ = P.mt_rows[mt];
-                    if (uni(nr_) > 0) task_gemm1<false>(P, mt, uni(r0_), uni(nr_), n);
+                    if (uni(nr_) > 0) task_gemm1<false>(P, mt, uni(r0_), uni(nr_), n, true);
                 } else {
                     if (!dense_gemm1(P, mt, n)) return 0;
                     bs.routed = true;  // (it waited for the scan's result word)
@@ -2770,14 +2808,16 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
                 return kTaskDone;
             }
             }
-            // the row tile's table entries are read together (one round trip)
+            // the row tile's table entries (and its neighbours' experts) are read together (one
+            // round trip)
             const int e_ = P.mt_expert[mt], r0_ = P.mt_row0[mt], nr_ = P.mt_rows[mt];
+            const int ep_ = mt > 0 ? P.mt_expert[mt - 1] : -1, en_ = mt + 1 < bs.mt ? P.mt_expert[mt + 1] : -1;
             const int e = uni(e_);
             // (a batch of one routing tile was grouped before the layout was published, and its
             // experts' events stay at rest, unless the debug flag holds one back)
             if (!dyn && (P.T > 1 || (P.debug & 1)) && !wg_wait_zero(P, P.ev_exp + e)) return 0;
             const unsigned long long t1 = now_ticks();
-            task_gemm1<WIDE>(P, e, uni(r0_), uni(nr_), n);
+            task_gemm1<WIDE>(P, e, uni(r0_), uni(nr_), n, single_row_tile(e, uni(ep_), uni(en_)));
             const unsigned long long t2 = now_ticks();
             count_task(P, K_GEMM1);
             // f range sp of this row tile complete: its down-projection tiles are ready; once
@@ -2801,10 +2841,12 @@ __device__ __forceinline__ int run_task(const MK_C Params &P, int g, Bases &bs, 
         // the row tile's table entries (published with the scan result this workgroup has
         // acquired) are read before the wait, so the two round trips overlap
         const int e_ = P.mt_expert[mt], r0_ = P.mt_row0[mt], nr_ = P.mt_rows[mt];
+        const int ep_ = mt > 0 ? P.mt_expert[mt - 1] : -1, en_ = mt + 1 < bs.mt ? P.mt_expert[mt + 1] : -1;
         if (P.dense && uni(nr_) == 0) return kTaskDone;  // an expert without tokens (static positions)
         if (!dyn && !wg_wait_zero(P, P.ev_h + mt * P.S + sp)) return 0;
         const unsigned long long t1 = now_ticks();
-        const bool done = task_gemm2<WIDE>(P, uni(e_), uni(r0_), uni(nr_), n, sp, mt);
+        const bool done = task_gemm2<WIDE>(P, uni(e_), uni(r0_), uni(nr_), n, sp, mt,
+                                           single_row_tile(uni(e_), uni(ep_), uni(en_)));
         const unsigned long long t2 = now_ticks();
         count_task(P, K_GEMM2);
         // y tile (mt, n) written: one fewer tile of its combine chunk
@@ -3230,10 +3272,13 @@ __global__ void __launch_bounds__(kThreads, 1) moe_unfused_gemm1(Params Parg) {
     const int Q = P.NB1 / P.S, j = uni((int)blockIdx.x), sp = uni((int)blockIdx.y);
     const int mt = j / Q;
     if (mt >= mt_total) return;
+    const int e = uni(P.mt_expert[mt]);
+    const bool single = single_row_tile(e, mt > 0 ? uni(P.mt_expert[mt - 1]) : -1,
+                                        mt + 1 < mt_total ? uni(P.mt_expert[mt + 1]) : -1);
     if (uni(ld_relaxed(P.ctl + CTL_MW)) > 0)
-        task_gemm1<true>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), sp * Q + (j - mt * Q));
+        task_gemm1<true>(P, e, uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), sp * Q + (j - mt * Q), single);
     else
-        task_gemm1<false>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), sp * Q + (j - mt * Q));
+        task_gemm1<false>(P, e, uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), sp * Q + (j - mt * Q), single);
 }
 // Down-projection tile j of f range sp = blockIdx.y.
 __global__ void __launch_bounds__(kThreads, 1) moe_unfused_gemm2(Params Parg) {
@@ -3243,10 +3288,13 @@ __global__ void __launch_bounds__(kThreads, 1) moe_unfused_gemm2(Params Parg) {
     const int N2 = wide ? P.NB2w : P.NB2, j = uni((int)blockIdx.x), sp = uni((int)blockIdx.y);
     const int mt = j / N2;
     if (mt >= mt_total) return;
+    const int e = uni(P.mt_expert[mt]);
+    const bool single = single_row_tile(e, mt > 0 ? uni(P.mt_expert[mt - 1]) : -1,
+                                        mt + 1 < mt_total ? uni(P.mt_expert[mt + 1]) : -1);
     if (wide)
-        task_gemm2<true>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), j - mt * N2, sp, mt);
+        task_gemm2<true>(P, e, uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), j - mt * N2, sp, mt, single);
     else
-        task_gemm2<false>(P, uni(P.mt_expert[mt]), uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), j - mt * N2, sp, mt);
+        task_gemm2<false>(P, e, uni(P.mt_row0[mt]), uni(P.mt_rows[mt]), j - mt * N2, sp, mt, single);
 }
 __global__ void __launch_bounds__(kThreads, 1) moe_unfused_combine(Params Parg) {
     const MK_C Params &P = *(const MK_C Params *)__builtin_amdgcn_kernarg_segment_ptr();
