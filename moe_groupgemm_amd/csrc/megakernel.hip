@@ -331,7 +331,9 @@ __device__ __forceinline__ void lds_dma16(const MK_G void *src, MK_L void *dst_w
 // The same with the non-temporal hint (cache policy bit nt), for the weight tiles of an expert
 // that has a single row tile: its weight bytes are read once.  On MI355X such loads measured
 // much faster (a decode forward streaming 2.8 GB of weights: 491 -> 446 us); for experts whose
-// row tiles share weight columns through L2 (and in the wide tiles) the hint measured slower.
+// row tiles share weight columns through L2 the hint measured slower, so they keep plain loads.
+// (Narrow tiles take the choice as a template argument; the wide tiles, whose K loop is
+// inlined, branch on a wave-uniform flag at each weight load.)
 __device__ __forceinline__ void lds_dma16_nt(const MK_G void *src, MK_L void *dst_wave_base) {
     __builtin_amdgcn_global_load_lds(src, dst_wave_base, 16, 0, 2);
 }
@@ -1761,6 +1763,7 @@ struct WideArgs {
     const MK_G uint16_t *B0, *B1;  // weight tile bases (k 0, column n0)
     uint32_t b_off[2];        // this lane's k-row * ldb + 16-byte chunk, per B block it loads
     int ldb, K, nrows;
+    int nt;  // weight loads with the non-temporal hint (the expert has this row tile only)
 };
 
 // Issue all four loads of one K stage (PART 0) or only load PART (1 .. 4: the two A blocks
@@ -1778,12 +1781,18 @@ __device__ __forceinline__ void wstage_load(const WideArgs &g, int k0, uint16_t 
     const size_t kk = (size_t)k0 * g.ldb;
     if constexpr (PART == 0 || PART == 1) lds_dma16(ab + g.a_off[0], (MK_L void *)(sA + (2 * w) * 512));
     if constexpr (PART == 0 || PART == 2) lds_dma16(ab + g.a_off[1], (MK_L void *)(sA + (2 * w + 1) * 512));
+    auto wl = [&](const MK_G uint16_t *src, uint16_t *dst) {
+        if (g.nt)
+            lds_dma16_nt(src, (MK_L void *)dst);
+        else
+            lds_dma16(src, (MK_L void *)dst);
+    };
     if constexpr (DUAL) {
-        if constexpr (PART == 0 || PART == 3) lds_dma16(g.B0 + kk + g.b_off[0], (MK_L void *)(sB0 + w * 512));
-        if constexpr (PART == 0 || PART == 4) lds_dma16(g.B1 + kk + g.b_off[0], (MK_L void *)(sB1 + w * 512));
+        if constexpr (PART == 0 || PART == 3) wl(g.B0 + kk + g.b_off[0], sB0 + w * 512);
+        if constexpr (PART == 0 || PART == 4) wl(g.B1 + kk + g.b_off[0], sB1 + w * 512);
     } else {
-        if constexpr (PART == 0 || PART == 3) lds_dma16(g.B0 + kk + g.b_off[0], (MK_L void *)(sB0 + (2 * w) * 512));
-        if constexpr (PART == 0 || PART == 4) lds_dma16(g.B0 + kk + g.b_off[1], (MK_L void *)(sB0 + (2 * w + 1) * 512));
+        if constexpr (PART == 0 || PART == 3) wl(g.B0 + kk + g.b_off[0], sB0 + (2 * w) * 512);
+        if constexpr (PART == 0 || PART == 4) wl(g.B0 + kk + g.b_off[1], sB0 + (2 * w + 1) * 512);
     }
 }
 
@@ -2089,7 +2098,7 @@ __device__ __forceinline__ void wout_store(const uint8_t *tile, MK_G uint16_t *d
 }
 
 // Wide gate/up tile: kWideBM rows x kWideBN1 columns of h.
-__device__ __forceinline__ void wide_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
+__device__ __forceinline__ void wide_gemm1(const MK_C Params &Pa, int e, int row0, int nrows, int n, bool single) {
     const MK_C Params &P = uni_params(Pa);
     e = uni(e);
     row0 = uni(row0);
@@ -2104,6 +2113,7 @@ __device__ __forceinline__ void wide_gemm1(const MK_C Params &Pa, int e, int row
     ga.B1 = P.W3 + (size_t)e * P.d * P.f + (size_t)n * BN;
     ga.ldb = P.f;
     ga.K = P.d;
+    ga.nt = uni(single ? 1 : 0);
     wide_offsets<true, BN>(ga, [&](int i) {
         return (uint32_t)(P.perm[row0 + wa_row(i, nrows)] / P.k) * (uint32_t)P.d;
     });
@@ -2128,7 +2138,7 @@ __device__ __forceinline__ void wide_gemm1(const MK_C Params &Pa, int e, int row
 }
 
 // Wide down-projection tile: kWideBM rows x kWideBN columns of y.
-__device__ __forceinline__ void wide_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n) {
+__device__ __forceinline__ void wide_gemm2(const MK_C Params &Pa, int e, int row0, int nrows, int n, bool single) {
     const MK_C Params &P = uni_params(Pa);
     e = uni(e);
     row0 = uni(row0);
@@ -2143,6 +2153,7 @@ __device__ __forceinline__ void wide_gemm2(const MK_C Params &Pa, int e, int row
     ga.B1 = ga.B0;
     ga.ldb = P.d;
     ga.K = P.f;
+    ga.nt = uni(single ? 1 : 0);
     wide_offsets<false, BN>(ga, [&](int i) { return (uint32_t)wa_row(i, nrows) * (uint32_t)P.f; });
     f32x4 acc0[C::NACC], acc1[C::NACC];
     wide_tile<false, BN>(ga, acc0, acc1, g_sm.u.g);
@@ -2219,7 +2230,7 @@ __device__ __forceinline__ void narrow_task_gemm1(const MK_C Params &P, int e, i
 template <bool WIDE>
 __device__ __forceinline__ void task_gemm1(const MK_C Params &P, int e, int row0, int nrows, int n, bool single) {
     if (WIDE && nrows > kBM)
-        wide_gemm1(P, e, row0, nrows, n);
+        wide_gemm1(P, e, row0, nrows, n, single);
     else if (single)
         narrow_task_gemm1<WIDE, true>(P, e, row0, nrows, n);
     else
@@ -2247,7 +2258,7 @@ __device__ __forceinline__ bool task_gemm2(const MK_C Params &P, int e, int row0
                                            bool single) {
     static_assert(kWideBN % kBN == 0, "a wide down tile spans whole narrow tiles");
     if (WIDE && nrows > kBM) {
-        wide_gemm2(P, e, row0, nrows, n);
+        wide_gemm2(P, e, row0, nrows, n, single);
         return true;
     }
     return single ? narrow_task_gemm2<WIDE, true>(P, e, row0, nrows, n, sp, mt)
