@@ -283,7 +283,8 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
  *                             with them (d / wide_BN2)
  *   "down_cols"               columns of a down-projection tile in a forward without wide row
  *                             tiles: wide_BN2 (two narrow column blocks in one tile) when BN is
- *                             BN1 and d a multiple of wide_BN2, else BN
+ *                             BN1, d a multiple of wide_BN2 and min(B*k, E) * (d / wide_BN2) * S
+ *                             such tasks would fill one round of the grid (256), else BN
  *   "S"                       f ranges of the down projection (1: not split)
  *   "wide_ok"                 1 when experts may take wide row tiles in this forward (the
  *                             kernel then gives them to experts with at least

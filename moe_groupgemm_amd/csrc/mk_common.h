@@ -171,8 +171,8 @@ struct Tiles {
     int NB2;     // down-projection tiles per narrow row tile and f range (d / DC)
     int NB2w;    // down-projection tiles per wide row tile (d / 256)
     int DC;      // columns of a down-projection task in a forward without wide row tiles: 256
-                 // (both 128-column halves in one two-weight tile) with full-width tiles and d a
-                 // multiple of 256, BN otherwise
+                 // (both 128-column halves in one two-weight tile) with full-width tiles, d a
+                 // multiple of 256 and enough such tasks to fill a round of the grid, BN otherwise
     int S;       // f ranges of the down projection
     int wide_ok; // wide row tiles allowed in this forward
 };
@@ -182,6 +182,12 @@ inline Tiles tile_config(const Shape &s, int64_t B) {
     t.NB1 = s.f / t.BN;
     t.S = down_splits(s, B);
     t.DC = t.BN == kBN && s.d % kWideBN == 0 ? kWideBN : t.BN;
+    {
+        // ... unless the forward's down-projection tasks of that width would not fill one round of
+        // the grid (at most min(B*k, E) row tiles): then the more, narrower tasks finish sooner
+        const int64_t rt = B * s.k < s.E ? B * s.k : s.E;
+        if (t.DC == kWideBN && rt * (s.d / kWideBN) * t.S < kGridDefault) t.DC = t.BN;
+    }
     t.NB2 = s.d / t.DC;
     t.NB2w = s.d / kWideBN;
     t.wide_ok = t.S == 1 && t.BN == kBN && s.d % kWideBN == 0 && s.f % kWideBN1 == 0;

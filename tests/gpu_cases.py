@@ -104,12 +104,11 @@ def expected_task_counts(layer, B):
     else:
         gemm1 = mt * info("NB1")
     S = info("S")
-    # a down-projection tile of a forward without wide row tiles spans two narrow column
-    # blocks exactly when the tiles are full width and d holds whole pairs of them
+    # a down-projection tile of a forward without wide row tiles spans one narrow column block
+    # or, with full-width tiles, two (forward_info "down_cols"); they tile d exactly
     dc = info("down_cols")
     assert dc * info("NB2") == layer.d, (dc, info("NB2"), layer.d)
-    assert dc == (2 * info("BN") if info("BN") == mk.moe_mk_plan_info(layer.plan, "BN1")
-                  and layer.d % (2 * info("BN")) == 0 else info("BN")), (dc, S, info("BN"))
+    assert dc == info("BN") or (dc == 2 * info("BN") == 2 * mk.moe_mk_plan_info(layer.plan, "BN1")), (dc, S)
     return {"route": info("route_tasks"), "topk": info("T"), "scan": 1, "group": info("T"),
             "gemm1": gemm1, "gemm2": S * mt * (info("NB2_wide") if mw else info("NB2")),
             "combine": info("combine_tasks")}

@@ -246,14 +246,14 @@ def test_wide_tiles_static_dynamic_identical():
 
 
 @pytest.mark.parametrize("sched", SCHEDS, ids=["static", "dynamic"])
-@pytest.mark.parametrize("d,f,S,dc", [(256, 4096, 2, 256), (384, 512, 1, 128)], ids=["split_pairs", "no_split"])
+@pytest.mark.parametrize("d,f,S,dc", [(256, 4096, 2, 128), (384, 512, 1, 128)], ids=["split", "no_split"])
 def test_exact_row_counts_narrow_forward(d, f, S, dc, sched):
     # A narrow forward whose routing is set by the input (token b's logit e is x[b, e]), so
     # the experts receive exactly 1, 16, 17, 40, 3, 0, 5 and 2 rows: row tiles at both sides of
-    # the 16-row tile variant.  With d = 256 the down projection is split in two f ranges and
-    # its tasks are two-weight tiles of 256 columns (forward_info "down_cols"), each split's
-    # partials added by the last one; with d = 384 it is not split and its tasks are
-    # 128-column tiles.
+    # the 16-row tile variant.  With d = 256 the down projection is split in two f ranges, each
+    # split's partials added by the last one; with d = 384 it is not split.  Either way its
+    # tasks are 128-column tiles (forward_info "down_cols": 256-column tasks would not fill a
+    # round of the grid here); the two-weight split tiles run in the Mixtral-shaped test.
     counts = [1, 16, 17, 40, 3, 0, 5, 2]
     E, k = len(counts), 1
     B = sum(counts)
