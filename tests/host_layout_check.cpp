@@ -144,6 +144,37 @@ int main() {
             prev = t;
         }
     }
+    // the per-batch policies of the named workloads: which forwards run the all-token gate/up
+    // (an expert idle with probability <= 1/4 in a one-tile batch), the width of the narrow
+    // down-projection tasks, the down-projection splits and the half-width tiles
+    {
+        struct Case {
+            Shape s;
+            int64_t B;
+            bool all_token;
+            int dc, S, BN;
+        };
+        const Case pol[] = {
+            {{8, 2, 4096, 14336}, 32, true, 256, 4, 128},    // Mixtral decode
+            {{8, 2, 4096, 14336}, 4, false, 256, 4, 128},    // Mixtral, a batch of 4: idle p = 0.32
+            {{64, 6, 2048, 1408}, 1, false, 64, 1, 64},      // sweep B = 1: half width
+            {{64, 6, 2048, 1408}, 3, false, 128, 1, 128},    // sweep B = 3: 18 x 8 pair tasks < 256
+            {{64, 6, 2048, 1408}, 16, true, 256, 1, 128},    // sweep B = 16: idle p = 0.21
+            {{64, 6, 2048, 1408}, 57, true, 256, 1, 128},
+            {{64, 6, 2048, 1408}, 128, false, 256, 1, 128},  // two routing tiles
+            {{256, 8, 7168, 2048}, 128, false, 256, 1, 128}, // DeepSeek-shaped
+            {{128, 8, 2048, 768}, 4096, false, 256, 1, 128}, // prefill
+            {{8, 2, 256, 512}, 16, true, 128, 1, 128},       // tiny: 8 experts x 1 pair task < 256
+        };
+        for (const Case &c : pol) {
+            ++cases;
+            const Tiles t = tile_config(c.s, c.B);
+            CHECK(all_token_gate_up(c.s, c.B) == c.all_token, "E=%d B=%lld: all-token %d", c.s.E, (long long)c.B,
+                  (int)all_token_gate_up(c.s, c.B));
+            CHECK(t.DC == c.dc && t.S == c.S && t.BN == c.BN, "E=%d B=%lld: DC %d S %d BN %d", c.s.E, (long long)c.B,
+                  t.DC, t.S, t.BN);
+        }
+    }
     std::printf("%d cases, %d failures\n", cases, fails);
     return fails != 0;
 }
