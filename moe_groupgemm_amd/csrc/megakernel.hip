@@ -35,6 +35,11 @@
 //   GEMM2(mt,s,n) down GroupGEMM tile over f range s -> y         -> ev_d[mt, column chunk]
 //   COMBINE(c)    out[b] = sum_i w[b,i] y[inv[b,i]] for 1, 4 or 8 tokens and 2048 columns,
 //                 after its tokens' grouping and the row tiles its rows use
+// In a batch of one routing tile where nearly every expert gets tokens (Params::dense), the
+// row tiles are one per expert and known from the start; a GEMM1 tile that starts before the
+// scan's result word is out runs over every token and keeps its expert's rows at the end, so
+// the gate/up weights stream while the batch is routed, and the scan arms ev_h with atomic adds.
+// Weight loads of experts that have a single row tile carry the non-temporal hint.
 #include <hip/hip_runtime.h>
 
 #include <mutex>

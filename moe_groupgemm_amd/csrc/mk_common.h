@@ -353,9 +353,10 @@ struct Params {
     // Set for the phase-per-kernel pipeline (the unfused baseline): kernel boundaries order
     // the phases, so the scan arms no events and the workspace stays at its rest state.
     int unfused;
-    // All-token gate/up (all_token_gate_up): row tile e is expert e's rows (possibly none),
-    // gate/up tile (e, n) computes h rows e*B .. e*B + B - 1 for every token, and in the dynamic
-    // schedule the top-k task and the gate/up tiles are handed out without a push.
+    // All-token gate/up (all_token_gate_up): row tile e is expert e's rows (possibly none); a
+    // gate/up tile that starts before the routing is known runs over every token and keeps its
+    // expert's grouped rows at the end; in the dynamic schedule the top-k task and the gate/up
+    // tiles are handed out without a push.
     int dense;
     int nImp;  // dynamic schedule: tickets handed out without a queue slot (routers, and with dense the top-k
                // task and the gate/up tiles)
