@@ -294,7 +294,10 @@ int64_t moe_mk_plan_info(moe_mk_plan_t plan, const char *key);
  *                             batch of one routing tile in which an expert gets no token with
  *                             probability (1 - k/E)^B <= 1/4, full-width tiles); the routing
  *                             view then lists one row tile per expert (rows 0 for an expert
- *                             without tokens).  0 with MOE_MK_DEBUG_GROUPED_GATE_UP set.
+ *                             without tokens).  The probability assumes roughly uniform routing;
+ *                             under strong skew the early tiles of idle experts stream their
+ *                             weights for nothing (at most one round of the grid's tiles).  0 with
+ *                             MOE_MK_DEBUG_GROUPED_GATE_UP set.
  * Returns -1 for an unknown key, an invalid plan, B < 1 or B*k >= 2^31.
  * Source: [RaMP] abstract (what follows from the batch size alone, as opposed to the
  * routing distribution, which only the device sees).
